@@ -1,0 +1,385 @@
+"""Pins for the fp64 CPU oracle: what the pages and the mathematics fix.
+
+Each test ties one oracle function to something other than itself: the
+worked moe_align_block_size example printed on the vLLM MoE page, a
+separately written brute-force form, a closed form, an invariant, or a
+special case that reduces to a textbook computation. None of these tests
+touches the GPU.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import brute
+from oracle import moe_oracle as om
+from workloads import make_config, make_layer, zipf_bias
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+
+
+def _adversarial_logits(rng, n, E):
+    """Random fp32 logits with planted ties, equal rows, -inf entries and signed zeros."""
+    L = rng.standard_normal((n, E)).astype(np.float32)
+    L[0, :] = 0.25  # all equal
+    L[1, : E // 2] = L[1, E // 2 :]  # every value duplicated
+    L[2, :] = -np.inf
+    L[2, E - 1] = 1.0
+    L[2, 0] = 0.5  # only a few finite
+    L[3, :] = np.where(np.arange(E) % 2 == 0, np.float32(0.0), np.float32(-0.0))
+    L[4, :] = np.round(L[4, :] * 2) / 2  # coarse grid: many ties
+    L[5, ::3] = -np.inf
+    return L
+
+
+# ---------------------------------------------------------------------------
+# The printed worked example
+# ---------------------------------------------------------------------------
+
+
+def test_worked_example_moe_align_block_size(golden_dir):
+    ex = json.load(open(os.path.join(golden_dir, "moe_align_block_size_example.json")))
+    e_top = np.array(ex["topk_ids_as_printed"]) - ex["id_base"]
+    E, K, BM = ex["E"], ex["K"], ex["BLOCK_SIZE_M"]
+    counts = oracle.expert_counts(e_top, E)
+    assert counts.tolist() == [ex["hits_per_expert"]] * E
+    perm, inv = oracle.permutation(e_top, E)
+    offsets = oracle.offsets_from_counts(counts)
+    # Rebuild the page's padded layout from (perm, offsets): each expert's
+    # segment padded to a multiple of BLOCK_SIZE_M, one expert id per block.
+    padded, block_expert = [], []
+    for e in range(E):
+        seg = perm[offsets[e] : offsets[e + 1]].tolist()
+        nblk = -(-len(seg) // BM)
+        padded += seg + ["PAD"] * (nblk * BM - len(seg))
+        block_expert += [e] * nblk
+    assert padded == ex["sorted_token_ids_as_printed"]
+    assert block_expert == ex["expert_ids_as_printed"]
+    assert len(padded) == ex["num_tokens_post_padded"]
+    assert (perm[inv] == np.arange(E * 3)).all()
+
+
+# ---------------------------------------------------------------------------
+# Router: softmax and top-K
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("E,K", [(8, 2), (8, 8), (64, 8), (5, 1), (64, 64), (3, 2)])
+def test_topk_matches_bruteforce_on_ties(E, K):
+    rng = np.random.default_rng(E * 100 + K)
+    L = _adversarial_logits(rng, 40, E) if E >= 6 else rng.standard_normal((40, E)).astype(np.float32)
+    e_top, w_top, p = oracle.route_from_logits(L, K, renorm=False)
+    for i, row in enumerate(L.tolist()):
+        a = brute.topk_argmax_passes(row, K)
+        b = brute.topk_full_sort(row, K)
+        assert e_top[i].tolist() == a == b, (i, row)
+        pb = brute.softmax_row(row)
+        np.testing.assert_allclose(p[i], pb, rtol=1e-13, atol=1e-300)
+
+
+def test_topk_invariants_and_renorm():
+    rng = np.random.default_rng(7)
+    L = _adversarial_logits(rng, 200, 16)
+    K = 4
+    e_top, w_top, p = oracle.route_from_logits(L, K, renorm=False)
+    for i in range(L.shape[0]):
+        sel = set(e_top[i].tolist())
+        assert len(sel) == K
+        unsel = [e for e in range(16) if e not in sel]
+        assert min(L[i, e_top[i]]) >= max(L[i, unsel])
+        assert (np.diff(w_top[i]) <= 0).all()  # non-increasing by slot
+        assert (w_top[i] >= 0).all()
+        # ties among selected: ascending expert index within equal logits
+        for k in range(K - 1):
+            if L[i, e_top[i, k]] == L[i, e_top[i, k + 1]]:
+                assert e_top[i, k] < e_top[i, k + 1]
+    e2, w2, _ = oracle.route_from_logits(L, K, renorm=True)
+    assert (e2 == e_top).all()
+    np.testing.assert_allclose(w2.sum(axis=1), 1.0, atol=1e-12)
+    np.testing.assert_allclose(w2, w_top / w_top.sum(axis=1, keepdims=True), rtol=1e-15)
+
+
+def test_softmax_closed_forms():
+    # Two experts: p0 = 1 / (1 + exp(l1 - l0)) (the logistic function).
+    L = np.array([[0.3, -1.2], [5.0, 5.0], [-40.0, 2.0]], dtype=np.float32)
+    _, _, p = oracle.route_from_logits(L, 1, renorm=False)
+    l64 = L.astype(np.float64)
+    np.testing.assert_allclose(p[:, 0], 1.0 / (1.0 + np.exp(l64[:, 1] - l64[:, 0])), rtol=1e-14)
+    # Shift invariance, rows sum to one, -inf gives probability 0.
+    rng = np.random.default_rng(3)
+    L = rng.standard_normal((20, 9)).astype(np.float32)
+    L[:, 4] = -np.inf
+    _, _, p1 = oracle.route_from_logits(L, 3, renorm=False)
+    _, _, p2 = oracle.route_from_logits(L + np.float32(8.0), 3, renorm=False)
+    np.testing.assert_allclose(p1.sum(axis=1), 1.0, atol=1e-14)
+    assert (p1[:, 4] == 0).all()
+    np.testing.assert_allclose(p1, p2, atol=1e-6)  # fp32 shift rounds the inputs slightly
+
+
+def test_topk_e_equals_k_renorm_is_full_softmax():
+    rng = np.random.default_rng(11)
+    L = rng.standard_normal((10, 6)).astype(np.float32)
+    e_top, w_top, p = oracle.route_from_logits(L, 6, renorm=True)
+    for i in range(10):
+        np.testing.assert_allclose(w_top[i], p[i, e_top[i]], rtol=1e-14)
+
+
+def test_router_logits_small_closed_form():
+    x = np.array([[1.0, 2.0], [0.5, -1.0]])
+    W = np.array([[1.0, 0.0, 2.0], [0.0, 1.0, -1.0]])
+    b = np.array([0.0, 1.0, -np.inf], dtype=np.float32)
+    L = oracle.router_logits(x, W, b)
+    assert L[0].tolist()[:2] == [1.0, 3.0] and L[1].tolist()[:2] == [0.5, 0.0]
+    assert np.isneginf(L[:, 2]).all()
+
+
+# ---------------------------------------------------------------------------
+# Counts, offsets, splits, permutation
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("n,E,K,ep", [(37, 8, 2, 4), (64, 8, 8, 1), (300, 64, 8, 8), (1, 4, 4, 2), (0, 8, 2, 2)])
+def test_dispatch_metadata_invariants(n, E, K, ep):
+    rng = np.random.default_rng(n + E + K)
+    L = rng.standard_normal((n, E)).astype(np.float32)
+    e_top, _, _ = oracle.route_from_logits(L, K, renorm=False) if n else (np.zeros((0, K), np.int32), None, None)
+    counts = oracle.expert_counts(e_top, E)
+    offsets = oracle.offsets_from_counts(counts)
+    splits = oracle.splits_by_rank(e_top, E, ep)
+    assert counts.sum() == n * K and (counts >= 0).all() and (counts <= n).all()
+    assert offsets[0] == 0 and offsets[-1] == n * K and (np.diff(offsets) == counts).all()
+    assert (splits == oracle.splits_from_offsets(offsets, ep)).all() and splits.sum() == n * K
+    perm, inv = oracle.permutation(e_top, E)
+    assert sorted(perm.tolist()) == list(range(n * K))  # bijection
+    assert (perm[inv] == np.arange(n * K)).all() and (inv[perm] == np.arange(n * K)).all()
+    flat = e_top.reshape(-1)
+    for e in range(E):
+        seg = perm[offsets[e] : offsets[e + 1]]
+        assert (flat[seg] == e).all()
+        assert (np.diff(seg) > 0).all()
+    # An independently written stable sort by expert gives the same order.
+    assert (np.argsort(flat, kind="stable") == perm).all()
+    if n * K <= 2400:
+        pb, ib = brute.permutation_triple_loop(e_top.tolist(), E)
+        assert perm.tolist() == pb and inv.tolist() == ib
+
+
+def test_splits_reject_bad_ep():
+    with pytest.raises(ValueError):
+        oracle.splits_by_rank(np.zeros((3, 2), np.int32), 8, 3)
+
+
+# ---------------------------------------------------------------------------
+# Experts and the whole layer
+# ---------------------------------------------------------------------------
+
+
+def _tiny(n=9, H=16, I=8, E=4, K=2, renorm=False, seed=5, dtype="f32"):  # noqa: E741
+    return make_layer(n, H, I, E, K, dtype=dtype, renorm=renorm, seed=seed, w_std=0.3)
+
+
+@pytest.mark.parametrize("renorm", [False, True])
+@pytest.mark.parametrize("E,K", [(4, 2), (4, 1), (4, 4), (6, 3)])
+def test_layer_matches_per_token_and_dense_bruteforce(E, K, renorm):
+    w = _tiny(E=E, K=K, renorm=renorm, seed=E * 10 + K)
+    out = oracle.forward(w.x_f32, w.W_gate_f32, w.W13_f32, w.W2_f32, K, renorm, keep_permuted=True)
+    e_b, w_b = brute.route(out["logits_f32"], K, renorm)
+    assert out["e_top"].tolist() == e_b
+    np.testing.assert_allclose(out["w_top"], np.array(w_b), rtol=1e-13)
+    y_tok = brute.layer_per_token(w.x_f32, e_b, w_b, w.W13_f32, w.W2_f32)
+    y_dense = brute.layer_dense(w.x_f32, e_b, w_b, w.W13_f32, w.W2_f32)
+    np.testing.assert_allclose(out["y"], y_tok, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(out["y"], y_dense, rtol=1e-12, atol=1e-14)
+    # The slot-order combine of the expert-major outputs is the same layer.
+    y_c = oracle.combine_slot_order(out["Y_perm"], out["inv"], out["w_top"], w.n, K)
+    np.testing.assert_allclose(out["y"], y_c, rtol=1e-12, atol=1e-14)
+
+
+def test_single_expert_is_plain_swiglu_ffn():
+    """E = 1, K = 1: the layer is one dense SwiGLU FFN; gate = first I columns."""
+    w = _tiny(E=1, K=1)
+    out = oracle.forward(w.x_f32, w.W_gate_f32, w.W13_f32, w.W2_f32, 1, False)
+    x = w.x_f32.astype(np.float64)
+    W_gate_proj = w.W13_f32[0][:, : w.I].astype(np.float64)
+    W_up_proj = w.W13_f32[0][:, w.I :].astype(np.float64)
+    g = np.einsum("nh,hi->ni", x, W_gate_proj)
+    u = np.einsum("nh,hi->ni", x, W_up_proj)
+    sig = np.array([[1.0 / (1.0 + math.exp(-v)) for v in row] for row in g])
+    ref = np.einsum("ni,ih->nh", g * sig * u, w.W2_f32[0].astype(np.float64))
+    assert (out["w_top"] == 1.0).all()
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_identical_experts_with_renorm_give_the_ffn():
+    """All experts equal and weights renormalised: y = FFN(x) whatever the routing."""
+    w = _tiny(E=5, K=3, renorm=True)
+    W13 = np.repeat(w.W13_f32[:1], 5, axis=0)
+    W2 = np.repeat(w.W2_f32[:1], 5, axis=0)
+    out = oracle.forward(w.x_f32, w.W_gate_f32, W13, W2, 3, True)
+    ref = np.stack([brute.ffn_token(w.x_f32[i], W13[0], W2[0]) for i in range(w.n)])
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_k_equals_e_with_renorm_is_dense_softmax_mixture():
+    w = _tiny(E=4, K=4, renorm=True)
+    out = oracle.forward(w.x_f32, w.W_gate_f32, w.W13_f32, w.W2_f32, 4, True)
+    L = out["logits_f32"].astype(np.float64)
+    p = np.exp(L - L.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    ref = np.zeros_like(out["y"])
+    for i in range(w.n):
+        for e in range(4):
+            ref[i] += p[i, e] * brute.ffn_token(w.x_f32[i], w.W13_f32[e], w.W2_f32[e])
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_linearity_in_w2():
+    w = _tiny(E=4, K=2)
+    out0 = oracle.forward(w.x_f32, w.W_gate_f32, w.W13_f32, np.zeros_like(w.W2_f32), 2, False)
+    assert (out0["y"] == 0).all()
+    a = oracle.forward(w.x_f32, w.W_gate_f32, w.W13_f32, w.W2_f32, 2, False)["y"]
+    b = oracle.forward(w.x_f32, w.W_gate_f32, w.W13_f32, 2.5 * w.W2_f32.astype(np.float64), 2, False)["y"]
+    np.testing.assert_allclose(b, 2.5 * a, rtol=1e-13, atol=1e-15)
+
+
+def test_silu_identities():
+    # silu(z) - silu(-z) = z, silu(0) = 0, and silu(z) ~ z for large z.
+    X = np.array([[1.0]])
+    for z in [-3.0, -0.5, 0.0, 0.7, 4.0]:
+        W13 = np.array([[z, 1.0]])  # gate column = z, up column = 1
+        W2 = np.array([[1.0]])
+        fz = oracle.expert_ffn(X, W13, W2)[0, 0]
+        fm = oracle.expert_ffn(X, np.array([[-z, 1.0]]), W2)[0, 0]
+        assert abs((fz - fm) - z) < 1e-15
+    big = oracle.expert_ffn(X, np.array([[40.0, 1.0]]), np.array([[1.0]]))[0, 0]
+    assert abs(big - 40.0) < 1e-12
+    # gate is the first half: gate = -3, up = 2 gives silu(-3) * 2, not silu(2) * (-3)
+    v = oracle.expert_ffn(X, np.array([[-3.0, 2.0]]), np.array([[1.0]]))[0, 0]
+    assert abs(v - (-3.0 / (1 + math.exp(3.0)) * 2.0)) < 1e-15
+
+
+def test_grouped_swiglu_matches_layer_segments():
+    w = _tiny(E=4, K=2)
+    out = oracle.forward(w.x_f32, w.W_gate_f32, w.W13_f32, w.W2_f32, 2, False, keep_permuted=True)
+    xp = w.x_f32[out["perm"] // 2]
+    Y = om.grouped_swiglu(xp, out["offsets"], w.W13_f32, w.W2_f32)
+    np.testing.assert_allclose(Y, out["Y_perm"], rtol=1e-14, atol=1e-16)
+
+
+# ---------------------------------------------------------------------------
+# The named workloads: properties the configs promise
+# ---------------------------------------------------------------------------
+
+
+def test_zipf_bias_recipe():
+    b = zipf_bias(64)
+    q = np.arange(1, 65, dtype=np.float64) ** -1.2
+    q /= q.sum()
+    finite = np.isfinite(b)
+    assert (~finite).sum() == 8 and np.isneginf(b[7::8]).all()
+    np.testing.assert_allclose(b[finite], (3 * np.log(q))[finite], rtol=1e-6)
+    assert (np.diff(b[finite]) < 0).all()  # rank 1 is the most favoured
+
+
+@pytest.mark.slow
+def test_skewed_config_routing_properties():
+    w = make_config("olmoe_skewed_bf16")
+    L = oracle.round_to_f32(oracle.router_logits(w.x_f32, w.W_gate_f32, w.bias))
+    e_top, _, _ = oracle.route_from_logits(L, w.K, renorm=False)
+    counts = oracle.expert_counts(e_top, w.E)
+    assert (counts[7::8] == 0).all()
+    cv = counts.std() / counts.mean()
+    assert cv > 1.0, cv
+    assert counts.max() == w.n  # a hot expert takes every token
+
+
+def test_tiny_config_routing_is_renormalised():
+    w = make_config("tiny_f32")
+    out = oracle.forward(w.x_f32, w.W_gate_f32, w.W13_f32, w.W2_f32, w.K, w.renorm)
+    np.testing.assert_allclose(out["w_top"].sum(1), 1.0, atol=1e-12)
+    assert out["counts"].sum() == w.n * w.K
+
+
+def test_ep_share_oracle_small():
+    from workloads.gen import make_ep_share
+
+    ep = make_ep_share(R=96, H=32, I=16, E_local=4, S=3, alpha=0.5, w_std=0.2)
+    mb = ep.micro_batches[0]
+    out = om.ep_share_forward(mb.x_f32, mb.eid, ep.W13_f32, ep.W2_f32)
+    # counts agree with the generator's own multinomial draw
+    assert (out["counts"] == mb.counts).all()
+    assert (out["counts"] == mb.source_counts.sum(0)).all()
+    # every row goes through its own expert, in arrival order
+    for r in range(ep.R):
+        ref = brute.ffn_token(mb.x_f32[r], ep.W13_f32[mb.eid[r]], ep.W2_f32[mb.eid[r]])
+        np.testing.assert_allclose(out["out"][r], ref, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: the pins above must notice plausible slips in the oracle
+# ---------------------------------------------------------------------------
+
+
+def _pins_pass(fn, *a):
+    try:
+        fn(*a)
+        return True
+    except AssertionError:
+        return False
+
+
+def test_planted_mistakes_are_caught(monkeypatch, golden_dir):
+    # 1. Ties to the highest expert index.
+    orig_route = om.route_from_logits
+
+    def route_ties_high(L, K, renorm):
+        L = np.asarray(L, np.float32)
+        E = L.shape[1]
+        e, w, p = orig_route(L[:, ::-1], K, renorm)
+        return (E - 1 - e).astype(np.int32), w, p[:, ::-1]
+
+    monkeypatch.setattr(oracle, "route_from_logits", route_ties_high)
+    assert not _pins_pass(test_topk_matches_bruteforce_on_ties, 8, 2)
+    monkeypatch.undo()
+
+    # 2. Gate and up halves swapped.
+    def ffn_swapped(X, W13, W2):
+        W13 = np.asarray(W13, np.float64)
+        I = W13.shape[1] // 2  # noqa: E741
+        return orig_ffn(X, np.concatenate([W13[:, I:], W13[:, :I]], axis=1), W2)
+
+    orig_ffn = om.expert_ffn
+    monkeypatch.setattr(om, "expert_ffn", ffn_swapped)
+    assert not _pins_pass(test_single_expert_is_plain_swiglu_ffn)
+    monkeypatch.undo()
+
+    # 3. Segments in descending token order (an unstable permutation).
+    orig_perm = om.permutation
+
+    def perm_reversed(e_top, E):
+        perm, _ = orig_perm(e_top, E)
+        counts = oracle.expert_counts(e_top, E)
+        offs = oracle.offsets_from_counts(counts)
+        perm = np.concatenate([perm[offs[e] : offs[e + 1]][::-1] for e in range(E)])
+        inv = np.empty_like(perm)
+        inv[perm] = np.arange(perm.size)
+        return perm, inv
+
+    monkeypatch.setattr(oracle, "permutation", perm_reversed)
+    assert not _pins_pass(test_worked_example_moe_align_block_size, golden_dir)
+    monkeypatch.undo()
+
+    # 4. Weights taken from the logits instead of the softmax.
+    def route_no_softmax(L, K, renorm):
+        e, w, p = orig_route(L, K, renorm)
+        return e, np.take_along_axis(np.asarray(L, np.float64), e.astype(np.int64), 1), p
+
+    monkeypatch.setattr(om, "route_from_logits", route_no_softmax)
+    assert not _pins_pass(test_layer_matches_per_token_and_dense_bruteforce, 4, 2, False)
+    monkeypatch.undo()
