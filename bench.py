@@ -1,0 +1,211 @@
+"""Benchmark of the MoE expert-layer forward on one MI355X.
+
+One step = one `moe_forward` call (router GEMM, softmax/top-K, counts,
+offsets and permutation with the row gather, grouped SwiGLU GEMM1 and GEMM2,
+weighted combine) over the OLMoE-shaped layer: n=4096 tokens, H=2048,
+I=1024, E=64 experts, top-8, bf16 storage with fp32 accumulation, synthetic
+seeded inputs already resident in HBM.
+
+Prints ONE JSON line with tokens/s for the whole layer, the grouped-GEMM
+TFLOP/s, per-stage times and bandwidths, the roofline of the dominant kernel
+(the GEMM1 + SwiGLU launch) timed with HIP events on the stream it runs on,
+and the CPU oracle timed on the host as a reported baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd tokens/s + grouped-GEMM TFLOP/s (% bf16 peak), OLMoE n=4096"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
+
+
+def _parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="olmoe_bf16", choices=["olmoe_bf16", "olmoe_skewed_bf16", "decode_bf16"])
+    p.add_argument("--stage-reps", type=int, default=20)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle wall time for the CPU baseline")
+    return p.parse_args()
+
+
+def _time_region(fn, reps, torch):
+    """Average ms per call of fn() over `reps` calls, HIP events on the current stream."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(
+            f"bench.py measures one GPU only: the layer runs on a single MI355X and this build has no "
+            f"multi-GPU path (asked for --gpus {args.gpus}).",
+            file=sys.stderr,
+        )
+        sys.exit(2)
+
+    import torch
+
+    import routing_token_permute_amd as moe
+    from workloads import make_config
+
+    dev = torch.device("cuda:0")
+    w = make_config(args.workload)
+    n, H, I, E, K = w.n, w.H, w.I, w.E, w.K  # noqa: E741
+
+    def to_dev(name):
+        b = w.bits(name)
+        return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x, Wg, W13, W2 = (to_dev(k) for k in ("x", "W_gate", "W13", "W2"))
+    bias = None if w.bias is None else torch.from_numpy(w.bias).to(dev)
+    y = torch.empty((n, H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(moe.moe_forward_workspace_size(n, H, I, E, K, torch.bfloat16), dtype=torch.uint8, device=dev)
+
+    def step():
+        moe.moe_forward(x, Wg, W13, W2, K, w.renorm, bias=bias, y=y, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms_events = _time_region(step, args.steps, torch)
+    wall = time.perf_counter() - t0
+    ms_per_step = ms_events
+    tokens_per_s = n / (ms_per_step * 1e-3)
+
+    # ---- per-stage timing: each stage alone, on its own inputs ----
+    logits, ids, wts = moe.moe_route(x, Wg, bias, K, w.renorm)
+    meta = moe.moe_permute(ids, x, E)
+    h = moe.moe_expert_w13_swiglu(meta["x_perm"], meta["offsets"], W13)
+    Yp = moe.moe_expert_w2(h, meta["offsets"], W2)
+    yc = moe.moe_unpermute_combine(Yp, meta["inv"], wts, n, K)
+    torch.cuda.synchronize()
+    counts = meta["counts"].cpu().numpy()
+    R = args.stage_reps
+    st = {
+        "route": _time_region(lambda: moe.moe_route(x, Wg, bias, K, w.renorm, logits=logits, topk_ids=ids, topk_w=wts), R, torch),
+        "permute": _time_region(lambda: moe.moe_permute(ids, x, E, out=meta), R, torch),
+        "gemm1_swiglu": _time_region(lambda: moe.moe_expert_w13_swiglu(meta["x_perm"], meta["offsets"], W13, h=h), R, torch),
+        "gemm2": _time_region(lambda: moe.moe_expert_w2(h, meta["offsets"], W2, Y_perm=Yp), R, torch),
+        "combine": _time_region(lambda: moe.moe_unpermute_combine(Yp, meta["inv"], wts, n, K, y=yc), R, torch),
+    }
+    nk = n * K
+    hit = int((counts > 0).sum())
+    flops1 = 2.0 * nk * H * 2 * I
+    flops2 = 2.0 * nk * I * H
+    # Algorithmic bytes per call (each input read once, each output written once).
+    bytes_ = {
+        "route": n * H * 2 + H * E * 2 + n * E * 4 + nk * 8,
+        "permute": nk * 4 + n * H * 2 + nk * H * 2 + nk * 8 + (2 * E + 2) * 4,
+        "gemm1_swiglu": nk * H * 2 + hit * H * 2 * I * 2 + nk * I * 2,
+        "gemm2": nk * I * 2 + hit * I * H * 2 + nk * H * 2,
+        "combine": nk * H * 2 + nk * 8 + n * H * 2,
+    }
+    stages = {}
+    for k, ms in st.items():
+        s = {"ms": round(ms, 5), "GB/s": round(bytes_[k] / (ms * 1e-3) / 1e9, 1)}
+        s["frac_hbm"] = round(s["GB/s"] / PEAK_HBM_GBPS, 4)
+        if k == "gemm1_swiglu":
+            s["TFLOP/s"] = round(flops1 / (ms * 1e-3) / 1e12, 1)
+        if k == "gemm2":
+            s["TFLOP/s"] = round(flops2 / (ms * 1e-3) / 1e12, 1)
+        stages[k] = s
+    gg_ms = st["gemm1_swiglu"] + st["gemm2"]
+    gg_tflops = (flops1 + flops2) / (gg_ms * 1e-3) / 1e12
+    g1_tflops = flops1 / (st["gemm1_swiglu"] * 1e-3) / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = _cpu_baseline(w, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights, OLMoE layer shapes; no checkpoint)",
+        "config": {"workload": args.workload, "n": n, "H": H, "I": I, "E": E, "K": K, "renorm": bool(w.renorm),
+                   "skewed_bias": w.bias is not None},
+        "grouped_gemm": {"TFLOP/s": round(gg_tflops, 1), "frac_bf16_peak": round(gg_tflops / PEAK_BF16_TFLOPS, 4),
+                         "GFLOP": round((flops1 + flops2) / 1e9, 1)},
+        "stages": stages,
+        "roofline": {
+            "kernel": "gemm_bf16_kernel<GATED=true> (GEMM1 + SwiGLU epilogue)",
+            "bound": "mfma",
+            "achieved": round(g1_tflops, 1),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(g1_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+        "experts_hit": hit,
+        "wall_s_timed_region": round(wall, 3),
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def _cpu_baseline(w, min_seconds):
+    """The fp64 oracle (as it stands) on the host: full-layer forwards until min_seconds pass."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.forward(w.x_f32, w.W_gate_f32, w.W13_f32, w.W2_f32, w.K, w.renorm, bias=w.bias)
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    el = time.perf_counter() - t0
+    return {
+        "value": round(w.n * reps / el, 1),
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"the full {w.n}-token layer forward (fp64 numpy, OpenBLAS), {reps} repetitions, {el:.1f} s",
+        "cpu": platform.processor() or platform.machine(),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,209 @@
+/*
+ * moe.h — C ABI of the single-GPU MoE expert-layer forward on MI355X (gfx950).
+ *
+ * The layer is Algorithm 2 "Single-GPU MoE Forward" of the page
+ * "MoE 分布式推理基础（基于 vLLM）" (cnblogs, §1.2 MoE Forward), with the
+ * router and experts as in the Hugging Face OlmoeTopKRouter /
+ * OlmoeExperts.forward source that section quotes:
+ *
+ *   logits = x · W_gate (+ bias)            (n, E)
+ *   p      = softmax(logits)                 (n, E)
+ *   (w_top, e_top) = TopK(p, K)              (n, K) each, optional renorm
+ *   for each expert e: X_e = rows of x routed to e,
+ *       Y_e = (SiLU(X_e·W13[e][:, :I]) * (X_e·W13[e][:, I:])) · W2[e]
+ *   y[i] = sum over the K slots of w_top[i,k] · Y_{e_top[i,k]}[row of (i,k)]
+ *
+ * Notation follows the page: n tokens, hidden size H, expert intermediate
+ * size I, E experts, top-K. Shapes are row-major:
+ *   x (n, H); W_gate (H, E); W13 (E, H, 2I) with gate = columns [0, I) and
+ *   up = columns [I, 2I); W2 (E, I, H); y (n, H).
+ *
+ * Conventions for every call:
+ *   - All array arguments are DEVICE pointers owned by the caller; the
+ *     library allocates no memory and keeps no per-call state. Scratch memory
+ *     is a caller-supplied workspace whose size the *_workspace_size
+ *     functions return.
+ *   - Calls are asynchronous on the given HIP stream (0 = the null stream)
+ *     and never synchronise the host. Results are valid once the stream has
+ *     reached the end of the call.
+ *   - Arguments are validated on the host before anything is enqueued:
+ *     MOE_EINVAL for null required pointers, negative or zero sizes where a
+ *     size must be positive, K outside [1, min(E, 64)], E outside
+ *     [1, 1024], ep not dividing E, a workspace smaller than required, or
+ *     shapes the kernels do not cover (bf16: H and I multiples of 64;
+ *     fp32: H and I multiples of 4); MOE_EUNSUPPORTED for a dtype value
+ *     that is not built. Nothing is enqueued when a call returns an error.
+ *   - MOE_EHIP reports a kernel launch failure (hipGetLastError after each
+ *     launch); the stream may then hold part of the call's work.
+ *   - n == 0 (or rows == 0) is valid: outputs that have one entry per expert
+ *     or rank are still written (zeros), nothing else is touched.
+ *   - Calls on different streams may run concurrently when their outputs
+ *     and workspaces do not overlap.
+ *   - Results are deterministic: the same inputs give bitwise-identical
+ *     outputs on every run (no floating-point atomics).
+ *   - Expert ids handed to the library must lie in [0, E); a pair whose id
+ *     lies outside is skipped (not counted, not placed; its perm/inv
+ *     entries are undefined) and never causes an out-of-bounds access.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,       /* bad argument, detected on the host before any launch */
+  MOE_EUNSUPPORTED = 2, /* dtype or shape combination not built */
+  MOE_EWORKSPACE = 3,   /* workspace pointer null or smaller than required */
+  MOE_EHIP = 4          /* a HIP launch failed */
+} moe_status;
+
+/* Element type of x, W_gate, W13, W2, x_perm, Y_perm and y.
+ * MOE_BF16: bfloat16 storage, fp32 accumulation (MFMA), the intermediate h
+ *           rounded to bf16 (round-to-nearest-even) before the second GEMM.
+ * MOE_F32:  fp32 storage and arithmetic throughout.
+ * Router logits, routing weights and the bias are fp32 in both cases. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Static description of a status code; never NULL. */
+const char* moe_status_string(moe_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int moe_version(void);
+
+/* ---------------------------------------------------------------------------
+ * moe_route — router GEMM, softmax and top-K (Algorithm 2 steps 1-3; the
+ * OlmoeTopKRouter source of the same section: F.linear, softmax, topk, and
+ * the optional division of the K weights by their sum).
+ *
+ *   x       (n, H) dtype, or NULL: then `logits` is an INPUT the caller filled
+ *           (fp32, (n, E)) and only softmax/top-K run.
+ *   W_gate  (H, E) dtype; ignored when x == NULL.
+ *   bias    (E) fp32 added to each logit after the product, or NULL. -inf
+ *           entries are allowed: such experts get probability 0 and are
+ *           only selected when fewer than K finite logits remain.
+ *   renorm  nonzero: w_top[i,:] /= sum_k w_top[i,k].
+ *   logits  (n, E) fp32: written when x != NULL, read when x == NULL.
+ *   topk_ids (n, K) int32 out: slot 0 holds the largest logit; experts are
+ *           ranked by (fp32 logit descending, expert index ascending), which
+ *           is the softmax order with ties to the lowest index, decided on
+ *           the fp32 logits (-0.0 counts as +0.0).
+ *   topk_w  (n, K) fp32 out: softmax probability of each selected expert
+ *           (max-subtracted, fp32), renormalised if asked.
+ * The router product accumulates in fp32 (bf16: MFMA). NaN logits are not
+ * supported (the selection is then unspecified, still in bounds).
+ * ------------------------------------------------------------------------- */
+moe_status moe_route(const void* x, const void* W_gate, const float* bias, int n, int H, int E, int K,
+                     int renorm, moe_dtype dt, float* logits, int32_t* topk_ids, float* topk_w,
+                     hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_permute — per-expert counts, offsets and per-rank splits, the stable
+ * expert-major permutation of the n*K (token, slot) pairs, and the row
+ * gather x_perm[p] = x[perm[p] / K].
+ *
+ * Defines: n_e = sum 1[e_top = e] (hit statistics under Algorithm 2);
+ * Algorithm 2 step 5/7 (the set I_e and the gather X_e); the expert-sorted
+ * order of moe_align_block_size in §2.3 of the same page (pairs sorted by
+ * expert, ascending flat index i*K+k within an expert, without padding);
+ * the per-rank send sizes of Algorithm 5 step 3 (§2.4); and the torchtitan
+ * `_local_reorder` of the page "0. goin" (§2.2).
+ *
+ *   topk_ids (n, K) int32, each in [0, E).
+ *   x        (n, H) dtype, or NULL to compute the metadata only.
+ *   ep       number of expert-parallel ranks (>= 1, divides E): rank j owns
+ *            experts [j*E/ep, (j+1)*E/ep).
+ *   counts   (E) int32 out: n_e.
+ *   offsets  (E+1) int32 out: offsets[0] = 0, offsets[e+1] = offsets[e] + n_e.
+ *   splits   (ep) int32 out: splits[j] = offsets[(j+1)E/ep] - offsets[jE/ep].
+ *   perm     (n*K) int32 out: perm[p] = flat pair index i*K+k at permuted row p.
+ *   inv      (n*K) int32 out: inv[perm[p]] = p.
+ *   x_perm   (n*K, H) dtype out, or NULL (required when x != NULL).
+ *   ws       workspace of at least moe_permute_workspace_size(n, E, K) bytes.
+ * ------------------------------------------------------------------------- */
+size_t moe_permute_workspace_size(int n, int E, int K);
+moe_status moe_permute(const int32_t* topk_ids, const void* x, int n, int H, int E, int K, int ep,
+                       moe_dtype dt, int32_t* counts, int32_t* offsets, int32_t* splits, int32_t* perm,
+                       int32_t* inv, void* x_perm, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_grouped_swiglu — every expert's SwiGLU FFN on its contiguous segment of
+ * expert-major rows (Algorithm 2 steps 8-9; "SwiGLU expert 的两段 GEMM" of
+ * the same section: gate_up = X_e @ W13[e]; gate, up = chunk(2); h =
+ * silu(gate) * up; Y_e = h @ W2[e]).
+ *
+ *   x_perm   (rows, H) dtype: row r belongs to expert e when
+ *            offsets[e] <= r < offsets[e+1].
+ *   offsets  (E+1) int32, DEVICE memory, nondecreasing, offsets[E] <= rows
+ *            (rows past offsets[E] are left untouched in Y_perm).
+ *   W13      (E, H, 2I) dtype; W2 (E, I, H) dtype.
+ *   Y_perm   (rows, H) dtype out.
+ *   ws       workspace of at least moe_grouped_swiglu_workspace_size(rows, I, dt)
+ *            bytes (it holds h, (rows, I)).
+ * ------------------------------------------------------------------------- */
+size_t moe_grouped_swiglu_workspace_size(int rows, int I, moe_dtype dt);
+moe_status moe_grouped_swiglu(const void* x_perm, const int32_t* offsets, int rows, const void* W13,
+                              const void* W2, int E, int H, int I, moe_dtype dt, void* Y_perm, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+
+/* The two halves of moe_grouped_swiglu, for callers that schedule or time
+ * them separately (same arguments and rules as above).
+ *
+ * moe_expert_w13_swiglu — Algorithm 2 step 8: for every expert segment,
+ *   h = SiLU(X_e · W13[e][:, :I]) * (X_e · W13[e][:, I:]), h (rows, I) dtype out
+ *   (bf16: fp32 accumulation, SiLU and product in fp32, then rounded to bf16).
+ * moe_expert_w2 — Algorithm 2 step 9: Y_perm = h · W2[e] per segment,
+ *   h (rows, I) dtype in, Y_perm (rows, H) dtype out.
+ * Neither needs a workspace. */
+moe_status moe_expert_w13_swiglu(const void* x_perm, const int32_t* offsets, int rows, const void* W13, int E, int H,
+                                 int I, moe_dtype dt, void* h, hipStream_t stream);
+moe_status moe_expert_w2(const void* h, const int32_t* offsets, int rows, const void* W2, int E, int H, int I,
+                         moe_dtype dt, void* Y_perm, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_unpermute_combine — weighted top-K reduction back to token order
+ * (Algorithm 2 steps 10-11, the scatter-add y[i] += Y_e[idx] * w_top[i,k];
+ * the `_unpermute` + weighted deterministic scatter-add of "0. goin" §2.2
+ * and its top-K slot reduction kernel, §2.3):
+ *
+ *   y[i] = sum_{k=0..K-1} w[i,k] * Y_perm[inv[i*K+k]]
+ *
+ * summed in slot order k = 0..K-1 with fp32 accumulation, then stored in dt.
+ *   Y_perm  (n*K, H) dtype; inv (n*K) int32 in [0, n*K);
+ *   topk_w  (n, K) fp32, or NULL for unit weights (with K = 1 this is a plain
+ *           un-permute back to arrival order);
+ *   y       (n, H) dtype out.
+ * ------------------------------------------------------------------------- */
+moe_status moe_unpermute_combine(const void* Y_perm, const int32_t* inv, const float* topk_w, int n, int H,
+                                 int K, moe_dtype dt, void* y, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_forward — the whole layer, Algorithm 2: moe_route, moe_permute (ep=1),
+ * moe_grouped_swiglu and moe_unpermute_combine enqueued back to back on one
+ * stream, with no host synchronisation.
+ *
+ *   y            (n, H) dtype out.
+ *   logits_out   (n, E) fp32 out, or NULL.
+ *   topk_ids_out (n, K) int32 out, or NULL.
+ *   topk_w_out   (n, K) fp32 out, or NULL.
+ *   counts_out   (E) int32 out, or NULL.
+ *   ws           workspace of at least moe_forward_workspace_size(...) bytes.
+ * ------------------------------------------------------------------------- */
+size_t moe_forward_workspace_size(int n, int H, int I, int E, int K, moe_dtype dt);
+moe_status moe_forward(const void* x, const void* W_gate, const float* bias, const void* W13, const void* W2,
+                       int n, int H, int I, int E, int K, int renorm, moe_dtype dt, void* y, float* logits_out,
+                       int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,24 @@
+"""MI355X-native single-GPU MoE expert-layer forward.
+
+The layer (router, softmax/top-K, expert-major permutation with counts,
+offsets and splits, grouped SwiGLU GEMM, weighted combine) runs in the HIP
+kernels of libmoe.so behind the C ABI in include/moe.h; this package is its
+Python binding. Build the library with `python -m routing_token_permute_amd.build`.
+"""
+
+from ._lib import (  # noqa: F401
+    LIB_PATH,
+    MOE_BF16,
+    MOE_F32,
+    MoEError,
+    load_library,
+    moe_expert_w2,
+    moe_expert_w13_swiglu,
+    moe_forward,
+    moe_forward_workspace_size,
+    moe_grouped_swiglu,
+    moe_permute,
+    moe_route,
+    moe_unpermute_combine,
+    status_string,
+)

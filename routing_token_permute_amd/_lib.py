@@ -1,0 +1,314 @@
+"""ctypes binding of libmoe.so: the C ABI declared in include/moe.h.
+
+This module only marshals arguments: it checks tensor shapes, dtypes and
+devices, allocates outputs and workspaces with torch (device memory and
+streams are torch's job here), and passes raw device pointers and the current
+HIP stream to the library. Every step of the layer runs in the library's HIP
+kernels. If the library is missing or cannot be loaded, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libmoe.so")
+
+MOE_F32 = 0
+MOE_BF16 = 1
+
+_VP = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+# (name, restype, argtypes) for every exported function of include/moe.h.
+SIGNATURES = {
+    "moe_status_string": (ctypes.c_char_p, [_I]),
+    "moe_version": (_I, []),
+    "moe_route": (_I, [_VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP]),
+    "moe_permute_workspace_size": (_SZ, [_I, _I, _I]),
+    "moe_permute": (_I, [_VP, _VP, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "moe_grouped_swiglu_workspace_size": (_SZ, [_I, _I, _I]),
+    "moe_grouped_swiglu": (_I, [_VP, _VP, _I, _VP, _VP, _I, _I, _I, _I, _VP, _VP, _SZ, _VP]),
+    "moe_expert_w13_swiglu": (_I, [_VP, _VP, _I, _VP, _I, _I, _I, _I, _VP, _VP]),
+    "moe_expert_w2": (_I, [_VP, _VP, _I, _VP, _I, _I, _I, _I, _VP, _VP]),
+    "moe_unpermute_combine": (_I, [_VP, _VP, _VP, _I, _I, _I, _I, _VP, _VP]),
+    "moe_forward_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "moe_forward": (
+        _I,
+        [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    ),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class MoEError(RuntimeError):
+    pass
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmoe.so once and attach the C signatures. Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise MoEError(
+            f"{path} is not built; build it with `python -m routing_token_permute_amd.build` "
+            "(there is no fallback implementation)"
+        )
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load_library().moe_status_string(code).decode()
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise MoEError(f"{what}: {status_string(code)}")
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise MoEError(f"unsupported dtype {t.dtype}; expected torch.bfloat16 or torch.float32")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device, stream: Optional[torch.cuda.Stream]):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype=None, device=None):
+    if not t.is_cuda:
+        raise MoEError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise MoEError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise MoEError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise MoEError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise MoEError(f"{name} is on {t.device}, expected {device}")
+
+
+def _empty(shape, dtype, device):
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
+    if ws is None:
+        return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    if ws.dtype != torch.uint8 or ws.numel() < nbytes or not ws.is_cuda:
+        raise MoEError(f"workspace must be a uint8 GPU tensor of at least {nbytes} bytes")
+    return ws
+
+
+# ---------------------------------------------------------------------------
+# The five entry points of include/moe.h
+# ---------------------------------------------------------------------------
+
+
+def moe_route(x, W_gate, bias, K: int, renorm: bool, logits=None, topk_ids=None, topk_w=None, stream=None, E=None):
+    """Router GEMM + softmax + top-K. With x None, `logits` (n, E) fp32 is the input.
+
+    Returns (logits, topk_ids, topk_w).
+    """
+    lib = load_library()
+    if x is not None:
+        n, H = x.shape
+        E = W_gate.shape[1]
+        dev = x.device
+        _need(x, "x", (n, H))
+        _need(W_gate, "W_gate", (H, E), x.dtype, dev)
+        dt = _dt(x)
+        if logits is None:
+            logits = _empty((n, E), torch.float32, dev)
+    else:
+        if logits is None:
+            raise MoEError("logits are required when x is None")
+        n, E = logits.shape
+        H = 0
+        dev = logits.device
+        dt = MOE_F32
+    _need(logits, "logits", (n, E), torch.float32, dev)
+    if bias is not None:
+        _need(bias, "bias", (E,), torch.float32, dev)
+    topk_ids = _empty((n, K), torch.int32, dev) if topk_ids is None else topk_ids
+    topk_w = _empty((n, K), torch.float32, dev) if topk_w is None else topk_w
+    _need(topk_ids, "topk_ids", (n, K), torch.int32, dev)
+    _need(topk_w, "topk_w", (n, K), torch.float32, dev)
+    code = lib.moe_route(
+        _ptr(x), _ptr(W_gate), _ptr(bias), n, H, E, K, int(bool(renorm)), dt,
+        _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _stream(dev, stream),
+    )
+    _check(code, "moe_route")
+    return logits, topk_ids, topk_w
+
+
+def moe_permute(topk_ids, x, E: int, ep: int = 1, out=None, ws=None, stream=None):
+    """Counts, offsets, splits, perm, inv and (when x is given) x_perm.
+
+    Returns a dict of tensors; `out` may supply any of them preallocated.
+    """
+    lib = load_library()
+    n, K = topk_ids.shape
+    dev = topk_ids.device
+    _need(topk_ids, "topk_ids", (n, K), torch.int32)
+    out = dict(out or {})
+    H = 0
+    dt = MOE_BF16
+    if x is not None:
+        H = x.shape[1]
+        _need(x, "x", (n, H), None, dev)
+        dt = _dt(x)
+        out.setdefault("x_perm", _empty((n * K, H), x.dtype, dev))
+        _need(out["x_perm"], "x_perm", (n * K, H), x.dtype, dev)
+    out.setdefault("counts", _empty((E,), torch.int32, dev))
+    out.setdefault("offsets", _empty((E + 1,), torch.int32, dev))
+    out.setdefault("splits", _empty((ep,), torch.int32, dev))
+    out.setdefault("perm", _empty((n * K,), torch.int32, dev))
+    out.setdefault("inv", _empty((n * K,), torch.int32, dev))
+    for name, shape in (("counts", (E,)), ("offsets", (E + 1,)), ("splits", (ep,)), ("perm", (n * K,)), ("inv", (n * K,))):
+        _need(out[name], name, shape, torch.int32, dev)
+    nbytes = lib.moe_permute_workspace_size(n, E, K)
+    ws = _workspace(nbytes, dev, ws)
+    code = lib.moe_permute(
+        _ptr(topk_ids), _ptr(x), n, H, E, K, ep, dt,
+        _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["splits"]), _ptr(out["perm"]), _ptr(out["inv"]),
+        _ptr(out.get("x_perm")), _ptr(ws), ws.numel(), _stream(dev, stream),
+    )
+    _check(code, "moe_permute")
+    return out
+
+
+def moe_grouped_swiglu(x_perm, offsets, W13, W2, Y_perm=None, ws=None, stream=None):
+    """Per-expert SwiGLU FFN on expert-major rows. Returns Y_perm (rows, H)."""
+    lib = load_library()
+    rows, H = x_perm.shape
+    E, H2, I2 = W13.shape
+    I = I2 // 2  # noqa: E741
+    dev = x_perm.device
+    if H2 != H:
+        raise MoEError(f"W13 is {tuple(W13.shape)}, expected (E, {H}, 2I)")
+    _need(x_perm, "x_perm", (rows, H))
+    _need(offsets, "offsets", (E + 1,), torch.int32, dev)
+    _need(W13, "W13", (E, H, 2 * I), x_perm.dtype, dev)
+    _need(W2, "W2", (E, I, H), x_perm.dtype, dev)
+    Y_perm = _empty((rows, H), x_perm.dtype, dev) if Y_perm is None else Y_perm
+    _need(Y_perm, "Y_perm", (rows, H), x_perm.dtype, dev)
+    dt = _dt(x_perm)
+    ws = _workspace(lib.moe_grouped_swiglu_workspace_size(rows, I, dt), dev, ws)
+    code = lib.moe_grouped_swiglu(
+        _ptr(x_perm), _ptr(offsets), rows, _ptr(W13), _ptr(W2), E, H, I, dt,
+        _ptr(Y_perm), _ptr(ws), ws.numel(), _stream(dev, stream),
+    )
+    _check(code, "moe_grouped_swiglu")
+    return Y_perm
+
+
+def moe_expert_w13_swiglu(x_perm, offsets, W13, h=None, stream=None):
+    """Algorithm 2 step 8 on expert-major rows: h = SiLU(X W13[:, :I]) * (X W13[:, I:])."""
+    lib = load_library()
+    rows, H = x_perm.shape
+    E, _, I2 = W13.shape
+    I = I2 // 2  # noqa: E741
+    dev = x_perm.device
+    _need(x_perm, "x_perm", (rows, H))
+    _need(offsets, "offsets", (E + 1,), torch.int32, dev)
+    _need(W13, "W13", (E, H, 2 * I), x_perm.dtype, dev)
+    h = _empty((rows, I), x_perm.dtype, dev) if h is None else h
+    _need(h, "h", (rows, I), x_perm.dtype, dev)
+    code = lib.moe_expert_w13_swiglu(
+        _ptr(x_perm), _ptr(offsets), rows, _ptr(W13), E, H, I, _dt(x_perm), _ptr(h), _stream(dev, stream)
+    )
+    _check(code, "moe_expert_w13_swiglu")
+    return h
+
+
+def moe_expert_w2(h, offsets, W2, Y_perm=None, stream=None):
+    """Algorithm 2 step 9 on expert-major rows: Y_perm = h W2[e] per segment."""
+    lib = load_library()
+    rows, I = h.shape  # noqa: E741
+    E, _, H = W2.shape
+    dev = h.device
+    _need(h, "h", (rows, I))
+    _need(offsets, "offsets", (E + 1,), torch.int32, dev)
+    _need(W2, "W2", (E, I, H), h.dtype, dev)
+    Y_perm = _empty((rows, H), h.dtype, dev) if Y_perm is None else Y_perm
+    _need(Y_perm, "Y_perm", (rows, H), h.dtype, dev)
+    code = lib.moe_expert_w2(_ptr(h), _ptr(offsets), rows, _ptr(W2), E, H, I, _dt(h), _ptr(Y_perm), _stream(dev, stream))
+    _check(code, "moe_expert_w2")
+    return Y_perm
+
+
+def moe_unpermute_combine(Y_perm, inv, topk_w, n: int, K: int, y=None, stream=None):
+    """y[i] = sum_k w[i,k] Y_perm[inv[i*K+k]] (unit weights when topk_w is None)."""
+    lib = load_library()
+    rows, H = Y_perm.shape
+    dev = Y_perm.device
+    _need(Y_perm, "Y_perm", (n * K, H))
+    _need(inv, "inv", (n * K,), torch.int32, dev)
+    if topk_w is not None:
+        _need(topk_w, "topk_w", (n, K), torch.float32, dev)
+    y = _empty((n, H), Y_perm.dtype, dev) if y is None else y
+    _need(y, "y", (n, H), Y_perm.dtype, dev)
+    code = lib.moe_unpermute_combine(
+        _ptr(Y_perm), _ptr(inv), _ptr(topk_w), n, H, K, _dt(Y_perm), _ptr(y), _stream(dev, stream)
+    )
+    _check(code, "moe_unpermute_combine")
+    return y
+
+
+def moe_forward_workspace_size(n, H, I, E, K, dtype) -> int:  # noqa: E741
+    return int(load_library().moe_forward_workspace_size(n, H, I, E, K, _dt(torch.empty(0, dtype=dtype))))
+
+
+def moe_forward(x, W_gate, W13, W2, K: int, renorm: bool, bias=None, y=None, ws=None, routing_out=False, stream=None):
+    """Whole layer. Returns y, or (y, logits, topk_ids, topk_w, counts) with routing_out."""
+    lib = load_library()
+    n, H = x.shape
+    E = W_gate.shape[1]
+    I = W13.shape[2] // 2  # noqa: E741
+    dev = x.device
+    _need(x, "x", (n, H))
+    _need(W_gate, "W_gate", (H, E), x.dtype, dev)
+    _need(W13, "W13", (E, H, 2 * I), x.dtype, dev)
+    _need(W2, "W2", (E, I, H), x.dtype, dev)
+    if bias is not None:
+        _need(bias, "bias", (E,), torch.float32, dev)
+    y = _empty((n, H), x.dtype, dev) if y is None else y
+    _need(y, "y", (n, H), x.dtype, dev)
+    dt = _dt(x)
+    ws = _workspace(lib.moe_forward_workspace_size(n, H, I, E, K, dt), dev, ws)
+    extra = [None] * 4
+    if routing_out:
+        extra = [
+            _empty((n, E), torch.float32, dev),
+            _empty((n, K), torch.int32, dev),
+            _empty((n, K), torch.float32, dev),
+            _empty((E,), torch.int32, dev),
+        ]
+    code = lib.moe_forward(
+        _ptr(x), _ptr(W_gate), _ptr(bias), _ptr(W13), _ptr(W2), n, H, I, E, K, int(bool(renorm)), dt,
+        _ptr(y), *[_ptr(t) for t in extra], _ptr(ws), ws.numel(), _stream(dev, stream),
+    )
+    _check(code, "moe_forward")
+    return (y, *extra) if routing_out else y

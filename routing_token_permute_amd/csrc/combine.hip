@@ -1,0 +1,70 @@
+// Weighted top-K combine: y[i] = sum_{k=0..K-1} w[i,k] * Y_perm[inv[i*K+k]].
+//
+// Algorithm 2 steps 10-11 of "MoE 分布式推理基础（基于 vLLM）" §1.2 (each
+// expert output row, times its routing weight, added into its token's row),
+// written as a gather per token so that no two workgroups touch the same
+// output row: the `_unpermute` plus deterministic weighted scatter-add of
+// "0. goin" §2.2 and its top-K slot reduction (§2.3). The K rows are summed
+// in slot order with fp32 fused multiply-adds, so the result is bitwise
+// reproducible. HBM-bound: every expert row is read once, every token row
+// written once, in 16-byte vectors.
+#include "moe_internal.hpp"
+
+namespace moe {
+namespace {
+
+// One workgroup per token; each thread owns 16-byte column chunks.
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y, const int32_t* __restrict__ inv,
+                                                      const float* __restrict__ w, int n, int row_vecs, int K,
+                                                      void* __restrict__ y) {
+  constexpr int EPV = BF16 ? 8 : 4;  // elements per 16-byte vector
+  const int i = blockIdx.x;
+  const int total = n * K;
+  const u32x4_t* Yv = (const u32x4_t*)Y;
+  for (int c = threadIdx.x; c < row_vecs; c += 256) {
+    float acc[EPV];
+#pragma unroll
+    for (int q = 0; q < EPV; ++q) acc[q] = 0.f;
+    for (int k = 0; k < K; ++k) {
+      const int r = inv[(size_t)i * K + k];
+      if ((unsigned)r >= (unsigned)total) continue;
+      const float wk = (w != nullptr) ? w[(size_t)i * K + k] : 1.f;
+      const u32x4_t v = Yv[(size_t)r * row_vecs + c];
+      if constexpr (BF16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] = fmaf(wk, __uint_as_float(v[q] << 16), acc[2 * q]);
+          acc[2 * q + 1] = fmaf(wk, __uint_as_float(v[q] & 0xFFFF0000u), acc[2 * q + 1]);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] = fmaf(wk, __uint_as_float(v[q]), acc[q]);
+      }
+    }
+    u32x4_t out;
+    if constexpr (BF16) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        out[q] = (uint32_t)f32_to_bf16(acc[2 * q]) | ((uint32_t)f32_to_bf16(acc[2 * q + 1]) << 16);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) out[q] = __float_as_uint(acc[q]);
+    }
+    ((u32x4_t*)y)[(size_t)i * row_vecs + c] = out;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void* Y_perm, const int32_t* inv, const float* topk_w, int n, int H, int K,
+                          moe_dtype dt, void* y, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (dt == MOE_BF16)
+    combine_kernel<true><<<n, 256, 0, s>>>(Y_perm, inv, topk_w, n, H / 8, K, y);
+  else
+    combine_kernel<false><<<n, 256, 0, s>>>(Y_perm, inv, topk_w, n, H / 4, K, y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

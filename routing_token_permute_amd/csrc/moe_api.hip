@@ -1,0 +1,202 @@
+// C ABI of the MoE expert-layer forward: argument checks, workspace layout and
+// the order in which the kernels are enqueued. Everything numeric runs in the
+// kernels of route.hip, permute.hip, grouped_gemm.hip and combine.hip.
+#include <stdint.h>
+
+#include "moe_internal.hpp"
+
+namespace {
+
+using namespace moe;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+size_t elt_size(moe_dtype dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+bool dtype_ok(moe_dtype dt) { return dt == MOE_BF16 || dt == MOE_F32; }
+
+// Shape rules the kernels rely on: bf16 GEMMs and the router advance K in
+// steps of 64; every row copy moves 16-byte vectors.
+bool hidden_ok(int H, moe_dtype dt) { return H > 0 && (dt == MOE_BF16 ? H % 64 == 0 : H % 4 == 0); }
+
+bool experts_ok(int E, int K) { return E >= 1 && E <= kMaxExperts && K >= 1 && K <= E && K <= kMaxTopK; }
+
+moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+size_t permute_ws(int n, int E, int K) {
+  const long long total = (long long)n * K;
+  const long long nblk = (total + kPermChunk - 1) / kPermChunk;
+  return align_up((size_t)(nblk > 0 ? nblk : 1) * E * sizeof(int32_t));
+}
+
+// moe_forward workspace, in order.
+struct ForwardLayout {
+  size_t logits, ids, w, counts, offsets, splits, perm, inv, pscratch, x_perm, h, Y_perm, total;
+};
+
+ForwardLayout forward_layout(int n, int H, int I, int E, int K, moe_dtype dt) {
+  ForwardLayout L{};
+  const size_t nk = (size_t)n * K;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes > 0 ? bytes : 1);
+    return at;
+  };
+  L.logits = take((size_t)n * E * 4);
+  L.ids = take(nk * 4);
+  L.w = take(nk * 4);
+  L.counts = take((size_t)E * 4);
+  L.offsets = take((size_t)(E + 1) * 4);
+  L.splits = take(4);
+  L.perm = take(nk * 4);
+  L.inv = take(nk * 4);
+  L.pscratch = take(permute_ws(n, E, K));
+  L.x_perm = take(nk * H * elt_size(dt));
+  L.h = take(nk * I * elt_size(dt));
+  L.Y_perm = take(nk * H * elt_size(dt));
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK:
+      return "MOE_OK: success";
+    case MOE_EINVAL:
+      return "MOE_EINVAL: invalid argument (null pointer, size or shape outside the supported range)";
+    case MOE_EUNSUPPORTED:
+      return "MOE_EUNSUPPORTED: dtype not built";
+    case MOE_EWORKSPACE:
+      return "MOE_EWORKSPACE: workspace missing or smaller than required";
+    case MOE_EHIP:
+      return "MOE_EHIP: a HIP kernel launch failed";
+  }
+  return "unknown moe_status";
+}
+
+int moe_version(void) { return 100; }
+
+moe_status moe_route(const void* x, const void* W_gate, const float* bias, int n, int H, int E, int K, int renorm,
+                     moe_dtype dt, float* logits, int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+  if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
+  if (n < 0 || !experts_ok(E, K)) return MOE_EINVAL;
+  if (n == 0) return MOE_OK;
+  if (logits == nullptr || topk_ids == nullptr || topk_w == nullptr) return MOE_EINVAL;
+  if (x != nullptr && (W_gate == nullptr || !hidden_ok(H, dt))) return MOE_EINVAL;
+  return from_hip(launch_route(x, W_gate, bias, n, H, E, K, renorm, dt, logits, topk_ids, topk_w, stream));
+}
+
+size_t moe_permute_workspace_size(int n, int E, int K) {
+  if (n < 0 || E < 1 || K < 1) return 0;
+  return permute_ws(n, E, K);
+}
+
+moe_status moe_permute(const int32_t* topk_ids, const void* x, int n, int H, int E, int K, int ep, moe_dtype dt,
+                       int32_t* counts, int32_t* offsets, int32_t* splits, int32_t* perm, int32_t* inv,
+                       void* x_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
+  if (n < 0 || !experts_ok(E, K) || ep < 1 || E % ep != 0) return MOE_EINVAL;
+  if ((long long)n * K > INT32_MAX) return MOE_EINVAL;
+  if (counts == nullptr || offsets == nullptr || splits == nullptr) return MOE_EINVAL;
+  if (n > 0 && (topk_ids == nullptr || perm == nullptr || inv == nullptr)) return MOE_EINVAL;
+  if (x != nullptr && (x_perm == nullptr || !hidden_ok(H, dt))) return MOE_EINVAL;
+  if (ws == nullptr || ws_bytes < permute_ws(n, E, K)) return MOE_EWORKSPACE;
+  return from_hip(launch_permute(topk_ids, x, n, H, E, K, ep, dt, counts, offsets, splits, perm, inv, x_perm,
+                                 (int32_t*)ws, stream));
+}
+
+size_t moe_grouped_swiglu_workspace_size(int rows, int I, moe_dtype dt) {
+  if (rows < 0 || I < 1 || !dtype_ok(dt)) return 0;
+  return align_up((size_t)rows * I * elt_size(dt));
+}
+
+moe_status moe_grouped_swiglu(const void* x_perm, const int32_t* offsets, int rows, const void* W13, const void* W2,
+                              int E, int H, int I, moe_dtype dt, void* Y_perm, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
+  if (rows < 0 || E < 1 || E > kMaxExperts || !hidden_ok(H, dt) || !hidden_ok(I, dt)) return MOE_EINVAL;
+  if (rows == 0) return MOE_OK;
+  if (x_perm == nullptr || offsets == nullptr || W13 == nullptr || W2 == nullptr || Y_perm == nullptr)
+    return MOE_EINVAL;
+  if (ws == nullptr || ws_bytes < (size_t)rows * I * elt_size(dt)) return MOE_EWORKSPACE;
+  return from_hip(launch_grouped_swiglu(x_perm, offsets, rows, W13, W2, E, H, I, dt, Y_perm, ws, stream));
+}
+
+static moe_status check_expert_gemm(const void* a, const int32_t* offsets, int rows, const void* w, int E, int H,
+                                    int I, moe_dtype dt, const void* out) {
+  if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
+  if (rows < 0 || E < 1 || E > kMaxExperts || !hidden_ok(H, dt) || !hidden_ok(I, dt)) return MOE_EINVAL;
+  if (rows > 0 && (a == nullptr || offsets == nullptr || w == nullptr || out == nullptr)) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+moe_status moe_expert_w13_swiglu(const void* x_perm, const int32_t* offsets, int rows, const void* W13, int E, int H,
+                                 int I, moe_dtype dt, void* h, hipStream_t stream) {
+  const moe_status st = check_expert_gemm(x_perm, offsets, rows, W13, E, H, I, dt, h);
+  if (st != MOE_OK) return st;
+  return from_hip(launch_w13_swiglu(x_perm, offsets, rows, W13, E, H, I, dt, h, stream));
+}
+
+moe_status moe_expert_w2(const void* h, const int32_t* offsets, int rows, const void* W2, int E, int H, int I,
+                         moe_dtype dt, void* Y_perm, hipStream_t stream) {
+  const moe_status st = check_expert_gemm(h, offsets, rows, W2, E, H, I, dt, Y_perm);
+  if (st != MOE_OK) return st;
+  return from_hip(launch_w2(h, offsets, rows, W2, E, H, I, dt, Y_perm, stream));
+}
+
+moe_status moe_unpermute_combine(const void* Y_perm, const int32_t* inv, const float* topk_w, int n, int H, int K,
+                                 moe_dtype dt, void* y, hipStream_t stream) {
+  if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
+  if (n < 0 || K < 1 || K > kMaxTopK || !hidden_ok(H, dt)) return MOE_EINVAL;
+  if ((long long)n * K > INT32_MAX) return MOE_EINVAL;
+  if (n == 0) return MOE_OK;
+  if (Y_perm == nullptr || inv == nullptr || y == nullptr) return MOE_EINVAL;
+  return from_hip(launch_combine(Y_perm, inv, topk_w, n, H, K, dt, y, stream));
+}
+
+size_t moe_forward_workspace_size(int n, int H, int I, int E, int K, moe_dtype dt) {
+  if (n < 0 || H < 1 || I < 1 || E < 1 || K < 1 || !dtype_ok(dt)) return 0;
+  return forward_layout(n, H, I, E, K, dt).total;
+}
+
+moe_status moe_forward(const void* x, const void* W_gate, const float* bias, const void* W13, const void* W2, int n,
+                       int H, int I, int E, int K, int renorm, moe_dtype dt, void* y, float* logits_out,
+                       int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
+  if (n < 0 || !experts_ok(E, K) || !hidden_ok(H, dt) || !hidden_ok(I, dt)) return MOE_EINVAL;
+  if ((long long)n * K > INT32_MAX) return MOE_EINVAL;
+  if (n > 0 && (x == nullptr || W_gate == nullptr || W13 == nullptr || W2 == nullptr || y == nullptr))
+    return MOE_EINVAL;
+  const ForwardLayout L = forward_layout(n, H, I, E, K, dt);
+  if (ws == nullptr || ws_bytes < L.total) return MOE_EWORKSPACE;
+  char* base = (char*)ws;
+  float* logits = logits_out ? logits_out : (float*)(base + L.logits);
+  int32_t* ids = topk_ids_out ? topk_ids_out : (int32_t*)(base + L.ids);
+  float* w = topk_w_out ? topk_w_out : (float*)(base + L.w);
+  int32_t* counts = counts_out ? counts_out : (int32_t*)(base + L.counts);
+  int32_t* offsets = (int32_t*)(base + L.offsets);
+  int32_t* splits = (int32_t*)(base + L.splits);
+  int32_t* perm = (int32_t*)(base + L.perm);
+  int32_t* inv = (int32_t*)(base + L.inv);
+
+  hipError_t e = launch_route(x, W_gate, bias, n, H, E, K, renorm, dt, logits, ids, w, stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  e = launch_permute(ids, x, n, H, E, K, 1, dt, counts, offsets, splits, perm, inv, base + L.x_perm,
+                     (int32_t*)(base + L.pscratch), stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  if (n == 0) return MOE_OK;
+  e = launch_grouped_swiglu(base + L.x_perm, offsets, n * K, W13, W2, E, H, I, dt, base + L.Y_perm, base + L.h,
+                            stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  return from_hip(launch_combine(base + L.Y_perm, inv, w, n, H, K, dt, y, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,100 @@
+// Internal declarations shared by the HIP kernels and the C-ABI layer.
+// Target: gfx950 (CDNA4), wave64.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// Largest expert count the kernels accept (LDS histograms and the router's
+// accumulators are sized for it) and the largest top-K (one lane per slot).
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 64;
+
+// moe_permute: pairs per counting block (256 threads x 8 pairs).
+constexpr int kPermThreads = 256;
+constexpr int kPermChunk = 2048;
+
+// bf16 grouped GEMM tile.
+constexpr int kGemmBM = 128;
+constexpr int kGemmBN = 128;
+constexpr int kGemmBK = 64;
+
+inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// Number of BM-row tiles covering any split of `rows` rows into E segments:
+// sum_e ceil(c_e / BM) <= (rows + min(E, rows) * (BM - 1)) / BM.
+inline int max_row_tiles(int rows, int E, int BM) {
+  long long nonempty = rows < E ? rows : E;
+  return (int)(((long long)rows + nonempty * (BM - 1)) / BM);
+}
+
+// ---- host launchers (each returns hipGetLastError() after its launches) ----
+
+hipError_t launch_route(const void* x, const void* W_gate, const float* bias, int n, int H, int E, int K,
+                        int renorm, moe_dtype dt, float* logits, int32_t* topk_ids, float* topk_w,
+                        hipStream_t s);
+
+// block_counts: workspace of ceil(n*K / kPermChunk) * E int32.
+hipError_t launch_permute(const int32_t* topk_ids, const void* x, int n, int H, int E, int K, int ep,
+                          moe_dtype dt, int32_t* counts, int32_t* offsets, int32_t* splits, int32_t* perm,
+                          int32_t* inv, void* x_perm, int32_t* block_counts, hipStream_t s);
+
+// h: workspace of rows * I elements of dt.
+hipError_t launch_grouped_swiglu(const void* x_perm, const int32_t* offsets, int rows, const void* W13,
+                                 const void* W2, int E, int H, int I, moe_dtype dt, void* Y_perm, void* h,
+                                 hipStream_t s);
+
+// The two GEMMs separately (launch_grouped_swiglu runs both).
+hipError_t launch_w13_swiglu(const void* x_perm, const int32_t* offsets, int rows, const void* W13, int E, int H,
+                             int I, moe_dtype dt, void* h, hipStream_t s);
+hipError_t launch_w2(const void* h, const int32_t* offsets, int rows, const void* W2, int E, int H, int I,
+                     moe_dtype dt, void* Y_perm, hipStream_t s);
+
+hipError_t launch_combine(const void* Y_perm, const int32_t* inv, const float* topk_w, int n, int H, int K,
+                          moe_dtype dt, void* y, hipStream_t s);
+
+}  // namespace moe
+
+// ---- device helpers ----
+#if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float -> bf16, round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+
+// LDS transpose read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lanes 4r..4r+3 together supply row r (16 consecutive 16-bit elements, 4
+// per lane); lane c of the group receives column c of those 4 rows.
+__device__ __forceinline__ bf16x4_t lds_read_tr16(const lds_char_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)p);
+}
+
+__device__ __forceinline__ u32x4_t lds_read_b128(const lds_char_t* p) {
+  return *(const __attribute__((address_space(3))) u32x4_t*)p;
+}
+
+__device__ __forceinline__ void lds_write_b128(lds_char_t* p, u32x4_t v) {
+  *(__attribute__((address_space(3))) u32x4_t*)p = v;
+}
+
+}  // namespace moe
+#endif

@@ -1,0 +1,344 @@
+"""Parity of every C-ABI call against the fp64 CPU oracle, on seeded inputs.
+
+Inputs follow the workload recipe (x ~ N(0, 1), weights ~ N(0, 0.02)) at
+every shape, so that outputs have the OLMoE layer's scale and the absolute
+error bound keeps its meaning next to the relative ones.
+
+Integer outputs (expert ids, counts, offsets, splits, perm, inv) and row
+copies must be bit-exact; floating-point outputs must stay within the
+layer's bounds (bf16: max-abs 2e-2 and relative Frobenius 1e-2; fp32: 1e-5
+for both; routing weights 1e-6; router logits relative Frobenius 1e-5). Sizes
+span several tiles with ragged tails, empty and hot experts, ties, and the
+full OLMoE-layer sizes the benchmark times.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import routing_token_permute_amd as moe
+from gpu_util import assert_close, dev_tensor, errors, layer_tensors, require_gpu, to_f64
+from oracle import moe_oracle as om
+from workloads import make_config, make_layer, random_bf16_matrix, zipf_bias
+from workloads.gen import make_ep_share
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def _ids_from_random_logits(n, E, K, seed, bias=None):
+    rng = np.random.default_rng(seed)
+    L = rng.standard_normal((n, E)).astype(np.float32)
+    if bias is not None:
+        L = L + bias
+    e_top, w_top, _ = oracle.route_from_logits(L, K, renorm=False)
+    return L, e_top, w_top
+
+
+def _tie_logits(n, E, seed):
+    rng = np.random.default_rng(seed)
+    L = rng.standard_normal((n, E)).astype(np.float32)
+    L[0::7] = 0.5  # all equal rows
+    L[1::7] = np.round(L[1::7] * 2) / 2  # coarse grid, many ties
+    h = E // 2
+    L[2::7, :h] = L[2::7, h : 2 * h]  # duplicated halves
+    L[3::7] = np.where(np.arange(E) % 2 == 0, np.float32(0.0), np.float32(-0.0))
+    L[4::7, ::3] = -np.inf
+    return L
+
+
+# ---------------------------------------------------------------------------
+# moe_route
+# ---------------------------------------------------------------------------
+
+ROUTE_CASES = [
+    # n, H, E, K, dtype, renorm, bias
+    (64, 128, 8, 2, "f32", True, None),
+    (300, 256, 64, 8, "bf16", False, None),
+    (4096, 2048, 64, 8, "bf16", False, None),
+    (4096, 2048, 64, 8, "bf16", False, "zipf"),
+    (37, 128, 16, 16, "bf16", True, None),
+    (1, 64, 1, 1, "bf16", False, None),
+    (130, 192, 100, 7, "bf16", True, None),
+    (50, 64, 256, 64, "bf16", False, None),
+    (33, 68, 5, 3, "f32", False, None),
+]
+
+
+@pytest.mark.parametrize("n,H,E,K,dtype,renorm,bias", ROUTE_CASES)
+def test_route(dev, n, H, E, K, dtype, renorm, bias):
+    b = zipf_bias(E) if bias == "zipf" else None
+    w = make_layer(n, H, 64, E, K, dtype=dtype, renorm=renorm, seed=n + E, bias=b)
+    t = layer_tensors(w, dev)
+    logits, ids, wts = moe.moe_route(t["x"], t["W_gate"], t["bias"], K, renorm)
+    torch.cuda.synchronize()
+    ref = oracle.router_logits(w.x_f32, w.W_gate_f32, w.bias)
+    got = logits.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(ref)
+    assert (np.isfinite(got) == fin).all() and (got[~fin] == ref[~fin]).all()
+    ma, rf = errors(got[fin], ref[fin])
+    print(f"[route logits n={n} E={E}] max_abs={ma:.2e} rel_frob={rf:.2e}", flush=True)
+    assert rf <= 1e-5 and ma <= 1e-4
+    # ids: the oracle routes from its own logits; rows whose top-K boundary is
+    # a near-tie (margin below the logit error bound) may legitimately differ.
+    L32 = oracle.round_to_f32(ref)
+    e_ref, w_ref, _ = oracle.route_from_logits(L32, K, renorm)
+    margin = oracle.topk_margin(L32, K)
+    safe = ~(margin <= 1e-4)
+    ids_h = ids.cpu().numpy()
+    assert (ids_h[safe] == e_ref[safe]).all()
+    assert safe.mean() > 0.5
+    for i in np.flatnonzero(~safe):  # near-ties: the chosen set must still be a top-K
+        kth = np.sort(ref[i])[::-1][K - 1]
+        assert (ref[i, ids_h[i]] >= kth - 2e-4).all()
+    np.testing.assert_allclose(wts.cpu().numpy()[safe], w_ref[safe], atol=1e-6, rtol=0)
+
+
+@pytest.mark.parametrize("n,E,K,renorm", [(200, 64, 8, False), (200, 64, 8, True), (90, 256, 64, True), (40, 5, 5, False), (70, 130, 9, False), (7, 1, 1, True)])
+def test_topk_from_logits_bit_exact(dev, n, E, K, renorm):
+    L = _tie_logits(n, E, seed=E + K)
+    logits = torch.from_numpy(L).to(dev)
+    _, ids, wts = moe.moe_route(None, None, None, K, renorm, logits=logits)
+    torch.cuda.synchronize()
+    e_ref, w_ref, _ = oracle.route_from_logits(L, K, renorm)
+    assert (ids.cpu().numpy() == e_ref).all()
+    np.testing.assert_allclose(wts.cpu().numpy(), w_ref, atol=1e-6, rtol=0)
+
+
+# ---------------------------------------------------------------------------
+# moe_permute
+# ---------------------------------------------------------------------------
+
+PERMUTE_CASES = [
+    # n, H, E, K, ep, ids
+    (300, 128, 8, 2, 4, "routed"),
+    (4096, 2048, 64, 8, 8, "routed"),
+    (4096, 2048, 64, 8, 8, "skewed"),
+    (256, 64, 64, 8, 1, "routed"),  # n*K = 2048: exactly one counting block
+    (1, 64, 8, 8, 2, "routed"),
+    (513, 192, 16, 4, 16, "random"),  # repeated experts within a row
+    (777, 64, 8, 1, 1, "one_hot"),  # every pair to one expert
+    (3001, 64, 256, 6, 32, "random"),
+    (64, 132, 8, 2, 1, "routed_f32"),
+]
+
+
+@pytest.mark.parametrize("n,H,E,K,ep,kind", PERMUTE_CASES)
+def test_permute(dev, n, H, E, K, ep, kind):
+    rng = np.random.default_rng(n * 7 + E)
+    if kind == "routed" or kind == "routed_f32":
+        _, e_top, _ = _ids_from_random_logits(n, E, K, seed=n)
+    elif kind == "skewed":
+        _, e_top, _ = _ids_from_random_logits(n, E, K, seed=n, bias=zipf_bias(E))
+    elif kind == "random":
+        e_top = rng.integers(0, E, size=(n, K)).astype(np.int32)
+    else:
+        e_top = np.full((n, K), 3, dtype=np.int32)
+    dtype = "f32" if kind == "routed_f32" else "bf16"
+    if dtype == "bf16":
+        xb, xf = random_bf16_matrix(rng, (n, H))
+    else:
+        xf = rng.standard_normal((n, H)).astype(np.float32)
+        xb = xf
+    x = dev_tensor(xb, dtype, dev)
+    out = moe.moe_permute(torch.from_numpy(e_top).to(dev), x, E, ep=ep)
+    torch.cuda.synchronize()
+    counts = oracle.expert_counts(e_top, E)
+    offsets = oracle.offsets_from_counts(counts)
+    perm, inv = oracle.permutation(e_top, E)
+    assert (out["counts"].cpu().numpy() == counts).all()
+    assert (out["offsets"].cpu().numpy() == offsets).all()
+    assert (out["splits"].cpu().numpy() == om.splits_by_rank(e_top, E, ep)).all()
+    assert (out["perm"].cpu().numpy() == perm).all()
+    assert (out["inv"].cpu().numpy() == inv).all()
+    xp = out["x_perm"].cpu()
+    xp = xp.view(torch.int16).numpy() if dtype == "bf16" else xp.numpy()
+    ref = np.asarray(xb)[perm // K]
+    assert (xp.view(ref.dtype) == ref).all()
+
+
+def test_permute_empty_and_metadata_only(dev):
+    E, K = 8, 2
+    ids = torch.zeros((0, K), dtype=torch.int32, device=dev)
+    out = moe.moe_permute(ids, None, E, ep=2)
+    torch.cuda.synchronize()
+    assert (out["counts"].cpu() == 0).all() and (out["offsets"].cpu() == 0).all() and (out["splits"].cpu() == 0).all()
+    _, e_top, _ = _ids_from_random_logits(100, E, K, seed=1)
+    out = moe.moe_permute(torch.from_numpy(e_top).to(dev), None, E)
+    torch.cuda.synchronize()
+    perm, _ = oracle.permutation(e_top, E)
+    assert (out["perm"].cpu().numpy() == perm).all()
+
+
+# ---------------------------------------------------------------------------
+# moe_grouped_swiglu
+# ---------------------------------------------------------------------------
+
+
+def _segments(kind, rows, E, rng):
+    if kind == "random":
+        cuts = np.sort(rng.integers(0, rows + 1, size=E - 1))
+        counts = np.diff(np.concatenate([[0], cuts, [rows]]))
+    elif kind == "edge":  # empty, single-row, tile+1, and the rest
+        counts = np.zeros(E, dtype=np.int64)
+        counts[1] = 1
+        counts[2] = 129
+        counts[3] = rows - 130
+    elif kind == "hot":  # one expert takes everything, in the middle
+        counts = np.zeros(E, dtype=np.int64)
+        counts[E // 2] = rows
+    else:
+        raise ValueError(kind)
+    return counts.astype(np.int64)
+
+
+GROUPED_CASES = [
+    # rows, E, H, I, dtype, kind
+    (300, 8, 128, 64, "bf16", "random"),
+    (1000, 4, 256, 128, "bf16", "edge"),
+    (777, 6, 192, 192, "bf16", "hot"),  # H % 128 == 64: masked output columns
+    (2500, 16, 512, 256, "bf16", "random"),
+    (130, 5, 64, 64, "f32", "edge"),
+    (300, 8, 128, 64, "f32", "random"),
+]
+
+
+@pytest.mark.parametrize("rows,E,H,I,dtype,kind", GROUPED_CASES)
+def test_grouped_swiglu(dev, rows, E, H, I, dtype, kind):  # noqa: E741
+    rng = np.random.default_rng(rows + H)
+    counts = _segments(kind, rows, E, rng)
+    offsets = oracle.offsets_from_counts(counts)
+    w = make_layer(1, H, I, E, 1, dtype=dtype, seed=rows)
+    if dtype == "bf16":
+        xb, xf = random_bf16_matrix(rng, (rows, H))
+    else:
+        xf = rng.standard_normal((rows, H)).astype(np.float32)
+        xb = xf
+    t = layer_tensors(w, dev)
+    Y = moe.moe_grouped_swiglu(dev_tensor(xb, dtype, dev), torch.from_numpy(offsets.astype(np.int32)).to(dev), t["W13"], t["W2"])
+    torch.cuda.synchronize()
+    ref = om.grouped_swiglu(xf, offsets, w.W13_f32, w.W2_f32)
+    assert_close(to_f64(Y), ref, dtype, f"grouped rows={rows} E={E} {kind}")
+
+
+def test_grouped_swiglu_leaves_rows_past_offsets(dev):
+    rows, E, H, I = 200, 4, 64, 64  # noqa: E741
+    counts = np.array([50, 0, 70, 30])  # offsets[E] = 150 < rows
+    offsets = oracle.offsets_from_counts(counts)
+    w = make_layer(1, H, I, E, 1, seed=3)
+    rng = np.random.default_rng(0)
+    xb, xf = random_bf16_matrix(rng, (rows, H))
+    t = layer_tensors(w, dev)
+    Y = torch.full((rows, H), 7.0, dtype=torch.bfloat16, device=dev)
+    moe.moe_grouped_swiglu(dev_tensor(xb, "bf16", dev), torch.from_numpy(offsets.astype(np.int32)).to(dev), t["W13"], t["W2"], Y_perm=Y)
+    torch.cuda.synchronize()
+    assert (Y[150:].float().cpu() == 7.0).all()
+    ref = om.grouped_swiglu(xf[:150], offsets, w.W13_f32, w.W2_f32)
+    assert_close(to_f64(Y[:150]), ref, "bf16", "grouped partial")
+
+
+# ---------------------------------------------------------------------------
+# moe_unpermute_combine
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("n,H,E,K,dtype,weighted", [(300, 128, 8, 2, "bf16", True), (4096, 2048, 64, 8, "bf16", True), (129, 64, 4, 1, "bf16", False), (64, 132, 8, 2, "f32", True), (50, 256, 16, 16, "bf16", True)])
+def test_combine(dev, n, H, E, K, dtype, weighted):
+    _, e_top, w_top = _ids_from_random_logits(n, E, K, seed=n + K)
+    perm, inv = oracle.permutation(e_top, E)
+    rng = np.random.default_rng(5)
+    if dtype == "bf16":
+        yb, yf = random_bf16_matrix(rng, (n * K, H))
+    else:
+        yf = rng.standard_normal((n * K, H)).astype(np.float32)
+        yb = yf
+    w32 = w_top.astype(np.float32)
+    wt = torch.from_numpy(w32).to(dev) if weighted else None
+    y = moe.moe_unpermute_combine(dev_tensor(yb, dtype, dev), torch.from_numpy(inv.astype(np.int32)).to(dev), wt, n, K)
+    torch.cuda.synchronize()
+    ref = oracle.combine_slot_order(yf, inv, w32 if weighted else None, n, K)
+    assert_close(to_f64(y), ref, dtype, f"combine n={n} K={K}")
+    if not weighted and K == 1 and dtype == "bf16":  # a plain un-permute is an exact copy
+        assert (y.cpu().view(torch.int16).numpy().view(np.uint16) == yb[inv]).all()
+
+
+# ---------------------------------------------------------------------------
+# moe_forward (whole layer)
+# ---------------------------------------------------------------------------
+
+
+def _forward_parity(dev, w, what):
+    t = layer_tensors(w, dev)
+    y, logits, ids, wts, counts = moe.moe_forward(t["x"], t["W_gate"], t["W13"], t["W2"], w.K, w.renorm, bias=t["bias"], routing_out=True)
+    torch.cuda.synchronize()
+    ref = oracle.forward(w.x_f32, w.W_gate_f32, w.W13_f32, w.W2_f32, w.K, w.renorm, bias=w.bias)
+    margin = oracle.topk_margin(ref["logits_f32"], w.K)
+    thr = 1e-4 if w.dtype == "bf16" else 1e-5
+    safe = ~(margin <= thr)
+    ids_h = ids.cpu().numpy()
+    print(f"[{what}] near-tie rows: {int((~safe).sum())} of {w.n}", flush=True)
+    assert (ids_h[safe] == ref["e_top"][safe]).all()
+    assert safe.mean() > 0.5
+    if safe.all():
+        assert (counts.cpu().numpy() == ref["counts"]).all()
+    np.testing.assert_allclose(wts.cpu().numpy()[safe], ref["w_top"][safe], atol=1e-6, rtol=0)
+    assert_close(to_f64(y)[safe], ref["y"][safe], w.dtype, what)
+    return y
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "decode_bf16", "olmoe_bf16", "olmoe_skewed_bf16"])
+def test_forward_configs(dev, name):
+    w = make_config(name)
+    y = _forward_parity(dev, w, name)
+    # Deterministic: a second call gives the same bits.
+    t = layer_tensors(w, dev)
+    y2 = moe.moe_forward(t["x"], t["W_gate"], t["W13"], t["W2"], w.K, w.renorm, bias=t["bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16) if y.dtype == torch.bfloat16 else y, y2.view(torch.int16) if y2.dtype == torch.bfloat16 else y2)
+
+
+@pytest.mark.parametrize("n,H,I,E,K,dtype,renorm", [(1, 64, 64, 8, 2, "bf16", False), (257, 128, 64, 1, 1, "bf16", False), (300, 128, 128, 8, 8, "bf16", True), (100, 64, 64, 16, 1, "f32", False), (45, 256, 192, 32, 4, "bf16", True)])
+def test_forward_small_shapes(dev, n, H, I, E, K, dtype, renorm):  # noqa: E741
+    w = make_layer(n, H, I, E, K, dtype=dtype, renorm=renorm, seed=n + H + I)
+    _forward_parity(dev, w, f"forward n={n} E={E} K={K}")
+
+
+def test_forward_zero_tokens(dev):
+    w = make_layer(4, 64, 64, 8, 2, seed=0)
+    t = layer_tensors(w, dev)
+    x0 = t["x"][:0]
+    y, logits, ids, wts, counts = moe.moe_forward(x0, t["W_gate"], t["W13"], t["W2"], 2, False, routing_out=True)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 64) and (counts.cpu() == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# One GPU's expert-parallel share (pre-received rows, K = 1, unit weights)
+# ---------------------------------------------------------------------------
+
+
+def _ep_share_run(dev, ep, mb, t13, t2, stream=None):
+    x = dev_tensor(mb.x_bits(), "bf16", dev)
+    eid = torch.from_numpy(mb.eid.reshape(-1, 1)).to(dev)
+    meta = moe.moe_permute(eid, x, ep.E_local, stream=stream)
+    Y = moe.moe_grouped_swiglu(meta["x_perm"], meta["offsets"], t13, t2, stream=stream)
+    out = moe.moe_unpermute_combine(Y, meta["inv"], None, ep.R, 1, stream=stream)
+    return meta, out
+
+
+def test_ep_share_full(dev):
+    ep = make_config("ep_share_bf16")
+    t13 = dev_tensor(ep.bits("W13"), "bf16", dev)
+    t2 = dev_tensor(ep.bits("W2"), "bf16", dev)
+    for mb in ep.micro_batches:
+        meta, out = _ep_share_run(dev, ep, mb, t13, t2)
+        torch.cuda.synchronize()
+        ref = om.ep_share_forward(mb.x_f32, mb.eid, ep.W13_f32, ep.W2_f32)
+        assert (meta["counts"].cpu().numpy() == mb.counts).all()
+        assert (meta["perm"].cpu().numpy() == ref["perm"]).all()
+        assert_close(to_f64(out), ref["out"], "bf16", f"ep share seed={mb.seed}")

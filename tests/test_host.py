@@ -1,0 +1,139 @@
+"""Host-side checks of the C-ABI library: it loads, exports every function
+include/moe.h declares, and rejects bad arguments before touching the GPU.
+No call here reaches a kernel launch."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import routing_token_permute_amd as moe
+from routing_token_permute_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+EINVAL, EUNSUP, EWS = 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from routing_token_permute_amd import build
+
+        build.build()
+    return moe.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for fn in ("moe_route", "moe_permute", "moe_grouped_swiglu", "moe_unpermute_combine", "moe_forward"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert names
+    for name in names:
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, f"binding lacks {name}"
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        s = moe.status_string(code)
+        assert s.startswith("MOE_")
+    assert "unknown" in moe.status_string(99)
+    assert lib.moe_version() >= 100
+
+
+def test_workspace_sizes(lib):
+    a = lib.moe_forward_workspace_size(4096, 2048, 1024, 64, 8, 1)
+    b = lib.moe_forward_workspace_size(32, 2048, 1024, 64, 8, 1)
+    assert a > b > 0
+    # x_perm + h + Y_perm dominate: nK * (2H + I) * 2 bytes
+    assert a >= 4096 * 8 * (2 * 2048 + 1024) * 2
+    assert lib.moe_permute_workspace_size(4096, 64, 8) >= 16 * 64 * 4
+    assert lib.moe_grouped_swiglu_workspace_size(32768, 1024, 1) >= 32768 * 1024 * 2
+    assert lib.moe_forward_workspace_size(-1, 2048, 1024, 64, 8, 1) == 0
+
+
+P = ctypes.c_void_p(16)  # a non-null dummy; validation rejects before it is used
+
+
+def test_route_rejects_bad_arguments(lib):
+    s = None
+    # K > E
+    assert lib.moe_route(P, P, None, 8, 64, 4, 5, 0, 1, P, P, P, s) == EINVAL
+    # E too large
+    assert lib.moe_route(P, P, None, 8, 64, 257, 2, 0, 1, P, P, P, s) == EINVAL
+    # bf16 hidden size not a multiple of 64
+    assert lib.moe_route(P, P, None, 8, 96, 8, 2, 0, 1, P, P, P, s) == EINVAL
+    # null outputs
+    assert lib.moe_route(P, P, None, 8, 64, 8, 2, 0, 1, None, P, P, s) == EINVAL
+    # unknown dtype
+    assert lib.moe_route(P, P, None, 8, 64, 8, 2, 0, 7, P, P, P, s) == EUNSUP
+    # negative n
+    assert lib.moe_route(P, P, None, -1, 64, 8, 2, 0, 1, P, P, P, s) == EINVAL
+
+
+def test_permute_rejects_bad_arguments(lib):
+    s = None
+    ws_ok = lib.moe_permute_workspace_size(100, 8, 2)
+    # ep does not divide E
+    assert lib.moe_permute(P, None, 100, 64, 8, 2, 3, 1, P, P, P, P, P, None, P, ws_ok, s) == EINVAL
+    # workspace too small
+    assert lib.moe_permute(P, None, 100, 64, 8, 2, 1, 1, P, P, P, P, P, None, P, 0, s) == EWS
+    # x given without x_perm
+    assert lib.moe_permute(P, P, 100, 64, 8, 2, 1, 1, P, P, P, P, P, None, P, ws_ok, s) == EINVAL
+    # null counts
+    assert lib.moe_permute(P, None, 100, 64, 8, 2, 1, 1, None, P, P, P, P, None, P, ws_ok, s) == EINVAL
+
+
+def test_grouped_and_combine_reject_bad_arguments(lib):
+    s = None
+    # I not a multiple of 64 for bf16
+    assert lib.moe_grouped_swiglu(P, P, 10, P, P, 4, 64, 48, 1, P, P, 1 << 20, s) == EINVAL
+    # workspace too small
+    assert lib.moe_grouped_swiglu(P, P, 10, P, P, 4, 64, 64, 1, P, P, 16, s) == EWS
+    # K too large
+    assert lib.moe_unpermute_combine(P, P, None, 10, 64, 65, 1, P, s) == EINVAL
+    # fp32 H not a multiple of 4
+    assert lib.moe_unpermute_combine(P, P, None, 10, 66, 2, 0, P, s) == EINVAL
+
+
+def test_forward_rejects_bad_arguments(lib):
+    s = None
+    ws = lib.moe_forward_workspace_size(16, 64, 64, 8, 2, 1)
+    args = [P, P, None, P, P, 16, 64, 64, 8, 2, 0, 1, P, None, None, None, None, P, ws, s]
+    bad = list(args)
+    bad[18] = ws - 1
+    assert lib.moe_forward(*bad) == EWS
+    bad = list(args)
+    bad[0] = None
+    assert lib.moe_forward(*bad) == EINVAL
+    bad = list(args)
+    bad[9] = 0  # K = 0
+    assert lib.moe_forward(*bad) == EINVAL
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(moe.MoEError):
+        _lib.load_library(str(tmp_path / "missing.so"))
+
+
+def test_oracle_is_not_imported_by_the_product():
+    pkg = os.path.join(ROOT, "routing_token_permute_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "oracle" not in text.replace("the oracle", ""), f
