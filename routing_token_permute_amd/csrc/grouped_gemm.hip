@@ -33,32 +33,73 @@
 namespace moe {
 namespace {
 
-constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
-constexpr int NTHR = 256;
-constexpr int A_BYTES = BM * BK * 2;      // 16 KB
-constexpr int B_BYTES = BK * BN * 2;      // 16 KB
-constexpr int STAGE = A_BYTES + B_BYTES;  // 32 KB
-constexpr int LDS_BYTES = 2 * STAGE;      // 64 KB
+constexpr int BN = kGemmBN, BK = kGemmBK;
+constexpr int B_BYTES = BK * BN * 2;      // 32 KB per stage
+constexpr int B_ROW = BN * 2;             // bytes per staged k-row of B
+static_assert(BN == 256 && BK == 64, "LDS layouts below assume 256-column, 64-deep stages");
 
-// A tile: BM rows x 64 k (128 B per row, 8 chunks of 16 B). Chunk c of row r
+// Stage geometry for a BM-row tile: A is BM x 64 (BM*128 bytes), B is 64 x 256.
+// BM = 128: three stages (144 KB); BM = 256: two stages (128 KB).
+template <int BM>
+struct TileCfg {
+  static constexpr int A_BYTES = BM * BK * 2;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int NSTAGE = (3 * STAGE <= 160 * 1024) ? 3 : 2;
+  static constexpr int EPI_BYTES = BM * 264 * 2;  // staged output tile (GEMM2 is the larger)
+  static constexpr int LDS_BYTES = (NSTAGE * STAGE > EPI_BYTES) ? NSTAGE * STAGE : EPI_BYTES;
+  static constexpr int REGIONS = STAGE / 1024;  // 1 KB DMA regions per stage
+};
+
+// Launch configuration of the bf16 path: BM-row tiles, WM x WN waves.
+#ifndef MOE_GEMM_BM
+#define MOE_GEMM_BM 256
+#define MOE_GEMM_WM 2
+#define MOE_GEMM_WN 4
+#endif
+constexpr int kBM = MOE_GEMM_BM, kGemmWM = MOE_GEMM_WM, kGemmWN = MOE_GEMM_WN;
+
+// A tile: 128 rows x 64 k (128 B per row = 8 chunks of 16 B). Chunk c of row r
 // sits at slot c ^ ((r / 2) % 8): 16 consecutive rows reading the same chunk
 // hit 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int a_off(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
-// B tile: 64 k-rows x 128 columns (256 B per row, 16 chunks). Chunk c of row
-// k sits at slot c ^ 2 * ((k % 4) + 4 * ((k / 8) % 2)): the 32 lanes of a
-// transpose read (8 k-rows x 4 eight-byte pieces) land on distinct banks.
-__device__ __forceinline__ int b_off(int k, int chunk) {
-  return k * 256 + ((chunk ^ (((k & 3) + ((k >> 3) & 1) * 4) << 1)) << 4);
+// B tile: 64 k-rows x 256 columns (512 B per row = 32 chunks). Chunk c of row
+// k sits at c ^ f(k), f(k) = 2 * ((k % 4) + 4 * ((k / 8) % 2)): the 32 lanes of
+// one transpose read (8 k-rows x 4 eight-byte pieces) land on 32 distinct
+// 8-byte bank pairs, and 16 lanes storing one row's chunks never collide.
+__device__ __forceinline__ int b_swz(int k) { return ((k & 3) + ((k >> 3) & 1) * 4) << 1; }
+__device__ __forceinline__ int b_off(int k, int chunk) { return k * B_ROW + ((chunk ^ b_swz(k)) << 4); }
+
+// Direct HBM -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
+// lane L's bytes land at LDS byte address lds_base + 16 * L, where lds_base is
+// wave-uniform (M0). Issued as inline assembly so that the compiler does not
+// treat every later LDS read as dependent on it; completion is awaited
+// explicitly with s_waitcnt vmcnt before the barrier that publishes a stage.
+// M0 is saved and restored around the copy because the compiler reserves it.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_base)
+      : "memory");
 }
 
 struct Tile {
-  int e, r0, r1;
+  int e, r0, r1, nb;
   bool valid;
 };
 
-// Row tile `mb` -> (expert, rows [r0, r1)). Every wave computes it alike.
-__device__ Tile find_tile(const int32_t* __restrict__ offsets, int E, int rows, int mb) {
+// Tiles are ordered expert by expert; within an expert, n-block-major, then
+// row tile. Tile t -> (expert, rows [r0, r1), n-block). Every wave computes
+// it alike from `offsets` with a wave-wide prefix sum of the per-expert tile
+// counts.
+template <int BM>
+__device__ Tile find_tile(const int32_t* __restrict__ offsets, int E, int rows, int NB, int t) {
   const int lane = lane_id();
   int carry = 0;
   for (int e0 = 0; e0 < E; e0 += 64) {
@@ -68,177 +109,250 @@ __device__ Tile find_tile(const int32_t* __restrict__ offsets, int E, int rows, 
       a = min(max(offsets[e], 0), rows);
       b = min(max(offsets[e + 1], a), rows);
     }
-    const int t = (b - a + BM - 1) / BM;
-    int incl = t;
+    const int mt = (b - a + BM - 1) / BM;
+    const int cnt = mt * NB;
+    int incl = cnt;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int o = __shfl_up(incl, off);
       if (lane >= off) incl += o;
     }
-    const int excl = incl - t;
-    const bool hit = (t > 0) && (mb >= carry + excl) && (mb < carry + incl);
+    const int excl = incl - cnt;
+    const bool hit = (cnt > 0) && (t >= carry + excl) && (t < carry + incl);
     const uint64_t bal = __ballot(hit);
     if (bal != 0) {
+      // An expert of n rows gets T = ceil(n / BM) row tiles of nearly equal
+      // height (the first n % T of them one row taller), so the last tile is
+      // never a sliver; waves skip the 16-row slices a tile does not fill.
       const int L = __ffsll((long long)bal) - 1;
-      const int ex = __shfl(excl, L), ah = __shfl(a, L), bh = __shfl(b, L);
-      const int r0 = ah + (mb - carry - ex) * BM;
-      return Tile{e0 + L, r0, min(r0 + BM, bh), true};
+      const int local = t - carry - __shfl(excl, L);
+      const int T = __shfl(mt, L);
+      const int ah = __shfl(a, L), n = __shfl(b, L) - ah;
+      const int m = local % T, q = n / T, rem = n % T;
+      const int r0 = ah + m * q + min(m, rem);
+      return Tile{e0 + L, r0, r0 + q + (m < rem ? 1 : 0), local / T, true};
     }
     carry += __shfl(incl, 63);
   }
-  return Tile{0, 0, 0, false};
+  return Tile{0, 0, 0, 0, false};
 }
 
-template <bool GATED>
-__global__ __launch_bounds__(NTHR, 2) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
-                                                           const int32_t* __restrict__ offsets, int E, int rows,
-                                                           int Kdim, const uint16_t* __restrict__ B, int ldb,
-                                                           long long b_expert_stride, int Nout, int up_col,
-                                                           uint16_t* __restrict__ C, int ldc, int n_tiles_n) {
-  __shared__ __attribute__((aligned(16))) char smem_raw[LDS_BYTES];
+// Workgroups are handed to the 8 XCDs round-robin (id % 8). Within each round
+// of 256 ids, give XCD x the contiguous tiles [32x, 32x + 32) so that the
+// workgroups sharing one expert's weight and activation tiles meet in one L2.
+__device__ __forceinline__ int xcd_remap(int bid, int G) {
+  constexpr int RS = 256;
+  const int full = (G / RS) * RS;
+  if (bid >= full) return bid;
+  const int w = bid % RS;
+  return (bid - w) + (w & 7) * (RS / 8) + (w >> 3);
+}
+
+// GATED (GEMM1): the 256 staged columns are 128 gate columns followed by the
+// matching 128 up columns; the tile writes 128 columns of h. Otherwise
+// (GEMM2): 256 output columns. WM x WN waves split the 128 x 256 tile; each
+// wave owns (128/WM) rows and (256/WN) staged columns (for GEMM1, half of
+// them gate and the matching half up).
+template <bool GATED, int BM, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
+                                                                    const int32_t* __restrict__ offsets, int E,
+                                                                    int rows, int Kdim,
+                                                                    const uint16_t* __restrict__ B, int ldb,
+                                                                    long long b_expert_stride, int Nout, int up_col,
+                                                                    uint16_t* __restrict__ C, int ldc, int NB) {
+  using Cfg = TileCfg<BM>;
+  constexpr int A_BYTES = Cfg::A_BYTES, STAGE = Cfg::STAGE, NSTAGE = Cfg::NSTAGE;
+  constexpr int NW = WM * WN;              // waves
+  constexpr int MT = BM / WM / 16;         // 16-row MFMA tiles per wave
+  constexpr int NT = BN / WN / 16;         // 16-column MFMA tiles per wave
+  constexpr int REG = Cfg::REGIONS / NW;   // 1 KB DMA regions per wave per stage
+  constexpr int DMA_PER_STAGE = REG;       // 16-byte loads per thread per stage
+  static_assert(NT % 2 == 0 && MT >= 1 && REG * NW == Cfg::REGIONS, "tile split");
+  __shared__ __attribute__((aligned(16))) char smem_raw[Cfg::LDS_BYTES];
   lds_char_t* smem = (lds_char_t*)smem_raw;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int mb = blockIdx.x / n_tiles_n, nb = blockIdx.x % n_tiles_n;
-  const Tile t = find_tile(offsets, E, rows, mb);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const Tile t = find_tile<BM>(offsets, E, rows, NB, xcd_remap(blockIdx.x, gridDim.x));
   if (!t.valid) return;
-  const int mrows = t.r1 - t.r0;
+  const int mrows = __builtin_amdgcn_readfirstlane(t.r1 - t.r0);
+  const int nb = t.nb;
 
-  // Global -> register assignment. A: 8 threads per 128-byte row slice.
-  const int ca = tid & 7, ra = tid >> 3;
-  const uint16_t* a_ptr[4];
-  bool a_ok[4];
+  // HBM -> LDS assignment. Each wave-wide DMA fills one 1 KB LDS region in
+  // lane order, so the swizzled LDS layout is produced by choosing which
+  // global chunk each lane fetches. Regions [0, BM/8) hold A (8 rows each),
+  // the next 32 regions hold B (2 k-rows each); wave w fills regions
+  // [w*REG, (w+1)*REG). Rows past the tile's last valid row and columns past
+  // Nout fetch a valid row/column instead: they only feed outputs that are
+  // never stored.
+  const uint32_t wave_u = wave;
+  constexpr int A_REG = A_BYTES / 1024;
+  const uint16_t* src[REG];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = ra + 32 * j;
-    a_ok[j] = r < mrows;
-    a_ptr[j] = A + (size_t)(t.r0 + (a_ok[j] ? r : 0)) * Kdim + ca * 8;
+  for (int j = 0; j < REG; ++j) {
+    const int r = wave * REG + j;
+    if (r < A_REG) {
+      const int row = 8 * r + (lane >> 3);
+      const int c = (lane & 7) ^ ((row >> 1) & 7);
+      src[j] = A + (size_t)(t.r0 + min(row, mrows - 1)) * Kdim + c * 8;
+    } else {
+      const int k = 2 * (r - A_BYTES / 1024) + (lane >> 5);
+      const int c = (lane & 31) ^ b_swz(k);
+      int col;
+      if constexpr (GATED) {
+        int gc = nb * 128 + (c & 15) * 8;
+        if (gc >= Nout) gc = 0;
+        col = (c < 16) ? gc : up_col + gc;
+      } else {
+        col = nb * 256 + c * 8;
+        if (col >= Nout) col = 0;
+      }
+      src[j] = B + (size_t)t.e * b_expert_stride + (size_t)k * ldb + col;
+    }
   }
-  // B: 16 threads per 256-byte k-row (gate half then up half for GEMM1).
-  const int cb = tid & 15, kb = tid >> 4;
-  int col;
-  if constexpr (GATED)
-    col = (cb < 8) ? (nb * 64 + cb * 8) : (up_col + nb * 64 + (cb - 8) * 8);
-  else
-    col = nb * 128 + cb * 8;
-  const bool b_ok = GATED ? true : (col < Nout);
-  const uint16_t* b_ptr = B + (size_t)t.e * b_expert_stride + (b_ok ? col : 0) + (size_t)kb * ldb;
-
-  u32x4_t ra_reg[4], rb_reg[4];
-  const u32x4_t zero4 = u32x4_t{0u, 0u, 0u, 0u};
-  auto gload = [&](int kt) {
-    const int k0 = kt * BK;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  auto issue = [&](int kt, int stage) {
+    const uint32_t base = lds0 + stage * STAGE + wave_u * REG * 1024;
+    const size_t ka = (size_t)kt * BK, kb = (size_t)kt * BK * ldb;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ra_reg[j] = a_ok[j] ? *(const u32x4_t*)(a_ptr[j] + k0) : zero4;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) rb_reg[j] = b_ok ? *(const u32x4_t*)(b_ptr + (size_t)(k0 + 16 * j) * ldb) : zero4;
-  };
-  auto sstore = [&](int buf) {
-    lds_char_t* As = smem + buf * STAGE;
-    lds_char_t* Bs = As + A_BYTES;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) lds_write_b128(As + a_off(ra + 32 * j, ca), ra_reg[j]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) lds_write_b128(Bs + b_off(kb + 16 * j, cb), rb_reg[j]);
+    for (int j = 0; j < REG; ++j) {
+      const int r = (int)(wave_u * REG + j);
+      // With a 2-stage ring every wait is vmcnt(0), so A regions wholly past
+      // the tile's rows need not be fetched (they are never read).
+      if (NSTAGE == 2 && r < A_REG && 8 * r >= mrows) continue;
+      dma16(src[j] + (r < A_REG ? ka : kb), base + j * 1024);
+    }
   };
 
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int g = lane >> 4, li = lane & 15, rr = li >> 2, cc = li & 3;
-  int a_rd[4][2];
+  // A operand (MFMA tile mt, k-step ks): row wm*(BM/WM) + mt*16 + li, chunk ks*4 + g.
+  const int a_sw = (li >> 1) & 7;
+  const int a_lane = (wm * (BM / WM) + li) * 128;
+  const int a_c0 = (g ^ a_sw) << 4, a_c1 = ((4 + g) ^ a_sw) << 4;
+  // B operand (MFMA tile nt, k-step ks, half h): k-row ks*32 + g*8 + h*4 + rr,
+  // columns col0(nt) + 4cc..+3; the swizzle depends on the lane only.
+  const int bsw = b_swz(g * 8 + rr);
+  const int b_lane = (g * 8 + rr) * B_ROW + cc * 8;
+  int b_col[NT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) a_rd[mt][ks] = a_off(wm * 64 + mt * 16 + li, ks * 4 + g);
-  int b_rd[4][2][2];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < NT; ++nt) {
     int col0;
     if constexpr (GATED)
-      col0 = (nt < 2) ? (wn * 32 + nt * 16) : (64 + wn * 32 + (nt - 2) * 16);
+      col0 = (nt < NT / 2) ? (wn * (BN / 2 / WN) + nt * 16) : (BN / 2 + wn * (BN / 2 / WN) + (nt - NT / 2) * 16);
     else
-      col0 = wn * 64 + nt * 16;
-    const int c = col0 + 4 * cc;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) b_rd[nt][ks][h] = b_off(ks * 32 + g * 8 + h * 4 + rr, c >> 3) + (c & 7) * 2;
+      col0 = wn * (BN / WN) + nt * 16;
+    b_col[nt] = b_lane + (((col0 >> 3) ^ bsw) << 4);
   }
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[MT][NT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = Kdim / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const lds_char_t* As = smem + buf * STAGE;
+  // 16-row MFMA slices of this wave that hold at least one valid row
+  // (wave-uniform); the rest are skipped.
+  const int vm = min(MT, max(0, (mrows - wm * (BM / WM) + 15) / 16));
+
+  // One 64-deep k-step from LDS stage `stage`, as two 32-deep halves. `full`
+  // is a constant at each call site: the branch-free body serves waves whose
+  // row slab is full, the guarded one the partly filled slab of a short tile.
+  auto compute_body = [&](int stage, bool full) {
+    const lds_char_t* As = smem + stage * STAGE;
     const lds_char_t* Bs = As + A_BYTES;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t a[4], b[4];
+      bf16x8_t a[MT], b[NT];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) a[mt] = __builtin_bit_cast(bf16x8_t, lds_read_b128(As + a_rd[mt][ks]));
+      for (int mt = 0; mt < MT; ++mt)
+        if (full || mt < vm)
+          a[mt] = __builtin_bit_cast(bf16x8_t, lds_read_b128(As + a_lane + mt * 16 * 128 + (ks ? a_c1 : a_c0)));
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const bf16x4_t lo = lds_read_tr16(Bs + b_rd[nt][ks][0]);
-        const bf16x4_t hi = lds_read_tr16(Bs + b_rd[nt][ks][1]);
+      for (int nt = 0; nt < NT; ++nt) {
+        const lds_char_t* p = Bs + b_col[nt] + ks * 32 * B_ROW;
+        const bf16x4_t lo = lds_read_tr16(p);
+        const bf16x4_t hi = lds_read_tr16(p + 4 * B_ROW);
         b[nt] = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
+        if (full || mt < vm) {
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
+          for (int nt = 0; nt < NT; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
+        }
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
-  }
+  };
+  // Pipeline over an NSTAGE-deep LDS ring: while k-step kt is multiplied,
+  // k-steps up to kt+NSTAGE-1 are in flight from HBM straight into LDS.
+  // Before the barrier that publishes stage kt, each wave waits until only
+  // its own loads of the later k-steps remain outstanding. The barrier also
+  // guarantees every wave has finished reading k-step kt-1, whose stage the
+  // next issue overwrites.
+  const int nk = Kdim / BK;
+  auto main_loop = [&](bool full) {
+#pragma unroll
+    for (int p = 0; p < NSTAGE - 1; ++p)
+      if (p < nk) issue(p, p);
+    int stage = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      if (NSTAGE == 3 && kt + 1 < nk)
+        asm volatile("s_waitcnt vmcnt(%0)" : : "n"(DMA_PER_STAGE) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+      __syncthreads();
+      const int nxt = kt + NSTAGE - 1;
+      if (nxt < nk) issue(nxt, stage == 0 ? NSTAGE - 1 : stage - 1);
+      if (full || vm > 0) compute_body(stage, full);
+      stage = (stage == NSTAGE - 1) ? 0 : stage + 1;
+    }
+  };
+  if (vm == MT)
+    main_loop(true);
+  else
+    main_loop(false);
+  __syncthreads();
 
   // Epilogue: lane (g, li) of MFMA tile (mt, nt) holds rows 4g..4g+3, column li.
+  // Stage the bf16 tile in LDS, then write 16-byte row pieces.
   uint16_t* Cs = (uint16_t*)smem_raw;
   if constexpr (GATED) {
-    constexpr int P = 72;  // bf16 per staged row (64 + 8 pad)
+    constexpr int P = 136;  // 128 h columns + 8 pad
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < NT / 2; ++nt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int row = wm * 64 + mt * 16 + 4 * g + j;
-          const int hc = wn * 32 + nt * 16 + li;
-          const float gv = acc[mt][nt][j], uv = acc[mt][nt + 2][j];
+          const int row = wm * (BM / WM) + mt * 16 + 4 * g + j;
+          const int hc = wn * (BN / 2 / WN) + nt * 16 + li;
+          const float gv = acc[mt][nt][j], uv = acc[mt][nt + NT / 2][j];
           const float hv = gv / (1.f + __expf(-gv)) * uv;
           Cs[row * P + hc] = f32_to_bf16(hv);
         }
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = (tid >> 3) + 32 * j, c = tid & 7;
-      if (row < mrows)
-        *(u32x4_t*)(C + (size_t)(t.r0 + row) * ldc + nb * 64 + c * 8) = *(const u32x4_t*)(Cs + row * P + c * 8);
+    for (int q = tid; q < BM * 16; q += 64 * NW) {
+      const int row = q >> 4, c = q & 15;
+      const int gc = nb * 128 + c * 8;
+      if (row < mrows && gc < Nout)
+        *(u32x4_t*)(C + (size_t)(t.r0 + row) * ldc + gc) = *(const u32x4_t*)(Cs + row * P + c * 8);
     }
   } else {
-    constexpr int P = 136;  // 128 + 8 pad
+    constexpr int P = 264;  // 256 + 8 pad
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int row = wm * 64 + mt * 16 + 4 * g + j;
-          const int c = wn * 64 + nt * 16 + li;
+          const int row = wm * (BM / WM) + mt * 16 + 4 * g + j;
+          const int c = wn * (BN / WN) + nt * 16 + li;
           Cs[row * P + c] = f32_to_bf16(acc[mt][nt][j]);
         }
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = (tid >> 4) + 16 * j, c = tid & 15;
-      const int gc = nb * 128 + c * 8;
+    for (int q = tid; q < BM * 32; q += 64 * NW) {
+      const int row = q >> 5, c = q & 31;
+      const int gc = nb * 256 + c * 8;
       if (row < mrows && gc < Nout)
         *(u32x4_t*)(C + (size_t)(t.r0 + row) * ldc + gc) = *(const u32x4_t*)(Cs + row * P + c * 8);
     }
@@ -286,9 +400,9 @@ hipError_t launch_w13_swiglu(const void* x_perm, const int32_t* offsets, int row
                              int I, moe_dtype dt, void* h, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   if (dt == MOE_BF16) {
-    const int mt = max_row_tiles(rows, E, BM);
-    const int n1 = I / 64;
-    gemm_bf16_kernel<true><<<mt * n1, NTHR, 0, s>>>((const uint16_t*)x_perm, offsets, E, rows, H,
+    const int mt = max_row_tiles(rows, E, kBM);
+    const int n1 = ceil_div(I, BN / 2);
+    gemm_bf16_kernel<true, kBM, kGemmWM, kGemmWN><<<mt * n1, 64 * kGemmWM * kGemmWN, 0, s>>>((const uint16_t*)x_perm, offsets, E, rows, H,
                                                     (const uint16_t*)W13, 2 * I, (long long)H * 2 * I, I, I,
                                                     (uint16_t*)h, I, n1);
   } else {
@@ -303,9 +417,9 @@ hipError_t launch_w2(const void* h, const int32_t* offsets, int rows, const void
                      moe_dtype dt, void* Y_perm, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   if (dt == MOE_BF16) {
-    const int mt = max_row_tiles(rows, E, BM);
+    const int mt = max_row_tiles(rows, E, kBM);
     const int n2 = ceil_div(H, BN);
-    gemm_bf16_kernel<false><<<mt * n2, NTHR, 0, s>>>((const uint16_t*)h, offsets, E, rows, I, (const uint16_t*)W2,
+    gemm_bf16_kernel<false, kBM, kGemmWM, kGemmWN><<<mt * n2, 64 * kGemmWM * kGemmWN, 0, s>>>((const uint16_t*)h, offsets, E, rows, I, (const uint16_t*)W2,
                                                      H, (long long)I * H, H, 0, (uint16_t*)Y_perm, H, n2);
   } else {
     dim3 g2(ceil_div(H, 64), ceil_div(rows, 4));

@@ -20,7 +20,7 @@ constexpr int kPermChunk = 2048;
 
 // bf16 grouped GEMM tile.
 constexpr int kGemmBM = 128;
-constexpr int kGemmBN = 128;
+constexpr int kGemmBN = 256;
 constexpr int kGemmBK = 64;
 
 inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
