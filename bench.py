@@ -100,9 +100,10 @@ def main():
     tokens_per_s = n / (ms_per_step * 1e-3)
 
     # ---- per-stage timing: each stage alone, on its own inputs ----
+    # The stages moe_forward enqueues, each timed alone on its own inputs.
     logits, ids, wts = moe.moe_route(x, Wg, bias, K, w.renorm)
-    meta = moe.moe_permute(ids, x, E)
-    h = moe.moe_expert_w13_swiglu(meta["x_perm"], meta["offsets"], W13)
+    meta = moe.moe_permute(ids, None, E)
+    h = moe.moe_expert_w13_swiglu_gather(x, meta["perm"], K, meta["offsets"], W13)
     Yp = moe.moe_expert_w2(h, meta["offsets"], W2)
     yc = moe.moe_unpermute_combine(Yp, meta["inv"], wts, n, K)
     torch.cuda.synchronize()
@@ -110,11 +111,14 @@ def main():
     R = args.stage_reps
     st = {
         "route": _time_region(lambda: moe.moe_route(x, Wg, bias, K, w.renorm, logits=logits, topk_ids=ids, topk_w=wts), R, torch),
-        "permute": _time_region(lambda: moe.moe_permute(ids, x, E, out=meta), R, torch),
-        "gemm1_swiglu": _time_region(lambda: moe.moe_expert_w13_swiglu(meta["x_perm"], meta["offsets"], W13, h=h), R, torch),
+        "permute": _time_region(lambda: moe.moe_permute(ids, None, E, out=meta), R, torch),
+        "gemm1_swiglu": _time_region(lambda: moe.moe_expert_w13_swiglu_gather(x, meta["perm"], K, meta["offsets"], W13, h=h), R, torch),
         "gemm2": _time_region(lambda: moe.moe_expert_w2(h, meta["offsets"], W2, Y_perm=Yp), R, torch),
         "combine": _time_region(lambda: moe.moe_unpermute_combine(Yp, meta["inv"], wts, n, K, y=yc), R, torch),
     }
+    # The standalone row gather of moe_permute (not part of moe_forward).
+    meta_x = moe.moe_permute(ids, x, E)
+    gather_ms = _time_region(lambda: moe.moe_permute(ids, x, E, out=meta_x), R, torch) - st["permute"]
     nk = n * K
     hit = int((counts > 0).sum())
     flops1 = 2.0 * nk * H * 2 * I
@@ -122,8 +126,8 @@ def main():
     # Algorithmic bytes per call (each input read once, each output written once).
     bytes_ = {
         "route": n * H * 2 + H * E * 2 + n * E * 4 + nk * 8,
-        "permute": nk * 4 + n * H * 2 + nk * H * 2 + nk * 8 + (2 * E + 2) * 4,
-        "gemm1_swiglu": nk * H * 2 + hit * H * 2 * I * 2 + nk * I * 2,
+        "permute": nk * 4 + nk * 8 + (2 * E + 2) * 4,
+        "gemm1_swiglu": nk * H * 2 + hit * H * 2 * I * 2 + nk * I * 2 + nk * 4,
         "gemm2": nk * I * 2 + hit * I * H * 2 + nk * H * 2,
         "combine": nk * H * 2 + nk * 8 + n * H * 2,
     }
@@ -136,6 +140,8 @@ def main():
         if k == "gemm2":
             s["TFLOP/s"] = round(flops2 / (ms * 1e-3) / 1e12, 1)
         stages[k] = s
+    stages["row_gather_standalone"] = {"ms": round(gather_ms, 5),
+                                       "GB/s": round((n * H * 2 + nk * H * 2) / (gather_ms * 1e-3) / 1e9, 1)}
     gg_ms = st["gemm1_swiglu"] + st["gemm2"]
     gg_tflops = (flops1 + flops2) / (gg_ms * 1e-3) / 1e12
     g1_tflops = flops1 / (st["gemm1_swiglu"] * 1e-3) / 1e12
@@ -163,7 +169,7 @@ def main():
                          "GFLOP": round((flops1 + flops2) / 1e9, 1)},
         "stages": stages,
         "roofline": {
-            "kernel": "gemm_bf16_kernel<GATED=true> (GEMM1 + SwiGLU epilogue)",
+            "kernel": "gemm_bf16_kernel<GATED=true, GATHER=true> (GEMM1 with fused row gather + SwiGLU epilogue)",
             "bound": "mfma",
             "achieved": round(g1_tflops, 1),
             "peak": PEAK_BF16_TFLOPS,

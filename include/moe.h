@@ -164,6 +164,15 @@ moe_status moe_grouped_swiglu(const void* x_perm, const int32_t* offsets, int ro
  * Neither needs a workspace. */
 moe_status moe_expert_w13_swiglu(const void* x_perm, const int32_t* offsets, int rows, const void* W13, int E, int H,
                                  int I, moe_dtype dt, void* h, hipStream_t stream);
+/* moe_expert_w13_swiglu_gather — Algorithm 2 steps 7-8 fused: the gather
+ * X_e = x[{i : (i,k) in I_e}] happens inside the GEMM's operand loads, so no
+ * permuted copy of x is written. Row r of h belongs to pair perm[r] = i*K+k
+ * and uses token row x[perm[r] / K].
+ *   x (n, H) dtype; perm (n*K) int32 from moe_permute; offsets (E+1) int32;
+ *   h (n*K, I) dtype out. perm entries outside [0, n*K) read token row 0. */
+moe_status moe_expert_w13_swiglu_gather(const void* x, const int32_t* perm, int n, int K, const int32_t* offsets,
+                                        const void* W13, int E, int H, int I, moe_dtype dt, void* h,
+                                        hipStream_t stream);
 moe_status moe_expert_w2(const void* h, const int32_t* offsets, int rows, const void* W2, int E, int H, int I,
                          moe_dtype dt, void* Y_perm, hipStream_t stream);
 
@@ -185,9 +194,10 @@ moe_status moe_unpermute_combine(const void* Y_perm, const int32_t* inv, const f
                                  int K, moe_dtype dt, void* y, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
- * moe_forward — the whole layer, Algorithm 2: moe_route, moe_permute (ep=1),
- * moe_grouped_swiglu and moe_unpermute_combine enqueued back to back on one
- * stream, with no host synchronisation.
+ * moe_forward — the whole layer, Algorithm 2: moe_route, the metadata part
+ * of moe_permute (ep=1), moe_expert_w13_swiglu_gather, moe_expert_w2 and
+ * moe_unpermute_combine enqueued back to back on one stream, with no host
+ * synchronisation.
  *
  *   y            (n, H) dtype out.
  *   logits_out   (n, E) fp32 out, or NULL.

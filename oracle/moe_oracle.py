@@ -160,21 +160,24 @@ def permutation(e_top, E: int):
 # ---------------------------------------------------------------------------
 
 
-def expert_ffn(X_e, W13_e, W2_e) -> np.ndarray:
-    """Y_e = (SiLU(X_e·W13[:, :I]) * (X_e·W13[:, I:])) · W2, in fp64.
+def expert_gate_up(X_e, W13_e) -> np.ndarray:
+    """Algorithm 2 step 8: G_e = SiLU(X_e·W13[:, :I]) * (X_e·W13[:, I:]), in fp64.
 
     [MoE-vLLM] §1.2: gate_up = X_e @ W13[e] of shape (n_e, 2I); gate, up =
-    gate_up.chunk(2, -1); h = silu(gate) * up; Y_e = h @ W2[e].
+    gate_up.chunk(2, -1); h = silu(gate) * up.
     """
     X_e = np.asarray(X_e, dtype=np.float64)
     W13_e = np.asarray(W13_e, dtype=np.float64)
-    W2_e = np.asarray(W2_e, dtype=np.float64)
     I = W13_e.shape[1] // 2  # noqa: E741
     gate_up = X_e @ W13_e
     gate, up = gate_up[:, :I], gate_up[:, I:]
     with np.errstate(over="ignore"):
-        h = gate / (1.0 + np.exp(-gate)) * up
-    return h @ W2_e
+        return gate / (1.0 + np.exp(-gate)) * up
+
+
+def expert_ffn(X_e, W13_e, W2_e) -> np.ndarray:
+    """Algorithm 2 steps 8-9: Y_e = G_e · W2[e], with G_e from expert_gate_up; fp64."""
+    return expert_gate_up(X_e, W13_e) @ np.asarray(W2_e, dtype=np.float64)
 
 
 def combine_slot_order(Y_perm, inv, w_top, n: int, K: int) -> np.ndarray:
@@ -277,6 +280,32 @@ def grouped_swiglu(x_perm, offsets, W13, W2) -> np.ndarray:
         a, b = offsets[e], offsets[e + 1]
         if b > a:
             out[a:b] = expert_ffn(x_perm[a:b], W13[e], W2[e])
+    return out
+
+
+def grouped_gate_up(x_perm, offsets, W13) -> np.ndarray:
+    """Algorithm 2 step 8 for every expert segment of expert-major rows; (rows, I) fp64."""
+    x_perm = np.asarray(x_perm)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    I = np.asarray(W13).shape[2] // 2  # noqa: E741
+    out = np.zeros((x_perm.shape[0], I), dtype=np.float64)
+    for e in range(offsets.size - 1):
+        a, b = offsets[e], offsets[e + 1]
+        if b > a:
+            out[a:b] = expert_gate_up(x_perm[a:b], W13[e])
+    return out
+
+
+def grouped_down(h, offsets, W2) -> np.ndarray:
+    """Algorithm 2 step 9 for every expert segment: Y_e = G_e · W2[e]; (rows, H) fp64."""
+    h = np.asarray(h)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    H = np.asarray(W2).shape[2]
+    out = np.zeros((h.shape[0], H), dtype=np.float64)
+    for e in range(offsets.size - 1):
+        a, b = offsets[e], offsets[e + 1]
+        if b > a:
+            out[a:b] = np.asarray(h[a:b], dtype=np.float64) @ np.asarray(W2[e], dtype=np.float64)
     return out
 
 

@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     load_library,
     moe_expert_w2,
     moe_expert_w13_swiglu,
+    moe_expert_w13_swiglu_gather,
     moe_forward,
     moe_forward_workspace_size,
     moe_grouped_swiglu,

@@ -35,6 +35,7 @@ SIGNATURES = {
     "moe_grouped_swiglu_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_grouped_swiglu": (_I, [_VP, _VP, _I, _VP, _VP, _I, _I, _I, _I, _VP, _VP, _SZ, _VP]),
     "moe_expert_w13_swiglu": (_I, [_VP, _VP, _I, _VP, _I, _I, _I, _I, _VP, _VP]),
+    "moe_expert_w13_swiglu_gather": (_I, [_VP, _VP, _I, _I, _VP, _VP, _I, _I, _I, _I, _VP, _VP]),
     "moe_expert_w2": (_I, [_VP, _VP, _I, _VP, _I, _I, _I, _I, _VP, _VP]),
     "moe_unpermute_combine": (_I, [_VP, _VP, _VP, _I, _I, _I, _I, _VP, _VP]),
     "moe_forward_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
@@ -240,6 +241,26 @@ def moe_expert_w13_swiglu(x_perm, offsets, W13, h=None, stream=None):
         _ptr(x_perm), _ptr(offsets), rows, _ptr(W13), E, H, I, _dt(x_perm), _ptr(h), _stream(dev, stream)
     )
     _check(code, "moe_expert_w13_swiglu")
+    return h
+
+
+def moe_expert_w13_swiglu_gather(x, perm, K, offsets, W13, h=None, stream=None):
+    """Algorithm 2 steps 7-8 fused: h rows for pairs perm[r], reading token rows x[perm[r] // K]."""
+    lib = load_library()
+    n, H = x.shape
+    E, _, I2 = W13.shape
+    I = I2 // 2  # noqa: E741
+    dev = x.device
+    _need(x, "x", (n, H))
+    _need(perm, "perm", (n * K,), torch.int32, dev)
+    _need(offsets, "offsets", (E + 1,), torch.int32, dev)
+    _need(W13, "W13", (E, H, 2 * I), x.dtype, dev)
+    h = _empty((n * K, I), x.dtype, dev) if h is None else h
+    _need(h, "h", (n * K, I), x.dtype, dev)
+    code = lib.moe_expert_w13_swiglu_gather(
+        _ptr(x), _ptr(perm), n, K, _ptr(offsets), _ptr(W13), E, H, I, _dt(x), _ptr(h), _stream(dev, stream)
+    )
+    _check(code, "moe_expert_w13_swiglu_gather")
     return h
 
 

@@ -153,10 +153,14 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) {
 // (GEMM2): 256 output columns. WM x WN waves split the 128 x 256 tile; each
 // wave owns (128/WM) rows and (256/WN) staged columns (for GEMM1, half of
 // them gate and the matching half up).
-template <bool GATED, int BM, int WM, int WN>
+// GATHER: A row r of the expert-major operand is row perm[r] / topk of the
+// token matrix A (n_a rows), i.e. the permutation gather is fused into the
+// HBM -> LDS copy and no permuted copy of the tokens is materialised.
+template <bool GATED, bool GATHER, int BM, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
-                                                                    const int32_t* __restrict__ offsets, int E,
-                                                                    int rows, int Kdim,
+                                                                    const int32_t* __restrict__ perm, int topk,
+                                                                    int n_a, const int32_t* __restrict__ offsets,
+                                                                    int E, int rows, int Kdim,
                                                                     const uint16_t* __restrict__ B, int ldb,
                                                                     long long b_expert_stride, int Nout, int up_col,
                                                                     uint16_t* __restrict__ C, int ldc, int NB) {
@@ -193,7 +197,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
     if (r < A_REG) {
       const int row = 8 * r + (lane >> 3);
       const int c = (lane & 7) ^ ((row >> 1) & 7);
-      src[j] = A + (size_t)(t.r0 + min(row, mrows - 1)) * Kdim + c * 8;
+      int arow = t.r0 + min(row, mrows - 1);
+      if constexpr (GATHER) {
+        const int f = perm[arow];
+        arow = ((unsigned)f < (unsigned)(n_a * topk)) ? f / topk : 0;
+      }
+      src[j] = A + (size_t)arow * Kdim + c * 8;
     } else {
       const int k = 2 * (r - A_BYTES / 1024) + (lane >> 5);
       const int c = (lane & 31) ^ b_swz(k);
@@ -360,8 +369,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
 }
 
 // fp32: one thread per output element; lanes run along the output columns.
-template <bool GATED>
+template <bool GATED, bool GATHER>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A,
+                                                      const int32_t* __restrict__ perm, int topk, int n_a,
                                                       const int32_t* __restrict__ offsets, int E, int rows,
                                                       int Kdim, const float* __restrict__ B, int ldb,
                                                       long long b_expert_stride, int Nout, int up_col,
@@ -380,7 +390,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
   }
   const int e = lo - 1;
   if (e < 0 || e >= E) return;
-  const float* a = A + (size_t)row * Kdim;
+  int arow = row;
+  if constexpr (GATHER) {
+    const int f = perm[row];
+    arow = ((unsigned)f < (unsigned)(n_a * topk)) ? f / topk : 0;
+  }
+  const float* a = A + (size_t)arow * Kdim;
   const float* b = B + (size_t)e * b_expert_stride + col;
   float gsum = 0.f, usum = 0.f;
   for (int k = 0; k < Kdim; ++k) {
@@ -396,21 +411,35 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 
 }  // namespace
 
-hipError_t launch_w13_swiglu(const void* x_perm, const int32_t* offsets, int rows, const void* W13, int E, int H,
-                             int I, moe_dtype dt, void* h, hipStream_t s) {
+namespace {
+template <bool GATHER>
+hipError_t w13_impl(const void* a, const int32_t* perm, int topk, int n_a, const int32_t* offsets, int rows,
+                    const void* W13, int E, int H, int I, moe_dtype dt, void* h, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   if (dt == MOE_BF16) {
     const int mt = max_row_tiles(rows, E, kBM);
     const int n1 = ceil_div(I, BN / 2);
-    gemm_bf16_kernel<true, kBM, kGemmWM, kGemmWN><<<mt * n1, 64 * kGemmWM * kGemmWN, 0, s>>>((const uint16_t*)x_perm, offsets, E, rows, H,
-                                                    (const uint16_t*)W13, 2 * I, (long long)H * 2 * I, I, I,
-                                                    (uint16_t*)h, I, n1);
+    gemm_bf16_kernel<true, GATHER, kBM, kGemmWM, kGemmWN><<<mt * n1, 64 * kGemmWM * kGemmWN, 0, s>>>(
+        (const uint16_t*)a, perm, topk, n_a, offsets, E, rows, H, (const uint16_t*)W13, 2 * I, (long long)H * 2 * I,
+        I, I, (uint16_t*)h, I, n1);
   } else {
     dim3 g1(ceil_div(I, 64), ceil_div(rows, 4));
-    gemm_f32_kernel<true><<<g1, 256, 0, s>>>((const float*)x_perm, offsets, E, rows, H, (const float*)W13, 2 * I,
-                                             (long long)H * 2 * I, I, I, (float*)h, I);
+    gemm_f32_kernel<true, GATHER><<<g1, 256, 0, s>>>((const float*)a, perm, topk, n_a, offsets, E, rows, H,
+                                                     (const float*)W13, 2 * I, (long long)H * 2 * I, I, I,
+                                                     (float*)h, I);
   }
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_w13_swiglu(const void* x_perm, const int32_t* offsets, int rows, const void* W13, int E, int H,
+                             int I, moe_dtype dt, void* h, hipStream_t s) {
+  return w13_impl<false>(x_perm, nullptr, 1, rows, offsets, rows, W13, E, H, I, dt, h, s);
+}
+
+hipError_t launch_w13_swiglu_gather(const void* x, const int32_t* perm, int n, int K, const int32_t* offsets,
+                                    const void* W13, int E, int H, int I, moe_dtype dt, void* h, hipStream_t s) {
+  return w13_impl<true>(x, perm, K, n, offsets, n * K, W13, E, H, I, dt, h, s);
 }
 
 hipError_t launch_w2(const void* h, const int32_t* offsets, int rows, const void* W2, int E, int H, int I,
@@ -419,11 +448,13 @@ hipError_t launch_w2(const void* h, const int32_t* offsets, int rows, const void
   if (dt == MOE_BF16) {
     const int mt = max_row_tiles(rows, E, kBM);
     const int n2 = ceil_div(H, BN);
-    gemm_bf16_kernel<false, kBM, kGemmWM, kGemmWN><<<mt * n2, 64 * kGemmWM * kGemmWN, 0, s>>>((const uint16_t*)h, offsets, E, rows, I, (const uint16_t*)W2,
+    gemm_bf16_kernel<false, false, kBM, kGemmWM, kGemmWN><<<mt * n2, 64 * kGemmWM * kGemmWN, 0, s>>>(
+        (const uint16_t*)h, nullptr, 1, rows, offsets, E, rows, I, (const uint16_t*)W2,
                                                      H, (long long)I * H, H, 0, (uint16_t*)Y_perm, H, n2);
   } else {
     dim3 g2(ceil_div(H, 64), ceil_div(rows, 4));
-    gemm_f32_kernel<false><<<g2, 256, 0, s>>>((const float*)h, offsets, E, rows, I, (const float*)W2, H,
+    gemm_f32_kernel<false, false><<<g2, 256, 0, s>>>((const float*)h, nullptr, 1, rows, offsets, E, rows, I,
+                                                     (const float*)W2, H,
                                               (long long)I * H, H, 0, (float*)Y_perm, H);
   }
   return hipGetLastError();

@@ -26,14 +26,14 @@ bool experts_ok(int E, int K) { return E >= 1 && E <= kMaxExperts && K >= 1 && K
 moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
 size_t permute_ws(int n, int E, int K) {
-  const long long total = (long long)n * K;
-  const long long nblk = (total + kPermChunk - 1) / kPermChunk;
-  return align_up((size_t)(nblk > 0 ? nblk : 1) * E * sizeof(int32_t));
+  (void)n;
+  (void)K;
+  return align_up((size_t)kPermMaxBlocks * E * sizeof(int32_t));
 }
 
 // moe_forward workspace, in order.
 struct ForwardLayout {
-  size_t logits, ids, w, counts, offsets, splits, perm, inv, pscratch, x_perm, h, Y_perm, total;
+  size_t logits, ids, w, counts, offsets, splits, perm, inv, pscratch, h, Y_perm, total;
 };
 
 ForwardLayout forward_layout(int n, int H, int I, int E, int K, moe_dtype dt) {
@@ -54,7 +54,6 @@ ForwardLayout forward_layout(int n, int H, int I, int E, int K, moe_dtype dt) {
   L.perm = take(nk * 4);
   L.inv = take(nk * 4);
   L.pscratch = take(permute_ws(n, E, K));
-  L.x_perm = take(nk * H * elt_size(dt));
   L.h = take(nk * I * elt_size(dt));
   L.Y_perm = take(nk * H * elt_size(dt));
   L.total = o;
@@ -144,6 +143,16 @@ moe_status moe_expert_w13_swiglu(const void* x_perm, const int32_t* offsets, int
   return from_hip(launch_w13_swiglu(x_perm, offsets, rows, W13, E, H, I, dt, h, stream));
 }
 
+moe_status moe_expert_w13_swiglu_gather(const void* x, const int32_t* perm, int n, int K, const int32_t* offsets,
+                                        const void* W13, int E, int H, int I, moe_dtype dt, void* h,
+                                        hipStream_t stream) {
+  if (n < 0 || K < 1 || K > kMaxTopK || (long long)n * K > INT32_MAX) return MOE_EINVAL;
+  if (n > 0 && perm == nullptr) return MOE_EINVAL;
+  const moe_status st = check_expert_gemm(x, offsets, n * K, W13, E, H, I, dt, h);
+  if (st != MOE_OK) return st;
+  return from_hip(launch_w13_swiglu_gather(x, perm, n, K, offsets, W13, E, H, I, dt, h, stream));
+}
+
 moe_status moe_expert_w2(const void* h, const int32_t* offsets, int rows, const void* W2, int E, int H, int I,
                          moe_dtype dt, void* Y_perm, hipStream_t stream) {
   const moe_status st = check_expert_gemm(h, offsets, rows, W2, E, H, I, dt, Y_perm);
@@ -189,12 +198,14 @@ moe_status moe_forward(const void* x, const void* W_gate, const float* bias, con
 
   hipError_t e = launch_route(x, W_gate, bias, n, H, E, K, renorm, dt, logits, ids, w, stream);
   if (e != hipSuccess) return MOE_EHIP;
-  e = launch_permute(ids, x, n, H, E, K, 1, dt, counts, offsets, splits, perm, inv, base + L.x_perm,
+  // Metadata only: GEMM1 gathers the token rows itself through perm.
+  e = launch_permute(ids, nullptr, n, H, E, K, 1, dt, counts, offsets, splits, perm, inv, nullptr,
                      (int32_t*)(base + L.pscratch), stream);
   if (e != hipSuccess) return MOE_EHIP;
   if (n == 0) return MOE_OK;
-  e = launch_grouped_swiglu(base + L.x_perm, offsets, n * K, W13, W2, E, H, I, dt, base + L.Y_perm, base + L.h,
-                            stream);
+  e = launch_w13_swiglu_gather(x, perm, n, K, offsets, W13, E, H, I, dt, base + L.h, stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  e = launch_w2(base + L.h, offsets, n * K, W2, E, H, I, dt, base + L.Y_perm, stream);
   if (e != hipSuccess) return MOE_EHIP;
   return from_hip(launch_combine(base + L.Y_perm, inv, w, n, H, K, dt, y, stream));
 }

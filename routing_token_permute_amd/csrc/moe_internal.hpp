@@ -14,9 +14,9 @@ namespace moe {
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 64;
 
-// moe_permute: pairs per counting block (256 threads x 8 pairs).
+// moe_permute: threads per count/place block; at most kPermMaxBlocks blocks.
 constexpr int kPermThreads = 256;
-constexpr int kPermChunk = 2048;
+constexpr int kPermMaxBlocks = 128;
 
 // bf16 grouped GEMM tile.
 constexpr int kGemmBM = 128;
@@ -38,7 +38,7 @@ hipError_t launch_route(const void* x, const void* W_gate, const float* bias, in
                         int renorm, moe_dtype dt, float* logits, int32_t* topk_ids, float* topk_w,
                         hipStream_t s);
 
-// block_counts: workspace of ceil(n*K / kPermChunk) * E int32.
+// block_counts: workspace of kPermMaxBlocks * E int32.
 hipError_t launch_permute(const int32_t* topk_ids, const void* x, int n, int H, int E, int K, int ep,
                           moe_dtype dt, int32_t* counts, int32_t* offsets, int32_t* splits, int32_t* perm,
                           int32_t* inv, void* x_perm, int32_t* block_counts, hipStream_t s);
@@ -51,6 +51,9 @@ hipError_t launch_grouped_swiglu(const void* x_perm, const int32_t* offsets, int
 // The two GEMMs separately (launch_grouped_swiglu runs both).
 hipError_t launch_w13_swiglu(const void* x_perm, const int32_t* offsets, int rows, const void* W13, int E, int H,
                              int I, moe_dtype dt, void* h, hipStream_t s);
+// GEMM1 reading token rows x[perm[r] / K] directly (no permuted copy of x).
+hipError_t launch_w13_swiglu_gather(const void* x, const int32_t* perm, int n, int K, const int32_t* offsets,
+                                    const void* W13, int E, int H, int I, moe_dtype dt, void* h, hipStream_t s);
 hipError_t launch_w2(const void* h, const int32_t* offsets, int rows, const void* W2, int E, int H, int I,
                      moe_dtype dt, void* Y_perm, hipStream_t s);
 

@@ -9,139 +9,193 @@
 // (§2.4); the torchtitan `_local_reorder` / `_permute` and the index
 // inversion kernel of "0. goin" (§2.2, §2.3) are the same operation.
 //
-// How: three small kernels over blocks of 2048 pairs, then a row gather.
-//   1. count:   per-block histogram in LDS (integer atomics: the result does
-//               not depend on their order).
-//   2. scan:    one workgroup turns the per-block histograms into counts,
-//               offsets, splits and each block's starting row per expert.
-//   3. place:   each wave walks its 512 pairs in 64-pair steps; lanes with
-//               the same expert are found with ballots over the id bits, and
-//               a lane's rank among them is a popcount of the lower lanes, so
-//               pairs keep ascending flat order inside every expert segment.
-//   4. gather:  one wave per destination row copies 16-byte vectors.
+// How: two launches over blocks of P pairs (at most 128 blocks).
+//   1. count:  per-block histogram in LDS (integer atomics: the result does
+//              not depend on their order).
+//   2. place:  every block reads all block histograms (a few KB from L2) and
+//              derives the per-expert totals, the exclusive offsets and its
+//              own starting row per expert, so no separate scan launch is
+//              needed; then each wave walks its part of the block in 64-pair
+//              steps. Lanes with the same expert are found with ballots over
+//              the id bits and ranked by a popcount of the lower lanes, so
+//              pairs keep ascending flat order inside every expert segment.
+// When x is given, a row gather follows: one wave per destination row copies
+// 16-byte vectors.
 #include "moe_internal.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kPairsPerThread = kPermChunk / kPermThreads;  // 8
-constexpr int kWaves = kPermThreads / 64;                   // 4
-constexpr int kPairsPerWave = kPermChunk / kWaves;          // 512
+constexpr int kWaves = kPermThreads / 64;  // 4
+constexpr int kMaxBlocks = kPermMaxBlocks;
+constexpr int kStepBatch = 8;              // 64-pair steps whose ids are loaded together
+
+// Pairs per block: a multiple of 256 (whole 64-pair steps for each of the 4
+// waves), at least 512, and large enough that there are at most kMaxBlocks.
+inline int pairs_per_block(int total) {
+  int p = ceil_div(ceil_div(total, kMaxBlocks), 256) * 256;
+  return p < 512 ? 512 : p;
+}
 
 __global__ __launch_bounds__(kPermThreads) void permute_count_kernel(const int32_t* __restrict__ ids, int total,
-                                                                     int E, int32_t* __restrict__ block_counts) {
+                                                                     int E, int P,
+                                                                     int32_t* __restrict__ block_counts) {
   __shared__ int hist[kMaxExperts];
   for (int e = threadIdx.x; e < E; e += kPermThreads) hist[e] = 0;
   __syncthreads();
-  const int base = blockIdx.x * kPermChunk;
-#pragma unroll
-  for (int j = 0; j < kPairsPerThread; ++j) {
-    const int f = base + j * kPermThreads + (int)threadIdx.x;
-    if (f < total) {
-      const int e = ids[f];
-      if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);
-    }
+  const int base = blockIdx.x * P;
+  const int end = min(base + P, total);
+  for (int f = base + (int)threadIdx.x; f < end; f += kPermThreads) {
+    const int e = ids[f];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kPermThreads) block_counts[(size_t)blockIdx.x * E + e] = hist[e];
 }
 
-// One workgroup of 256 threads (E <= 256): thread e owns expert e.
-// In: block_counts[b][e]. Out: block_counts[b][e] becomes the first row of
-// block b's pairs for expert e; counts, offsets, splits.
-__global__ __launch_bounds__(kMaxExperts) void permute_scan_kernel(int32_t* __restrict__ block_counts, int nblk,
-                                                                   int E, int ep, int32_t* __restrict__ counts,
-                                                                   int32_t* __restrict__ offsets,
-                                                                   int32_t* __restrict__ splits) {
-  __shared__ int scan[kMaxExperts];
-  __shared__ int offs[kMaxExperts + 1];
-  const int e = threadIdx.x;
-  int total = 0;
-  if (e < E) {
-    for (int b = 0; b < nblk; ++b) {
-      const int c = block_counts[(size_t)b * E + e];
-      block_counts[(size_t)b * E + e] = total;
-      total += c;
-    }
-    counts[e] = total;
+// Lanes of this wave whose expert id equals this lane's (ballots over the id
+// bits); `valid` lanes only match valid lanes.
+__device__ __forceinline__ uint64_t same_expert_lanes(int e, bool valid, int id_bits) {
+  uint64_t same = __ballot(valid);
+  for (int b = 0; b < id_bits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t m = __ballot(bit);
+    same &= bit ? m : ~m;
   }
-  scan[e] = (e < E) ? total : 0;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the 256 slots.
-  for (int d = 1; d < kMaxExperts; d <<= 1) {
-    const int v = (e >= d) ? scan[e - d] : 0;
-    __syncthreads();
-    scan[e] += v;
-    __syncthreads();
-  }
-  const int excl = scan[e] - ((e < E) ? total : 0);
-  if (e < E) {
-    offs[e] = excl;
-    offsets[e] = excl;
-    if (e == E - 1) {
-      offs[E] = scan[e];
-      offsets[E] = scan[e];
-    }
-    for (int b = 0; b < nblk; ++b) block_counts[(size_t)b * E + e] += excl;
-  }
-  __syncthreads();
-  if (e < ep) {
-    const int El = E / ep;
-    splits[e] = offs[(e + 1) * El] - offs[e * El];
-  }
+  return same;
 }
 
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Block b places its P pairs. It first derives, from every block's counts,
+// the per-expert totals, the exclusive offsets and the number of pairs of each
+// expert in the blocks before it (block 0 also writes counts, offsets and
+// splits); then each wave walks its quarter of the block in 64-pair steps and
+// places pairs in ascending flat order.
 __global__ __launch_bounds__(kPermThreads) void permute_place_kernel(const int32_t* __restrict__ ids, int total,
-                                                                     int E, int id_bits,
-                                                                     const int32_t* __restrict__ block_base,
+                                                                     int E, int ep, int P, int nblk, int id_bits,
+                                                                     const int32_t* __restrict__ block_counts,
+                                                                     int32_t* __restrict__ counts,
+                                                                     int32_t* __restrict__ offsets,
+                                                                     int32_t* __restrict__ splits,
                                                                      int32_t* __restrict__ perm,
                                                                      int32_t* __restrict__ inv) {
+  __shared__ int scan[kMaxExperts];
+  __shared__ int offs[kMaxExperts + 1];
   __shared__ int next[kWaves][kMaxExperts];  // next free row per (wave, expert)
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int i = threadIdx.x; i < kWaves * kMaxExperts; i += kPermThreads) (&next[0][0])[i] = 0;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = blockIdx.x;
+  // Column sums over the blocks (thread e owns expert e).
+  int before = 0, tot = 0;
+  if (tid < E) {
+    for (int b0 = 0; b0 < nblk; b0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) c[q] = (b0 + q < nblk) ? block_counts[(size_t)(b0 + q) * E + tid] : 0;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        before += (b0 + q < b) ? c[q] : 0;
+        tot += c[q];
+      }
+    }
+  }
+  if (tid < kMaxExperts) scan[tid] = (tid < E) ? tot : 0;
+  for (int i = tid; i < kWaves * kMaxExperts; i += kPermThreads) (&next[0][0])[i] = 0;
   __syncthreads();
-  const int wbase = blockIdx.x * kPermChunk + wave * kPairsPerWave;
-  // Pass 1: how many of this wave's pairs go to each expert.
-  for (int s = 0; s < kPairsPerWave / 64; ++s) {
-    const int f = wbase + s * 64 + lane;
-    const int e = (f < total) ? ids[f] : -1;
-    if ((unsigned)e < (unsigned)E) atomicAdd(&next[wave][e], 1);
+  for (int d = 1; d < kMaxExperts; d <<= 1) {  // inclusive scan over the experts
+    int v = 0;
+    if (tid < kMaxExperts && tid >= d) v = scan[tid - d];
+    __syncthreads();
+    if (tid < kMaxExperts) scan[tid] += v;
+    __syncthreads();
+  }
+  if (tid < E) {
+    const int excl = scan[tid] - tot;
+    offs[tid] = excl;
+    if (tid == E - 1) offs[E] = scan[tid];
+    if (b == 0) {
+      counts[tid] = tot;
+      offsets[tid] = excl;
+      if (tid == E - 1) offsets[E] = scan[tid];
+    }
+  }
+  // Pass 1: this wave's pairs per expert.
+  const int per_wave = P / kWaves;
+  const int wbase = b * P + wave * per_wave;
+  const int steps = per_wave / 64;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int s0 = 0; s0 < steps; s0 += kStepBatch) {
+    int eid[kStepBatch];
+#pragma unroll
+    for (int q = 0; q < kStepBatch; ++q) {
+      const int f = wbase + (s0 + q) * 64 + lane;
+      eid[q] = (s0 + q < steps && f < total) ? ids[f] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < kStepBatch; ++q) {
+      const int e = eid[q];
+      const bool valid = (unsigned)e < (unsigned)E;
+      const uint64_t same = same_expert_lanes(e, valid, id_bits);
+      if (valid && (same & below) == 0) next[wave][e] += __popcll(same);
+      wave_sync_lds();
+    }
   }
   __syncthreads();
-  // Each wave's first row per expert: the block's first row plus the
-  // pairs of the lower waves.
-  for (int e = threadIdx.x; e < E; e += kPermThreads) {
-    int run = block_base[(size_t)blockIdx.x * E + e];
+  if (b == 0 && tid < ep) {
+    const int El = E / ep;
+    splits[tid] = offs[(tid + 1) * El] - offs[tid * El];
+  }
+  // Each wave's first row per expert: offset + earlier blocks + lower waves.
+  if (tid < E) {
+    int run = offs[tid] + before;
     for (int w = 0; w < kWaves; ++w) {
-      const int c = next[w][e];
-      next[w][e] = run;
+      const int c = next[w][tid];
+      next[w][tid] = run;
       run += c;
     }
   }
   __syncthreads();
-  // Pass 2: place pairs in ascending flat order.
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int s = 0; s < kPairsPerWave / 64; ++s) {
-    const int f = wbase + s * 64 + lane;
-    const int e = (f < total) ? ids[f] : -1;
-    const bool valid = (unsigned)e < (unsigned)E;
-    uint64_t same = __ballot(valid);
-    for (int b = 0; b < id_bits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t m = __ballot(bit);
-      same &= bit ? m : ~m;
+  // Pass 2: stable placement.
+  for (int s0 = 0; s0 < steps; s0 += kStepBatch) {
+    int eid[kStepBatch];
+#pragma unroll
+    for (int q = 0; q < kStepBatch; ++q) {
+      const int f = wbase + (s0 + q) * 64 + lane;
+      eid[q] = (s0 + q < steps && f < total) ? ids[f] : -1;
     }
-    const int rank = __popcll(same & below);
-    int pos = 0;
-    if (valid) pos = next[wave][e] + rank;
-    __builtin_amdgcn_wave_barrier();
-    if (valid) {
-      perm[pos] = f;
-      inv[f] = pos;
-      if (rank == 0) next[wave][e] = pos + __popcll(same);
+#pragma unroll
+    for (int q = 0; q < kStepBatch; ++q) {
+      const int f = wbase + (s0 + q) * 64 + lane;
+      const int e = eid[q];
+      const bool valid = (unsigned)e < (unsigned)E;
+      const uint64_t same = same_expert_lanes(e, valid, id_bits);
+      const int rank = __popcll(same & below);
+      int pos = 0;
+      if (valid) pos = next[wave][e] + rank;
+      wave_sync_lds();
+      if (valid) {
+        perm[pos] = f;
+        inv[f] = pos;
+        if (rank == 0) next[wave][e] = pos + __popcll(same);
+      }
+      wave_sync_lds();
     }
-    __builtin_amdgcn_wave_barrier();
   }
+}
+
+// No pairs: counts, offsets and splits are all zero.
+__global__ __launch_bounds__(kMaxExperts) void permute_empty_kernel(int E, int ep, int32_t* __restrict__ counts,
+                                                                    int32_t* __restrict__ offsets,
+                                                                    int32_t* __restrict__ splits) {
+  const int t = threadIdx.x;
+  if (t < E) counts[t] = 0;
+  if (t <= E) offsets[t] = 0;
+  if (t < ep) splits[t] = 0;
 }
 
 // x_perm[p] = x[perm[p] / K]: one wave per row, 16-byte vectors.
@@ -164,13 +218,17 @@ hipError_t launch_permute(const int32_t* topk_ids, const void* x, int n, int H, 
                           moe_dtype dt, int32_t* counts, int32_t* offsets, int32_t* splits, int32_t* perm,
                           int32_t* inv, void* x_perm, int32_t* block_counts, hipStream_t s) {
   const int total = n * K;
-  const int nblk = ceil_div(total, kPermChunk);
+  const int P = pairs_per_block(total);
+  const int nblk = total > 0 ? ceil_div(total, P) : 0;
   int id_bits = 0;
   while ((1 << id_bits) < E) ++id_bits;
-  if (nblk > 0) permute_count_kernel<<<nblk, kPermThreads, 0, s>>>(topk_ids, total, E, block_counts);
-  permute_scan_kernel<<<1, kMaxExperts, 0, s>>>(block_counts, nblk, E, ep, counts, offsets, splits);
-  if (nblk > 0)
-    permute_place_kernel<<<nblk, kPermThreads, 0, s>>>(topk_ids, total, E, id_bits, block_counts, perm, inv);
+  if (nblk > 0) {
+    permute_count_kernel<<<nblk, kPermThreads, 0, s>>>(topk_ids, total, E, P, block_counts);
+    permute_place_kernel<<<nblk, kPermThreads, 0, s>>>(topk_ids, total, E, ep, P, nblk, id_bits, block_counts,
+                                                       counts, offsets, splits, perm, inv);
+  } else {
+    permute_empty_kernel<<<1, kMaxExperts, 0, s>>>(E, ep, counts, offsets, splits);
+  }
   if (x != nullptr && total > 0) {
     const int elt = (dt == MOE_BF16) ? 2 : 4;
     const int row_vecs = H * elt / 16;

@@ -1,13 +1,25 @@
 // Router: logits = x · W_gate (+ bias), softmax, top-K (optional renorm).
 //
 // Algorithm 2 steps 1-3 of "MoE 分布式推理基础（基于 vLLM）" §1.2 and the
-// OlmoeTopKRouter source quoted there. The router product is small and
-// HBM-bound (x is read once); each workgroup stages a 64-row slice of W_gate
-// in LDS, runs bf16 MFMA 16x16x32 on 16-token groups (one group per wave),
-// keeps the fp32 logits in LDS and then does softmax and top-K with one wave
-// per token: each lane owns up to four experts, and each of the K passes is a
-// wave-wide maximum of a 64-bit key (order-preserving logit bits, then the
-// complemented expert index), so ties go to the lowest index.
+// OlmoeTopKRouter source quoted there (linear layer, softmax, topk, and the
+// optional division of the K weights by their sum).
+//
+// bf16 path. One workgroup serves 16 tokens; its WK waves split the hidden
+// dimension. Each wave streams its own 64-row slices of W_gate through a
+// private double buffer in LDS (the next slice is fetched into registers
+// while the current one feeds the MFMAs) and turns them into MFMA B operands
+// with the gfx950 LDS transpose read; the token rows are the A operands,
+// loaded from HBM one slice ahead. bf16 MFMA 16x16x32 accumulates in fp32.
+// The WK partial logit tiles are summed in LDS in wave order, so the result
+// does not depend on timing.
+//
+// Top-K. For each token one wave ranks every expert: lane e counts the
+// experts that come before it in the order (logit descending, index
+// ascending), scanning the token's order keys in LDS; the lanes whose rank is
+// below K write slot `rank`. The row maximum falls out of the same scan, and
+// the exp of each logit is computed once by its lane and the denominator is
+// summed in expert order by every lane, so all lanes hold bitwise the same
+// value. No cross-lane reductions are needed.
 #include <math.h>
 
 #include "moe_internal.hpp"
@@ -15,269 +27,278 @@
 namespace moe {
 namespace {
 
-// Larger logit -> larger key; among equal logits the lower expert index wins.
-// -0.0 is folded into +0.0 so that the two compare equal.
-__device__ __forceinline__ uint64_t route_key(float v, int e) {
+// Order key of a logit: larger logit -> larger key; -0.0 is folded into +0.0
+// so that the two compare equal; -inf maps above 0, which marks "no expert".
+__device__ __forceinline__ uint32_t order_key(float v) {
   uint32_t u = __float_as_uint(v);
   if (u == 0x80000000u) u = 0u;
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint64_t)(~(uint32_t)e);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ float key_logit(uint64_t key) {
-  uint32_t hi = (uint32_t)(key >> 32);
-  uint32_t u = (hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi;
-  return __uint_as_float(u);
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-__device__ __forceinline__ int key_expert(uint64_t key) { return (int)(~(uint32_t)key); }
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint64_t o = __shfl_xor(v, off);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
-// Butterfly sum: every lane ends with the same, order-fixed value.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
-
-// Softmax + top-K of one row of E fp32 logits, one wave. EPL = experts per lane.
+// Softmax + top-K of one token whose E logits (fp32) and order keys sit in
+// LDS; one wave, EPL experts per lane (EPL * 64 >= E). `ex` is wave-private
+// LDS scratch of kMaxExperts + kMaxTopK floats.
 template <int EPL>
-__device__ void topk_softmax_row(const float* row, int E, int K, int renorm, int32_t* ids_out, float* w_out) {
+__device__ void topk_token(const float* lg, const uint32_t* keys, int E, int K, int renorm, float* ex,
+                           int32_t* ids_out, float* w_out) {
   const int lane = lane_id();
-  float v[EPL];
-  uint64_t key[EPL];
+  uint32_t mine[EPL];
+  int rank[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    mine[j] = (lane + 64 * j < E) ? keys[lane + 64 * j] : 0u;
+    rank[j] = 0;
+  }
+  uint32_t kmax = 0u;
+#pragma unroll 8
+  for (int f = 0; f < E; ++f) {
+    const uint32_t kf = keys[f];  // same address in every lane: an LDS broadcast
+    kmax = kf > kmax ? kf : kmax;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) rank[j] += (kf > mine[j]) || (kf == mine[j] && f < lane + 64 * j);
+  }
+  const float m = key_value(kmax);
+  // Each expert's exp(l - m) once, by its own lane; then every lane sums them
+  // in expert order, so all lanes hold bitwise the same denominator.
+#pragma unroll
+  for (int j = 0; j < EPL; ++j)
+    if (lane + 64 * j < E) ex[lane + 64 * j] = expf(lg[lane + 64 * j] - m);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float s = 0.f;
+#pragma unroll 8
+  for (int f = 0; f < E; ++f) s += ex[f];
+  float* slot = ex + kMaxExperts;  // K weights in slot order, for the renorm sum
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane + 64 * j;
-    if (e < E) {
-      v[j] = row[e];
-      key[j] = route_key(v[j], e);
-    } else {
-      v[j] = -INFINITY;
-      key[j] = 0;  // below every real key, including a -inf logit
+    if (e < E && rank[j] < K) {
+      const float w = ex[e] / s;
+      ids_out[rank[j]] = e;
+      if (renorm)
+        slot[rank[j]] = w;
+      else
+        w_out[rank[j]] = w;
     }
   }
-  float m = 0.f, my_l = 0.f;
-  int my_e = 0;
-  for (int k = 0; k < K; ++k) {
-    uint64_t best = key[0];
-#pragma unroll
-    for (int j = 1; j < EPL; ++j) best = key[j] > best ? key[j] : best;
-    best = wave_max_u64(best);
-#pragma unroll
-    for (int j = 0; j < EPL; ++j)
-      if (key[j] == best) key[j] = 0;
-    const float lv = key_logit(best);
-    if (k == 0) m = lv;
-    if (lane == k) {
-      my_e = key_expert(best);
-      my_l = lv;
-    }
-  }
-  float s = 0.f;
-#pragma unroll
-  for (int j = 0; j < EPL; ++j)
-    if (lane + 64 * j < E) s += expf(v[j] - m);
-  s = wave_sum(s);
-  float wk = expf(my_l - m) / s;
   if (renorm) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     float t = 0.f;
-    for (int k = 0; k < K; ++k) t += __shfl(wk, k);
-    wk = wk / t;
+    for (int k = 0; k < K; ++k) t += slot[k];
+    if (lane < K) w_out[lane] = slot[lane] / t;
   }
-  if (lane < K) {
-    ids_out[lane] = my_e;
-    w_out[lane] = wk;
-  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int EPL>
-__device__ __forceinline__ void topk_dispatch(const float* row, int E, int K, int renorm, int32_t* ids, float* w) {
-  topk_softmax_row<EPL>(row, E, K, renorm, ids, w);
-}
-
-__device__ void topk_any(const float* row, int E, int K, int renorm, int32_t* ids, float* w) {
+// `scratch`: kMaxExperts + kMaxTopK floats of LDS private to the calling wave.
+__device__ void topk_token_any(const float* lg, const uint32_t* keys, int E, int K, int renorm, float* scratch,
+                               int32_t* ids, float* w) {
   if (E <= 64)
-    topk_dispatch<1>(row, E, K, renorm, ids, w);
+    topk_token<1>(lg, keys, E, K, renorm, scratch, ids, w);
   else if (E <= 128)
-    topk_dispatch<2>(row, E, K, renorm, ids, w);
+    topk_token<2>(lg, keys, E, K, renorm, scratch, ids, w);
   else
-    topk_dispatch<4>(row, E, K, renorm, ids, w);
+    topk_token<4>(lg, keys, E, K, renorm, scratch, ids, w);
 }
 
-// ---------------------------------------------------------------------------
-// bf16 router: WAVES waves per workgroup, 16 tokens per wave, NT = Epad/16
-// expert tiles of 16 columns.
-// ---------------------------------------------------------------------------
-constexpr int kRouteBK = 64;
-constexpr int kRouteLdsBytes = 2 * kRouteBK * kMaxExperts * 2;  // 64 KB: two W_gate slices
+constexpr int kScratch = kMaxExperts + kMaxTopK;  // floats of top-K scratch per wave
 
-template <int WAVES, int NT>
-__global__ __launch_bounds__(64 * WAVES) void route_bf16_kernel(const uint16_t* __restrict__ x,
-                                                                const uint16_t* __restrict__ Wg,
-                                                                const float* __restrict__ bias, int n, int H,
-                                                                int E, int K, int renorm,
-                                                                float* __restrict__ logits,
-                                                                int32_t* __restrict__ ids,
-                                                                float* __restrict__ wout) {
-  constexpr int TOK = 16 * WAVES;
-  constexpr int EPAD = 16 * NT;
-  constexpr int PITCH = EPAD * 2;              // bytes per staged W_gate row
-  constexpr int SLICE = kRouteBK * PITCH;      // bytes per staged slice
-  constexpr int LPITCH = EPAD + 1;             // floats per logit row in LDS
-  static_assert(2 * SLICE <= kRouteLdsBytes, "W_gate slice too large");
-  static_assert(TOK * LPITCH * 4 <= kRouteLdsBytes, "logit tile too large");
-  __shared__ __attribute__((aligned(16))) char smem_raw[kRouteLdsBytes];
+// ---------------------------------------------------------------------------
+// bf16 router: 16 tokens per workgroup, WK waves split H, NT expert tiles.
+// ---------------------------------------------------------------------------
+constexpr int kTok = 16;
+constexpr int kSliceRows = 64;
+
+template <int NT, int WK>
+struct RouteCfg {
+  static constexpr int EPAD = 16 * NT;
+  static constexpr int PITCH = EPAD * 2;                  // bytes per staged W_gate row
+  static constexpr int SLICE = kSliceRows * PITCH;        // bytes per staged slice
+  static constexpr int STAGING = WK * 2 * SLICE;          // per-wave double buffers
+  static constexpr int LPITCH = EPAD + 1;                 // floats per logit row
+  static constexpr int PARTIAL = WK * kTok * EPAD * 4;    // per-wave partial tiles
+  static constexpr int LOGITS = kTok * LPITCH * 8;        // logits + order keys
+  static constexpr int SLOTS = WK * kScratch * 4;         // top-K scratch, one row per wave
+  static constexpr int AFTER = PARTIAL + LOGITS + SLOTS;
+  static constexpr int LDS = STAGING > AFTER ? STAGING : AFTER;
+  static constexpr int CHUNKS = kSliceRows * EPAD / 8;    // 16-byte pieces per slice
+  static constexpr int CPL = (CHUNKS + 63) / 64;          // pieces per lane
+};
+
+template <int NT, int WK>
+__global__ __launch_bounds__(64 * WK) void route_bf16_kernel(const uint16_t* __restrict__ x,
+                                                             const uint16_t* __restrict__ Wg,
+                                                             const float* __restrict__ bias, int n, int H, int E,
+                                                             int K, int renorm, float* __restrict__ logits,
+                                                             int32_t* __restrict__ ids, float* __restrict__ wout) {
+  using C = RouteCfg<NT, WK>;
+  constexpr int EPAD = C::EPAD, PITCH = C::PITCH, SLICE = C::SLICE;
+  __shared__ __attribute__((aligned(16))) char smem_raw[C::LDS];
   lds_char_t* smem = (lds_char_t*)smem_raw;
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, li = lane & 15;
-  const int t0 = blockIdx.x * TOK;
-  const int my_tok = t0 + wave * 16 + li;  // token whose x row this lane feeds to the MFMA
+  const int t0 = blockIdx.x * kTok;
+  const int my_tok = t0 + li;
   const bool tok_ok = my_tok < n;
-  const uint16_t* xrow = x + (size_t)(tok_ok ? my_tok : 0) * H;
+  const uint16_t* xrow = x + (size_t)(tok_ok ? my_tok : 0) * H + g * 8;
+  const bool vecW = (E % 8) == 0;
+  const int nslices = H / kSliceRows;
+  const int rounds = (nslices + WK - 1) / WK;
+  lds_char_t* mybuf = smem + wave * 2 * SLICE;
 
   f32x4_t acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const bool vecW = (E % 8) == 0;
-  const int nslices = H / kRouteBK;
-
-  auto stage = [&](int s, int buf) {
-    // W_gate rows [s*64, s*64+64), columns [0, EPAD): 8 elements per item.
-    lds_char_t* dst = smem + buf * SLICE;
-    const int k0 = s * kRouteBK;
-    for (int it = tid; it < kRouteBK * (EPAD / 8); it += 64 * WAVES) {
-      const int kr = it / (EPAD / 8), c = it % (EPAD / 8);
-      const int e0 = c * 8;
-      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-      const uint16_t* src = Wg + (size_t)(k0 + kr) * E + e0;
-      if (vecW && e0 + 8 <= E) {
-        v = *(const u32x4_t*)src;
-      } else {
-        uint16_t tmp[8];
+  u32x4_t wreg[C::CPL];
+  u32x4_t xa[2];
+  auto fetch = [&](int s) {  // W_gate slice s into registers, x operands of slice s
+    const int k0 = s * kSliceRows;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) tmp[q] = (e0 + q < E) ? src[q] : (uint16_t)0;
-        v = u32x4_t{tmp[0] | ((uint32_t)tmp[1] << 16), tmp[2] | ((uint32_t)tmp[3] << 16),
-                    tmp[4] | ((uint32_t)tmp[5] << 16), tmp[6] | ((uint32_t)tmp[7] << 16)};
+    for (int q = 0; q < C::CPL; ++q) {
+      const int it = lane + 64 * q;
+      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+      if (it < C::CHUNKS) {
+        const int kr = it / (EPAD / 8), e0 = (it % (EPAD / 8)) * 8;
+        const uint16_t* src = Wg + (size_t)(k0 + kr) * E + e0;
+        if (vecW && e0 + 8 <= E) {
+          v = *(const u32x4_t*)src;
+        } else {
+          uint32_t p[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e0 + e < E) p[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+          v = u32x4_t{p[0], p[1], p[2], p[3]};
+        }
       }
-      lds_write_b128(dst + kr * PITCH + c * 16, v);
+      wreg[q] = v;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      xa[ks] = tok_ok ? *(const u32x4_t*)(xrow + k0 + ks * 32) : u32x4_t{0u, 0u, 0u, 0u};
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < C::CPL; ++q) {
+      const int it = lane + 64 * q;
+      if (it < C::CHUNKS) {
+        const int kr = it / (EPAD / 8), c = it % (EPAD / 8);
+        lds_write_b128(mybuf + buf * SLICE + kr * PITCH + c * 16, wreg[q]);
+      }
     }
   };
 
-  stage(0, 0);
-  __syncthreads();
-  for (int s = 0; s < nslices; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nslices) stage(s + 1, buf ^ 1);
-    const lds_char_t* wb = smem + buf * SLICE;
+  // Round r: wave w handles slice r*WK + w. Every wave runs the same number
+  // of rounds so the barriers match; waves past the last slice idle.
+  const int s0 = wave;
+  if (s0 < nslices) fetch(s0);
+  for (int r = 0; r < rounds; ++r) {
+    const int s = r * WK + wave;
+    const bool active = s < nslices;
+    u32x4_t xcur[2] = {xa[0], xa[1]};
+    if (active) stash(r & 1);
+    if (active && s + WK < nslices) fetch(s + WK);
+    __syncthreads();
+    if (active) {
+      const lds_char_t* wb = mybuf + (r & 1) * SLICE;
+      const int rr = li >> 2, cc = li & 3;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t a = bf16x8_t{};
-      if (tok_ok) {
-        u32x4_t av = *(const u32x4_t*)(xrow + s * kRouteBK + ks * 32 + g * 8);
-        a = __builtin_bit_cast(bf16x8_t, av);
-      }
-      const int r = li >> 2, c = li & 3;
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xcur[ks]);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int col = nt * 16 + 4 * c;
-        const lds_char_t* p0 = wb + (ks * 32 + g * 8 + r) * PITCH + col * 2;
-        bf16x4_t lo = lds_read_tr16(p0);
-        bf16x4_t hi = lds_read_tr16(p0 + 4 * PITCH);
-        bf16x8_t b = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[nt], 0, 0, 0);
+        for (int nt = 0; nt < NT; ++nt) {
+          const lds_char_t* p0 = wb + (ks * 32 + g * 8 + rr) * PITCH + (nt * 16 + 4 * cc) * 2;
+          const bf16x4_t lo = lds_read_tr16(p0);
+          const bf16x4_t hi = lds_read_tr16(p0 + 4 * PITCH);
+          const bf16x8_t b = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[nt], 0, 0, 0);
+        }
       }
     }
     __syncthreads();
   }
 
-  // Logits: lane (g, li) of tile nt holds rows 4g..4g+3 (tokens), column li (expert).
-  float* lsm = (float*)smem_raw;
+  // Partial tiles: lane (g, li) of tile nt holds tokens 4g..4g+3, expert nt*16+li.
+  float* part = (float*)smem_raw;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int e = nt * 16 + li;
-    const float b = (bias != nullptr && e < E) ? bias[e] : 0.f;
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tl = wave * 16 + 4 * g + j;
-      const float v = acc[nt][j] + b;
-      lsm[tl * LPITCH + e] = v;
-      const int t = t0 + tl;
-      if (e < E && t < n) logits[(size_t)t * E + e] = v;
+    for (int j = 0; j < 4; ++j) part[(wave * kTok + 4 * g + j) * EPAD + nt * 16 + li] = acc[nt][j];
+  __syncthreads();
+  float* lg = part + WK * kTok * EPAD;                      // [kTok][LPITCH] logits
+  uint32_t* keys = (uint32_t*)(lg + kTok * C::LPITCH);     // [kTok][LPITCH] order keys
+  float* slots = (float*)(keys + kTok * C::LPITCH);        // [WK][kScratch]
+  for (int q = tid; q < kTok * EPAD; q += 64 * WK) {
+    const int tl = q / EPAD, e = q % EPAD;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < WK; ++w) v += part[(w * kTok + tl) * EPAD + e];
+    if (e < E) {
+      if (bias != nullptr) v += bias[e];
+      lg[tl * C::LPITCH + e] = v;
+      keys[tl * C::LPITCH + e] = order_key(v);
+      if (t0 + tl < n) logits[(size_t)(t0 + tl) * E + e] = v;
     }
   }
   __syncthreads();
-  for (int q = 0; q < 16; ++q) {
-    const int tl = wave * 16 + q;
+  for (int tl = wave; tl < kTok; tl += WK) {
     const int t = t0 + tl;
     if (t >= n) break;
-    topk_any(lsm + tl * LPITCH, E, K, renorm, ids + (size_t)t * K, wout + (size_t)t * K);
+    topk_token_any(lg + tl * C::LPITCH, keys + tl * C::LPITCH, E, K, renorm, slots + wave * kScratch,
+                   ids + (size_t)t * K, wout + (size_t)t * K);
   }
 }
 
 // ---------------------------------------------------------------------------
 // fp32 router: one wave per token, lanes over experts, sequential fp32 FMA
-// over the hidden dimension.
+// over the hidden dimension. Also the softmax/top-K-only entry (x == NULL).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict__ x, const float* __restrict__ Wg,
-                                                        const float* __restrict__ bias, int n, int H, int E,
+                                                        const float* __restrict__ bias,
+                                                        const float* __restrict__ logits_in, int n, int H, int E,
                                                         int K, int renorm, float* __restrict__ logits,
                                                         int32_t* __restrict__ ids, float* __restrict__ wout) {
-  __shared__ float lsm[4][kMaxExperts];
+  __shared__ float lg[4][kMaxExperts];
+  __shared__ uint32_t keys[4][kMaxExperts];
+  __shared__ float slots[4][kScratch];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= n) return;
-  const float* xr = x + (size_t)t * H;
   for (int e = lane; e < E; e += 64) {
-    float acc = 0.f;
-    for (int h = 0; h < H; ++h) acc = fmaf(xr[h], Wg[(size_t)h * E + e], acc);
-    if (bias != nullptr) acc += bias[e];
-    lsm[wave][e] = acc;
-    logits[(size_t)t * E + e] = acc;
+    float v;
+    if (x != nullptr) {
+      const float* xr = x + (size_t)t * H;
+      v = 0.f;
+      for (int h = 0; h < H; ++h) v = fmaf(xr[h], Wg[(size_t)h * E + e], v);
+      if (bias != nullptr) v += bias[e];
+      logits[(size_t)t * E + e] = v;
+    } else {
+      v = logits_in[(size_t)t * E + e];
+    }
+    lg[wave][e] = v;
+    keys[wave][e] = order_key(v);
   }
-  __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  topk_any(lsm[wave], E, K, renorm, ids + (size_t)t * K, wout + (size_t)t * K);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  topk_token_any(lg[wave], keys[wave], E, K, renorm, slots[wave], ids + (size_t)t * K, wout + (size_t)t * K);
 }
 
-// Softmax + top-K only, from caller-supplied logits: one wave per token.
-__global__ __launch_bounds__(256) void topk_only_kernel(const float* __restrict__ logits, int n, int E, int K,
-                                                        int renorm, int32_t* __restrict__ ids,
-                                                        float* __restrict__ wout) {
-  const int wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= n) return;
-  topk_any(logits + (size_t)t * E, E, K, renorm, ids + (size_t)t * K, wout + (size_t)t * K);
-}
-
-template <int WAVES>
-hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* Wg, const float* bias, int n, int H, int E, int K,
-                             int renorm, float* logits, int32_t* ids, float* w, hipStream_t s) {
-  const int grid = ceil_div(n, 16 * WAVES);
-  const int nt = ceil_div(E, 16);
-  if (nt <= 1)
-    route_bf16_kernel<WAVES, 1><<<grid, 64 * WAVES, 0, s>>>(x, Wg, bias, n, H, E, K, renorm, logits, ids, w);
-  else if (nt <= 2)
-    route_bf16_kernel<WAVES, 2><<<grid, 64 * WAVES, 0, s>>>(x, Wg, bias, n, H, E, K, renorm, logits, ids, w);
-  else if (nt <= 4)
-    route_bf16_kernel<WAVES, 4><<<grid, 64 * WAVES, 0, s>>>(x, Wg, bias, n, H, E, K, renorm, logits, ids, w);
-  else if (nt <= 8)
-    route_bf16_kernel<WAVES, 8><<<grid, 64 * WAVES, 0, s>>>(x, Wg, bias, n, H, E, K, renorm, logits, ids, w);
-  else
-    route_bf16_kernel<WAVES, 16><<<grid, 64 * WAVES, 0, s>>>(x, Wg, bias, n, H, E, K, renorm, logits, ids, w);
-  return hipGetLastError();
+template <int NT, int WK>
+void launch_bf16(const uint16_t* x, const uint16_t* Wg, const float* bias, int n, int H, int E, int K, int renorm,
+                 float* logits, int32_t* ids, float* w, hipStream_t s) {
+  static_assert(RouteCfg<NT, WK>::LDS <= 160 * 1024, "router LDS budget");
+  route_bf16_kernel<NT, WK><<<ceil_div(n, kTok), 64 * WK, 0, s>>>(x, Wg, bias, n, H, E, K, renorm, logits, ids, w);
 }
 
 }  // namespace
@@ -286,15 +307,26 @@ hipError_t launch_route(const void* x, const void* W_gate, const float* bias, in
                         int renorm, moe_dtype dt, float* logits, int32_t* topk_ids, float* topk_w,
                         hipStream_t s) {
   if (n == 0) return hipSuccess;
-  if (x == nullptr) {
-    topk_only_kernel<<<ceil_div(n, 4), 256, 0, s>>>(logits, n, E, K, renorm, topk_ids, topk_w);
+  if (x != nullptr && dt == MOE_BF16) {
+    const uint16_t* xb = (const uint16_t*)x;
+    const uint16_t* wb = (const uint16_t*)W_gate;
+    const int nt = ceil_div(E, 16);
+    if (nt <= 1)
+      launch_bf16<1, 8>(xb, wb, bias, n, H, E, K, renorm, logits, topk_ids, topk_w, s);
+    else if (nt <= 2)
+      launch_bf16<2, 8>(xb, wb, bias, n, H, E, K, renorm, logits, topk_ids, topk_w, s);
+    else if (nt <= 4)
+      launch_bf16<4, 8>(xb, wb, bias, n, H, E, K, renorm, logits, topk_ids, topk_w, s);
+    else if (nt <= 8)
+      launch_bf16<8, 4>(xb, wb, bias, n, H, E, K, renorm, logits, topk_ids, topk_w, s);
+    else
+      launch_bf16<16, 2>(xb, wb, bias, n, H, E, K, renorm, logits, topk_ids, topk_w, s);
     return hipGetLastError();
   }
-  if (dt == MOE_BF16)
-    return launch_route_bf16<2>((const uint16_t*)x, (const uint16_t*)W_gate, bias, n, H, E, K, renorm, logits,
-                                topk_ids, topk_w, s);
-  route_f32_kernel<<<ceil_div(n, 4), 256, 0, s>>>((const float*)x, (const float*)W_gate, bias, n, H, E, K, renorm,
-                                                   logits, topk_ids, topk_w);
+  // fp32 router, or softmax/top-K from caller-supplied logits (x == NULL).
+  route_f32_kernel<<<ceil_div(n, 4), 256, 0, s>>>((const float*)x, (const float*)W_gate, bias,
+                                                   x == nullptr ? logits : nullptr, n, H, E, K, renorm, logits,
+                                                   topk_ids, topk_w);
   return hipGetLastError();
 }
 

@@ -49,12 +49,19 @@ def errors(got: np.ndarray, ref: np.ndarray):
 TOL = {"bf16": (2e-2, 1e-2), "f32": (1e-5, 1e-5)}
 
 
-def assert_close(got, ref, dtype: str, what: str):
+def assert_close(got, ref, dtype: str, what: str, intermediate: bool = False):
     """The layer's bounds (max-abs and relative Frobenius), plus the largest error
     relative to the largest reference value under the same relative bound, which
-    stays meaningful when outputs are much smaller than one."""
+    stays meaningful when outputs are much smaller than one.
+
+    `intermediate`: the SwiGLU activation h, whose values reach ~10 at the
+    OLMoE scale; stored in bf16 its rounding alone can exceed the layer's
+    absolute bound, which is stated for the layer output y. Such arrays are
+    held to the two relative bounds only."""
     ma, rf = errors(got, ref)
     tol_ma, tol_rf = TOL[dtype]
+    if intermediate:
+        tol_ma = float("inf")
     scale = float(np.abs(ref).max()) if np.size(ref) else 0.0
     rmax = ma / scale if scale > 0 else ma
     print(f"[{what}] max_abs={ma:.3e} rel_frob={rf:.3e} max_rel_to_peak={rmax:.3e} "

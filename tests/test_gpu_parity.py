@@ -226,6 +226,32 @@ def test_grouped_swiglu(dev, rows, E, H, I, dtype, kind):  # noqa: E741
     assert_close(to_f64(Y), ref, dtype, f"grouped rows={rows} E={E} {kind}")
 
 
+@pytest.mark.parametrize("n,H,I,E,K,kind", [(300, 128, 64, 8, 2, "routed"), (1000, 256, 192, 16, 4, "skewed"), (4096, 2048, 1024, 64, 8, "routed")])
+def test_expert_gemm_halves_and_gather(dev, n, H, I, E, K, kind):  # noqa: E741
+    """GEMM1 (+SwiGLU) alone, GEMM1 with the gather fused, and GEMM2 alone."""
+    w = make_layer(n, H, I, E, K, seed=n + I)
+    bias = zipf_bias(E) if kind == "skewed" else None
+    _, e_top, _ = _ids_from_random_logits(n, E, K, seed=n, bias=bias)
+    counts = oracle.expert_counts(e_top, E)
+    offsets = oracle.offsets_from_counts(counts)
+    perm, _ = oracle.permutation(e_top, E)
+    t = layer_tensors(w, dev)
+    off_d = torch.from_numpy(offsets.astype(np.int32)).to(dev)
+    perm_d = torch.from_numpy(perm.astype(np.int32)).to(dev)
+    xp = t["x"][perm_d.long() // K].contiguous()
+    h1 = moe.moe_expert_w13_swiglu(xp, off_d, t["W13"])
+    h2 = moe.moe_expert_w13_swiglu_gather(t["x"], perm_d, K, off_d, t["W13"])
+    torch.cuda.synchronize()
+    assert torch.equal(h1.view(torch.int16), h2.view(torch.int16))  # same kernel arithmetic, same bits
+    ref_h = om.grouped_gate_up(w.x_f32[perm // K], offsets, w.W13_f32)
+    assert_close(to_f64(h1), ref_h, "bf16", f"gate_up n={n} E={E}", intermediate=True)
+    # GEMM2 alone, on an independent seeded h of the same scale as SwiGLU outputs.
+    hb, hf = random_bf16_matrix(np.random.default_rng(n), (n * K, I), std=0.3)
+    Y = moe.moe_expert_w2(dev_tensor(hb, "bf16", dev), off_d, t["W2"])
+    torch.cuda.synchronize()
+    assert_close(to_f64(Y), om.grouped_down(hf, offsets, w.W2_f32), "bf16", f"down n={n} E={E}")
+
+
 def test_grouped_swiglu_leaves_rows_past_offsets(dev):
     rows, E, H, I = 200, 4, 64, 64  # noqa: E741
     counts = np.array([50, 0, 70, 30])  # offsets[E] = 150 < rows
