@@ -39,11 +39,89 @@ def _parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="olmoe_bf16", choices=["olmoe_bf16", "olmoe_skewed_bf16", "decode_bf16"])
+    p.add_argument("--workload", default="olmoe_bf16",
+                   choices=["olmoe_bf16", "olmoe_skewed_bf16", "decode_bf16", "ep_share_bf16"])
     p.add_argument("--stage-reps", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle wall time for the CPU baseline")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy kernel (to scale FETCH_SIZE / WRITE_SIZE)")
+    p.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
+                   help="turn four rocprofv3 --pmc csv directories into the traffic summary printed on stdout")
     return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# HBM traffic of the dominant kernel, from rocprofv3 counters
+# ---------------------------------------------------------------------------
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm1_swiglu_gather_olmoe_n4096.txt")
+GEMM_SOURCE = os.path.join(ROOT, "routing_token_permute_amd", "csrc", "grouped_gemm.hip")
+COPY_BYTES = 1 << 30
+
+
+def _source_hash():
+    import hashlib
+
+    return hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def _pmc_mean(d, counter, match):
+    import csv
+    import glob
+
+    vals = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and match(r["Kernel_Name"]):
+                vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} samples matching in {d}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def _summarize_traffic(dirs):
+    fd, wd, cfd, cwd = dirs
+    is_g1 = lambda k: "gemm_bf16_kernel<true, true" in k  # noqa: E731
+    is_copy = lambda k: "copy" in k.lower() or "elementwise" in k.lower()  # noqa: E731
+    fetch_kib, nf = _pmc_mean(fd, "FETCH_SIZE", is_g1)
+    write_kib, nw = _pmc_mean(wd, "WRITE_SIZE", is_g1)
+    cal_f, _ = _pmc_mean(cfd, "FETCH_SIZE", is_copy)
+    cal_w, _ = _pmc_mean(cwd, "WRITE_SIZE", is_copy)
+    f_scale = COPY_BYTES / (cal_f * 1024.0)
+    w_scale = COPY_BYTES / (cal_w * 1024.0)
+    out = {
+        "kernel": "gemm_bf16_kernel<true, true, ...> (GEMM1 + SwiGLU, gather fused), OLMoE n=4096",
+        "source_sha256_16": _source_hash(),
+        "fetch_kib_per_dispatch": round(fetch_kib, 1), "fetch_dispatches": nf,
+        "write_kib_per_dispatch": round(write_kib, 1), "write_dispatches": nw,
+        "copy_1GiB_fetch_kib": round(cal_f, 1), "copy_1GiB_write_kib": round(cal_w, 1),
+        "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+        "hbm_bytes_per_launch": round(fetch_kib * 1024 * f_scale + write_kib * 1024 * w_scale),
+    }
+    print(json.dumps(out, indent=1))
+
+
+def _traffic_bytes():
+    """HBM bytes per GEMM1 launch from the committed counter summary, or None when
+    the summary is missing or was taken on a different kernel source."""
+    try:
+        d = json.loads(open(TRAFFIC_FILE).read().split("\n```json\n", 1)[-1].split("\n```", 1)[0])
+    except (OSError, ValueError):
+        return None
+    if d.get("source_sha256_16") != _source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def _copy_calibration():
+    import torch
+
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}))
 
 
 def _time_region(fn, reps, torch):
@@ -61,6 +139,12 @@ def _time_region(fn, reps, torch):
 
 def main():
     args = _parse()
+    if args.summarize_traffic:
+        _summarize_traffic(args.summarize_traffic)
+        return
+    if args.copy_calibration:
+        _copy_calibration()
+        return
     if args.gpus != 1:
         print(
             f"bench.py measures one GPU only: the layer runs on a single MI355X and this build has no "
@@ -74,6 +158,9 @@ def main():
     import routing_token_permute_amd as moe
     from workloads import make_config
 
+    if args.workload == "ep_share_bf16":
+        _bench_ep_share(args)
+        return
     dev = torch.device("cuda:0")
     w = make_config(args.workload)
     n, H, I, E, K = w.n, w.H, w.I, w.E, w.K  # noqa: E741
@@ -175,10 +262,105 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(g1_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": _traffic_bytes(),
         },
         "experts_hit": hit,
         "wall_s_timed_region": round(wall, 3),
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def _bench_ep_share(args):
+    """One GPU's expert-parallel share, two micro-batches of 16384 received rows,
+    8 local experts: the four controls of a two-stream overlap measurement.
+
+    T_A: both micro-batches' expert GEMMs alone (one stream); T_B: their
+    permute + unpermute alone (one stream); T_C: everything serial on one
+    stream; T_D: the two-stream schedule permute(A); [GEMM(A) || permute(B)];
+    [GEMM(B) || unpermute(A)]; unpermute(B). Hidden fraction of the
+    permute/unpermute time: 1 - (T_D - T_A) / T_B.
+    """
+    import torch
+
+    import oracle
+    from routing_token_permute_amd import ep_share as eps
+    from workloads import make_config
+
+    dev = torch.device("cuda:0")
+    ep = make_config("ep_share_bf16")
+    tb = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    W13, W2 = tb(ep.bits("W13")), tb(ep.bits("W2"))
+    mbs = [eps.prepare(eps.MicroBatch(tb(m.x_bits()), torch.from_numpy(m.eid.reshape(-1, 1)).to(dev)), ep.E_local, ep.I)
+           for m in ep.micro_batches]
+    a, b = mbs
+    s0 = torch.cuda.current_stream(dev)
+    compute, comm = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+    eps.run_serial(a, b, W13, W2, ep.E_local, s0)  # fills every buffer the controls read
+    torch.cuda.synchronize()
+
+    def timed(fn, streams):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        first = streams[0]
+        start.record(first)
+        for st in streams[1:]:
+            st.wait_event(start)
+        for _ in range(args.steps):
+            fn()
+        for st in streams[1:]:
+            e = torch.cuda.Event()
+            e.record(st)
+            first.wait_event(e)
+        end.record(first)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / args.steps
+
+    t_a = timed(lambda: (eps.experts(a, W13, W2, s0), eps.experts(b, W13, W2, s0)), [s0])
+    t_b = timed(lambda: (eps.permute(a, ep.E_local, s0), eps.permute(b, ep.E_local, s0), eps.unpermute(a, s0),
+                         eps.unpermute(b, s0)), [s0])
+    t_c = timed(lambda: eps.run_serial(a, b, W13, W2, ep.E_local, s0), [s0])
+    t_d = timed(lambda: eps.run_two_streams(a, b, W13, W2, ep.E_local, compute, comm), [compute, comm])
+    rows = 2 * ep.R
+    flops = 2 * ep.flops_per_micro_batch
+    cpu = None
+    if not args.no_cpu_baseline:
+        import time as _t
+
+        reps, t0 = 0, _t.perf_counter()
+        while True:
+            for m in ep.micro_batches:
+                oracle.ep_share_forward(m.x_f32, m.eid, ep.W13_f32, ep.W2_f32)
+            reps += 1
+            if _t.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        el = _t.perf_counter() - t0
+        cpu = {"value": round(rows * reps / el, 1), "unit": "rows/s", "cores": len(os.sched_getaffinity(0)),
+               "kind": "oracle", "sample": f"both micro-batches, {reps} repetitions, {el:.1f} s"}
+    out = {
+        "metric": "EP-share two-micro-batch expert layer rows/s (permute + SwiGLU grouped GEMM + unpermute)",
+        "value": round(rows / (t_d * 1e-3), 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_d, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (Dirichlet(0.5) expert shares, 8 source ranks, N(0,1) rows, N(0,0.02) weights)",
+        "config": {"workload": "ep_share_bf16", "rows_per_micro_batch": ep.R, "micro_batches": 2,
+                   "E_local": ep.E_local, "H": ep.H, "I": ep.I,
+                   "counts": [m.counts.tolist() for m in ep.micro_batches]},
+        "overlap": {"T_A_gemm_ms": round(t_a, 4), "T_B_permute_unpermute_ms": round(t_b, 4),
+                    "T_C_serial_ms": round(t_c, 4), "T_D_two_streams_ms": round(t_d, 4),
+                    "hidden_fraction": round(1 - (t_d - t_a) / t_b, 4), "speedup_serial_over_overlap": round(t_c / t_d, 4),
+                    "gemm_TFLOP/s_alone": round(flops / (t_a * 1e-3) / 1e12, 1),
+                    "gemm_TFLOP/s_in_overlap": round(flops / (t_d * 1e-3) / 1e12, 1)},
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(dev),
     }

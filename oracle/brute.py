@@ -87,18 +87,29 @@ def permutation_triple_loop(e_top, E: int):
     return perm, inv
 
 
-def ffn_token(x_i, W13_e, W2_e):
-    """One token through one SwiGLU expert, with explicit loops over I."""
+def gate_up_token(x_i, W13_e):
+    """One token's SwiGLU activation h (length I), with explicit loops over I."""
     x_i = np.asarray(x_i, dtype=np.float64)
     W13_e = np.asarray(W13_e, dtype=np.float64)
-    W2_e = np.asarray(W2_e, dtype=np.float64)
     I = W13_e.shape[1] // 2  # noqa: E741
     h = np.zeros(I, dtype=np.float64)
     for j in range(I):
         g = float(np.dot(x_i, W13_e[:, j]))
         u = float(np.dot(x_i, W13_e[:, I + j]))
         h[j] = g * (1.0 / (1.0 + math.exp(-g))) * u
-    return h @ W2_e
+    return h
+
+
+def down_token(h_i, W2_e):
+    """One row of the down projection, column by column."""
+    h_i = np.asarray(h_i, dtype=np.float64)
+    W2_e = np.asarray(W2_e, dtype=np.float64)
+    return np.array([float(np.dot(h_i, W2_e[:, c])) for c in range(W2_e.shape[1])])
+
+
+def ffn_token(x_i, W13_e, W2_e):
+    """One token through one SwiGLU expert."""
+    return down_token(gate_up_token(x_i, W13_e), W2_e)
 
 
 def layer_per_token(x, e_top, w_top, W13, W2):

@@ -39,24 +39,26 @@ constexpr int B_ROW = BN * 2;             // bytes per staged k-row of B
 static_assert(BN == 256 && BK == 64, "LDS layouts below assume 256-column, 64-deep stages");
 
 // Stage geometry for a BM-row tile: A is BM x 64 (BM*128 bytes), B is 64 x 256.
-// BM = 128: three stages (144 KB); BM = 256: two stages (128 KB).
+// As many stages as fit in 160 KB of LDS, at most four: BM = 256 gets two
+// (128 KB), BM = 128 three (144 KB), BM = 32 four (144 KB).
 template <int BM>
 struct TileCfg {
   static constexpr int A_BYTES = BM * BK * 2;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int NSTAGE = (3 * STAGE <= 160 * 1024) ? 3 : 2;
+  static constexpr int FIT = (160 * 1024) / STAGE;
+  static constexpr int NSTAGE = FIT > 4 ? 4 : FIT;
   static constexpr int EPI_BYTES = BM * 264 * 2;  // staged output tile (GEMM2 is the larger)
   static constexpr int LDS_BYTES = (NSTAGE * STAGE > EPI_BYTES) ? NSTAGE * STAGE : EPI_BYTES;
   static constexpr int REGIONS = STAGE / 1024;  // 1 KB DMA regions per stage
 };
 
-// Launch configuration of the bf16 path: BM-row tiles, WM x WN waves.
-#ifndef MOE_GEMM_BM
-#define MOE_GEMM_BM 256
-#define MOE_GEMM_WM 2
-#define MOE_GEMM_WN 4
-#endif
-constexpr int kBM = MOE_GEMM_BM, kGemmWM = MOE_GEMM_WM, kGemmWN = MOE_GEMM_WN;
+// Launch configurations of the bf16 path (BM-row tiles, WM x WN waves):
+// large experts use 256-row tiles with 8 waves; when experts average few
+// rows (decode-like batches) 32-row tiles with a 4-stage ring keep the
+// weight stream deep instead.
+constexpr int kBM = 256, kGemmWM = 2, kGemmWN = 4;
+constexpr int kSmallBM = 32, kSmallWM = 1, kSmallWN = 4;
+constexpr int kSmallRowsPerExpert = 64;  // rows / E at or below this: small tiles
 
 // A tile: 128 rows x 64 k (128 B per row = 8 chunks of 16 B). Chunk c of row r
 // sits at slot c ^ ((r / 2) % 8): 16 consecutive rows reading the same chunk
@@ -172,6 +174,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
   constexpr int REG = Cfg::REGIONS / NW;   // 1 KB DMA regions per wave per stage
   constexpr int DMA_PER_STAGE = REG;       // 16-byte loads per thread per stage
   static_assert(NT % 2 == 0 && MT >= 1 && REG * NW == Cfg::REGIONS, "tile split");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 4 && 2 * DMA_PER_STAGE <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(16))) char smem_raw[Cfg::LDS_BYTES];
   lds_char_t* smem = (lds_char_t*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -305,7 +308,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
       if (p < nk) issue(p, p);
     int stage = 0;
     for (int kt = 0; kt < nk; ++kt) {
-      if (NSTAGE == 3 && kt + 1 < nk)
+      // Stages issued after k-step kt and still allowed in flight.
+      const int later = min(NSTAGE - 2, nk - 1 - kt);
+      if (later >= 2)
+        asm volatile("s_waitcnt vmcnt(%0)" : : "n"(2 * DMA_PER_STAGE) : "memory");
+      else if (later == 1)
         asm volatile("s_waitcnt vmcnt(%0)" : : "n"(DMA_PER_STAGE) : "memory");
       else
         asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
@@ -412,16 +419,35 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 }  // namespace
 
 namespace {
+template <bool GATED, bool GATHER, int BM, int WM, int WN>
+void launch_cfg(const void* a, const int32_t* perm, int topk, int n_a, const int32_t* offsets, int E, int rows,
+                int Kdim, const void* B, int ldb, long long bstride, int Nout, int up_col, void* C, int ldc, int NB,
+                hipStream_t s) {
+  const int mt = max_row_tiles(rows, E, BM);
+  gemm_bf16_kernel<GATED, GATHER, BM, WM, WN><<<mt * NB, 64 * WM * WN, 0, s>>>(
+      (const uint16_t*)a, perm, topk, n_a, offsets, E, rows, Kdim, (const uint16_t*)B, ldb, bstride, Nout, up_col,
+      (uint16_t*)C, ldc, NB);
+}
+
+template <bool GATED, bool GATHER>
+void launch_bf16(const void* a, const int32_t* perm, int topk, int n_a, const int32_t* offsets, int E, int rows,
+                 int Kdim, const void* B, int ldb, long long bstride, int Nout, int up_col, void* C, int ldc, int NB,
+                 hipStream_t s) {
+  if ((long long)rows <= (long long)kSmallRowsPerExpert * E)
+    launch_cfg<GATED, GATHER, kSmallBM, kSmallWM, kSmallWN>(a, perm, topk, n_a, offsets, E, rows, Kdim, B, ldb,
+                                                            bstride, Nout, up_col, C, ldc, NB, s);
+  else
+    launch_cfg<GATED, GATHER, kBM, kGemmWM, kGemmWN>(a, perm, topk, n_a, offsets, E, rows, Kdim, B, ldb, bstride,
+                                                     Nout, up_col, C, ldc, NB, s);
+}
+
 template <bool GATHER>
 hipError_t w13_impl(const void* a, const int32_t* perm, int topk, int n_a, const int32_t* offsets, int rows,
                     const void* W13, int E, int H, int I, moe_dtype dt, void* h, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   if (dt == MOE_BF16) {
-    const int mt = max_row_tiles(rows, E, kBM);
-    const int n1 = ceil_div(I, BN / 2);
-    gemm_bf16_kernel<true, GATHER, kBM, kGemmWM, kGemmWN><<<mt * n1, 64 * kGemmWM * kGemmWN, 0, s>>>(
-        (const uint16_t*)a, perm, topk, n_a, offsets, E, rows, H, (const uint16_t*)W13, 2 * I, (long long)H * 2 * I,
-        I, I, (uint16_t*)h, I, n1);
+    launch_bf16<true, GATHER>(a, perm, topk, n_a, offsets, E, rows, H, W13, 2 * I, (long long)H * 2 * I, I, I, h, I,
+                              ceil_div(I, BN / 2), s);
   } else {
     dim3 g1(ceil_div(I, 64), ceil_div(rows, 4));
     gemm_f32_kernel<true, GATHER><<<g1, 256, 0, s>>>((const float*)a, perm, topk, n_a, offsets, E, rows, H,
@@ -446,16 +472,12 @@ hipError_t launch_w2(const void* h, const int32_t* offsets, int rows, const void
                      moe_dtype dt, void* Y_perm, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   if (dt == MOE_BF16) {
-    const int mt = max_row_tiles(rows, E, kBM);
-    const int n2 = ceil_div(H, BN);
-    gemm_bf16_kernel<false, false, kBM, kGemmWM, kGemmWN><<<mt * n2, 64 * kGemmWM * kGemmWN, 0, s>>>(
-        (const uint16_t*)h, nullptr, 1, rows, offsets, E, rows, I, (const uint16_t*)W2,
-                                                     H, (long long)I * H, H, 0, (uint16_t*)Y_perm, H, n2);
+    launch_bf16<false, false>(h, nullptr, 1, rows, offsets, E, rows, I, W2, H, (long long)I * H, H, 0, Y_perm, H,
+                              ceil_div(H, BN), s);
   } else {
     dim3 g2(ceil_div(H, 64), ceil_div(rows, 4));
     gemm_f32_kernel<false, false><<<g2, 256, 0, s>>>((const float*)h, nullptr, 1, rows, offsets, E, rows, I,
-                                                     (const float*)W2, H,
-                                              (long long)I * H, H, 0, (float*)Y_perm, H);
+                                                     (const float*)W2, H, (long long)I * H, H, 0, (float*)Y_perm, H);
   }
   return hipGetLastError();
 }

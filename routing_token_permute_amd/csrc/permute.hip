@@ -32,7 +32,9 @@ constexpr int kStepBatch = 8;              // 64-pair steps whose ids are loaded
 
 // Pairs per block: a multiple of 256 (whole 64-pair steps for each of the 4
 // waves), at least 512, and large enough that there are at most kMaxBlocks.
+// Up to 2048 pairs fit one block (8 steps per wave), which needs no count launch.
 inline int pairs_per_block(int total) {
+  if (total <= 2048) return 2048;
   int p = ceil_div(ceil_div(total, kMaxBlocks), 256) * 256;
   return p < 512 ? 512 : p;
 }
@@ -71,11 +73,13 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Block b places its P pairs. It first derives, from every block's counts,
-// the per-expert totals, the exclusive offsets and the number of pairs of each
+// Block b places its P pairs. Each wave first counts its quarter of the
+// block per expert; then the block derives, from every block's counts, the
+// per-expert totals, the exclusive offsets and the number of pairs of each
 // expert in the blocks before it (block 0 also writes counts, offsets and
-// splits); then each wave walks its quarter of the block in 64-pair steps and
-// places pairs in ascending flat order.
+// splits); finally each wave walks its quarter in 64-pair steps and places
+// pairs in ascending flat order. With one block, no count launch precedes it
+// (block_counts == NULL) and its own counts are the totals.
 __global__ __launch_bounds__(kPermThreads) void permute_place_kernel(const int32_t* __restrict__ ids, int total,
                                                                      int E, int ep, int P, int nblk, int id_bits,
                                                                      const int32_t* __restrict__ block_counts,
@@ -90,40 +94,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_place_kernel(const int32
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.x;
-  // Column sums over the blocks (thread e owns expert e).
-  int before = 0, tot = 0;
-  if (tid < E) {
-    for (int b0 = 0; b0 < nblk; b0 += 16) {
-      int c[16];
-#pragma unroll
-      for (int q = 0; q < 16; ++q) c[q] = (b0 + q < nblk) ? block_counts[(size_t)(b0 + q) * E + tid] : 0;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        before += (b0 + q < b) ? c[q] : 0;
-        tot += c[q];
-      }
-    }
-  }
-  if (tid < kMaxExperts) scan[tid] = (tid < E) ? tot : 0;
   for (int i = tid; i < kWaves * kMaxExperts; i += kPermThreads) (&next[0][0])[i] = 0;
   __syncthreads();
-  for (int d = 1; d < kMaxExperts; d <<= 1) {  // inclusive scan over the experts
-    int v = 0;
-    if (tid < kMaxExperts && tid >= d) v = scan[tid - d];
-    __syncthreads();
-    if (tid < kMaxExperts) scan[tid] += v;
-    __syncthreads();
-  }
-  if (tid < E) {
-    const int excl = scan[tid] - tot;
-    offs[tid] = excl;
-    if (tid == E - 1) offs[E] = scan[tid];
-    if (b == 0) {
-      counts[tid] = tot;
-      offsets[tid] = excl;
-      if (tid == E - 1) offsets[E] = scan[tid];
-    }
-  }
   // Pass 1: this wave's pairs per expert.
   const int per_wave = P / kWaves;
   const int wbase = b * P + wave * per_wave;
@@ -143,6 +115,46 @@ __global__ __launch_bounds__(kPermThreads) void permute_place_kernel(const int32
       const uint64_t same = same_expert_lanes(e, valid, id_bits);
       if (valid && (same & below) == 0) next[wave][e] += __popcll(same);
       wave_sync_lds();
+    }
+  }
+  __syncthreads();
+  // Per-expert totals and the pairs of each expert in earlier blocks (thread e
+  // owns expert e). With a single block (block_counts == NULL) the totals are
+  // this block's own counts.
+  int before = 0, tot = 0;
+  if (tid < E) {
+    if (block_counts == nullptr) {
+      for (int w = 0; w < kWaves; ++w) tot += next[w][tid];
+    } else {
+      for (int b0 = 0; b0 < nblk; b0 += 16) {
+        int c[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) c[q] = (b0 + q < nblk) ? block_counts[(size_t)(b0 + q) * E + tid] : 0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          before += (b0 + q < b) ? c[q] : 0;
+          tot += c[q];
+        }
+      }
+    }
+  }
+  if (tid < kMaxExperts) scan[tid] = (tid < E) ? tot : 0;
+  __syncthreads();
+  for (int d = 1; d < kMaxExperts; d <<= 1) {  // inclusive scan over the experts
+    int v = 0;
+    if (tid < kMaxExperts && tid >= d) v = scan[tid - d];
+    __syncthreads();
+    if (tid < kMaxExperts) scan[tid] += v;
+    __syncthreads();
+  }
+  if (tid < E) {
+    const int excl = scan[tid] - tot;
+    offs[tid] = excl;
+    if (tid == E - 1) offs[E] = scan[tid];
+    if (b == 0) {
+      counts[tid] = tot;
+      offsets[tid] = excl;
+      if (tid == E - 1) offsets[E] = scan[tid];
     }
   }
   __syncthreads();
@@ -194,7 +206,8 @@ __global__ __launch_bounds__(kMaxExperts) void permute_empty_kernel(int E, int e
                                                                     int32_t* __restrict__ splits) {
   const int t = threadIdx.x;
   if (t < E) counts[t] = 0;
-  if (t <= E) offsets[t] = 0;
+  if (t < E) offsets[t] = 0;
+  if (t == 0) offsets[E] = 0;
   if (t < ep) splits[t] = 0;
 }
 
@@ -222,7 +235,10 @@ hipError_t launch_permute(const int32_t* topk_ids, const void* x, int n, int H, 
   const int nblk = total > 0 ? ceil_div(total, P) : 0;
   int id_bits = 0;
   while ((1 << id_bits) < E) ++id_bits;
-  if (nblk > 0) {
+  if (nblk == 1) {
+    permute_place_kernel<<<1, kPermThreads, 0, s>>>(topk_ids, total, E, ep, P, 1, id_bits, nullptr, counts,
+                                                    offsets, splits, perm, inv);
+  } else if (nblk > 1) {
     permute_count_kernel<<<nblk, kPermThreads, 0, s>>>(topk_ids, total, E, P, block_counts);
     permute_place_kernel<<<nblk, kPermThreads, 0, s>>>(topk_ids, total, E, ep, P, nblk, id_bits, block_counts,
                                                        counts, offsets, splits, perm, inv);

@@ -1,0 +1,109 @@
+"""One GPU's expert-parallel share with two micro-batches on two HIP streams.
+
+What it models: the rows this GPU received for its local experts in an
+expert-parallel exchange arrive rank-major; `_permute` makes them
+expert-major for the grouped GEMM, the local experts run, and `_unpermute`
+puts the results back in arrival order before the reverse exchange ("0. goin",
+§2.2, torchtitan's standard dispatcher). With two micro-batches, one
+micro-batch's expert GEMMs cover the other's dispatch/combine work: the
+Domino-style interleave of "XTuner Domino EP" (execution path: a compute
+stream, a communication stream and events placed at the first consumer) and
+"大模型系统中的通算融合" §3.1 (MB0's expert GEMM covers MB1's dispatch, MB1's
+covers MB0's combine). On one GPU the exchange itself is absent; the permute
+and unpermute kernels stand on the second stream.
+
+This module only orders library calls on streams; every step runs in the
+HIP kernels of libmoe.so (moe_permute with K = 1, moe_grouped_swiglu,
+moe_unpermute_combine with unit weights).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+
+@dataclasses.dataclass
+class MicroBatch:
+    """Device buffers of one micro-batch: received rows, their local expert ids
+    (R, 1) int32, and the outputs/scratch the schedule fills."""
+
+    x: torch.Tensor  # (R, H) received rows, arrival order
+    eid: torch.Tensor  # (R, 1) int32 local expert of each row
+    meta: dict = dataclasses.field(default_factory=dict)
+    Y_perm: Optional[torch.Tensor] = None
+    out: Optional[torch.Tensor] = None
+    ws_perm: Optional[torch.Tensor] = None
+    ws_gemm: Optional[torch.Tensor] = None
+
+
+def prepare(mb: MicroBatch, E_local: int, I: int) -> MicroBatch:  # noqa: E741
+    """Allocate every buffer the schedule writes (torch allocations, outside the timed work)."""
+    R, H = mb.x.shape
+    dev = mb.x.device
+    lib = _lib.load_library()
+    mb.meta = {
+        "x_perm": torch.empty((R, H), dtype=mb.x.dtype, device=dev),
+        "counts": torch.empty((E_local,), dtype=torch.int32, device=dev),
+        "offsets": torch.empty((E_local + 1,), dtype=torch.int32, device=dev),
+        "splits": torch.empty((1,), dtype=torch.int32, device=dev),
+        "perm": torch.empty((R,), dtype=torch.int32, device=dev),
+        "inv": torch.empty((R,), dtype=torch.int32, device=dev),
+    }
+    mb.Y_perm = torch.empty((R, H), dtype=mb.x.dtype, device=dev)
+    mb.out = torch.empty((R, H), dtype=mb.x.dtype, device=dev)
+    mb.ws_perm = torch.empty(lib.moe_permute_workspace_size(R, E_local, 1), dtype=torch.uint8, device=dev)
+    dt = _lib._dt(mb.x)
+    mb.ws_gemm = torch.empty(lib.moe_grouped_swiglu_workspace_size(R, I, dt), dtype=torch.uint8, device=dev)
+    return mb
+
+
+def permute(mb: MicroBatch, E_local: int, stream) -> None:
+    _lib.moe_permute(mb.eid, mb.x, E_local, out=mb.meta, ws=mb.ws_perm, stream=stream)
+
+
+def experts(mb: MicroBatch, W13: torch.Tensor, W2: torch.Tensor, stream) -> None:
+    _lib.moe_grouped_swiglu(mb.meta["x_perm"], mb.meta["offsets"], W13, W2, Y_perm=mb.Y_perm, ws=mb.ws_gemm,
+                            stream=stream)
+
+
+def unpermute(mb: MicroBatch, stream) -> None:
+    R = mb.x.shape[0]
+    _lib.moe_unpermute_combine(mb.Y_perm, mb.meta["inv"], None, R, 1, y=mb.out, stream=stream)
+
+
+def run_serial(a: MicroBatch, b: MicroBatch, W13, W2, E_local: int, stream) -> None:
+    """Both micro-batches, every step on one stream (the serial control)."""
+    for mb in (a, b):
+        permute(mb, E_local, stream)
+        experts(mb, W13, W2, stream)
+        unpermute(mb, stream)
+
+
+def run_two_streams(a: MicroBatch, b: MicroBatch, W13, W2, E_local: int, compute, comm) -> None:
+    """permute(A); [experts(A) || permute(B)]; [experts(B) || unpermute(A)]; unpermute(B).
+
+    `compute` runs the expert GEMMs, `comm` the permute/unpermute kernels;
+    each dependency is an event recorded after the producer and waited on by
+    the first consumer only. Both streams must be current-device torch
+    streams; the caller synchronises on both when it needs the outputs.
+    """
+    ev = {k: torch.cuda.Event() for k in ("permA", "permB", "gemmA", "gemmB")}
+    permute(a, E_local, comm)
+    ev["permA"].record(comm)
+    permute(b, E_local, comm)
+    ev["permB"].record(comm)
+    compute.wait_event(ev["permA"])
+    experts(a, W13, W2, compute)
+    ev["gemmA"].record(compute)
+    compute.wait_event(ev["permB"])
+    experts(b, W13, W2, compute)
+    ev["gemmB"].record(compute)
+    comm.wait_event(ev["gemmA"])
+    unpermute(a, comm)
+    comm.wait_event(ev["gemmB"])
+    unpermute(b, comm)

@@ -368,3 +368,32 @@ def test_ep_share_full(dev):
         assert (meta["counts"].cpu().numpy() == mb.counts).all()
         assert (meta["perm"].cpu().numpy() == ref["perm"]).all()
         assert_close(to_f64(out), ref["out"], "bf16", f"ep share seed={mb.seed}")
+
+
+def test_ep_share_two_streams_match_serial(dev):
+    """The two-stream schedule gives bitwise the same outputs as one stream, twice in a row."""
+    from routing_token_permute_amd import ep_share as eps
+
+    ep = make_config("ep_share_bf16")
+    t13 = dev_tensor(ep.bits("W13"), "bf16", dev)
+    t2 = dev_tensor(ep.bits("W2"), "bf16", dev)
+
+    def mbs():
+        return [eps.prepare(eps.MicroBatch(dev_tensor(m.x_bits(), "bf16", dev),
+                                           torch.from_numpy(m.eid.reshape(-1, 1)).to(dev)), ep.E_local, ep.I)
+                for m in ep.micro_batches]
+
+    serial = mbs()
+    eps.run_serial(serial[0], serial[1], t13, t2, ep.E_local, torch.cuda.current_stream(dev))
+    torch.cuda.synchronize()
+    two = mbs()
+    compute, comm = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+    for _ in range(2):
+        for mb in two:
+            mb.out.zero_()
+        torch.cuda.synchronize()
+        eps.run_two_streams(two[0], two[1], t13, t2, ep.E_local, compute, comm)
+        torch.cuda.synchronize()
+        for s_mb, t_mb in zip(serial, two):
+            assert torch.equal(s_mb.out.view(torch.int16), t_mb.out.view(torch.int16))
+            assert torch.equal(s_mb.meta["perm"], t_mb.meta["perm"])

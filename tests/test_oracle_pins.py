@@ -264,6 +264,24 @@ def test_silu_identities():
     assert abs(v - (-3.0 / (1 + math.exp(3.0)) * 2.0)) < 1e-15
 
 
+def test_grouped_gate_up_and_down_match_row_by_row_bruteforce():
+    """Per-segment steps 8 and 9 against per-row loops, with an empty segment."""
+    rng = np.random.default_rng(21)
+    E, H, I, rows = 4, 12, 6, 17  # noqa: E741
+    counts = np.array([5, 0, 9, 3])
+    offsets = oracle.offsets_from_counts(counts)
+    x = rng.standard_normal((rows, H))
+    W13 = rng.standard_normal((E, H, 2 * I)) * 0.3
+    W2 = rng.standard_normal((E, I, H)) * 0.3
+    h = om.grouped_gate_up(x, offsets, W13)
+    y = om.grouped_down(h, offsets, W2)
+    for e in range(E):
+        for r in range(offsets[e], offsets[e + 1]):
+            np.testing.assert_allclose(h[r], brute.gate_up_token(x[r], W13[e]), rtol=1e-13, atol=1e-15)
+            np.testing.assert_allclose(y[r], brute.down_token(h[r], W2[e]), rtol=1e-13, atol=1e-15)
+    assert (h[offsets[-1]:] == 0).all() and (y[offsets[-1]:] == 0).all()
+
+
 def test_grouped_swiglu_matches_layer_segments():
     w = _tiny(E=4, K=2)
     out = oracle.forward(w.x_f32, w.W_gate_f32, w.W13_f32, w.W2_f32, 2, False, keep_permuted=True)
