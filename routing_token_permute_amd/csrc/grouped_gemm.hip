@@ -5,65 +5,81 @@
 // h = silu(gate) * up, Y_e = h @ W2[e].
 //
 // bf16 path (fp32 accumulation on MFMA 16x16x32):
-//   * One workgroup (4 waves, 2x2) per 128x128 output tile; each wave owns
-//     64x64 as 4x4 MFMA tiles. K advances 64 at a time through two LDS
-//     stages: the next slice is fetched into registers while the current
-//     one feeds the MFMAs.
-//   * Row tiles never straddle experts. The tile -> (expert, first row) map
-//     is derived on the device from `offsets` (a wave-wide prefix sum of the
-//     per-expert tile counts), so no host synchronisation is needed and the
-//     grid is sized for the worst split of the rows.
+//   * Output tiles of 256 rows x 256 columns, 8 waves (2 x 4); each wave owns
+//     128 x 64 outputs as 8 x 4 MFMA tiles. Decode-like batches use 32-row
+//     tiles with 4 waves instead.
+//   * Persistent workgroups, one per compute unit, walk a strided list of
+//     tile slots. Row tiles never straddle experts; the slot -> (expert,
+//     rows, column block) map is derived on the device from `offsets` (a
+//     wave-wide prefix sum of the per-expert tile counts), so no host
+//     synchronisation is needed.
+//   * Both operands go straight from HBM into a ring of LDS stages with
+//     global_load_lds_dwordx4 (32-deep k-steps, up to five stages in 160 KB),
+//     each lane fetching the chunk that lands where the swizzled layout
+//     wants it. GEMM1 reads its A rows x[perm[r] / K] in that same copy, so
+//     no permuted copy of the tokens is made.
 //   * The weights stay in the pages' row-major (H, 2I) and (I, H) layouts,
-//     i.e. K-major rows. They are staged in LDS as they come from HBM and
-//     turned into MFMA B operands with the gfx950 LDS transpose read
-//     (ds_read_b64_tr_b16); A rows are K-contiguous and read with 16-byte
-//     LDS loads. Both LDS tiles use XOR swizzles that keep those reads and
-//     the 16-byte stores free of bank conflicts.
-//   * GEMM1 tiles pair 64 gate columns j with the 64 up columns I + j, so a
+//     i.e. K-major rows, and become MFMA operands through the gfx950 LDS
+//     transpose read (ds_read_b64_tr_b16); A rows are K-contiguous and read
+//     with ds_read_b128. Both LDS layouts are XOR-swizzled so those reads run
+//     without bank conflicts.
+//   * GEMM1 tiles pair 128 gate columns j with the 128 up columns I + j, so a
 //     lane holds gate and up of the same output in registers and the SwiGLU
 //     epilogue (fp32, then bf16 round-to-nearest-even) needs no extra pass.
-//     Outputs are staged through LDS and written as 16-byte rows.
+//     Outputs are written straight from registers as 16-byte pieces while
+//     the next tile's first k-steps are already in flight.
 //
 // fp32 path: one thread per output element, fp32 FMA over K. It serves the
 // small fp32 workloads, where launch latency dominates.
 #include <math.h>
+
+#include <algorithm>
 
 #include "moe_internal.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int BN = kGemmBN, BK = kGemmBK;
-constexpr int B_BYTES = BK * BN * 2;      // 32 KB per stage
+constexpr int BN = kGemmBN;
 constexpr int B_ROW = BN * 2;             // bytes per staged k-row of B
-static_assert(BN == 256 && BK == 64, "LDS layouts below assume 256-column, 64-deep stages");
+static_assert(BN == 256, "LDS layouts below assume 256-column stages");
 
-// Stage geometry for a BM-row tile: A is BM x 64 (BM*128 bytes), B is 64 x 256.
-// As many stages as fit in 160 KB of LDS, at most four: BM = 256 gets two
-// (128 KB), BM = 128 three (144 KB), BM = 32 four (144 KB).
-template <int BM>
+constexpr int kMaxStages = 5;
+
+// Stage geometry for a BM-row tile advancing BK (32 or 64) along K: A is
+// BM x BK, B is BK x 256. As many stages as fit in 160 KB of LDS, at most
+// four (two later stages stay in flight while one is multiplied).
+template <int BM, int BK>
 struct TileCfg {
-  static constexpr int A_BYTES = BM * BK * 2;
+  static_assert(BK == 32 || BK == 64, "k-step");
+  static constexpr int A_ROW = BK * 2;  // bytes per staged row of A
+  static constexpr int A_BYTES = BM * A_ROW;
+  static constexpr int B_BYTES = BK * B_ROW;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int FIT = (160 * 1024) / STAGE;
-  static constexpr int NSTAGE = FIT > 4 ? 4 : FIT;
-  static constexpr int EPI_BYTES = BM * 264 * 2;  // staged output tile (GEMM2 is the larger)
-  static constexpr int LDS_BYTES = (NSTAGE * STAGE > EPI_BYTES) ? NSTAGE * STAGE : EPI_BYTES;
+  static constexpr int NSTAGE = FIT > kMaxStages ? kMaxStages : FIT;
+  static constexpr int LDS_BYTES = NSTAGE * STAGE;
   static constexpr int REGIONS = STAGE / 1024;  // 1 KB DMA regions per stage
+  static constexpr int A_ROWS_PER_REGION = 1024 / A_ROW;
 };
 
 // Launch configurations of the bf16 path (BM-row tiles, WM x WN waves):
 // large experts use 256-row tiles with 8 waves; when experts average few
 // rows (decode-like batches) 32-row tiles with a 4-stage ring keep the
 // weight stream deep instead.
-constexpr int kBM = 256, kGemmWM = 2, kGemmWN = 4;
-constexpr int kSmallBM = 32, kSmallWM = 1, kSmallWN = 4;
+constexpr int kBM = 256, kBK = 32, kGemmWM = 2, kGemmWN = 4;
+constexpr int kSmallBM = 32, kSmallBK = 64, kSmallWM = 1, kSmallWN = 4;
 constexpr int kSmallRowsPerExpert = 64;  // rows / E at or below this: small tiles
 
-// A tile: 128 rows x 64 k (128 B per row = 8 chunks of 16 B). Chunk c of row r
-// sits at slot c ^ ((r / 2) % 8): 16 consecutive rows reading the same chunk
-// hit 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int a_off(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+// A tile: BM rows x BK k (2 * BK bytes per row, in 16-byte chunks). Chunk c
+// of row r sits at slot c ^ swz(r), swz(r) = (r / 2) % (chunks per row). With
+// it, the wave-wide ds_read_b128 of one MFMA A operand (16 rows at the same
+// chunk) runs at the full LDS rate of gfx950: 4 cycles per instruction,
+// measured with a per-CU timing probe, where the (r / 4) % 4 form of the
+// 64-byte rows takes 8. The DMA writes of a row are lane-linear and never
+// collide.
+template <int BK>
+__device__ __forceinline__ int a_swz(int row) { return (row >> 1) & (BK / 8 - 1); }
 
 // B tile: 64 k-rows x 256 columns (512 B per row = 32 chunks). Chunk c of row
 // k sits at c ^ f(k), f(k) = 2 * ((k % 4) + 4 * ((k / 8) % 2)): the 32 lanes of
@@ -158,69 +174,87 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) {
 // GATHER: A row r of the expert-major operand is row perm[r] / topk of the
 // token matrix A (n_a rows), i.e. the permutation gather is fused into the
 // HBM -> LDS copy and no permuted copy of the tokens is materialised.
-template <bool GATED, bool GATHER, int BM, int WM, int WN>
+template <bool GATED, bool GATHER, int BM, int BK, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                                     const int32_t* __restrict__ perm, int topk,
                                                                     int n_a, const int32_t* __restrict__ offsets,
                                                                     int E, int rows, int Kdim,
                                                                     const uint16_t* __restrict__ B, int ldb,
                                                                     long long b_expert_stride, int Nout, int up_col,
-                                                                    uint16_t* __restrict__ C, int ldc, int NB) {
-  using Cfg = TileCfg<BM>;
-  constexpr int A_BYTES = Cfg::A_BYTES, STAGE = Cfg::STAGE, NSTAGE = Cfg::NSTAGE;
+                                                                    uint16_t* __restrict__ C, int ldc, int NB,
+                                                                    int n_slots) {
+  using Cfg = TileCfg<BM, BK>;
+  constexpr int A_BYTES = Cfg::A_BYTES, STAGE = Cfg::STAGE, NSTAGE = Cfg::NSTAGE, A_ROW = Cfg::A_ROW;
+  constexpr int KS = BK / 32;              // 32-deep MFMA steps per stage
   constexpr int NW = WM * WN;              // waves
   constexpr int MT = BM / WM / 16;         // 16-row MFMA tiles per wave
   constexpr int NT = BN / WN / 16;         // 16-column MFMA tiles per wave
   constexpr int REG = Cfg::REGIONS / NW;   // 1 KB DMA regions per wave per stage
   constexpr int DMA_PER_STAGE = REG;       // 16-byte loads per thread per stage
-  static_assert(NT % 2 == 0 && MT >= 1 && REG * NW == Cfg::REGIONS, "tile split");
-  static_assert(NSTAGE >= 2 && NSTAGE <= 4 && 2 * DMA_PER_STAGE <= 63, "vmcnt range");
+  constexpr int A_REG = A_BYTES / 1024;    // regions holding A
+  static_assert(NT % (GATED ? 4 : 2) == 0 && MT >= 1 && REG * NW == Cfg::REGIONS, "tile split");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 5 && 4 * DMA_PER_STAGE <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(16))) char smem_raw[Cfg::LDS_BYTES];
   lds_char_t* smem = (lds_char_t*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const Tile t = find_tile<BM>(offsets, E, rows, NB, xcd_remap(blockIdx.x, gridDim.x));
-  if (!t.valid) return;
-  const int mrows = __builtin_amdgcn_readfirstlane(t.r1 - t.r0);
-  const int nb = t.nb;
+  const uint32_t wave_u = wave;
+  const int wm = wave / WN, wn = wave % WN;
+  const int g = lane >> 4, li = lane & 15, rr = li >> 2, cc = li & 3;
+  const int nk = Kdim / BK;
+
+  // Tile slots: this workgroup takes slots blockIdx.x, blockIdx.x + gridDim.x,
+  // ... of the n_slots the worst split of the rows can need; a slot past the
+  // real tile count comes back invalid.
+  int slot_id = blockIdx.x;
+  auto next_tile = [&]() {
+    Tile t{0, 0, 0, 0, false};
+    while (slot_id < n_slots && !t.valid) {
+      t = find_tile<BM>(offsets, E, rows, NB, xcd_remap(slot_id, n_slots));
+      slot_id += gridDim.x;
+    }
+    return t;
+  };
 
   // HBM -> LDS assignment. Each wave-wide DMA fills one 1 KB LDS region in
   // lane order, so the swizzled LDS layout is produced by choosing which
-  // global chunk each lane fetches. Regions [0, BM/8) hold A (8 rows each),
-  // the next 32 regions hold B (2 k-rows each); wave w fills regions
-  // [w*REG, (w+1)*REG). Rows past the tile's last valid row and columns past
-  // Nout fetch a valid row/column instead: they only feed outputs that are
-  // never stored.
-  const uint32_t wave_u = wave;
-  constexpr int A_REG = A_BYTES / 1024;
+  // global chunk each lane fetches. The first A_REG regions hold A
+  // (1024/A_ROW rows each), the rest hold B (2 k-rows each); wave w fills
+  // regions [w*REG, (w+1)*REG). Rows past the tile's last valid row and
+  // columns past Nout fetch a valid row/column instead: they only feed
+  // outputs that are never stored.
   const uint16_t* src[REG];
+  auto set_sources = [&](const Tile& t) {
+    const int mrows = t.r1 - t.r0;
 #pragma unroll
-  for (int j = 0; j < REG; ++j) {
-    const int r = wave * REG + j;
-    if (r < A_REG) {
-      const int row = 8 * r + (lane >> 3);
-      const int c = (lane & 7) ^ ((row >> 1) & 7);
-      int arow = t.r0 + min(row, mrows - 1);
-      if constexpr (GATHER) {
-        const int f = perm[arow];
-        arow = ((unsigned)f < (unsigned)(n_a * topk)) ? f / topk : 0;
-      }
-      src[j] = A + (size_t)arow * Kdim + c * 8;
-    } else {
-      const int k = 2 * (r - A_BYTES / 1024) + (lane >> 5);
-      const int c = (lane & 31) ^ b_swz(k);
-      int col;
-      if constexpr (GATED) {
-        int gc = nb * 128 + (c & 15) * 8;
-        if (gc >= Nout) gc = 0;
-        col = (c < 16) ? gc : up_col + gc;
+    for (int j = 0; j < REG; ++j) {
+      const int r = wave * REG + j;
+      if (r < A_REG) {
+        constexpr int CPR = A_ROW / 16;  // 16-byte chunks per A row
+        const int row = Cfg::A_ROWS_PER_REGION * r + lane / CPR;
+        const int c = (lane % CPR) ^ a_swz<BK>(row);
+        int arow = t.r0 + min(row, mrows - 1);
+        if constexpr (GATHER) {
+          const int f = perm[arow];
+          arow = ((unsigned)f < (unsigned)(n_a * topk)) ? f / topk : 0;
+        }
+        src[j] = A + (size_t)arow * Kdim + c * 8;
       } else {
-        col = nb * 256 + c * 8;
-        if (col >= Nout) col = 0;
+        const int k = 2 * (r - A_REG) + (lane >> 5);
+        const int c = (lane & 31) ^ b_swz(k);
+        int col;
+        if constexpr (GATED) {
+          int gc = t.nb * 128 + (c & 15) * 8;
+          if (gc >= Nout) gc = 0;
+          col = (c < 16) ? gc : up_col + gc;
+        } else {
+          col = t.nb * 256 + c * 8;
+          if (col >= Nout) col = 0;
+        }
+        src[j] = B + (size_t)t.e * b_expert_stride + (size_t)k * ldb + col;
       }
-      src[j] = B + (size_t)t.e * b_expert_stride + (size_t)k * ldb + col;
     }
-  }
+  };
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   auto issue = [&](int kt, int stage) {
     const uint32_t base = lds0 + stage * STAGE + wave_u * REG * 1024;
@@ -228,18 +262,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
 #pragma unroll
     for (int j = 0; j < REG; ++j) {
       const int r = (int)(wave_u * REG + j);
-      // With a 2-stage ring every wait is vmcnt(0), so A regions wholly past
-      // the tile's rows need not be fetched (they are never read).
-      if (NSTAGE == 2 && r < A_REG && 8 * r >= mrows) continue;
       dma16(src[j] + (r < A_REG ? ka : kb), base + j * 1024);
     }
   };
+  auto issue_first = [&]() {
+#pragma unroll
+    for (int p = 0; p < NSTAGE - 1; ++p)
+      if (p < nk) issue(p, p);
+  };
 
-  const int wm = wave / WN, wn = wave % WN;
-  const int g = lane >> 4, li = lane & 15, rr = li >> 2, cc = li & 3;
-  // A operand (MFMA tile mt, k-step ks): row wm*(BM/WM) + mt*16 + li, chunk ks*4 + g.
-  const int a_sw = (li >> 1) & 7;
-  const int a_lane = (wm * (BM / WM) + li) * 128;
+  // A operand (MFMA tile mt, k-step ks): row wm*(BM/WM) + mt*16 + li, chunk
+  // ks*4 + g; the swizzle depends on the lane only.
+  const int a_sw = a_swz<BK>(li);
+  const int a_lane = (wm * (BM / WM) + li) * A_ROW;
   const int a_c0 = (g ^ a_sw) << 4, a_c1 = ((4 + g) ^ a_sw) << 4;
   // B operand (MFMA tile nt, k-step ks, half h): k-row ks*32 + g*8 + h*4 + rr,
   // columns col0(nt) + 4cc..+3; the swizzle depends on the lane only.
@@ -257,121 +292,173 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
   }
 
   f32x4_t acc[MT][NT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  int vm = 0;  // 16-row MFMA slices of this wave holding a valid row (wave-uniform)
 
-  // 16-row MFMA slices of this wave that hold at least one valid row
-  // (wave-uniform); the rest are skipped.
-  const int vm = min(MT, max(0, (mrows - wm * (BM / WM) + 15) / 16));
-
-  // One 64-deep k-step from LDS stage `stage`, as two 32-deep halves. `full`
-  // is a constant at each call site: the branch-free body serves waves whose
-  // row slab is full, the guarded one the partly filled slab of a short tile.
-  auto compute_body = [&](int stage, bool full) {
+  // Operands of one BK-deep k-step, read from LDS stage `stage`, and the
+  // MFMAs over them. `full` is a constant at each call site: the branch-free
+  // form serves waves whose row slab is full, the guarded one the partly
+  // filled slab of a short tile.
+  using AOps = bf16x8_t[KS][MT];
+  using BOps = bf16x8_t[KS][NT];
+  auto load_ops = [&](int stage, bool full, AOps& a, BOps& b) {
     const lds_char_t* As = smem + stage * STAGE;
     const lds_char_t* Bs = As + A_BYTES;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t a[MT], b[NT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        if (full || mt < vm)
-          a[mt] = __builtin_bit_cast(bf16x8_t, lds_read_b128(As + a_lane + mt * 16 * 128 + (ks ? a_c1 : a_c0)));
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const lds_char_t* p = Bs + b_col[nt] + ks * 32 * B_ROW;
         const bf16x4_t lo = lds_read_tr16(p);
         const bf16x4_t hi = lds_read_tr16(p + 4 * B_ROW);
-        b[nt] = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        b[ks][nt] = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        if (full || mt < vm)
+          a[ks][mt] = __builtin_bit_cast(bf16x8_t, lds_read_b128(As + a_lane + mt * 16 * A_ROW + (ks ? a_c1 : a_c0)));
+    }
+  };
+  // The B operand goes first, so each accumulator tile is the transposed
+  // product (see the epilogue).
+  auto mma = [&](bool full, const AOps& a, const BOps& b) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
         if (full || mt < vm) {
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt)
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[ks][nt], a[ks][mt], acc[mt][nt], 0, 0, 0);
         }
-    }
   };
-  // Pipeline over an NSTAGE-deep LDS ring: while k-step kt is multiplied,
-  // k-steps up to kt+NSTAGE-1 are in flight from HBM straight into LDS.
-  // Before the barrier that publishes stage kt, each wave waits until only
-  // its own loads of the later k-steps remain outstanding. The barrier also
-  // guarantees every wave has finished reading k-step kt-1, whose stage the
-  // next issue overwrites.
-  const int nk = Kdim / BK;
+  // Waits until at most `stages` of this wave's later DMA stages are still
+  // in flight (every stage is DMA_PER_STAGE loads per lane). Stores still in
+  // flight from the previous tile only make the wait longer.
+  auto wait_dma = [&](int stages) {
+    if (stages >= 4)
+      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(4 * DMA_PER_STAGE) : "memory");
+    else if (stages == 3)
+      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(3 * DMA_PER_STAGE) : "memory");
+    else if (stages == 2)
+      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(2 * DMA_PER_STAGE) : "memory");
+    else if (stages == 1)
+      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(DMA_PER_STAGE) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+  };
+  // Pipeline over an NSTAGE-deep LDS ring; the first NSTAGE-1 k-steps are
+  // already in flight. While k-step kt is multiplied, k-steps up to
+  // kt+NSTAGE-1 are in flight from HBM straight into LDS. Before the barrier
+  // that publishes stage kt, each wave waits until only its own loads of
+  // later k-steps remain outstanding. The barrier also guarantees that every
+  // wave has finished reading k-step kt-1 (its MFMAs consumed those reads),
+  // whose slot the next issue overwrites.
   auto main_loop = [&](bool full) {
-#pragma unroll
-    for (int p = 0; p < NSTAGE - 1; ++p)
-      if (p < nk) issue(p, p);
-    int stage = 0;
+    int slot = 0;  // ring slot of k-step kt
     for (int kt = 0; kt < nk; ++kt) {
-      // Stages issued after k-step kt and still allowed in flight.
-      const int later = min(NSTAGE - 2, nk - 1 - kt);
-      if (later >= 2)
-        asm volatile("s_waitcnt vmcnt(%0)" : : "n"(2 * DMA_PER_STAGE) : "memory");
-      else if (later == 1)
-        asm volatile("s_waitcnt vmcnt(%0)" : : "n"(DMA_PER_STAGE) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+      wait_dma(min(NSTAGE - 2, nk - 1 - kt));
       __syncthreads();
-      const int nxt = kt + NSTAGE - 1;
-      if (nxt < nk) issue(nxt, stage == 0 ? NSTAGE - 1 : stage - 1);
-      if (full || vm > 0) compute_body(stage, full);
-      stage = (stage == NSTAGE - 1) ? 0 : stage + 1;
+      if (kt + NSTAGE - 1 < nk) issue(kt + NSTAGE - 1, slot == 0 ? NSTAGE - 1 : slot - 1);
+      if (full || vm > 0) {
+        AOps a;
+        BOps b;
+        load_ops(slot, full, a, b);
+        mma(full, a, b);
+      }
+      slot = (slot == NSTAGE - 1) ? 0 : slot + 1;
     }
   };
-  if (vm == MT)
-    main_loop(true);
-  else
-    main_loop(false);
-  __syncthreads();
 
-  // Epilogue: lane (g, li) of MFMA tile (mt, nt) holds rows 4g..4g+3, column li.
-  // Stage the bf16 tile in LDS, then write 16-byte row pieces.
-  uint16_t* Cs = (uint16_t*)smem_raw;
-  if constexpr (GATED) {
-    constexpr int P = 136;  // 128 h columns + 8 pad
+  // Epilogue. Lane (g, li) of accumulator tile (mt, nt) holds output row
+  // mt*16 + li of the wave's slab at the four consecutive columns
+  // col0(nt) + 4g .. +3. Values are rounded to bf16 (nearest even); then the
+  // lanes g and g^1 of each pair of adjacent 16-column tiles swap halves, so
+  // that each lane holds 8 consecutive columns of one tile and writes them
+  // with one 16-byte store straight to HBM (a row's 32 columns of the pair go
+  // out as one 64-byte piece). The stores drain while the next tile is
+  // multiplied.
+  auto pack2 = [](float v0, float v1) {
+    return (uint32_t)f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16);
+  };
+  const bool odd = (g & 1) != 0;
+  // Tiles P (columns colP..colP+15) and Q = P + 16 of one row: pP/pQ are this
+  // lane's packed columns 4g..4g+3 of each. Even g keeps P and receives the
+  // partner's P (columns 4g+4..4g+7); odd g keeps Q and receives the
+  // partner's Q (columns 4g-4..4g-1). All lanes take part in the exchange.
+  auto store_pair = [&](uint16_t* crow, bool ok, int colP, u32x2_t pP, u32x2_t pQ) {
+    const u32x2_t send = odd ? pP : pQ;
+    const u32x2_t got{(uint32_t)__shfl_xor((int)send[0], 16), (uint32_t)__shfl_xor((int)send[1], 16)};
+    if (!ok) return;
+    if (odd)
+      *(u32x4_t*)(crow + colP + 16 + 4 * (g - 1)) = u32x4_t{got[0], got[1], pQ[0], pQ[1]};
+    else
+      *(u32x4_t*)(crow + colP + 4 * g) = u32x4_t{pP[0], pP[1], got[0], got[1]};
+  };
+  auto store_tile = [&](const Tile& t) {
+    const int mrows = t.r1 - t.r0;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if (mt >= vm) continue;
+      const int row = wm * (BM / WM) + mt * 16 + li;
+      const bool row_ok = row < mrows;
+      uint16_t* crow = C + (size_t)(t.r0 + min(row, mrows - 1)) * ldc;
+      if constexpr (GATED) {
+        u32x2_t hp[NT / 2];
+#pragma unroll
+        for (int nt = 0; nt < NT / 2; ++nt) {
+          float hv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float gv = acc[mt][nt][j], uv = acc[mt][nt + NT / 2][j];
+            hv[j] = gv / (1.f + __expf(-gv)) * uv;
+          }
+          hp[nt] = u32x2_t{pack2(hv[0], hv[1]), pack2(hv[2], hv[3])};
+        }
+#pragma unroll
+        for (int q = 0; q < NT / 2; q += 2) {
+          const int colP = t.nb * (BN / 2) + wn * (BN / 2 / WN) + q * 16;
+          store_pair(crow, row_ok && colP < Nout, colP, hp[q], hp[q + 1]);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < NT; q += 2) {
+          const f32x4_t u = acc[mt][q], v = acc[mt][q + 1];
+          const int colP = t.nb * BN + wn * (BN / WN) + q * 16;
+          store_pair(crow, row_ok && colP < Nout, colP, u32x2_t{pack2(u[0], u[1]), pack2(u[2], u[3])},
+                     u32x2_t{pack2(v[0], v[1]), pack2(v[2], v[3])});
+        }
+      }
+    }
+  };
+
+  // Persistent loop over this workgroup's tiles. Before the epilogue of a
+  // tile, the first NSTAGE-1 k-steps of the next one are put in flight (the
+  // barrier after the main loop frees the whole ring), so the DMA of the
+  // next tile and the stores of this one overlap.
+  Tile t = next_tile();
+  if (!t.valid) return;
+  set_sources(t);
+  issue_first();
+  for (;;) {
+    const int mrows = __builtin_amdgcn_readfirstlane(t.r1 - t.r0);
+    vm = min(MT, max(0, (mrows - wm * (BM / WM) + 15) / 16));
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < NT / 2; ++nt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int row = wm * (BM / WM) + mt * 16 + 4 * g + j;
-          const int hc = wn * (BN / 2 / WN) + nt * 16 + li;
-          const float gv = acc[mt][nt][j], uv = acc[mt][nt + NT / 2][j];
-          const float hv = gv / (1.f + __expf(-gv)) * uv;
-          Cs[row * P + hc] = f32_to_bf16(hv);
-        }
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (vm == MT)
+      main_loop(true);
+    else
+      main_loop(false);
     __syncthreads();
-    for (int q = tid; q < BM * 16; q += 64 * NW) {
-      const int row = q >> 4, c = q & 15;
-      const int gc = nb * 128 + c * 8;
-      if (row < mrows && gc < Nout)
-        *(u32x4_t*)(C + (size_t)(t.r0 + row) * ldc + gc) = *(const u32x4_t*)(Cs + row * P + c * 8);
+    const Tile nt_ = next_tile();
+    if (nt_.valid) {
+      set_sources(nt_);
+      issue_first();
     }
-  } else {
-    constexpr int P = 264;  // 256 + 8 pad
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int row = wm * (BM / WM) + mt * 16 + 4 * g + j;
-          const int c = wn * (BN / WN) + nt * 16 + li;
-          Cs[row * P + c] = f32_to_bf16(acc[mt][nt][j]);
-        }
-    __syncthreads();
-    for (int q = tid; q < BM * 32; q += 64 * NW) {
-      const int row = q >> 5, c = q & 31;
-      const int gc = nb * 256 + c * 8;
-      if (row < mrows && gc < Nout)
-        *(u32x4_t*)(C + (size_t)(t.r0 + row) * ldc + gc) = *(const u32x4_t*)(Cs + row * P + c * 8);
-    }
+    store_tile(t);
+    if (!nt_.valid) break;
+    t = nt_;
   }
 }
 
@@ -419,14 +506,30 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 }  // namespace
 
 namespace {
-template <bool GATED, bool GATHER, int BM, int WM, int WN>
+// Compute units of the current device (one persistent workgroup each),
+// looked up once per device.
+int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static int cached[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <bool GATED, bool GATHER, int BM, int BK, int WM, int WN>
 void launch_cfg(const void* a, const int32_t* perm, int topk, int n_a, const int32_t* offsets, int E, int rows,
                 int Kdim, const void* B, int ldb, long long bstride, int Nout, int up_col, void* C, int ldc, int NB,
                 hipStream_t s) {
-  const int mt = max_row_tiles(rows, E, BM);
-  gemm_bf16_kernel<GATED, GATHER, BM, WM, WN><<<mt * NB, 64 * WM * WN, 0, s>>>(
+  const int n_slots = max_row_tiles(rows, E, BM) * NB;
+  const int grid = std::min(n_slots, device_cu_count());
+  gemm_bf16_kernel<GATED, GATHER, BM, BK, WM, WN><<<grid, 64 * WM * WN, 0, s>>>(
       (const uint16_t*)a, perm, topk, n_a, offsets, E, rows, Kdim, (const uint16_t*)B, ldb, bstride, Nout, up_col,
-      (uint16_t*)C, ldc, NB);
+      (uint16_t*)C, ldc, NB, n_slots);
 }
 
 template <bool GATED, bool GATHER>
@@ -434,10 +537,10 @@ void launch_bf16(const void* a, const int32_t* perm, int topk, int n_a, const in
                  int Kdim, const void* B, int ldb, long long bstride, int Nout, int up_col, void* C, int ldc, int NB,
                  hipStream_t s) {
   if ((long long)rows <= (long long)kSmallRowsPerExpert * E)
-    launch_cfg<GATED, GATHER, kSmallBM, kSmallWM, kSmallWN>(a, perm, topk, n_a, offsets, E, rows, Kdim, B, ldb,
+    launch_cfg<GATED, GATHER, kSmallBM, kSmallBK, kSmallWM, kSmallWN>(a, perm, topk, n_a, offsets, E, rows, Kdim, B, ldb,
                                                             bstride, Nout, up_col, C, ldc, NB, s);
   else
-    launch_cfg<GATED, GATHER, kBM, kGemmWM, kGemmWN>(a, perm, topk, n_a, offsets, E, rows, Kdim, B, ldb, bstride,
+    launch_cfg<GATED, GATHER, kBM, kBK, kGemmWM, kGemmWN>(a, perm, topk, n_a, offsets, E, rows, Kdim, B, ldb, bstride,
                                                      Nout, up_col, C, ldc, NB, s);
 }
 
