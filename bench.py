@@ -137,6 +137,26 @@ def _time_region(fn, reps, torch):
     return start.elapsed_time(end) / reps
 
 
+def _time_each(fn, reps, torch, flush=None):
+    """Per-call ms of fn() over `reps` calls, one HIP event pair per call on the
+    current stream; flush() (not timed) runs before each call when given."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        if flush is not None:
+            flush()
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def _pcts(ms):
+    q = np.percentile(np.asarray(ms), [10, 50, 90])
+    return {"p10_ms": round(float(q[0]), 5), "p50_ms": round(float(q[1]), 5), "p90_ms": round(float(q[2]), 5)}
+
+
 def main():
     args = _parse()
     if args.summarize_traffic:
@@ -185,6 +205,8 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = ms_events
     tokens_per_s = n / (ms_per_step * 1e-3)
+    # Spread of single steps (events around each call; not the headline figure).
+    step_spread = _pcts(_time_each(step, max(args.steps, 10), torch))
 
     # ---- per-stage timing: each stage alone, on its own inputs ----
     # The stages moe_forward enqueues, each timed alone on its own inputs.
@@ -203,6 +225,17 @@ def main():
         "gemm2": _time_region(lambda: moe.moe_expert_w2(h, meta["offsets"], W2, Y_perm=Yp), R, torch),
         "combine": _time_region(lambda: moe.moe_unpermute_combine(Yp, meta["inv"], wts, n, K, y=yc), R, torch),
     }
+    # Cold-cache times of the memory-bound stages: a 512 MB buffer is written
+    # before every call so that its inputs are not left in L2 or the 256 MB MALL.
+    junk = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = lambda: junk.fill_(1)  # noqa: E731
+    cold = {
+        "route": _time_each(lambda: moe.moe_route(x, Wg, bias, K, w.renorm, logits=logits, topk_ids=ids, topk_w=wts),
+                            R, torch, flush),
+        "permute": _time_each(lambda: moe.moe_permute(ids, None, E, out=meta), R, torch, flush),
+        "combine": _time_each(lambda: moe.moe_unpermute_combine(Yp, meta["inv"], wts, n, K, y=yc), R, torch, flush),
+    }
+    del junk
     # The standalone row gather of moe_permute (not part of moe_forward).
     meta_x = moe.moe_permute(ids, x, E)
     gather_ms = _time_region(lambda: moe.moe_permute(ids, x, E, out=meta_x), R, torch) - st["permute"]
@@ -227,6 +260,10 @@ def main():
         if k == "gemm2":
             s["TFLOP/s"] = round(flops2 / (ms * 1e-3) / 1e12, 1)
         stages[k] = s
+    for k, v in cold.items():
+        c = _pcts(v)
+        c["GB/s_at_p50"] = round(bytes_[k] / (c["p50_ms"] * 1e-3) / 1e9, 1)
+        stages[k]["cold"] = c
     stages["row_gather_standalone"] = {"ms": round(gather_ms, 5),
                                        "GB/s": round((n * H * 2 + nk * H * 2) / (gather_ms * 1e-3) / 1e9, 1)}
     gg_ms = st["gemm1_swiglu"] + st["gemm2"]
@@ -245,6 +282,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "step_spread": step_spread,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
