@@ -205,6 +205,7 @@ GROUPED_CASES = [
     (2500, 16, 512, 256, "bf16", "random"),
     (130, 5, 64, 64, "f32", "edge"),
     (300, 8, 128, 64, "f32", "random"),
+    (76800, 256, 128, 64, "bf16", "random"),  # E at its maximum, 2 row tiles per expert: >1 tile per workgroup
 ]
 
 
@@ -328,7 +329,7 @@ def test_forward_configs(dev, name):
     assert torch.equal(y.view(torch.int16) if y.dtype == torch.bfloat16 else y, y2.view(torch.int16) if y2.dtype == torch.bfloat16 else y2)
 
 
-@pytest.mark.parametrize("n,H,I,E,K,dtype,renorm", [(1, 64, 64, 8, 2, "bf16", False), (257, 128, 64, 1, 1, "bf16", False), (300, 128, 128, 8, 8, "bf16", True), (100, 64, 64, 16, 1, "f32", False), (45, 256, 192, 32, 4, "bf16", True)])
+@pytest.mark.parametrize("n,H,I,E,K,dtype,renorm", [(1, 64, 64, 8, 2, "bf16", False), (257, 128, 64, 1, 1, "bf16", False), (300, 128, 128, 8, 8, "bf16", True), (100, 64, 64, 16, 1, "f32", False), (45, 256, 192, 32, 4, "bf16", True), (300, 128, 64, 256, 64, "bf16", True)])
 def test_forward_small_shapes(dev, n, H, I, E, K, dtype, renorm):  # noqa: E741
     w = make_layer(n, H, I, E, K, dtype=dtype, renorm=renorm, seed=n + H + I)
     _forward_parity(dev, w, f"forward n={n} E={E} K={K}")
