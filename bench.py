@@ -300,7 +300,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(g1_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": _traffic_bytes(),
+            # The counter summary covers the OLMoE n=4096 workload only.
+            "traffic": _traffic_bytes() if args.workload == "olmoe_bf16" else None,
         },
         "experts_hit": hit,
         "wall_s_timed_region": round(wall, 3),
