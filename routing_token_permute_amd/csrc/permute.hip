@@ -9,7 +9,9 @@
 // (§2.4); the torchtitan `_local_reorder` / `_permute` and the index
 // inversion kernel of "0. goin" (§2.2, §2.3) are the same operation.
 //
-// How: two launches over blocks of P pairs (at most 128 blocks).
+// How: up to 4096 pairs, one workgroup with the ids staged in LDS
+// (permute_single_kernel). Beyond that, two launches over blocks of P pairs
+// (at most 128 blocks):
 //   1. count:  per-block histogram in LDS (integer atomics: the result does
 //              not depend on their order).
 //   2. place:  every block reads all block histograms (a few KB from L2) and
@@ -30,11 +32,10 @@ constexpr int kWaves = kPermThreads / 64;  // 4
 constexpr int kMaxBlocks = kPermMaxBlocks;
 constexpr int kStepBatch = 8;              // 64-pair steps whose ids are loaded together
 
-// Pairs per block: a multiple of 256 (whole 64-pair steps for each of the 4
-// waves), at least 512, and large enough that there are at most kMaxBlocks.
-// Up to 2048 pairs fit one block (8 steps per wave), which needs no count launch.
+// Pairs per block of the count + place launches: a multiple of 256 (whole
+// 64-pair steps for each of the 4 waves), at least 512, and large enough that
+// there are at most kMaxBlocks.
 inline int pairs_per_block(int total) {
-  if (total <= 2048) return 2048;
   int p = ceil_div(ceil_div(total, kMaxBlocks), 256) * 256;
   return p < 512 ? 512 : p;
 }
@@ -78,8 +79,7 @@ __device__ __forceinline__ void wave_sync_lds() {
 // per-expert totals, the exclusive offsets and the number of pairs of each
 // expert in the blocks before it (block 0 also writes counts, offsets and
 // splits); finally each wave walks its quarter in 64-pair steps and places
-// pairs in ascending flat order. With one block, no count launch precedes it
-// (block_counts == NULL) and its own counts are the totals.
+// pairs in ascending flat order.
 __global__ __launch_bounds__(kPermThreads) void permute_place_kernel(const int32_t* __restrict__ ids, int total,
                                                                      int E, int ep, int P, int nblk, int id_bits,
                                                                      const int32_t* __restrict__ block_counts,
@@ -119,22 +119,17 @@ __global__ __launch_bounds__(kPermThreads) void permute_place_kernel(const int32
   }
   __syncthreads();
   // Per-expert totals and the pairs of each expert in earlier blocks (thread e
-  // owns expert e). With a single block (block_counts == NULL) the totals are
-  // this block's own counts.
+  // owns expert e).
   int before = 0, tot = 0;
   if (tid < E) {
-    if (block_counts == nullptr) {
-      for (int w = 0; w < kWaves; ++w) tot += next[w][tid];
-    } else {
-      for (int b0 = 0; b0 < nblk; b0 += 16) {
-        int c[16];
+    for (int b0 = 0; b0 < nblk; b0 += 16) {
+      int c[16];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) c[q] = (b0 + q < nblk) ? block_counts[(size_t)(b0 + q) * E + tid] : 0;
+      for (int q = 0; q < 16; ++q) c[q] = (b0 + q < nblk) ? block_counts[(size_t)(b0 + q) * E + tid] : 0;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          before += (b0 + q < b) ? c[q] : 0;
-          tot += c[q];
-        }
+      for (int q = 0; q < 16; ++q) {
+        before += (b0 + q < b) ? c[q] : 0;
+        tot += c[q];
       }
     }
   }
@@ -200,6 +195,133 @@ __global__ __launch_bounds__(kPermThreads) void permute_place_kernel(const int32
   }
 }
 
+// Up to kSingleMaxPairs pairs: one workgroup of 16 waves does everything with
+// the ids staged in LDS (one round trip to memory). Wave w owns pairs
+// [w * chunk, (w + 1) * chunk) in 64-pair steps. Pass 1 counts them per
+// (wave, expert) with LDS atomic adds by the first lane of each group of
+// same-expert lanes; the per-expert totals, the exclusive offsets and the
+// per-wave starting rows follow; pass 2 repeats the walk, the group leader
+// reserving its group's rows with an atomic add that returns the old count,
+// and every lane placing its pair at leader's old count + its rank among the
+// lower lanes of its group. Each wave's adds to one counter run in program
+// order, so pairs keep ascending flat order inside every expert segment.
+constexpr int kSingleWaves = 16;
+// Up to here one workgroup beats the count + place launches (4 steps per
+// wave; at 32768 pairs the walks take about 37 us against 14 us for them).
+constexpr int kSingleMaxPairs = 4096;
+
+__global__ __launch_bounds__(64 * kSingleWaves) void permute_single_kernel(const int32_t* __restrict__ ids, int total,
+                                                                         int E, int ep, int id_bits,
+                                                                         int32_t* __restrict__ counts,
+                                                                         int32_t* __restrict__ offsets,
+                                                                         int32_t* __restrict__ splits,
+                                                                         int32_t* __restrict__ perm,
+                                                                         int32_t* __restrict__ inv) {
+  __shared__ __attribute__((aligned(16))) int sid[kSingleMaxPairs];
+  __shared__ int cnt[kSingleWaves][kMaxExperts];
+  __shared__ int offs[kMaxExperts + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int i = tid; i < kSingleWaves * kMaxExperts; i += 64 * kSingleWaves) (&cnt[0][0])[i] = 0;
+  // Stage the ids: 16-byte pieces where the source is aligned, the rest one by one.
+  const int vec = ((uintptr_t)ids % 16 == 0) ? total / 4 : 0;
+  {
+    constexpr int kPer = (kSingleMaxPairs / 4 + 64 * kSingleWaves - 1) / (64 * kSingleWaves);  // pieces per thread
+    u32x4_t v[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int c = tid + q * 64 * kSingleWaves;
+      v[q] = (c < vec) ? ((const u32x4_t*)ids)[c] : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int c = tid + q * 64 * kSingleWaves;
+      if (c < vec) *(u32x4_t*)&sid[4 * c] = v[q];
+    }
+    for (int f = 4 * vec + tid; f < total; f += 64 * kSingleWaves) sid[f] = ids[f];
+  }
+  __syncthreads();
+  const int chunk = ((total + kSingleWaves * 64 - 1) / (kSingleWaves * 64)) * 64;
+  const int f0 = wave * chunk, f1 = min(total, f0 + chunk);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // Pass 1: counts per (wave, expert).
+#pragma unroll 4
+  for (int base = f0; base < f1; base += 64) {
+    const int f = base + lane;
+    const int e = (f < f1) ? sid[f] : -1;
+    const bool valid = (unsigned)e < (unsigned)E;
+    const uint64_t same = same_expert_lanes(e, valid, id_bits);
+    if (valid && (same & below) == 0) atomicAdd(&cnt[wave][e], (int)__popcll(same));
+  }
+  __syncthreads();
+  // Totals, exclusive offsets (wave 0: 4 consecutive experts per lane, then a
+  // shuffle scan), and each wave's first row per expert.
+  if (wave == 0) {
+    int t4[4], run = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane * 4 + j;
+      int tt = 0;
+      if (e < E)
+        for (int w = 0; w < kSingleWaves; ++w) tt += cnt[w][e];
+      t4[j] = tt;
+      run += tt;
+    }
+    int incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    int ex = incl - run;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane * 4 + j;
+      if (e < E) {
+        offs[e] = ex;
+        counts[e] = t4[j];
+        offsets[e] = ex;
+      }
+      ex += t4[j];
+    }
+    if (lane == 63) {
+      offs[E] = incl;
+      offsets[E] = incl;
+    }
+  }
+  __syncthreads();
+  if (tid < ep) {
+    const int El = E / ep;
+    splits[tid] = offs[(tid + 1) * El] - offs[tid * El];
+  }
+  if (tid < E) {
+    int run = offs[tid];
+    for (int w = 0; w < kSingleWaves; ++w) {
+      const int c = cnt[w][tid];
+      cnt[w][tid] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  // Pass 2: stable placement.
+#pragma unroll 4
+  for (int base = f0; base < f1; base += 64) {
+    const int f = base + lane;
+    const int e = (f < f1) ? sid[f] : -1;
+    const bool valid = (unsigned)e < (unsigned)E;
+    const uint64_t same = same_expert_lanes(e, valid, id_bits);
+    const int rank = __popcll(same & below);
+    int old = 0;
+    if (valid && rank == 0) old = atomicAdd(&cnt[wave][e], (int)__popcll(same));
+    const int leader = valid ? (__ffsll((long long)same) - 1) : lane;
+    const int pos = __shfl(old, leader) + rank;
+    if (valid) {
+      perm[pos] = f;
+      inv[f] = pos;
+    }
+  }
+}
+
 // No pairs: counts, offsets and splits are all zero.
 __global__ __launch_bounds__(kMaxExperts) void permute_empty_kernel(int E, int ep, int32_t* __restrict__ counts,
                                                                     int32_t* __restrict__ offsets,
@@ -235,10 +357,10 @@ hipError_t launch_permute(const int32_t* topk_ids, const void* x, int n, int H, 
   const int nblk = total > 0 ? ceil_div(total, P) : 0;
   int id_bits = 0;
   while ((1 << id_bits) < E) ++id_bits;
-  if (nblk == 1) {
-    permute_place_kernel<<<1, kPermThreads, 0, s>>>(topk_ids, total, E, ep, P, 1, id_bits, nullptr, counts,
-                                                    offsets, splits, perm, inv);
-  } else if (nblk > 1) {
+  if (total > 0 && total <= kSingleMaxPairs) {
+    permute_single_kernel<<<1, 64 * kSingleWaves, 0, s>>>(topk_ids, total, E, ep, id_bits, counts, offsets, splits,
+                                                          perm, inv);
+  } else if (total > 0) {
     permute_count_kernel<<<nblk, kPermThreads, 0, s>>>(topk_ids, total, E, P, block_counts);
     permute_place_kernel<<<nblk, kPermThreads, 0, s>>>(topk_ids, total, E, ep, P, nblk, id_bits, block_counts,
                                                        counts, offsets, splits, perm, inv);

@@ -125,6 +125,9 @@ PERMUTE_CASES = [
     (777, 64, 8, 1, 1, "one_hot"),  # every pair to one expert
     (3001, 64, 256, 6, 32, "random"),
     (64, 132, 8, 2, 1, "routed_f32"),
+    (5000, 64, 64, 8, 4, "routed"),  # 40000 pairs: past the single-workgroup limit, count + place launches
+    (4096, 64, 8, 8, 1, "one_hot"),  # all 32768 pairs in one segment (count + place launches)
+    (512, 64, 8, 8, 1, "one_hot"),  # 4096 pairs in one segment: the single-workgroup maximum
 ]
 
 
@@ -329,7 +332,7 @@ def test_forward_configs(dev, name):
     assert torch.equal(y.view(torch.int16) if y.dtype == torch.bfloat16 else y, y2.view(torch.int16) if y2.dtype == torch.bfloat16 else y2)
 
 
-@pytest.mark.parametrize("n,H,I,E,K,dtype,renorm", [(1, 64, 64, 8, 2, "bf16", False), (257, 128, 64, 1, 1, "bf16", False), (300, 128, 128, 8, 8, "bf16", True), (100, 64, 64, 16, 1, "f32", False), (45, 256, 192, 32, 4, "bf16", True), (300, 128, 64, 256, 64, "bf16", True)])
+@pytest.mark.parametrize("n,H,I,E,K,dtype,renorm", [(1, 64, 64, 8, 2, "bf16", False), (257, 128, 64, 1, 1, "bf16", False), (300, 128, 128, 8, 8, "bf16", True), (100, 64, 64, 16, 1, "f32", False), (45, 256, 192, 32, 4, "bf16", True), (300, 128, 64, 256, 64, "bf16", True), (4500, 128, 64, 64, 8, "bf16", False)])
 def test_forward_small_shapes(dev, n, H, I, E, K, dtype, renorm):  # noqa: E741
     w = make_layer(n, H, I, E, K, dtype=dtype, renorm=renorm, seed=n + H + I)
     _forward_parity(dev, w, f"forward n={n} E={E} K={K}")
