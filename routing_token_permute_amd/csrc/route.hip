@@ -43,7 +43,7 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 // LDS; one wave, EPL experts per lane (EPL * 64 >= E). `ex` is wave-private
 // LDS scratch of kMaxExperts + kMaxTopK floats.
 template <int EPL>
-__device__ void topk_token(const float* lg, const uint32_t* keys, int E, int K, int renorm, float* ex,
+__device__ __forceinline__ void topk_token(const float* lg, const uint32_t* keys, int E, int K, int renorm, float* ex,
                            int32_t* ids_out, float* w_out) {
   const int lane = lane_id();
   uint32_t mine[EPL];
@@ -100,7 +100,9 @@ __device__ void topk_token(const float* lg, const uint32_t* keys, int E, int K, 
 }
 
 // `scratch`: kMaxExperts + kMaxTopK floats of LDS private to the calling wave.
-__device__ void topk_token_any(const float* lg, const uint32_t* keys, int E, int K, int renorm, float* scratch,
+// Inlined, so that the LDS arrays keep their address space (a call would pass
+// them as generic pointers and read them with flat loads).
+__device__ __forceinline__ void topk_token_any(const float* lg, const uint32_t* keys, int E, int K, int renorm, float* scratch,
                                int32_t* ids, float* w) {
   if (E <= 64)
     topk_token<1>(lg, keys, E, K, renorm, scratch, ids, w);
