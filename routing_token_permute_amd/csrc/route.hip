@@ -40,8 +40,9 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 }
 
 // Softmax + top-K of one token whose E logits (fp32) and order keys sit in
-// LDS; one wave, EPL experts per lane (EPL * 64 >= E). `ex` is wave-private
-// LDS scratch of kMaxExperts + kMaxTopK floats.
+// LDS; one wave, EPL experts per lane (EPL * 64 >= E). `keys` and `ex` (the
+// wave-private LDS scratch of kMaxExperts + kMaxTopK floats) are 16-byte
+// aligned.
 template <int EPL>
 __device__ __forceinline__ void topk_token(const float* lg, const uint32_t* keys, int E, int K, int renorm, float* ex,
                            int32_t* ids_out, float* w_out) {
@@ -54,13 +55,23 @@ __device__ __forceinline__ void topk_token(const float* lg, const uint32_t* keys
     rank[j] = 0;
   }
   uint32_t kmax = 0u;
-#pragma unroll 8
-  for (int f = 0; f < E; ++f) {
-    const uint32_t kf = keys[f];  // same address in every lane: an LDS broadcast
+  auto visit = [&](uint32_t kf, int f) {
     kmax = kf > kmax ? kf : kmax;
 #pragma unroll
     for (int j = 0; j < EPL; ++j) rank[j] += (kf > mine[j]) || (kf == mine[j] && f < lane + 64 * j);
+  };
+  // Four keys per read (the same 16 bytes in every lane: an LDS broadcast).
+  const int E4 = E & ~3;
+  const u32x4_t* k4 = (const u32x4_t*)__builtin_assume_aligned(keys, 16);
+#pragma unroll 4
+  for (int f = 0; f < E4; f += 4) {
+    const u32x4_t kv = k4[f >> 2];
+    visit(kv[0], f);
+    visit(kv[1], f + 1);
+    visit(kv[2], f + 2);
+    visit(kv[3], f + 3);
   }
+  for (int f = E4; f < E; ++f) visit(keys[f], f);
   const float m = key_value(kmax);
   // Each expert's exp(l - m) once, by its own lane; then every lane sums them
   // in expert order, so all lanes hold bitwise the same denominator.
@@ -71,8 +82,16 @@ __device__ __forceinline__ void topk_token(const float* lg, const uint32_t* keys
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   float s = 0.f;
-#pragma unroll 8
-  for (int f = 0; f < E; ++f) s += ex[f];
+  const f32x4_t* x4 = (const f32x4_t*)__builtin_assume_aligned(ex, 16);
+#pragma unroll 4
+  for (int f = 0; f < E4; f += 4) {
+    const f32x4_t v = x4[f >> 2];
+    s += v[0];
+    s += v[1];
+    s += v[2];
+    s += v[3];
+  }
+  for (int f = E4; f < E; ++f) s += ex[f];
   float* slot = ex + kMaxExperts;  // K weights in slot order, for the renorm sum
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
@@ -126,7 +145,7 @@ struct RouteCfg {
   static constexpr int PITCH = EPAD * 2;                  // bytes per staged W_gate row
   static constexpr int SLICE = kSliceRows * PITCH;        // bytes per staged slice
   static constexpr int STAGING = WK * 2 * SLICE;          // per-wave double buffers
-  static constexpr int LPITCH = EPAD + 1;                 // floats per logit row
+  static constexpr int LPITCH = EPAD + 4;                 // floats per logit row (16-byte rows)
   static constexpr int PARTIAL = WK * kTok * EPAD * 4;    // per-wave partial tiles
   static constexpr int LOGITS = kTok * LPITCH * 8;        // logits + order keys
   static constexpr int SLOTS = WK * kScratch * 4;         // top-K scratch, one row per wave
@@ -270,9 +289,9 @@ __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict_
                                                         const float* __restrict__ logits_in, int n, int H, int E,
                                                         int K, int renorm, float* __restrict__ logits,
                                                         int32_t* __restrict__ ids, float* __restrict__ wout) {
-  __shared__ float lg[4][kMaxExperts];
-  __shared__ uint32_t keys[4][kMaxExperts];
-  __shared__ float slots[4][kScratch];
+  __shared__ __attribute__((aligned(16))) float lg[4][kMaxExperts];
+  __shared__ __attribute__((aligned(16))) uint32_t keys[4][kMaxExperts];
+  __shared__ __attribute__((aligned(16))) float slots[4][kScratch];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= n) return;
