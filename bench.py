@@ -225,10 +225,12 @@ def main():
         "gemm2": _time_region(lambda: moe.moe_expert_w2(h, meta["offsets"], W2, Y_perm=Yp), R, torch),
         "combine": _time_region(lambda: moe.moe_unpermute_combine(Yp, meta["inv"], wts, n, K, y=yc), R, torch),
     }
-    # Cold-cache times of the memory-bound stages: a 512 MB buffer is written
-    # before every call so that its inputs are not left in L2 or the 256 MB MALL.
-    junk = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    flush = lambda: junk.fill_(1)  # noqa: E731
+    # Cold-cache times of the memory-bound stages: a 512 MB buffer is read
+    # before every call so that the stage's inputs are not left in L2 or the
+    # 256 MB MALL (a read, so that no dirty lines are written back during the
+    # timed call).
+    junk = torch.zeros((512 << 20) // 4, dtype=torch.float32, device=dev)
+    flush = lambda: junk.sum()  # noqa: E731
     cold = {
         "route": _time_each(lambda: moe.moe_route(x, Wg, bias, K, w.renorm, logits=logits, topk_ids=ids, topk_w=wts),
                             R, torch, flush),

@@ -13,7 +13,11 @@
 namespace moe {
 namespace {
 
-// One workgroup per token; each thread owns 16-byte column chunks.
+// One workgroup per token; each thread owns 16-byte column chunks. The K
+// rows are fetched in batches of kBatch loads in flight per thread, then
+// accumulated in slot order.
+constexpr int kBatch = 8;
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y, const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w, int n, int row_vecs, int K,
@@ -26,20 +30,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y
     float acc[EPV];
 #pragma unroll
     for (int q = 0; q < EPV; ++q) acc[q] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int r = inv[(size_t)i * K + k];
-      if ((unsigned)r >= (unsigned)total) continue;
-      const float wk = (w != nullptr) ? w[(size_t)i * K + k] : 1.f;
-      const u32x4_t v = Yv[(size_t)r * row_vecs + c];
-      if constexpr (BF16) {
+    for (int k0 = 0; k0 < K; k0 += kBatch) {
+      u32x4_t v[kBatch];
+      float wk[kBatch];
+      bool ok[kBatch];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] = fmaf(wk, __uint_as_float(v[q] << 16), acc[2 * q]);
-          acc[2 * q + 1] = fmaf(wk, __uint_as_float(v[q] & 0xFFFF0000u), acc[2 * q + 1]);
+      for (int j = 0; j < kBatch; ++j) {
+        const int k = k0 + j;
+        const int r = (k < K) ? inv[(size_t)i * K + k] : -1;
+        ok[j] = (unsigned)r < (unsigned)total;  // rows out of range add nothing
+        wk[j] = ok[j] ? ((w != nullptr) ? w[(size_t)i * K + k] : 1.f) : 0.f;
+        v[j] = ok[j] ? Yv[(size_t)r * row_vecs + c] : u32x4_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (!ok[j]) continue;
+        if constexpr (BF16) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[2 * q] = fmaf(wk[j], __uint_as_float(v[j][q] << 16), acc[2 * q]);
+            acc[2 * q + 1] = fmaf(wk[j], __uint_as_float(v[j][q] & 0xFFFF0000u), acc[2 * q + 1]);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[q] = fmaf(wk[j], __uint_as_float(v[j][q]), acc[q]);
         }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] = fmaf(wk, __uint_as_float(v[q]), acc[q]);
       }
     }
     u32x4_t out;

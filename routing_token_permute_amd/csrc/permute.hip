@@ -344,7 +344,16 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict
   if ((unsigned)f >= (unsigned)total) return;
   const u32x4_t* src = (const u32x4_t*)x + (size_t)(f / K) * row_vecs;
   u32x4_t* dst = (u32x4_t*)x_perm + (size_t)p * row_vecs;
-  for (int c = lane; c < row_vecs; c += 64) dst[c] = src[c];
+  // Four 16-byte loads in flight per lane, then their stores.
+  int c = lane;
+  for (; c + 192 < row_vecs; c += 256) {
+    const u32x4_t v0 = src[c], v1 = src[c + 64], v2 = src[c + 128], v3 = src[c + 192];
+    dst[c] = v0;
+    dst[c + 64] = v1;
+    dst[c + 128] = v2;
+    dst[c + 192] = v3;
+  }
+  for (; c < row_vecs; c += 64) dst[c] = src[c];
 }
 
 }  // namespace
