@@ -5,9 +5,9 @@
 // h = silu(gate) * up, Y_e = h @ W2[e].
 //
 // bf16 path (fp32 accumulation on MFMA 16x16x32):
-//   * Output tiles of 256 rows x 256 columns, 8 waves (2 x 4); each wave owns
-//     128 x 64 outputs as 8 x 4 MFMA tiles. Decode-like batches use 32-row
-//     tiles with 4 waves instead.
+//   * Output tiles of 256 rows x 256 columns, 16 waves (4 x 4, four per SIMD);
+//     each wave owns 64 x 64 outputs as 4 x 4 MFMA tiles. Decode-like batches
+//     use 32-row tiles with 4 waves instead.
 //   * Persistent workgroups, one per compute unit, walk a strided list of
 //     tile slots. Row tiles never straddle experts; the slot -> (expert,
 //     rows, column block) map is derived on the device from `offsets` (a
@@ -64,10 +64,10 @@ struct TileCfg {
 };
 
 // Launch configurations of the bf16 path (BM-row tiles, WM x WN waves):
-// large experts use 256-row tiles with 8 waves; when experts average few
+// large experts use 256-row tiles with 16 waves; when experts average few
 // rows (decode-like batches) 32-row tiles with a 4-stage ring keep the
 // weight stream deep instead.
-constexpr int kBM = 256, kBK = 32, kGemmWM = 2, kGemmWN = 4;
+constexpr int kBM = 256, kBK = 32, kGemmWM = 4, kGemmWN = 4;
 constexpr int kSmallBM = 32, kSmallBK = 64, kSmallWM = 1, kSmallWN = 4;
 constexpr int kSmallRowsPerExpert = 64;  // rows / E at or below this: small tiles
 
