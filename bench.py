@@ -60,9 +60,17 @@ COPY_BYTES = 1 << 30
 
 
 def _source_hash():
+    """Hash of the GEMM source's code: comment text and blank lines are left out,
+    so that editing a comment does not orphan the counter summary."""
     import hashlib
+    import re
 
-    return hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()[:16]
+    code = []
+    for line in open(GEMM_SOURCE, encoding="utf-8"):
+        line = re.sub(r"//.*", "", line).rstrip()
+        if line:
+            code.append(line)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def _pmc_mean(d, counter, match):

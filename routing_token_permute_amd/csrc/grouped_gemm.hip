@@ -48,7 +48,7 @@ constexpr int kMaxStages = 5;
 
 // Stage geometry for a BM-row tile advancing BK (32 or 64) along K: A is
 // BM x BK, B is BK x 256. As many stages as fit in 160 KB of LDS, at most
-// four (two later stages stay in flight while one is multiplied).
+// kMaxStages (all but one stay in flight while one is multiplied).
 template <int BM, int BK>
 struct TileCfg {
   static_assert(BK == 32 || BK == 64, "k-step");
@@ -81,7 +81,7 @@ constexpr int kSmallRowsPerExpert = 64;  // rows / E at or below this: small til
 template <int BK>
 __device__ __forceinline__ int a_swz(int row) { return (row >> 1) & (BK / 8 - 1); }
 
-// B tile: 64 k-rows x 256 columns (512 B per row = 32 chunks). Chunk c of row
+// B tile: BK k-rows x 256 columns (512 B per row = 32 chunks). Chunk c of row
 // k sits at c ^ f(k), f(k) = 2 * ((k % 4) + 4 * ((k / 8) % 2)): the 32 lanes of
 // one transpose read (8 k-rows x 4 eight-byte pieces) land on 32 distinct
 // 8-byte bank pairs, and 16 lanes storing one row's chunks never collide.
@@ -168,8 +168,8 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) {
 
 // GATED (GEMM1): the 256 staged columns are 128 gate columns followed by the
 // matching 128 up columns; the tile writes 128 columns of h. Otherwise
-// (GEMM2): 256 output columns. WM x WN waves split the 128 x 256 tile; each
-// wave owns (128/WM) rows and (256/WN) staged columns (for GEMM1, half of
+// (GEMM2): 256 output columns. WM x WN waves split the BM x 256 tile; each
+// wave owns (BM/WM) rows and (256/WN) staged columns (for GEMM1, half of
 // them gate and the matching half up).
 // GATHER: A row r of the expert-major operand is row perm[r] / topk of the
 // token matrix A (n_a rows), i.e. the permutation gather is fused into the
