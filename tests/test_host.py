@@ -137,3 +137,15 @@ def test_oracle_is_not_imported_by_the_product():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert "oracle" not in text.replace("the oracle", ""), f
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus N > 1 exits with status 2 and says why, before touching a device."""
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
