@@ -31,4 +31,5 @@ from .moe_oracle import (  # noqa: F401
     splits_by_rank,
     splits_from_offsets,
     topk_margin,
+    weighted_rows_token_order,
 )

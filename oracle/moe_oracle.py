@@ -180,6 +180,21 @@ def expert_ffn(X_e, W13_e, W2_e) -> np.ndarray:
     return expert_gate_up(X_e, W13_e) @ np.asarray(W2_e, dtype=np.float64)
 
 
+def weighted_rows_token_order(Y_perm, inv, w_top, n: int, K: int) -> np.ndarray:
+    """Z[i*K + k] = w_top[i, k] · Y_perm[inv[i*K + k]]; fp64.
+
+    The summands of Algorithm 2 step 11 ([MoE-vLLM] §1.2: each expert output
+    row times its routing weight), laid out in flat pair (token-major) order,
+    which is where the fused second MoE layer of [Fusion] §4.2.5 lands them
+    (gather back to token order and weighting folded into the expert GEMM).
+    Summing each token's K consecutive rows gives combine_slot_order.
+    """
+    Y_perm = np.asarray(Y_perm, dtype=np.float64)
+    inv = np.asarray(inv).reshape(n * K)
+    w = np.asarray(w_top, dtype=np.float64).reshape(n * K)
+    return w[:, None] * Y_perm[inv]
+
+
 def combine_slot_order(Y_perm, inv, w_top, n: int, K: int) -> np.ndarray:
     """y[i] = sum_{k=0..K-1} w_top[i, k] · Y_perm[inv[i*K + k]], k ascending; fp64.
 

@@ -401,3 +401,21 @@ def test_planted_mistakes_are_caught(monkeypatch, golden_dir):
     monkeypatch.setattr(om, "route_from_logits", route_no_softmax)
     assert not _pins_pass(test_layer_matches_per_token_and_dense_bruteforce, 4, 2, False)
     monkeypatch.undo()
+
+
+def test_weighted_rows_token_order_sums_to_the_combine():
+    """[Fusion] §4.2.5's fused second layer only moves Algorithm 2 step 11's summands: each token's K weighted
+    rows, summed, are the slot-order combine; row i*K+k is slot k of token i (its expert row times its weight)."""
+    n, E, K, H = 37, 6, 3, 5
+    rng = np.random.default_rng(11)
+    L = rng.standard_normal((n, E)).astype(np.float32)
+    e_top, w_top, _ = oracle.route_from_logits(L, K, renorm=False)
+    perm, inv = oracle.permutation(e_top, E)
+    Y = rng.standard_normal((n * K, H))
+    Z = oracle.weighted_rows_token_order(Y, inv, w_top, n, K)
+    ref = oracle.combine_slot_order(Y, inv, w_top, n, K)
+    np.testing.assert_allclose(Z.reshape(n, K, H).sum(axis=1), ref, rtol=1e-13, atol=1e-13)
+    for i, k in [(0, 0), (5, 2), (n - 1, 1)]:
+        p = inv[i * K + k]
+        assert perm[p] == i * K + k
+        np.testing.assert_allclose(Z[i * K + k], w_top[i, k] * Y[p], rtol=0, atol=0)
