@@ -1,8 +1,8 @@
 """Benchmark of the MoE expert-layer forward on one MI355X.
 
 One step = one `moe_forward` call (router GEMM, softmax/top-K, counts,
-offsets and permutation with the row gather, grouped SwiGLU GEMM1 and GEMM2,
-weighted combine) over the OLMoE-shaped layer: n=4096 tokens, H=2048,
+offsets and permutation, grouped SwiGLU GEMM1 with the row gather fused,
+GEMM2, weighted combine) over the OLMoE-shaped layer: n=4096 tokens, H=2048,
 I=1024, E=64 experts, top-8, bf16 storage with fp32 accumulation, synthetic
 seeded inputs already resident in HBM.
 
@@ -223,6 +223,10 @@ def main():
     h = moe.moe_expert_w13_swiglu_gather(x, meta["perm"], K, meta["offsets"], W13)
     Yp = moe.moe_expert_w2(h, meta["offsets"], W2)
     yc = moe.moe_unpermute_combine(Yp, meta["inv"], wts, n, K)
+    # The alternative second half (routing weights and un-permutation in
+    # GEMM2's epilogue, then a contiguous sum of each token's K rows).
+    Yt = moe.moe_expert_w2_scatter(h, meta["offsets"], meta["perm"], wts, W2)
+    ys = moe.moe_sum_slots(Yt, n, K)
     torch.cuda.synchronize()
     counts = meta["counts"].cpu().numpy()
     R = args.stage_reps
@@ -232,6 +236,9 @@ def main():
         "gemm1_swiglu": _time_region(lambda: moe.moe_expert_w13_swiglu_gather(x, meta["perm"], K, meta["offsets"], W13, h=h), R, torch),
         "gemm2": _time_region(lambda: moe.moe_expert_w2(h, meta["offsets"], W2, Y_perm=Yp), R, torch),
         "combine": _time_region(lambda: moe.moe_unpermute_combine(Yp, meta["inv"], wts, n, K, y=yc), R, torch),
+        "alt_gemm2_scatter": _time_region(
+            lambda: moe.moe_expert_w2_scatter(h, meta["offsets"], meta["perm"], wts, W2, Y_tok=Yt), R, torch),
+        "alt_slot_sum": _time_region(lambda: moe.moe_sum_slots(Yt, n, K, y=ys), R, torch),
     }
     # Cold-cache times of the memory-bound stages: a 512 MB buffer is read
     # before every call so that the stage's inputs are not left in L2 or the
@@ -260,6 +267,8 @@ def main():
         "gemm1_swiglu": nk * H * 2 + hit * H * 2 * I * 2 + nk * I * 2 + nk * 4,
         "gemm2": nk * I * 2 + hit * I * H * 2 + nk * H * 2,
         "combine": nk * H * 2 + nk * 8 + n * H * 2,
+        "alt_gemm2_scatter": nk * I * 2 + hit * I * H * 2 + nk * H * 2 + nk * 8,
+        "alt_slot_sum": nk * H * 2 + n * H * 2,
     }
     stages = {}
     for k, ms in st.items():
@@ -267,7 +276,7 @@ def main():
         s["frac_hbm"] = round(s["GB/s"] / PEAK_HBM_GBPS, 4)
         if k == "gemm1_swiglu":
             s["TFLOP/s"] = round(flops1 / (ms * 1e-3) / 1e12, 1)
-        if k == "gemm2":
+        if k in ("gemm2", "alt_gemm2_scatter"):
             s["TFLOP/s"] = round(flops2 / (ms * 1e-3) / 1e12, 1)
         stages[k] = s
     for k, v in cold.items():

@@ -177,6 +177,38 @@ moe_status moe_expert_w2(const void* h, const int32_t* offsets, int rows, const 
                          moe_dtype dt, void* Y_perm, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_expert_w2_scatter — Algorithm 2 steps 9-11 with the weight and the
+ * un-permutation in GEMM2's epilogue: the second MoE layer of "大模型系统中的
+ * 通算融合" §4.2.5 (expert GEMM, gather back to token order, weighted top-K
+ * reduce) with its gather and weighting folded into the GEMM, and the output
+ * landing in the layout its consumer reads (§8.5 of the same page):
+ *
+ *   Y_tok[perm[p]] = topk_w[perm[p]] * (h[p] · W2[e])   for every row p of
+ *   expert e's segment, the product accumulated in fp32 and rounded to dt
+ *   after the scaling.
+ *
+ *   h (rows, I) dtype; offsets (E+1) int32; perm (rows) int32 from
+ *   moe_permute (perm[p] = i*K+k, rows = n*K); topk_w (rows) fp32, indexed by
+ *   the flat pair index (the (n, K) routing weights); Y_tok (rows, H) dtype
+ *   out, row i*K+k holding token i's slot k. perm entries outside [0, rows)
+ *   write nothing. No workspace.
+ * ------------------------------------------------------------------------- */
+moe_status moe_expert_w2_scatter(const void* h, const int32_t* offsets, int rows, const int32_t* perm,
+                                 const float* topk_w, const void* W2, int E, int H, int I, moe_dtype dt,
+                                 void* Y_tok, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_sum_slots — the top-K reduction over rows that moe_expert_w2_scatter
+ * already weighted and placed in token order (Algorithm 2 step 11):
+ *
+ *   y[i] = sum_{k=0..K-1} Y_tok[i*K+k]
+ *
+ * in slot order with fp32 accumulation, then stored in dt.
+ *   Y_tok (n*K, H) dtype; y (n, H) dtype out.
+ * ------------------------------------------------------------------------- */
+moe_status moe_sum_slots(const void* Y_tok, int n, int H, int K, moe_dtype dt, void* y, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * moe_unpermute_combine — weighted top-K reduction back to token order
  * (Algorithm 2 steps 10-11, the scatter-add y[i] += Y_e[idx] * w_top[i,k];
  * the `_unpermute` + weighted deterministic scatter-add of "0. goin" §2.2

@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     MoEError,
     load_library,
     moe_expert_w2,
+    moe_expert_w2_scatter,
     moe_expert_w13_swiglu,
     moe_expert_w13_swiglu_gather,
     moe_forward,
@@ -20,6 +21,7 @@ from ._lib import (  # noqa: F401
     moe_grouped_swiglu,
     moe_permute,
     moe_route,
+    moe_sum_slots,
     moe_unpermute_combine,
     status_string,
 )

@@ -37,6 +37,8 @@ SIGNATURES = {
     "moe_expert_w13_swiglu": (_I, [_VP, _VP, _I, _VP, _I, _I, _I, _I, _VP, _VP]),
     "moe_expert_w13_swiglu_gather": (_I, [_VP, _VP, _I, _I, _VP, _VP, _I, _I, _I, _I, _VP, _VP]),
     "moe_expert_w2": (_I, [_VP, _VP, _I, _VP, _I, _I, _I, _I, _VP, _VP]),
+    "moe_expert_w2_scatter": (_I, [_VP, _VP, _I, _VP, _VP, _VP, _I, _I, _I, _I, _VP, _VP]),
+    "moe_sum_slots": (_I, [_VP, _I, _I, _I, _I, _VP, _VP]),
     "moe_unpermute_combine": (_I, [_VP, _VP, _VP, _I, _I, _I, _I, _VP, _VP]),
     "moe_forward_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "moe_forward": (
@@ -278,6 +280,40 @@ def moe_expert_w2(h, offsets, W2, Y_perm=None, stream=None):
     code = lib.moe_expert_w2(_ptr(h), _ptr(offsets), rows, _ptr(W2), E, H, I, _dt(h), _ptr(Y_perm), _stream(dev, stream))
     _check(code, "moe_expert_w2")
     return Y_perm
+
+
+def moe_expert_w2_scatter(h, offsets, perm, topk_w, W2, Y_tok=None, stream=None):
+    """GEMM2 with the weight and un-permutation in its epilogue:
+    Y_tok[perm[p]] = topk_w.flat[perm[p]] * (h[p] W2[e]). topk_w is (n, K) fp32."""
+    lib = load_library()
+    rows, I = h.shape  # noqa: E741
+    E, _, H = W2.shape
+    dev = h.device
+    _need(h, "h", (rows, I))
+    _need(offsets, "offsets", (E + 1,), torch.int32, dev)
+    _need(perm, "perm", (rows,), torch.int32, dev)
+    if topk_w.numel() != rows or topk_w.dtype != torch.float32 or not topk_w.is_contiguous() or topk_w.device != dev:
+        raise MoEError(f"topk_w: expected {rows} contiguous fp32 values on {dev}")
+    _need(W2, "W2", (E, I, H), h.dtype, dev)
+    Y_tok = _empty((rows, H), h.dtype, dev) if Y_tok is None else Y_tok
+    _need(Y_tok, "Y_tok", (rows, H), h.dtype, dev)
+    code = lib.moe_expert_w2_scatter(_ptr(h), _ptr(offsets), rows, _ptr(perm), _ptr(topk_w), _ptr(W2), E, H, I,
+                                     _dt(h), _ptr(Y_tok), _stream(dev, stream))
+    _check(code, "moe_expert_w2_scatter")
+    return Y_tok
+
+
+def moe_sum_slots(Y_tok, n: int, K: int, y=None, stream=None):
+    """y[i] = sum_k Y_tok[i*K+k] in slot order (fp32 accumulation)."""
+    lib = load_library()
+    rows, H = Y_tok.shape
+    dev = Y_tok.device
+    _need(Y_tok, "Y_tok", (n * K, H))
+    y = _empty((n, H), Y_tok.dtype, dev) if y is None else y
+    _need(y, "y", (n, H), Y_tok.dtype, dev)
+    code = lib.moe_sum_slots(_ptr(Y_tok), n, H, K, _dt(Y_tok), _ptr(y), _stream(dev, stream))
+    _check(code, "moe_sum_slots")
+    return y
 
 
 def moe_unpermute_combine(Y_perm, inv, topk_w, n: int, K: int, y=None, stream=None):

@@ -70,7 +70,62 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y
   }
 }
 
+// y[i] = sum_k Y_tok[i*K + k]: the K rows of token i are contiguous (the
+// weighted-scatter GEMM2 already applied the routing weights), summed in slot
+// order in fp32.
+template <bool BF16>
+__global__ __launch_bounds__(256) void sum_slots_kernel(const void* __restrict__ Y, int n, int row_vecs, int K,
+                                                        void* __restrict__ y) {
+  constexpr int EPV = BF16 ? 8 : 4;
+  const int i = blockIdx.x;
+  const u32x4_t* Yv = (const u32x4_t*)Y + (size_t)i * K * row_vecs;
+  for (int c = threadIdx.x; c < row_vecs; c += 256) {
+    float acc[EPV];
+#pragma unroll
+    for (int q = 0; q < EPV; ++q) acc[q] = 0.f;
+    for (int k0 = 0; k0 < K; k0 += kBatch) {
+      u32x4_t v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        v[j] = (k0 + j < K) ? Yv[(size_t)(k0 + j) * row_vecs + c] : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (k0 + j >= K) break;
+        if constexpr (BF16) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[2 * q] += __uint_as_float(v[j][q] << 16);
+            acc[2 * q + 1] += __uint_as_float(v[j][q] & 0xFFFF0000u);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[q] += __uint_as_float(v[j][q]);
+        }
+      }
+    }
+    u32x4_t out;
+    if constexpr (BF16) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        out[q] = (uint32_t)f32_to_bf16(acc[2 * q]) | ((uint32_t)f32_to_bf16(acc[2 * q + 1]) << 16);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) out[q] = __float_as_uint(acc[q]);
+    }
+    ((u32x4_t*)y)[(size_t)i * row_vecs + c] = out;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_sum_slots(const void* Y_tok, int n, int H, int K, moe_dtype dt, void* y, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (dt == MOE_BF16)
+    sum_slots_kernel<true><<<n, 256, 0, s>>>(Y_tok, n, H / 8, K, y);
+  else
+    sum_slots_kernel<false><<<n, 256, 0, s>>>(Y_tok, n, H / 4, K, y);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const void* Y_perm, const int32_t* inv, const float* topk_w, int n, int H, int K,
                           moe_dtype dt, void* y, hipStream_t s) {

@@ -174,10 +174,14 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) {
 // GATHER: A row r of the expert-major operand is row perm[r] / topk of the
 // token matrix A (n_a rows), i.e. the permutation gather is fused into the
 // HBM -> LDS copy and no permuted copy of the tokens is materialised.
-template <bool GATED, bool GATHER, int BM, int BK, int WM, int WN>
+// SCATTER (GEMM2 only): output row r goes to row perm[r] of C (flat pair
+// order, n_a rows) scaled by wrow[perm[r]] before the bf16 rounding, i.e. the
+// routing weight and the un-permutation are fused into the epilogue.
+template <bool GATED, bool GATHER, bool SCATTER, int BM, int BK, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                                     const int32_t* __restrict__ perm, int topk,
-                                                                    int n_a, const int32_t* __restrict__ offsets,
+                                                                    int n_a, const float* __restrict__ wrow,
+                                                                    const int32_t* __restrict__ offsets,
                                                                     int E, int rows, int Kdim,
                                                                     const uint16_t* __restrict__ B, int ldb,
                                                                     long long b_expert_stride, int Nout, int up_col,
@@ -193,6 +197,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
   constexpr int DMA_PER_STAGE = REG;       // 16-byte loads per thread per stage
   constexpr int A_REG = A_BYTES / 1024;    // regions holding A
   static_assert(NT % (GATED ? 4 : 2) == 0 && MT >= 1 && REG * NW == Cfg::REGIONS, "tile split");
+  static_assert(!(SCATTER && (GATED || GATHER)), "the weighted scatter is a GEMM2 epilogue");
   static_assert(NSTAGE >= 2 && NSTAGE <= 5 && 4 * DMA_PER_STAGE <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(16))) char smem_raw[Cfg::LDS_BYTES];
   lds_char_t* smem = (lds_char_t*)smem_raw;
@@ -394,14 +399,34 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
     else
       *(u32x4_t*)(crow + colP + 4 * g) = u32x4_t{pP[0], pP[1], got[0], got[1]};
   };
+  // SCATTER: each lane's destination rows and weights, loaded when the tile
+  // starts so that the epilogue does not wait for them.
+  int sc_row[MT];
+  float sc_w[MT];
+  auto load_scatter = [&](const Tile& t) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int row = wm * (BM / WM) + mt * 16 + li;
+      const int f = perm[t.r0 + min(row, t.r1 - t.r0 - 1)];
+      sc_row[mt] = f;
+      sc_w[mt] = ((unsigned)f < (unsigned)n_a) ? wrow[f] : 0.f;
+    }
+  };
   auto store_tile = [&](const Tile& t) {
     const int mrows = t.r1 - t.r0;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       if (mt >= vm) continue;
       const int row = wm * (BM / WM) + mt * 16 + li;
-      const bool row_ok = row < mrows;
-      uint16_t* crow = C + (size_t)(t.r0 + min(row, mrows - 1)) * ldc;
+      bool row_ok = row < mrows;
+      int crow_i = t.r0 + min(row, mrows - 1);
+      float wr = 1.f;
+      if constexpr (SCATTER) {
+        row_ok = row_ok && (unsigned)sc_row[mt] < (unsigned)n_a;
+        crow_i = row_ok ? sc_row[mt] : 0;
+        wr = sc_w[mt];
+      }
+      uint16_t* crow = C + (size_t)crow_i * ldc;
       if constexpr (GATED) {
         u32x2_t hp[NT / 2];
 #pragma unroll
@@ -422,7 +447,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
       } else {
 #pragma unroll
         for (int q = 0; q < NT; q += 2) {
-          const f32x4_t u = acc[mt][q], v = acc[mt][q + 1];
+          f32x4_t u = acc[mt][q], v = acc[mt][q + 1];
+          if constexpr (SCATTER) {
+            u *= wr;
+            v *= wr;
+          }
           const int colP = t.nb * BN + wn * (BN / WN) + q * 16;
           store_pair(crow, row_ok && colP < Nout, colP, u32x2_t{pack2(u[0], u[1]), pack2(u[2], u[3])},
                      u32x2_t{pack2(v[0], v[1]), pack2(v[2], v[3])});
@@ -440,6 +469,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
   set_sources(t);
   issue_first();
   for (;;) {
+    if constexpr (SCATTER) load_scatter(t);
     const int mrows = __builtin_amdgcn_readfirstlane(t.r1 - t.r0);
     vm = min(MT, max(0, (mrows - wm * (BM / WM) + 15) / 16));
 #pragma unroll
@@ -463,9 +493,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
 }
 
 // fp32: one thread per output element; lanes run along the output columns.
-template <bool GATED, bool GATHER>
+template <bool GATED, bool GATHER, bool SCATTER>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A,
                                                       const int32_t* __restrict__ perm, int topk, int n_a,
+                                                      const float* __restrict__ wrow,
                                                       const int32_t* __restrict__ offsets, int E, int rows,
                                                       int Kdim, const float* __restrict__ B, int ldb,
                                                       long long b_expert_stride, int Nout, int up_col,
@@ -497,10 +528,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
     gsum = fmaf(av, b[(size_t)k * ldb], gsum);
     if constexpr (GATED) usum = fmaf(av, b[(size_t)k * ldb + up_col], usum);
   }
-  if constexpr (GATED)
+  if constexpr (GATED) {
     C[(size_t)row * ldc + col] = gsum / (1.f + expf(-gsum)) * usum;
-  else
+  } else if constexpr (SCATTER) {
+    const int f = perm[row];
+    if ((unsigned)f < (unsigned)n_a) C[(size_t)f * ldc + col] = wrow[f] * gsum;
+  } else {
     C[(size_t)row * ldc + col] = gsum;
+  }
 }
 
 }  // namespace
@@ -521,27 +556,27 @@ int device_cu_count() {
   return cached[dev];
 }
 
-template <bool GATED, bool GATHER, int BM, int BK, int WM, int WN>
-void launch_cfg(const void* a, const int32_t* perm, int topk, int n_a, const int32_t* offsets, int E, int rows,
-                int Kdim, const void* B, int ldb, long long bstride, int Nout, int up_col, void* C, int ldc, int NB,
-                hipStream_t s) {
+template <bool GATED, bool GATHER, bool SCATTER, int BM, int BK, int WM, int WN>
+void launch_cfg(const void* a, const int32_t* perm, int topk, int n_a, const float* wrow, const int32_t* offsets,
+                int E, int rows, int Kdim, const void* B, int ldb, long long bstride, int Nout, int up_col, void* C,
+                int ldc, int NB, hipStream_t s) {
   const int n_slots = max_row_tiles(rows, E, BM) * NB;
   const int grid = std::min(n_slots, device_cu_count());
-  gemm_bf16_kernel<GATED, GATHER, BM, BK, WM, WN><<<grid, 64 * WM * WN, 0, s>>>(
-      (const uint16_t*)a, perm, topk, n_a, offsets, E, rows, Kdim, (const uint16_t*)B, ldb, bstride, Nout, up_col,
-      (uint16_t*)C, ldc, NB, n_slots);
+  gemm_bf16_kernel<GATED, GATHER, SCATTER, BM, BK, WM, WN><<<grid, 64 * WM * WN, 0, s>>>(
+      (const uint16_t*)a, perm, topk, n_a, wrow, offsets, E, rows, Kdim, (const uint16_t*)B, ldb, bstride, Nout,
+      up_col, (uint16_t*)C, ldc, NB, n_slots);
 }
 
-template <bool GATED, bool GATHER>
+template <bool GATED, bool GATHER, bool SCATTER = false>
 void launch_bf16(const void* a, const int32_t* perm, int topk, int n_a, const int32_t* offsets, int E, int rows,
                  int Kdim, const void* B, int ldb, long long bstride, int Nout, int up_col, void* C, int ldc, int NB,
-                 hipStream_t s) {
+                 hipStream_t s, const float* wrow = nullptr) {
   if ((long long)rows <= (long long)kSmallRowsPerExpert * E)
-    launch_cfg<GATED, GATHER, kSmallBM, kSmallBK, kSmallWM, kSmallWN>(a, perm, topk, n_a, offsets, E, rows, Kdim, B, ldb,
-                                                            bstride, Nout, up_col, C, ldc, NB, s);
+    launch_cfg<GATED, GATHER, SCATTER, kSmallBM, kSmallBK, kSmallWM, kSmallWN>(
+        a, perm, topk, n_a, wrow, offsets, E, rows, Kdim, B, ldb, bstride, Nout, up_col, C, ldc, NB, s);
   else
-    launch_cfg<GATED, GATHER, kBM, kBK, kGemmWM, kGemmWN>(a, perm, topk, n_a, offsets, E, rows, Kdim, B, ldb, bstride,
-                                                     Nout, up_col, C, ldc, NB, s);
+    launch_cfg<GATED, GATHER, SCATTER, kBM, kBK, kGemmWM, kGemmWN>(a, perm, topk, n_a, wrow, offsets, E, rows, Kdim, B,
+                                                              ldb, bstride, Nout, up_col, C, ldc, NB, s);
 }
 
 template <bool GATHER>
@@ -553,7 +588,8 @@ hipError_t w13_impl(const void* a, const int32_t* perm, int topk, int n_a, const
                               ceil_div(I, BN / 2), s);
   } else {
     dim3 g1(ceil_div(I, 64), ceil_div(rows, 4));
-    gemm_f32_kernel<true, GATHER><<<g1, 256, 0, s>>>((const float*)a, perm, topk, n_a, offsets, E, rows, H,
+    gemm_f32_kernel<true, GATHER, false><<<g1, 256, 0, s>>>((const float*)a, perm, topk, n_a, nullptr, offsets, E,
+                                                            rows, H,
                                                      (const float*)W13, 2 * I, (long long)H * 2 * I, I, I,
                                                      (float*)h, I);
   }
@@ -579,8 +615,25 @@ hipError_t launch_w2(const void* h, const int32_t* offsets, int rows, const void
                               ceil_div(H, BN), s);
   } else {
     dim3 g2(ceil_div(H, 64), ceil_div(rows, 4));
-    gemm_f32_kernel<false, false><<<g2, 256, 0, s>>>((const float*)h, nullptr, 1, rows, offsets, E, rows, I,
-                                                     (const float*)W2, H, (long long)I * H, H, 0, (float*)Y_perm, H);
+    gemm_f32_kernel<false, false, false><<<g2, 256, 0, s>>>((const float*)h, nullptr, 1, rows, nullptr, offsets, E,
+                                                            rows, I, (const float*)W2, H, (long long)I * H, H, 0,
+                                                            (float*)Y_perm, H);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_w2_scatter(const void* h, const int32_t* offsets, int rows, const int32_t* perm,
+                             const float* topk_w, const void* W2, int E, int H, int I, moe_dtype dt, void* Y_tok,
+                             hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (dt == MOE_BF16) {
+    launch_bf16<false, false, true>(h, perm, 1, rows, offsets, E, rows, I, W2, H, (long long)I * H, H, 0, Y_tok, H,
+                                    ceil_div(H, BN), s, topk_w);
+  } else {
+    dim3 g2(ceil_div(H, 64), ceil_div(rows, 4));
+    gemm_f32_kernel<false, false, true><<<g2, 256, 0, s>>>((const float*)h, perm, 1, rows, topk_w, offsets, E, rows,
+                                                           I, (const float*)W2, H, (long long)I * H, H, 0,
+                                                           (float*)Y_tok, H);
   }
   return hipGetLastError();
 }

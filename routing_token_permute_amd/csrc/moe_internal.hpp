@@ -57,6 +57,13 @@ hipError_t launch_w13_swiglu_gather(const void* x, const int32_t* perm, int n, i
 hipError_t launch_w2(const void* h, const int32_t* offsets, int rows, const void* W2, int E, int H, int I,
                      moe_dtype dt, void* Y_perm, hipStream_t s);
 
+// GEMM2 with the routing weight and the un-permutation in its epilogue:
+// Y_tok[perm[p]] = topk_w[perm[p]] * (h[p] . W2[e(p)]), rows in flat pair order.
+hipError_t launch_w2_scatter(const void* h, const int32_t* offsets, int rows, const int32_t* perm,
+                             const float* topk_w, const void* W2, int E, int H, int I, moe_dtype dt, void* Y_tok,
+                             hipStream_t s);
+// y[i] = sum_k Y_tok[i*K + k] in slot order (fp32 accumulation).
+hipError_t launch_sum_slots(const void* Y_tok, int n, int H, int K, moe_dtype dt, void* y, hipStream_t s);
 hipError_t launch_combine(const void* Y_perm, const int32_t* inv, const float* topk_w, int n, int H, int K,
                           moe_dtype dt, void* y, hipStream_t s);
 

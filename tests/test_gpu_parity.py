@@ -273,6 +273,54 @@ def test_grouped_swiglu_leaves_rows_past_offsets(dev):
 
 
 # ---------------------------------------------------------------------------
+# moe_expert_w2_scatter and moe_sum_slots (GEMM2 with the weighted
+# un-permutation in its epilogue, then the contiguous slot sum)
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("n,H,I,E,K,dtype", [(300, 128, 64, 8, 2, "bf16"), (4096, 2048, 1024, 64, 8, "bf16"), (32, 2048, 1024, 64, 8, "bf16"), (100, 64, 64, 8, 2, "f32"), (513, 192, 128, 16, 4, "bf16")])
+def test_w2_scatter(dev, n, H, I, E, K, dtype):  # noqa: E741
+    w = make_layer(n, H, I, E, K, dtype=dtype, seed=n + 2 * I)
+    _, e_top, w_top = _ids_from_random_logits(n, E, K, seed=n + 1)
+    counts = oracle.expert_counts(e_top, E)
+    offsets = oracle.offsets_from_counts(counts)
+    perm, inv = oracle.permutation(e_top, E)
+    rng = np.random.default_rng(n + 3)
+    if dtype == "bf16":
+        hb, hf = random_bf16_matrix(rng, (n * K, I), std=0.3)
+    else:
+        hf = (0.3 * rng.standard_normal((n * K, I))).astype(np.float32)
+        hb = hf
+    t = layer_tensors(w, dev)
+    w32 = w_top.astype(np.float32)
+    Yt = moe.moe_expert_w2_scatter(dev_tensor(hb, dtype, dev), torch.from_numpy(offsets.astype(np.int32)).to(dev),
+                                   torch.from_numpy(perm.astype(np.int32)).to(dev), torch.from_numpy(w32).to(dev),
+                                   t["W2"])
+    torch.cuda.synchronize()
+    Yp = om.grouped_down(hf, offsets, w.W2_f32)
+    ref = oracle.weighted_rows_token_order(Yp, inv, w32, n, K)
+    assert_close(to_f64(Yt), ref, dtype, f"w2 scatter n={n} E={E} K={K}")
+
+
+@pytest.mark.parametrize("n,H,K,dtype", [(300, 128, 2, "bf16"), (4096, 2048, 8, "bf16"), (64, 132, 3, "f32"), (50, 256, 16, "bf16"), (7, 64, 1, "bf16")])
+def test_sum_slots(dev, n, H, K, dtype):
+    rng = np.random.default_rng(n + K)
+    if dtype == "bf16":
+        yb, yf = random_bf16_matrix(rng, (n * K, H))
+    else:
+        yf = rng.standard_normal((n * K, H)).astype(np.float32)
+        yb = yf
+    y = moe.moe_sum_slots(dev_tensor(yb, dtype, dev), n, K)
+    torch.cuda.synchronize()
+    ref = oracle.combine_slot_order(yf, np.arange(n * K), None, n, K)
+    # Unweighted sums of K unit-variance rows reach |y| ~ 4 sqrt(K): the bf16
+    # rounding of the output is relative, so only the relative bounds apply.
+    assert_close(to_f64(y), ref, dtype, f"slot sum n={n} K={K}", intermediate=True)
+    if K == 1 and dtype == "bf16":  # one slot: an exact copy
+        assert (y.cpu().view(torch.int16).numpy().view(np.uint16) == yb).all()
+
+
+# ---------------------------------------------------------------------------
 # moe_unpermute_combine
 # ---------------------------------------------------------------------------
 

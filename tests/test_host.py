@@ -149,3 +149,20 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_scatter_and_slot_sum_reject_bad_arguments(lib):
+    s = None
+    # null perm / weights with rows > 0
+    assert lib.moe_expert_w2_scatter(P, P, 8, None, P, P, 4, 64, 64, 1, P, s) == EINVAL
+    assert lib.moe_expert_w2_scatter(P, P, 8, P, None, P, 4, 64, 64, 1, P, s) == EINVAL
+    # bf16 sizes not multiples of 64
+    assert lib.moe_expert_w2_scatter(P, P, 8, P, P, P, 4, 96, 64, 1, P, s) == EINVAL
+    # unknown dtype
+    assert lib.moe_expert_w2_scatter(P, P, 8, P, P, P, 4, 64, 64, 9, P, s) == EUNSUP
+    # slot sum: K out of range, null output, bad hidden size
+    assert lib.moe_sum_slots(P, 8, 64, 0, 1, P, s) == EINVAL
+    assert lib.moe_sum_slots(P, 8, 64, 65, 1, P, s) == EINVAL
+    assert lib.moe_sum_slots(P, 8, 64, 2, 1, None, s) == EINVAL
+    assert lib.moe_sum_slots(P, 8, 96, 2, 1, P, s) == EINVAL
+    assert lib.moe_sum_slots(P, 0, 64, 2, 1, None, s) == 0  # n == 0 is a no-op
