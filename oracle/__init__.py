@@ -17,19 +17,27 @@ Pages cited in this package (titles as they appear on the pages):
 """
 
 from .moe_oracle import (  # noqa: F401
+    backward,
+    combine_backward,
     combine_slot_order,
+    dispatch_backward,
     ep_share_forward,
     expert_counts,
     expert_ffn,
     forward,
+    gate_up_preactivations,
+    grouped_data_grad,
     grouped_swiglu,
+    grouped_weight_grad,
     offsets_from_counts,
     permutation,
     round_to_f32,
     route_from_logits,
+    router_backward,
     router_logits,
     splits_by_rank,
     splits_from_offsets,
+    swiglu_backward,
     topk_margin,
     weighted_rows_token_order,
 )

@@ -1,4 +1,4 @@
-"""fp64 CPU oracle of the single-GPU MoE expert-layer forward.
+"""fp64 CPU oracle of the single-GPU MoE expert layer: forward and its gradient.
 
 TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this module; the product path never
@@ -10,7 +10,8 @@ It is the plain definition of what the layer computes, written from
 "Single-GPU MoE Forward". Floating point is fp64 throughout; inputs are the
 exact values the device sees (bf16 or fp32, widened). Library primitives used
 as steps: numpy matmul, exp, sort and nonzero. Nothing is blocked, fused or
-reordered beyond what the definition states.
+reordered beyond what the definition states. The backward at the end of the
+file is the chain rule of that forward, pinned by finite differences.
 
 Readings taken where the pages leave a step open (each is also stated where it
 is used):
@@ -56,7 +57,7 @@ def round_to_f32(a) -> np.ndarray:
     return np.asarray(a, dtype=np.float64).astype(np.float32)
 
 
-def route_from_logits(logits_f32, K: int, renorm: bool):
+def route_from_logits(logits_f32, K: int, renorm: bool, keep_fp64: bool = False):
     """Algorithm 2 steps 2-3: p = softmax(logits); (w_top, e_top) = TopK(p, K).
 
     The router code in [MoE-vLLM] §1.2 takes `torch.topk(router_probs, k=K)`
@@ -64,9 +65,16 @@ def route_from_logits(logits_f32, K: int, renorm: bool):
     The ranking key is the fp32 logit (descending) with ties to the lowest
     expert index; the weights are the fp64 softmax of those fp32 logits.
 
+    `keep_fp64` takes the logits as given (no rounding to fp32): the same
+    definition in exact arithmetic, which the finite-difference check of the
+    gradients needs (rounding the logits to fp32 would swamp a small step).
+
     Returns e_top (n, K) int32, w_top (n, K) fp64, p (n, E) fp64.
     """
-    L = np.asarray(logits_f32, dtype=np.float32).astype(np.float64)
+    if keep_fp64:
+        L = np.asarray(logits_f32, dtype=np.float64)
+    else:
+        L = np.asarray(logits_f32, dtype=np.float32).astype(np.float64)
     n, E = L.shape
     if not 1 <= K <= E:
         raise ValueError(f"K={K} must lie in [1, E={E}]")
@@ -230,13 +238,15 @@ def forward(
     routing_logits_f32=None,
     ep: int = 1,
     keep_permuted: bool = False,
+    fp64_routing: bool = False,
 ):
     """Algorithm 2 of [MoE-vLLM] §1.2, with its dispatch metadata.
 
     Steps 1-3 route (from `routing_logits_f32` when given, else from the fp64
     logits rounded to fp32); steps 4-12 loop over experts e = 0..E-1, skip
     empty ones, gather X_e, run the SwiGLU expert and scatter-add each output
-    row times its weight into y (fp64, starting at zero).
+    row times its weight into y (fp64, starting at zero). `fp64_routing`
+    routes from the fp64 logits themselves (see route_from_logits).
 
     Returns a dict with logits (fp64 or None), logits_f32, e_top, w_top, p,
     counts, offsets, splits, perm, inv, y, and Y_perm (expert-major expert
@@ -248,8 +258,8 @@ def forward(
     logits = None
     if routing_logits_f32 is None:
         logits = router_logits(x, W_gate, bias)
-        routing_logits_f32 = round_to_f32(logits)
-    e_top, w_top, p = route_from_logits(routing_logits_f32, K, renorm)
+        routing_logits_f32 = logits if fp64_routing else round_to_f32(logits)
+    e_top, w_top, p = route_from_logits(routing_logits_f32, K, renorm, keep_fp64=fp64_routing)
 
     counts = expert_counts(e_top, E)
     offsets = offsets_from_counts(counts)
@@ -270,6 +280,7 @@ def forward(
     return dict(
         logits=logits,
         logits_f32=np.asarray(routing_logits_f32, dtype=np.float32),
+        routing_logits=np.asarray(routing_logits_f32, dtype=np.float64 if fp64_routing else np.float32),
         e_top=e_top,
         w_top=w_top,
         p=p,
@@ -344,3 +355,183 @@ def ep_share_forward(x_recv, eid, W13, W2):
     Y_perm = grouped_swiglu(np.asarray(x_recv)[perm], offsets, W13, W2)
     out = combine_slot_order(Y_perm, inv, None, R, 1)
     return dict(counts=counts, offsets=offsets, perm=perm, inv=inv, Y_perm=Y_perm, out=out)
+
+
+# ---------------------------------------------------------------------------
+# Backward: the gradient of the layer above (chain rule, fp64)
+# ---------------------------------------------------------------------------
+#
+# The pages give no formulas for the training backward; they name its pieces:
+# the backward of a dispatch is a combine and the backward of a combine is a
+# dispatch that also yields the routing-score gradient ([Fusion] §6.2.4,
+# [goin] §2.3 (d) and the top-K gradient kernels of its table (e)). What is
+# computed is the plain definition: the derivative of `forward`, with the
+# top-K selection held fixed (it is piecewise constant), written out step by
+# step in the reverse order of Algorithm 2.
+
+
+def gate_up_preactivations(x_perm, offsets, W13) -> np.ndarray:
+    """[gate | up] = X_e · W13[e] for every expert segment of expert-major rows; (rows, 2I) fp64."""
+    x_perm = np.asarray(x_perm, dtype=np.float64)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    out = np.zeros((x_perm.shape[0], np.asarray(W13).shape[2]), dtype=np.float64)
+    for e in range(offsets.size - 1):
+        a, b = offsets[e], offsets[e + 1]
+        if b > a:
+            out[a:b] = x_perm[a:b] @ np.asarray(W13[e], dtype=np.float64)
+    return out
+
+
+def combine_backward(dy, Y_perm, inv, w_top, n: int, K: int):
+    """Gradient of combine_slot_order (the backward of a combine is a dispatch).
+
+    With y[i] = sum_k w[i,k] · Y_perm[inv[iK+k]]:
+      dY_perm[inv[iK+k]] = w[i,k] · dy[i]     (dy sent to each of the token's rows)
+      dw[i,k] = <dy[i], Y_perm[inv[iK+k]]>     (the routing-score gradient)
+    Returns dY_perm (n*K, H) and dw (n, K), fp64.
+    """
+    dy = np.asarray(dy, dtype=np.float64)
+    Y_perm = np.asarray(Y_perm, dtype=np.float64)
+    inv = np.asarray(inv).reshape(n, K)
+    w = np.asarray(w_top, dtype=np.float64).reshape(n, K)
+    dY_perm = np.zeros_like(Y_perm)
+    dw = np.zeros((n, K), dtype=np.float64)
+    for k in range(K):
+        dY_perm[inv[:, k]] = w[:, k : k + 1] * dy
+        dw[:, k] = np.sum(dy * Y_perm[inv[:, k]], axis=1)
+    return dY_perm, dw
+
+
+def dispatch_backward(dX_perm, inv, n: int, K: int) -> np.ndarray:
+    """Gradient of the row gather X_perm[p] = x[perm[p] / K] (the backward of a
+    dispatch is a combine with unit weights): dx[i] = sum_k dX_perm[inv[iK+k]]."""
+    return combine_slot_order(dX_perm, inv, None, n, K)
+
+
+def swiglu_backward(dh, gate_up) -> np.ndarray:
+    """Gradient of h = SiLU(g) · u with respect to [g | u].
+
+    SiLU(g) = g·s with s = 1 / (1 + e^-g), so d SiLU/dg = s · (1 + g·(1 - s)):
+      dg = dh · u · s · (1 + g·(1 - s)),   du = dh · g · s.
+    Returns [dg | du], shape (rows, 2I), fp64.
+    """
+    dh = np.asarray(dh, dtype=np.float64)
+    gu = np.asarray(gate_up, dtype=np.float64)
+    I = gu.shape[1] // 2  # noqa: E741
+    g, u = gu[:, :I], gu[:, I:]
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-g))
+    return np.concatenate([dh * u * s * (1.0 + g * (1.0 - s)), dh * g * s], axis=1)
+
+
+def grouped_data_grad(dout, offsets, W) -> np.ndarray:
+    """Gradient of out_e = in_e · W[e] with respect to in_e: din_e = dout_e · W[e]^T per segment; fp64."""
+    dout = np.asarray(dout, dtype=np.float64)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    W = np.asarray(W)
+    din = np.zeros((dout.shape[0], W.shape[1]), dtype=np.float64)
+    for e in range(offsets.size - 1):
+        a, b = offsets[e], offsets[e + 1]
+        if b > a:
+            din[a:b] = dout[a:b] @ np.asarray(W[e], dtype=np.float64).T
+    return din
+
+
+def grouped_weight_grad(inp, dout, offsets) -> np.ndarray:
+    """Gradient of out_e = in_e · W[e] with respect to W[e]: dW[e] = in_e^T · dout_e.
+
+    An expert with no rows gets a zero gradient. Returns (E, cols(in), cols(dout)) fp64.
+    """
+    inp = np.asarray(inp, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    E = offsets.size - 1
+    dW = np.zeros((E, inp.shape[1], dout.shape[1]), dtype=np.float64)
+    for e in range(E):
+        a, b = offsets[e], offsets[e + 1]
+        if b > a:
+            dW[e] = inp[a:b].T @ dout[a:b]
+    return dW
+
+
+def router_backward(routing_logits, e_top, dw, K: int, renorm: bool, x=None, W_gate=None, keep_fp64: bool = False):
+    """Gradient through Algorithm 2 steps 1-3 given dw = dL/dw_top.
+
+    Top-K picks s[i,k] = p[i, e_top[i,k]] (the selection is held fixed). With
+    renormalisation w = s / S, S = sum_k s, so ds_k = (dw_k - sum_j dw_j w_j) / S;
+    without it ds = dw. The dense dp has ds at the selected experts and zero
+    elsewhere, and the softmax backward gives dlogits = p ⊙ (dp - <p, dp>).
+    The router product logits = x · W_gate + bias then gives
+    dx = dlogits · W_gate^T, dW_gate = x^T · dlogits, dbias = sum_i dlogits[i].
+
+    Returns dict(dlogits (n, E), and when x and W_gate are given dx, dW_gate,
+    dbias), fp64.
+    """
+    e_top = np.asarray(e_top).astype(np.int64)
+    dw = np.asarray(dw, dtype=np.float64)
+    _, w_top, p = route_from_logits(routing_logits, K, renorm, keep_fp64=keep_fp64)
+    if renorm:
+        s = np.take_along_axis(p, e_top, axis=1)
+        S = s.sum(axis=1, keepdims=True)
+        ds = (dw - np.sum(dw * w_top, axis=1, keepdims=True)) / S
+    else:
+        ds = dw
+    dp = np.zeros_like(p)
+    np.put_along_axis(dp, e_top, ds, axis=1)
+    dlogits = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+    out = dict(dlogits=dlogits)
+    if x is not None and W_gate is not None:
+        out["dx"] = dlogits @ np.asarray(W_gate, dtype=np.float64).T
+        out["dW_gate"] = np.asarray(x, dtype=np.float64).T @ dlogits
+        out["dbias"] = dlogits.sum(axis=0)
+    return out
+
+
+def backward(x, W_gate, W13, W2, K: int, renorm: bool, dy, bias=None, fp64_routing: bool = False):
+    """Gradients of the layer's y = forward(...)["y"] for an upstream dy (n, H).
+
+    Steps, in the reverse order of Algorithm 2:
+      1. combine backward: dY_perm, dw (combine_backward);
+      2. GEMM2: dh = dY_perm · W2[e]^T, dW2[e] = h_e^T · dY_e;
+      3. SwiGLU: [dg | du] from dh and the pre-activations (swiglu_backward);
+      4. GEMM1: dX_perm = [dg | du] · W13[e]^T, dW13[e] = X_e^T · [dg | du];
+      5. dispatch backward: dx = sum over each token's rows of dX_perm;
+      6. router: dlogits, and its share of dx, dW_gate and dbias.
+    Returns dict(dx, dW_gate, dbias, dW13, dW2, dlogits, dw, plus the
+    intermediates dY_perm, dgu, dX_perm, gate_up, h, x_perm) in fp64, and the
+    forward dict under "fwd".
+    """
+    x = np.asarray(x)
+    n, H = x.shape
+    f = forward(x, W_gate, W13, W2, K, renorm, bias=bias, keep_permuted=True, fp64_routing=fp64_routing)
+    perm, inv, offsets = f["perm"], f["inv"], f["offsets"]
+    x_perm = np.asarray(x, dtype=np.float64)[perm // K]
+    gate_up = gate_up_preactivations(x_perm, offsets, W13)
+    I = gate_up.shape[1] // 2  # noqa: E741
+    with np.errstate(over="ignore"):
+        h = gate_up[:, :I] / (1.0 + np.exp(-gate_up[:, :I])) * gate_up[:, I:]
+
+    dY_perm, dw = combine_backward(dy, f["Y_perm"], inv, f["w_top"], n, K)
+    dh = grouped_data_grad(dY_perm, offsets, W2)
+    dW2 = grouped_weight_grad(h, dY_perm, offsets)
+    dgu = swiglu_backward(dh, gate_up)
+    dX_perm = grouped_data_grad(dgu, offsets, W13)
+    dW13 = grouped_weight_grad(x_perm, dgu, offsets)
+    dx = dispatch_backward(dX_perm, inv, n, K)
+    r = router_backward(f["routing_logits"], f["e_top"], dw, K, renorm, x=x, W_gate=W_gate, keep_fp64=fp64_routing)
+    return dict(
+        dx=dx + r["dx"],
+        dW_gate=r["dW_gate"],
+        dbias=r["dbias"],
+        dW13=dW13,
+        dW2=dW2,
+        dlogits=r["dlogits"],
+        dw=dw,
+        dY_perm=dY_perm,
+        dgu=dgu,
+        dX_perm=dX_perm,
+        gate_up=gate_up,
+        h=h,
+        x_perm=x_perm,
+        fwd=f,
+    )

@@ -356,7 +356,7 @@ def test_planted_mistakes_are_caught(monkeypatch, golden_dir):
     # 1. Ties to the highest expert index.
     orig_route = om.route_from_logits
 
-    def route_ties_high(L, K, renorm):
+    def route_ties_high(L, K, renorm, keep_fp64=False):
         L = np.asarray(L, np.float32)
         E = L.shape[1]
         e, w, p = orig_route(L[:, ::-1], K, renorm)
@@ -394,8 +394,8 @@ def test_planted_mistakes_are_caught(monkeypatch, golden_dir):
     monkeypatch.undo()
 
     # 4. Weights taken from the logits instead of the softmax.
-    def route_no_softmax(L, K, renorm):
-        e, w, p = orig_route(L, K, renorm)
+    def route_no_softmax(L, K, renorm, keep_fp64=False):
+        e, w, p = orig_route(L, K, renorm, keep_fp64)
         return e, np.take_along_axis(np.asarray(L, np.float64), e.astype(np.int64), 1), p
 
     monkeypatch.setattr(om, "route_from_logits", route_no_softmax)
@@ -419,3 +419,192 @@ def test_weighted_rows_token_order_sums_to_the_combine():
         p = inv[i * K + k]
         assert perm[p] == i * K + k
         np.testing.assert_allclose(Z[i * K + k], w_top[i, k] * Y[p], rtol=0, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# Backward: the gradient of the layer, pinned by finite differences and by
+# the dispatch/combine duality
+# ---------------------------------------------------------------------------
+
+
+def _grad_problem(n=7, H=6, I=4, E=5, K=2, seed=3, bias=True):  # noqa: E741
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, H))
+    W_gate = rng.standard_normal((H, E))
+    b = rng.standard_normal(E) if bias else None
+    W13 = rng.standard_normal((E, H, 2 * I)) * 0.5
+    W2 = rng.standard_normal((E, I, H)) * 0.5
+    dy = rng.standard_normal((n, H))
+    return x, W_gate, b, W13, W2, dy
+
+
+def _fd_check(x, W_gate, b, W13, W2, dy, K, renorm, seed=0, eps=1e-6, tol=2e-7):
+    """Central differences of L = <dy, y> along a random direction per input,
+    against <gradient, direction>; the top-K selection must not move."""
+    g = oracle.backward(x, W_gate, W13, W2, K, renorm, dy, bias=b, fp64_routing=True)
+    e_ref = g["fwd"]["e_top"]
+    params = dict(x=x, W_gate=W_gate, W13=W13, W2=W2)
+    grads = dict(x=g["dx"], W_gate=g["dW_gate"], W13=g["dW13"], W2=g["dW2"])
+    if b is not None:
+        params["bias"], grads["bias"] = b, g["dbias"]
+    rng = np.random.default_rng(seed)
+    for name, val in params.items():
+        V = rng.standard_normal(np.shape(val))
+
+        def loss(sign):
+            p = dict(params)
+            p[name] = val + sign * eps * V
+            f = oracle.forward(p["x"], p["W_gate"], p["W13"], p["W2"], K, renorm, bias=p.get("bias"), fp64_routing=True)
+            assert (f["e_top"] == e_ref).all(), "the step moved the top-K selection"
+            return float(np.sum(dy * f["y"]))
+
+        fd = (loss(+1) - loss(-1)) / (2 * eps)
+        an = float(np.sum(grads[name] * V))
+        assert abs(fd - an) <= tol * (abs(an) + np.sqrt(np.sum(grads[name] ** 2)) * np.sqrt(V.size)), (name, fd, an)
+
+
+@pytest.mark.parametrize("renorm", [False, True])
+@pytest.mark.parametrize("E,K", [(5, 2), (4, 1), (6, 6), (3, 3)])
+def test_backward_matches_finite_differences(E, K, renorm):
+    """Every gradient (x, W_gate, bias, W13, W2) of the fp64 layer agrees with central differences."""
+    _fd_check(*_grad_problem(E=E, K=K, seed=E * 10 + K), K, renorm)
+
+
+def test_backward_finite_differences_per_element():
+    """Single-element differences for a few entries of each input (no averaging over a direction)."""
+    x, W_gate, b, W13, W2, dy = _grad_problem(n=5, H=4, I=3, E=4, K=2, seed=9)
+    g = oracle.backward(x, W_gate, W13, W2, 2, True, dy, bias=b, fp64_routing=True)
+    eps = 1e-6
+
+    def L(**kw):
+        p = dict(x=x, W_gate=W_gate, W13=W13, W2=W2, bias=b)
+        p.update(kw)
+        f = oracle.forward(p["x"], p["W_gate"], p["W13"], p["W2"], 2, True, bias=p["bias"], fp64_routing=True)
+        return float(np.sum(dy * f["y"]))
+
+    for name, val, gr in [("x", x, g["dx"]), ("W_gate", W_gate, g["dW_gate"]), ("W13", W13, g["dW13"]),
+                          ("W2", W2, g["dW2"]), ("bias", b, g["dbias"])]:
+        flat = np.asarray(val).reshape(-1)
+        for j in [0, flat.size // 3, flat.size - 1]:
+            d = np.zeros_like(flat)
+            d[j] = eps
+            fd = (L(**{name: val + d.reshape(val.shape)}) - L(**{name: val - d.reshape(val.shape)})) / (2 * eps)
+            assert abs(fd - gr.reshape(-1)[j]) <= 1e-7 * (1 + abs(fd)), (name, j, fd, gr.reshape(-1)[j])
+
+
+def test_combine_and_dispatch_backward_are_adjoints():
+    """[Fusion] §6.2.4 and [goin] §2.3 (d): the backward of a combine is a dispatch and the backward of a
+    dispatch is a combine. For fixed weights both maps are linear, so each gradient map is the adjoint:
+    <combine(Y), dy> = <Y, combine_backward(dy)>, <gather(x), dX> = <x, dispatch_backward(dX)>; and dw is
+    the derivative of <combine(Y), dy> in w, which is linear too."""
+    rng = np.random.default_rng(4)
+    n, E, K, H = 23, 7, 3, 5
+    L = rng.standard_normal((n, E)).astype(np.float32)
+    e_top, w_top, _ = oracle.route_from_logits(L, K, renorm=False)
+    perm, inv = oracle.permutation(e_top, E)
+    Y = rng.standard_normal((n * K, H))
+    dy = rng.standard_normal((n, H))
+    dY, dw = oracle.combine_backward(dy, Y, inv, w_top, n, K)
+    lhs = np.sum(oracle.combine_slot_order(Y, inv, w_top, n, K) * dy)
+    assert abs(lhs - np.sum(Y * dY)) <= 1e-12 * (1 + abs(lhs))
+    assert abs(lhs - np.sum(w_top * dw)) <= 1e-12 * (1 + abs(lhs))
+    x = rng.standard_normal((n, H))
+    dX = rng.standard_normal((n * K, H))
+    lhs = np.sum(x[perm // K] * dX)
+    assert abs(lhs - np.sum(x * oracle.dispatch_backward(dX, inv, n, K))) <= 1e-12 * (1 + abs(lhs))
+
+
+def test_swiglu_backward_closed_forms():
+    """At g = 0: SiLU'(0) = 1/2 and SiLU(0) = 0, so dg = dh·u/2 and du = 0; for large g, SiLU'(g) -> 1 and
+    SiLU(g) -> g; for very negative g both go to 0."""
+    dh = np.array([[2.0, -3.0, 1.0]])
+    gu = np.array([[0.0, 40.0, -40.0, 5.0, 7.0, 11.0]])
+    d = oracle.swiglu_backward(dh, gu)
+    np.testing.assert_allclose(d[0, :3], [2.0 * 5.0 * 0.5, -3.0 * 7.0 * 1.0, 0.0], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(d[0, 3:], [0.0, -3.0 * 40.0, 0.0], rtol=1e-12, atol=1e-12)
+
+
+def test_router_backward_single_expert_and_dense_cases():
+    """E = K = 1: the softmax of one logit is constant, so the router gradient vanishes. K = E with
+    renormalisation: the weights are the full softmax, and dlogits is the softmax Jacobian applied to dw."""
+    rng = np.random.default_rng(2)
+    n, E = 6, 1
+    r = oracle.router_backward(rng.standard_normal((n, E)), np.zeros((n, 1), np.int32), rng.standard_normal((n, 1)),
+                               1, False, keep_fp64=True)
+    assert np.abs(r["dlogits"]).max() == 0.0
+    E = 4
+    Lg = rng.standard_normal((n, E))
+    e_top, _, p = oracle.route_from_logits(Lg, E, True, keep_fp64=True)
+    dw = rng.standard_normal((n, E))
+    r = oracle.router_backward(Lg, e_top, dw, E, True, keep_fp64=True)
+    dp = np.zeros((n, E))
+    np.put_along_axis(dp, e_top.astype(np.int64), dw, axis=1)
+    for i in range(n):
+        J = np.diag(p[i]) - np.outer(p[i], p[i])  # Jacobian of softmax (symmetric)
+        np.testing.assert_allclose(r["dlogits"][i], J @ dp[i], rtol=1e-12, atol=1e-14)
+
+
+def test_planted_backward_mistakes_are_caught(monkeypatch):
+    prob = _grad_problem(E=5, K=2, seed=52)
+    _fd_check(*prob, 2, True)
+
+    def check():
+        _fd_check(*prob, 2, True)
+
+    # 1. SiLU derivative without its g·(1 - s) term.
+    def swiglu_short(dh, gu):
+        I = gu.shape[1] // 2  # noqa: E741
+        g, u = gu[:, :I], gu[:, I:]
+        s = 1 / (1 + np.exp(-g))
+        return np.concatenate([dh * u * s, dh * g * s], axis=1)
+
+    monkeypatch.setattr(om, "swiglu_backward", swiglu_short)
+    assert not _pins_pass(check)
+    monkeypatch.undo()
+
+    # 2. Softmax backward without the <p, dp> term.
+    orig_rb = om.router_backward
+
+    def router_no_centering(Lg, e_top, dw, K, renorm, x=None, W_gate=None, keep_fp64=False):
+        r = orig_rb(Lg, e_top, dw, K, renorm, x=x, W_gate=W_gate, keep_fp64=keep_fp64)
+        _, _, p = oracle.route_from_logits(Lg, K, renorm, keep_fp64=keep_fp64)
+        dp = np.zeros_like(p)
+        np.put_along_axis(dp, np.asarray(e_top, np.int64), dw, axis=1)
+        r["dlogits"] = p * dp
+        r["dx"] = r["dlogits"] @ np.asarray(W_gate).T
+        r["dW_gate"] = np.asarray(x).T @ r["dlogits"]
+        r["dbias"] = r["dlogits"].sum(0)
+        return r
+
+    monkeypatch.setattr(om, "router_backward", router_no_centering)
+    assert not _pins_pass(check)
+    monkeypatch.undo()
+
+    # 3. Renormalisation ignored in the backward.
+    def router_no_renorm(Lg, e_top, dw, K, renorm, x=None, W_gate=None, keep_fp64=False):
+        return orig_rb(Lg, e_top, dw, K, False, x=x, W_gate=W_gate, keep_fp64=keep_fp64)
+
+    monkeypatch.setattr(om, "router_backward", router_no_renorm)
+    assert not _pins_pass(check)
+    monkeypatch.undo()
+
+    # 4. Weight gradient with the operands the wrong way round (dout^T · in, transposed back).
+    orig_wg = om.grouped_weight_grad
+
+    def wg_swapped(inp, dout, offsets):
+        inp = np.asarray(inp, np.float64)
+        return orig_wg(inp[:, ::-1], dout, offsets)
+
+    monkeypatch.setattr(om, "grouped_weight_grad", wg_swapped)
+    assert not _pins_pass(check)
+    monkeypatch.undo()
+
+    # 5. Combine backward that forgets the routing weight.
+    orig_cb = om.combine_backward
+
+    def cb_unweighted(dy, Y, inv, w, n, K):
+        return orig_cb(dy, Y, inv, np.ones_like(np.asarray(w, np.float64)), n, K)
+
+    monkeypatch.setattr(om, "combine_backward", cb_unweighted)
+    assert not _pins_pass(check)
+    monkeypatch.undo()
