@@ -29,7 +29,7 @@
  *   - Arguments are validated on the host before anything is enqueued:
  *     MOE_EINVAL for null required pointers, negative or zero sizes where a
  *     size must be positive, K outside [1, min(E, 64)], E outside
- *     [1, 1024], ep not dividing E, a workspace smaller than required, or
+ *     [1, 256], ep not dividing E, a workspace smaller than required, or
  *     shapes the kernels do not cover (bf16: H and I multiples of 64;
  *     fp32: H and I multiples of 4); MOE_EUNSUPPORTED for a dtype value
  *     that is not built. Nothing is enqueued when a call returns an error.
@@ -243,6 +243,153 @@ moe_status moe_forward(const void* x, const void* W_gate, const float* bias, con
                        int n, int H, int I, int E, int K, int renorm, moe_dtype dt, void* y, float* logits_out,
                        int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
                        hipStream_t stream);
+
+/* ===========================================================================
+ * Backward (training) pass of the same layer.
+ *
+ * The pages name the pieces of the training backward without formulas: the
+ * backward of a dispatch is a combine, and the backward of a combine is a
+ * dispatch that also yields the routing-score gradient ("大模型系统中的通算
+ * 融合" §6.2.4; "0. goin" §2.3 (d), and its kernel table (e), which lists a
+ * top-K gradient expansion and a routing-score gradient kernel). What is
+ * computed is the gradient of the forward above for an upstream dy, with the
+ * top-K selection held fixed:
+ *
+ *   dY_perm[inv[iK+k]] = w[i,k] dy[i];     dw[i,k] = <dy[i], Y_perm[inv[iK+k]]>
+ *   dh = dY_e · W2[e]^T;                   dW2[e] = h_e^T · dY_e
+ *   dgate = dh * up * s * (1 + gate * (1 - s)),  dup = dh * gate * s,
+ *           s = 1 / (1 + e^-gate)
+ *   dX_e = [dgate | dup] · W13[e]^T;       dW13[e] = X_e^T · [dgate | dup]
+ *   dx[i] = sum_k dX_perm[inv[iK+k]] + dlogits[i] · W_gate^T
+ *   ds = dw, or (dw - <dw, w>) / S with S = sum_k s under renormalisation;
+ *   dp = ds at the selected experts, 0 elsewhere;
+ *   dlogits = p * (dp - <p, dp>);  dW_gate = x^T · dlogits;  dbias = sum_i dlogits
+ *
+ * bf16: every product accumulates in fp32; gradients with the shape of a
+ * bf16 tensor (dx, dY_perm, dgate_up, dX_perm, dW13, dW2) are rounded to bf16
+ * once; the router gradients (dw, dlogits, dW_gate, dbias) stay fp32.
+ * ========================================================================= */
+
+/* ---------------------------------------------------------------------------
+ * moe_expert_w13_swiglu_gather_train — moe_expert_w13_swiglu_gather that also
+ * stores the pre-activations the backward needs.
+ *   gate_up (n*K, 2I) dtype out: [gate | up] = X_e · W13[e] per row, rounded
+ *           to dt (bf16: from the same fp32 accumulators as h).
+ * Other arguments as moe_expert_w13_swiglu_gather.
+ * ------------------------------------------------------------------------- */
+moe_status moe_expert_w13_swiglu_gather_train(const void* x, const int32_t* perm, int n, int K,
+                                              const int32_t* offsets, const void* W13, int E, int H, int I,
+                                              moe_dtype dt, void* h, void* gate_up, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_forward_train — moe_forward that keeps what the backward reads. Every
+ * saved buffer is caller-owned and written:
+ *   logits (n, E) fp32; topk_ids (n, K) int32; topk_w (n, K) fp32;
+ *   offsets (E+1) int32; perm, inv (n*K) int32;
+ *   gate_up (n*K, 2I) dtype; h (n*K, I) dtype; Y_perm (n*K, H) dtype.
+ *   y (n, H) dtype out.
+ *   ws  at least moe_forward_train_workspace_size(n, E, K) bytes (counts,
+ *       splits and the permutation's block counts).
+ * ------------------------------------------------------------------------- */
+size_t moe_forward_train_workspace_size(int n, int E, int K);
+moe_status moe_forward_train(const void* x, const void* W_gate, const float* bias, const void* W13, const void* W2,
+                             int n, int H, int I, int E, int K, int renorm, moe_dtype dt, void* y, float* logits,
+                             int32_t* topk_ids, float* topk_w, int32_t* offsets, int32_t* perm, int32_t* inv,
+                             void* gate_up, void* h, void* Y_perm, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_combine_backward — gradient of moe_unpermute_combine (a dispatch of dy
+ * plus the routing-score gradient):
+ *   dY_perm[inv[i*K+k]] = w[i,k] * dy[i]      (n*K, H) dtype out
+ *   dw[i,k] = <dy[i], Y_perm[inv[i*K+k]]>     (n, K) fp32 out, fp32 sums in a
+ *                                             fixed order
+ *   dy (n, H) dtype; Y_perm (n*K, H) dtype; inv (n*K) int32; topk_w (n, K) fp32.
+ * ------------------------------------------------------------------------- */
+moe_status moe_combine_backward(const void* dy, const void* Y_perm, const int32_t* inv, const float* topk_w, int n,
+                                int H, int K, moe_dtype dt, void* dY_perm, float* dw, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_expert_w2_backward — data gradient through GEMM2 and SwiGLU, per expert
+ * segment of the expert-major rows:
+ *   dh = dY_perm[p] · W2[e]^T, then
+ *   dgate_up[p] = [dh * up * s * (1 + gate*(1 - s)) | dh * gate * s]
+ * with [gate | up] = gate_up[p] (the saved pre-activations).
+ *   dY_perm (rows, H), gate_up (rows, 2I), W2 (E, I, H) dtype;
+ *   dgate_up (rows, 2I) dtype out.
+ * ------------------------------------------------------------------------- */
+moe_status moe_expert_w2_backward(const void* dY_perm, const int32_t* offsets, int rows, const void* W2,
+                                  const void* gate_up, int E, int H, int I, moe_dtype dt, void* dgate_up,
+                                  hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_expert_w13_backward — data gradient through GEMM1:
+ *   dX_perm[p] = dgate_up[p] · W13[e]^T     (rows, H) dtype out
+ *   dgate_up (rows, 2I), W13 (E, H, 2I) dtype.
+ * ------------------------------------------------------------------------- */
+moe_status moe_expert_w13_backward(const void* dgate_up, const int32_t* offsets, int rows, const void* W13, int E,
+                                   int H, int I, moe_dtype dt, void* dX_perm, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_expert_weight_grad — weight gradient of a grouped product
+ * out_e = a_e · W[e], contracted over each expert's rows:
+ *   dW[e] = a[offsets[e]:offsets[e+1]]^T · b[offsets[e]:offsets[e+1]]
+ *   a (rows, M), b (rows, N) dtype; dW (E, M, N) dtype out. An expert with no
+ *   rows gets zeros. dW2 is (a, b) = (h, dY_perm) with (M, N) = (I, H); dW13
+ *   is (x_perm, dgate_up) with (H, 2I). M and N follow the rules for H.
+ * ------------------------------------------------------------------------- */
+moe_status moe_expert_weight_grad(const void* a, const void* b, const int32_t* offsets, int rows, int E, int M, int N,
+                                  moe_dtype dt, void* dW, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_dispatch_backward — gradient of the row gather x_perm[p] = x[perm[p]/K]
+ * (a combine with unit weights), plus an optional fp32 addend:
+ *   dx[i] = add[i] + sum_{k=0..K-1} dX_perm[inv[i*K+k]]
+ * summed in fp32 (add first, then slot order) and rounded once.
+ *   dX_perm (n*K, H) dtype; inv (n*K) int32; add (n, H) fp32 or NULL;
+ *   dx (n, H) dtype out.
+ * ------------------------------------------------------------------------- */
+moe_status moe_dispatch_backward(const void* dX_perm, const int32_t* inv, const float* add, int n, int H, int K,
+                                 moe_dtype dt, void* dx, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_route_backward — gradient through routing (top-K weights, softmax and
+ * the router product) given dw = dL/dtopk_w:
+ *   dlogits (n, E) fp32 out (always);
+ *   dx_router (n, H) fp32 out = dlogits · W_gate^T, or NULL to skip;
+ *   dW_gate (H, E) fp32 out = x^T · dlogits, or NULL;
+ *   dbias (E) fp32 out = sum_i dlogits[i], or NULL.
+ *   x (n, H), W_gate (H, E) dtype (x unused when dW_gate and dbias are NULL;
+ *   W_gate unused when dx_router is NULL; H is only checked when one of
+ *   dx_router, dW_gate, dbias is wanted); logits (n, E) fp32 as written by
+ *   moe_route; topk_ids, topk_w (n, K) as written by moe_route; dw (n, K) fp32.
+ *   The softmax is recomputed from the logits in fp32. dW_gate and dbias sum
+ *   over at most 32 token chunks in a fixed order.
+ *   ws  moe_route_backward_workspace_size(n, H, E) bytes (0 when dW_gate and
+ *       dbias are NULL: ws may then be NULL).
+ * ------------------------------------------------------------------------- */
+size_t moe_route_backward_workspace_size(int n, int H, int E);
+moe_status moe_route_backward(const void* x, const void* W_gate, const float* logits, const int32_t* topk_ids,
+                              const float* topk_w, const float* dw, int n, int H, int E, int K, int renorm,
+                              moe_dtype dt, float* dlogits, float* dx_router, float* dW_gate, float* dbias, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_backward — the whole layer's backward on one stream: combine backward,
+ * route backward, GEMM2 + SwiGLU data gradient, dW2, GEMM1 data gradient,
+ * dispatch backward (with the router's share of dx), row gather of x, dW13.
+ *   dy (n, H) dtype; x, W_gate, W13, W2 as given to moe_forward_train;
+ *   logits ... Y_perm: the buffers moe_forward_train saved;
+ *   dx (n, H) dtype out; dW_gate (H, E) fp32 out; dbias (E) fp32 out or NULL;
+ *   dW13 (E, H, 2I), dW2 (E, I, H) dtype out.
+ *   ws  at least moe_backward_workspace_size(...) bytes.
+ * ------------------------------------------------------------------------- */
+size_t moe_backward_workspace_size(int n, int H, int I, int E, int K, moe_dtype dt);
+moe_status moe_backward(const void* dy, const void* x, const void* W_gate, const void* W13, const void* W2, int n,
+                        int H, int I, int E, int K, int renorm, moe_dtype dt, const float* logits,
+                        const int32_t* topk_ids, const float* topk_w, const int32_t* offsets, const int32_t* perm,
+                        const int32_t* inv, const void* gate_up, const void* h, const void* Y_perm, void* dx,
+                        float* dW_gate, float* dbias, void* dW13, void* dW2, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
 
 #ifdef __cplusplus
 } /* extern "C" */

@@ -45,6 +45,29 @@ SIGNATURES = {
         _I,
         [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     ),
+    "moe_expert_w13_swiglu_gather_train": (_I, [_VP, _VP, _I, _I, _VP, _VP, _I, _I, _I, _I, _VP, _VP, _VP]),
+    "moe_forward_train_workspace_size": (_SZ, [_I, _I, _I]),
+    "moe_forward_train": (
+        _I,
+        [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+         _VP, _SZ, _VP],
+    ),
+    "moe_combine_backward": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _I, _VP, _VP, _VP]),
+    "moe_expert_w2_backward": (_I, [_VP, _VP, _I, _VP, _VP, _I, _I, _I, _I, _VP, _VP]),
+    "moe_expert_w13_backward": (_I, [_VP, _VP, _I, _VP, _I, _I, _I, _I, _VP, _VP]),
+    "moe_expert_weight_grad": (_I, [_VP, _VP, _VP, _I, _I, _I, _I, _I, _VP, _VP]),
+    "moe_dispatch_backward": (_I, [_VP, _VP, _VP, _I, _I, _I, _I, _VP, _VP]),
+    "moe_route_backward_workspace_size": (_SZ, [_I, _I, _I]),
+    "moe_route_backward": (
+        _I,
+        [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    ),
+    "moe_backward_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "moe_backward": (
+        _I,
+        [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+         _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    ),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -369,3 +392,240 @@ def moe_forward(x, W_gate, W13, W2, K: int, renorm: bool, bias=None, y=None, ws=
     )
     _check(code, "moe_forward")
     return (y, *extra) if routing_out else y
+
+
+# ---------------------------------------------------------------------------
+# Backward (training) entry points
+# ---------------------------------------------------------------------------
+
+
+def moe_expert_w13_swiglu_gather_train(x, perm, K, offsets, W13, h=None, gate_up=None, stream=None):
+    """moe_expert_w13_swiglu_gather that also writes the pre-activations [gate | up].
+
+    Returns (h (n*K, I), gate_up (n*K, 2I))."""
+    lib = load_library()
+    n, H = x.shape
+    E, _, I2 = W13.shape
+    I = I2 // 2  # noqa: E741
+    dev = x.device
+    _need(x, "x", (n, H))
+    _need(perm, "perm", (n * K,), torch.int32, dev)
+    _need(offsets, "offsets", (E + 1,), torch.int32, dev)
+    _need(W13, "W13", (E, H, 2 * I), x.dtype, dev)
+    h = _empty((n * K, I), x.dtype, dev) if h is None else h
+    gate_up = _empty((n * K, 2 * I), x.dtype, dev) if gate_up is None else gate_up
+    _need(h, "h", (n * K, I), x.dtype, dev)
+    _need(gate_up, "gate_up", (n * K, 2 * I), x.dtype, dev)
+    code = lib.moe_expert_w13_swiglu_gather_train(
+        _ptr(x), _ptr(perm), n, K, _ptr(offsets), _ptr(W13), E, H, I, _dt(x), _ptr(h), _ptr(gate_up),
+        _stream(dev, stream),
+    )
+    _check(code, "moe_expert_w13_swiglu_gather_train")
+    return h, gate_up
+
+
+def moe_forward_train(x, W_gate, W13, W2, K: int, renorm: bool, bias=None, saved=None, y=None, ws=None, stream=None):
+    """The layer's forward keeping what moe_backward reads.
+
+    Returns (y, saved) where saved is a dict of logits, topk_ids, topk_w,
+    offsets, perm, inv, gate_up, h, Y_perm (preallocated ones may be passed in
+    `saved`)."""
+    lib = load_library()
+    n, H = x.shape
+    E = W_gate.shape[1]
+    I = W13.shape[2] // 2  # noqa: E741
+    dev, dt_t = x.device, x.dtype
+    _need(x, "x", (n, H))
+    _need(W_gate, "W_gate", (H, E), dt_t, dev)
+    _need(W13, "W13", (E, H, 2 * I), dt_t, dev)
+    _need(W2, "W2", (E, I, H), dt_t, dev)
+    if bias is not None:
+        _need(bias, "bias", (E,), torch.float32, dev)
+    shapes = dict(
+        logits=((n, E), torch.float32), topk_ids=((n, K), torch.int32), topk_w=((n, K), torch.float32),
+        offsets=((E + 1,), torch.int32), perm=((n * K,), torch.int32), inv=((n * K,), torch.int32),
+        gate_up=((n * K, 2 * I), dt_t), h=((n * K, I), dt_t), Y_perm=((n * K, H), dt_t),
+    )
+    saved = dict(saved or {})
+    for name, (shape, dtype) in shapes.items():
+        saved.setdefault(name, _empty(shape, dtype, dev))
+        _need(saved[name], name, shape, dtype, dev)
+    y = _empty((n, H), dt_t, dev) if y is None else y
+    _need(y, "y", (n, H), dt_t, dev)
+    ws = _workspace(lib.moe_forward_train_workspace_size(n, E, K), dev, ws)
+    code = lib.moe_forward_train(
+        _ptr(x), _ptr(W_gate), _ptr(bias), _ptr(W13), _ptr(W2), n, H, I, E, K, int(bool(renorm)), _dt(x), _ptr(y),
+        *[_ptr(saved[k]) for k in shapes], _ptr(ws), ws.numel(), _stream(dev, stream),
+    )
+    _check(code, "moe_forward_train")
+    return y, saved
+
+
+def moe_combine_backward(dy, Y_perm, inv, topk_w, n: int, K: int, dY_perm=None, dw=None, stream=None):
+    """dY_perm[inv[iK+k]] = w[i,k] dy[i] and dw[i,k] = <dy[i], Y_perm[inv[iK+k]]>. Returns (dY_perm, dw)."""
+    lib = load_library()
+    H = dy.shape[1]
+    dev = dy.device
+    _need(dy, "dy", (n, H))
+    _need(Y_perm, "Y_perm", (n * K, H), dy.dtype, dev)
+    _need(inv, "inv", (n * K,), torch.int32, dev)
+    _need(topk_w, "topk_w", (n, K), torch.float32, dev)
+    dY_perm = _empty((n * K, H), dy.dtype, dev) if dY_perm is None else dY_perm
+    dw = _empty((n, K), torch.float32, dev) if dw is None else dw
+    _need(dY_perm, "dY_perm", (n * K, H), dy.dtype, dev)
+    _need(dw, "dw", (n, K), torch.float32, dev)
+    code = lib.moe_combine_backward(_ptr(dy), _ptr(Y_perm), _ptr(inv), _ptr(topk_w), n, H, K, _dt(dy), _ptr(dY_perm),
+                                    _ptr(dw), _stream(dev, stream))
+    _check(code, "moe_combine_backward")
+    return dY_perm, dw
+
+
+def moe_expert_w2_backward(dY_perm, offsets, W2, gate_up, dgate_up=None, stream=None):
+    """dgate_up = SwiGLU'(gate_up) applied to dY_perm W2[e]^T per expert segment."""
+    lib = load_library()
+    rows, H = dY_perm.shape
+    E, I, _ = W2.shape  # noqa: E741
+    dev = dY_perm.device
+    _need(dY_perm, "dY_perm", (rows, H))
+    _need(offsets, "offsets", (E + 1,), torch.int32, dev)
+    _need(W2, "W2", (E, I, H), dY_perm.dtype, dev)
+    _need(gate_up, "gate_up", (rows, 2 * I), dY_perm.dtype, dev)
+    dgate_up = _empty((rows, 2 * I), dY_perm.dtype, dev) if dgate_up is None else dgate_up
+    _need(dgate_up, "dgate_up", (rows, 2 * I), dY_perm.dtype, dev)
+    code = lib.moe_expert_w2_backward(_ptr(dY_perm), _ptr(offsets), rows, _ptr(W2), _ptr(gate_up), E, H, I,
+                                      _dt(dY_perm), _ptr(dgate_up), _stream(dev, stream))
+    _check(code, "moe_expert_w2_backward")
+    return dgate_up
+
+
+def moe_expert_w13_backward(dgate_up, offsets, W13, dX_perm=None, stream=None):
+    """dX_perm = dgate_up W13[e]^T per expert segment."""
+    lib = load_library()
+    rows, I2 = dgate_up.shape
+    E, H, _ = W13.shape
+    I = I2 // 2  # noqa: E741
+    dev = dgate_up.device
+    _need(dgate_up, "dgate_up", (rows, 2 * I))
+    _need(offsets, "offsets", (E + 1,), torch.int32, dev)
+    _need(W13, "W13", (E, H, 2 * I), dgate_up.dtype, dev)
+    dX_perm = _empty((rows, H), dgate_up.dtype, dev) if dX_perm is None else dX_perm
+    _need(dX_perm, "dX_perm", (rows, H), dgate_up.dtype, dev)
+    code = lib.moe_expert_w13_backward(_ptr(dgate_up), _ptr(offsets), rows, _ptr(W13), E, H, I, _dt(dgate_up),
+                                       _ptr(dX_perm), _stream(dev, stream))
+    _check(code, "moe_expert_w13_backward")
+    return dX_perm
+
+
+def moe_expert_weight_grad(a, b, offsets, dW=None, stream=None):
+    """dW[e] = a[seg e]^T b[seg e] over each expert's rows. Returns dW (E, M, N)."""
+    lib = load_library()
+    rows, M = a.shape
+    N = b.shape[1]
+    E = offsets.shape[0] - 1
+    dev = a.device
+    _need(a, "a", (rows, M))
+    _need(b, "b", (rows, N), a.dtype, dev)
+    _need(offsets, "offsets", (E + 1,), torch.int32, dev)
+    dW = _empty((E, M, N), a.dtype, dev) if dW is None else dW
+    _need(dW, "dW", (E, M, N), a.dtype, dev)
+    code = lib.moe_expert_weight_grad(_ptr(a), _ptr(b), _ptr(offsets), rows, E, M, N, _dt(a), _ptr(dW),
+                                      _stream(dev, stream))
+    _check(code, "moe_expert_weight_grad")
+    return dW
+
+
+def moe_dispatch_backward(dX_perm, inv, n: int, K: int, add=None, dx=None, stream=None):
+    """dx[i] = add[i] + sum_k dX_perm[inv[iK+k]] (add: (n, H) fp32 or None)."""
+    lib = load_library()
+    H = dX_perm.shape[1]
+    dev = dX_perm.device
+    _need(dX_perm, "dX_perm", (n * K, H))
+    _need(inv, "inv", (n * K,), torch.int32, dev)
+    if add is not None:
+        _need(add, "add", (n, H), torch.float32, dev)
+    dx = _empty((n, H), dX_perm.dtype, dev) if dx is None else dx
+    _need(dx, "dx", (n, H), dX_perm.dtype, dev)
+    code = lib.moe_dispatch_backward(_ptr(dX_perm), _ptr(inv), _ptr(add), n, H, K, _dt(dX_perm), _ptr(dx),
+                                     _stream(dev, stream))
+    _check(code, "moe_dispatch_backward")
+    return dx
+
+
+def moe_route_backward(x, W_gate, logits, topk_ids, topk_w, dw, renorm: bool, want_dx=True, want_weights=True,
+                       ws=None, stream=None):
+    """Gradient through routing given dw = dL/dtopk_w.
+
+    Returns dict(dlogits, dx_router or None, dW_gate or None, dbias or None), all fp32."""
+    lib = load_library()
+    n, E = logits.shape
+    K = topk_ids.shape[1]
+    dev = logits.device
+    src = W_gate if W_gate is not None else x
+    H = 0 if src is None else (W_gate.shape[0] if W_gate is not None else x.shape[1])
+    dt_t = torch.float32 if src is None else src.dtype
+    _need(logits, "logits", (n, E), torch.float32, dev)
+    _need(topk_ids, "topk_ids", (n, K), torch.int32, dev)
+    _need(topk_w, "topk_w", (n, K), torch.float32, dev)
+    _need(dw, "dw", (n, K), torch.float32, dev)
+    if want_dx:
+        _need(W_gate, "W_gate", (H, E), dt_t, dev)
+    if want_weights:
+        _need(x, "x", (n, H), dt_t, dev)
+    out = dict(
+        dlogits=_empty((n, E), torch.float32, dev),
+        dx_router=_empty((n, H), torch.float32, dev) if want_dx else None,
+        dW_gate=_empty((H, E), torch.float32, dev) if want_weights else None,
+        dbias=_empty((E,), torch.float32, dev) if want_weights else None,
+    )
+    nbytes = lib.moe_route_backward_workspace_size(n, H, E) if want_weights else 0
+    ws = _workspace(nbytes, dev, ws)
+    code = lib.moe_route_backward(
+        _ptr(x), _ptr(W_gate), _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _ptr(dw), n, H, E, K, int(bool(renorm)),
+        _dt(torch.empty(0, dtype=dt_t)), _ptr(out["dlogits"]), _ptr(out["dx_router"]), _ptr(out["dW_gate"]),
+        _ptr(out["dbias"]), _ptr(ws), ws.numel(), _stream(dev, stream),
+    )
+    _check(code, "moe_route_backward")
+    return out
+
+
+def moe_backward_workspace_size(n, H, I, E, K, dtype) -> int:  # noqa: E741
+    return int(load_library().moe_backward_workspace_size(n, H, I, E, K, _dt(torch.empty(0, dtype=dtype))))
+
+
+def moe_backward(dy, x, W_gate, W13, W2, K: int, renorm: bool, saved, grads=None, ws=None, stream=None):
+    """The layer's backward from moe_forward_train's saved buffers.
+
+    Returns dict(dx, dW_gate (fp32), dbias (fp32), dW13, dW2); `grads` may
+    supply any of them preallocated."""
+    lib = load_library()
+    n, H = x.shape
+    E = W_gate.shape[1]
+    I = W13.shape[2] // 2  # noqa: E741
+    dev, dt_t = x.device, x.dtype
+    _need(dy, "dy", (n, H), dt_t, dev)
+    _need(x, "x", (n, H))
+    _need(W_gate, "W_gate", (H, E), dt_t, dev)
+    _need(W13, "W13", (E, H, 2 * I), dt_t, dev)
+    _need(W2, "W2", (E, I, H), dt_t, dev)
+    shapes = dict(
+        logits=((n, E), torch.float32), topk_ids=((n, K), torch.int32), topk_w=((n, K), torch.float32),
+        offsets=((E + 1,), torch.int32), perm=((n * K,), torch.int32), inv=((n * K,), torch.int32),
+        gate_up=((n * K, 2 * I), dt_t), h=((n * K, I), dt_t), Y_perm=((n * K, H), dt_t),
+    )
+    for name, (shape, dtype) in shapes.items():
+        _need(saved[name], name, shape, dtype, dev)
+    gshapes = dict(dx=((n, H), dt_t), dW_gate=((H, E), torch.float32), dbias=((E,), torch.float32),
+                   dW13=((E, H, 2 * I), dt_t), dW2=((E, I, H), dt_t))
+    grads = dict(grads or {})
+    for name, (shape, dtype) in gshapes.items():
+        grads.setdefault(name, _empty(shape, dtype, dev))
+        _need(grads[name], name, shape, dtype, dev)
+    dt = _dt(x)
+    ws = _workspace(lib.moe_backward_workspace_size(n, H, I, E, K, dt), dev, ws)
+    code = lib.moe_backward(
+        _ptr(dy), _ptr(x), _ptr(W_gate), _ptr(W13), _ptr(W2), n, H, I, E, K, int(bool(renorm)), dt,
+        *[_ptr(saved[k]) for k in shapes], *[_ptr(grads[k]) for k in gshapes], _ptr(ws), ws.numel(),
+        _stream(dev, stream),
+    )
+    _check(code, "moe_backward")
+    return grads

@@ -15,13 +15,14 @@ namespace {
 
 // One workgroup per token; each thread owns 16-byte column chunks. The K
 // rows are fetched in batches of kBatch loads in flight per thread, then
-// accumulated in slot order.
+// accumulated in slot order. ADD: the sum starts from an fp32 row of `add`
+// (n, row_vecs * EPV) instead of zero, before the single rounding.
 constexpr int kBatch = 8;
 
-template <bool BF16>
+template <bool BF16, bool ADD = false>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y, const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w, int n, int row_vecs, int K,
-                                                      void* __restrict__ y) {
+                                                      void* __restrict__ y, const float* __restrict__ add) {
   constexpr int EPV = BF16 ? 8 : 4;  // elements per 16-byte vector
   const int i = blockIdx.x;
   const int total = n * K;
@@ -30,6 +31,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y
     float acc[EPV];
 #pragma unroll
     for (int q = 0; q < EPV; ++q) acc[q] = 0.f;
+    if constexpr (ADD) {
+      const u32x4_t* a = (const u32x4_t*)(add + ((size_t)i * row_vecs + c) * EPV);
+#pragma unroll
+      for (int q = 0; q < EPV / 4; ++q) {
+        const u32x4_t v = a[q];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[4 * q + j] = __uint_as_float(v[j]);
+      }
+    }
     for (int k0 = 0; k0 < K; k0 += kBatch) {
       u32x4_t v[kBatch];
       float wk[kBatch];
@@ -131,9 +141,21 @@ hipError_t launch_combine(const void* Y_perm, const int32_t* inv, const float* t
                           moe_dtype dt, void* y, hipStream_t s) {
   if (n == 0) return hipSuccess;
   if (dt == MOE_BF16)
-    combine_kernel<true><<<n, 256, 0, s>>>(Y_perm, inv, topk_w, n, H / 8, K, y);
+    combine_kernel<true><<<n, 256, 0, s>>>(Y_perm, inv, topk_w, n, H / 8, K, y, nullptr);
   else
-    combine_kernel<false><<<n, 256, 0, s>>>(Y_perm, inv, topk_w, n, H / 4, K, y);
+    combine_kernel<false><<<n, 256, 0, s>>>(Y_perm, inv, topk_w, n, H / 4, K, y, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_backward(const void* dX_perm, const int32_t* inv, const float* add, int n, int H, int K,
+                                    moe_dtype dt, void* dx, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  // Unit weights: each token sums the gradients of its K rows (slot order).
+  if (add == nullptr) return launch_combine(dX_perm, inv, nullptr, n, H, K, dt, dx, s);
+  if (dt == MOE_BF16)
+    combine_kernel<true, true><<<n, 256, 0, s>>>(dX_perm, inv, nullptr, n, H / 8, K, dx, add);
+  else
+    combine_kernel<false, true><<<n, 256, 0, s>>>(dX_perm, inv, nullptr, n, H / 4, K, dx, add);
   return hipGetLastError();
 }
 

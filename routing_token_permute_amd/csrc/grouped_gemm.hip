@@ -35,33 +35,10 @@
 
 #include <algorithm>
 
-#include "moe_internal.hpp"
+#include "gemm_tiles.hpp"
 
 namespace moe {
 namespace {
-
-constexpr int BN = kGemmBN;
-constexpr int B_ROW = BN * 2;             // bytes per staged k-row of B
-static_assert(BN == 256, "LDS layouts below assume 256-column stages");
-
-constexpr int kMaxStages = 5;
-
-// Stage geometry for a BM-row tile advancing BK (32 or 64) along K: A is
-// BM x BK, B is BK x 256. As many stages as fit in 160 KB of LDS, at most
-// kMaxStages (all but one stay in flight while one is multiplied).
-template <int BM, int BK>
-struct TileCfg {
-  static_assert(BK == 32 || BK == 64, "k-step");
-  static constexpr int A_ROW = BK * 2;  // bytes per staged row of A
-  static constexpr int A_BYTES = BM * A_ROW;
-  static constexpr int B_BYTES = BK * B_ROW;
-  static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int FIT = (160 * 1024) / STAGE;
-  static constexpr int NSTAGE = FIT > kMaxStages ? kMaxStages : FIT;
-  static constexpr int LDS_BYTES = NSTAGE * STAGE;
-  static constexpr int REGIONS = STAGE / 1024;  // 1 KB DMA regions per stage
-  static constexpr int A_ROWS_PER_REGION = 1024 / A_ROW;
-};
 
 // Launch configurations of the bf16 path (BM-row tiles, WM x WN waves):
 // large experts use 256-row tiles with 16 waves; when experts average few
@@ -70,101 +47,6 @@ struct TileCfg {
 constexpr int kBM = 256, kBK = 32, kGemmWM = 4, kGemmWN = 4;
 constexpr int kSmallBM = 32, kSmallBK = 64, kSmallWM = 1, kSmallWN = 4;
 constexpr int kSmallRowsPerExpert = 64;  // rows / E at or below this: small tiles
-
-// A tile: BM rows x BK k (2 * BK bytes per row, in 16-byte chunks). Chunk c
-// of row r sits at slot c ^ swz(r), swz(r) = (r / 2) % (chunks per row). With
-// it, the wave-wide ds_read_b128 of one MFMA A operand (16 rows at the same
-// chunk) runs at the full LDS rate of gfx950: 4 cycles per instruction,
-// measured with a per-CU timing probe, where the (r / 4) % 4 form of the
-// 64-byte rows takes 8. The DMA writes of a row are lane-linear and never
-// collide.
-template <int BK>
-__device__ __forceinline__ int a_swz(int row) { return (row >> 1) & (BK / 8 - 1); }
-
-// B tile: BK k-rows x 256 columns (512 B per row = 32 chunks). Chunk c of row
-// k sits at c ^ f(k), f(k) = 2 * ((k % 4) + 4 * ((k / 8) % 2)): the 32 lanes of
-// one transpose read (8 k-rows x 4 eight-byte pieces) land on 32 distinct
-// 8-byte bank pairs, and 16 lanes storing one row's chunks never collide.
-__device__ __forceinline__ int b_swz(int k) { return ((k & 3) + ((k >> 3) & 1) * 4) << 1; }
-__device__ __forceinline__ int b_off(int k, int chunk) { return k * B_ROW + ((chunk ^ b_swz(k)) << 4); }
-
-// Direct HBM -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
-// lane L's bytes land at LDS byte address lds_base + 16 * L, where lds_base is
-// wave-uniform (M0). Issued as inline assembly so that the compiler does not
-// treat every later LDS read as dependent on it; completion is awaited
-// explicitly with s_waitcnt vmcnt before the barrier that publishes a stage.
-// M0 is saved and restored around the copy because the compiler reserves it.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(lds_base)
-      : "memory");
-}
-
-struct Tile {
-  int e, r0, r1, nb;
-  bool valid;
-};
-
-// Tiles are ordered expert by expert; within an expert, n-block-major, then
-// row tile. Tile t -> (expert, rows [r0, r1), n-block). Every wave computes
-// it alike from `offsets` with a wave-wide prefix sum of the per-expert tile
-// counts.
-template <int BM>
-__device__ Tile find_tile(const int32_t* __restrict__ offsets, int E, int rows, int NB, int t) {
-  const int lane = lane_id();
-  int carry = 0;
-  for (int e0 = 0; e0 < E; e0 += 64) {
-    const int e = e0 + lane;
-    int a = 0, b = 0;
-    if (e < E) {
-      a = min(max(offsets[e], 0), rows);
-      b = min(max(offsets[e + 1], a), rows);
-    }
-    const int mt = (b - a + BM - 1) / BM;
-    const int cnt = mt * NB;
-    int incl = cnt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(incl, off);
-      if (lane >= off) incl += o;
-    }
-    const int excl = incl - cnt;
-    const bool hit = (cnt > 0) && (t >= carry + excl) && (t < carry + incl);
-    const uint64_t bal = __ballot(hit);
-    if (bal != 0) {
-      // An expert of n rows gets T = ceil(n / BM) row tiles of nearly equal
-      // height (the first n % T of them one row taller), so the last tile is
-      // never a sliver; waves skip the 16-row slices a tile does not fill.
-      const int L = __ffsll((long long)bal) - 1;
-      const int local = t - carry - __shfl(excl, L);
-      const int T = __shfl(mt, L);
-      const int ah = __shfl(a, L), n = __shfl(b, L) - ah;
-      const int m = local % T, q = n / T, rem = n % T;
-      const int r0 = ah + m * q + min(m, rem);
-      return Tile{e0 + L, r0, r0 + q + (m < rem ? 1 : 0), local / T, true};
-    }
-    carry += __shfl(incl, 63);
-  }
-  return Tile{0, 0, 0, 0, false};
-}
-
-// Workgroups are handed to the 8 XCDs round-robin (id % 8). Within each round
-// of 256 ids, give XCD x the contiguous tiles [32x, 32x + 32) so that the
-// workgroups sharing one expert's weight and activation tiles meet in one L2.
-__device__ __forceinline__ int xcd_remap(int bid, int G) {
-  constexpr int RS = 256;
-  const int full = (G / RS) * RS;
-  if (bid >= full) return bid;
-  const int w = bid % RS;
-  return (bid - w) + (w & 7) * (RS / 8) + (w >> 3);
-}
 
 // GATED (GEMM1): the 256 staged columns are 128 gate columns followed by the
 // matching 128 up columns; the tile writes 128 columns of h. Otherwise
@@ -177,7 +59,9 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) {
 // SCATTER (GEMM2 only): output row r goes to row perm[r] of C (flat pair
 // order, n_a rows) scaled by wrow[perm[r]] before the bf16 rounding, i.e. the
 // routing weight and the un-permutation are fused into the epilogue.
-template <bool GATED, bool GATHER, bool SCATTER, int BM, int BK, int WM, int WN>
+// SAVE (GEMM1 only): the pre-activations [gate | up] are also written, rounded
+// to bf16, to gu_out (row stride 2 * up_col), for the backward pass.
+template <bool GATED, bool GATHER, bool SCATTER, int BM, int BK, int WM, int WN, bool SAVE = false>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                                     const int32_t* __restrict__ perm, int topk,
                                                                     int n_a, const float* __restrict__ wrow,
@@ -186,7 +70,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
                                                                     const uint16_t* __restrict__ B, int ldb,
                                                                     long long b_expert_stride, int Nout, int up_col,
                                                                     uint16_t* __restrict__ C, int ldc, int NB,
-                                                                    int n_slots) {
+                                                                    int n_slots, uint16_t* __restrict__ gu_out) {
   using Cfg = TileCfg<BM, BK>;
   constexpr int A_BYTES = Cfg::A_BYTES, STAGE = Cfg::STAGE, NSTAGE = Cfg::NSTAGE, A_ROW = Cfg::A_ROW;
   constexpr int KS = BK / 32;              // 32-deep MFMA steps per stage
@@ -198,6 +82,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
   constexpr int A_REG = A_BYTES / 1024;    // regions holding A
   static_assert(NT % (GATED ? 4 : 2) == 0 && MT >= 1 && REG * NW == Cfg::REGIONS, "tile split");
   static_assert(!(SCATTER && (GATED || GATHER)), "the weighted scatter is a GEMM2 epilogue");
+  static_assert(!SAVE || GATED, "the pre-activations belong to GEMM1");
   static_assert(NSTAGE >= 2 && NSTAGE <= 5 && 4 * DMA_PER_STAGE <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(16))) char smem_raw[Cfg::LDS_BYTES];
   lds_char_t* smem = (lds_char_t*)smem_raw;
@@ -444,6 +329,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
           const int colP = t.nb * (BN / 2) + wn * (BN / 2 / WN) + q * 16;
           store_pair(crow, row_ok && colP < Nout, colP, hp[q], hp[q + 1]);
         }
+        if constexpr (SAVE) {
+          uint16_t* grow = gu_out + (size_t)crow_i * (2 * up_col);
+#pragma unroll
+          for (int q = 0; q < NT / 2; q += 2) {
+            const int colP = t.nb * (BN / 2) + wn * (BN / 2 / WN) + q * 16;
+            const f32x4_t g0 = acc[mt][q], g1 = acc[mt][q + 1];
+            const f32x4_t u0 = acc[mt][q + NT / 2], u1 = acc[mt][q + 1 + NT / 2];
+            store_pair(grow, row_ok && colP < Nout, colP, u32x2_t{pack2(g0[0], g0[1]), pack2(g0[2], g0[3])},
+                       u32x2_t{pack2(g1[0], g1[1]), pack2(g1[2], g1[3])});
+            store_pair(grow + up_col, row_ok && colP < Nout, colP, u32x2_t{pack2(u0[0], u0[1]), pack2(u0[2], u0[3])},
+                       u32x2_t{pack2(u1[0], u1[1]), pack2(u1[2], u1[3])});
+          }
+        }
       } else {
 #pragma unroll
         for (int q = 0; q < NT; q += 2) {
@@ -493,14 +391,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
 }
 
 // fp32: one thread per output element; lanes run along the output columns.
-template <bool GATED, bool GATHER, bool SCATTER>
+template <bool GATED, bool GATHER, bool SCATTER, bool SAVE = false>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A,
                                                       const int32_t* __restrict__ perm, int topk, int n_a,
                                                       const float* __restrict__ wrow,
                                                       const int32_t* __restrict__ offsets, int E, int rows,
                                                       int Kdim, const float* __restrict__ B, int ldb,
                                                       long long b_expert_stride, int Nout, int up_col,
-                                                      float* __restrict__ C, int ldc) {
+                                                      float* __restrict__ C, int ldc, float* __restrict__ gu_out) {
   const int col = blockIdx.x * 64 + (threadIdx.x & 63);
   const int row = blockIdx.y * 4 + (threadIdx.x >> 6);
   if (row >= rows || col >= Nout) return;
@@ -530,6 +428,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
   }
   if constexpr (GATED) {
     C[(size_t)row * ldc + col] = gsum / (1.f + expf(-gsum)) * usum;
+    if constexpr (SAVE) {
+      gu_out[(size_t)row * 2 * up_col + col] = gsum;
+      gu_out[(size_t)row * 2 * up_col + up_col + col] = usum;
+    }
   } else if constexpr (SCATTER) {
     const int f = perm[row];
     if ((unsigned)f < (unsigned)n_a) C[(size_t)f * ldc + col] = wrow[f] * gsum;
@@ -541,57 +443,44 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 }  // namespace
 
 namespace {
-// Compute units of the current device (one persistent workgroup each),
-// looked up once per device.
-int device_cu_count() {
-  constexpr int kMaxDevices = 64;
-  static int cached[kMaxDevices] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
 
-template <bool GATED, bool GATHER, bool SCATTER, int BM, int BK, int WM, int WN>
+template <bool GATED, bool GATHER, bool SCATTER, int BM, int BK, int WM, int WN, bool SAVE>
 void launch_cfg(const void* a, const int32_t* perm, int topk, int n_a, const float* wrow, const int32_t* offsets,
                 int E, int rows, int Kdim, const void* B, int ldb, long long bstride, int Nout, int up_col, void* C,
-                int ldc, int NB, hipStream_t s) {
+                int ldc, int NB, void* gu_out, hipStream_t s) {
   const int n_slots = max_row_tiles(rows, E, BM) * NB;
   const int grid = std::min(n_slots, device_cu_count());
-  gemm_bf16_kernel<GATED, GATHER, SCATTER, BM, BK, WM, WN><<<grid, 64 * WM * WN, 0, s>>>(
+  gemm_bf16_kernel<GATED, GATHER, SCATTER, BM, BK, WM, WN, SAVE><<<grid, 64 * WM * WN, 0, s>>>(
       (const uint16_t*)a, perm, topk, n_a, wrow, offsets, E, rows, Kdim, (const uint16_t*)B, ldb, bstride, Nout,
-      up_col, (uint16_t*)C, ldc, NB, n_slots);
+      up_col, (uint16_t*)C, ldc, NB, n_slots, (uint16_t*)gu_out);
 }
 
-template <bool GATED, bool GATHER, bool SCATTER = false>
+template <bool GATED, bool GATHER, bool SCATTER = false, bool SAVE = false>
 void launch_bf16(const void* a, const int32_t* perm, int topk, int n_a, const int32_t* offsets, int E, int rows,
                  int Kdim, const void* B, int ldb, long long bstride, int Nout, int up_col, void* C, int ldc, int NB,
-                 hipStream_t s, const float* wrow = nullptr) {
+                 hipStream_t s, const float* wrow = nullptr, void* gu_out = nullptr) {
   if ((long long)rows <= (long long)kSmallRowsPerExpert * E)
-    launch_cfg<GATED, GATHER, SCATTER, kSmallBM, kSmallBK, kSmallWM, kSmallWN>(
-        a, perm, topk, n_a, wrow, offsets, E, rows, Kdim, B, ldb, bstride, Nout, up_col, C, ldc, NB, s);
+    launch_cfg<GATED, GATHER, SCATTER, kSmallBM, kSmallBK, kSmallWM, kSmallWN, SAVE>(
+        a, perm, topk, n_a, wrow, offsets, E, rows, Kdim, B, ldb, bstride, Nout, up_col, C, ldc, NB, gu_out, s);
   else
-    launch_cfg<GATED, GATHER, SCATTER, kBM, kBK, kGemmWM, kGemmWN>(a, perm, topk, n_a, wrow, offsets, E, rows, Kdim, B,
-                                                              ldb, bstride, Nout, up_col, C, ldc, NB, s);
+    launch_cfg<GATED, GATHER, SCATTER, kBM, kBK, kGemmWM, kGemmWN, SAVE>(
+        a, perm, topk, n_a, wrow, offsets, E, rows, Kdim, B, ldb, bstride, Nout, up_col, C, ldc, NB, gu_out, s);
 }
 
-template <bool GATHER>
+template <bool GATHER, bool SAVE = false>
 hipError_t w13_impl(const void* a, const int32_t* perm, int topk, int n_a, const int32_t* offsets, int rows,
-                    const void* W13, int E, int H, int I, moe_dtype dt, void* h, hipStream_t s) {
+                    const void* W13, int E, int H, int I, moe_dtype dt, void* h, hipStream_t s,
+                    void* gu_out = nullptr) {
   if (rows == 0) return hipSuccess;
   if (dt == MOE_BF16) {
-    launch_bf16<true, GATHER>(a, perm, topk, n_a, offsets, E, rows, H, W13, 2 * I, (long long)H * 2 * I, I, I, h, I,
-                              ceil_div(I, BN / 2), s);
+    launch_bf16<true, GATHER, false, SAVE>(a, perm, topk, n_a, offsets, E, rows, H, W13, 2 * I,
+                                           (long long)H * 2 * I, I, I, h, I, ceil_div(I, BN / 2), s, nullptr,
+                                           gu_out);
   } else {
     dim3 g1(ceil_div(I, 64), ceil_div(rows, 4));
-    gemm_f32_kernel<true, GATHER, false><<<g1, 256, 0, s>>>((const float*)a, perm, topk, n_a, nullptr, offsets, E,
-                                                            rows, H,
-                                                     (const float*)W13, 2 * I, (long long)H * 2 * I, I, I,
-                                                     (float*)h, I);
+    gemm_f32_kernel<true, GATHER, false, SAVE><<<g1, 256, 0, s>>>(
+        (const float*)a, perm, topk, n_a, nullptr, offsets, E, rows, H, (const float*)W13, 2 * I,
+        (long long)H * 2 * I, I, I, (float*)h, I, (float*)gu_out);
   }
   return hipGetLastError();
 }
@@ -607,6 +496,12 @@ hipError_t launch_w13_swiglu_gather(const void* x, const int32_t* perm, int n, i
   return w13_impl<true>(x, perm, K, n, offsets, n * K, W13, E, H, I, dt, h, s);
 }
 
+hipError_t launch_w13_swiglu_gather_train(const void* x, const int32_t* perm, int n, int K, const int32_t* offsets,
+                                          const void* W13, int E, int H, int I, moe_dtype dt, void* h, void* gate_up,
+                                          hipStream_t s) {
+  return w13_impl<true, true>(x, perm, K, n, offsets, n * K, W13, E, H, I, dt, h, s, gate_up);
+}
+
 hipError_t launch_w2(const void* h, const int32_t* offsets, int rows, const void* W2, int E, int H, int I,
                      moe_dtype dt, void* Y_perm, hipStream_t s) {
   if (rows == 0) return hipSuccess;
@@ -617,7 +512,7 @@ hipError_t launch_w2(const void* h, const int32_t* offsets, int rows, const void
     dim3 g2(ceil_div(H, 64), ceil_div(rows, 4));
     gemm_f32_kernel<false, false, false><<<g2, 256, 0, s>>>((const float*)h, nullptr, 1, rows, nullptr, offsets, E,
                                                             rows, I, (const float*)W2, H, (long long)I * H, H, 0,
-                                                            (float*)Y_perm, H);
+                                                            (float*)Y_perm, H, nullptr);
   }
   return hipGetLastError();
 }
@@ -633,7 +528,7 @@ hipError_t launch_w2_scatter(const void* h, const int32_t* offsets, int rows, co
     dim3 g2(ceil_div(H, 64), ceil_div(rows, 4));
     gemm_f32_kernel<false, false, true><<<g2, 256, 0, s>>>((const float*)h, perm, 1, rows, topk_w, offsets, E, rows,
                                                            I, (const float*)W2, H, (long long)I * H, H, 0,
-                                                           (float*)Y_tok, H);
+                                                           (float*)Y_tok, H, nullptr);
   }
   return hipGetLastError();
 }

@@ -1,6 +1,7 @@
-// C ABI of the MoE expert-layer forward: argument checks, workspace layout and
-// the order in which the kernels are enqueued. Everything numeric runs in the
-// kernels of route.hip, permute.hip, grouped_gemm.hip and combine.hip.
+// C ABI of the MoE expert layer (forward and backward): argument checks,
+// workspace layouts and the order in which the kernels are enqueued.
+// Everything numeric runs in the kernels of route.hip, permute.hip,
+// grouped_gemm.hip, combine.hip, grouped_gemm_bwd.hip and backward.hip.
 #include <stdint.h>
 
 #include "moe_internal.hpp"
@@ -56,6 +57,53 @@ ForwardLayout forward_layout(int n, int H, int I, int E, int K, moe_dtype dt) {
   L.pscratch = take(permute_ws(n, E, K));
   L.h = take(nk * I * elt_size(dt));
   L.Y_perm = take(nk * H * elt_size(dt));
+  L.total = o;
+  return L;
+}
+
+// moe_forward_train workspace: what the forward uses but does not save.
+struct TrainLayout {
+  size_t counts, splits, pscratch, total;
+};
+
+TrainLayout train_layout(int n, int E, int K) {
+  TrainLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes > 0 ? bytes : 1);
+    return at;
+  };
+  L.counts = take((size_t)E * 4);
+  L.splits = take(4);
+  L.pscratch = take(permute_ws(n, E, K));
+  L.total = o;
+  return L;
+}
+
+size_t route_bwd_ws(int n, int H, int E) { return align_up((size_t)route_bwd_chunks(n) * (H + 1) * E * 4); }
+
+// moe_backward workspace, in order. rows_a holds dY_perm, then dX_perm, then
+// the gathered x_perm (each dead before the next is written, in stream order).
+struct BackwardLayout {
+  size_t rows_a, dgu, dw, dlogits, dx_router, rws, total;
+};
+
+BackwardLayout backward_layout(int n, int H, int I, int E, int K, moe_dtype dt) {
+  BackwardLayout L{};
+  const size_t nk = (size_t)n * K;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes > 0 ? bytes : 1);
+    return at;
+  };
+  L.rows_a = take(nk * H * elt_size(dt));
+  L.dgu = take(nk * 2 * I * elt_size(dt));
+  L.dw = take(nk * 4);
+  L.dlogits = take((size_t)n * E * 4);
+  L.dx_router = take((size_t)n * H * 4);
+  L.rws = take(route_bwd_ws(n, H, E));
   L.total = o;
   return L;
 }
@@ -229,6 +277,182 @@ moe_status moe_forward(const void* x, const void* W_gate, const float* bias, con
   e = launch_w2(base + L.h, offsets, n * K, W2, E, H, I, dt, base + L.Y_perm, stream);
   if (e != hipSuccess) return MOE_EHIP;
   return from_hip(launch_combine(base + L.Y_perm, inv, w, n, H, K, dt, y, stream));
+}
+
+// ---------------------------------------------------------------------------
+// Backward
+// ---------------------------------------------------------------------------
+
+moe_status moe_expert_w13_swiglu_gather_train(const void* x, const int32_t* perm, int n, int K,
+                                              const int32_t* offsets, const void* W13, int E, int H, int I,
+                                              moe_dtype dt, void* h, void* gate_up, hipStream_t stream) {
+  if (n < 0 || K < 1 || K > kMaxTopK || (long long)n * K > INT32_MAX) return MOE_EINVAL;
+  if (n > 0 && (perm == nullptr || gate_up == nullptr)) return MOE_EINVAL;
+  const moe_status st = check_expert_gemm(x, offsets, n * K, W13, E, H, I, dt, h);
+  if (st != MOE_OK) return st;
+  return from_hip(launch_w13_swiglu_gather_train(x, perm, n, K, offsets, W13, E, H, I, dt, h, gate_up, stream));
+}
+
+size_t moe_forward_train_workspace_size(int n, int E, int K) {
+  if (n < 0 || E < 1 || K < 1) return 0;
+  return train_layout(n, E, K).total;
+}
+
+moe_status moe_forward_train(const void* x, const void* W_gate, const float* bias, const void* W13, const void* W2,
+                             int n, int H, int I, int E, int K, int renorm, moe_dtype dt, void* y, float* logits,
+                             int32_t* topk_ids, float* topk_w, int32_t* offsets, int32_t* perm, int32_t* inv,
+                             void* gate_up, void* h, void* Y_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
+  if (n < 0 || !experts_ok(E, K) || !hidden_ok(H, dt) || !hidden_ok(I, dt)) return MOE_EINVAL;
+  if ((long long)n * K > INT32_MAX) return MOE_EINVAL;
+  if (offsets == nullptr) return MOE_EINVAL;
+  if (n > 0 && (x == nullptr || W_gate == nullptr || W13 == nullptr || W2 == nullptr || y == nullptr ||
+                logits == nullptr || topk_ids == nullptr || topk_w == nullptr || perm == nullptr || inv == nullptr ||
+                gate_up == nullptr || h == nullptr || Y_perm == nullptr))
+    return MOE_EINVAL;
+  const TrainLayout L = train_layout(n, E, K);
+  if (ws == nullptr || ws_bytes < L.total) return MOE_EWORKSPACE;
+  char* base = (char*)ws;
+  hipError_t e = launch_route(x, W_gate, bias, n, H, E, K, renorm, dt, logits, topk_ids, topk_w, stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  e = launch_permute(topk_ids, nullptr, n, H, E, K, 1, dt, (int32_t*)(base + L.counts), offsets,
+                     (int32_t*)(base + L.splits), perm, inv, nullptr, (int32_t*)(base + L.pscratch), stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  if (n == 0) return MOE_OK;
+  e = launch_w13_swiglu_gather_train(x, perm, n, K, offsets, W13, E, H, I, dt, h, gate_up, stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  e = launch_w2(h, offsets, n * K, W2, E, H, I, dt, Y_perm, stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  return from_hip(launch_combine(Y_perm, inv, topk_w, n, H, K, dt, y, stream));
+}
+
+moe_status moe_combine_backward(const void* dy, const void* Y_perm, const int32_t* inv, const float* topk_w, int n,
+                                int H, int K, moe_dtype dt, void* dY_perm, float* dw, hipStream_t stream) {
+  if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
+  if (n < 0 || K < 1 || K > kMaxTopK || !hidden_ok(H, dt)) return MOE_EINVAL;
+  if ((long long)n * K > INT32_MAX) return MOE_EINVAL;
+  if (n == 0) return MOE_OK;
+  if (dy == nullptr || Y_perm == nullptr || inv == nullptr || topk_w == nullptr || dY_perm == nullptr ||
+      dw == nullptr)
+    return MOE_EINVAL;
+  return from_hip(launch_combine_backward(dy, Y_perm, inv, topk_w, n, H, K, dt, dY_perm, dw, stream));
+}
+
+moe_status moe_expert_w2_backward(const void* dY_perm, const int32_t* offsets, int rows, const void* W2,
+                                  const void* gate_up, int E, int H, int I, moe_dtype dt, void* dgate_up,
+                                  hipStream_t stream) {
+  const moe_status st = check_expert_gemm(dY_perm, offsets, rows, W2, E, H, I, dt, dgate_up);
+  if (st != MOE_OK) return st;
+  if (rows > 0 && gate_up == nullptr) return MOE_EINVAL;
+  return from_hip(launch_w2_backward(dY_perm, offsets, rows, W2, gate_up, E, H, I, dt, dgate_up, stream));
+}
+
+moe_status moe_expert_w13_backward(const void* dgate_up, const int32_t* offsets, int rows, const void* W13, int E,
+                                   int H, int I, moe_dtype dt, void* dX_perm, hipStream_t stream) {
+  const moe_status st = check_expert_gemm(dgate_up, offsets, rows, W13, E, H, I, dt, dX_perm);
+  if (st != MOE_OK) return st;
+  return from_hip(launch_w13_backward(dgate_up, offsets, rows, W13, E, H, I, dt, dX_perm, stream));
+}
+
+moe_status moe_expert_weight_grad(const void* a, const void* b, const int32_t* offsets, int rows, int E, int M, int N,
+                                  moe_dtype dt, void* dW, hipStream_t stream) {
+  if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
+  if (rows < 0 || E < 1 || E > kMaxExperts || !hidden_ok(M, dt) || !hidden_ok(N, dt)) return MOE_EINVAL;
+  if (offsets == nullptr || dW == nullptr) return MOE_EINVAL;
+  if (rows > 0 && (a == nullptr || b == nullptr)) return MOE_EINVAL;
+  return from_hip(launch_weight_grad(a, b, offsets, rows, E, M, N, dt, dW, stream));
+}
+
+moe_status moe_dispatch_backward(const void* dX_perm, const int32_t* inv, const float* add, int n, int H, int K,
+                                 moe_dtype dt, void* dx, hipStream_t stream) {
+  if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
+  if (n < 0 || K < 1 || K > kMaxTopK || !hidden_ok(H, dt)) return MOE_EINVAL;
+  if ((long long)n * K > INT32_MAX) return MOE_EINVAL;
+  if (n == 0) return MOE_OK;
+  if (dX_perm == nullptr || inv == nullptr || dx == nullptr) return MOE_EINVAL;
+  return from_hip(launch_dispatch_backward(dX_perm, inv, add, n, H, K, dt, dx, stream));
+}
+
+size_t moe_route_backward_workspace_size(int n, int H, int E) {
+  if (n < 0 || H < 0 || E < 1) return 0;
+  return route_bwd_ws(n, H, E);
+}
+
+moe_status moe_route_backward(const void* x, const void* W_gate, const float* logits, const int32_t* topk_ids,
+                              const float* topk_w, const float* dw, int n, int H, int E, int K, int renorm,
+                              moe_dtype dt, float* dlogits, float* dx_router, float* dW_gate, float* dbias, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
+  if (n < 0 || !experts_ok(E, K)) return MOE_EINVAL;
+  const bool weights = dW_gate != nullptr || dbias != nullptr;
+  if ((dx_router != nullptr || weights) && !hidden_ok(H, dt)) return MOE_EINVAL;
+  if (n == 0) {  // no tokens: the weight gradients are zero
+    if (dW_gate != nullptr && launch_fill_zero(dW_gate, (size_t)H * E * 4, stream) != hipSuccess) return MOE_EHIP;
+    if (dbias != nullptr && launch_fill_zero(dbias, (size_t)E * 4, stream) != hipSuccess) return MOE_EHIP;
+    return MOE_OK;
+  }
+  if (logits == nullptr || topk_ids == nullptr || topk_w == nullptr || dw == nullptr || dlogits == nullptr)
+    return MOE_EINVAL;
+  if (dx_router != nullptr && W_gate == nullptr) return MOE_EINVAL;
+  if (weights && x == nullptr) return MOE_EINVAL;
+  if (weights && (ws == nullptr || ws_bytes < route_bwd_ws(n, H, E))) return MOE_EWORKSPACE;
+  return from_hip(launch_route_backward(x, W_gate, logits, topk_ids, topk_w, dw, n, H, E, K, renorm, dt, dlogits,
+                                        dx_router, dW_gate, dbias, (float*)ws, stream));
+}
+
+size_t moe_backward_workspace_size(int n, int H, int I, int E, int K, moe_dtype dt) {
+  if (n < 0 || H < 1 || I < 1 || E < 1 || K < 1 || !dtype_ok(dt)) return 0;
+  return backward_layout(n, H, I, E, K, dt).total;
+}
+
+moe_status moe_backward(const void* dy, const void* x, const void* W_gate, const void* W13, const void* W2, int n,
+                        int H, int I, int E, int K, int renorm, moe_dtype dt, const float* logits,
+                        const int32_t* topk_ids, const float* topk_w, const int32_t* offsets, const int32_t* perm,
+                        const int32_t* inv, const void* gate_up, const void* h, const void* Y_perm, void* dx,
+                        float* dW_gate, float* dbias, void* dW13, void* dW2, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
+  if (n < 0 || !experts_ok(E, K) || !hidden_ok(H, dt) || !hidden_ok(I, dt)) return MOE_EINVAL;
+  if ((long long)n * K > INT32_MAX) return MOE_EINVAL;
+  if (offsets == nullptr || dW_gate == nullptr || dW13 == nullptr || dW2 == nullptr) return MOE_EINVAL;
+  if (n > 0 && (dy == nullptr || x == nullptr || W_gate == nullptr || W13 == nullptr || W2 == nullptr ||
+                logits == nullptr || topk_ids == nullptr || topk_w == nullptr || perm == nullptr || inv == nullptr ||
+                gate_up == nullptr || h == nullptr || Y_perm == nullptr || dx == nullptr))
+    return MOE_EINVAL;
+  const BackwardLayout L = backward_layout(n, H, I, E, K, dt);
+  if (ws == nullptr || ws_bytes < L.total) return MOE_EWORKSPACE;
+  char* base = (char*)ws;
+  void* rows_a = base + L.rows_a;
+  void* dgu = base + L.dgu;
+  float* dw = (float*)(base + L.dw);
+  float* dlogits = (float*)(base + L.dlogits);
+  float* dx_router = (float*)(base + L.dx_router);
+  const int rows = n * K;
+
+  hipError_t e = hipSuccess;
+  if (n == 0) {  // no rows: every weight gradient is zero
+    e = launch_fill_zero(dW13, (size_t)E * H * 2 * I * elt_size(dt), stream);
+    if (e == hipSuccess) e = launch_fill_zero(dW2, (size_t)E * I * H * elt_size(dt), stream);
+    if (e == hipSuccess) e = launch_fill_zero(dW_gate, (size_t)H * E * 4, stream);
+    if (e == hipSuccess && dbias != nullptr) e = launch_fill_zero(dbias, (size_t)E * 4, stream);
+    return from_hip(e);
+  }
+  e = launch_combine_backward(dy, Y_perm, inv, topk_w, n, H, K, dt, rows_a, dw, stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  e = launch_route_backward(x, W_gate, logits, topk_ids, topk_w, dw, n, H, E, K, renorm, dt, dlogits, dx_router,
+                            dW_gate, dbias, (float*)(base + L.rws), stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  e = launch_w2_backward(rows_a, offsets, rows, W2, gate_up, E, H, I, dt, dgu, stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  e = launch_weight_grad(h, rows_a, offsets, rows, E, I, H, dt, dW2, stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  e = launch_w13_backward(dgu, offsets, rows, W13, E, H, I, dt, rows_a, stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  e = launch_dispatch_backward(rows_a, inv, dx_router, n, H, K, dt, dx, stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  e = launch_gather_rows(x, perm, n, H, K, dt, rows_a, stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  return from_hip(launch_weight_grad(rows_a, dgu, offsets, rows, E, H, 2 * I, dt, dW13, stream));
 }
 
 }  // extern "C"

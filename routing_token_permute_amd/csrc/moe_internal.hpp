@@ -18,6 +18,9 @@ constexpr int kMaxTopK = 64;
 constexpr int kPermThreads = 256;
 constexpr int kPermMaxBlocks = 128;
 
+// Router backward: dW_gate is summed over at most this many token chunks.
+constexpr int kRouteBwdMaxChunks = 32;
+
 // bf16 grouped GEMM tile.
 constexpr int kGemmBM = 128;
 constexpr int kGemmBN = 256;
@@ -66,6 +69,40 @@ hipError_t launch_w2_scatter(const void* h, const int32_t* offsets, int rows, co
 hipError_t launch_sum_slots(const void* Y_tok, int n, int H, int K, moe_dtype dt, void* y, hipStream_t s);
 hipError_t launch_combine(const void* Y_perm, const int32_t* inv, const float* topk_w, int n, int H, int K,
                           moe_dtype dt, void* y, hipStream_t s);
+
+// ---- backward ----
+
+// GEMM1 that also writes the pre-activations [gate | up] (rows, 2I) for the backward.
+hipError_t launch_w13_swiglu_gather_train(const void* x, const int32_t* perm, int n, int K, const int32_t* offsets,
+                                          const void* W13, int E, int H, int I, moe_dtype dt, void* h, void* gate_up,
+                                          hipStream_t s);
+// x_perm[p] = x[perm[p] / K] for all n*K rows.
+hipError_t launch_gather_rows(const void* x, const int32_t* perm, int n, int H, int K, moe_dtype dt, void* x_perm,
+                              hipStream_t s);
+// dY_perm[inv[iK+k]] = w[i,k] dy[i]; dw[i,k] = <dy[i], Y_perm[inv[iK+k]]>.
+hipError_t launch_combine_backward(const void* dy, const void* Y_perm, const int32_t* inv, const float* topk_w, int n,
+                                   int H, int K, moe_dtype dt, void* dY_perm, float* dw, hipStream_t s);
+// dx[i] = (add[i] if add) + sum_k dX_perm[inv[iK+k]], slot order, one rounding.
+hipError_t launch_dispatch_backward(const void* dX_perm, const int32_t* inv, const float* add, int n, int H, int K,
+                                    moe_dtype dt, void* dx, hipStream_t s);
+// dgate_up = SwiGLU'(gate_up) applied to dY_perm . W2[e]^T.
+hipError_t launch_w2_backward(const void* dY_perm, const int32_t* offsets, int rows, const void* W2,
+                              const void* gate_up, int E, int H, int I, moe_dtype dt, void* dgate_up, hipStream_t s);
+// dX_perm = dgate_up . W13[e]^T.
+hipError_t launch_w13_backward(const void* dgate_up, const int32_t* offsets, int rows, const void* W13, int E, int H,
+                               int I, moe_dtype dt, void* dX_perm, hipStream_t s);
+// dW[e] = a_e^T . b_e over each expert's rows; a (rows, M), b (rows, N), dW (E, M, N).
+hipError_t launch_weight_grad(const void* a, const void* b, const int32_t* offsets, int rows, int E, int M, int N,
+                              moe_dtype dt, void* dW, hipStream_t s);
+// Zero `bytes` (a multiple of 4) with a kernel.
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// Token chunks of the dW_gate reduction for n tokens.
+int route_bwd_chunks(int n);
+// ws: route_bwd_chunks(n) * (H + 1) * E floats (only when dW_gate or dbias is wanted).
+hipError_t launch_route_backward(const void* x, const void* W_gate, const float* logits, const int32_t* ids,
+                                 const float* topk_w, const float* dw, int n, int H, int E, int K, int renorm,
+                                 moe_dtype dt, float* dlogits, float* dx_router, float* dW_gate, float* dbias,
+                                 float* ws, hipStream_t s);
 
 }  // namespace moe
 

@@ -358,6 +358,15 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict
 
 }  // namespace
 
+hipError_t launch_gather_rows(const void* x, const int32_t* perm, int n, int H, int K, moe_dtype dt, void* x_perm,
+                              hipStream_t s) {
+  const int total = n * K;
+  if (total == 0) return hipSuccess;
+  const int row_vecs = H * (dt == MOE_BF16 ? 2 : 4) / 16;
+  gather_rows_kernel<<<ceil_div(total, 4), 256, 0, s>>>((const char*)x, row_vecs, perm, K, total, (char*)x_perm);
+  return hipGetLastError();
+}
+
 hipError_t launch_permute(const int32_t* topk_ids, const void* x, int n, int H, int E, int K, int ep,
                           moe_dtype dt, int32_t* counts, int32_t* offsets, int32_t* splits, int32_t* perm,
                           int32_t* inv, void* x_perm, int32_t* block_counts, hipStream_t s) {

@@ -166,3 +166,50 @@ def test_scatter_and_slot_sum_reject_bad_arguments(lib):
     assert lib.moe_sum_slots(P, 8, 64, 2, 1, None, s) == EINVAL
     assert lib.moe_sum_slots(P, 8, 96, 2, 1, P, s) == EINVAL
     assert lib.moe_sum_slots(P, 0, 64, 2, 1, None, s) == 0  # n == 0 is a no-op
+
+
+def test_backward_calls_reject_bad_arguments(lib):
+    s = None
+    # combine backward: K out of range, null dw, bad hidden size, unknown dtype
+    assert lib.moe_combine_backward(P, P, P, P, 8, 64, 65, 1, P, P, s) == EINVAL
+    assert lib.moe_combine_backward(P, P, P, P, 8, 64, 2, 1, P, None, s) == EINVAL
+    assert lib.moe_combine_backward(P, P, P, P, 8, 96, 2, 1, P, P, s) == EINVAL
+    assert lib.moe_combine_backward(P, P, P, P, 8, 64, 2, 9, P, P, s) == EUNSUP
+    assert lib.moe_combine_backward(None, None, None, None, 0, 64, 2, 1, None, None, s) == 0
+    # GEMM2 backward without the saved pre-activations; bad I
+    assert lib.moe_expert_w2_backward(P, P, 8, P, None, 4, 64, 64, 1, P, s) == EINVAL
+    assert lib.moe_expert_w2_backward(P, P, 8, P, P, 4, 64, 48, 1, P, s) == EINVAL
+    assert lib.moe_expert_w13_backward(P, P, 8, P, 4, 64, 64, 1, None, s) == EINVAL
+    assert lib.moe_expert_w13_backward(P, P, 8, P, 300, 64, 64, 1, P, s) == EINVAL  # E > 256
+    # weight gradient: null output, bad M, null inputs with rows > 0
+    assert lib.moe_expert_weight_grad(P, P, P, 8, 4, 64, 64, 1, None, s) == EINVAL
+    assert lib.moe_expert_weight_grad(P, P, P, 8, 4, 65, 64, 1, P, s) == EINVAL
+    assert lib.moe_expert_weight_grad(None, P, P, 8, 4, 64, 64, 1, P, s) == EINVAL
+    # dispatch backward
+    assert lib.moe_dispatch_backward(P, P, None, 8, 64, 0, 1, P, s) == EINVAL
+    assert lib.moe_dispatch_backward(P, None, None, 8, 64, 2, 1, P, s) == EINVAL
+    # route backward: K > E, missing workspace for the weight gradients, missing W_gate for dx
+    rws = lib.moe_route_backward_workspace_size(16, 64, 8)
+    assert rws >= (64 + 1) * 8 * 4  # one token chunk of partial dW_gate and dbias
+    assert lib.moe_route_backward(P, P, P, P, P, P, 16, 64, 8, 9, 0, 1, P, P, P, P, P, rws, s) == EINVAL
+    assert lib.moe_route_backward(P, P, P, P, P, P, 16, 64, 8, 2, 0, 1, P, P, P, P, None, 0, s) == EWS
+    assert lib.moe_route_backward(P, None, P, P, P, P, 16, 64, 8, 2, 0, 1, P, P, None, None, None, 0, s) == EINVAL
+    # whole backward: small workspace, missing gradient output
+    ws = lib.moe_backward_workspace_size(16, 64, 64, 8, 2, 1)
+    assert ws >= 16 * 2 * (64 + 128) * 2
+    args = [P, P, P, P, P, 16, 64, 64, 8, 2, 0, 1] + [P] * 9 + [P, P, P, P, P] + [P, ws, s]
+    bad = list(args)
+    bad[-2] = ws - 1
+    assert lib.moe_backward(*bad) == EWS
+    bad = list(args)
+    bad[24] = None  # dW13
+    assert lib.moe_backward(*bad) == EINVAL
+    # training forward: null saved buffer
+    fws = lib.moe_forward_train_workspace_size(16, 8, 2)
+    fargs = [P, P, None, P, P, 16, 64, 64, 8, 2, 0, 1, P] + [P] * 9 + [P, fws, s]
+    bad = list(fargs)
+    bad[20] = None  # gate_up
+    assert lib.moe_forward_train(*bad) == EINVAL
+    bad = list(fargs)
+    bad[-2] = 0
+    assert lib.moe_forward_train(*bad) == EWS
