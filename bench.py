@@ -40,7 +40,7 @@ def _parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="olmoe_bf16",
-                   choices=["olmoe_bf16", "olmoe_skewed_bf16", "decode_bf16", "ep_share_bf16"])
+                   choices=["olmoe_bf16", "olmoe_skewed_bf16", "decode_bf16", "ep_share_bf16", "olmoe_train_bf16"])
     p.add_argument("--stage-reps", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle wall time for the CPU baseline")
@@ -188,6 +188,9 @@ def main():
 
     if args.workload == "ep_share_bf16":
         _bench_ep_share(args)
+        return
+    if args.workload == "olmoe_train_bf16":
+        _bench_train(args)
         return
     dev = torch.device("cuda:0")
     w = make_config(args.workload)
@@ -425,16 +428,167 @@ def _bench_ep_share(args):
     print(json.dumps(out), flush=True)
 
 
+def _bench_train(args):
+    """Training step of the OLMoE n=4096 layer: moe_forward_train then
+    moe_backward for a seeded upstream gradient. Reports fwd+bwd tokens/s, the
+    two halves, and each backward stage alone with its FLOP rate or bandwidth."""
+    import torch
+
+    import routing_token_permute_amd as moe
+    from workloads import make_config, random_bf16_matrix
+
+    dev = torch.device("cuda:0")
+    w = make_config("olmoe_bf16")
+    n, H, I, E, K = w.n, w.H, w.I, w.E, w.K  # noqa: E741
+
+    def to_dev(b):
+        return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x, Wg, W13, W2 = (to_dev(w.bits(k)) for k in ("x", "W_gate", "W13", "W2"))
+    dy = to_dev(random_bf16_matrix(np.random.default_rng(w.n), (n, H))[0])
+    y, saved = moe.moe_forward_train(x, Wg, W13, W2, K, w.renorm)
+    grads = moe.moe_backward(dy, x, Wg, W13, W2, K, w.renorm, saved)
+    fws = torch.empty(moe.load_library().moe_forward_train_workspace_size(n, E, K), dtype=torch.uint8, device=dev)
+    bws = torch.empty(moe.moe_backward_workspace_size(n, H, I, E, K, torch.bfloat16), dtype=torch.uint8, device=dev)
+
+    def fwd():
+        moe.moe_forward_train(x, Wg, W13, W2, K, w.renorm, saved=saved, y=y, ws=fws)
+
+    def bwd():
+        moe.moe_backward(dy, x, Wg, W13, W2, K, w.renorm, saved, grads=grads, ws=bws)
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms_step = _time_region(step, args.steps, torch)
+    wall = time.perf_counter() - t0
+    R = args.stage_reps
+    ms_fwd = _time_region(fwd, R, torch)
+    ms_bwd = _time_region(bwd, R, torch)
+
+    # Backward stages alone, on the saved tensors.
+    off, perm, inv = saved["offsets"], saved["perm"], saved["inv"]
+    dY, dw = moe.moe_combine_backward(dy, saved["Y_perm"], inv, saved["topk_w"], n, K)
+    dgu = moe.moe_expert_w2_backward(dY, off, W2, saved["gate_up"])
+    dX = moe.moe_expert_w13_backward(dgu, off, W13)
+    rb = moe.moe_route_backward(x, Wg, saved["logits"], saved["topk_ids"], saved["topk_w"], dw, w.renorm)
+    dx = moe.moe_dispatch_backward(dX, inv, n, K, add=rb["dx_router"])
+    x_perm = moe.moe_permute(saved["topk_ids"], x, E)["x_perm"]
+    dW2 = moe.moe_expert_weight_grad(saved["h"], dY, off)
+    dW13 = moe.moe_expert_weight_grad(x_perm, dgu, off)
+    meta = moe.moe_permute(saved["topk_ids"], None, E)
+    torch.cuda.synchronize()
+    hit = int((meta["counts"].cpu().numpy() > 0).sum())
+    st = {
+        "combine_bwd": _time_region(lambda: moe.moe_combine_backward(dy, saved["Y_perm"], inv, saved["topk_w"], n, K,
+                                                                     dY_perm=dY, dw=dw), R, torch),
+        "route_bwd": _time_region(lambda: moe.moe_route_backward(x, Wg, saved["logits"], saved["topk_ids"],
+                                                                 saved["topk_w"], dw, w.renorm), R, torch),
+        "gemm2_dgrad_swiglu": _time_region(lambda: moe.moe_expert_w2_backward(dY, off, W2, saved["gate_up"],
+                                                                              dgate_up=dgu), R, torch),
+        "gemm2_wgrad": _time_region(lambda: moe.moe_expert_weight_grad(saved["h"], dY, off, dW=dW2), R, torch),
+        "gemm1_dgrad": _time_region(lambda: moe.moe_expert_w13_backward(dgu, off, W13, dX_perm=dX), R, torch),
+        "dispatch_bwd": _time_region(lambda: moe.moe_dispatch_backward(dX, inv, n, K, add=rb["dx_router"], dx=dx),
+                                     R, torch),
+        "gemm1_wgrad": _time_region(lambda: moe.moe_expert_weight_grad(x_perm, dgu, off, dW=dW13), R, torch),
+    }
+    nk = n * K
+    f_small, f_big = 2.0 * nk * H * I, 2.0 * nk * H * 2 * I
+    flops = {"gemm2_dgrad_swiglu": f_small, "gemm2_wgrad": f_small, "gemm1_dgrad": f_big, "gemm1_wgrad": f_big}
+    bytes_ = {
+        "combine_bwd": n * H * 2 + 2 * nk * H * 2 + nk * 12,
+        "route_bwd": n * E * 4 + nk * 12 + n * H * 2 + H * E * 2 + n * E * 4 + n * H * 4 + H * E * 4,
+        "dispatch_bwd": nk * H * 2 + nk * 4 + n * H * 4 + n * H * 2,
+    }
+    stages = {}
+    for k, ms in st.items():
+        s_ = {"ms": round(ms, 5)}
+        if k in flops:
+            s_["TFLOP/s"] = round(flops[k] / (ms * 1e-3) / 1e12, 1)
+            s_["frac_bf16_peak"] = round(flops[k] / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        else:
+            s_["GB/s"] = round(bytes_[k] / (ms * 1e-3) / 1e9, 1)
+            s_["frac_hbm"] = round(bytes_[k] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)
+        stages[k] = s_
+    bwd_gemm_ms = sum(st[k] for k in flops)
+    bwd_gemm_tf = sum(flops.values()) / (bwd_gemm_ms * 1e-3) / 1e12
+    dom = max(flops, key=lambda k: st[k])
+    dom_tf = flops[dom] / (st[dom] * 1e-3) / 1e12
+    cpu = None if args.no_cpu_baseline else _cpu_baseline_train(w, dy_seed=w.n, min_seconds=args.cpu_seconds)
+    out = {
+        "metric": "MoE layer fwd+bwd tokens/s (training step of one layer), OLMoE n=4096",
+        "value": round(n / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "ms_forward_train": round(ms_fwd, 5),
+        "ms_backward": round(ms_bwd, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) tokens and upstream gradient, N(0,0.02) weights, OLMoE layer shapes)",
+        "config": {"workload": "olmoe_train_bf16", "n": n, "H": H, "I": I, "E": E, "K": K, "renorm": bool(w.renorm)},
+        "backward_grouped_gemm": {"TFLOP/s": round(bwd_gemm_tf, 1),
+                                  "frac_bf16_peak": round(bwd_gemm_tf / PEAK_BF16_TFLOPS, 4),
+                                  "GFLOP": round(sum(flops.values()) / 1e9, 1)},
+        "stages": stages,
+        "roofline": {"kernel": f"gemm_bwd_bf16_kernel ({dom})", "bound": "mfma", "achieved": round(dom_tf, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "experts_hit": hit,
+        "wall_s_timed_region": round(wall, 3),
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def _cpu_baseline_train(w, dy_seed, min_seconds, sample_tokens=512):
+    """The fp64 oracle's gradient on the host, on the first `sample_tokens` tokens of the layer."""
+    import oracle
+    from workloads import random_bf16_matrix
+
+    m = min(sample_tokens, w.n)
+    dy = random_bf16_matrix(np.random.default_rng(dy_seed), (w.n, w.H))[1][:m]
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.backward(w.x_f32[:m], w.W_gate_f32, w.W13_f32, w.W2_f32, w.K, w.renorm, dy, bias=w.bias)
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    el = time.perf_counter() - t0
+    return {
+        "value": round(m * reps / el, 1),
+        "unit": "tokens/s",
+        "cores": _blas_threads(),
+        "kind": "oracle",
+        "sample": f"fp64 forward + gradient of the first {m} tokens of the layer, {reps} repetitions, {el:.1f} s",
+    }
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+
+        return int(max([d.get("num_threads", 1) for d in threadpool_info()] or [1]))
+    except Exception:  # noqa: BLE001
+        return len(os.sched_getaffinity(0))
+
+
 def _cpu_baseline(w, min_seconds):
     """The fp64 oracle (as it stands) on the host: full-layer forwards until min_seconds pass."""
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = len(os.sched_getaffinity(0))
+    threads = _blas_threads()
     reps = 0
     t0 = time.perf_counter()
     while True:

@@ -362,10 +362,13 @@ moe_status moe_dispatch_backward(const void* dX_perm, const int32_t* inv, const 
  *   W_gate unused when dx_router is NULL; H is only checked when one of
  *   dx_router, dW_gate, dbias is wanted); logits (n, E) fp32 as written by
  *   moe_route; topk_ids, topk_w (n, K) as written by moe_route; dw (n, K) fp32.
- *   The softmax is recomputed from the logits in fp32. dW_gate and dbias sum
- *   over at most 32 token chunks in a fixed order.
- *   ws  moe_route_backward_workspace_size(n, H, E) bytes (0 when dW_gate and
- *       dbias are NULL: ws may then be NULL).
+ *   The softmax is recomputed from the logits in fp32. For bf16 with E a
+ *   multiple of 32 the two router products run on MFMA with dlogits split
+ *   into bf16 halves hi + lo (their sum is dlogits to about 2^-18 relative);
+ *   otherwise with fp32 FMAs. dW_gate and dbias are sums of per-chunk partial
+ *   sums taken in a fixed order.
+ *   ws  moe_route_backward_workspace_size(n, H, E) bytes when any of
+ *       dx_router, dW_gate, dbias is wanted (else unused and may be NULL).
  * ------------------------------------------------------------------------- */
 size_t moe_route_backward_workspace_size(int n, int H, int E);
 moe_status moe_route_backward(const void* x, const void* W_gate, const float* logits, const int32_t* topk_ids,

@@ -577,7 +577,7 @@ def moe_route_backward(x, W_gate, logits, topk_ids, topk_w, dw, renorm: bool, wa
         dW_gate=_empty((H, E), torch.float32, dev) if want_weights else None,
         dbias=_empty((E,), torch.float32, dev) if want_weights else None,
     )
-    nbytes = lib.moe_route_backward_workspace_size(n, H, E) if want_weights else 0
+    nbytes = lib.moe_route_backward_workspace_size(n, H, E) if (want_weights or want_dx) else 0
     ws = _workspace(nbytes, dev, ws)
     code = lib.moe_route_backward(
         _ptr(x), _ptr(W_gate), _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _ptr(dw), n, H, E, K, int(bool(renorm)),

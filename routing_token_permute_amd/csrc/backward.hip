@@ -116,18 +116,28 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const void* __restrict
 
 // Router backward, per block of kRbTok tokens. Phase 1 (one wave per token):
 // softmax from the saved fp32 logits, the renormalisation and softmax
-// backward, dlogits written to HBM and LDS. Phase 2: dx_router = dlogits .
-// W_gate^T, one thread per hidden column h over all tokens of the block.
+// backward, dlogits written to HBM and LDS.
+// PREP (bf16, E a multiple of 32): the two router products then run on MFMA
+// (grouped_gemm_bwd.hip), so phase 1 also writes dlogits split into bf16
+// halves, hilo[i] = [hi | lo] with hi = bf16(d) and lo = bf16(d - hi) (their
+// sum is d to about 2^-18 relative), the block's column sums of dlogits
+// (part_b[block][e], tokens in order) and, from block 0, the row offsets the
+// GEMMs group by: row_off = {0, n} and chunk_off[g] = min(n, g * chunk).
+// Otherwise phase 2 computes dx_router = dlogits . W_gate^T here, one thread
+// per hidden column h over all tokens of the block.
 constexpr int kRbTok = 16;
 
-template <bool BF16>
+template <bool BF16, bool PREP>
 __global__ __launch_bounds__(256) void route_bwd_token_kernel(const float* __restrict__ logits,
                                                               const int32_t* __restrict__ ids,
                                                               const float* __restrict__ w,
                                                               const float* __restrict__ dw, int n, int E, int K,
                                                               int renorm, const void* __restrict__ W_gate, int H,
                                                               float* __restrict__ dlogits,
-                                                              float* __restrict__ dx_router) {
+                                                              float* __restrict__ dx_router,
+                                                              uint16_t* __restrict__ hilo, float* __restrict__ part_b,
+                                                              int32_t* __restrict__ row_off,
+                                                              int32_t* __restrict__ chunk_off, int S, int chunk) {
   __shared__ __attribute__((aligned(16))) float dl[kRbTok][kMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * kRbTok;
@@ -176,10 +186,30 @@ __global__ __launch_bounds__(256) void route_bwd_token_kernel(const float* __res
         const float v = __expf(L[e] - m) * rz * (dp - pdp);
         dl[tt][e] = v;
         dlogits[(size_t)i * E + e] = v;
+        if constexpr (PREP) {
+          const uint16_t hi = f32_to_bf16(v);
+          hilo[(size_t)i * 2 * E + e] = hi;
+          hilo[(size_t)i * 2 * E + E + e] = f32_to_bf16(v - bf16_to_f32(hi));
+        }
       }
     }
   }
   __syncthreads();
+  if constexpr (PREP) {
+    if (tid < E) {
+      float v = 0.f;
+      for (int t = 0; t < kRbTok; ++t) v += dl[t][tid];  // rows past n hold zeros
+      part_b[(size_t)blockIdx.x * E + tid] = v;
+    }
+    if (blockIdx.x == 0) {
+      if (tid == 0) {
+        row_off[0] = 0;
+        row_off[1] = n;
+      }
+      for (int g = tid; g <= S; g += 256) chunk_off[g] = (int)min((long long)n, (long long)g * chunk);
+    }
+    return;
+  }
   if (dx_router == nullptr) return;
   const int nt = min(kRbTok, n - t0);
   for (int h = tid; h < H; h += 256) {
@@ -317,7 +347,89 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < words; i += (long long)gridDim.x * 256) p[i] = 0u;
 }
 
+// MFMA path: dW_gate[h][e] = sum_g (part[g][h][e] + part[g][h][E + e]) (the hi
+// and lo halves of chunk g, chunks in order), one thread per (h, e) in the
+// first ceil(H*E / 256) workgroups; dbias[e] = sum_b part_b[b][e], one wave per
+// e in the workgroups after them (lane j sums blocks j, j+64, ... in order,
+// then a fixed butterfly across the lanes).
+__global__ __launch_bounds__(256) void route_bwd_reduce_hilo_kernel(const float* __restrict__ part, int S, int H,
+                                                                    int E, const float* __restrict__ part_b, int nb,
+                                                                    float* __restrict__ dW_gate,
+                                                                    float* __restrict__ dbias) {
+  const long long HE = (long long)H * E;
+  const int wblocks = (int)((HE + 255) / 256);
+  if ((int)blockIdx.x < wblocks) {
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= HE || dW_gate == nullptr) return;
+    const long long h = idx / E, e = idx % E;
+    const float* p = part + (size_t)h * 2 * E + e;
+    const size_t gs = (size_t)H * 2 * E;
+    float v = 0.f;
+    // Batches of 8 chunks: 16 loads in flight, then summed in chunk order.
+    for (int g0 = 0; g0 < S; g0 += 8) {
+      float a[8], b[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        a[j] = g0 + j < S ? p[(size_t)(g0 + j) * gs] : 0.f;
+        b[j] = g0 + j < S ? p[(size_t)(g0 + j) * gs + E] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v += a[j] + b[j];
+    }
+    dW_gate[idx] = v;
+    return;
+  }
+  const int e = ((int)blockIdx.x - wblocks) * 4 + (int)(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (e >= E || dbias == nullptr) return;
+  float v = 0.f;
+  for (int b = lane; b < nb; b += 64) v += part_b[(size_t)b * E + e];
+  v = wave_sum(v);
+  if (lane == 0) dbias[e] = v;
+}
+
+// Token chunks of the MFMA dW_gate product: about one 256-column block of
+// H per compute unit, chunks at least 64 tokens long.
+int route_mfma_chunks(int n, int H) {
+  const int mb = (H + 255) / 256;
+  int S = (256 + mb - 1) / mb;
+  S = std::min(S, 64);
+  S = std::min(S, std::max(1, (n + 63) / 64));
+  return S;
+}
+
+bool route_mfma_path(moe_dtype dt, int E) { return dt == MOE_BF16 && E % 32 == 0; }
+
+// Workspace pieces of the MFMA path, in bytes, each rounded up to 256.
+struct RouteMfmaLayout {
+  size_t hilo, part_b, offs, part, total;
+};
+
+size_t up256(size_t v) { return (v + 255) / 256 * 256; }
+
+RouteMfmaLayout route_mfma_layout(int n, int H, int E) {
+  RouteMfmaLayout L{};
+  const int S = route_mfma_chunks(n, H);
+  size_t o = 0;
+  L.hilo = o;
+  o += up256((size_t)n * 2 * E * 2);
+  L.part_b = o;
+  o += up256((size_t)ceil_div(n, kRbTok) * E * 4);
+  L.offs = o;
+  o += up256((size_t)(S + 3) * 4);
+  L.part = o;
+  o += up256((size_t)S * H * 2 * E * 4);
+  L.total = o;
+  return L;
+}
+
 }  // namespace
+
+size_t route_bwd_workspace(int n, int H, int E) {
+  const size_t fma = up256((size_t)route_bwd_chunks(n) * (H + 1) * E * 4);
+  const size_t mfma = route_mfma_layout(n, H, E).total;
+  return std::max(fma, mfma);
+}
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
   const long long words = (long long)(bytes / 4);
@@ -345,21 +457,48 @@ hipError_t launch_combine_backward(const void* dy, const void* Y_perm, const int
 hipError_t launch_route_backward(const void* x, const void* W_gate, const float* logits, const int32_t* ids,
                                  const float* topk_w, const float* dw, int n, int H, int E, int K, int renorm,
                                  moe_dtype dt, float* dlogits, float* dx_router, float* dW_gate, float* dbias,
-                                 float* ws, hipStream_t s) {
+                                 void* ws, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const int nb = ceil_div(n, kRbTok);
+  const bool weights = dW_gate != nullptr || dbias != nullptr;
+  hipError_t e = hipSuccess;
+  if (route_mfma_path(dt, E) && (dx_router != nullptr || weights)) {
+    const RouteMfmaLayout L = route_mfma_layout(n, H, E);
+    char* base = (char*)ws;
+    uint16_t* hilo = (uint16_t*)(base + L.hilo);
+    float* part_b = (float*)(base + L.part_b);
+    int32_t* row_off = (int32_t*)(base + L.offs);
+    int32_t* chunk_off = row_off + 2;
+    float* part = (float*)(base + L.part);
+    const int S = route_mfma_chunks(n, H);
+    const int chunk = ceil_div(n, S);
+    route_bwd_token_kernel<true, true><<<nb, 256, 0, s>>>(logits, ids, topk_w, dw, n, E, K, renorm, W_gate, H,
+                                                          dlogits, nullptr, hilo, part_b, row_off, chunk_off, S,
+                                                          chunk);
+    e = hipGetLastError();
+    if (e == hipSuccess && dx_router != nullptr) e = launch_router_dx_mfma(hilo, row_off, n, W_gate, H, E, dx_router, s);
+    if (e == hipSuccess && weights) e = launch_router_dw_mfma(x, hilo, chunk_off, S, n, H, E, part, s);
+    if (e == hipSuccess && weights) {
+      const int blocks = ceil_div((long long)H * E, 256) + ceil_div(E, 4);
+      route_bwd_reduce_hilo_kernel<<<blocks, 256, 0, s>>>(part, S, H, E, part_b, nb, dW_gate, dbias);
+      e = hipGetLastError();
+    }
+    return e;
+  }
   if (dt == MOE_BF16)
-    route_bwd_token_kernel<true><<<nb, 256, 0, s>>>(logits, ids, topk_w, dw, n, E, K, renorm, W_gate, H, dlogits,
-                                                    dx_router);
+    route_bwd_token_kernel<true, false><<<nb, 256, 0, s>>>(logits, ids, topk_w, dw, n, E, K, renorm, W_gate, H,
+                                                           dlogits, dx_router, nullptr, nullptr, nullptr, nullptr, 0,
+                                                           0);
   else
-    route_bwd_token_kernel<false><<<nb, 256, 0, s>>>(logits, ids, topk_w, dw, n, E, K, renorm, W_gate, H, dlogits,
-                                                     dx_router);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || (dW_gate == nullptr && dbias == nullptr)) return e;
+    route_bwd_token_kernel<false, false><<<nb, 256, 0, s>>>(logits, ids, topk_w, dw, n, E, K, renorm, W_gate, H,
+                                                            dlogits, dx_router, nullptr, nullptr, nullptr, nullptr, 0,
+                                                            0);
+  e = hipGetLastError();
+  if (e != hipSuccess || !weights) return e;
   const int S = route_bwd_chunks(n);
   const int chunk = ceil_div(n, S);
-  float* part = ws;
-  float* part_b = ws + (size_t)S * H * E;
+  float* part = (float*)ws;
+  float* part_b = part + (size_t)S * H * E;
   dim3 g(ceil_div(H, 64), S);
   if (dt == MOE_BF16)
     route_bwd_weight_kernel<true><<<g, 256, 0, s>>>(x, dlogits, n, H, E, chunk, part, part_b);

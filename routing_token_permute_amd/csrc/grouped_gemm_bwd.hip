@@ -39,7 +39,11 @@ namespace {
 
 constexpr int kBwdBM = 256, kBwdBK = 32, kBwdWM = 4, kBwdWN = 4;
 
-enum BwdMode : int { kDgradSwiglu = 0, kDgrad = 1, kWgrad = 2 };
+// kDgradF32 and kWgradF32 are the data- and weight-gradient layouts with fp32
+// outputs (for the router's products, whose gradients stay fp32); in
+// kDgradF32 the k index of B restarts every `kwrap` columns, so that
+// [hi | lo] halves of a split A operand meet the same B values.
+enum BwdMode : int { kDgradSwiglu = 0, kDgrad = 1, kWgrad = 2, kDgradF32 = 3, kWgradF32 = 4 };
 
 // Source of every k-row copied past the end of an expert's rows (zero at
 // program load; nothing writes it).
@@ -57,16 +61,19 @@ struct BTile {
 //    (rows, Ndim) operand, ldb.
 // C: data gradients: (rows, ldc) rows; kDgradSwiglu writes dgate at column n
 //    and dup at column I + n. Weight gradients: C + e * c_stride, (Mdim, Ndim)
-//    with row stride ldc.
+//    with row stride ldc. bf16, or fp32 in the F32 modes.
 // gu: kDgradSwiglu only, the saved pre-activations [gate | up], row stride 2I.
 template <int MODE>
 __global__ __launch_bounds__(64 * kBwdWM * kBwdWN, 1) void gemm_bwd_bf16_kernel(
     const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ B, int ldb, long long b_stride,
     const int32_t* __restrict__ offsets, int E, int rows, int Mdim, int Ndim, int Kdim,
-    const uint16_t* __restrict__ gu, int I, uint16_t* __restrict__ C, int ldc, long long c_stride, int MB, int NB,
-    int n_slots) {
+    const uint16_t* __restrict__ gu, int I, void* __restrict__ Cv, int ldc, long long c_stride, int MB, int NB,
+    int n_slots, int kwrap) {
   constexpr int BM = kBwdBM, BK = kBwdBK, WM = kBwdWM, WN = kBwdWN;
-  constexpr bool WGRAD = MODE == kWgrad;
+  constexpr bool WGRAD = MODE == kWgrad || MODE == kWgradF32;
+  constexpr bool OUTF32 = MODE == kDgradF32 || MODE == kWgradF32;
+  uint16_t* __restrict__ C = (uint16_t*)Cv;
+  float* __restrict__ Cf = (float*)Cv;
   using Cfg = TileCfg<BM, BK>;
   constexpr int A_BYTES = Cfg::A_BYTES, STAGE = Cfg::STAGE, NSTAGE = Cfg::NSTAGE;
   constexpr int NW = WM * WN;
@@ -161,7 +168,9 @@ __global__ __launch_bounds__(64 * kBwdWM * kBwdWN, 1) void gemm_bwd_bf16_kernel(
 #pragma unroll
     for (int j = 0; j < REG; ++j) {
       const uint16_t* p;
-      if constexpr (!WGRAD) {
+      if constexpr (MODE == kDgradF32) {
+        p = src[j] + (size_t)(a_half ? kt * BK : (kt * BK) % kwrap);
+      } else if constexpr (!WGRAD) {
         p = src[j] + (size_t)kt * BK;
       } else {
         const int row = kr0 + kt * BK + srow[j];
@@ -271,7 +280,24 @@ __global__ __launch_bounds__(64 * kBwdWM * kBwdWN, 1) void gemm_bwd_bf16_kernel(
     for (int mt = 0; mt < MT; ++mt) {
       if (mt >= vm) continue;
       const int row = wm * (BM / WM) + mt * 16 + li;
-      if constexpr (WGRAD) {
+      if constexpr (OUTF32) {
+        // Four consecutive fp32 columns per lane and tile: one 16-byte store.
+        bool ok;
+        float* crow;
+        if constexpr (WGRAD) {
+          const int m = t.mb * BM + row;
+          ok = m < Mdim;
+          crow = Cf + (size_t)t.e * c_stride + (size_t)min(m, Mdim - 1) * ldc;
+        } else {
+          ok = row < t.r1 - t.r0;
+          crow = Cf + (size_t)(t.r0 + min(row, t.r1 - t.r0 - 1)) * ldc;
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int col = t.nb * BN + wn * (BN / WN) + nt * 16 + 4 * g;
+          if (ok && col < Ndim) *(f32x4_t*)(crow + col) = acc[mt][nt];
+        }
+      } else if constexpr (WGRAD) {
         const int m = t.mb * BM + row;
         uint16_t* crow = C + (size_t)t.e * c_stride + (size_t)min(m, Mdim - 1) * ldc;
 #pragma unroll
@@ -408,17 +434,18 @@ __global__ __launch_bounds__(256) void gemm_bwd_f32_kernel(const float* __restri
 template <int MODE>
 hipError_t launch_bwd(const void* A, int lda, const void* B, int ldb, long long b_stride, const int32_t* offsets,
                       int E, int rows, int Mdim, int Ndim, int Kdim, const void* gu, int I, void* C, int ldc,
-                      long long c_stride, moe_dtype dt, hipStream_t s) {
+                      long long c_stride, moe_dtype dt, hipStream_t s, int kwrap = 0) {
+  constexpr bool WG = MODE == kWgrad || MODE == kWgradF32;
   if (dt == MOE_BF16) {
     const int NB = ceil_div(Ndim, BN);
-    const int MB = MODE == kWgrad ? ceil_div(Mdim, kBwdBM) : 1;
-    const int n_slots = MODE == kWgrad ? E * MB * NB : max_row_tiles(rows, E, kBwdBM) * NB;
+    const int MB = WG ? ceil_div(Mdim, kBwdBM) : 1;
+    const int n_slots = WG ? E * MB * NB : max_row_tiles(rows, E, kBwdBM) * NB;
     if (n_slots == 0) return hipSuccess;
     const int grid = std::min(n_slots, device_cu_count());
     gemm_bwd_bf16_kernel<MODE><<<grid, 64 * kBwdWM * kBwdWN, 0, s>>>(
         (const uint16_t*)A, lda, (const uint16_t*)B, ldb, b_stride, offsets, E, rows, Mdim, Ndim, Kdim,
-        (const uint16_t*)gu, I, (uint16_t*)C, ldc, c_stride, MB, NB, n_slots);
-  } else {
+        (const uint16_t*)gu, I, C, ldc, c_stride, MB, NB, n_slots, kwrap);
+  } else if constexpr (MODE <= kWgrad) {
     dim3 grid(ceil_div(Ndim, 64), ceil_div(MODE == kWgrad ? Mdim : rows, 4), MODE == kWgrad ? E : 1);
     gemm_bwd_f32_kernel<MODE><<<grid, 256, 0, s>>>((const float*)A, lda, (const float*)B, ldb, b_stride, offsets, E,
                                                    rows, Mdim, Ndim, Kdim, (const float*)gu, I, (float*)C, ldc,
@@ -428,6 +455,20 @@ hipError_t launch_bwd(const void* A, int lda, const void* B, int ldb, long long 
 }
 
 }  // namespace
+
+hipError_t launch_router_dx_mfma(const void* dl_hilo, const int32_t* row_offsets, int n, const void* W_gate, int H,
+                                 int E, float* dx_router, hipStream_t s) {
+  // dx_router = [dl_hi | dl_lo] . [W_gate | W_gate]^T: K = 2E, B's k index wraps at E.
+  return launch_bwd<kDgradF32>(dl_hilo, 2 * E, W_gate, E, 0, row_offsets, 1, n, 0, H, 2 * E, nullptr, 0, dx_router,
+                               H, 0, MOE_BF16, s, E);
+}
+
+hipError_t launch_router_dw_mfma(const void* x, const void* dl_hilo, const int32_t* chunk_offsets, int S, int n,
+                                 int H, int E, float* part, hipStream_t s) {
+  // part[g] = x_g^T . [dl_hi | dl_lo]_g for each token chunk g: (S, H, 2E) fp32.
+  return launch_bwd<kWgradF32>(x, H, dl_hilo, 2 * E, 0, chunk_offsets, S, n, H, 2 * E, 0, nullptr, 0, part, 2 * E,
+                               (long long)H * 2 * E, MOE_BF16, s);
+}
 
 hipError_t launch_w2_backward(const void* dY_perm, const int32_t* offsets, int rows, const void* W2,
                               const void* gate_up, int E, int H, int I, moe_dtype dt, void* dgate_up, hipStream_t s) {

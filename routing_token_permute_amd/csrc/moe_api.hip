@@ -81,7 +81,7 @@ TrainLayout train_layout(int n, int E, int K) {
   return L;
 }
 
-size_t route_bwd_ws(int n, int H, int E) { return align_up((size_t)route_bwd_chunks(n) * (H + 1) * E * 4); }
+size_t route_bwd_ws(int n, int H, int E) { return align_up(route_bwd_workspace(n, H, E)); }
 
 // moe_backward workspace, in order. rows_a holds dY_perm, then dX_perm, then
 // the gathered x_perm (each dead before the next is written, in stream order).
@@ -395,9 +395,10 @@ moe_status moe_route_backward(const void* x, const void* W_gate, const float* lo
     return MOE_EINVAL;
   if (dx_router != nullptr && W_gate == nullptr) return MOE_EINVAL;
   if (weights && x == nullptr) return MOE_EINVAL;
-  if (weights && (ws == nullptr || ws_bytes < route_bwd_ws(n, H, E))) return MOE_EWORKSPACE;
+  if ((weights || dx_router != nullptr) && (ws == nullptr || ws_bytes < route_bwd_ws(n, H, E)))
+    return MOE_EWORKSPACE;
   return from_hip(launch_route_backward(x, W_gate, logits, topk_ids, topk_w, dw, n, H, E, K, renorm, dt, dlogits,
-                                        dx_router, dW_gate, dbias, (float*)ws, stream));
+                                        dx_router, dW_gate, dbias, ws, stream));
 }
 
 size_t moe_backward_workspace_size(int n, int H, int I, int E, int K, moe_dtype dt) {
@@ -440,7 +441,7 @@ moe_status moe_backward(const void* dy, const void* x, const void* W_gate, const
   e = launch_combine_backward(dy, Y_perm, inv, topk_w, n, H, K, dt, rows_a, dw, stream);
   if (e != hipSuccess) return MOE_EHIP;
   e = launch_route_backward(x, W_gate, logits, topk_ids, topk_w, dw, n, H, E, K, renorm, dt, dlogits, dx_router,
-                            dW_gate, dbias, (float*)(base + L.rws), stream);
+                            dW_gate, dbias, base + L.rws, stream);
   if (e != hipSuccess) return MOE_EHIP;
   e = launch_w2_backward(rows_a, offsets, rows, W2, gate_up, E, H, I, dt, dgu, stream);
   if (e != hipSuccess) return MOE_EHIP;

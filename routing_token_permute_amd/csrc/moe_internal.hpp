@@ -98,11 +98,22 @@ hipError_t launch_weight_grad(const void* a, const void* b, const int32_t* offse
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 // Token chunks of the dW_gate reduction for n tokens.
 int route_bwd_chunks(int n);
-// ws: route_bwd_chunks(n) * (H + 1) * E floats (only when dW_gate or dbias is wanted).
+// Workspace bytes of launch_route_backward.
+size_t route_bwd_workspace(int n, int H, int E);
+// ws: route_bwd_workspace(n, H, E) bytes (only used when dx_router, dW_gate
+// or dbias is wanted).
 hipError_t launch_route_backward(const void* x, const void* W_gate, const float* logits, const int32_t* ids,
                                  const float* topk_w, const float* dw, int n, int H, int E, int K, int renorm,
                                  moe_dtype dt, float* dlogits, float* dx_router, float* dW_gate, float* dbias,
-                                 float* ws, hipStream_t s);
+                                 void* ws, hipStream_t s);
+// The router's two products on MFMA (bf16 path, E a multiple of 32), from the
+// split dlogits [hi | lo] (n, 2E) bf16:
+//   dx_router (n, H) fp32 = hilo . [W_gate | W_gate]^T, rows grouped by row_offsets = {0, n};
+//   part (S, H, 2E) fp32 = x_g^T . hilo_g per token chunk g of chunk_offsets (S+1).
+hipError_t launch_router_dx_mfma(const void* dl_hilo, const int32_t* row_offsets, int n, const void* W_gate, int H,
+                                 int E, float* dx_router, hipStream_t s);
+hipError_t launch_router_dw_mfma(const void* x, const void* dl_hilo, const int32_t* chunk_offsets, int S, int n,
+                                 int H, int E, float* part, hipStream_t s);
 
 }  // namespace moe
 
