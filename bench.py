@@ -42,6 +42,8 @@ def _parse():
     p.add_argument("--workload", default="olmoe_bf16",
                    choices=["olmoe_bf16", "olmoe_skewed_bf16", "decode_bf16", "ep_share_bf16", "olmoe_train_bf16"])
     p.add_argument("--stage-reps", type=int, default=20)
+    p.add_argument("--comm-cus", type=int, nargs="*", default=[8, 16, 32, 64],
+                   help="ep_share_bf16: compute units given to the permute/unpermute stream in the CU-masked runs")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle wall time for the CPU baseline")
     p.add_argument("--copy-calibration", action="store_true",
@@ -385,6 +387,23 @@ def _bench_ep_share(args):
                          eps.unpermute(b, s0)), [s0])
     t_c = timed(lambda: eps.run_serial(a, b, W13, W2, ep.E_local, s0), [s0])
     t_d = timed(lambda: eps.run_two_streams(a, b, W13, W2, ep.E_local, compute, comm), [compute, comm])
+    # CU-masked split ([Fusion] §6.4's T_total(S_comm) = max(T_compute(S - S_comm), T_comm(S_comm)) + T_sync):
+    # the permute/unpermute stream gets S_comm compute units, the GEMM stream the rest.
+    split = []
+    for n_comm in args.comm_cus:
+        ms = eps.MaskedStreams(n_comm, dev)
+        try:
+            tc = ms.compute
+            t_comp = timed(lambda: (eps.experts(a, W13, W2, tc), eps.experts(b, W13, W2, tc)), [tc])
+            cm = ms.comm
+            t_comm = timed(lambda: (eps.permute(a, ep.E_local, cm), eps.permute(b, ep.E_local, cm),
+                                    eps.unpermute(a, cm), eps.unpermute(b, cm)), [cm])
+            t_tot = timed(lambda: eps.run_two_streams(a, b, W13, W2, ep.E_local, tc, cm), [tc, cm])
+        finally:
+            torch.cuda.synchronize()
+            ms.close()
+        split.append({"S_comm_cus": n_comm, "T_compute_ms": round(t_comp, 4), "T_comm_ms": round(t_comm, 4),
+                      "T_total_ms": round(t_tot, 4), "T_sync_ms": round(t_tot - max(t_comp, t_comm), 4)})
     rows = 2 * ep.R
     flops = 2 * ep.flops_per_micro_batch
     cpu = None
@@ -421,7 +440,8 @@ def _bench_ep_share(args):
                     "T_C_serial_ms": round(t_c, 4), "T_D_two_streams_ms": round(t_d, 4),
                     "hidden_fraction": round(1 - (t_d - t_a) / t_b, 4), "speedup_serial_over_overlap": round(t_c / t_d, 4),
                     "gemm_TFLOP/s_alone": round(flops / (t_a * 1e-3) / 1e12, 1),
-                    "gemm_TFLOP/s_in_overlap": round(flops / (t_d * 1e-3) / 1e12, 1)},
+                    "gemm_TFLOP/s_in_overlap": round(flops / (t_d * 1e-3) / 1e12, 1),
+                    "cu_split": split},
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(dev),
     }

@@ -143,5 +143,22 @@ inline int device_cu_count() {
   return cached[dev];
 }
 
+// Compute units a launch on stream s can use: the stream's CU mask when it
+// has one (hipExtStreamCreateWithCUMask), else the device's count. A
+// persistent grid larger than this would leave workgroups waiting for a CU
+// while the others hold their whole share of tiles.
+inline int stream_cu_count(hipStream_t s) {
+  const int dev_cus = device_cu_count();
+  if (s == nullptr) return dev_cus;
+  uint32_t mask[16] = {};
+  if (hipExtStreamGetCUMask(s, 16, mask) != hipSuccess) {
+    (void)hipGetLastError();
+    return dev_cus;
+  }
+  int n = 0;
+  for (int i = 0; i < 16; ++i) n += __builtin_popcount(mask[i]);
+  return (n > 0 && n < dev_cus) ? n : dev_cus;
+}
+
 }  // namespace
 }  // namespace moe

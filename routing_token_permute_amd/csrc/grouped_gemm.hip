@@ -449,7 +449,7 @@ void launch_cfg(const void* a, const int32_t* perm, int topk, int n_a, const flo
                 int E, int rows, int Kdim, const void* B, int ldb, long long bstride, int Nout, int up_col, void* C,
                 int ldc, int NB, void* gu_out, hipStream_t s) {
   const int n_slots = max_row_tiles(rows, E, BM) * NB;
-  const int grid = std::min(n_slots, device_cu_count());
+  const int grid = std::min(n_slots, stream_cu_count(s));
   gemm_bf16_kernel<GATED, GATHER, SCATTER, BM, BK, WM, WN, SAVE><<<grid, 64 * WM * WN, 0, s>>>(
       (const uint16_t*)a, perm, topk, n_a, wrow, offsets, E, rows, Kdim, (const uint16_t*)B, ldb, bstride, Nout,
       up_col, (uint16_t*)C, ldc, NB, n_slots, (uint16_t*)gu_out);

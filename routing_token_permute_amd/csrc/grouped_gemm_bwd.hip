@@ -441,7 +441,7 @@ hipError_t launch_bwd(const void* A, int lda, const void* B, int ldb, long long 
     const int MB = WG ? ceil_div(Mdim, kBwdBM) : 1;
     const int n_slots = WG ? E * MB * NB : max_row_tiles(rows, E, kBwdBM) * NB;
     if (n_slots == 0) return hipSuccess;
-    const int grid = std::min(n_slots, device_cu_count());
+    const int grid = std::min(n_slots, stream_cu_count(s));
     gemm_bwd_bf16_kernel<MODE><<<grid, 64 * kBwdWM * kBwdWN, 0, s>>>(
         (const uint16_t*)A, lda, (const uint16_t*)B, ldb, b_stride, offsets, E, rows, Mdim, Ndim, Kdim,
         (const uint16_t*)gu, I, C, ldc, c_stride, MB, NB, n_slots, kwrap);

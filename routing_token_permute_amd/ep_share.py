@@ -107,3 +107,76 @@ def run_two_streams(a: MicroBatch, b: MicroBatch, W13, W2, E_local: int, compute
     unpermute(a, comm)
     comm.wait_event(ev["gemmB"])
     unpermute(b, comm)
+
+
+# ---------------------------------------------------------------------------
+# CU-masked stream split
+# ---------------------------------------------------------------------------
+#
+# "大模型系统中的通算融合" §6.4 models the split of a GPU's compute units
+# between communication and compute as T_total(S_comm) = max(T_compute(S -
+# S_comm), T_comm(S_comm)) + T_sync. Here the permute/unpermute stream gets
+# S_comm compute units and the GEMM stream the rest, through HIP stream CU
+# masks; the grouped GEMM sizes its persistent grid by its stream's mask.
+
+
+def comm_cu_bits(n_comm: int, n_cus: int = 256, xcds: int = 8):
+    """CU indices for the communication stream: n_comm / xcds per XCD, spread
+    so that they stay balanced across XCDs whether the mask's bit i counts CUs
+    XCD by XCD (i // (n_cus / xcds)) or round-robin (i % xcds)."""
+    per = n_cus // xcds
+    if n_comm % xcds or not 0 < n_comm <= n_cus // 2:
+        raise ValueError(f"n_comm={n_comm} must be a positive multiple of {xcds} up to {n_cus // 2}")
+    m = n_comm // xcds
+    bits = []
+    for x in range(xcds):
+        picked = []
+        z = 0
+        while len(picked) < m:
+            for y in range(per // xcds):
+                b = x * per + (x + xcds * y + z) % per
+                if b not in picked:
+                    picked.append(b)
+                if len(picked) == m:
+                    break
+            z += 1
+        bits += picked
+    return sorted(bits)
+
+
+class MaskedStreams:
+    """A compute stream and a communication stream with complementary CU masks
+    (HIP streams created with hipExtStreamCreateWithCUMask, default priority),
+    usable as torch streams. Call close() to destroy them."""
+
+    def __init__(self, n_comm: int, device):
+        import ctypes
+
+        self._hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch has loaded
+        n_cus = torch.cuda.get_device_properties(device).multi_processor_count
+        comm = set(comm_cu_bits(n_comm, n_cus))
+        words = (n_cus + 31) // 32
+
+        def mask(bits):
+            m = (ctypes.c_uint32 * words)()
+            for b in bits:
+                m[b // 32] |= 1 << (b % 32)
+            return m
+
+        self._handles = []
+        streams = []
+        for bits in ([b for b in range(n_cus) if b not in comm], sorted(comm)):
+            h = ctypes.c_void_p()
+            rc = self._hip.hipExtStreamCreateWithCUMask(ctypes.byref(h), ctypes.c_uint32(words), mask(bits))
+            if rc != 0:
+                self.close()
+                raise RuntimeError(f"hipExtStreamCreateWithCUMask failed ({rc})")
+            self._handles.append(h)
+            streams.append(torch.cuda.ExternalStream(h.value, device=device))
+        self.compute, self.comm = streams
+        self.n_comm, self.n_compute = n_comm, n_cus - n_comm
+
+    def close(self):
+        for h in self._handles:
+            self._hip.hipStreamDestroy(h)
+        self._handles = []

@@ -449,3 +449,34 @@ def test_ep_share_two_streams_match_serial(dev):
         for s_mb, t_mb in zip(serial, two):
             assert torch.equal(s_mb.out.view(torch.int16), t_mb.out.view(torch.int16))
             assert torch.equal(s_mb.meta["perm"], t_mb.meta["perm"])
+
+
+def test_ep_share_cu_masked_streams_match_serial(dev):
+    """The two-stream schedule on CU-masked streams (16 units for permute/unpermute, the rest for the GEMMs)
+    gives bitwise the outputs of the serial run; the GEMM sizes its grid by its stream's mask."""
+    from routing_token_permute_amd import ep_share as eps
+
+    ep = make_config("ep_share_bf16")
+    t13 = dev_tensor(ep.bits("W13"), "bf16", dev)
+    t2 = dev_tensor(ep.bits("W2"), "bf16", dev)
+
+    def mbs():
+        return [eps.prepare(eps.MicroBatch(dev_tensor(m.x_bits(), "bf16", dev),
+                                           torch.from_numpy(m.eid.reshape(-1, 1)).to(dev)), ep.E_local, ep.I)
+                for m in ep.micro_batches]
+
+    serial = mbs()
+    eps.run_serial(serial[0], serial[1], t13, t2, ep.E_local, torch.cuda.current_stream(dev))
+    torch.cuda.synchronize()
+    ms = eps.MaskedStreams(16, dev)
+    try:
+        assert ms.n_compute == torch.cuda.get_device_properties(dev).multi_processor_count - 16
+        for _ in range(2):
+            over = mbs()
+            eps.run_two_streams(over[0], over[1], t13, t2, ep.E_local, ms.compute, ms.comm)
+            torch.cuda.synchronize()
+            for s_, o_ in zip(serial, over):
+                assert torch.equal(s_.out.view(torch.int16), o_.out.view(torch.int16))
+    finally:
+        torch.cuda.synchronize()
+        ms.close()

@@ -213,3 +213,20 @@ def test_backward_calls_reject_bad_arguments(lib):
     bad = list(fargs)
     bad[-2] = 0
     assert lib.moe_forward_train(*bad) == EWS
+
+
+def test_comm_cu_bits_balanced_across_xcds():
+    """The communication stream's CUs are spread evenly over the 8 XCDs under both ways of numbering CUs in a
+    mask (XCD by XCD, or round-robin), and the sizes outside the supported range are refused."""
+    import collections
+
+    from routing_token_permute_amd.ep_share import comm_cu_bits
+
+    for n in (8, 16, 24, 32, 64, 128):
+        b = comm_cu_bits(n)
+        assert len(b) == n == len(set(b)) and all(0 <= x < 256 for x in b)
+        assert sorted(collections.Counter(x // 32 for x in b).values()) == [n // 8] * 8
+        assert sorted(collections.Counter(x % 8 for x in b).values()) == [n // 8] * 8
+    for bad in (0, 7, 12, 136):
+        with pytest.raises(ValueError):
+            comm_cu_bits(bad)
