@@ -16,6 +16,7 @@ Pages cited in this package (titles as they appear on the pages):
               aigcage.com.
 """
 
+from . import fp8  # noqa: F401
 from .moe_oracle import (  # noqa: F401
     backward,
     combine_backward,

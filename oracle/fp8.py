@@ -1,0 +1,110 @@
+"""fp64 CPU oracle of the layer with FP8 expert weights.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): imported by the test
+suite, the smoke check and the benchmark's CPU-baseline leg, never by the
+product path.
+
+[Fusion] §8.4 ("低精度通信") lists FP8 payloads with per-token or per-block
+scales and asks that the GEMM consume the low-precision format directly, and
+§4.4 describes Mega MoE's first linear with low-precision weights prepared
+ahead of time. Here the expert weights W13 and W2 are stored as FP8 E4M3 with
+one fp32 scale per output column (a per-block scale whose block is the whole
+contraction dimension), prepared once, and the layer is otherwise Algorithm 2.
+
+FP8 E4M3 (the OCP 8-bit floating-point format, "E4M3FN"): 1 sign bit, 4
+exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds the
+subnormals m * 2^-9; no infinities; the two codes with all exponent and
+mantissa bits set (0x7F, 0xFF) are NaN, so the largest finite value is
+1.75 * 2^8 = 448 (code 0x7E).
+
+Readings (also listed with the design notes):
+  * Scale of column n: s = amax_k |w[k, n]| / 448 in fp32 (one rounded
+    division); s = 1 when the column is all zero.
+  * Code of w: the E4M3 value nearest to the fp32 quotient w / s (one rounded
+    fp32 division), ties to the code with an even mantissa, magnitudes beyond
+    448 saturated to 448 (they can only arise from the rounding of w / s).
+  * Dequantized weight: decode(code) * s, exact in fp64.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import moe_oracle
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode_table() -> np.ndarray:
+    """Value of each of the 256 codes (float64; NaN for 0x7F and 0xFF), from the format's definition."""
+    vals = np.empty(256, dtype=np.float64)
+    for c in range(256):
+        sign = -1.0 if c & 0x80 else 1.0
+        e = (c >> 3) & 0xF
+        m = c & 0x7
+        if e == 0xF and m == 0x7:
+            vals[c] = np.nan
+        elif e == 0:
+            vals[c] = sign * m * 2.0**-9
+        else:
+            vals[c] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+_TABLE = e4m3_decode_table()
+# Non-negative finite codes 0x00..0x7E in increasing order of value.
+_POS_CODES = np.arange(0x7F, dtype=np.int64)
+_POS_VALS = _TABLE[_POS_CODES]
+assert np.all(np.diff(_POS_VALS) > 0)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    return _TABLE[np.asarray(codes, dtype=np.int64)]
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest E4M3 code of each value (ties to even mantissa, saturating at +-448); uint8.
+
+    Works on the exact values given (the callers pass fp32 quotients). NaN is
+    not expected and not handled.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.searchsorted(_POS_VALS, a, side="left")  # first value >= a
+    hi = np.minimum(hi, len(_POS_VALS) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _POS_VALS[lo]
+    d_hi = _POS_VALS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (_POS_CODES[hi] % 2 == 0))
+    code = np.where(pick_hi, _POS_CODES[hi], _POS_CODES[lo])
+    code = np.where(a == _POS_VALS[hi], _POS_CODES[hi], code)  # exact hits (covers a == 0)
+    sign = (np.signbit(x) & (code != 0)).astype(np.int64) << 7
+    return (code | sign).astype(np.uint8)
+
+
+def quantize_columns(W) -> tuple:
+    """FP8 weights of one stack of matrices W (E, K, N) (row-major, K rows of N
+    columns), one scale per output column n.
+
+    Returns (codes (E, N, K) uint8 -- each column's K codes contiguous, the
+    layout the device GEMMs read -- and scales (E, N) float32).
+    """
+    W32 = np.asarray(W, dtype=np.float32)
+    amax = np.max(np.abs(W32), axis=1)  # (E, N) fp32, exact
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    q = (W32 / scale[:, None, :]).astype(np.float32)  # one rounded fp32 division per weight
+    codes = e4m3_encode(q)  # (E, K, N)
+    return np.ascontiguousarray(np.transpose(codes, (0, 2, 1))), scale
+
+
+def dequantize_columns(codes, scale) -> np.ndarray:
+    """W'[e, k, n] = decode(codes[e, n, k]) * scale[e, n] in fp64, shape (E, K, N)."""
+    v = e4m3_decode(codes) * np.asarray(scale, dtype=np.float64)[:, :, None]
+    return np.transpose(v, (0, 2, 1))
+
+
+def forward_fp8(x, W_gate, W13_codes, s13, W2_codes, s2, K: int, renorm: bool, bias=None, **kw):
+    """Algorithm 2 with the dequantized FP8 expert weights (moe_oracle.forward on W13', W2')."""
+    W13 = dequantize_columns(W13_codes, s13)
+    W2 = dequantize_columns(W2_codes, s2)
+    return moe_oracle.forward(x, W_gate, W13, W2, K, renorm, bias=bias, **kw)

@@ -608,3 +608,145 @@ def test_planted_backward_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(om, "combine_backward", cb_unweighted)
     assert not _pins_pass(check)
     monkeypatch.undo()
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 weights: the format's definition and the column quantizer
+# ---------------------------------------------------------------------------
+
+
+def test_e4m3_table_landmarks():
+    """Values fixed by the format: 1.0 = 0x38, the largest finite 448 = 0x7E, the smallest normal 2^-6 = 0x08,
+    the smallest subnormal 2^-9 = 0x01, zero and minus zero, NaN at 0x7F/0xFF, and 127 distinct non-negative
+    finite values in increasing code order."""
+    t = oracle.fp8.e4m3_decode_table()
+    assert t[0x38] == 1.0 and t[0x7E] == 448.0 and t[0x08] == 2.0**-6 and t[0x01] == 2.0**-9
+    assert t[0x00] == 0.0 and t[0x80] == 0.0 and np.signbit(t[0x80])
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    assert t[0xB8] == -1.0 and t[0xFE] == -448.0
+    assert t[0x3C] == 1.5 and t[0x40] == 2.0 and t[0x07] == 7 * 2.0**-9
+    pos = t[:0x7F]
+    assert np.all(np.diff(pos) > 0) and len(np.unique(pos)) == 127
+    np.testing.assert_array_equal(t[0x80:0xFF], -t[0x00:0x7F])
+
+
+def test_e4m3_encode_round_trip_ties_and_saturation():
+    f = oracle.fp8
+    t = f.e4m3_decode_table()
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF, 0x80)])
+    np.testing.assert_array_equal(f.e4m3_encode(t[codes]), codes.astype(np.uint8))  # exact values map to themselves
+    # Midpoints between neighbours go to the even code; just off the midpoint, to the nearer one.
+    for c in range(0, 0x7E):
+        a, b = t[c], t[c + 1]
+        mid = (a + b) / 2
+        even = c if c % 2 == 0 else c + 1
+        assert f.e4m3_encode(np.array([mid]))[0] == even
+        assert f.e4m3_encode(np.array([np.nextafter(mid, -np.inf)]))[0] == c
+        assert f.e4m3_encode(np.array([np.nextafter(mid, np.inf)]))[0] == c + 1
+        assert f.e4m3_encode(np.array([-mid]))[0] == (even | 0x80 if even else 0)
+    # Saturation beyond the largest finite value; tiny values round to zero.
+    np.testing.assert_array_equal(f.e4m3_encode(np.array([448.0, 464.0, 1e6, -1e6])), [0x7E, 0x7E, 0x7E, 0xFE])
+    assert f.e4m3_encode(np.array([2.0**-11]))[0] == 0  # a quarter of the smallest subnormal
+
+
+def test_e4m3_encode_error_bound_and_monotone():
+    """|x - decode(encode(x))| is at most half the gap to the neighbouring value (the definition of nearest),
+    and encoding is monotone."""
+    f = oracle.fp8
+    rng = np.random.default_rng(8)
+    x = np.sort(np.concatenate([rng.uniform(-448, 448, 4000), rng.normal(0, 1e-2, 4000), rng.normal(0, 3, 4000)]))
+    c = f.e4m3_encode(x)
+    v = f.e4m3_decode(c)
+    pos = f.e4m3_decode_table()[:0x7F]
+    gaps = np.diff(pos)
+    # gap at |x|: the spacing of the interval containing |x|
+    idx = np.clip(np.searchsorted(pos, np.abs(x), side="right") - 1, 0, len(gaps) - 1)
+    assert np.all(np.abs(x - v) <= gaps[idx] / 2 + 1e-300)
+    assert np.all(np.diff(v) >= 0)
+
+
+def test_quantize_columns_scales_and_exact_grid():
+    """Each column's largest magnitude maps to 448 (code 0x7E) and the scales are amax / 448 in fp32; a column
+    that already lies on the FP8 grid times a power of two is reproduced exactly; a zero column gets scale 1."""
+    f = oracle.fp8
+    rng = np.random.default_rng(3)
+    W = rng.standard_normal((2, 40, 24)).astype(np.float32) * np.float32(0.02)
+    W[1, :, 5] = 0.0
+    t = f.e4m3_decode_table()
+    grid = t[rng.integers(0, 0x7F, 40)] * 2.0**-12  # FP8 values times 2^-12, exact in fp32
+    grid[0] = 448 * 2.0**-12  # make the column's amax a grid value so its scale is exactly 2^-12
+    W[0, :, 3] = grid.astype(np.float32)
+    codes, s = f.quantize_columns(W)
+    assert codes.shape == (2, 24, 40) and codes.dtype == np.uint8 and s.dtype == np.float32
+    amax = np.abs(W).max(axis=1)
+    exp_s = np.where(amax > 0, amax / np.float32(448), np.float32(1))
+    np.testing.assert_array_equal(s, exp_s)
+    for e in range(2):
+        for n in range(24):
+            if amax[e, n] > 0:
+                k = np.argmax(np.abs(W[e, :, n]))
+                assert codes[e, n, k] & 0x7F == 0x7E
+    assert s[1, 5] == 1.0 and (codes[1, 5] == 0).all()
+    Wd = f.dequantize_columns(codes, s)
+    np.testing.assert_array_equal(Wd[0, :, 3], grid)
+    # Relative error per column bounded by the format's half-ulp at the top of the range (2^-4 of amax).
+    assert np.all(np.abs(Wd - W) <= amax[:, None, :] * 2.0**-4 * 1.0000001)
+
+
+def test_forward_fp8_is_the_layer_on_dequantized_weights():
+    """With weights already on the scaled FP8 grid the FP8 layer equals the plain layer on those weights, and
+    for random weights it stays within the quantisation error of the bf16 layer."""
+    f = oracle.fp8
+    w = make_layer(20, 32, 16, 4, 2, dtype="f32", seed=6)
+    c13, s13 = f.quantize_columns(w.W13_f32)
+    c2, s2 = f.quantize_columns(w.W2_f32)
+    got = f.forward_fp8(w.x_f32, w.W_gate_f32, c13, s13, c2, s2, w.K, w.renorm)
+    W13d, W2d = f.dequantize_columns(c13, s13), f.dequantize_columns(c2, s2)
+    ref = oracle.forward(w.x_f32, w.W_gate_f32, W13d, W2d, w.K, w.renorm)
+    np.testing.assert_allclose(got["y"], ref["y"], rtol=0, atol=0)
+    c13b, s13b = f.quantize_columns(W13d.astype(np.float32))  # quantizing grid values again changes nothing
+    np.testing.assert_array_equal(c13b, c13)
+    np.testing.assert_array_equal(s13b, s13)
+    plain = oracle.forward(w.x_f32, w.W_gate_f32, w.W13_f32, w.W2_f32, w.K, w.renorm)
+    rel = np.linalg.norm(got["y"] - plain["y"]) / np.linalg.norm(plain["y"])
+    assert 1e-3 < rel < 0.1
+
+
+def test_planted_fp8_mistakes_are_caught(monkeypatch):
+    f = oracle.fp8
+    orig_encode = f.e4m3_encode
+
+    # 1. Ties rounded away from zero instead of to even.
+    def encode_ties_away(x):
+        x = np.asarray(x, dtype=np.float64)
+        c = orig_encode(x).astype(np.int64)
+        v = f.e4m3_decode(c)
+        nxt = f.e4m3_decode(np.minimum((c & 0x7F) + 1, 0x7E) | (c & 0x80))
+        tie = np.abs(np.abs(x) - (np.abs(v) + np.abs(nxt)) / 2) == 0
+        return np.where(tie & (np.abs(x) > np.abs(v)), (c & 0x7F) + 1 | (c & 0x80), c).astype(np.uint8)
+
+    monkeypatch.setattr(f, "e4m3_encode", encode_ties_away)
+    assert not _pins_pass(test_e4m3_encode_round_trip_ties_and_saturation)
+    monkeypatch.undo()
+
+    # 2. Exponent bias 8 in the decode table.
+    orig_table = f.e4m3_decode_table
+
+    def table_bias8():
+        return orig_table() / 2.0
+
+    monkeypatch.setattr(f, "e4m3_decode_table", table_bias8)
+    assert not _pins_pass(test_e4m3_table_landmarks)
+    monkeypatch.undo()
+
+    # 3. Scales per input row instead of per output column.
+    def quantize_rows(W):
+        W32 = np.asarray(W, dtype=np.float32)
+        amax = np.max(np.abs(W32), axis=2)
+        scale = np.where(amax > 0, amax / np.float32(448), np.float32(1)).astype(np.float32)
+        codes = orig_encode((W32 / scale[:, :, None]).astype(np.float32))
+        return np.ascontiguousarray(np.transpose(codes, (0, 2, 1))), scale
+
+    monkeypatch.setattr(f, "quantize_columns", quantize_rows)
+    assert not _pins_pass(test_quantize_columns_scales_and_exact_grid)
+    monkeypatch.undo()
