@@ -40,7 +40,8 @@ def _parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="olmoe_bf16",
-                   choices=["olmoe_bf16", "olmoe_skewed_bf16", "decode_bf16", "ep_share_bf16", "olmoe_train_bf16"])
+                   choices=["olmoe_bf16", "olmoe_skewed_bf16", "decode_bf16", "ep_share_bf16", "olmoe_train_bf16",
+                            "decode_fp8", "olmoe_fp8"])
     p.add_argument("--stage-reps", type=int, default=20)
     p.add_argument("--comm-cus", type=int, nargs="*", default=[8, 16, 32, 64],
                    help="ep_share_bf16: compute units given to the permute/unpermute stream in the CU-masked runs")
@@ -193,6 +194,9 @@ def main():
         return
     if args.workload == "olmoe_train_bf16":
         _bench_train(args)
+        return
+    if args.workload in ("decode_fp8", "olmoe_fp8"):
+        _bench_fp8(args)
         return
     dev = torch.device("cuda:0")
     w = make_config(args.workload)
@@ -563,6 +567,121 @@ def _bench_train(args):
         "roofline": {"kernel": f"gemm_bwd_bf16_kernel ({dom})", "bound": "mfma", "achieved": round(dom_tf, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": None},
+        "experts_hit": hit,
+        "wall_s_timed_region": round(wall, 3),
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def _bench_fp8(args):
+    """The layer with FP8 E4M3 expert weights (per-column fp32 scales, quantized
+    on the device before timing) on the decode (n=32) or OLMoE (n=4096) batch:
+    tokens/s, the FP8 GEMMs' bandwidth against their weight bytes, and the bf16
+    layer on the same inputs for comparison."""
+    import torch
+
+    import routing_token_permute_amd as moe
+    from workloads import make_config
+
+    dev = torch.device("cuda:0")
+    base = "decode_bf16" if args.workload == "decode_fp8" else "olmoe_bf16"
+    w = make_config(base)
+    n, H, I, E, K = w.n, w.H, w.I, w.E, w.K  # noqa: E741
+
+    def to_dev(name):
+        return torch.from_numpy(w.bits(name).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x, Wg, W13, W2 = (to_dev(k) for k in ("x", "W_gate", "W13", "W2"))
+    q13, s13 = moe.moe_quantize_fp8(W13)
+    q2, s2 = moe.moe_quantize_fp8(W2)
+    y = torch.empty((n, H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(moe.moe_forward_workspace_size(n, H, I, E, K, torch.bfloat16), dtype=torch.uint8, device=dev)
+
+    def step():
+        moe.moe_forward_fp8(x, Wg, q13, s13, q2, s2, K, w.renorm, y=y, ws=ws)
+
+    def step_bf16():
+        moe.moe_forward(x, Wg, W13, W2, K, w.renorm, y=y, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = _time_region(step, args.steps, torch)
+    wall = time.perf_counter() - t0
+    spread = _pcts(_time_each(step, max(args.steps, 10), torch))
+    ms_bf16 = _time_region(step_bf16, args.steps, torch)
+    logits, ids, wts = moe.moe_route(x, Wg, None, K, w.renorm)
+    meta = moe.moe_permute(ids, None, E)
+    h = moe.moe_expert_w13_swiglu_gather_fp8(x, meta["perm"], K, meta["offsets"], q13, s13)
+    Yp = moe.moe_expert_w2_fp8(h, meta["offsets"], q2, s2)
+    torch.cuda.synchronize()
+    hit = int((meta["counts"].cpu().numpy() > 0).sum())
+    R = args.stage_reps
+    st = {
+        "gemm1_swiglu_fp8": _time_region(
+            lambda: moe.moe_expert_w13_swiglu_gather_fp8(x, meta["perm"], K, meta["offsets"], q13, s13, h=h), R, torch),
+        "gemm2_fp8": _time_region(lambda: moe.moe_expert_w2_fp8(h, meta["offsets"], q2, s2, Y_perm=Yp), R, torch),
+    }
+    nk = n * K
+    bytes_ = {  # algorithmic: activations once, FP8 codes and scales of the hit experts once, outputs once
+        "gemm1_swiglu_fp8": nk * H * 2 + hit * (2 * I * H + 2 * I * 4) + nk * I * 2 + nk * 4,
+        "gemm2_fp8": nk * I * 2 + hit * (H * I + H * 4) + nk * H * 2,
+    }
+    flops = {"gemm1_swiglu_fp8": 2.0 * nk * H * 2 * I, "gemm2_fp8": 2.0 * nk * I * H}
+    stages = {}
+    for k, v in st.items():
+        gbs = bytes_[k] / (v * 1e-3) / 1e9
+        stages[k] = {"ms": round(v, 5), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBPS, 4),
+                     "TFLOP/s": round(flops[k] / (v * 1e-3) / 1e12, 1)}
+    dom = "gemm1_swiglu_fp8"
+    if args.workload == "decode_fp8":
+        roof = {"kernel": "gemm_w8_kernel<GATED=true, GATHER=true> (GEMM1 + SwiGLU, FP8 weights)", "bound": "hbm",
+                "achieved": stages[dom]["GB/s"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": stages[dom]["frac_hbm"], "traffic": None}
+    else:
+        tf = stages[dom]["TFLOP/s"]
+        roof = {"kernel": "gemm_w8_kernel<GATED=true, GATHER=true> (GEMM1 + SwiGLU, FP8 weights)", "bound": "mfma",
+                "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                "traffic": None}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        c13, r13 = oracle.fp8.quantize_columns(w.W13_f32)
+        c2, r2 = oracle.fp8.quantize_columns(w.W2_f32)
+        m = min(n, 512)
+        reps, t1 = 0, time.perf_counter()
+        while True:
+            oracle.fp8.forward_fp8(w.x_f32[:m], w.W_gate_f32, c13, r13, c2, r2, K, w.renorm)
+            reps += 1
+            if time.perf_counter() - t1 >= args.cpu_seconds:
+                break
+        el = time.perf_counter() - t1
+        cpu = {"value": round(m * reps / el, 1), "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
+               "sample": f"fp64 layer on the dequantized FP8 weights, first {m} tokens, {reps} repetitions, {el:.1f} s "
+                         f"(weight quantization not timed)"}
+    out = {
+        "metric": f"MoE layer fwd tokens/s with FP8 E4M3 expert weights, {base.split('_')[0]} n={n}",
+        "value": round(n / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "step_spread": spread,
+        "ms_per_step_bf16_weights": round(ms_bf16, 5),
+        "speedup_over_bf16_weights": round(ms_bf16 / ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 activations, fp8 e4m3 weights",
+        "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights quantized per output column; OLMoE layer shapes)",
+        "config": {"workload": args.workload, "n": n, "H": H, "I": I, "E": E, "K": K, "renorm": bool(w.renorm)},
+        "stages": stages,
+        "roofline": roof,
         "experts_hit": hit,
         "wall_s_timed_region": round(wall, 3),
         "cpu_baseline": cpu,

@@ -394,6 +394,62 @@ moe_status moe_backward(const void* dy, const void* x, const void* W_gate, const
                         float* dW_gate, float* dbias, void* dW13, void* dW2, void* ws, size_t ws_bytes,
                         hipStream_t stream);
 
+/* ===========================================================================
+ * FP8 expert weights.
+ *
+ * "大模型系统中的通算融合" §8.4 asks for low-precision payloads with per-token
+ * or per-block scales that the GEMM consumes directly; §4.4 describes Mega
+ * MoE's first linear with low-precision weights prepared ahead of time. Here
+ * W13 and W2 are stored as OCP FP8 E4M3 codes (1 sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits, no infinities, largest finite 448) with one fp32
+ * scale per output column; activations stay bf16 and the products accumulate
+ * in fp32 on bf16 MFMA (E4M3 values are exact in bf16). The layer is
+ * otherwise the one above; dt must be MOE_BF16 (else MOE_EUNSUPPORTED).
+ * ========================================================================= */
+
+/* ---------------------------------------------------------------------------
+ * moe_quantize_fp8 — FP8 codes and column scales of a stack of weights
+ * W (E, Kd, N) row-major (W13: Kd = H, N = 2I; W2: Kd = I, N = H):
+ *   scales[e, n] = max_k |W[e, k, n]| / 448 (fp32; 1 for an all-zero column);
+ *   codes[e, n, k] = nearest E4M3 value of the fp32 quotient W[e, k, n] /
+ *                    scales[e, n], ties to the even mantissa, magnitudes
+ *                    beyond 448 saturated to 448.
+ * codes are column-major per expert: each output column's Kd codes are
+ * contiguous (the layout the GEMMs read). Kd must be a multiple of 64, N of 4.
+ *   W dtype (bf16 or fp32); codes (E, N, Kd) uint8 out; scales (E, N) fp32 out.
+ * ------------------------------------------------------------------------- */
+moe_status moe_quantize_fp8(const void* W, int E, int Kd, int N, moe_dtype dt, uint8_t* codes, float* scales,
+                            hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_expert_w13_swiglu_gather_fp8 — moe_expert_w13_swiglu_gather with FP8
+ * W13: gate_up[r] = (x[perm[r]/K] · W13'[e]) where W13'[e][k, n] =
+ * decode(W13q[e, n, k]) * s13[e, n], accumulated in fp32, the column scale
+ * applied to the accumulator, then h = SiLU(gate) * up rounded to bf16.
+ *   W13q (E, 2I, H) uint8; s13 (E, 2I) fp32; other arguments as the bf16 call.
+ * ------------------------------------------------------------------------- */
+moe_status moe_expert_w13_swiglu_gather_fp8(const void* x, const int32_t* perm, int n, int K, const int32_t* offsets,
+                                            const uint8_t* W13q, const float* s13, int E, int H, int I, moe_dtype dt,
+                                            void* h, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_expert_w2_fp8 — moe_expert_w2 with FP8 W2: Y_perm[p] = h[p] · W2'[e],
+ * W2'[e][k, n] = decode(W2q[e, n, k]) * s2[e, n].
+ *   W2q (E, H, I) uint8; s2 (E, H) fp32.
+ * ------------------------------------------------------------------------- */
+moe_status moe_expert_w2_fp8(const void* h, const int32_t* offsets, int rows, const uint8_t* W2q, const float* s2,
+                             int E, int H, int I, moe_dtype dt, void* Y_perm, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_forward_fp8 — moe_forward with FP8 expert weights (route, permute
+ * metadata, FP8 GEMM1 with the gather fused, FP8 GEMM2, combine). Workspace:
+ * moe_forward_workspace_size(n, H, I, E, K, MOE_BF16) bytes.
+ * ------------------------------------------------------------------------- */
+moe_status moe_forward_fp8(const void* x, const void* W_gate, const float* bias, const uint8_t* W13q,
+                           const float* s13, const uint8_t* W2q, const float* s2, int n, int H, int I, int E, int K,
+                           int renorm, moe_dtype dt, void* y, float* logits_out, int32_t* topk_ids_out,
+                           float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

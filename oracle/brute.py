@@ -135,3 +135,22 @@ def layer_dense(x, e_top, w_top, W13, W2):
             if e in weight:
                 y[i] += weight[e] * ffn_token(x[i], W13[e], W2[e])
     return y
+
+
+def e4m3_encode_by_search(x) -> np.ndarray:
+    """The E4M3 encoder as a search: among the 127 non-negative finite values
+    (codes 0x00..0x7E), the one nearest |x| (clamped to 448), the even code on
+    a tie, with the sign of x unless the code is 0."""
+    from .fp8 import e4m3_decode_table
+
+    vals = e4m3_decode_table()[:0x7F]
+    out = np.empty(np.shape(x), dtype=np.uint8)
+    flat_x = np.asarray(x, dtype=np.float64).reshape(-1)
+    flat_o = out.reshape(-1)
+    for i, v in enumerate(flat_x):
+        a = min(abs(v), 448.0)
+        d = np.abs(vals - a)
+        best = np.flatnonzero(d == d.min())
+        c = int(best[0]) if len(best) == 1 else int(best[best % 2 == 0][0])
+        flat_o[i] = c | (0x80 if (np.signbit(v) and c != 0) else 0)
+    return out

@@ -52,10 +52,6 @@ def e4m3_decode_table() -> np.ndarray:
 
 
 _TABLE = e4m3_decode_table()
-# Non-negative finite codes 0x00..0x7E in increasing order of value.
-_POS_CODES = np.arange(0x7F, dtype=np.int64)
-_POS_VALS = _TABLE[_POS_CODES]
-assert np.all(np.diff(_POS_VALS) > 0)
 
 
 def e4m3_decode(codes) -> np.ndarray:
@@ -65,19 +61,26 @@ def e4m3_decode(codes) -> np.ndarray:
 def e4m3_encode(x) -> np.ndarray:
     """Nearest E4M3 code of each value (ties to even mantissa, saturating at +-448); uint8.
 
-    Works on the exact values given (the callers pass fp32 quotients). NaN is
-    not expected and not handled.
+    Written from the format: below the smallest normal 2^-6 the values are
+    m * 2^-9, so the code is rint(|x| * 2^9) (m = 8 lands on code 8, the
+    smallest normal); above it |x| = f * 2^E with f in [1, 2), the mantissa is
+    rint((f - 1) * 8) with ties to even, a mantissa of 8 carries into the
+    exponent, and the code is (E + 7) * 8 + m. Works on the exact values given
+    (the callers pass fp32 quotients); NaN is not expected. oracle/brute.py
+    restates the same map as a nearest-value search over the 127 non-negative
+    codes, and the pins compare the two.
     """
     x = np.asarray(x, dtype=np.float64)
     a = np.minimum(np.abs(x), E4M3_MAX)
-    hi = np.searchsorted(_POS_VALS, a, side="left")  # first value >= a
-    hi = np.minimum(hi, len(_POS_VALS) - 1)
-    lo = np.maximum(hi - 1, 0)
-    d_lo = a - _POS_VALS[lo]
-    d_hi = _POS_VALS[hi] - a
-    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (_POS_CODES[hi] % 2 == 0))
-    code = np.where(pick_hi, _POS_CODES[hi], _POS_CODES[lo])
-    code = np.where(a == _POS_VALS[hi], _POS_CODES[hi], code)  # exact hits (covers a == 0)
+    sub = a < 2.0**-6
+    m_sub = np.rint(a * 512.0)
+    mant, ex = np.frexp(np.where(sub, 1.0, a))  # a = mant * 2^ex, mant in [0.5, 1)
+    E = ex - 1
+    m = np.rint((mant * 2.0 - 1.0) * 8.0)
+    carry = m == 8
+    E = np.where(carry, E + 1, E)
+    m = np.where(carry, 0, m)
+    code = np.where(sub, m_sub, (E + 7) * 8 + m).astype(np.int64)
     sign = (np.signbit(x) & (code != 0)).astype(np.int64) << 7
     return (code | sign).astype(np.uint8)
 

@@ -18,17 +18,21 @@ from ._lib import (  # noqa: F401
     moe_dispatch_backward,
     moe_expert_w2,
     moe_expert_w2_backward,
+    moe_expert_w2_fp8,
     moe_expert_w2_scatter,
     moe_expert_w13_swiglu,
     moe_expert_w13_backward,
     moe_expert_w13_swiglu_gather,
+    moe_expert_w13_swiglu_gather_fp8,
     moe_expert_w13_swiglu_gather_train,
     moe_expert_weight_grad,
     moe_forward,
+    moe_forward_fp8,
     moe_forward_train,
     moe_forward_workspace_size,
     moe_grouped_swiglu,
     moe_permute,
+    moe_quantize_fp8,
     moe_route,
     moe_route_backward,
     moe_sum_slots,

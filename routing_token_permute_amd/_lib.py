@@ -62,6 +62,13 @@ SIGNATURES = {
         _I,
         [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     ),
+    "moe_quantize_fp8": (_I, [_VP, _I, _I, _I, _I, _VP, _VP, _VP]),
+    "moe_expert_w13_swiglu_gather_fp8": (_I, [_VP, _VP, _I, _I, _VP, _VP, _VP, _I, _I, _I, _I, _VP, _VP]),
+    "moe_expert_w2_fp8": (_I, [_VP, _VP, _I, _VP, _VP, _I, _I, _I, _I, _VP, _VP]),
+    "moe_forward_fp8": (
+        _I,
+        [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    ),
     "moe_backward_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "moe_backward": (
         _I,
@@ -629,3 +636,93 @@ def moe_backward(dy, x, W_gate, W13, W2, K: int, renorm: bool, saved, grads=None
     )
     _check(code, "moe_backward")
     return grads
+
+
+# ---------------------------------------------------------------------------
+# FP8 expert weights
+# ---------------------------------------------------------------------------
+
+
+def moe_quantize_fp8(W, codes=None, scales=None, stream=None):
+    """FP8 E4M3 codes (E, N, Kd) uint8 and column scales (E, N) fp32 of weights W (E, Kd, N)."""
+    lib = load_library()
+    E, Kd, N = W.shape
+    dev = W.device
+    _need(W, "W", (E, Kd, N))
+    codes = _empty((E, N, Kd), torch.uint8, dev) if codes is None else codes
+    scales = _empty((E, N), torch.float32, dev) if scales is None else scales
+    _need(codes, "codes", (E, N, Kd), torch.uint8, dev)
+    _need(scales, "scales", (E, N), torch.float32, dev)
+    code = lib.moe_quantize_fp8(_ptr(W), E, Kd, N, _dt(W), _ptr(codes), _ptr(scales), _stream(dev, stream))
+    _check(code, "moe_quantize_fp8")
+    return codes, scales
+
+
+def moe_expert_w13_swiglu_gather_fp8(x, perm, K, offsets, W13q, s13, h=None, stream=None):
+    """GEMM1 + SwiGLU with FP8 W13 (codes (E, 2I, H), scales (E, 2I)), rows gathered through perm."""
+    lib = load_library()
+    n, H = x.shape
+    E, I2, _ = W13q.shape
+    I = I2 // 2  # noqa: E741
+    dev = x.device
+    _need(x, "x", (n, H))
+    _need(perm, "perm", (n * K,), torch.int32, dev)
+    _need(offsets, "offsets", (E + 1,), torch.int32, dev)
+    _need(W13q, "W13q", (E, 2 * I, H), torch.uint8, dev)
+    _need(s13, "s13", (E, 2 * I), torch.float32, dev)
+    h = _empty((n * K, I), x.dtype, dev) if h is None else h
+    _need(h, "h", (n * K, I), x.dtype, dev)
+    code = lib.moe_expert_w13_swiglu_gather_fp8(_ptr(x), _ptr(perm), n, K, _ptr(offsets), _ptr(W13q), _ptr(s13), E,
+                                                H, I, _dt(x), _ptr(h), _stream(dev, stream))
+    _check(code, "moe_expert_w13_swiglu_gather_fp8")
+    return h
+
+
+def moe_expert_w2_fp8(h, offsets, W2q, s2, Y_perm=None, stream=None):
+    """GEMM2 with FP8 W2 (codes (E, H, I), scales (E, H))."""
+    lib = load_library()
+    rows, I = h.shape  # noqa: E741
+    E, H, _ = W2q.shape
+    dev = h.device
+    _need(h, "h", (rows, I))
+    _need(offsets, "offsets", (E + 1,), torch.int32, dev)
+    _need(W2q, "W2q", (E, H, I), torch.uint8, dev)
+    _need(s2, "s2", (E, H), torch.float32, dev)
+    Y_perm = _empty((rows, H), h.dtype, dev) if Y_perm is None else Y_perm
+    _need(Y_perm, "Y_perm", (rows, H), h.dtype, dev)
+    code = lib.moe_expert_w2_fp8(_ptr(h), _ptr(offsets), rows, _ptr(W2q), _ptr(s2), E, H, I, _dt(h), _ptr(Y_perm),
+                                 _stream(dev, stream))
+    _check(code, "moe_expert_w2_fp8")
+    return Y_perm
+
+
+def moe_forward_fp8(x, W_gate, W13q, s13, W2q, s2, K: int, renorm: bool, bias=None, y=None, ws=None,
+                    routing_out=False, stream=None):
+    """The layer with FP8 expert weights. Returns y, or (y, logits, topk_ids, topk_w, counts) with routing_out."""
+    lib = load_library()
+    n, H = x.shape
+    E = W_gate.shape[1]
+    I = W13q.shape[1] // 2  # noqa: E741
+    dev = x.device
+    _need(x, "x", (n, H))
+    _need(W_gate, "W_gate", (H, E), x.dtype, dev)
+    _need(W13q, "W13q", (E, 2 * I, H), torch.uint8, dev)
+    _need(s13, "s13", (E, 2 * I), torch.float32, dev)
+    _need(W2q, "W2q", (E, H, I), torch.uint8, dev)
+    _need(s2, "s2", (E, H), torch.float32, dev)
+    if bias is not None:
+        _need(bias, "bias", (E,), torch.float32, dev)
+    y = _empty((n, H), x.dtype, dev) if y is None else y
+    _need(y, "y", (n, H), x.dtype, dev)
+    dt = _dt(x)
+    ws = _workspace(lib.moe_forward_workspace_size(n, H, I, E, K, dt), dev, ws)
+    extra = [None] * 4
+    if routing_out:
+        extra = [_empty((n, E), torch.float32, dev), _empty((n, K), torch.int32, dev),
+                 _empty((n, K), torch.float32, dev), _empty((E,), torch.int32, dev)]
+    code = lib.moe_forward_fp8(
+        _ptr(x), _ptr(W_gate), _ptr(bias), _ptr(W13q), _ptr(s13), _ptr(W2q), _ptr(s2), n, H, I, E, K,
+        int(bool(renorm)), dt, _ptr(y), *[_ptr(t) for t in extra], _ptr(ws), ws.numel(), _stream(dev, stream),
+    )
+    _check(code, "moe_forward_fp8")
+    return (y, *extra) if routing_out else y

@@ -456,4 +456,77 @@ moe_status moe_backward(const void* dy, const void* x, const void* W_gate, const
   return from_hip(launch_weight_grad(rows_a, dgu, offsets, rows, E, H, 2 * I, dt, dW13, stream));
 }
 
+// ---------------------------------------------------------------------------
+// FP8 expert weights
+// ---------------------------------------------------------------------------
+
+moe_status moe_quantize_fp8(const void* W, int E, int Kd, int N, moe_dtype dt, uint8_t* codes, float* scales,
+                            hipStream_t stream) {
+  if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
+  if (E < 0 || !hidden_ok(Kd, MOE_BF16) || N < 1 || N % 4 != 0) return MOE_EINVAL;
+  if (E == 0) return MOE_OK;
+  if (W == nullptr || codes == nullptr || scales == nullptr) return MOE_EINVAL;
+  return from_hip(launch_quantize_fp8(W, E, Kd, N, dt, codes, scales, stream));
+}
+
+static moe_status check_fp8_gemm(const void* a, const int32_t* offsets, int rows, const void* wq, const float* sc,
+                                 int E, int H, int I, moe_dtype dt, const void* out) {
+  if (dt != MOE_BF16) return MOE_EUNSUPPORTED;  // FP8 weights pair with bf16 activations
+  if (rows < 0 || E < 1 || E > kMaxExperts || !hidden_ok(H, dt) || !hidden_ok(I, dt)) return MOE_EINVAL;
+  if (rows > 0 && (a == nullptr || offsets == nullptr || wq == nullptr || sc == nullptr || out == nullptr))
+    return MOE_EINVAL;
+  return MOE_OK;
+}
+
+moe_status moe_expert_w13_swiglu_gather_fp8(const void* x, const int32_t* perm, int n, int K, const int32_t* offsets,
+                                            const uint8_t* W13q, const float* s13, int E, int H, int I, moe_dtype dt,
+                                            void* h, hipStream_t stream) {
+  if (n < 0 || K < 1 || K > kMaxTopK || (long long)n * K > INT32_MAX) return MOE_EINVAL;
+  if (n > 0 && perm == nullptr) return MOE_EINVAL;
+  const moe_status st = check_fp8_gemm(x, offsets, n * K, W13q, s13, E, H, I, dt, h);
+  if (st != MOE_OK) return st;
+  return from_hip(launch_w13_swiglu_gather_fp8(x, perm, n, K, offsets, W13q, s13, E, H, I, h, stream));
+}
+
+moe_status moe_expert_w2_fp8(const void* h, const int32_t* offsets, int rows, const uint8_t* W2q, const float* s2,
+                             int E, int H, int I, moe_dtype dt, void* Y_perm, hipStream_t stream) {
+  const moe_status st = check_fp8_gemm(h, offsets, rows, W2q, s2, E, H, I, dt, Y_perm);
+  if (st != MOE_OK) return st;
+  return from_hip(launch_w2_fp8(h, offsets, rows, W2q, s2, E, H, I, Y_perm, stream));
+}
+
+moe_status moe_forward_fp8(const void* x, const void* W_gate, const float* bias, const uint8_t* W13q,
+                           const float* s13, const uint8_t* W2q, const float* s2, int n, int H, int I, int E, int K,
+                           int renorm, moe_dtype dt, void* y, float* logits_out, int32_t* topk_ids_out,
+                           float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
+  if (dt != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (n < 0 || !experts_ok(E, K) || !hidden_ok(H, dt) || !hidden_ok(I, dt)) return MOE_EINVAL;
+  if ((long long)n * K > INT32_MAX) return MOE_EINVAL;
+  if (n > 0 && (x == nullptr || W_gate == nullptr || W13q == nullptr || s13 == nullptr || W2q == nullptr ||
+                s2 == nullptr || y == nullptr))
+    return MOE_EINVAL;
+  const ForwardLayout L = forward_layout(n, H, I, E, K, dt);
+  if (ws == nullptr || ws_bytes < L.total) return MOE_EWORKSPACE;
+  char* base = (char*)ws;
+  float* logits = logits_out ? logits_out : (float*)(base + L.logits);
+  int32_t* ids = topk_ids_out ? topk_ids_out : (int32_t*)(base + L.ids);
+  float* w = topk_w_out ? topk_w_out : (float*)(base + L.w);
+  int32_t* counts = counts_out ? counts_out : (int32_t*)(base + L.counts);
+  int32_t* offsets = (int32_t*)(base + L.offsets);
+  int32_t* perm = (int32_t*)(base + L.perm);
+  int32_t* inv = (int32_t*)(base + L.inv);
+  hipError_t e = launch_route(x, W_gate, bias, n, H, E, K, renorm, dt, logits, ids, w, stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  e = launch_permute(ids, nullptr, n, H, E, K, 1, dt, counts, offsets, (int32_t*)(base + L.splits), perm, inv,
+                     nullptr, (int32_t*)(base + L.pscratch), stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  if (n == 0) return MOE_OK;
+  e = launch_w13_swiglu_gather_fp8(x, perm, n, K, offsets, W13q, s13, E, H, I, base + L.h, stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  e = launch_w2_fp8(base + L.h, offsets, n * K, W2q, s2, E, H, I, base + L.Y_perm, stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  return from_hip(launch_combine(base + L.Y_perm, inv, w, n, H, K, dt, y, stream));
+}
+
 }  // extern "C"

@@ -115,6 +115,20 @@ hipError_t launch_router_dx_mfma(const void* dl_hilo, const int32_t* row_offsets
 hipError_t launch_router_dw_mfma(const void* x, const void* dl_hilo, const int32_t* chunk_offsets, int S, int n,
                                  int H, int E, float* part, hipStream_t s);
 
+// ---- FP8 E4M3 expert weights ----
+
+// codes (E, N, Kd) = nearest E4M3 codes of W (E, Kd, N) / scales (E, N),
+// scales = column amax / 448 (1 for a zero column).
+hipError_t launch_quantize_fp8(const void* W, int E, int Kd, int N, moe_dtype dt, uint8_t* codes, float* scales,
+                               hipStream_t s);
+// GEMM1 + SwiGLU with W13 codes (E, 2I, H) and scales (E, 2I), rows gathered through perm.
+hipError_t launch_w13_swiglu_gather_fp8(const void* x, const int32_t* perm, int n, int K, const int32_t* offsets,
+                                        const uint8_t* W13q, const float* s13, int E, int H, int I, void* h,
+                                        hipStream_t s);
+// GEMM2 with W2 codes (E, H, I) and scales (E, H).
+hipError_t launch_w2_fp8(const void* h, const int32_t* offsets, int rows, const uint8_t* W2q, const float* s2, int E,
+                         int H, int I, void* Y_perm, hipStream_t s);
+
 }  // namespace moe
 
 // ---- device helpers ----

@@ -750,3 +750,17 @@ def test_planted_fp8_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(f, "quantize_columns", quantize_rows)
     assert not _pins_pass(test_quantize_columns_scales_and_exact_grid)
     monkeypatch.undo()
+
+
+def test_e4m3_encode_matches_nearest_search():
+    """The exponent/mantissa encoder equals the nearest-value search on every code, every midpoint and its two
+    neighbours, and random values across the whole range (both signs)."""
+    f = oracle.fp8
+    t = f.e4m3_decode_table()[:0x7F]
+    mids = (t[:-1] + t[1:]) / 2
+    pts = np.concatenate([t, mids, np.nextafter(mids, -np.inf), np.nextafter(mids, np.inf), [500.0, 1e-12, 0.0]])
+    rng = np.random.default_rng(21)
+    pts = np.concatenate([pts, rng.uniform(0, 460, 2000), np.abs(rng.normal(0, 0.01, 2000)),
+                          2.0 ** rng.uniform(-12, 9, 2000)])
+    pts = np.concatenate([pts, -pts]).astype(np.float32).astype(np.float64)
+    np.testing.assert_array_equal(f.e4m3_encode(pts), brute.e4m3_encode_by_search(pts))
