@@ -20,9 +20,10 @@
  *
  * Conventions for every call:
  *   - All array arguments are DEVICE pointers owned by the caller; the
- *     library allocates no memory and keeps no per-call state. Scratch memory
- *     is a caller-supplied workspace whose size the *_workspace_size
- *     functions return.
+ *     library allocates no memory and keeps no per-call state (moe_backward
+ *     keeps one auxiliary stream per device, see there). Scratch memory is a
+ *     caller-supplied workspace whose size the *_workspace_size functions
+ *     return.
  *   - Calls are asynchronous on the given HIP stream (0 = the null stream)
  *     and never synchronise the host. Results are valid once the stream has
  *     reached the end of the call.
@@ -377,9 +378,15 @@ moe_status moe_route_backward(const void* x, const void* W_gate, const float* lo
                               size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
- * moe_backward — the whole layer's backward on one stream: combine backward,
- * route backward, GEMM2 + SwiGLU data gradient, dW2, GEMM1 data gradient,
- * dispatch backward (with the router's share of dx), row gather of x, dW13.
+ * moe_backward — the whole layer's backward: combine backward, route
+ * backward, GEMM2 + SwiGLU data gradient, dW2, GEMM1 data gradient, dispatch
+ * backward (with the router's share of dx), row gather of x, dW13. The route
+ * backward, dW2, the gather and dW13 run on a second HIP stream (one per
+ * device, default priority, created on the first call and kept for the
+ * process), forked from and joined back into `stream` with events, so that
+ * they overlap the main chain; when that stream cannot be created everything
+ * runs on `stream`. All work is ordered after earlier work on `stream`, and
+ * later work on `stream` sees every output.
  *   dy (n, H) dtype; x, W_gate, W13, W2 as given to moe_forward_train;
  *   logits ... Y_perm: the buffers moe_forward_train saved;
  *   dx (n, H) dtype out; dW_gate (H, E) fp32 out; dbias (E) fp32 out or NULL;

@@ -4,6 +4,8 @@
 // grouped_gemm.hip, combine.hip, grouped_gemm_bwd.hip and backward.hip.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "moe_internal.hpp"
 
 namespace {
@@ -83,10 +85,10 @@ TrainLayout train_layout(int n, int E, int K) {
 
 size_t route_bwd_ws(int n, int H, int E) { return align_up(route_bwd_workspace(n, H, E)); }
 
-// moe_backward workspace, in order. rows_a holds dY_perm, then dX_perm, then
-// the gathered x_perm (each dead before the next is written, in stream order).
+// moe_backward workspace, in order. rows_a holds dY_perm, then dX_perm (dY_perm
+// is dead once dgate_up and dW2 are done); rows_b the gathered x_perm.
 struct BackwardLayout {
-  size_t rows_a, dgu, dw, dlogits, dx_router, rws, total;
+  size_t rows_a, rows_b, dgu, dw, dlogits, dx_router, rws, total;
 };
 
 BackwardLayout backward_layout(int n, int H, int I, int E, int K, moe_dtype dt) {
@@ -99,6 +101,7 @@ BackwardLayout backward_layout(int n, int H, int I, int E, int K, moe_dtype dt) 
     return at;
   };
   L.rows_a = take(nk * H * elt_size(dt));
+  L.rows_b = take(nk * H * elt_size(dt));
   L.dgu = take(nk * 2 * I * elt_size(dt));
   L.dw = take(nk * 4);
   L.dlogits = take((size_t)n * E * 4);
@@ -106,6 +109,35 @@ BackwardLayout backward_layout(int n, int H, int I, int E, int K, moe_dtype dt) 
   L.rws = take(route_bwd_ws(n, H, E));
   L.total = o;
   return L;
+}
+
+// A second stream per device for the backward's independent branches, with
+// its fork/join events; created on first use and kept for the process. The
+// mutex keeps each call's record/wait sequence in one piece when several host
+// threads enqueue at once.
+struct AuxStream {
+  hipStream_t s = nullptr;
+  hipEvent_t ev[4] = {};
+  bool ok = false;
+  bool tried = false;
+};
+
+std::mutex g_aux_mutex;
+
+AuxStream* aux_stream() {
+  constexpr int kMaxDevices = 64;
+  static AuxStream aux[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  AuxStream& a = aux[dev];
+  if (!a.tried) {
+    a.tried = true;
+    bool ok = hipStreamCreateWithFlags(&a.s, hipStreamNonBlocking) == hipSuccess;
+    for (int i = 0; i < 4 && ok; ++i) ok = hipEventCreateWithFlags(&a.ev[i], hipEventDisableTiming) == hipSuccess;
+    a.ok = ok;
+    if (!ok) (void)hipGetLastError();
+  }
+  return a.ok ? &a : nullptr;
 }
 
 }  // namespace
@@ -438,22 +470,34 @@ moe_status moe_backward(const void* dy, const void* x, const void* W_gate, const
     if (e == hipSuccess && dbias != nullptr) e = launch_fill_zero(dbias, (size_t)E * 4, stream);
     return from_hip(e);
   }
+  void* rows_b = base + L.rows_b;
+  // Two branches run beside the main chain on a second stream:
+  //   main: combine bwd -> dgate_up ------(join 1)-> dX_perm -> dispatch bwd -(join 2)
+  //   aux:             \-> route bwd -> dW2 -/   \-> gather x_perm -> dW13 ----/
+  // dW2 and dgate_up both read dY_perm, which dX_perm overwrites after join 1.
+  std::lock_guard<std::mutex> lock(g_aux_mutex);
+  AuxStream* aux = aux_stream();
+  hipStream_t side = aux ? aux->s : stream;
+  auto fork = [&](int i, hipStream_t from, hipStream_t to) {
+    if (from == to) return hipSuccess;
+    hipError_t r = hipEventRecord(aux->ev[i], from);
+    return r == hipSuccess ? hipStreamWaitEvent(to, aux->ev[i], 0) : r;
+  };
   e = launch_combine_backward(dy, Y_perm, inv, topk_w, n, H, K, dt, rows_a, dw, stream);
-  if (e != hipSuccess) return MOE_EHIP;
-  e = launch_route_backward(x, W_gate, logits, topk_ids, topk_w, dw, n, H, E, K, renorm, dt, dlogits, dx_router,
-                            dW_gate, dbias, base + L.rws, stream);
-  if (e != hipSuccess) return MOE_EHIP;
-  e = launch_w2_backward(rows_a, offsets, rows, W2, gate_up, E, H, I, dt, dgu, stream);
-  if (e != hipSuccess) return MOE_EHIP;
-  e = launch_weight_grad(h, rows_a, offsets, rows, E, I, H, dt, dW2, stream);
-  if (e != hipSuccess) return MOE_EHIP;
-  e = launch_w13_backward(dgu, offsets, rows, W13, E, H, I, dt, rows_a, stream);
-  if (e != hipSuccess) return MOE_EHIP;
-  e = launch_dispatch_backward(rows_a, inv, dx_router, n, H, K, dt, dx, stream);
-  if (e != hipSuccess) return MOE_EHIP;
-  e = launch_gather_rows(x, perm, n, H, K, dt, rows_a, stream);
-  if (e != hipSuccess) return MOE_EHIP;
-  return from_hip(launch_weight_grad(rows_a, dgu, offsets, rows, E, H, 2 * I, dt, dW13, stream));
+  if (e == hipSuccess) e = fork(0, stream, side);
+  if (e == hipSuccess)
+    e = launch_route_backward(x, W_gate, logits, topk_ids, topk_w, dw, n, H, E, K, renorm, dt, dlogits, dx_router,
+                              dW_gate, dbias, base + L.rws, side);
+  if (e == hipSuccess) e = launch_weight_grad(h, rows_a, offsets, rows, E, I, H, dt, dW2, side);
+  if (e == hipSuccess) e = launch_w2_backward(rows_a, offsets, rows, W2, gate_up, E, H, I, dt, dgu, stream);
+  if (e == hipSuccess) e = fork(1, side, stream);    // join 1: dW2 and the router gradients are done
+  if (e == hipSuccess) e = fork(2, stream, side);    // dgate_up is ready for dW13
+  if (e == hipSuccess) e = launch_gather_rows(x, perm, n, H, K, dt, rows_b, side);
+  if (e == hipSuccess) e = launch_weight_grad(rows_b, dgu, offsets, rows, E, H, 2 * I, dt, dW13, side);
+  if (e == hipSuccess) e = launch_w13_backward(dgu, offsets, rows, W13, E, H, I, dt, rows_a, stream);
+  if (e == hipSuccess) e = launch_dispatch_backward(rows_a, inv, dx_router, n, H, K, dt, dx, stream);
+  if (e == hipSuccess) e = fork(3, side, stream);    // join 2: dW13 is done
+  return from_hip(e);
 }
 
 // ---------------------------------------------------------------------------
