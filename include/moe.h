@@ -1,5 +1,6 @@
 /*
- * moe.h — C ABI of the single-GPU MoE expert-layer forward on MI355X (gfx950).
+ * moe.h — C ABI of the single-GPU MoE expert layer on MI355X (gfx950): the
+ * forward, its pieces, the backward (training) pass and FP8 expert weights.
  *
  * The layer is Algorithm 2 "Single-GPU MoE Forward" of the page
  * "MoE 分布式推理基础（基于 vLLM）" (cnblogs, §1.2 MoE Forward), with the
@@ -386,7 +387,9 @@ moe_status moe_route_backward(const void* x, const void* W_gate, const float* lo
  * process), forked from and joined back into `stream` with events, so that
  * they overlap the main chain; when that stream cannot be created everything
  * runs on `stream`. All work is ordered after earlier work on `stream`, and
- * later work on `stream` sees every output.
+ * later work on `stream` sees every output. The call can be captured in a HIP
+ * graph (the fork and join are events), except the first call on a device,
+ * which creates the second stream.
  *   dy (n, H) dtype; x, W_gate, W13, W2 as given to moe_forward_train;
  *   logits ... Y_perm: the buffers moe_forward_train saved;
  *   dx (n, H) dtype out; dW_gate (H, E) fp32 out; dbias (E) fp32 out or NULL;
