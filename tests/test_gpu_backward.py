@@ -314,7 +314,7 @@ def test_backward_small_shapes(dev, n, H, I, E, K, dtype, renorm):  # noqa: E741
     _backward_parity(dev, w, f"backward n={n} H={H} I={I} E={E} K={K} {dtype}")
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "decode_bf16", "olmoe_bf16"])
+@pytest.mark.parametrize("name", ["tiny_f32", "decode_bf16", "olmoe_bf16", "olmoe_skewed_bf16"])
 def test_backward_configs(dev, name):
     w = make_config(name)
     g1 = _backward_parity(dev, w, f"backward {name}")

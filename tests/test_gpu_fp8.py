@@ -129,7 +129,7 @@ def _forward_fp8_parity(dev, w, what):
     assert rel < 0.1
 
 
-@pytest.mark.parametrize("name", ["decode_bf16", "olmoe_bf16", "tiny_bf16"])
+@pytest.mark.parametrize("name", ["decode_bf16", "olmoe_bf16", "olmoe_skewed_bf16", "tiny_bf16"])
 def test_forward_fp8_configs(dev, name):
     w = make_config(name) if name != "tiny_bf16" else make_layer(64, 128, 64, 8, 2, renorm=True, seed=2)
     _forward_fp8_parity(dev, w, f"forward fp8 {name}")
