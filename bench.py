@@ -502,7 +502,8 @@ def _bench_train(args):
     dX = moe.moe_expert_w13_backward(dgu, off, W13)
     rb = moe.moe_route_backward(x, Wg, saved["logits"], saved["topk_ids"], saved["topk_w"], dw, w.renorm)
     dx = moe.moe_dispatch_backward(dX, inv, n, K, add=rb["dx_router"])
-    x_perm = moe.moe_permute(saved["topk_ids"], x, E)["x_perm"]
+    xmeta = moe.moe_permute(saved["topk_ids"], x, E)
+    x_perm = xmeta["x_perm"]
     dW2 = moe.moe_expert_weight_grad(saved["h"], dY, off)
     dW13 = moe.moe_expert_weight_grad(x_perm, dgu, off)
     meta = moe.moe_permute(saved["topk_ids"], None, E)
@@ -520,14 +521,20 @@ def _bench_train(args):
         "dispatch_bwd": _time_region(lambda: moe.moe_dispatch_backward(dX, inv, n, K, add=rb["dx_router"], dx=dx),
                                      R, torch),
         "gemm1_wgrad": _time_region(lambda: moe.moe_expert_weight_grad(x_perm, dgu, off, dW=dW13), R, torch),
+        "gemm1_wgrad_gather": _time_region(lambda: moe.moe_expert_weight_grad_gather(x, perm, K, dgu, off, dW=dW13),
+                                           R, torch),
+        "x_gather": _time_region(lambda: moe.moe_permute(saved["topk_ids"], x, E, out=xmeta), R, torch)
+        - _time_region(lambda: moe.moe_permute(saved["topk_ids"], None, E, out=meta), R, torch),
     }
     nk = n * K
     f_small, f_big = 2.0 * nk * H * I, 2.0 * nk * H * 2 * I
-    flops = {"gemm2_dgrad_swiglu": f_small, "gemm2_wgrad": f_small, "gemm1_dgrad": f_big, "gemm1_wgrad": f_big}
+    flops = {"gemm2_dgrad_swiglu": f_small, "gemm2_wgrad": f_small, "gemm1_dgrad": f_big, "gemm1_wgrad": f_big,
+             "gemm1_wgrad_gather": f_big}
     bytes_ = {
         "combine_bwd": n * H * 2 + 2 * nk * H * 2 + nk * 12,
         "route_bwd": n * E * 4 + nk * 12 + n * H * 2 + H * E * 2 + n * E * 4 + n * H * 4 + H * E * 4,
         "dispatch_bwd": nk * H * 2 + nk * 4 + n * H * 4 + n * H * 2,
+        "x_gather": n * H * 2 + nk * H * 2 + nk * 4,
     }
     stages = {}
     for k, ms in st.items():
@@ -539,9 +546,11 @@ def _bench_train(args):
             s_["GB/s"] = round(bytes_[k] / (ms * 1e-3) / 1e9, 1)
             s_["frac_hbm"] = round(bytes_[k] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)
         stages[k] = s_
-    bwd_gemm_ms = sum(st[k] for k in flops)
-    bwd_gemm_tf = sum(flops.values()) / (bwd_gemm_ms * 1e-3) / 1e12
-    dom = max(flops, key=lambda k: st[k])
+    # the backward uses the explicit gather + dW13, not the gathered alternative
+    bwd_gemm_ms = sum(st[k] for k in flops if k != "gemm1_wgrad_gather")
+    bwd_flops = sum(v for k, v in flops.items() if k != "gemm1_wgrad_gather")
+    bwd_gemm_tf = bwd_flops / (bwd_gemm_ms * 1e-3) / 1e12
+    dom = max((k for k in flops if k != "gemm1_wgrad_gather"), key=lambda k: st[k])
     dom_tf = flops[dom] / (st[dom] * 1e-3) / 1e12
     cpu = None if args.no_cpu_baseline else _cpu_baseline_train(w, dy_seed=w.n, min_seconds=args.cpu_seconds)
     out = {
@@ -562,7 +571,7 @@ def _bench_train(args):
         "config": {"workload": "olmoe_train_bf16", "n": n, "H": H, "I": I, "E": E, "K": K, "renorm": bool(w.renorm)},
         "backward_grouped_gemm": {"TFLOP/s": round(bwd_gemm_tf, 1),
                                   "frac_bf16_peak": round(bwd_gemm_tf / PEAK_BF16_TFLOPS, 4),
-                                  "GFLOP": round(sum(flops.values()) / 1e9, 1)},
+                                  "GFLOP": round(bwd_flops / 1e9, 1)},
         "stages": stages,
         "roofline": {"kernel": f"gemm_bwd_bf16_kernel ({dom})", "bound": "mfma", "achieved": round(dom_tf, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),

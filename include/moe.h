@@ -343,6 +343,21 @@ moe_status moe_expert_weight_grad(const void* a, const void* b, const int32_t* o
                                   moe_dtype dt, void* dW, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_expert_weight_grad_gather — moe_expert_weight_grad with the rows of a
+ * read through the permutation: row r of a_e is x[perm[r] / K], so dW13 is
+ * formed straight from the token matrix without a permuted copy of it:
+ *   dW[e] = sum over rows r of expert e of x[perm[r] / K]^T b[r]
+ *   x (n, M) dtype; perm (n*K) int32 from moe_permute; b (n*K, N) dtype;
+ *   dW (E, M, N) dtype out (zeros for an expert without rows).
+ * It saves the (n*K, M) permuted copy of x; at the OLMoE shape it measured
+ * slower than moe_permute's gather plus moe_expert_weight_grad (410 us
+ * against 31 + 337 us), so moe_backward uses the latter.
+ * ------------------------------------------------------------------------- */
+moe_status moe_expert_weight_grad_gather(const void* x, const int32_t* perm, int n, int K, const void* b,
+                                         const int32_t* offsets, int E, int M, int N, moe_dtype dt, void* dW,
+                                         hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * moe_dispatch_backward — gradient of the row gather x_perm[p] = x[perm[p]/K]
  * (a combine with unit weights), plus an optional fp32 addend:
  *   dx[i] = add[i] + sum_{k=0..K-1} dX_perm[inv[i*K+k]]

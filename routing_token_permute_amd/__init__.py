@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     moe_expert_w13_swiglu_gather_fp8,
     moe_expert_w13_swiglu_gather_train,
     moe_expert_weight_grad,
+    moe_expert_weight_grad_gather,
     moe_forward,
     moe_forward_fp8,
     moe_forward_train,

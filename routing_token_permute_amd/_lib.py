@@ -56,6 +56,7 @@ SIGNATURES = {
     "moe_expert_w2_backward": (_I, [_VP, _VP, _I, _VP, _VP, _I, _I, _I, _I, _VP, _VP]),
     "moe_expert_w13_backward": (_I, [_VP, _VP, _I, _VP, _I, _I, _I, _I, _VP, _VP]),
     "moe_expert_weight_grad": (_I, [_VP, _VP, _VP, _I, _I, _I, _I, _I, _VP, _VP]),
+    "moe_expert_weight_grad_gather": (_I, [_VP, _VP, _I, _I, _VP, _VP, _I, _I, _I, _I, _VP, _VP]),
     "moe_dispatch_backward": (_I, [_VP, _VP, _VP, _I, _I, _I, _I, _VP, _VP]),
     "moe_route_backward_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_route_backward": (
@@ -538,6 +539,25 @@ def moe_expert_weight_grad(a, b, offsets, dW=None, stream=None):
     code = lib.moe_expert_weight_grad(_ptr(a), _ptr(b), _ptr(offsets), rows, E, M, N, _dt(a), _ptr(dW),
                                       _stream(dev, stream))
     _check(code, "moe_expert_weight_grad")
+    return dW
+
+
+def moe_expert_weight_grad_gather(x, perm, K: int, b, offsets, dW=None, stream=None):
+    """dW[e] = sum over rows r of expert e of x[perm[r] // K]^T b[r]. Returns dW (E, M, N)."""
+    lib = load_library()
+    n, M = x.shape
+    rows, N = b.shape
+    E = offsets.shape[0] - 1
+    dev = x.device
+    _need(x, "x", (n, M))
+    _need(perm, "perm", (n * K,), torch.int32, dev)
+    _need(b, "b", (n * K, N), x.dtype, dev)
+    _need(offsets, "offsets", (E + 1,), torch.int32, dev)
+    dW = _empty((E, M, N), x.dtype, dev) if dW is None else dW
+    _need(dW, "dW", (E, M, N), x.dtype, dev)
+    code = lib.moe_expert_weight_grad_gather(_ptr(x), _ptr(perm), n, K, _ptr(b), _ptr(offsets), E, M, N, _dt(x),
+                                             _ptr(dW), _stream(dev, stream))
+    _check(code, "moe_expert_weight_grad_gather")
     return dW
 
 

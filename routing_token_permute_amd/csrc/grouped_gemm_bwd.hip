@@ -43,11 +43,28 @@ constexpr int kBwdBM = 256, kBwdBK = 32, kBwdWM = 4, kBwdWN = 4;
 // outputs (for the router's products, whose gradients stay fp32); in
 // kDgradF32 the k index of B restarts every `kwrap` columns, so that
 // [hi | lo] halves of a split A operand meet the same B values.
-enum BwdMode : int { kDgradSwiglu = 0, kDgrad = 1, kWgrad = 2, kDgradF32 = 3, kWgradF32 = 4 };
+// kWgradGather is kWgrad with the A rows gathered: k-row r of A is row
+// perm[r] / topk of the (n_a, Mdim) token matrix (dW13 straight from x).
+enum BwdMode : int { kDgradSwiglu = 0, kDgrad = 1, kWgrad = 2, kDgradF32 = 3, kWgradF32 = 4, kWgradGather = 5 };
 
 // Source of every k-row copied past the end of an expert's rows (zero at
 // program load; nothing writes it).
 __device__ __attribute__((aligned(16))) uint16_t kZeroRow[BN];
+
+// Token rows of pair rows r0 .. r0+3 (row perm[r] / topk; -1 from r1 on); r0
+// and r1 are wave-uniform, so the loads are scalar.
+__device__ __forceinline__ int4 token_rows4(const int32_t* __restrict__ perm, int r0, int r1, int topk, int n_a) {
+  int t[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    t[q] = -1;
+    if (r0 + q < r1) {
+      const int f = perm[r0 + q];
+      t[q] = ((unsigned)f < (unsigned)(n_a * topk)) ? f / topk : 0;
+    }
+  }
+  return int4{t[0], t[1], t[2], t[3]};
+}
 
 struct BTile {
   int e, r0, r1, mb, nb;
@@ -68,9 +85,10 @@ __global__ __launch_bounds__(64 * kBwdWM * kBwdWN, 1) void gemm_bwd_bf16_kernel(
     const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ B, int ldb, long long b_stride,
     const int32_t* __restrict__ offsets, int E, int rows, int Mdim, int Ndim, int Kdim,
     const uint16_t* __restrict__ gu, int I, void* __restrict__ Cv, int ldc, long long c_stride, int MB, int NB,
-    int n_slots, int kwrap) {
+    int n_slots, int kwrap, const int32_t* __restrict__ perm, int topk, int n_a) {
   constexpr int BM = kBwdBM, BK = kBwdBK, WM = kBwdWM, WN = kBwdWN;
-  constexpr bool WGRAD = MODE == kWgrad || MODE == kWgradF32;
+  constexpr bool WGRAD = MODE == kWgrad || MODE == kWgradF32 || MODE == kWgradGather;
+  constexpr bool GATHER_A = MODE == kWgradGather;
   constexpr bool OUTF32 = MODE == kDgradF32 || MODE == kWgradF32;
   uint16_t* __restrict__ C = (uint16_t*)Cv;
   float* __restrict__ Cf = (float*)Cv;
@@ -95,7 +113,7 @@ __global__ __launch_bounds__(64 * kBwdWM * kBwdWN, 1) void gemm_bwd_bf16_kernel(
   const bool a_half = wave * REG < HALF_REG;
 
   int slot_id = blockIdx.x;
-  auto tile_of = [&](int t) {
+  auto tile_of = [&](int t) __attribute__((always_inline)) {
     BTile b{0, 0, 0, 0, 0, false};
     if constexpr (WGRAD) {
       const int per = MB * NB;
@@ -112,7 +130,7 @@ __global__ __launch_bounds__(64 * kBwdWM * kBwdWN, 1) void gemm_bwd_bf16_kernel(
     }
     return b;
   };
-  auto next_tile = [&]() {
+  auto next_tile = [&]() __attribute__((always_inline)) {
     BTile t{0, 0, 0, 0, 0, false};
     while (slot_id < n_slots && !t.valid) {
       t = tile_of(xcd_remap(slot_id, n_slots));
@@ -132,10 +150,20 @@ __global__ __launch_bounds__(64 * kBwdWM * kBwdWN, 1) void gemm_bwd_bf16_kernel(
   const uint16_t* zsrc[REG];
   int srow[REG];
   int ld_rows = 0, kr0 = 0, kr1 = 0, nk = 0;
-  auto set_sources = [&](const BTile& t) {
-    kr0 = t.r0;
-    kr1 = t.r1;
-    nk = WGRAD ? (t.r1 - t.r0 + BK - 1) / BK : Kdim / BK;
+  // GATHER_A: token rows of the four k-rows an A-half wave copies at the next
+  // issued k-step (k-rows 4*wave .. 4*wave+3 of the stage), -1 past the
+  // expert's rows. Wave-uniform, loaded with scalar loads one k-step ahead so
+  // that the vector-memory count of the copies is not disturbed.
+  int4 pf = int4{-1, -1, -1, -1};
+  auto load_pf = [&](int kt) __attribute__((always_inline)) {
+    pf = token_rows4(perm, __builtin_amdgcn_readfirstlane(kr0 + kt * BK + 4 * wave), kr1, topk, n_a);
+  };
+  auto set_sources = [&](const BTile& t) __attribute__((always_inline)) {
+    // Every lane computes the same tile; readfirstlane makes that visible to
+    // the compiler, so the k-loop and the row bounds stay scalar.
+    kr0 = __builtin_amdgcn_readfirstlane(t.r0);
+    kr1 = __builtin_amdgcn_readfirstlane(t.r1);
+    nk = WGRAD ? (kr1 - kr0 + BK - 1) / BK : Kdim / BK;
 #pragma unroll
     for (int j = 0; j < REG; ++j) {
       const int r = (wave * REG + j) % HALF_REG;  // region within the half
@@ -161,9 +189,11 @@ __global__ __launch_bounds__(64 * kBwdWM * kBwdWN, 1) void gemm_bwd_bf16_kernel(
       }
     }
     ld_rows = a_half ? lda : ldb;
+    if constexpr (GATHER_A)
+      if (a_half) load_pf(0);
   };
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  auto issue = [&](int kt, int stage) {
+  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
     const uint32_t base = lds0 + stage * STAGE + wave_u * REG * 1024;
 #pragma unroll
     for (int j = 0; j < REG; ++j) {
@@ -172,14 +202,20 @@ __global__ __launch_bounds__(64 * kBwdWM * kBwdWN, 1) void gemm_bwd_bf16_kernel(
         p = src[j] + (size_t)(a_half ? kt * BK : (kt * BK) % kwrap);
       } else if constexpr (!WGRAD) {
         p = src[j] + (size_t)kt * BK;
+      } else if (GATHER_A && a_half) {
+        const int q = srow[j] & 3;  // this lane's k-row among the wave's four
+        const int tok = (q & 2) ? ((q & 1) ? pf.w : pf.z) : ((q & 1) ? pf.y : pf.x);
+        p = tok >= 0 ? src[j] + (size_t)tok * ld_rows : zsrc[j];
       } else {
         const int row = kr0 + kt * BK + srow[j];
         p = row < kr1 ? src[j] + (size_t)row * ld_rows : zsrc[j];
       }
       dma16(p, base + j * 1024);
     }
+    if constexpr (GATHER_A)
+      if (a_half) load_pf(kt + 1);
   };
-  auto issue_first = [&]() {
+  auto issue_first = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < NSTAGE - 1; ++p)
       if (p < nk) issue(p, p);
@@ -207,7 +243,7 @@ __global__ __launch_bounds__(64 * kBwdWM * kBwdWN, 1) void gemm_bwd_bf16_kernel(
   f32x4_t acc[MT][NT];
   int vm = MT;  // 16-row slices of this wave holding a valid row (wave-uniform)
 
-  auto frag = [&](const lds_char_t* p) {
+  auto frag = [&](const lds_char_t* p) __attribute__((always_inline)) {
     if constexpr (WGRAD) {
       const bf16x4_t lo = lds_read_tr16(p);
       const bf16x4_t hi = lds_read_tr16(p + 4 * B_ROW);
@@ -216,7 +252,7 @@ __global__ __launch_bounds__(64 * kBwdWM * kBwdWN, 1) void gemm_bwd_bf16_kernel(
       return __builtin_bit_cast(bf16x8_t, lds_read_b128(p));
     }
   };
-  auto step = [&](int stage, bool full) {
+  auto step = [&](int stage, bool full) __attribute__((always_inline)) {
     const lds_char_t* As = smem + stage * STAGE;
     const lds_char_t* Bs = As + A_BYTES;
     bf16x8_t a[MT], b[NT];
@@ -233,7 +269,7 @@ __global__ __launch_bounds__(64 * kBwdWM * kBwdWN, 1) void gemm_bwd_bf16_kernel(
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[nt], a[mt], acc[mt][nt], 0, 0, 0);
       }
   };
-  auto wait_dma = [&](int stages) {
+  auto wait_dma = [&](int stages) __attribute__((always_inline)) {
     if (stages >= 3)
       asm volatile("s_waitcnt vmcnt(%0)" : : "n"(3 * DMA_PER_STAGE) : "memory");
     else if (stages == 2)
@@ -246,7 +282,7 @@ __global__ __launch_bounds__(64 * kBwdWM * kBwdWN, 1) void gemm_bwd_bf16_kernel(
   // Same ring discipline as the forward GEMM: before the barrier that
   // publishes k-step kt, each wave waits until only its own copies of later
   // k-steps remain in flight; the barrier also frees the slot of k-step kt-1.
-  auto main_loop = [&](bool full) {
+  auto main_loop = [&](bool full) __attribute__((always_inline)) {
     int slot = 0;
     for (int kt = 0; kt < nk; ++kt) {
       wait_dma(min(NSTAGE - 2, nk - 1 - kt));
@@ -264,9 +300,9 @@ __global__ __launch_bounds__(64 * kBwdWM * kBwdWN, 1) void gemm_bwd_bf16_kernel(
   auto pack2 = [](float v0, float v1) {
     return (uint32_t)f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16);
   };
-  auto pack4 = [&](const float* v) { return u32x2_t{pack2(v[0], v[1]), pack2(v[2], v[3])}; };
+  auto pack4 = [&](const float* v) __attribute__((always_inline)) { return u32x2_t{pack2(v[0], v[1]), pack2(v[2], v[3])}; };
   const bool odd = (g & 1) != 0;
-  auto store_pair = [&](uint16_t* crow, bool ok, int colP, u32x2_t pP, u32x2_t pQ) {
+  auto store_pair = [&](uint16_t* crow, bool ok, int colP, u32x2_t pP, u32x2_t pQ) __attribute__((always_inline)) {
     const u32x2_t send = odd ? pP : pQ;
     const u32x2_t got{(uint32_t)__shfl_xor((int)send[0], 16), (uint32_t)__shfl_xor((int)send[1], 16)};
     if (!ok) return;
@@ -275,7 +311,7 @@ __global__ __launch_bounds__(64 * kBwdWM * kBwdWN, 1) void gemm_bwd_bf16_kernel(
     else
       *(u32x4_t*)(crow + colP + 4 * g) = u32x4_t{pP[0], pP[1], got[0], got[1]};
   };
-  auto store_tile = [&](const BTile& t) {
+  auto store_tile = [&](const BTile& t) __attribute__((always_inline)) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       if (mt >= vm) continue;
@@ -393,16 +429,24 @@ __global__ __launch_bounds__(256) void gemm_bwd_f32_kernel(const float* __restri
                                                            const int32_t* __restrict__ offsets, int E, int rows,
                                                            int Mdim, int Ndim, int Kdim, const float* __restrict__ gu,
                                                            int I, float* __restrict__ C, int ldc,
-                                                           long long c_stride) {
+                                                           long long c_stride, const int32_t* __restrict__ perm,
+                                                           int topk, int n_a) {
   const int col = blockIdx.x * 64 + (threadIdx.x & 63);
   const int row = blockIdx.y * 4 + (threadIdx.x >> 6);
   if (col >= Ndim) return;
-  if constexpr (MODE == kWgrad) {
+  if constexpr (MODE == kWgrad || MODE == kWgradGather) {
     const int e = blockIdx.z;
     if (row >= Mdim) return;
     const int r0 = min(max(offsets[e], 0), rows), r1 = min(max(offsets[e + 1], r0), rows);
     float sum = 0.f;
-    for (int r = r0; r < r1; ++r) sum = fmaf(A[(size_t)r * lda + row], B[(size_t)r * ldb + col], sum);
+    for (int r = r0; r < r1; ++r) {
+      int ar = r;
+      if constexpr (MODE == kWgradGather) {
+        const int f = perm[r];
+        ar = ((unsigned)f < (unsigned)(n_a * topk)) ? f / topk : 0;
+      }
+      sum = fmaf(A[(size_t)ar * lda + row], B[(size_t)r * ldb + col], sum);
+    }
     C[(size_t)e * c_stride + (size_t)row * ldc + col] = sum;
   } else {
     if (row >= rows) return;
@@ -434,8 +478,9 @@ __global__ __launch_bounds__(256) void gemm_bwd_f32_kernel(const float* __restri
 template <int MODE>
 hipError_t launch_bwd(const void* A, int lda, const void* B, int ldb, long long b_stride, const int32_t* offsets,
                       int E, int rows, int Mdim, int Ndim, int Kdim, const void* gu, int I, void* C, int ldc,
-                      long long c_stride, moe_dtype dt, hipStream_t s, int kwrap = 0) {
-  constexpr bool WG = MODE == kWgrad || MODE == kWgradF32;
+                      long long c_stride, moe_dtype dt, hipStream_t s, int kwrap = 0,
+                      const int32_t* perm = nullptr, int topk = 1, int n_a = 0) {
+  constexpr bool WG = MODE == kWgrad || MODE == kWgradF32 || MODE == kWgradGather;
   if (dt == MOE_BF16) {
     const int NB = ceil_div(Ndim, BN);
     const int MB = WG ? ceil_div(Mdim, kBwdBM) : 1;
@@ -444,12 +489,12 @@ hipError_t launch_bwd(const void* A, int lda, const void* B, int ldb, long long 
     const int grid = std::min(n_slots, stream_cu_count(s));
     gemm_bwd_bf16_kernel<MODE><<<grid, 64 * kBwdWM * kBwdWN, 0, s>>>(
         (const uint16_t*)A, lda, (const uint16_t*)B, ldb, b_stride, offsets, E, rows, Mdim, Ndim, Kdim,
-        (const uint16_t*)gu, I, C, ldc, c_stride, MB, NB, n_slots, kwrap);
-  } else if constexpr (MODE <= kWgrad) {
-    dim3 grid(ceil_div(Ndim, 64), ceil_div(MODE == kWgrad ? Mdim : rows, 4), MODE == kWgrad ? E : 1);
+        (const uint16_t*)gu, I, C, ldc, c_stride, MB, NB, n_slots, kwrap, perm, topk, n_a);
+  } else if constexpr (MODE <= kWgrad || MODE == kWgradGather) {
+    dim3 grid(ceil_div(Ndim, 64), ceil_div(WG ? Mdim : rows, 4), WG ? E : 1);
     gemm_bwd_f32_kernel<MODE><<<grid, 256, 0, s>>>((const float*)A, lda, (const float*)B, ldb, b_stride, offsets, E,
                                                    rows, Mdim, Ndim, Kdim, (const float*)gu, I, (float*)C, ldc,
-                                                   c_stride);
+                                                   c_stride, perm, topk, n_a);
   }
   return hipGetLastError();
 }
@@ -489,6 +534,13 @@ hipError_t launch_w13_backward(const void* dgate_up, const int32_t* offsets, int
 hipError_t launch_weight_grad(const void* a, const void* b, const int32_t* offsets, int rows, int E, int M, int N,
                               moe_dtype dt, void* dW, hipStream_t s) {
   return launch_bwd<kWgrad>(a, M, b, N, 0, offsets, E, rows, M, N, 0, nullptr, 0, dW, N, (long long)M * N, dt, s);
+}
+
+hipError_t launch_weight_grad_gather(const void* x, const int32_t* perm, int n, int K, const void* b,
+                                     const int32_t* offsets, int E, int M, int N, moe_dtype dt, void* dW,
+                                     hipStream_t s) {
+  return launch_bwd<kWgradGather>(x, M, b, N, 0, offsets, E, n * K, M, N, 0, nullptr, 0, dW, N, (long long)M * N, dt,
+                                  s, 0, perm, K, n);
 }
 
 }  // namespace moe

@@ -86,7 +86,9 @@ TrainLayout train_layout(int n, int E, int K) {
 size_t route_bwd_ws(int n, int H, int E) { return align_up(route_bwd_workspace(n, H, E)); }
 
 // moe_backward workspace, in order. rows_a holds dY_perm, then dX_perm (dY_perm
-// is dead once dgate_up and dW2 are done); rows_b the gathered x_perm.
+// is dead once dgate_up and dW2 are done); rows_b the gathered x_perm. (dW13
+// straight from x through perm, moe_expert_weight_grad_gather, needs no
+// rows_b but measured slower than the gather plus the plain weight gradient.)
 struct BackwardLayout {
   size_t rows_a, rows_b, dgu, dw, dlogits, dx_router, rws, total;
 };
@@ -393,6 +395,17 @@ moe_status moe_expert_weight_grad(const void* a, const void* b, const int32_t* o
   if (offsets == nullptr || dW == nullptr) return MOE_EINVAL;
   if (rows > 0 && (a == nullptr || b == nullptr)) return MOE_EINVAL;
   return from_hip(launch_weight_grad(a, b, offsets, rows, E, M, N, dt, dW, stream));
+}
+
+moe_status moe_expert_weight_grad_gather(const void* x, const int32_t* perm, int n, int K, const void* b,
+                                         const int32_t* offsets, int E, int M, int N, moe_dtype dt, void* dW,
+                                         hipStream_t stream) {
+  if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
+  if (n < 0 || K < 1 || K > kMaxTopK || (long long)n * K > INT32_MAX) return MOE_EINVAL;
+  if (E < 1 || E > kMaxExperts || !hidden_ok(M, dt) || !hidden_ok(N, dt)) return MOE_EINVAL;
+  if (offsets == nullptr || dW == nullptr) return MOE_EINVAL;
+  if (n > 0 && (x == nullptr || perm == nullptr || b == nullptr)) return MOE_EINVAL;
+  return from_hip(launch_weight_grad_gather(x, perm, n, K, b, offsets, E, M, N, dt, dW, stream));
 }
 
 moe_status moe_dispatch_backward(const void* dX_perm, const int32_t* inv, const float* add, int n, int H, int K,

@@ -96,6 +96,10 @@ hipError_t launch_weight_grad(const void* a, const void* b, const int32_t* offse
                               moe_dtype dt, void* dW, hipStream_t s);
 // Zero `bytes` (a multiple of 4) with a kernel.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// dW[e] = x_e^T . b_e with the rows of x gathered: row r of x_e is x[perm[r] / K].
+hipError_t launch_weight_grad_gather(const void* x, const int32_t* perm, int n, int K, const void* b,
+                                     const int32_t* offsets, int E, int M, int N, moe_dtype dt, void* dW,
+                                     hipStream_t s);
 // Token chunks of the dW_gate reduction for n tokens.
 int route_bwd_chunks(int n);
 // Workspace bytes of launch_route_backward.

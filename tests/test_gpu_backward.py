@@ -194,6 +194,29 @@ def test_expert_weight_grad(dev, rows, E, M, N, dtype, kind):
         assert_close(got, ref, dtype, f"dW rows={rows} E={E} M={M} N={N} {kind}", intermediate=True)
 
 
+@pytest.mark.parametrize("n,K,E,M,N,dtype,kind", [(300, 2, 8, 64, 128, "bf16", "routed"), (1000, 4, 16, 192, 256, "bf16", "skewed"),
+                                                  (4096, 8, 64, 2048, 2048, "bf16", "routed"), (65, 3, 5, 64, 64, "f32", "routed"),
+                                                  (7, 2, 8, 64, 128, "bf16", "routed")])
+def test_expert_weight_grad_gather(dev, n, K, E, M, N, dtype, kind):
+    """dW13 with the rows of x read through perm equals the weight gradient of the explicitly gathered rows."""
+    rng = np.random.default_rng(n + M)
+    bias = zipf_bias(E) if kind == "skewed" else None
+    _, e_top, _, perm, _, offsets = _routing(n, E, K, seed=n + 5, bias=bias)
+    xb, xf = _draw(rng, (n, M), dtype)
+    bb, bf = _draw(rng, (n * K, N), dtype)
+    dW = torch.full((E, M, N), float("nan"), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device=dev)
+    moe.moe_expert_weight_grad_gather(dev_tensor(xb, dtype, dev), _i32(perm, dev), K, dev_tensor(bb, dtype, dev),
+                                      _i32(offsets, dev), dW=dW)
+    torch.cuda.synchronize()
+    got = to_f64(dW)
+    assert np.isfinite(got).all()
+    ref = oracle.grouped_weight_grad(xf[perm // K], bf, offsets)
+    counts = np.diff(offsets)
+    for e in np.flatnonzero(counts == 0):
+        assert (got[e] == 0).all()
+    assert_close(got, ref, dtype, f"dW gathered n={n} K={K} E={E} M={M} N={N}", intermediate=True)
+
+
 # ---------------------------------------------------------------------------
 # moe_route_backward
 # ---------------------------------------------------------------------------
