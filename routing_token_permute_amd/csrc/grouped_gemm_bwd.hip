@@ -311,6 +311,16 @@ __global__ __launch_bounds__(64 * kBwdWM * kBwdWN, 1) void gemm_bwd_bf16_kernel(
     else
       *(u32x4_t*)(crow + colP + 4 * g) = u32x4_t{pP[0], pP[1], got[0], got[1]};
   };
+  // Inverse of store_pair: pP/pQ receive this lane's columns 4g..4g+3 of tiles
+  // P (colP..colP+15) and Q = P + 16 from one 16-byte load per lane.
+  auto load_pair = [&](const uint16_t* row, int colP, u32x2_t& pP, u32x2_t& pQ) __attribute__((always_inline)) {
+    const u32x4_t v = *(const u32x4_t*)(row + (odd ? colP + 16 + 4 * (g - 1) : colP + 4 * g));
+    const u32x2_t keep = odd ? u32x2_t{v[2], v[3]} : u32x2_t{v[0], v[1]};
+    const u32x2_t give = odd ? u32x2_t{v[0], v[1]} : u32x2_t{v[2], v[3]};
+    const u32x2_t got{(uint32_t)__shfl_xor((int)give[0], 16), (uint32_t)__shfl_xor((int)give[1], 16)};
+    pP = odd ? got : keep;
+    pQ = odd ? keep : got;
+  };
   auto store_tile = [&](const BTile& t) __attribute__((always_inline)) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -351,17 +361,17 @@ __global__ __launch_bounds__(64 * kBwdWM * kBwdWN, 1) void gemm_bwd_bf16_kernel(
         if constexpr (MODE == kDgradSwiglu) {
           // dgate = dh * up * s * (1 + gate * (1 - s)), dup = dh * gate * s,
           // s = 1 / (1 + exp(-gate)), from the saved bf16 pre-activations.
+          // The gate/up values of a pair of adjacent 16-column tiles come in
+          // with one 16-byte load per lane, the mirror of store_pair: lane g
+          // loads where it would store and swaps halves with lane g^1.
           const uint16_t* grow = gu + r * (size_t)(2 * I);
 #pragma unroll
           for (int q = 0; q < NT; q += 2) {
             u32x2_t gv[2], uv[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              int col = t.nb * BN + wn * (BN / WN) + (q + h) * 16 + 4 * g;
-              if (col >= Ndim) col = 0;
-              gv[h] = *(const u32x2_t*)(grow + col);
-              uv[h] = *(const u32x2_t*)(grow + I + col);
-            }
+            int colP = t.nb * BN + wn * (BN / WN) + q * 16;
+            if (colP >= Ndim) colP = 0;  // feeds only outputs that are never stored
+            load_pair(grow, colP, gv[0], gv[1]);
+            load_pair(grow + I, colP, uv[0], uv[1]);
             float dg[2][4], du[2][4];
 #pragma unroll
             for (int h = 0; h < 2; ++h)
@@ -375,10 +385,10 @@ __global__ __launch_bounds__(64 * kBwdWM * kBwdWN, 1) void gemm_bwd_bf16_kernel(
                 dg[h][j] = dh * ua * s * (1.f + ga * (1.f - s));
                 du[h][j] = dh * ga * s;
               }
-            const int colP = t.nb * BN + wn * (BN / WN) + q * 16;
-            const bool ok = row_ok && colP < Ndim;
-            store_pair(crow, ok, colP, pack4(dg[0]), pack4(dg[1]));
-            store_pair(crow + I, ok, colP, pack4(du[0]), pack4(du[1]));
+            const int colS = t.nb * BN + wn * (BN / WN) + q * 16;
+            const bool ok = row_ok && colS < Ndim;
+            store_pair(crow, ok, colS, pack4(dg[0]), pack4(dg[1]));
+            store_pair(crow + I, ok, colS, pack4(du[0]), pack4(du[1]));
           }
         } else {
 #pragma unroll
