@@ -36,13 +36,19 @@ constexpr int kW8BK = 64;           // k per stage (bytes per B row, elements pe
 constexpr int kW8ARow = kW8BK * 2;  // bytes per staged A row
 constexpr int kW8BRow = kW8BK;      // bytes per staged B row
 
+// At most three stages. The 32-row decode tiles stream 16 KB of codes per
+// stage, yet a deeper ring made them slower: at n=32 GEMM1 took 49.9, 50.8,
+// 55.4, 59.4 and 62 us with 3, 4, 5, 6 and 8 stages, and 58 us with 2. The
+// 256-row tiles fit three 48 KB stages in any case.
+constexpr int kW8MaxStages = 3;
+
 template <int BM>
 struct W8Cfg {
   static constexpr int A_BYTES = BM * kW8ARow;
   static constexpr int B_BYTES = BN * kW8BRow;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int FIT = (160 * 1024) / STAGE;
-  static constexpr int NSTAGE = FIT > kMaxStages ? kMaxStages : FIT;
+  static constexpr int NSTAGE = FIT > kW8MaxStages ? kW8MaxStages : FIT;
   static constexpr int LDS_BYTES = NSTAGE * STAGE;
   static constexpr int REGIONS = STAGE / 1024;
 };
@@ -87,7 +93,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_w8_kernel(
   constexpr int A_REG = A_BYTES / 1024;
   constexpr int DMA_PER_STAGE = REG;
   static_assert(REG * NW == Cfg::REGIONS && NT % (GATED ? 4 : 2) == 0, "tile split");
-  static_assert(NSTAGE >= 2 && NSTAGE <= 5 && 3 * DMA_PER_STAGE <= 63, "vmcnt range");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 8 && 6 * DMA_PER_STAGE <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(16))) char smem_raw[Cfg::LDS_BYTES];
   lds_char_t* smem = (lds_char_t*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -202,15 +208,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_w8_kernel(
         }
     }
   };
+  // Waits until at most `stages` (<= NSTAGE - 2) of this wave's later stages
+  // are still in flight.
   auto wait_dma = [&](int stages) {
-    if (stages >= 3)
-      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(3 * DMA_PER_STAGE) : "memory");
-    else if (stages == 2)
-      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(2 * DMA_PER_STAGE) : "memory");
-    else if (stages == 1)
-      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(DMA_PER_STAGE) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+    switch (stages) {
+      case 0: asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); break;
+      case 1: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(DMA_PER_STAGE) : "memory"); break;
+      case 2: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(2 * DMA_PER_STAGE) : "memory"); break;
+      case 3: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(3 * DMA_PER_STAGE) : "memory"); break;
+      case 4: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(4 * DMA_PER_STAGE) : "memory"); break;
+      case 5: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(5 * DMA_PER_STAGE) : "memory"); break;
+      default: asm volatile("s_waitcnt vmcnt(%0)" : : "n"(6 * DMA_PER_STAGE) : "memory"); break;
+    }
   };
   // The ring discipline of grouped_gemm.hip: wait for this wave's copies of
   // k-step kt, publish it with the barrier (which also frees the slot of
