@@ -67,6 +67,8 @@ ROUTE_CASES = [
     (130, 192, 100, 7, "bf16", True, None),
     (50, 64, 256, 64, "bf16", False, None),
     (33, 68, 5, 3, "f32", False, None),
+    (65536, 256, 64, 8, "bf16", False, None),  # 4096 workgroups
+    (20000, 512, 128, 8, "bf16", True, None),  # 128 experts: 8 expert tiles, 4 waves over H
 ]
 
 
@@ -128,6 +130,10 @@ PERMUTE_CASES = [
     (5000, 64, 64, 8, 4, "routed"),  # 40000 pairs: past the single-workgroup limit, count + place launches
     (4096, 64, 8, 8, 1, "one_hot"),  # all 32768 pairs in one segment (count + place launches)
     (512, 64, 8, 8, 1, "one_hot"),  # 4096 pairs in one segment: the single-workgroup maximum
+    (16384, 64, 64, 8, 8, "routed"),  # 131072 pairs: 128 blocks of 1024 (four 64-pair steps per wave)
+    (65536, 64, 64, 8, 8, "random"),  # 524288 pairs: blocks of 4096, two batches of 64-pair steps per wave
+    (70001, 64, 256, 3, 32, "random"),  # 210003 pairs, 256 experts: the last block is partial
+    (65536, 64, 8, 8, 1, "one_hot"),  # 524288 pairs in one segment
 ]
 
 
@@ -384,6 +390,33 @@ def test_forward_configs(dev, name):
 def test_forward_small_shapes(dev, n, H, I, E, K, dtype, renorm):  # noqa: E741
     w = make_layer(n, H, I, E, K, dtype=dtype, renorm=renorm, seed=n + H + I)
     _forward_parity(dev, w, f"forward n={n} E={E} K={K}")
+
+
+def test_forward_large_batch_sampled(dev):
+    """The OLMoE layer on 16384 tokens (131072 expert rows, about 20 GEMM tiles per CU): every token's
+    routing is checked, and the outputs of 512 sampled tokens against the oracle run on those tokens
+    alone (the layer treats each token independently)."""
+    w = make_config("olmoe_bf16")
+    n = 16384
+    rng = np.random.default_rng(16384)
+    xb, xf = random_bf16_matrix(rng, (n, w.H))
+    t = layer_tensors(w, dev)
+    x = dev_tensor(xb, "bf16", dev)
+    y, logits, ids, wts, counts = moe.moe_forward(x, t["W_gate"], t["W13"], t["W2"], w.K, w.renorm, routing_out=True)
+    torch.cuda.synchronize()
+    L = oracle.round_to_f32(oracle.router_logits(xf, w.W_gate_f32, None))
+    e_ref, w_ref, _ = oracle.route_from_logits(L, w.K, w.renorm)
+    safe = ~(oracle.topk_margin(L, w.K) <= 1e-4)
+    ids_h = ids.cpu().numpy()
+    print(f"[forward n={n}] near-tie rows: {int((~safe).sum())} of {n}", flush=True)
+    assert (ids_h[safe] == e_ref[safe]).all()
+    if safe.all():
+        assert (counts.cpu().numpy() == oracle.expert_counts(e_ref, w.E)).all()
+    assert int(counts.sum()) == n * w.K
+    sample = np.sort(rng.choice(np.flatnonzero(safe), size=512, replace=False))
+    ref = oracle.forward(xf[sample], w.W_gate_f32, w.W13_f32, w.W2_f32, w.K, w.renorm)
+    assert (ref["e_top"] == e_ref[sample]).all()
+    assert_close(to_f64(y)[sample], ref["y"], "bf16", f"forward n={n}, 512 sampled tokens")
 
 
 def test_forward_zero_tokens(dev):
