@@ -83,7 +83,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
   static_assert(NT % (GATED ? 4 : 2) == 0 && MT >= 1 && REG * NW == Cfg::REGIONS, "tile split");
   static_assert(!(SCATTER && (GATED || GATHER)), "the weighted scatter is a GEMM2 epilogue");
   static_assert(!SAVE || GATED, "the pre-activations belong to GEMM1");
-  static_assert(NSTAGE >= 2 && NSTAGE <= 5 && 4 * DMA_PER_STAGE <= 63, "vmcnt range");
+  // Epilogue stores per wave and tile when they go out as buffer stores
+  // (every wave issues all of them; lanes without a valid output carry an
+  // out-of-range offset, which the hardware drops), so that the waits of the
+  // next tile can count them exactly. The weighted scatter keeps plain stores.
+  constexpr bool ST_COUNTED = !SCATTER;
+  constexpr int ST = !ST_COUNTED ? 0 : GATED ? MT * (NT / 4) * (SAVE ? 3 : 1) : MT * (NT / 2);
+  static_assert(NSTAGE >= 2 && NSTAGE <= 5 && (NSTAGE - 2) * DMA_PER_STAGE + ST <= 63, "vmcnt range");
+  static_assert(NSTAGE - 2 <= 3, "wait_dma covers up to three later stages");
   __shared__ __attribute__((aligned(16))) char smem_raw[Cfg::LDS_BYTES];
   lds_char_t* smem = (lds_char_t*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -225,9 +232,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
   // in flight (every stage is DMA_PER_STAGE loads per lane). Stores still in
   // flight from the previous tile only make the wait longer.
   auto wait_dma = [&](int stages) {
-    if (stages >= 4)
-      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(4 * DMA_PER_STAGE) : "memory");
-    else if (stages == 3)
+    if (stages >= 3)
       asm volatile("s_waitcnt vmcnt(%0)" : : "n"(3 * DMA_PER_STAGE) : "memory");
     else if (stages == 2)
       asm volatile("s_waitcnt vmcnt(%0)" : : "n"(2 * DMA_PER_STAGE) : "memory");
@@ -236,6 +241,21 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
     else
       asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
   };
+  // The same wait for a k-step that was put in flight before the previous
+  // tile's ST epilogue stores: those stores are younger than it, so they may
+  // stay outstanding too. Vector memory operations retire in issue order, so
+  // the count still proves that this k-step has landed, and the stores drain
+  // behind the first k-steps instead of holding them up.
+  auto wait_dma_st = [&](int stages) {
+    if (stages >= 3)
+      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(3 * DMA_PER_STAGE + ST) : "memory");
+    else if (stages == 2)
+      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(2 * DMA_PER_STAGE + ST) : "memory");
+    else if (stages == 1)
+      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(DMA_PER_STAGE + ST) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(ST) : "memory");
+  };
   // Pipeline over an NSTAGE-deep LDS ring; the first NSTAGE-1 k-steps are
   // already in flight. While k-step kt is multiplied, k-steps up to
   // kt+NSTAGE-1 are in flight from HBM straight into LDS. Before the barrier
@@ -243,10 +263,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
   // later k-steps remain outstanding. The barrier also guarantees that every
   // wave has finished reading k-step kt-1 (its MFMAs consumed those reads),
   // whose slot the next issue overwrites.
-  auto main_loop = [&](bool full) {
+  // after_st: this wave issued the previous tile's ST epilogue stores right
+  // after the first NSTAGE-1 k-steps of this tile.
+  auto main_loop = [&](bool full, bool after_st) {
     int slot = 0;  // ring slot of k-step kt
     for (int kt = 0; kt < nk; ++kt) {
-      wait_dma(min(NSTAGE - 2, nk - 1 - kt));
+      if (ST_COUNTED && after_st && kt <= NSTAGE - 2)
+        wait_dma_st(min(NSTAGE - 2, nk - 1 - kt));
+      else
+        wait_dma(min(NSTAGE - 2, nk - 1 - kt));
       __syncthreads();
       if (kt + NSTAGE - 1 < nk) issue(kt + NSTAGE - 1, slot == 0 ? NSTAGE - 1 : slot - 1);
       if (full || vm > 0) {
@@ -284,6 +309,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
     else
       *(u32x4_t*)(crow + colP + 4 * g) = u32x4_t{pP[0], pP[1], got[0], got[1]};
   };
+  // The same exchange, stored through a buffer resource whose base is the
+  // tile's first output row: `rowoff` is the byte offset of this lane's row,
+  // and a lane without a valid output sends an offset past the resource's
+  // range, so the store instruction is issued by every wave (ST per tile) and
+  // only the valid lanes write.
+  constexpr uint32_t kDropped = 0x80000000u;
+  auto store_pair_buf = [&](__amdgpu_buffer_rsrc_t rs, uint32_t rowoff, bool ok, int colP, u32x2_t pP, u32x2_t pQ) {
+    const u32x2_t send = odd ? pP : pQ;
+    const u32x2_t got{(uint32_t)__shfl_xor((int)send[0], 16), (uint32_t)__shfl_xor((int)send[1], 16)};
+    const int col = odd ? colP + 16 + 4 * (g - 1) : colP + 4 * g;
+    const u32x4_t v = odd ? u32x4_t{got[0], got[1], pQ[0], pQ[1]} : u32x4_t{pP[0], pP[1], got[0], got[1]};
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, ok ? rowoff + (uint32_t)col * 2u : kDropped, 0, 0);
+  };
   // SCATTER: each lane's destination rows and weights, loaded when the tile
   // starts so that the epilogue does not wait for them.
   int sc_row[MT];
@@ -297,7 +335,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
       sc_w[mt] = ((unsigned)f < (unsigned)n_a) ? wrow[f] : 0.f;
     }
   };
-  auto store_tile = [&](const Tile& t) {
+  auto store_tile_plain = [&](const Tile& t) {
     const int mrows = t.r1 - t.r0;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -358,6 +396,72 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
     }
   };
 
+  // Counted form (every path but the scatter): ST buffer stores per wave,
+  // also for the 16-row slices a short tile does not fill.
+  auto store_tile_counted = [&](const Tile& t) {
+    const int r0 = __builtin_amdgcn_readfirstlane(t.r0);
+    const int mrows = __builtin_amdgcn_readfirstlane(t.r1 - t.r0);
+    const __amdgpu_buffer_rsrc_t rc =
+        __builtin_amdgcn_make_buffer_rsrc(C + (size_t)r0 * ldc, 0, (int)((uint32_t)mrows * (uint32_t)ldc * 2u),
+                                          0x00020000);
+    __amdgpu_buffer_rsrc_t rg = rc;
+    if constexpr (SAVE)
+      rg = __builtin_amdgcn_make_buffer_rsrc(gu_out + (size_t)r0 * (2 * up_col), 0,
+                                             (int)((uint32_t)mrows * (uint32_t)(2 * up_col) * 2u), 0x00020000);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int row = wm * (BM / WM) + mt * 16 + li;
+      const bool row_ok = mt < vm && row < mrows;
+      const uint32_t coff = (uint32_t)row * (uint32_t)ldc * 2u;
+      if constexpr (GATED) {
+        u32x2_t hp[NT / 2];
+#pragma unroll
+        for (int nt = 0; nt < NT / 2; ++nt) {
+          float hv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float gv = acc[mt][nt][j], uv = acc[mt][nt + NT / 2][j];
+            hv[j] = gv / (1.f + __expf(-gv)) * uv;
+          }
+          hp[nt] = u32x2_t{pack2(hv[0], hv[1]), pack2(hv[2], hv[3])};
+        }
+#pragma unroll
+        for (int q = 0; q < NT / 2; q += 2) {
+          const int colP = t.nb * (BN / 2) + wn * (BN / 2 / WN) + q * 16;
+          store_pair_buf(rc, coff, row_ok && colP < Nout, colP, hp[q], hp[q + 1]);
+        }
+        if constexpr (SAVE) {
+          const uint32_t goff = (uint32_t)row * (uint32_t)(2 * up_col) * 2u;
+#pragma unroll
+          for (int q = 0; q < NT / 2; q += 2) {
+            const int colP = t.nb * (BN / 2) + wn * (BN / 2 / WN) + q * 16;
+            const f32x4_t g0 = acc[mt][q], g1 = acc[mt][q + 1];
+            const f32x4_t u0 = acc[mt][q + NT / 2], u1 = acc[mt][q + 1 + NT / 2];
+            store_pair_buf(rg, goff, row_ok && colP < Nout, colP, u32x2_t{pack2(g0[0], g0[1]), pack2(g0[2], g0[3])},
+                           u32x2_t{pack2(g1[0], g1[1]), pack2(g1[2], g1[3])});
+            store_pair_buf(rg, goff + (uint32_t)up_col * 2u, row_ok && colP < Nout, colP,
+                           u32x2_t{pack2(u0[0], u0[1]), pack2(u0[2], u0[3])},
+                           u32x2_t{pack2(u1[0], u1[1]), pack2(u1[2], u1[3])});
+          }
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < NT; q += 2) {
+          const f32x4_t u = acc[mt][q], v = acc[mt][q + 1];
+          const int colP = t.nb * BN + wn * (BN / WN) + q * 16;
+          store_pair_buf(rc, coff, row_ok && colP < Nout, colP, u32x2_t{pack2(u[0], u[1]), pack2(u[2], u[3])},
+                         u32x2_t{pack2(v[0], v[1]), pack2(v[2], v[3])});
+        }
+      }
+    }
+  };
+  auto store_tile = [&](const Tile& t) {
+    if constexpr (ST_COUNTED)
+      store_tile_counted(t);
+    else
+      store_tile_plain(t);
+  };
+
   // Persistent loop over this workgroup's tiles. Before the epilogue of a
   // tile, the first NSTAGE-1 k-steps of the next one are put in flight (the
   // barrier after the main loop frees the whole ring), so the DMA of the
@@ -366,6 +470,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
   if (!t.valid) return;
   set_sources(t);
   issue_first();
+  bool after_st = false;
   for (;;) {
     if constexpr (SCATTER) load_scatter(t);
     const int mrows = __builtin_amdgcn_readfirstlane(t.r1 - t.r0);
@@ -375,9 +480,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (vm == MT)
-      main_loop(true);
+      main_loop(true, after_st);
     else
-      main_loop(false);
+      main_loop(false, after_st);
     __syncthreads();
     const Tile nt_ = next_tile();
     if (nt_.valid) {
@@ -387,6 +492,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
     store_tile(t);
     if (!nt_.valid) break;
     t = nt_;
+    after_st = true;
   }
 }
 
