@@ -13,13 +13,11 @@
 // The WK partial logit tiles are summed in LDS in wave order, so the result
 // does not depend on timing.
 //
-// Top-K. For each token one wave ranks every expert: lane e counts the
-// experts that come before it in the order (logit descending, index
-// ascending), scanning the token's order keys in LDS; the lanes whose rank is
-// below K write slot `rank`. The row maximum falls out of the same scan, and
-// the exp of each logit is computed once by its lane and the denominator is
-// summed in expert order by every lane, so all lanes hold bitwise the same
-// value. No cross-lane reductions are needed.
+// Top-K. One wave per token, one expert per lane (more for E > 64): the row
+// maximum and the softmax denominator are wave reductions over DPP lane
+// moves in a fixed order; then K rounds each take the largest remaining order
+// key (logit descending) and, among equal keys, the lowest expert index (a
+// ballot of the lanes that hold it), and clear it. Slot k is written by lane k.
 #include <math.h>
 
 #include "moe_internal.hpp"
@@ -39,83 +37,108 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+// Wave-wide reductions over the 64 lanes with DPP lane moves: two quad
+// swaps, the half-row and row mirrors (every lane of a 16-lane row then
+// holds the row's result), then the row-15 and row-31 broadcasts into the
+// upper rows; lane 63 ends with the total, read back as a wave constant.
+// The order of the fp32 additions is fixed, so the sum is deterministic.
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, int ctrl_sel) {
+  switch (ctrl_sel) {
+    case 0: return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false);   // quad [1,0,3,2]
+    case 1: return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false);   // quad [2,3,0,1]
+    case 2: return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false);  // row half mirror
+    case 3: return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false);  // row mirror
+    case 4: return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false);  // row bcast 15
+    default: return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false); // row bcast 31
+  }
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    const uint32_t o = dpp_u32(v, i);
+    v = o > v ? o : v;
+  }
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    // Rows that a broadcast step leaves out add nothing.
+    const uint32_t o = dpp_u32(__float_as_uint(v), i);
+    const bool take = i < 4 || (i == 4 ? ((lane_id() >> 4) & 1) : (lane_id() >> 5));
+    v += take ? __uint_as_float(o) : 0.f;
+  }
+  return __uint_as_float(__builtin_amdgcn_readlane((int)__float_as_uint(v), 63));
+}
+
 // Softmax + top-K of one token whose E logits (fp32) and order keys sit in
-// LDS; one wave, EPL experts per lane (EPL * 64 >= E). `keys` and `ex` (the
-// wave-private LDS scratch of kMaxExperts + kMaxTopK floats) are 16-byte
-// aligned.
+// LDS; one wave, EPL experts per lane (EPL * 64 >= E). The K experts are
+// taken one at a time: the largest remaining order key over the wave, and
+// among equal keys the lowest expert index (a ballot of the lanes holding
+// it); that expert's key is then cleared. The first round's maximum is the
+// softmax's row maximum. `ex` (wave-private LDS scratch) is not needed here.
 template <int EPL>
 __device__ __forceinline__ void topk_token(const float* lg, const uint32_t* keys, int E, int K, int renorm, float* ex,
-                           int32_t* ids_out, float* w_out) {
+                                           int32_t* ids_out, float* w_out) {
+  (void)ex;
   const int lane = lane_id();
-  uint32_t mine[EPL];
-  int rank[EPL];
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) {
-    mine[j] = (lane + 64 * j < E) ? keys[lane + 64 * j] : 0u;
-    rank[j] = 0;
-  }
-  uint32_t kmax = 0u;
-  auto visit = [&](uint32_t kf, int f) {
-    kmax = kf > kmax ? kf : kmax;
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) rank[j] += (kf > mine[j]) || (kf == mine[j] && f < lane + 64 * j);
-  };
-  // Four keys per read (the same 16 bytes in every lane: an LDS broadcast).
-  const int E4 = E & ~3;
-  const u32x4_t* k4 = (const u32x4_t*)__builtin_assume_aligned(keys, 16);
-#pragma unroll 4
-  for (int f = 0; f < E4; f += 4) {
-    const u32x4_t kv = k4[f >> 2];
-    visit(kv[0], f);
-    visit(kv[1], f + 1);
-    visit(kv[2], f + 2);
-    visit(kv[3], f + 3);
-  }
-  for (int f = E4; f < E; ++f) visit(keys[f], f);
-  const float m = key_value(kmax);
-  // Each expert's exp(l - m) once, by its own lane; then every lane sums them
-  // in expert order, so all lanes hold bitwise the same denominator.
-#pragma unroll
-  for (int j = 0; j < EPL; ++j)
-    if (lane + 64 * j < E) ex[lane + 64 * j] = expf(lg[lane + 64 * j] - m);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  float s = 0.f;
-  const f32x4_t* x4 = (const f32x4_t*)__builtin_assume_aligned(ex, 16);
-#pragma unroll 4
-  for (int f = 0; f < E4; f += 4) {
-    const f32x4_t v = x4[f >> 2];
-    s += v[0];
-    s += v[1];
-    s += v[2];
-    s += v[3];
-  }
-  for (int f = E4; f < E; ++f) s += ex[f];
-  float* slot = ex + kMaxExperts;  // K weights in slot order, for the renorm sum
+  uint32_t key[EPL];
+  float exv[EPL];
+  uint32_t lmax = 0u;
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane + 64 * j;
-    if (e < E && rank[j] < K) {
-      const float w = ex[e] / s;
-      ids_out[rank[j]] = e;
-      if (renorm)
-        slot[rank[j]] = w;
-      else
-        w_out[rank[j]] = w;
+    key[j] = e < E ? keys[e] : 0u;
+    lmax = key[j] > lmax ? key[j] : lmax;
+  }
+  const uint32_t kmax = wave_max_u32(lmax);
+  const float m = key_value(kmax);
+  float part = 0.f;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + 64 * j;
+    exv[j] = e < E ? expf(lg[e] - m) : 0.f;
+    part += exv[j];
+  }
+  const float s = wave_sum_f32(part);
+  int my_id = 0;
+  float my_w = 0.f, t = 0.f;
+  for (int k = 0; k < K; ++k) {
+    uint32_t mx = kmax;
+    if (k > 0) {
+      lmax = 0u;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) lmax = key[j] > lmax ? key[j] : lmax;
+      mx = wave_max_u32(lmax);
     }
+    int win = -1;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const uint64_t b = __ballot(key[j] == mx);
+      if (win < 0 && b != 0) win = 64 * j + __ffsll((long long)b) - 1;
+    }
+    win = __builtin_amdgcn_readfirstlane(win);
+    const int wl = win & 63, wj = win >> 6;
+    float ev = exv[0];
+#pragma unroll
+    for (int j = 1; j < EPL; ++j)
+      if (j == wj) ev = exv[j];
+    const float w = __uint_as_float(__builtin_amdgcn_readlane((int)__float_as_uint(ev), wl)) / s;
+    t += w;
+    if (lane == k) {
+      my_id = win;
+      my_w = w;
+    }
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if (lane + 64 * j == win) key[j] = 0u;
   }
-  if (renorm) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    float t = 0.f;
-    for (int k = 0; k < K; ++k) t += slot[k];
-    if (lane < K) w_out[lane] = slot[lane] / t;
+  if (lane < K) {
+    ids_out[lane] = my_id;
+    w_out[lane] = renorm ? my_w / t : my_w;
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // `scratch`: kMaxExperts + kMaxTopK floats of LDS private to the calling wave.
