@@ -33,7 +33,8 @@
  *     size must be positive, K outside [1, min(E, 64)], E outside
  *     [1, 256], ep not dividing E, a workspace smaller than required, or
  *     shapes the kernels do not cover (bf16: H and I multiples of 64;
- *     fp32: H and I multiples of 4); MOE_EUNSUPPORTED for a dtype value
+ *     fp32: H and I multiples of 4; H and I at most 2^20);
+ *     MOE_EUNSUPPORTED for a dtype value
  *     that is not built. Nothing is enqueued when a call returns an error.
  *   - MOE_EHIP reports a kernel launch failure (hipGetLastError after each
  *     launch); the stream may then hold part of the call's work.

@@ -21,8 +21,13 @@ size_t elt_size(moe_dtype dt) { return dt == MOE_BF16 ? 2 : 4; }
 bool dtype_ok(moe_dtype dt) { return dt == MOE_BF16 || dt == MOE_F32; }
 
 // Shape rules the kernels rely on: bf16 GEMMs and the router advance K in
-// steps of 64; every row copy moves 16-byte vectors.
-bool hidden_ok(int H, moe_dtype dt) { return H > 0 && (dt == MOE_BF16 ? H % 64 == 0 : H % 4 == 0); }
+// steps of 64; every row copy moves 16-byte vectors. The GEMM epilogues
+// address a tile's outputs with 32-bit byte offsets (at most 256 rows of up
+// to 2 * kMaxHidden bf16 values), so hidden sizes are bounded.
+constexpr int kMaxHidden = 1 << 20;
+bool hidden_ok(int H, moe_dtype dt) {
+  return H > 0 && H <= kMaxHidden && (dt == MOE_BF16 ? H % 64 == 0 : H % 4 == 0);
+}
 
 bool experts_ok(int E, int K) { return E >= 1 && E <= kMaxExperts && K >= 1 && K <= E && K <= kMaxTopK; }
 

@@ -55,7 +55,11 @@ def _routing(n, E, K, seed):
 # n, H, I, E, K: the 32-row tile configuration (rows / E <= 64) and the 256-row
 # one, each with I and H that leave a masked column tail (I % 128 = 64 for
 # GEMM1, H % 256 = 192 for GEMM2).
-CASES = [(100, 192, 192, 16, 4), (700, 448, 192, 8, 2), (1300, 192, 320, 12, 3)]
+# The last two have more tiles than an MI355X has compute units (256), so
+# workgroups go on to further tiles and their first k-steps wait behind the
+# previous tile's counted stores.
+CASES = [(100, 192, 192, 16, 4), (700, 448, 192, 8, 2), (1300, 192, 320, 12, 3),
+         (512, 704, 320, 64, 8), (2048, 704, 320, 64, 8)]
 
 
 @pytest.mark.parametrize("n,H,I,E,K", CASES)

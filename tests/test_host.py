@@ -122,6 +122,10 @@ def test_forward_rejects_bad_arguments(lib):
     bad = list(args)
     bad[9] = 0  # K = 0
     assert lib.moe_forward(*bad) == EINVAL
+    for i in (6, 7):  # H, then I, above 2^20 (the GEMM epilogues' 32-bit tile offsets)
+        bad = list(args)
+        bad[i] = (1 << 20) + 64
+        assert lib.moe_forward(*bad) == EINVAL
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
