@@ -396,6 +396,8 @@ def _bench_ep_share(args):
                          eps.unpermute(b, s0)), [s0])
     t_c = timed(lambda: eps.run_serial(a, b, W13, W2, ep.E_local, s0), [s0])
     t_d = timed(lambda: eps.run_two_streams(a, b, W13, W2, ep.E_local, compute, comm), [compute, comm])
+    # The same work with the permute and unpermute folded into the GEMMs (one stream).
+    t_f = timed(lambda: eps.run_fused(a, b, W13, W2, ep.E_local, s0), [s0])
     # CU-masked split ([Fusion] §6.4's T_total(S_comm) = max(T_compute(S - S_comm), T_comm(S_comm)) + T_sync):
     # the permute/unpermute stream gets S_comm compute units, the GEMM stream the rest.
     split = []
@@ -451,6 +453,10 @@ def _bench_ep_share(args):
                     "gemm_TFLOP/s_alone": round(flops / (t_a * 1e-3) / 1e12, 1),
                     "gemm_TFLOP/s_in_overlap": round(flops / (t_d * 1e-3) / 1e12, 1),
                     "cu_split": split},
+        "fused_schedule": {"T_F_ms": round(t_f, 4), "rows/s": round(rows / (t_f * 1e-3), 1),
+                           "speedup_over_two_streams": round(t_d / t_f, 4),
+                           "what": "metadata-only permute, GEMM1 reading rows through perm, GEMM2 storing rows at "
+                                   "their arrival positions (unit weights); one stream"},
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(dev),
     }

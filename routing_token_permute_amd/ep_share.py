@@ -15,6 +15,14 @@ and unpermute kernels stand on the second stream.
 This module only orders library calls on streams; every step runs in the
 HIP kernels of libmoe.so (moe_permute with K = 1, moe_grouped_swiglu,
 moe_unpermute_combine with unit weights).
+
+The fused schedule does the same work with no expert-major copies: the
+permute writes only the metadata, the first GEMM reads the received rows
+through perm (the `x[T_b]` gather of "MoE 分布式推理基础（基于 vLLM）" §2.3),
+and the second GEMM stores each output row straight at its arrival position
+(the weighted scatter epilogue with unit weights, as in the second fused MoE
+layer of "大模型系统中的通算融合" §4.2.5). A weight of exactly 1 leaves the
+fp32 accumulator unchanged, so the result is bitwise the serial schedule's.
 """
 
 from __future__ import annotations
@@ -39,6 +47,9 @@ class MicroBatch:
     out: Optional[torch.Tensor] = None
     ws_perm: Optional[torch.Tensor] = None
     ws_gemm: Optional[torch.Tensor] = None
+    h: Optional[torch.Tensor] = None  # fused schedule: SwiGLU activations, expert-major
+    ones: Optional[torch.Tensor] = None  # fused schedule: unit weights (R, 1) fp32
+    out_fused: Optional[torch.Tensor] = None  # fused schedule: outputs, arrival order
 
 
 def prepare(mb: MicroBatch, E_local: int, I: int) -> MicroBatch:  # noqa: E741
@@ -59,6 +70,9 @@ def prepare(mb: MicroBatch, E_local: int, I: int) -> MicroBatch:  # noqa: E741
     mb.ws_perm = torch.empty(lib.moe_permute_workspace_size(R, E_local, 1), dtype=torch.uint8, device=dev)
     dt = _lib._dt(mb.x)
     mb.ws_gemm = torch.empty(lib.moe_grouped_swiglu_workspace_size(R, I, dt), dtype=torch.uint8, device=dev)
+    mb.h = torch.empty((R, I), dtype=mb.x.dtype, device=dev)
+    mb.ones = torch.ones((R, 1), dtype=torch.float32, device=dev)
+    mb.out_fused = torch.empty((R, H), dtype=mb.x.dtype, device=dev)
     return mb
 
 
@@ -74,6 +88,28 @@ def experts(mb: MicroBatch, W13: torch.Tensor, W2: torch.Tensor, stream) -> None
 def unpermute(mb: MicroBatch, stream) -> None:
     R = mb.x.shape[0]
     _lib.moe_unpermute_combine(mb.Y_perm, mb.meta["inv"], None, R, 1, y=mb.out, stream=stream)
+
+
+def permute_meta(mb: MicroBatch, E_local: int, stream) -> None:
+    """counts, offsets, perm and inv only (no expert-major copy of the rows)."""
+    meta = {k: v for k, v in mb.meta.items() if k != "x_perm"}
+    _lib.moe_permute(mb.eid, None, E_local, out=meta, ws=mb.ws_perm, stream=stream)
+
+
+def experts_fused(mb: MicroBatch, W13: torch.Tensor, W2: torch.Tensor, stream) -> None:
+    """GEMM1 + SwiGLU reading the received rows through perm, then GEMM2 storing
+    each row at its arrival position."""
+    perm, offsets = mb.meta["perm"], mb.meta["offsets"]
+    _lib.moe_expert_w13_swiglu_gather(mb.x, perm, 1, offsets, W13, h=mb.h, stream=stream)
+    _lib.moe_expert_w2_scatter(mb.h, offsets, perm, mb.ones, W2, Y_tok=mb.out_fused, stream=stream)
+
+
+def run_fused(a: MicroBatch, b: MicroBatch, W13, W2, E_local: int, stream) -> None:
+    """Both micro-batches on one stream with the permute and unpermute folded
+    into the GEMMs; outputs in out_fused."""
+    for mb in (a, b):
+        permute_meta(mb, E_local, stream)
+        experts_fused(mb, W13, W2, stream)
 
 
 def run_serial(a: MicroBatch, b: MicroBatch, W13, W2, E_local: int, stream) -> None:

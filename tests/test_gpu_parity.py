@@ -101,7 +101,7 @@ def test_route(dev, n, H, E, K, dtype, renorm, bias):
     np.testing.assert_allclose(wts.cpu().numpy()[safe], w_ref[safe], atol=1e-6, rtol=0)
 
 
-@pytest.mark.parametrize("n,E,K,renorm", [(200, 64, 8, False), (200, 64, 8, True), (90, 256, 64, True), (40, 5, 5, False), (70, 130, 9, False), (7, 1, 1, True)])
+@pytest.mark.parametrize("n,E,K,renorm", [(200, 64, 8, False), (200, 64, 8, True), (90, 256, 64, True), (40, 5, 5, False), (70, 130, 9, False), (7, 1, 1, True), (150, 100, 6, True), (60, 128, 17, False)])
 def test_topk_from_logits_bit_exact(dev, n, E, K, renorm):
     L = _tie_logits(n, E, seed=E + K)
     logits = torch.from_numpy(L).to(dev)
@@ -482,6 +482,28 @@ def test_ep_share_two_streams_match_serial(dev):
         for s_mb, t_mb in zip(serial, two):
             assert torch.equal(s_mb.out.view(torch.int16), t_mb.out.view(torch.int16))
             assert torch.equal(s_mb.meta["perm"], t_mb.meta["perm"])
+
+
+def test_ep_share_fused_matches_serial(dev):
+    """The fused schedule (metadata-only permute, gather-fused GEMM1, GEMM2 storing rows at their arrival
+    positions with unit weights) gives bitwise the serial schedule's outputs, twice in a row."""
+    from routing_token_permute_amd import ep_share as eps
+
+    ep = make_config("ep_share_bf16")
+    t13 = dev_tensor(ep.bits("W13"), "bf16", dev)
+    t2 = dev_tensor(ep.bits("W2"), "bf16", dev)
+    mbs = [eps.prepare(eps.MicroBatch(dev_tensor(m.x_bits(), "bf16", dev),
+                                      torch.from_numpy(m.eid.reshape(-1, 1)).to(dev)), ep.E_local, ep.I)
+           for m in ep.micro_batches]
+    s0 = torch.cuda.current_stream(dev)
+    eps.run_serial(mbs[0], mbs[1], t13, t2, ep.E_local, s0)
+    for _ in range(2):
+        for mb in mbs:
+            mb.out_fused.zero_()
+        eps.run_fused(mbs[0], mbs[1], t13, t2, ep.E_local, s0)
+        torch.cuda.synchronize()
+        for mb in mbs:
+            assert torch.equal(mb.out.view(torch.int16), mb.out_fused.view(torch.int16))
 
 
 def test_ep_share_cu_masked_streams_match_serial(dev):
