@@ -674,9 +674,9 @@ def _bench_fp8(args):
     hit = int((meta["counts"].cpu().numpy() > 0).sum())
     R = args.stage_reps
     st = {
-        "gemm1_swiglu_fp8": _time_region(
+        "gemm1_swiglu_fp8": _time_region_graph(
             lambda: moe.moe_expert_w13_swiglu_gather_fp8(x, meta["perm"], K, meta["offsets"], q13, s13, h=h), R, torch),
-        "gemm2_fp8": _time_region(lambda: moe.moe_expert_w2_fp8(h, meta["offsets"], q2, s2, Y_perm=Yp), R, torch),
+        "gemm2_fp8": _time_region_graph(lambda: moe.moe_expert_w2_fp8(h, meta["offsets"], q2, s2, Y_perm=Yp), R, torch),
     }
     nk = n * K
     bytes_ = {  # algorithmic: activations once, FP8 codes and scales of the hit experts once, outputs once
