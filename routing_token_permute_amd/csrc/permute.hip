@@ -91,6 +91,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_place_kernel(const int32
   __shared__ int scan[kMaxExperts];
   __shared__ int offs[kMaxExperts + 1];
   __shared__ int next[kWaves][kMaxExperts];  // next free row per (wave, expert)
+  __shared__ int part_before[kPermThreads], part_tot[kPermThreads];  // [g * E + e]
+  __shared__ int wave_tot[kWaves];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.x;
@@ -118,30 +120,52 @@ __global__ __launch_bounds__(kPermThreads) void permute_place_kernel(const int32
     }
   }
   __syncthreads();
-  // Per-expert totals and the pairs of each expert in earlier blocks (thread e
-  // owns expert e).
-  int before = 0, tot = 0;
-  if (tid < E) {
-    for (int b0 = 0; b0 < nblk; b0 += 16) {
-      int c[16];
+  // Per-expert totals and the pairs of each expert in earlier blocks. The G =
+  // kPermThreads / E threads of expert e split the block histograms (thread
+  // (g, e) reads blocks g, g + G, ...), so their loads are in flight together;
+  // the partial sums meet in LDS.
+  const int G = kPermThreads / E;  // >= 1: E <= kMaxExperts = kPermThreads
+  {
+    const int e = tid % E, g = tid / E;
+    int pb = 0, pt = 0;
+    if (g < G) {
+      for (int b0 = g; b0 < nblk; b0 += 16 * G) {
+        int c[16];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) c[q] = (b0 + q < nblk) ? block_counts[(size_t)(b0 + q) * E + tid] : 0;
+        for (int q = 0; q < 16; ++q) {
+          const int bb = b0 + q * G;
+          c[q] = (bb < nblk) ? block_counts[(size_t)bb * E + e] : 0;
+        }
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        before += (b0 + q < b) ? c[q] : 0;
-        tot += c[q];
+        for (int q = 0; q < 16; ++q) {
+          pb += (b0 + q * G < b) ? c[q] : 0;
+          pt += c[q];
+        }
       }
+      part_before[g * E + e] = pb;
+      part_tot[g * E + e] = pt;
     }
   }
-  if (tid < kMaxExperts) scan[tid] = (tid < E) ? tot : 0;
   __syncthreads();
-  for (int d = 1; d < kMaxExperts; d <<= 1) {  // inclusive scan over the experts
-    int v = 0;
-    if (tid < kMaxExperts && tid >= d) v = scan[tid - d];
-    __syncthreads();
-    if (tid < kMaxExperts) scan[tid] += v;
-    __syncthreads();
+  int before = 0, tot = 0;
+  if (tid < E) {
+    for (int g = 0; g < G; ++g) {
+      before += part_before[g * E + tid];
+      tot += part_tot[g * E + tid];
+    }
   }
+  // Inclusive scan of the totals over the experts: a shuffle scan within each
+  // wave's 64 experts, then the totals of the lower waves.
+  int incl = (tid < E) ? tot : 0;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) incl += wave_tot[w];
+  if (tid < kMaxExperts) scan[tid] = incl;
   if (tid < E) {
     const int excl = scan[tid] - tot;
     offs[tid] = excl;
