@@ -26,8 +26,10 @@
 //   * GEMM1 tiles pair 128 gate columns j with the 128 up columns I + j, so a
 //     lane holds gate and up of the same output in registers and the SwiGLU
 //     epilogue (fp32, then bf16 round-to-nearest-even) needs no extra pass.
-//     Outputs are written straight from registers as 16-byte pieces while
-//     the next tile's first k-steps are already in flight.
+//     Outputs are written straight from registers as 16-byte buffer stores
+//     while the next tile's first k-steps are already in flight; every wave
+//     issues the same number of them, so the waits of those k-steps can let
+//     the stores drain behind them.
 //
 // fp32 path: one thread per output element, fp32 FMA over K. It serves the
 // small fp32 workloads, where launch latency dominates.
