@@ -18,8 +18,8 @@ constexpr int kMaxStages = 5;
 
 // Stage geometry for a BM-row tile advancing BK (32 or 64) along K: A is
 // BM x BK, B is BK x 256. As many stages as fit in 160 KB of LDS, at most
-// kMaxStages (all but one stay in flight while one is multiplied).
-template <int BM, int BK>
+// CAP (all but one stay in flight while one is multiplied).
+template <int BM, int BK, int CAP = kMaxStages>
 struct TileCfg {
   static_assert(BK == 32 || BK == 64, "k-step");
   static constexpr int A_ROW = BK * 2;  // bytes per staged row of A
@@ -27,7 +27,7 @@ struct TileCfg {
   static constexpr int B_BYTES = BK * B_ROW;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int FIT = (160 * 1024) / STAGE;
-  static constexpr int NSTAGE = FIT > kMaxStages ? kMaxStages : FIT;
+  static constexpr int NSTAGE = FIT > CAP ? CAP : FIT;
   static constexpr int LDS_BYTES = NSTAGE * STAGE;
   static constexpr int REGIONS = STAGE / 1024;  // 1 KB DMA regions per stage
   static constexpr int A_ROWS_PER_REGION = 1024 / A_ROW;

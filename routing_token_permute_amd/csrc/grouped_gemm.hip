@@ -73,7 +73,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
                                                                     long long b_expert_stride, int Nout, int up_col,
                                                                     uint16_t* __restrict__ C, int ldc, int NB,
                                                                     int n_slots, uint16_t* __restrict__ gu_out) {
-  using Cfg = TileCfg<BM, BK>;
+  // GEMM2 (256-row tiles, K = I) runs on a 3-stage ring: measured a little
+  // faster than five stages, whose deeper copy lead buys nothing there.
+  using Cfg = TileCfg<BM, BK, (!GATED && BM == 256) ? 3 : kMaxStages>;
   constexpr int A_BYTES = Cfg::A_BYTES, STAGE = Cfg::STAGE, NSTAGE = Cfg::NSTAGE, A_ROW = Cfg::A_ROW;
   constexpr int KS = BK / 32;              // 32-deep MFMA steps per stage
   constexpr int NW = WM * WN;              // waves
