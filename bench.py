@@ -43,6 +43,9 @@ def _parse():
                    choices=["olmoe_bf16", "olmoe_skewed_bf16", "decode_bf16", "ep_share_bf16", "olmoe_train_bf16",
                             "decode_fp8", "olmoe_fp8"])
     p.add_argument("--stage-reps", type=int, default=20)
+    p.add_argument("--settle-ms", type=float, default=300.0,
+                   help="after the warmup steps, keep running untimed steps until this much wall time has passed "
+                        "since the first (the device's clocks ramp up under load)")
     p.add_argument("--comm-cus", type=int, nargs="*", default=[8, 16, 32, 64],
                    help="ep_share_bf16: compute units given to the permute/unpermute stream in the CU-masked runs")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -133,6 +136,20 @@ def _copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}))
+
+
+def _warm(fn, n, torch, settle_ms):
+    """n untimed calls of fn(), then more until settle_ms of wall time have passed
+    since the first. Under load the device's clocks take tens of milliseconds to
+    settle, and calls in that window run several percent slower."""
+    t0 = time.perf_counter()
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
+    while (time.perf_counter() - t0) * 1e3 < settle_ms:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
 
 
 def _time_region(fn, reps, torch):
@@ -246,9 +263,7 @@ def main():
     def step():
         moe.moe_forward(x, Wg, W13, W2, K, w.renorm, bias=bias, y=y, ws=ws)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    _warm(step, args.warmup, torch, args.settle_ms)
     t0 = time.perf_counter()
     ms_events = _time_region(step, args.steps, torch)
     wall = time.perf_counter() - t0
@@ -356,6 +371,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(ms_per_step, 5),
         "step_spread": step_spread,
         "higher_is_better": True,
@@ -407,9 +423,7 @@ def _bench_ep_share(args):
 
     def timed(fn, streams):
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for _ in range(args.warmup):
-            fn()
-        torch.cuda.synchronize()
+        _warm(fn, args.warmup, torch, args.settle_ms)
         first = streams[0]
         start.record(first)
         for st in streams[1:]:
@@ -471,6 +485,7 @@ def _bench_ep_share(args):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(t_d, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -529,9 +544,7 @@ def _bench_train(args):
         fwd()
         bwd()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    _warm(step, args.warmup, torch, args.settle_ms)
     t0 = time.perf_counter()
     ms_step = _time_region(step, args.steps, torch)
     wall = time.perf_counter() - t0
@@ -604,6 +617,7 @@ def _bench_train(args):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(ms_step, 5),
         "ms_forward_train": round(ms_fwd, 5),
         "ms_backward": round(ms_bwd, 5),
@@ -658,9 +672,7 @@ def _bench_fp8(args):
     def step_bf16():
         moe.moe_forward(x, Wg, W13, W2, K, w.renorm, y=y, ws=ws)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    _warm(step, args.warmup, torch, args.settle_ms)
     t0 = time.perf_counter()
     ms = _time_region(step, args.steps, torch)
     wall = time.perf_counter() - t0
@@ -723,6 +735,7 @@ def _bench_fp8(args):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(ms, 5),
         "step_spread": spread,
         "ms_per_step_bf16_weights": round(ms_bf16, 5),
