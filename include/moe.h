@@ -36,10 +36,19 @@
  *     fp32: H and I multiples of 4; H and I at most 2^20);
  *     MOE_EUNSUPPORTED for a dtype value
  *     that is not built. Nothing is enqueued when a call returns an error.
+ *   - Alignment: every row matrix (x, x_perm, h, gate_up, Y_perm, y and
+ *     their gradients), every weight array (W_gate, W13, W2, FP8 codes and
+ *     scales), the fp32 router-gradient buffers, the `add` addend and every
+ *     workspace must be 16-byte aligned (the kernels move them with 16-byte
+ *     vector loads, LDS DMA and buffer stores); the per-pair and per-expert
+ *     int32/fp32 arrays (topk_ids, topk_w, logits, bias, counts, offsets,
+ *     splits, perm, inv, dw, dlogits, dbias) 4-byte aligned. A misaligned
+ *     pointer gives MOE_EINVAL before anything is enqueued.
  *   - MOE_EHIP reports a kernel launch failure (hipGetLastError after each
  *     launch); the stream may then hold part of the call's work.
  *   - n == 0 (or rows == 0) is valid: outputs that have one entry per expert
- *     or rank are still written (zeros), nothing else is touched.
+ *     or rank are still written (zeros), nothing else is touched; the
+ *     layer calls (moe_forward, moe_forward_fp8) then need no workspace.
  *   - Calls on different streams may run concurrently when their outputs
  *     and workspaces do not overlap.
  *   - Results are deterministic: the same inputs give bitwise-identical
@@ -242,6 +251,10 @@ moe_status moe_unpermute_combine(const void* Y_perm, const int32_t* inv, const f
  *   ws           workspace of at least moe_forward_workspace_size(...) bytes.
  * ------------------------------------------------------------------------- */
 size_t moe_forward_workspace_size(int n, int H, int I, int E, int K, moe_dtype dt);
+
+/* The same size under the name of the layer's planned interface
+ * (workspace of moe_forward). */
+size_t moe_workspace_size(int n, int H, int I, int E, int K, moe_dtype dt);
 moe_status moe_forward(const void* x, const void* W_gate, const float* bias, const void* W13, const void* W2,
                        int n, int H, int I, int E, int K, int renorm, moe_dtype dt, void* y, float* logits_out,
                        int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
@@ -402,10 +415,15 @@ moe_status moe_route_backward(const void* x, const void* W_gate, const float* lo
  * device, default priority, created on the first call and kept for the
  * process), forked from and joined back into `stream` with events, so that
  * they overlap the main chain; when that stream cannot be created everything
- * runs on `stream`. All work is ordered after earlier work on `stream`, and
- * later work on `stream` sees every output. The call can be captured in a HIP
- * graph (the fork and join are events), except the first call on a device,
- * which creates the second stream.
+ * runs on `stream`. The second stream is shared by all calls on the device
+ * (their enqueue sequences are serialised by a mutex, so backward calls on
+ * different streams share its queue); while it belongs to a graph capture
+ * other than `stream`'s (another thread's capture that forked into it and has
+ * not ended), the call runs every branch on `stream` instead, in the same
+ * order. All work is ordered after earlier work on `stream`, and later work
+ * on `stream` sees every output. The call can be captured in a HIP graph (the
+ * fork and join are events), except the first call on a device, which
+ * creates the second stream.
  *   dy (n, H) dtype; x, W_gate, W13, W2 as given to moe_forward_train;
  *   logits ... Y_perm: the buffers moe_forward_train saved;
  *   dx (n, H) dtype out; dW_gate (H, E) fp32 out; dbias (E) fp32 out or NULL;

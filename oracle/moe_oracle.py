@@ -487,8 +487,12 @@ def router_backward(routing_logits, e_top, dw, K: int, renorm: bool, x=None, W_g
     return out
 
 
-def backward(x, W_gate, W13, W2, K: int, renorm: bool, dy, bias=None, fp64_routing: bool = False):
+def backward(x, W_gate, W13, W2, K: int, renorm: bool, dy, bias=None, fp64_routing: bool = False,
+             routing_logits_f32=None):
     """Gradients of the layer's y = forward(...)["y"] for an upstream dy (n, H).
+
+    `routing_logits_f32`, when given, is the routing input of steps 1-3 (as in
+    forward); the router's own gradients are then taken at those logits.
 
     Steps, in the reverse order of Algorithm 2:
       1. combine backward: dY_perm, dw (combine_backward);
@@ -503,7 +507,8 @@ def backward(x, W_gate, W13, W2, K: int, renorm: bool, dy, bias=None, fp64_routi
     """
     x = np.asarray(x)
     n, H = x.shape
-    f = forward(x, W_gate, W13, W2, K, renorm, bias=bias, keep_permuted=True, fp64_routing=fp64_routing)
+    f = forward(x, W_gate, W13, W2, K, renorm, bias=bias, keep_permuted=True, fp64_routing=fp64_routing,
+                routing_logits_f32=routing_logits_f32)
     perm, inv, offsets = f["perm"], f["inv"], f["offsets"]
     x_perm = np.asarray(x, dtype=np.float64)[perm // K]
     gate_up = gate_up_preactivations(x_perm, offsets, W13)

@@ -10,6 +10,8 @@ kernels. If the library is missing or cannot be loaded, every call raises.
 from __future__ import annotations
 
 import ctypes
+import functools
+import inspect
 import os
 from typing import Optional
 
@@ -41,6 +43,7 @@ SIGNATURES = {
     "moe_sum_slots": (_I, [_VP, _I, _I, _I, _I, _VP, _VP]),
     "moe_unpermute_combine": (_I, [_VP, _VP, _VP, _I, _I, _I, _I, _VP, _VP]),
     "moe_forward_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "moe_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "moe_forward": (
         _I,
         [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
@@ -125,6 +128,24 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _on_stream(fn):
+    """Run a binding with `stream` (when given) as torch's current stream, so
+    that every output and workspace it allocates belongs to that stream's pool:
+    torch's caching allocator then never hands such a block to work on another
+    stream while the library's kernels may still use it."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        s = sig.bind(*args, **kwargs).arguments.get("stream")
+        if s is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.stream(s):
+            return fn(*args, **kwargs)
+
+    return wrapper
+
+
 def _stream(device: torch.device, stream: Optional[torch.cuda.Stream]):
     s = stream if stream is not None else torch.cuda.current_stream(device)
     return ctypes.c_void_p(s.cuda_stream)
@@ -160,6 +181,7 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
 # ---------------------------------------------------------------------------
 
 
+@_on_stream
 def moe_route(x, W_gate, bias, K: int, renorm: bool, logits=None, topk_ids=None, topk_w=None, stream=None, E=None):
     """Router GEMM + softmax + top-K. With x None, `logits` (n, E) fp32 is the input.
 
@@ -197,6 +219,7 @@ def moe_route(x, W_gate, bias, K: int, renorm: bool, logits=None, topk_ids=None,
     return logits, topk_ids, topk_w
 
 
+@_on_stream
 def moe_permute(topk_ids, x, E: int, ep: int = 1, out=None, ws=None, stream=None):
     """Counts, offsets, splits, perm, inv and (when x is given) x_perm.
 
@@ -233,6 +256,7 @@ def moe_permute(topk_ids, x, E: int, ep: int = 1, out=None, ws=None, stream=None
     return out
 
 
+@_on_stream
 def moe_grouped_swiglu(x_perm, offsets, W13, W2, Y_perm=None, ws=None, stream=None):
     """Per-expert SwiGLU FFN on expert-major rows. Returns Y_perm (rows, H)."""
     lib = load_library()
@@ -258,6 +282,7 @@ def moe_grouped_swiglu(x_perm, offsets, W13, W2, Y_perm=None, ws=None, stream=No
     return Y_perm
 
 
+@_on_stream
 def moe_expert_w13_swiglu(x_perm, offsets, W13, h=None, stream=None):
     """Algorithm 2 step 8 on expert-major rows: h = SiLU(X W13[:, :I]) * (X W13[:, I:])."""
     lib = load_library()
@@ -277,6 +302,7 @@ def moe_expert_w13_swiglu(x_perm, offsets, W13, h=None, stream=None):
     return h
 
 
+@_on_stream
 def moe_expert_w13_swiglu_gather(x, perm, K, offsets, W13, h=None, stream=None):
     """Algorithm 2 steps 7-8 fused: h rows for pairs perm[r], reading token rows x[perm[r] // K]."""
     lib = load_library()
@@ -297,6 +323,7 @@ def moe_expert_w13_swiglu_gather(x, perm, K, offsets, W13, h=None, stream=None):
     return h
 
 
+@_on_stream
 def moe_expert_w2(h, offsets, W2, Y_perm=None, stream=None):
     """Algorithm 2 step 9 on expert-major rows: Y_perm = h W2[e] per segment."""
     lib = load_library()
@@ -313,6 +340,7 @@ def moe_expert_w2(h, offsets, W2, Y_perm=None, stream=None):
     return Y_perm
 
 
+@_on_stream
 def moe_expert_w2_scatter(h, offsets, perm, topk_w, W2, Y_tok=None, stream=None):
     """GEMM2 with the weight and un-permutation in its epilogue:
     Y_tok[perm[p]] = topk_w.flat[perm[p]] * (h[p] W2[e]). topk_w is (n, K) fp32."""
@@ -334,6 +362,7 @@ def moe_expert_w2_scatter(h, offsets, perm, topk_w, W2, Y_tok=None, stream=None)
     return Y_tok
 
 
+@_on_stream
 def moe_sum_slots(Y_tok, n: int, K: int, y=None, stream=None):
     """y[i] = sum_k Y_tok[i*K+k] in slot order (fp32 accumulation)."""
     lib = load_library()
@@ -347,6 +376,7 @@ def moe_sum_slots(Y_tok, n: int, K: int, y=None, stream=None):
     return y
 
 
+@_on_stream
 def moe_unpermute_combine(Y_perm, inv, topk_w, n: int, K: int, y=None, stream=None):
     """y[i] = sum_k w[i,k] Y_perm[inv[i*K+k]] (unit weights when topk_w is None)."""
     lib = load_library()
@@ -365,10 +395,12 @@ def moe_unpermute_combine(Y_perm, inv, topk_w, n: int, K: int, y=None, stream=No
     return y
 
 
+@_on_stream
 def moe_forward_workspace_size(n, H, I, E, K, dtype) -> int:  # noqa: E741
     return int(load_library().moe_forward_workspace_size(n, H, I, E, K, _dt(torch.empty(0, dtype=dtype))))
 
 
+@_on_stream
 def moe_forward(x, W_gate, W13, W2, K: int, renorm: bool, bias=None, y=None, ws=None, routing_out=False, stream=None):
     """Whole layer. Returns y, or (y, logits, topk_ids, topk_w, counts) with routing_out."""
     lib = load_library()
@@ -407,6 +439,7 @@ def moe_forward(x, W_gate, W13, W2, K: int, renorm: bool, bias=None, y=None, ws=
 # ---------------------------------------------------------------------------
 
 
+@_on_stream
 def moe_expert_w13_swiglu_gather_train(x, perm, K, offsets, W13, h=None, gate_up=None, stream=None):
     """moe_expert_w13_swiglu_gather that also writes the pre-activations [gate | up].
 
@@ -432,6 +465,7 @@ def moe_expert_w13_swiglu_gather_train(x, perm, K, offsets, W13, h=None, gate_up
     return h, gate_up
 
 
+@_on_stream
 def moe_forward_train(x, W_gate, W13, W2, K: int, renorm: bool, bias=None, saved=None, y=None, ws=None, stream=None):
     """The layer's forward keeping what moe_backward reads.
 
@@ -469,6 +503,7 @@ def moe_forward_train(x, W_gate, W13, W2, K: int, renorm: bool, bias=None, saved
     return y, saved
 
 
+@_on_stream
 def moe_combine_backward(dy, Y_perm, inv, topk_w, n: int, K: int, dY_perm=None, dw=None, stream=None):
     """dY_perm[inv[iK+k]] = w[i,k] dy[i] and dw[i,k] = <dy[i], Y_perm[inv[iK+k]]>. Returns (dY_perm, dw)."""
     lib = load_library()
@@ -488,6 +523,7 @@ def moe_combine_backward(dy, Y_perm, inv, topk_w, n: int, K: int, dY_perm=None, 
     return dY_perm, dw
 
 
+@_on_stream
 def moe_expert_w2_backward(dY_perm, offsets, W2, gate_up, dgate_up=None, stream=None):
     """dgate_up = SwiGLU'(gate_up) applied to dY_perm W2[e]^T per expert segment."""
     lib = load_library()
@@ -506,6 +542,7 @@ def moe_expert_w2_backward(dY_perm, offsets, W2, gate_up, dgate_up=None, stream=
     return dgate_up
 
 
+@_on_stream
 def moe_expert_w13_backward(dgate_up, offsets, W13, dX_perm=None, stream=None):
     """dX_perm = dgate_up W13[e]^T per expert segment."""
     lib = load_library()
@@ -524,6 +561,7 @@ def moe_expert_w13_backward(dgate_up, offsets, W13, dX_perm=None, stream=None):
     return dX_perm
 
 
+@_on_stream
 def moe_expert_weight_grad(a, b, offsets, dW=None, stream=None):
     """dW[e] = a[seg e]^T b[seg e] over each expert's rows. Returns dW (E, M, N)."""
     lib = load_library()
@@ -542,6 +580,7 @@ def moe_expert_weight_grad(a, b, offsets, dW=None, stream=None):
     return dW
 
 
+@_on_stream
 def moe_expert_weight_grad_gather(x, perm, K: int, b, offsets, dW=None, stream=None):
     """dW[e] = sum over rows r of expert e of x[perm[r] // K]^T b[r]. Returns dW (E, M, N)."""
     lib = load_library()
@@ -561,6 +600,7 @@ def moe_expert_weight_grad_gather(x, perm, K: int, b, offsets, dW=None, stream=N
     return dW
 
 
+@_on_stream
 def moe_dispatch_backward(dX_perm, inv, n: int, K: int, add=None, dx=None, stream=None):
     """dx[i] = add[i] + sum_k dX_perm[inv[iK+k]] (add: (n, H) fp32 or None)."""
     lib = load_library()
@@ -578,6 +618,7 @@ def moe_dispatch_backward(dX_perm, inv, n: int, K: int, add=None, dx=None, strea
     return dx
 
 
+@_on_stream
 def moe_route_backward(x, W_gate, logits, topk_ids, topk_w, dw, renorm: bool, want_dx=True, want_weights=True,
                        ws=None, stream=None):
     """Gradient through routing given dw = dL/dtopk_w.
@@ -615,10 +656,12 @@ def moe_route_backward(x, W_gate, logits, topk_ids, topk_w, dw, renorm: bool, wa
     return out
 
 
+@_on_stream
 def moe_backward_workspace_size(n, H, I, E, K, dtype) -> int:  # noqa: E741
     return int(load_library().moe_backward_workspace_size(n, H, I, E, K, _dt(torch.empty(0, dtype=dtype))))
 
 
+@_on_stream
 def moe_backward(dy, x, W_gate, W13, W2, K: int, renorm: bool, saved, grads=None, ws=None, stream=None):
     """The layer's backward from moe_forward_train's saved buffers.
 
@@ -663,6 +706,7 @@ def moe_backward(dy, x, W_gate, W13, W2, K: int, renorm: bool, saved, grads=None
 # ---------------------------------------------------------------------------
 
 
+@_on_stream
 def moe_quantize_fp8(W, codes=None, scales=None, stream=None):
     """FP8 E4M3 codes (E, N, Kd) uint8 and column scales (E, N) fp32 of weights W (E, Kd, N)."""
     lib = load_library()
@@ -678,6 +722,7 @@ def moe_quantize_fp8(W, codes=None, scales=None, stream=None):
     return codes, scales
 
 
+@_on_stream
 def moe_expert_w13_swiglu_gather_fp8(x, perm, K, offsets, W13q, s13, h=None, stream=None):
     """GEMM1 + SwiGLU with FP8 W13 (codes (E, 2I, H), scales (E, 2I)), rows gathered through perm."""
     lib = load_library()
@@ -698,6 +743,7 @@ def moe_expert_w13_swiglu_gather_fp8(x, perm, K, offsets, W13q, s13, h=None, str
     return h
 
 
+@_on_stream
 def moe_expert_w2_fp8(h, offsets, W2q, s2, Y_perm=None, stream=None):
     """GEMM2 with FP8 W2 (codes (E, H, I), scales (E, H))."""
     lib = load_library()
@@ -716,6 +762,7 @@ def moe_expert_w2_fp8(h, offsets, W2q, s2, Y_perm=None, stream=None):
     return Y_perm
 
 
+@_on_stream
 def moe_forward_fp8(x, W_gate, W13q, s13, W2q, s2, K: int, renorm: bool, bias=None, y=None, ws=None,
                     routing_out=False, stream=None):
     """The layer with FP8 expert weights. Returns y, or (y, logits, topk_ids, topk_w, counts) with routing_out."""

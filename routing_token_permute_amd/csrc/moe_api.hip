@@ -4,6 +4,7 @@
 // grouped_gemm.hip, combine.hip, grouped_gemm_bwd.hip and backward.hip.
 #include <stdint.h>
 
+#include <initializer_list>
 #include <mutex>
 
 #include "moe_internal.hpp"
@@ -32,6 +33,18 @@ bool hidden_ok(int H, moe_dtype dt) {
 bool experts_ok(int E, int K) { return E >= 1 && E <= kMaxExperts && K >= 1 && K <= E && K <= kMaxTopK; }
 
 moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+// Pointer alignment the kernels rely on: row matrices, weights, workspaces
+// and fp32 row buffers are moved with 16-byte vector loads, 16-byte LDS DMA
+// and 16-byte buffer stores; per-pair int32/fp32 arrays with 4-byte accesses.
+// A null pointer passes (optional arguments are checked for presence apart).
+bool aligned(std::initializer_list<const void*> ps, uintptr_t a) {
+  for (const void* p : ps)
+    if (((uintptr_t)p & (a - 1)) != 0) return false;
+  return true;
+}
+bool vec_ok(std::initializer_list<const void*> ps) { return aligned(ps, 16); }
+bool word_ok(std::initializer_list<const void*> ps) { return aligned(ps, 4); }
 
 size_t permute_ws(int n, int E, int K) {
   (void)n;
@@ -147,6 +160,65 @@ AuxStream* aux_stream() {
   return a.ok ? &a : nullptr;
 }
 
+// Argument checks of the layer call (everything
+// but the workspace).
+moe_status check_forward(const void* x, const void* W_gate, const float* bias, const void* W13, const void* W2,
+                         int n, int H, int I, int E, int K, moe_dtype dt, const void* y, const float* logits_out,
+                         const int32_t* topk_ids_out, const float* topk_w_out, const int32_t* counts_out) {
+  if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
+  if (n < 0 || !experts_ok(E, K) || !hidden_ok(H, dt) || !hidden_ok(I, dt)) return MOE_EINVAL;
+  if ((long long)n * K > INT32_MAX) return MOE_EINVAL;
+  if (n > 0 && (x == nullptr || W_gate == nullptr || W13 == nullptr || W2 == nullptr || y == nullptr))
+    return MOE_EINVAL;
+  if (!vec_ok({x, W_gate, W13, W2, y}) || !word_ok({bias, logits_out, topk_ids_out, topk_w_out, counts_out}))
+    return MOE_EINVAL;
+  return MOE_OK;
+}
+
+// The layer's launches over a workspace laid out by forward_layout at `base`
+// (n > 0, arguments checked).
+moe_status forward_enqueue(const void* x, const void* W_gate, const float* bias, const void* W13, const void* W2,
+                           int n, int H, int I, int E, int K, int renorm, moe_dtype dt, void* y, float* logits_out,
+                           int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, char* base,
+                           hipStream_t stream) {
+  const ForwardLayout L = forward_layout(n, H, I, E, K, dt);
+  float* logits = logits_out ? logits_out : (float*)(base + L.logits);
+  int32_t* ids = topk_ids_out ? topk_ids_out : (int32_t*)(base + L.ids);
+  float* w = topk_w_out ? topk_w_out : (float*)(base + L.w);
+  int32_t* counts = counts_out ? counts_out : (int32_t*)(base + L.counts);
+  int32_t* offsets = (int32_t*)(base + L.offsets);
+  int32_t* splits = (int32_t*)(base + L.splits);
+  int32_t* perm = (int32_t*)(base + L.perm);
+  int32_t* inv = (int32_t*)(base + L.inv);
+
+  hipError_t e = launch_route(x, W_gate, bias, n, H, E, K, renorm, dt, logits, ids, w, stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  // Metadata only: GEMM1 gathers the token rows itself through perm.
+  e = launch_permute(ids, nullptr, n, H, E, K, 1, dt, counts, offsets, splits, perm, inv, nullptr,
+                     (int32_t*)(base + L.pscratch), stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  e = launch_w13_swiglu_gather(x, perm, n, K, offsets, W13, E, H, I, dt, base + L.h, stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  // Expert-major GEMM2, then the gathered weighted combine: measured a little
+  // faster here than moe_expert_w2_scatter + moe_sum_slots, whose scattered
+  // row stores cost GEMM2 more than the contiguous sum saves.
+  e = launch_w2(base + L.h, offsets, n * K, W2, E, H, I, dt, base + L.Y_perm, stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  return from_hip(launch_combine(base + L.Y_perm, inv, w, n, H, K, dt, y, stream));
+}
+
+// Capture state of a stream: 0 when it is not being captured, else the id of
+// the capture it belongs to; ~0 when the query fails (treated as busy).
+unsigned long long capture_id(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  unsigned long long id = 0;
+  if (hipStreamGetCaptureInfo(s, &st, &id) != hipSuccess) {
+    (void)hipGetLastError();
+    return ~0ull;
+  }
+  return st == hipStreamCaptureStatusNone ? 0ull : (id == 0 ? ~1ull : id);
+}
+
 }  // namespace
 
 extern "C" {
@@ -176,6 +248,7 @@ moe_status moe_route(const void* x, const void* W_gate, const float* bias, int n
   if (n == 0) return MOE_OK;
   if (logits == nullptr || topk_ids == nullptr || topk_w == nullptr) return MOE_EINVAL;
   if (x != nullptr && (W_gate == nullptr || !hidden_ok(H, dt))) return MOE_EINVAL;
+  if (!vec_ok({x, W_gate}) || !word_ok({bias, logits, topk_ids, topk_w})) return MOE_EINVAL;
   return from_hip(launch_route(x, W_gate, bias, n, H, E, K, renorm, dt, logits, topk_ids, topk_w, stream));
 }
 
@@ -194,6 +267,7 @@ moe_status moe_permute(const int32_t* topk_ids, const void* x, int n, int H, int
   if (n > 0 && (topk_ids == nullptr || perm == nullptr || inv == nullptr)) return MOE_EINVAL;
   if (x != nullptr && (x_perm == nullptr || !hidden_ok(H, dt))) return MOE_EINVAL;
   if (ws == nullptr || ws_bytes < permute_ws(n, E, K)) return MOE_EWORKSPACE;
+  if (!vec_ok({x, x_perm, ws}) || !word_ok({topk_ids, counts, offsets, splits, perm, inv})) return MOE_EINVAL;
   return from_hip(launch_permute(topk_ids, x, n, H, E, K, ep, dt, counts, offsets, splits, perm, inv, x_perm,
                                  (int32_t*)ws, stream));
 }
@@ -212,6 +286,7 @@ moe_status moe_grouped_swiglu(const void* x_perm, const int32_t* offsets, int ro
   if (x_perm == nullptr || offsets == nullptr || W13 == nullptr || W2 == nullptr || Y_perm == nullptr)
     return MOE_EINVAL;
   if (ws == nullptr || ws_bytes < (size_t)rows * I * elt_size(dt)) return MOE_EWORKSPACE;
+  if (!vec_ok({x_perm, W13, W2, Y_perm, ws}) || !word_ok({offsets})) return MOE_EINVAL;
   return from_hip(launch_grouped_swiglu(x_perm, offsets, rows, W13, W2, E, H, I, dt, Y_perm, ws, stream));
 }
 
@@ -220,6 +295,7 @@ static moe_status check_expert_gemm(const void* a, const int32_t* offsets, int r
   if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
   if (rows < 0 || E < 1 || E > kMaxExperts || !hidden_ok(H, dt) || !hidden_ok(I, dt)) return MOE_EINVAL;
   if (rows > 0 && (a == nullptr || offsets == nullptr || w == nullptr || out == nullptr)) return MOE_EINVAL;
+  if (!vec_ok({a, w, out}) || !word_ok({offsets})) return MOE_EINVAL;
   return MOE_OK;
 }
 
@@ -234,7 +310,7 @@ moe_status moe_expert_w13_swiglu_gather(const void* x, const int32_t* perm, int 
                                         const void* W13, int E, int H, int I, moe_dtype dt, void* h,
                                         hipStream_t stream) {
   if (n < 0 || K < 1 || K > kMaxTopK || (long long)n * K > INT32_MAX) return MOE_EINVAL;
-  if (n > 0 && perm == nullptr) return MOE_EINVAL;
+  if ((n > 0 && perm == nullptr) || !word_ok({perm})) return MOE_EINVAL;
   const moe_status st = check_expert_gemm(x, offsets, n * K, W13, E, H, I, dt, h);
   if (st != MOE_OK) return st;
   return from_hip(launch_w13_swiglu_gather(x, perm, n, K, offsets, W13, E, H, I, dt, h, stream));
@@ -253,6 +329,7 @@ moe_status moe_expert_w2_scatter(const void* h, const int32_t* offsets, int rows
   const moe_status st = check_expert_gemm(h, offsets, rows, W2, E, H, I, dt, Y_tok);
   if (st != MOE_OK) return st;
   if (rows > 0 && (perm == nullptr || topk_w == nullptr)) return MOE_EINVAL;
+  if (!word_ok({perm, topk_w})) return MOE_EINVAL;
   return from_hip(launch_w2_scatter(h, offsets, rows, perm, topk_w, W2, E, H, I, dt, Y_tok, stream));
 }
 
@@ -261,7 +338,7 @@ moe_status moe_sum_slots(const void* Y_tok, int n, int H, int K, moe_dtype dt, v
   if (n < 0 || K < 1 || K > kMaxTopK || !hidden_ok(H, dt)) return MOE_EINVAL;
   if ((long long)n * K > INT32_MAX) return MOE_EINVAL;
   if (n == 0) return MOE_OK;
-  if (Y_tok == nullptr || y == nullptr) return MOE_EINVAL;
+  if (Y_tok == nullptr || y == nullptr || !vec_ok({Y_tok, y})) return MOE_EINVAL;
   return from_hip(launch_sum_slots(Y_tok, n, H, K, dt, y, stream));
 }
 
@@ -272,6 +349,7 @@ moe_status moe_unpermute_combine(const void* Y_perm, const int32_t* inv, const f
   if ((long long)n * K > INT32_MAX) return MOE_EINVAL;
   if (n == 0) return MOE_OK;
   if (Y_perm == nullptr || inv == nullptr || y == nullptr) return MOE_EINVAL;
+  if (!vec_ok({Y_perm, y}) || !word_ok({inv, topk_w})) return MOE_EINVAL;
   return from_hip(launch_combine(Y_perm, inv, topk_w, n, H, K, dt, y, stream));
 }
 
@@ -280,42 +358,23 @@ size_t moe_forward_workspace_size(int n, int H, int I, int E, int K, moe_dtype d
   return forward_layout(n, H, I, E, K, dt).total;
 }
 
+size_t moe_workspace_size(int n, int H, int I, int E, int K, moe_dtype dt) {
+  return moe_forward_workspace_size(n, H, I, E, K, dt);
+}
+
 moe_status moe_forward(const void* x, const void* W_gate, const float* bias, const void* W13, const void* W2, int n,
                        int H, int I, int E, int K, int renorm, moe_dtype dt, void* y, float* logits_out,
                        int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
                        hipStream_t stream) {
-  if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
-  if (n < 0 || !experts_ok(E, K) || !hidden_ok(H, dt) || !hidden_ok(I, dt)) return MOE_EINVAL;
-  if ((long long)n * K > INT32_MAX) return MOE_EINVAL;
-  if (n > 0 && (x == nullptr || W_gate == nullptr || W13 == nullptr || W2 == nullptr || y == nullptr))
-    return MOE_EINVAL;
-  const ForwardLayout L = forward_layout(n, H, I, E, K, dt);
-  if (ws == nullptr || ws_bytes < L.total) return MOE_EWORKSPACE;
-  char* base = (char*)ws;
-  float* logits = logits_out ? logits_out : (float*)(base + L.logits);
-  int32_t* ids = topk_ids_out ? topk_ids_out : (int32_t*)(base + L.ids);
-  float* w = topk_w_out ? topk_w_out : (float*)(base + L.w);
-  int32_t* counts = counts_out ? counts_out : (int32_t*)(base + L.counts);
-  int32_t* offsets = (int32_t*)(base + L.offsets);
-  int32_t* splits = (int32_t*)(base + L.splits);
-  int32_t* perm = (int32_t*)(base + L.perm);
-  int32_t* inv = (int32_t*)(base + L.inv);
-
-  hipError_t e = launch_route(x, W_gate, bias, n, H, E, K, renorm, dt, logits, ids, w, stream);
-  if (e != hipSuccess) return MOE_EHIP;
-  // Metadata only: GEMM1 gathers the token rows itself through perm.
-  e = launch_permute(ids, nullptr, n, H, E, K, 1, dt, counts, offsets, splits, perm, inv, nullptr,
-                     (int32_t*)(base + L.pscratch), stream);
-  if (e != hipSuccess) return MOE_EHIP;
-  if (n == 0) return MOE_OK;
-  e = launch_w13_swiglu_gather(x, perm, n, K, offsets, W13, E, H, I, dt, base + L.h, stream);
-  if (e != hipSuccess) return MOE_EHIP;
-  // Expert-major GEMM2, then the gathered weighted combine: measured a little
-  // faster here than moe_expert_w2_scatter + moe_sum_slots, whose scattered
-  // row stores cost GEMM2 more than the contiguous sum saves.
-  e = launch_w2(base + L.h, offsets, n * K, W2, E, H, I, dt, base + L.Y_perm, stream);
-  if (e != hipSuccess) return MOE_EHIP;
-  return from_hip(launch_combine(base + L.Y_perm, inv, w, n, H, K, dt, y, stream));
+  const moe_status st = check_forward(x, W_gate, bias, W13, W2, n, H, I, E, K, dt, y, logits_out, topk_ids_out,
+                                      topk_w_out, counts_out);
+  if (st != MOE_OK) return st;
+  if (!vec_ok({ws})) return MOE_EINVAL;
+  if (n == 0)  // no tokens: nothing to compute; the optional counts are all zero
+    return counts_out ? from_hip(launch_fill_zero(counts_out, (size_t)E * 4, stream)) : MOE_OK;
+  if (ws == nullptr || ws_bytes < forward_layout(n, H, I, E, K, dt).total) return MOE_EWORKSPACE;
+  return forward_enqueue(x, W_gate, bias, W13, W2, n, H, I, E, K, renorm, dt, y, logits_out, topk_ids_out,
+                         topk_w_out, counts_out, (char*)ws, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -327,6 +386,7 @@ moe_status moe_expert_w13_swiglu_gather_train(const void* x, const int32_t* perm
                                               moe_dtype dt, void* h, void* gate_up, hipStream_t stream) {
   if (n < 0 || K < 1 || K > kMaxTopK || (long long)n * K > INT32_MAX) return MOE_EINVAL;
   if (n > 0 && (perm == nullptr || gate_up == nullptr)) return MOE_EINVAL;
+  if (!vec_ok({gate_up}) || !word_ok({perm})) return MOE_EINVAL;
   const moe_status st = check_expert_gemm(x, offsets, n * K, W13, E, H, I, dt, h);
   if (st != MOE_OK) return st;
   return from_hip(launch_w13_swiglu_gather_train(x, perm, n, K, offsets, W13, E, H, I, dt, h, gate_up, stream));
@@ -348,6 +408,9 @@ moe_status moe_forward_train(const void* x, const void* W_gate, const float* bia
   if (n > 0 && (x == nullptr || W_gate == nullptr || W13 == nullptr || W2 == nullptr || y == nullptr ||
                 logits == nullptr || topk_ids == nullptr || topk_w == nullptr || perm == nullptr || inv == nullptr ||
                 gate_up == nullptr || h == nullptr || Y_perm == nullptr))
+    return MOE_EINVAL;
+  if (!vec_ok({x, W_gate, W13, W2, y, gate_up, h, Y_perm, ws}) ||
+      !word_ok({bias, logits, topk_ids, topk_w, offsets, perm, inv}))
     return MOE_EINVAL;
   const TrainLayout L = train_layout(n, E, K);
   if (ws == nullptr || ws_bytes < L.total) return MOE_EWORKSPACE;
@@ -374,6 +437,7 @@ moe_status moe_combine_backward(const void* dy, const void* Y_perm, const int32_
   if (dy == nullptr || Y_perm == nullptr || inv == nullptr || topk_w == nullptr || dY_perm == nullptr ||
       dw == nullptr)
     return MOE_EINVAL;
+  if (!vec_ok({dy, Y_perm, dY_perm}) || !word_ok({inv, topk_w, dw})) return MOE_EINVAL;
   return from_hip(launch_combine_backward(dy, Y_perm, inv, topk_w, n, H, K, dt, dY_perm, dw, stream));
 }
 
@@ -382,7 +446,7 @@ moe_status moe_expert_w2_backward(const void* dY_perm, const int32_t* offsets, i
                                   hipStream_t stream) {
   const moe_status st = check_expert_gemm(dY_perm, offsets, rows, W2, E, H, I, dt, dgate_up);
   if (st != MOE_OK) return st;
-  if (rows > 0 && gate_up == nullptr) return MOE_EINVAL;
+  if ((rows > 0 && gate_up == nullptr) || !vec_ok({gate_up})) return MOE_EINVAL;
   return from_hip(launch_w2_backward(dY_perm, offsets, rows, W2, gate_up, E, H, I, dt, dgate_up, stream));
 }
 
@@ -399,6 +463,7 @@ moe_status moe_expert_weight_grad(const void* a, const void* b, const int32_t* o
   if (rows < 0 || E < 1 || E > kMaxExperts || !hidden_ok(M, dt) || !hidden_ok(N, dt)) return MOE_EINVAL;
   if (offsets == nullptr || dW == nullptr) return MOE_EINVAL;
   if (rows > 0 && (a == nullptr || b == nullptr)) return MOE_EINVAL;
+  if (!vec_ok({a, b, dW}) || !word_ok({offsets})) return MOE_EINVAL;
   return from_hip(launch_weight_grad(a, b, offsets, rows, E, M, N, dt, dW, stream));
 }
 
@@ -410,6 +475,7 @@ moe_status moe_expert_weight_grad_gather(const void* x, const int32_t* perm, int
   if (E < 1 || E > kMaxExperts || !hidden_ok(M, dt) || !hidden_ok(N, dt)) return MOE_EINVAL;
   if (offsets == nullptr || dW == nullptr) return MOE_EINVAL;
   if (n > 0 && (x == nullptr || perm == nullptr || b == nullptr)) return MOE_EINVAL;
+  if (!vec_ok({x, b, dW}) || !word_ok({perm, offsets})) return MOE_EINVAL;
   return from_hip(launch_weight_grad_gather(x, perm, n, K, b, offsets, E, M, N, dt, dW, stream));
 }
 
@@ -420,6 +486,7 @@ moe_status moe_dispatch_backward(const void* dX_perm, const int32_t* inv, const 
   if ((long long)n * K > INT32_MAX) return MOE_EINVAL;
   if (n == 0) return MOE_OK;
   if (dX_perm == nullptr || inv == nullptr || dx == nullptr) return MOE_EINVAL;
+  if (!vec_ok({dX_perm, add, dx}) || !word_ok({inv})) return MOE_EINVAL;
   return from_hip(launch_dispatch_backward(dX_perm, inv, add, n, H, K, dt, dx, stream));
 }
 
@@ -445,6 +512,8 @@ moe_status moe_route_backward(const void* x, const void* W_gate, const float* lo
     return MOE_EINVAL;
   if (dx_router != nullptr && W_gate == nullptr) return MOE_EINVAL;
   if (weights && x == nullptr) return MOE_EINVAL;
+  if (!vec_ok({x, W_gate, dx_router, dW_gate, ws}) || !word_ok({logits, topk_ids, topk_w, dw, dlogits, dbias}))
+    return MOE_EINVAL;
   if ((weights || dx_router != nullptr) && (ws == nullptr || ws_bytes < route_bwd_ws(n, H, E)))
     return MOE_EWORKSPACE;
   return from_hip(launch_route_backward(x, W_gate, logits, topk_ids, topk_w, dw, n, H, E, K, renorm, dt, dlogits,
@@ -470,6 +539,9 @@ moe_status moe_backward(const void* dy, const void* x, const void* W_gate, const
                 logits == nullptr || topk_ids == nullptr || topk_w == nullptr || perm == nullptr || inv == nullptr ||
                 gate_up == nullptr || h == nullptr || Y_perm == nullptr || dx == nullptr))
     return MOE_EINVAL;
+  if (!vec_ok({dy, x, W_gate, W13, W2, gate_up, h, Y_perm, dx, dW_gate, dW13, dW2, ws}) ||
+      !word_ok({logits, topk_ids, topk_w, offsets, perm, inv, dbias}))
+    return MOE_EINVAL;
   const BackwardLayout L = backward_layout(n, H, I, E, K, dt);
   if (ws == nullptr || ws_bytes < L.total) return MOE_EWORKSPACE;
   char* base = (char*)ws;
@@ -493,8 +565,17 @@ moe_status moe_backward(const void* dy, const void* x, const void* W_gate, const
   //   main: combine bwd -> dgate_up ------(join 1)-> dX_perm -> dispatch bwd -(join 2)
   //   aux:             \-> route bwd -> dW2 -/   \-> gather x_perm -> dW13 ----/
   // dW2 and dgate_up both read dY_perm, which dX_perm overwrites after join 1.
+  // The second stream is shared by every call on this device, so it is used
+  // only when it is free of other work's graph capture: when it is being
+  // captured into another capture than the caller's stream (a capture on
+  // another thread that forked into it and has not ended yet), the branches
+  // run on the caller's stream instead, in the same order as above.
   std::lock_guard<std::mutex> lock(g_aux_mutex);
   AuxStream* aux = aux_stream();
+  if (aux != nullptr) {
+    const unsigned long long aux_cap = capture_id(aux->s);
+    if (aux_cap == ~0ull || (aux_cap != 0 && aux_cap != capture_id(stream))) aux = nullptr;
+  }
   hipStream_t side = aux ? aux->s : stream;
   auto fork = [&](int i, hipStream_t from, hipStream_t to) {
     if (from == to) return hipSuccess;
@@ -527,7 +608,7 @@ moe_status moe_quantize_fp8(const void* W, int E, int Kd, int N, moe_dtype dt, u
   if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
   if (E < 0 || !hidden_ok(Kd, MOE_BF16) || N < 1 || N % 4 != 0) return MOE_EINVAL;
   if (E == 0) return MOE_OK;
-  if (W == nullptr || codes == nullptr || scales == nullptr) return MOE_EINVAL;
+  if (W == nullptr || codes == nullptr || scales == nullptr || !vec_ok({W, codes, scales})) return MOE_EINVAL;
   return from_hip(launch_quantize_fp8(W, E, Kd, N, dt, codes, scales, stream));
 }
 
@@ -537,6 +618,7 @@ static moe_status check_fp8_gemm(const void* a, const int32_t* offsets, int rows
   if (rows < 0 || E < 1 || E > kMaxExperts || !hidden_ok(H, dt) || !hidden_ok(I, dt)) return MOE_EINVAL;
   if (rows > 0 && (a == nullptr || offsets == nullptr || wq == nullptr || sc == nullptr || out == nullptr))
     return MOE_EINVAL;
+  if (!vec_ok({a, wq, sc, out}) || !word_ok({offsets})) return MOE_EINVAL;
   return MOE_OK;
 }
 
@@ -568,6 +650,11 @@ moe_status moe_forward_fp8(const void* x, const void* W_gate, const float* bias,
   if (n > 0 && (x == nullptr || W_gate == nullptr || W13q == nullptr || s13 == nullptr || W2q == nullptr ||
                 s2 == nullptr || y == nullptr))
     return MOE_EINVAL;
+  if (!vec_ok({x, W_gate, W13q, s13, W2q, s2, y, ws}) ||
+      !word_ok({bias, logits_out, topk_ids_out, topk_w_out, counts_out}))
+    return MOE_EINVAL;
+  if (n == 0)  // no tokens: nothing to compute; the optional counts are all zero
+    return counts_out ? from_hip(launch_fill_zero(counts_out, (size_t)E * 4, stream)) : MOE_OK;
   const ForwardLayout L = forward_layout(n, H, I, E, K, dt);
   if (ws == nullptr || ws_bytes < L.total) return MOE_EWORKSPACE;
   char* base = (char*)ws;
@@ -583,7 +670,6 @@ moe_status moe_forward_fp8(const void* x, const void* W_gate, const float* bias,
   e = launch_permute(ids, nullptr, n, H, E, K, 1, dt, counts, offsets, (int32_t*)(base + L.splits), perm, inv,
                      nullptr, (int32_t*)(base + L.pscratch), stream);
   if (e != hipSuccess) return MOE_EHIP;
-  if (n == 0) return MOE_OK;
   e = launch_w13_swiglu_gather_fp8(x, perm, n, K, offsets, W13q, s13, E, H, I, base + L.h, stream);
   if (e != hipSuccess) return MOE_EHIP;
   e = launch_w2_fp8(base + L.h, offsets, n * K, W2q, s2, E, H, I, base + L.Y_perm, stream);

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import routing_token_permute_amd as moe
-from gpu_util import assert_close, dev_tensor, layer_tensors, require_gpu, to_f64
+from gpu_util import assert_close, dev_tensor, errors, layer_tensors, require_gpu, to_f64
 from oracle import fp8 as of8
 from oracle import moe_oracle as om
 from workloads import make_config, make_layer
@@ -117,13 +117,24 @@ def _forward_fp8_parity(dev, w, what):
     y, logits, ids, wts, counts = moe.moe_forward_fp8(t["x"], t["W_gate"], q13, s13, q2, s2, w.K, w.renorm,
                                                       bias=t["bias"], routing_out=True)
     torch.cuda.synchronize()
-    ref = of8.forward_fp8(w.x_f32, w.W_gate_f32, c13, r13, c2, r2, w.K, w.renorm, bias=w.bias)
-    safe = ~(oracle.topk_margin(ref["logits_f32"], w.K) <= 1e-4)
-    print(f"[{what}] near-tie rows: {int((~safe).sum())} of {w.n}", flush=True)
-    assert (ids.cpu().numpy()[safe] == ref["e_top"][safe]).all()
-    assert_close(to_f64(y)[safe], ref["y"][safe], "bf16", what)
+    # Router logits against the fp64 product, then both sides route from the
+    # device's fp32 logits, so every row is compared.
+    ref_logits = oracle.router_logits(w.x_f32, w.W_gate_f32, w.bias)
+    L = logits.cpu().numpy()
+    fin = np.isfinite(ref_logits)
+    assert (np.isfinite(L) == fin).all()
+    ma, rf = errors(L[fin].astype(np.float64), ref_logits[fin])
+    assert rf <= 1e-5 and ma <= 1e-4
+    ref = of8.forward_fp8(w.x_f32, w.W_gate_f32, c13, r13, c2, r2, w.K, w.renorm, bias=w.bias,
+                          routing_logits_f32=L)
+    print(f"[{what}] rows at a top-K near-tie, all compared: {int((oracle.topk_margin(L, w.K) <= 1e-4).sum())}",
+          flush=True)
+    assert (ids.cpu().numpy() == ref["e_top"]).all()
+    assert (counts.cpu().numpy() == ref["counts"]).all()
+    assert_close(to_f64(y), ref["y"], "bf16", what)
     # FP8 weights move the output by about the quantisation error of the weights, not more.
-    plain = oracle.forward(w.x_f32, w.W_gate_f32, w.W13_f32, w.W2_f32, w.K, w.renorm, bias=w.bias)
+    plain = oracle.forward(w.x_f32, w.W_gate_f32, w.W13_f32, w.W2_f32, w.K, w.renorm, bias=w.bias,
+                           routing_logits_f32=L)
     rel = np.linalg.norm(ref["y"] - plain["y"]) / np.linalg.norm(plain["y"])
     print(f"[{what}] FP8 vs bf16 weights: rel_frob={rel:.3e}", flush=True)
     assert rel < 0.1

@@ -86,19 +86,15 @@ def test_route(dev, n, H, E, K, dtype, renorm, bias):
     ma, rf = errors(got[fin], ref[fin])
     print(f"[route logits n={n} E={E}] max_abs={ma:.2e} rel_frob={rf:.2e}", flush=True)
     assert rf <= 1e-5 and ma <= 1e-4
-    # ids: the oracle routes from its own logits; rows whose top-K boundary is
-    # a near-tie (margin below the logit error bound) may legitimately differ.
-    L32 = oracle.round_to_f32(ref)
-    e_ref, w_ref, _ = oracle.route_from_logits(L32, K, renorm)
-    margin = oracle.topk_margin(L32, K)
-    safe = ~(margin <= 1e-4)
-    ids_h = ids.cpu().numpy()
-    assert (ids_h[safe] == e_ref[safe]).all()
-    assert safe.mean() > 0.5
-    for i in np.flatnonzero(~safe):  # near-ties: the chosen set must still be a top-K
-        kth = np.sort(ref[i])[::-1][K - 1]
-        assert (ref[i, ids_h[i]] >= kth - 2e-4).all()
-    np.testing.assert_allclose(wts.cpu().numpy()[safe], w_ref[safe], atol=1e-6, rtol=0)
+    # Routing on every row: the oracle routes from the device's fp32 logits
+    # (identical inputs to steps 2-3), so ids must match bit for bit, near-ties
+    # of the top-K boundary included.
+    L = logits.cpu().numpy()
+    e_ref, w_ref, _ = oracle.route_from_logits(L, K, renorm)
+    print(f"[route n={n} E={E}] rows at a top-K near-tie: {int((oracle.topk_margin(L, K) <= 1e-4).sum())}",
+          flush=True)
+    assert (ids.cpu().numpy() == e_ref).all()
+    np.testing.assert_allclose(wts.cpu().numpy(), w_ref, atol=1e-6, rtol=0)
 
 
 @pytest.mark.parametrize("n,E,K,renorm", [(200, 64, 8, False), (200, 64, 8, True), (90, 256, 64, True), (40, 5, 5, False), (70, 130, 9, False), (7, 1, 1, True), (150, 100, 6, True), (60, 128, 17, False)])
@@ -356,22 +352,48 @@ def test_combine(dev, n, H, E, K, dtype, weighted):
 # ---------------------------------------------------------------------------
 
 
+def _check_logits(got_logits, ref_fp64, what):
+    """Device router logits against the oracle's fp64 product (step 1): the same
+    -inf entries, and relative Frobenius <= 1e-5 and max-abs <= 1e-4 on the rest."""
+    got = got_logits.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(ref_fp64)
+    assert (np.isfinite(got) == fin).all() and (got[~fin] == ref_fp64[~fin]).all()
+    ma, rf = errors(got[fin], ref_fp64[fin])
+    print(f"[{what} logits] max_abs={ma:.2e} rel_frob={rf:.2e}", flush=True)
+    assert rf <= 1e-5 and ma <= 1e-4
+
+
+def _check_dispatch(dev, ids, counts, ref, E, what):
+    """Steps 3-5 of every row, bit-exact: ids and counts from the layer call, and
+    offsets, splits, perm and inv from the permute kernel the layer runs, on the
+    layer's own ids."""
+    ids_h = ids.cpu().numpy()
+    assert (ids_h == ref["e_top"]).all(), f"{what}: expert ids differ"
+    assert (counts.cpu().numpy() == ref["counts"]).all(), f"{what}: counts differ"
+    meta = moe.moe_permute(ids, None, E)
+    torch.cuda.synchronize()
+    for k in ("offsets", "perm", "inv"):
+        assert (meta[k].cpu().numpy() == ref[k]).all(), f"{what}: {k} differ"
+    assert (meta["splits"].cpu().numpy() == ref["splits"]).all()
+
+
 def _forward_parity(dev, w, what):
+    """The whole layer on every row. Both sides route from the same fp32 logits:
+    the device's, which are first held to the oracle's fp64 router product. Then
+    routing and dispatch are compared bit-exact and y within the layer's bounds,
+    near-ties of the top-K boundary included."""
     t = layer_tensors(w, dev)
     y, logits, ids, wts, counts = moe.moe_forward(t["x"], t["W_gate"], t["W13"], t["W2"], w.K, w.renorm, bias=t["bias"], routing_out=True)
     torch.cuda.synchronize()
-    ref = oracle.forward(w.x_f32, w.W_gate_f32, w.W13_f32, w.W2_f32, w.K, w.renorm, bias=w.bias)
-    margin = oracle.topk_margin(ref["logits_f32"], w.K)
-    thr = 1e-4 if w.dtype == "bf16" else 1e-5
-    safe = ~(margin <= thr)
-    ids_h = ids.cpu().numpy()
-    print(f"[{what}] near-tie rows: {int((~safe).sum())} of {w.n}", flush=True)
-    assert (ids_h[safe] == ref["e_top"][safe]).all()
-    assert safe.mean() > 0.5
-    if safe.all():
-        assert (counts.cpu().numpy() == ref["counts"]).all()
-    np.testing.assert_allclose(wts.cpu().numpy()[safe], ref["w_top"][safe], atol=1e-6, rtol=0)
-    assert_close(to_f64(y)[safe], ref["y"][safe], w.dtype, what)
+    _check_logits(logits, oracle.router_logits(w.x_f32, w.W_gate_f32, w.bias), what)
+    L = logits.cpu().numpy()
+    ref = oracle.forward(w.x_f32, w.W_gate_f32, w.W13_f32, w.W2_f32, w.K, w.renorm, bias=w.bias,
+                         routing_logits_f32=L)
+    near = int((oracle.topk_margin(L, w.K) <= 1e-4).sum())
+    print(f"[{what}] rows at a top-K near-tie (margin <= 1e-4), all compared: {near} of {w.n}", flush=True)
+    _check_dispatch(dev, ids, counts, ref, w.E, what)
+    np.testing.assert_allclose(wts.cpu().numpy(), ref["w_top"], atol=1e-6, rtol=0)
+    assert_close(to_f64(y), ref["y"], w.dtype, what)
     return y
 
 
@@ -394,8 +416,9 @@ def test_forward_small_shapes(dev, n, H, I, E, K, dtype, renorm):  # noqa: E741
 
 def test_forward_large_batch_sampled(dev):
     """The OLMoE layer on 16384 tokens (131072 expert rows, about 20 GEMM tiles per CU): every token's
-    routing is checked, and the outputs of 512 sampled tokens against the oracle run on those tokens
-    alone (the layer treats each token independently)."""
+    routing and dispatch is checked bit-exact (the oracle routes from the device's fp32 logits, which are
+    held to the fp64 router product first), and the outputs of 512 sampled tokens against the oracle run
+    on those tokens alone (the layer treats each token independently)."""
     w = make_config("olmoe_bf16")
     n = 16384
     rng = np.random.default_rng(16384)
@@ -404,19 +427,44 @@ def test_forward_large_batch_sampled(dev):
     x = dev_tensor(xb, "bf16", dev)
     y, logits, ids, wts, counts = moe.moe_forward(x, t["W_gate"], t["W13"], t["W2"], w.K, w.renorm, routing_out=True)
     torch.cuda.synchronize()
-    L = oracle.round_to_f32(oracle.router_logits(xf, w.W_gate_f32, None))
+    what = f"forward n={n}"
+    _check_logits(logits, oracle.router_logits(xf, w.W_gate_f32, None), what)
+    L = logits.cpu().numpy()
     e_ref, w_ref, _ = oracle.route_from_logits(L, w.K, w.renorm)
-    safe = ~(oracle.topk_margin(L, w.K) <= 1e-4)
-    ids_h = ids.cpu().numpy()
-    print(f"[forward n={n}] near-tie rows: {int((~safe).sum())} of {n}", flush=True)
-    assert (ids_h[safe] == e_ref[safe]).all()
-    if safe.all():
-        assert (counts.cpu().numpy() == oracle.expert_counts(e_ref, w.E)).all()
-    assert int(counts.sum()) == n * w.K
-    sample = np.sort(rng.choice(np.flatnonzero(safe), size=512, replace=False))
-    ref = oracle.forward(xf[sample], w.W_gate_f32, w.W13_f32, w.W2_f32, w.K, w.renorm)
+    counts_ref = oracle.expert_counts(e_ref, w.E)
+    perm_ref, inv_ref = oracle.permutation(e_ref, w.E)
+    ref_all = dict(e_top=e_ref, counts=counts_ref, offsets=oracle.offsets_from_counts(counts_ref),
+                   splits=oracle.splits_by_rank(e_ref, w.E, 1), perm=perm_ref, inv=inv_ref)
+    print(f"[{what}] rows at a top-K near-tie, all compared: {int((oracle.topk_margin(L, w.K) <= 1e-4).sum())}",
+          flush=True)
+    _check_dispatch(dev, ids, counts, ref_all, w.E, what)
+    np.testing.assert_allclose(wts.cpu().numpy(), w_ref, atol=1e-6, rtol=0)
+    sample = np.sort(rng.choice(n, size=512, replace=False))
+    ref = oracle.forward(xf[sample], w.W_gate_f32, w.W13_f32, w.W2_f32, w.K, w.renorm, routing_logits_f32=L[sample])
     assert (ref["e_top"] == e_ref[sample]).all()
-    assert_close(to_f64(y)[sample], ref["y"], "bf16", f"forward n={n}, 512 sampled tokens")
+    assert_close(to_f64(y)[sample], ref["y"], "bf16", f"{what}, 512 sampled tokens")
+
+
+def test_forward_side_stream_internal_workspace(dev):
+    """moe_forward on a side stream with the binding allocating the workspace and outputs: those blocks
+    belong to the side stream, so work on the main stream that allocates and overwrites memory right
+    after the call cannot receive them while the side stream's kernels still use them."""
+    w = make_config("olmoe_bf16")
+    t = layer_tensors(w, dev)
+    ref = moe.moe_forward(t["x"], t["W_gate"], t["W13"], t["W2"], w.K, w.renorm)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    for _ in range(3):
+        y = moe.moe_forward(t["x"], t["W_gate"], t["W13"], t["W2"], w.K, w.renorm, stream=side)
+        nbytes = moe.moe_forward_workspace_size(w.n, w.H, w.I, w.E, w.K, torch.bfloat16)
+        junk = torch.empty(nbytes, dtype=torch.uint8, device=dev)  # main stream
+        junk.fill_(0x7F)
+        del junk
+        torch.cuda.current_stream(dev).wait_stream(side)
+        assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
+        y.record_stream(torch.cuda.current_stream(dev))
+    torch.cuda.synchronize()
 
 
 def test_forward_zero_tokens(dev):

@@ -234,3 +234,40 @@ def test_comm_cu_bits_balanced_across_xcds():
     for bad in (0, 7, 12, 136):
         with pytest.raises(ValueError):
             comm_cu_bits(bad)
+
+
+def test_misaligned_pointers_are_rejected(lib):
+    """Row matrices, weights and workspaces must be 16-byte aligned, per-pair arrays 4-byte aligned
+    (the kernels' vector loads, LDS DMA and buffer stores): an offset pointer gives MOE_EINVAL before
+    any launch."""
+    s = None
+    A = ctypes.c_void_p(0x10000)       # 16-byte aligned
+    M8 = ctypes.c_void_p(0x10008)      # 8-byte aligned only
+    M2 = ctypes.c_void_p(0x10002)      # 2-byte aligned only
+    ws = lib.moe_forward_workspace_size(16, 64, 64, 8, 2, 1)
+    args = [A, A, None, A, A, 16, 64, 64, 8, 2, 0, 1, A, None, None, None, None, A, ws, s]
+    for i in (0, 1, 3, 4, 12, 17):  # x, W_gate, W13, W2, y, ws
+        bad = list(args)
+        bad[i] = M8
+        assert lib.moe_forward(*bad) == EINVAL, i
+    for i in (13, 14, 15, 16):  # logits, ids, weights, counts: 4-byte arrays
+        bad = list(args)
+        bad[i] = M2
+        assert lib.moe_forward(*bad) == EINVAL, i
+    # route, combine, the expert GEMMs and the backward pieces
+    assert lib.moe_route(M8, A, None, 8, 64, 8, 2, 0, 1, A, A, A, s) == EINVAL
+    assert lib.moe_route(A, A, None, 8, 64, 8, 2, 0, 1, A, M2, A, s) == EINVAL
+    assert lib.moe_unpermute_combine(M8, A, None, 10, 64, 2, 1, A, s) == EINVAL
+    assert lib.moe_unpermute_combine(A, A, None, 10, 64, 2, 1, M8, s) == EINVAL
+    assert lib.moe_expert_w2(A, A, 8, M8, 4, 64, 64, 1, A, s) == EINVAL
+    assert lib.moe_expert_w13_swiglu_gather(A, M2, 4, 2, A, A, 4, 64, 64, 1, A, s) == EINVAL
+    assert lib.moe_dispatch_backward(A, A, M8, 8, 64, 2, 1, A, s) == EINVAL
+    pws = lib.moe_permute_workspace_size(100, 8, 2)
+    assert lib.moe_permute(A, None, 100, 64, 8, 2, 1, 1, A, A, A, A, A, None, M8, pws, s) == EINVAL
+
+
+def test_zero_tokens_needs_no_workspace(lib):
+    """n == 0 is a no-op for the layer call (nothing to write without counts_out), workspace or not."""
+    assert lib.moe_forward(None, None, None, None, None, 0, 64, 64, 8, 2, 0, 1, None, None, None, None, None,
+                           None, 0, None) == 0
+    assert lib.moe_workspace_size(16, 64, 64, 8, 2, 1) == lib.moe_forward_workspace_size(16, 64, 64, 8, 2, 1)
