@@ -74,7 +74,8 @@ typedef enum {
   MOE_EINVAL = 1,       /* bad argument, detected on the host before any launch */
   MOE_EUNSUPPORTED = 2, /* dtype or shape combination not built */
   MOE_EWORKSPACE = 3,   /* workspace pointer null or smaller than required */
-  MOE_EHIP = 4          /* a HIP launch failed */
+  MOE_EHIP = 4,         /* a HIP launch failed */
+  MOE_ETOOLARGE = 5     /* moe_forward_noalloc: the problem needs more than its fixed scratch */
 } moe_status;
 
 /* Element type of x, W_gate, W13, W2, x_perm, Y_perm and y.
@@ -259,6 +260,27 @@ moe_status moe_forward(const void* x, const void* W_gate, const float* bias, con
                        int n, int H, int I, int E, int K, int renorm, moe_dtype dt, void* y, float* logits_out,
                        int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
                        hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_forward_noalloc — moe_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments without the workspace, the same
+ * kernels and bitwise the same outputs. Its scratch is a fixed device array
+ * of moe_forward_noalloc_max_bytes() bytes (64 MiB) that the library holds on
+ * every device it runs on until the process ends; a problem whose
+ * moe_forward_workspace_size exceeds it returns MOE_ETOOLARGE before anything
+ * is enqueued (at the OLMoE layer shape, H = 2048, I = 1024, E = 64, K = 8,
+ * that is n above about 1300 tokens). The call allocates nothing. Every call
+ * on a device shares that one scratch array: calls that overlap on one
+ * device (other streams, other threads) race and must be ordered by the
+ * caller. Nothing in the scratch needs clearing between calls.
+ * ------------------------------------------------------------------------- */
+size_t moe_forward_noalloc_max_bytes(void);
+moe_status moe_forward_noalloc(const void* x, const void* W_gate, const float* bias, const void* W13,
+                               const void* W2, int n, int H, int I, int E, int K, int renorm, moe_dtype dt, void* y,
+                               float* logits_out, int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out,
+                               hipStream_t stream);
+
 
 /* ===========================================================================
  * Backward (training) pass of the same layer.

@@ -29,6 +29,7 @@ from ._lib import (  # noqa: F401
     moe_expert_weight_grad_gather,
     moe_forward,
     moe_forward_fp8,
+    moe_forward_noalloc,
     moe_forward_train,
     moe_forward_workspace_size,
     moe_grouped_swiglu,

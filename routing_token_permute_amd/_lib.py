@@ -44,6 +44,11 @@ SIGNATURES = {
     "moe_unpermute_combine": (_I, [_VP, _VP, _VP, _I, _I, _I, _I, _VP, _VP]),
     "moe_forward_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "moe_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "moe_forward_noalloc_max_bytes": (_SZ, []),
+    "moe_forward_noalloc": (
+        _I,
+        [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP],
+    ),
     "moe_forward": (
         _I,
         [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
@@ -431,6 +436,39 @@ def moe_forward(x, W_gate, W13, W2, K: int, renorm: bool, bias=None, y=None, ws=
         _ptr(y), *[_ptr(t) for t in extra], _ptr(ws), ws.numel(), _stream(dev, stream),
     )
     _check(code, "moe_forward")
+    return (y, *extra) if routing_out else y
+
+
+@_on_stream
+def moe_forward_noalloc(x, W_gate, W13, W2, K: int, renorm: bool, bias=None, y=None, routing_out=False, stream=None):
+    """moe_forward on the library's fixed device scratch (no workspace argument; the library
+    allocates nothing). Returns y, or (y, logits, topk_ids, topk_w, counts) with routing_out."""
+    lib = load_library()
+    n, H = x.shape
+    E = W_gate.shape[1]
+    I = W13.shape[2] // 2  # noqa: E741
+    dev = x.device
+    _need(x, "x", (n, H))
+    _need(W_gate, "W_gate", (H, E), x.dtype, dev)
+    _need(W13, "W13", (E, H, 2 * I), x.dtype, dev)
+    _need(W2, "W2", (E, I, H), x.dtype, dev)
+    if bias is not None:
+        _need(bias, "bias", (E,), torch.float32, dev)
+    y = _empty((n, H), x.dtype, dev) if y is None else y
+    _need(y, "y", (n, H), x.dtype, dev)
+    extra = [None] * 4
+    if routing_out:
+        extra = [
+            _empty((n, E), torch.float32, dev),
+            _empty((n, K), torch.int32, dev),
+            _empty((n, K), torch.float32, dev),
+            _empty((E,), torch.int32, dev),
+        ]
+    code = lib.moe_forward_noalloc(
+        _ptr(x), _ptr(W_gate), _ptr(bias), _ptr(W13), _ptr(W2), n, H, I, E, K, int(bool(renorm)), _dt(x),
+        _ptr(y), *[_ptr(t) for t in extra], _stream(dev, stream),
+    )
+    _check(code, "moe_forward_noalloc")
     return (y, *extra) if routing_out else y
 
 

@@ -207,6 +207,36 @@ moe_status forward_enqueue(const void* x, const void* W_gate, const float* bias,
   return from_hip(launch_combine(base + L.Y_perm, inv, w, n, H, K, dt, y, stream));
 }
 
+// Scratch of moe_forward_noalloc: the workspace of moe_forward, in a static
+// device array that every device the library runs on holds from the first
+// call to the end of the process. Every call on a device shares it (calls
+// that overlap on one device race); no part needs to start at zero, since
+// every region is written by the call before it is read.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; the array's name itself is a
+// host-side stand-in that must never reach a kernel.
+char* scratch_ptr() {
+  constexpr int kMaxDevices = 64;
+  static char* ptrs[kMaxDevices] = {};
+  static std::once_flag once[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::call_once(once[dev], [dev] {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess && p != nullptr)
+      ptrs[dev] = (char*)p;
+    else
+      (void)hipGetLastError();
+  });
+  return ptrs[dev];
+}
+
 // Capture state of a stream: 0 when it is not being captured, else the id of
 // the capture it belongs to; ~0 when the query fails (treated as busy).
 unsigned long long capture_id(hipStream_t s) {
@@ -235,6 +265,9 @@ const char* moe_status_string(moe_status s) {
       return "MOE_EWORKSPACE: workspace missing or smaller than required";
     case MOE_EHIP:
       return "MOE_EHIP: a HIP kernel launch failed";
+    case MOE_ETOOLARGE:
+      return "MOE_ETOOLARGE: the problem needs more scratch than moe_forward_noalloc holds "
+             "(moe_forward_noalloc_max_bytes); use moe_forward with a workspace";
   }
   return "unknown moe_status";
 }
@@ -375,6 +408,24 @@ moe_status moe_forward(const void* x, const void* W_gate, const float* bias, con
   if (ws == nullptr || ws_bytes < forward_layout(n, H, I, E, K, dt).total) return MOE_EWORKSPACE;
   return forward_enqueue(x, W_gate, bias, W13, W2, n, H, I, E, K, renorm, dt, y, logits_out, topk_ids_out,
                          topk_w_out, counts_out, (char*)ws, stream);
+}
+
+size_t moe_forward_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+moe_status moe_forward_noalloc(const void* x, const void* W_gate, const float* bias, const void* W13, const void* W2,
+                               int n, int H, int I, int E, int K, int renorm, moe_dtype dt, void* y,
+                               float* logits_out, int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out,
+                               hipStream_t stream) {
+  const moe_status st = check_forward(x, W_gate, bias, W13, W2, n, H, I, E, K, dt, y, logits_out, topk_ids_out,
+                                      topk_w_out, counts_out);
+  if (st != MOE_OK) return st;
+  if (n == 0)
+    return counts_out ? from_hip(launch_fill_zero(counts_out, (size_t)E * 4, stream)) : MOE_OK;
+  if (forward_layout(n, H, I, E, K, dt).total > kNoAllocScratchBytes) return MOE_ETOOLARGE;
+  char* base = scratch_ptr();
+  if (base == nullptr) return MOE_EHIP;
+  return forward_enqueue(x, W_gate, bias, W13, W2, n, H, I, E, K, renorm, dt, y, logits_out, topk_ids_out,
+                         topk_w_out, counts_out, base, stream);
 }
 
 // ---------------------------------------------------------------------------
