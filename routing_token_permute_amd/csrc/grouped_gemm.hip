@@ -14,7 +14,7 @@
 //     wave-wide prefix sum of the per-expert tile counts), so no host
 //     synchronisation is needed.
 //   * Both operands go straight from HBM into a ring of LDS stages with
-//     global_load_lds_dwordx4 (32-deep k-steps, up to five stages in 160 KB),
+//     global_load_lds_dwordx4 (32-deep k-steps, three stages of 32 KB),
 //     each lane fetching the chunk that lands where the swizzled layout
 //     wants it. GEMM1 reads its A rows x[perm[r] / K] in that same copy, so
 //     no permuted copy of the tokens is made.
@@ -73,9 +73,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
                                                                     long long b_expert_stride, int Nout, int up_col,
                                                                     uint16_t* __restrict__ C, int ldc, int NB,
                                                                     int n_slots, uint16_t* __restrict__ gu_out) {
-  // GEMM2 (256-row tiles, K = I) runs on a 3-stage ring: measured a little
-  // faster than five stages, whose deeper copy lead buys nothing there.
-  using Cfg = TileCfg<BM, BK, (!GATED && BM == 256) ? 3 : kMaxStages>;
+  // The 256-row tiles run on a 3-stage ring: measured a little faster than
+  // four or five stages for both GEMMs, whose deeper copy lead buys nothing.
+  using Cfg = TileCfg<BM, BK, (BM == 256) ? 3 : kMaxStages>;
   constexpr int A_BYTES = Cfg::A_BYTES, STAGE = Cfg::STAGE, NSTAGE = Cfg::NSTAGE, A_ROW = Cfg::A_ROW;
   constexpr int KS = BK / 32;              // 32-deep MFMA steps per stage
   constexpr int NW = WM * WN;              // waves
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float gv = acc[mt][nt][j], uv = acc[mt][nt + NT / 2][j];
-            hv[j] = gv / (1.f + __expf(-gv)) * uv;
+            hv[j] = swiglu_f32(gv, uv);
           }
           hp[nt] = u32x2_t{pack2(hv[0], hv[1]), pack2(hv[2], hv[3])};
         }
@@ -425,7 +425,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float gv = acc[mt][nt][j], uv = acc[mt][nt + NT / 2][j];
-            hv[j] = gv / (1.f + __expf(-gv)) * uv;
+            hv[j] = swiglu_f32(gv, uv);
           }
           hp[nt] = u32x2_t{pack2(hv[0], hv[1]), pack2(hv[2], hv[3])};
         }

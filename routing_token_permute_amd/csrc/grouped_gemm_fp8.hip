@@ -284,7 +284,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_w8_kernel(
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float gv = acc[mt][nt][j] * sc[nt][j], uv = acc[mt][nt + NT / 2][j] * sc[nt + NT / 2][j];
-            hv[j] = gv / (1.f + __expf(-gv)) * uv;
+            hv[j] = swiglu_f32(gv, uv);
           }
           hp[nt] = u32x2_t{pack2(hv[0], hv[1]), pack2(hv[2], hv[3])};
         }

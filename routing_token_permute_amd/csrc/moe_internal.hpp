@@ -157,6 +157,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
+// SwiGLU of one output: SiLU(g) * u = g * u / (1 + e^-g), with e^-g from the
+// hardware base-2 exponential and the quotient from the hardware reciprocal
+// (each about 1 ulp of fp32, far below the bf16 rounding that follows). For
+// g -> -inf, e^-g overflows to +inf and the reciprocal to 0, the exact limit.
+__device__ __forceinline__ float swiglu_f32(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
+  return g * __builtin_amdgcn_rcpf(1.f + e) * u;
+}
+
 // LDS transpose read (ds_read_b64_tr_b16): within each group of 16 lanes,
 // lanes 4r..4r+3 together supply row r (16 consecutive 16-bit elements, 4
 // per lane); lane c of the group receives column c of those 4 rows.
