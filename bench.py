@@ -49,18 +49,22 @@ def _parse():
     p.add_argument("--comm-cus", type=int, nargs="*", default=[8, 16, 32, 64],
                    help="ep_share_bf16: compute units given to the permute/unpermute stream in the CU-masked runs")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--headline-only", action="store_true",
+                   help="olmoe_bf16: leave out the other configurations (tiny, skewed, decode, EP share)")
+    p.add_argument("--profile-forward", type=int, default=0, metavar="N",
+                   help="only run N moe_forward calls of the workload (for rocprofv3 counter passes)")
+    p.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                   help="turn rocprofv3 --pmc csv directories into the per-kernel counter summary printed on stdout")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle wall time for the CPU baseline")
     p.add_argument("--copy-calibration", action="store_true",
-                   help="only run a plain 1 GiB device-to-device copy kernel (to scale FETCH_SIZE / WRITE_SIZE)")
-    p.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
-                   help="turn four rocprofv3 --pmc csv directories into the traffic summary printed on stdout")
+                   help="only run a plain 1 GiB device-to-device copy kernel (a known-bytes check of the HBM counters)")
     return p.parse_args()
 
 
 # ---------------------------------------------------------------------------
-# HBM traffic of the dominant kernel, from rocprofv3 counters
+# rocprofv3 counter summaries
 # ---------------------------------------------------------------------------
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm1_swiglu_gather_olmoe_n4096.txt")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_moe_forward_olmoe_n4096.md")
 GEMM_SOURCE = os.path.join(ROOT, "routing_token_permute_amd", "csrc", "grouped_gemm.hip")
 COPY_BYTES = 1 << 30
 
@@ -79,52 +83,106 @@ def _source_hash():
     return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
-def _pmc_mean(d, counter, match):
+def _kernel_label(name):
+    if "route_bf16_kernel" in name or "route_f32_kernel" in name:
+        return "route"
+    for k in ("permute_single_kernel", "permute_count_kernel", "permute_place_kernel", "gather_rows_kernel",
+              "sum_slots_kernel"):
+        if k in name:
+            return k.replace("_kernel", "")
+    if "combine_kernel" in name:
+        return "combine"
+    if "gemm_bf16_kernel<" in name:
+        args = name.split("gemm_bf16_kernel<", 1)[1].split(">", 1)[0].split(",")
+        gated, bm = args[0].strip() == "true", args[3].strip()
+        return ("gemm1_swiglu" if gated else "gemm2") + f"_bm{bm}"
+    if "FillFunctor" in name:
+        return "fill_1GiB"
+    if "copy" in name.lower() or "elementwise" in name.lower():
+        return "copy_1GiB"
+    return name.split("(")[0][-60:]
+
+
+def _summarize_counters(dirs):
+    """Per-kernel means over the dispatches of every --pmc pass (the first
+    dispatch of each kernel, with cold caches, is left out when there are more),
+    and the figures derived from them: MFMA busy share of the SIMD cycles, bf16
+    MFMA TFLOP/s, LDS / TA / TD busy shares of the CU cycles, L2 hit rate, and
+    HBM bytes from the per-size memory request counters of L2 (32/64/128-byte
+    reads, 64-byte and other writes)."""
     import csv
     import glob
+    from collections import defaultdict
 
-    vals = []
-    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-        for r in csv.DictReader(open(f)):
-            if r["Counter_Name"] == counter and match(r["Kernel_Name"]):
-                vals.append(float(r["Counter_Value"]))
-    if not vals:
-        raise SystemExit(f"no {counter} samples matching in {d}")
-    return sum(vals) / len(vals), len(vals)
-
-
-def _summarize_traffic(dirs):
-    fd, wd, cfd, cwd = dirs
-    is_g1 = lambda k: "gemm_bf16_kernel<true, true" in k  # noqa: E731
-    is_copy = lambda k: "copy" in k.lower() or "elementwise" in k.lower()  # noqa: E731
-    fetch_kib, nf = _pmc_mean(fd, "FETCH_SIZE", is_g1)
-    write_kib, nw = _pmc_mean(wd, "WRITE_SIZE", is_g1)
-    cal_f, _ = _pmc_mean(cfd, "FETCH_SIZE", is_copy)
-    cal_w, _ = _pmc_mean(cwd, "WRITE_SIZE", is_copy)
-    f_scale = COPY_BYTES / (cal_f * 1024.0)
-    w_scale = COPY_BYTES / (cal_w * 1024.0)
-    out = {
-        "kernel": "gemm_bf16_kernel<true, true, ...> (GEMM1 + SwiGLU, gather fused), OLMoE n=4096",
-        "source_sha256_16": _source_hash(),
-        "fetch_kib_per_dispatch": round(fetch_kib, 1), "fetch_dispatches": nf,
-        "write_kib_per_dispatch": round(write_kib, 1), "write_dispatches": nw,
-        "copy_1GiB_fetch_kib": round(cal_f, 1), "copy_1GiB_write_kib": round(cal_w, 1),
-        "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
-        "hbm_bytes_per_launch": round(fetch_kib * 1024 * f_scale + write_kib * 1024 * w_scale),
-    }
+    vals = defaultdict(lambda: defaultdict(list))
+    durs = defaultdict(list)
+    agent = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*agent_info.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r.get("Agent_Type") == "GPU":
+                    agent = {k: int(r[k]) for k in ("Num_Xcc", "Cu_Count", "Simd_Count", "Max_Engine_Clk_Fcompute")}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            per = defaultdict(list)
+            for r in csv.DictReader(open(f)):
+                per[(r["Kernel_Name"], r["Counter_Name"])].append(
+                    (int(r["Dispatch_Id"]), float(r["Counter_Value"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+            for (kname, cname), rows in per.items():
+                rows.sort()
+                if len(rows) > 1:
+                    rows = rows[1:]
+                lab = _kernel_label(kname)
+                vals[lab][cname] += [v for _, v, _ in rows]
+                durs[lab] += [t for _, _, t in rows]
+    xcc = agent.get("Num_Xcc", 8)
+    cus = agent.get("Cu_Count", 256)
+    simds = agent.get("Simd_Count", 1024)
+    out = {"agent": agent, "source_sha256_16": _source_hash(), "kernels": {}}
+    for lab, cv in sorted(vals.items()):
+        m = {c: sum(v) / len(v) for c, v in cv.items()}
+        dur = sum(durs[lab]) / len(durs[lab]) * 1e-9
+        k = {"duration_us": round(dur * 1e6, 2), "dispatches_per_pass": len(next(iter(cv.values())))}
+        cyc = m.get("GRBM_GUI_ACTIVE", 0) / xcc
+        if cyc:
+            k["sclk_GHz_effective"] = round(cyc / dur / 1e9, 3)
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+                k["mfma_busy"] = round(m["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * cyc), 4)
+            for c, key in (("SQ_LDS_IDX_ACTIVE", "lds_busy"), ("TA_TA_BUSY_sum", "ta_busy"), ("TD_TD_BUSY_sum", "td_busy")):
+                if c in m:
+                    k[key] = round(m[c] / (cus * cyc), 4)
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in m:
+            k["mfma_bf16_TFLOP/s"] = round(m["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / dur / 1e12, 1)
+        if "SQ_WAIT_ANY" in m and m.get("SQ_WAVE_CYCLES"):
+            k["wave_wait_share"] = round(m["SQ_WAIT_ANY"] / m["SQ_WAVE_CYCLES"], 4)
+        if "SQ_LDS_BANK_CONFLICT" in m:
+            k["lds_bank_conflict_cycles"] = m["SQ_LDS_BANK_CONFLICT"]
+        if m.get("TCC_REQ_sum"):
+            k["l2_hit_rate"] = round(m.get("TCC_HIT_sum", 0) / m["TCC_REQ_sum"], 4)
+        if "TCC_EA0_RDREQ_128B_sum" in m:
+            rd = 32 * m.get("TCC_EA0_RDREQ_32B_sum", 0) + 64 * m.get("TCC_EA0_RDREQ_64B_sum", 0) + \
+                128 * m["TCC_EA0_RDREQ_128B_sum"]
+            k["hbm_read_bytes"] = round(rd)
+        if "TCC_EA0_WRREQ_sum" in m:
+            w64 = m.get("TCC_EA0_WRREQ_64B_sum", 0)
+            k["hbm_write_bytes"] = round(64 * w64 + 32 * (m["TCC_EA0_WRREQ_sum"] - w64))
+        if "hbm_read_bytes" in k and "hbm_write_bytes" in k:
+            k["hbm_bytes"] = k["hbm_read_bytes"] + k["hbm_write_bytes"]
+            k["hbm_GB/s"] = round(k["hbm_bytes"] / dur / 1e9, 1)
+        out["kernels"][lab] = k
     print(json.dumps(out, indent=1))
 
 
 def _traffic_bytes():
-    """HBM bytes per GEMM1 launch from the committed counter summary, or None when
-    the summary is missing or was taken on a different kernel source."""
+    """HBM bytes per GEMM1 launch (read + write, from L2's per-size memory request
+    counters) from the committed counter summary, or None when the summary is
+    missing or was taken on a different GEMM source."""
     try:
-        d = json.loads(open(TRAFFIC_FILE).read().split("\n```json\n", 1)[-1].split("\n```", 1)[0])
+        d = json.loads(open(COUNTERS_FILE).read().split("\n```json\n", 1)[-1].split("\n```", 1)[0])
     except (OSError, ValueError):
         return None
     if d.get("source_sha256_16") != _source_hash():
         return None
-    return d.get("hbm_bytes_per_launch")
+    return d.get("kernels", {}).get("gemm1_swiglu_bm256", {}).get("hbm_bytes")
 
 
 def _copy_calibration():
@@ -217,10 +275,164 @@ def _pcts(ms):
     return {"p10_ms": round(float(q[0]), 5), "p50_ms": round(float(q[1]), 5), "p90_ms": round(float(q[2]), 5)}
 
 
+def _to_dev_bits(w, name, dev, torch):
+    b = w.bits(name)
+    if w.dtype == "bf16":
+        return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(b, dtype=np.float32)).to(dev)
+
+
+def _expert_load(counts):
+    """Per-expert row counts n_e: histogram, coefficient of variation, hot/empty experts."""
+    c = np.asarray(counts, dtype=np.int64)
+    edges = [0, 1, 2, 3, 5, 9, 17, 33, 65, 129, 257, 513, 1025, 2049, 4097, 1 << 30]
+    hist = {}
+    for lo, hi in zip(edges[:-1], edges[1:]):
+        k = int(((c >= lo) & (c < hi)).sum())
+        if k:
+            hist[f"{lo}" if hi == lo + 1 else f"{lo}-{hi - 1}"] = k
+    mu = float(c.mean())
+    return {"n_e_hist": hist, "cv": round(float(c.std()) / mu, 4) if mu > 0 else None,
+            "n_e_min": int(c.min()), "n_e_max": int(c.max()), "experts_hit": int((c > 0).sum()),
+            "empty_experts": int((c == 0).sum())}
+
+
+def _layer_bench(w, args, torch, moe, dev, detail):
+    """One layer workload: moe_forward timed over args.steps calls (HIP events on the
+    current stream, after the warmup and clock-settle phase), the stages moe_forward
+    enqueues timed alone from HIP-graph replays, the expert load, and GEMM1's roofline
+    (MFMA-bound or weight-stream-bound by its algorithmic intensity against the ridge)."""
+    n, H, I, E, K = w.n, w.H, w.I, w.E, w.K  # noqa: E741
+    x, Wg, W13, W2 = (_to_dev_bits(w, k, dev, torch) for k in ("x", "W_gate", "W13", "W2"))
+    bias = None if w.bias is None else torch.from_numpy(w.bias).to(dev)
+    tdt = x.dtype
+    esz = 2 if w.dtype == "bf16" else 4
+    y = torch.empty((n, H), dtype=tdt, device=dev)
+    ws = torch.empty(moe.moe_forward_workspace_size(n, H, I, E, K, tdt), dtype=torch.uint8, device=dev)
+
+    def step():
+        moe.moe_forward(x, Wg, W13, W2, K, w.renorm, bias=bias, y=y, ws=ws)
+
+    _warm(step, args.warmup, torch, args.settle_ms)
+    t0 = time.perf_counter()
+    ms = _time_region(step, args.steps, torch)
+    wall = time.perf_counter() - t0
+    spread = _pcts(_time_each(step, max(args.steps, 10), torch))
+    logits, ids, wts = moe.moe_route(x, Wg, bias, K, w.renorm)
+    meta = moe.moe_permute(ids, None, E)
+    h = moe.moe_expert_w13_swiglu_gather(x, meta["perm"], K, meta["offsets"], W13)
+    Yp = moe.moe_expert_w2(h, meta["offsets"], W2)
+    yc = moe.moe_unpermute_combine(Yp, meta["inv"], wts, n, K)
+    torch.cuda.synchronize()
+    counts = meta["counts"].cpu().numpy()
+    R = args.stage_reps
+    st = {
+        "route": _time_region_graph(lambda: moe.moe_route(x, Wg, bias, K, w.renorm, logits=logits, topk_ids=ids, topk_w=wts), R, torch),
+        "permute": _time_region_graph(lambda: moe.moe_permute(ids, None, E, out=meta), R, torch),
+        "gemm1_swiglu": _time_region_graph(lambda: moe.moe_expert_w13_swiglu_gather(x, meta["perm"], K, meta["offsets"], W13, h=h), R, torch),
+        "gemm2": _time_region_graph(lambda: moe.moe_expert_w2(h, meta["offsets"], W2, Y_perm=Yp), R, torch),
+        "combine": _time_region_graph(lambda: moe.moe_unpermute_combine(Yp, meta["inv"], wts, n, K, y=yc), R, torch),
+    }
+    nk = n * K
+    hit = int((counts > 0).sum())
+    flops1 = 2.0 * nk * H * 2 * I
+    flops2 = 2.0 * nk * I * H
+    # Algorithmic bytes per call (each input read once, each output written once;
+    # weights of the experts that received rows).
+    bytes_ = {
+        "route": n * H * esz + H * E * esz + n * E * 4 + nk * 8,
+        "permute": nk * 4 + nk * 8 + (2 * E + 2) * 4,
+        "gemm1_swiglu": nk * H * esz + hit * H * 2 * I * esz + nk * I * esz + nk * 4,
+        "gemm2": nk * I * esz + hit * I * H * esz + nk * H * esz,
+        "combine": nk * H * esz + nk * 8 + n * H * esz,
+    }
+    stages = {}
+    for k, v in st.items():
+        s_ = {"ms": round(v, 5), "GB/s": round(bytes_[k] / (v * 1e-3) / 1e9, 1)}
+        s_["frac_hbm"] = round(s_["GB/s"] / PEAK_HBM_GBPS, 4)
+        if k == "gemm1_swiglu":
+            s_["TFLOP/s"] = round(flops1 / (v * 1e-3) / 1e12, 1)
+        if k == "gemm2":
+            s_["TFLOP/s"] = round(flops2 / (v * 1e-3) / 1e12, 1)
+        stages[k] = s_
+    gg_ms = st["gemm1_swiglu"] + st["gemm2"]
+    gg = (flops1 + flops2) / (gg_ms * 1e-3) / 1e12
+    g1_kernel = "gemm_bf16_kernel<GATED=true, GATHER=true> (GEMM1 with fused row gather + SwiGLU epilogue)"
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    if flops1 / bytes_["gemm1_swiglu"] >= ridge:
+        a = stages["gemm1_swiglu"]["TFLOP/s"]
+        roof = {"kernel": g1_kernel, "bound": "mfma", "achieved": a, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(a / PEAK_BF16_TFLOPS, 4)}
+    else:
+        a = stages["gemm1_swiglu"]["GB/s"]
+        roof = {"kernel": g1_kernel, "bound": "hbm", "achieved": a, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(a / PEAK_HBM_GBPS, 4)}
+    roof["traffic"] = None
+    out = {"ms": round(ms, 5), "tokens/s": round(n / (ms * 1e-3), 1), "step_spread": spread,
+           "wall_s_timed_region": round(wall, 3),
+           "grouped_gemm": {"TFLOP/s": round(gg, 1), "frac_bf16_peak": round(gg / PEAK_BF16_TFLOPS, 4),
+                            "GFLOP": round((flops1 + flops2) / 1e9, 1)},
+           "stages": stages, "expert_load": _expert_load(counts), "roofline": roof}
+    if not detail:
+        return out
+    # The alternative second half (routing weights and un-permutation in GEMM2's
+    # epilogue, then a contiguous sum of each token's K rows), cold-cache times of
+    # the memory-bound stages, and the standalone row gather of moe_permute.
+    Yt = moe.moe_expert_w2_scatter(h, meta["offsets"], meta["perm"], wts, W2)
+    ys = moe.moe_sum_slots(Yt, n, K)
+    alt = {
+        "alt_gemm2_scatter": (_time_region_graph(
+            lambda: moe.moe_expert_w2_scatter(h, meta["offsets"], meta["perm"], wts, W2, Y_tok=Yt), R, torch),
+            nk * I * esz + hit * I * H * esz + nk * H * esz + nk * 8, flops2),
+        "alt_slot_sum": (_time_region_graph(lambda: moe.moe_sum_slots(Yt, n, K, y=ys), R, torch),
+                         nk * H * esz + n * H * esz, None),
+    }
+    for k, (v, b, f) in alt.items():
+        stages[k] = {"ms": round(v, 5), "GB/s": round(b / (v * 1e-3) / 1e9, 1),
+                     "frac_hbm": round(b / (v * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+        if f:
+            stages[k]["TFLOP/s"] = round(f / (v * 1e-3) / 1e12, 1)
+    # Cold-cache times: a 512 MB buffer is read before every call so that the
+    # stage's inputs are in neither L2 nor the 256 MB MALL.
+    junk = torch.zeros((512 << 20) // 4, dtype=torch.float32, device=dev)
+    flush = lambda: junk.sum()  # noqa: E731
+    cold = {
+        "route": _time_each(lambda: moe.moe_route(x, Wg, bias, K, w.renorm, logits=logits, topk_ids=ids, topk_w=wts),
+                            R, torch, flush),
+        "permute": _time_each(lambda: moe.moe_permute(ids, None, E, out=meta), R, torch, flush),
+        "combine": _time_each(lambda: moe.moe_unpermute_combine(Yp, meta["inv"], wts, n, K, y=yc), R, torch, flush),
+    }
+    del junk
+    for k, v in cold.items():
+        c = _pcts(v)
+        c["GB/s_at_p50"] = round(bytes_[k] / (c["p50_ms"] * 1e-3) / 1e9, 1)
+        stages[k]["cold"] = c
+    meta_x = moe.moe_permute(ids, x, E)
+    gather_ms = _time_region_graph(lambda: moe.moe_permute(ids, x, E, out=meta_x), R, torch) - st["permute"]
+    stages["row_gather_standalone"] = {"ms": round(gather_ms, 5),
+                                       "GB/s": round((n * H * esz + nk * H * esz) / (gather_ms * 1e-3) / 1e9, 1)}
+    return out
+
+
+def _peaks(moe):
+    """The published MI355X peaks the roofline uses, beside the figures derived
+    from the device's own properties (compute units x 4096 bf16 FLOP per clock
+    per CU x peak shader clock)."""
+    try:
+        d = moe.device_info()
+    except Exception as e:  # noqa: BLE001
+        return {"error": str(e)}
+    cu, sclk = d["compute_units"], d["sclk_khz"] * 1e3
+    return {"used": {"bf16_dense_TFLOP/s": PEAK_BF16_TFLOPS, "hbm_GB/s": PEAK_HBM_GBPS, "source": "published"},
+            "device": {"compute_units": cu, "peak_sclk_MHz": round(sclk / 1e6, 1),
+                       "bf16_dense_TFLOP/s": round(cu * 4096 * sclk / 1e12, 1),
+                       "mem_clk_MHz": round(d["mem_clk_khz"] / 1e3, 1), "mem_bus_bits": d["mem_bus_bits"]}}
+
+
 def main():
     args = _parse()
-    if args.summarize_traffic:
-        _summarize_traffic(args.summarize_traffic)
+    if args.summarize_counters:
+        _summarize_counters(args.summarize_counters)
         return
     if args.copy_calibration:
         _copy_calibration()
@@ -238,6 +450,9 @@ def main():
     import routing_token_permute_amd as moe
     from workloads import make_config
 
+    if args.profile_forward:
+        _profile_forward(args, torch, moe)
+        return
     if args.workload == "ep_share_bf16":
         _bench_ep_share(args)
         return
@@ -249,116 +464,27 @@ def main():
         return
     dev = torch.device("cuda:0")
     w = make_config(args.workload)
-    n, H, I, E, K = w.n, w.H, w.I, w.E, w.K  # noqa: E741
+    head = _layer_bench(w, args, torch, moe, dev, detail=True)
+    roof = dict(head["roofline"])
+    if args.workload == "olmoe_bf16":
+        roof["traffic"] = _traffic_bytes()
 
-    def to_dev(name):
-        b = w.bits(name)
-        return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
-
-    x, Wg, W13, W2 = (to_dev(k) for k in ("x", "W_gate", "W13", "W2"))
-    bias = None if w.bias is None else torch.from_numpy(w.bias).to(dev)
-    y = torch.empty((n, H), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(moe.moe_forward_workspace_size(n, H, I, E, K, torch.bfloat16), dtype=torch.uint8, device=dev)
-
-    def step():
-        moe.moe_forward(x, Wg, W13, W2, K, w.renorm, bias=bias, y=y, ws=ws)
-
-    _warm(step, args.warmup, torch, args.settle_ms)
-    t0 = time.perf_counter()
-    ms_events = _time_region(step, args.steps, torch)
-    wall = time.perf_counter() - t0
-    ms_per_step = ms_events
-    tokens_per_s = n / (ms_per_step * 1e-3)
-    # Spread of single steps (events around each call; not the headline figure).
-    step_spread = _pcts(_time_each(step, max(args.steps, 10), torch))
-
-    # ---- per-stage timing: each stage alone, on its own inputs ----
-    # The stages moe_forward enqueues, each timed alone on its own inputs.
-    logits, ids, wts = moe.moe_route(x, Wg, bias, K, w.renorm)
-    meta = moe.moe_permute(ids, None, E)
-    h = moe.moe_expert_w13_swiglu_gather(x, meta["perm"], K, meta["offsets"], W13)
-    Yp = moe.moe_expert_w2(h, meta["offsets"], W2)
-    yc = moe.moe_unpermute_combine(Yp, meta["inv"], wts, n, K)
-    # The alternative second half (routing weights and un-permutation in
-    # GEMM2's epilogue, then a contiguous sum of each token's K rows).
-    Yt = moe.moe_expert_w2_scatter(h, meta["offsets"], meta["perm"], wts, W2)
-    ys = moe.moe_sum_slots(Yt, n, K)
-    torch.cuda.synchronize()
-    counts = meta["counts"].cpu().numpy()
-    R = args.stage_reps
-    # Stage figures from graph replays, without the host's per-call launch cost.
-    st = {
-        "route": _time_region_graph(lambda: moe.moe_route(x, Wg, bias, K, w.renorm, logits=logits, topk_ids=ids, topk_w=wts), R, torch),
-        "permute": _time_region_graph(lambda: moe.moe_permute(ids, None, E, out=meta), R, torch),
-        "gemm1_swiglu": _time_region_graph(lambda: moe.moe_expert_w13_swiglu_gather(x, meta["perm"], K, meta["offsets"], W13, h=h), R, torch),
-        "gemm2": _time_region_graph(lambda: moe.moe_expert_w2(h, meta["offsets"], W2, Y_perm=Yp), R, torch),
-        "combine": _time_region_graph(lambda: moe.moe_unpermute_combine(Yp, meta["inv"], wts, n, K, y=yc), R, torch),
-        "alt_gemm2_scatter": _time_region_graph(
-            lambda: moe.moe_expert_w2_scatter(h, meta["offsets"], meta["perm"], wts, W2, Y_tok=Yt), R, torch),
-        "alt_slot_sum": _time_region_graph(lambda: moe.moe_sum_slots(Yt, n, K, y=ys), R, torch),
-    }
-    # Cold-cache times of the memory-bound stages: a 512 MB buffer is read
-    # before every call so that the stage's inputs are not left in L2 or the
-    # 256 MB MALL (a read, so that no dirty lines are written back during the
-    # timed call).
-    junk = torch.zeros((512 << 20) // 4, dtype=torch.float32, device=dev)
-    flush = lambda: junk.sum()  # noqa: E731
-    cold = {
-        "route": _time_each(lambda: moe.moe_route(x, Wg, bias, K, w.renorm, logits=logits, topk_ids=ids, topk_w=wts),
-                            R, torch, flush),
-        "permute": _time_each(lambda: moe.moe_permute(ids, None, E, out=meta), R, torch, flush),
-        "combine": _time_each(lambda: moe.moe_unpermute_combine(Yp, meta["inv"], wts, n, K, y=yc), R, torch, flush),
-    }
-    del junk
-    # The standalone row gather of moe_permute (not part of moe_forward).
-    meta_x = moe.moe_permute(ids, x, E)
-    gather_ms = _time_region_graph(lambda: moe.moe_permute(ids, x, E, out=meta_x), R, torch) - st["permute"]
-    nk = n * K
-    hit = int((counts > 0).sum())
-    flops1 = 2.0 * nk * H * 2 * I
-    flops2 = 2.0 * nk * I * H
-    # Algorithmic bytes per call (each input read once, each output written once).
-    bytes_ = {
-        "route": n * H * 2 + H * E * 2 + n * E * 4 + nk * 8,
-        "permute": nk * 4 + nk * 8 + (2 * E + 2) * 4,
-        "gemm1_swiglu": nk * H * 2 + hit * H * 2 * I * 2 + nk * I * 2 + nk * 4,
-        "gemm2": nk * I * 2 + hit * I * H * 2 + nk * H * 2,
-        "combine": nk * H * 2 + nk * 8 + n * H * 2,
-        "alt_gemm2_scatter": nk * I * 2 + hit * I * H * 2 + nk * H * 2 + nk * 8,
-        "alt_slot_sum": nk * H * 2 + n * H * 2,
-    }
-    stages = {}
-    for k, ms in st.items():
-        s = {"ms": round(ms, 5), "GB/s": round(bytes_[k] / (ms * 1e-3) / 1e9, 1)}
-        s["frac_hbm"] = round(s["GB/s"] / PEAK_HBM_GBPS, 4)
-        if k == "gemm1_swiglu":
-            s["TFLOP/s"] = round(flops1 / (ms * 1e-3) / 1e12, 1)
-        if k in ("gemm2", "alt_gemm2_scatter"):
-            s["TFLOP/s"] = round(flops2 / (ms * 1e-3) / 1e12, 1)
-        stages[k] = s
-    for k, v in cold.items():
-        c = _pcts(v)
-        c["GB/s_at_p50"] = round(bytes_[k] / (c["p50_ms"] * 1e-3) / 1e9, 1)
-        stages[k]["cold"] = c
-    stages["row_gather_standalone"] = {"ms": round(gather_ms, 5),
-                                       "GB/s": round((n * H * 2 + nk * H * 2) / (gather_ms * 1e-3) / 1e9, 1)}
-    gg_ms = st["gemm1_swiglu"] + st["gemm2"]
-    gg_tflops = (flops1 + flops2) / (gg_ms * 1e-3) / 1e12
-    g1_tflops = flops1 / (st["gemm1_swiglu"] * 1e-3) / 1e12
-
-    # GEMM1's bound follows from its algorithmic intensity against the ridge:
-    # at n=4096 it is an MFMA-bound contraction, at decode sizes a weight stream.
-    g1_kernel = "gemm_bf16_kernel<GATED=true, GATHER=true> (GEMM1 with fused row gather + SwiGLU epilogue)"
-    # The counter summary covers the OLMoE n=4096 workload only.
-    g1_traffic = _traffic_bytes() if args.workload == "olmoe_bf16" else None
-    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
-    if flops1 / bytes_["gemm1_swiglu"] >= ridge:
-        g1_roof = {"kernel": g1_kernel, "bound": "mfma", "achieved": round(g1_tflops, 1), "peak": PEAK_BF16_TFLOPS,
-                   "unit": "TFLOP/s", "frac": round(g1_tflops / PEAK_BF16_TFLOPS, 4), "traffic": g1_traffic}
-    else:
-        g1_gbs = stages["gemm1_swiglu"]["GB/s"]
-        g1_roof = {"kernel": g1_kernel, "bound": "hbm", "achieved": g1_gbs, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                   "frac": round(g1_gbs / PEAK_HBM_GBPS, 4), "traffic": g1_traffic}
+    # The other configurations of the same layer, each with its own roofline.
+    configs = {}
+    if args.workload == "olmoe_bf16" and not args.headline_only:
+        for name in ("tiny_f32", "olmoe_skewed_bf16", "decode_bf16"):
+            r = _layer_bench(make_config(name), args, torch, moe, dev, detail=False)
+            if name == "tiny_f32":  # parity configuration: launch-bound, no roofline
+                r = {k: r[k] for k in ("ms", "tokens/s", "step_spread", "expert_load")}
+                r["note"] = "parity configuration (n=64, H=128): launch-bound, time reported, no roofline"
+            if name == "decode_bf16":
+                wc = make_config(name)
+                hit = r["expert_load"]["experts_hit"]
+                wbytes = hit * 3 * wc.H * wc.I * 2  # W13 (H x 2I) and W2 (I x H) of the hit experts
+                r["weight_stream"] = {"bytes": wbytes, "GB/s_over_forward": round(wbytes / (r["ms"] * 1e-3) / 1e9, 1),
+                                      "frac_hbm_over_forward": round(wbytes / (r["ms"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+            configs[name] = r
+        configs["ep_share_bf16"] = _ep_share_core(args, torch, dev, cu_split=False, cpu=False)[0]
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -366,34 +492,50 @@ def main():
 
     out = {
         "metric": METRIC,
-        "value": round(tokens_per_s, 1),
+        "value": head["tokens/s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "settle_ms": args.settle_ms,
-        "ms_per_step": round(ms_per_step, 5),
-        "step_spread": step_spread,
+        "ms_per_step": head["ms"],
+        "step_spread": head["step_spread"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights, OLMoE layer shapes; no checkpoint)",
-        "config": {"workload": args.workload, "n": n, "H": H, "I": I, "E": E, "K": K, "renorm": bool(w.renorm),
-                   "skewed_bias": w.bias is not None},
-        "grouped_gemm": {"TFLOP/s": round(gg_tflops, 1), "frac_bf16_peak": round(gg_tflops / PEAK_BF16_TFLOPS, 4),
-                         "GFLOP": round((flops1 + flops2) / 1e9, 1)},
-        "stages": stages,
-        "roofline": g1_roof,
-        "experts_hit": hit,
-        "wall_s_timed_region": round(wall, 3),
+        "config": {"workload": args.workload, "n": w.n, "H": w.H, "I": w.I, "E": w.E, "K": w.K,
+                   "renorm": bool(w.renorm), "skewed_bias": w.bias is not None},
+        "grouped_gemm": head["grouped_gemm"],
+        "stages": head["stages"],
+        "roofline": roof,
+        "expert_load": head["expert_load"],
+        "wall_s_timed_region": head["wall_s_timed_region"],
+        "configs": configs,
+        "peaks": _peaks(moe),
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(dev),
     }
     print(json.dumps(out), flush=True)
 
 
-def _bench_ep_share(args):
+def _profile_forward(args, torch, moe):
+    """A few moe_forward calls of the workload and nothing else, for rocprofv3
+    counter passes (no timing, no CPU work beyond the input upload)."""
+    from workloads import make_config
+
+    dev = torch.device("cuda:0")
+    w = make_config(args.workload)
+    x, Wg, W13, W2 = (_to_dev_bits(w, k, dev, torch) for k in ("x", "W_gate", "W13", "W2"))
+    bias = None if w.bias is None else torch.from_numpy(w.bias).to(dev)
+    for _ in range(args.profile_forward):
+        moe.moe_forward(x, Wg, W13, W2, w.K, w.renorm, bias=bias)
+    torch.cuda.synchronize()
+    print(json.dumps({"profiled": args.workload, "forwards": args.profile_forward}), flush=True)
+
+
+def _ep_share_core(args, torch, dev, cu_split=True, cpu=True):
     """One GPU's expert-parallel share, two micro-batches of 16384 received rows,
     8 local experts: the four controls of a two-stream overlap measurement.
 
@@ -401,15 +543,14 @@ def _bench_ep_share(args):
     permute + unpermute alone (one stream); T_C: everything serial on one
     stream; T_D: the two-stream schedule permute(A); [GEMM(A) || permute(B)];
     [GEMM(B) || unpermute(A)]; unpermute(B). Hidden fraction of the
-    permute/unpermute time: 1 - (T_D - T_A) / T_B.
+    permute/unpermute time: 1 - (T_D - T_A) / T_B. T_F: the fused one-stream
+    schedule. Returns a dict (and the CPU oracle baseline when `cpu`).
     """
-    import torch
-
     import oracle
+    import routing_token_permute_amd as moe
     from routing_token_permute_amd import ep_share as eps
     from workloads import make_config
 
-    dev = torch.device("cuda:0")
     ep = make_config("ep_share_bf16")
     tb = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
     W13, W2 = tb(ep.bits("W13")), tb(ep.bits("W2"))
@@ -445,10 +586,14 @@ def _bench_ep_share(args):
     t_d = timed(lambda: eps.run_two_streams(a, b, W13, W2, ep.E_local, compute, comm), [compute, comm])
     # The same work with the permute and unpermute folded into the GEMMs (one stream).
     t_f = timed(lambda: eps.run_fused(a, b, W13, W2, ep.E_local, s0), [s0])
+    # The dominant kernel: micro-batch A's GEMM1 + SwiGLU alone (graph replays).
+    g1 = _time_region_graph(lambda: moe.moe_expert_w13_swiglu(a.meta["x_perm"], a.meta["offsets"], W13, h=a.h),
+                            args.stage_reps, torch)
+    g1_tf = 2.0 * ep.R * ep.H * 2 * ep.I / (g1 * 1e-3) / 1e12
     # CU-masked split ([Fusion] §6.4's T_total(S_comm) = max(T_compute(S - S_comm), T_comm(S_comm)) + T_sync):
     # the permute/unpermute stream gets S_comm compute units, the GEMM stream the rest.
     split = []
-    for n_comm in args.comm_cus:
+    for n_comm in (args.comm_cus if cu_split else []):
         ms = eps.MaskedStreams(n_comm, dev)
         try:
             tc = ms.compute
@@ -464,48 +609,67 @@ def _bench_ep_share(args):
                       "T_total_ms": round(t_tot, 4), "T_sync_ms": round(t_tot - max(t_comp, t_comm), 4)})
     rows = 2 * ep.R
     flops = 2 * ep.flops_per_micro_batch
-    cpu = None
-    if not args.no_cpu_baseline:
-        import time as _t
-
-        reps, t0 = 0, _t.perf_counter()
+    out = {
+        "rows/s_two_streams": round(rows / (t_d * 1e-3), 1),
+        "rows/s_fused": round(rows / (t_f * 1e-3), 1),
+        "overlap": {"T_A_gemm_ms": round(t_a, 4), "T_B_permute_unpermute_ms": round(t_b, 4),
+                    "T_C_serial_ms": round(t_c, 4), "T_D_two_streams_ms": round(t_d, 4),
+                    "hidden_fraction": round(1 - (t_d - t_a) / t_b, 4), "speedup_serial_over_overlap": round(t_c / t_d, 4),
+                    "gemm_TFLOP/s_alone": round(flops / (t_a * 1e-3) / 1e12, 1),
+                    "gemm_TFLOP/s_in_overlap": round(flops / (t_d * 1e-3) / 1e12, 1)},
+        "fused_schedule": {"T_F_ms": round(t_f, 4), "speedup_over_two_streams": round(t_d / t_f, 4),
+                           "what": "metadata-only permute, GEMM1 reading rows through perm, GEMM2 storing rows at "
+                                   "their arrival positions (unit weights); one stream"},
+        "expert_load": [_expert_load(m.counts) for m in ep.micro_batches],
+        "roofline": {"kernel": "gemm_bf16_kernel<GATED=true, GATHER=false> (micro-batch A GEMM1 + SwiGLU)",
+                     "bound": "mfma", "achieved": round(g1_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(g1_tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "config": {"rows_per_micro_batch": ep.R, "micro_batches": 2, "E_local": ep.E_local, "H": ep.H, "I": ep.I},
+    }
+    if split:
+        out["overlap"]["cu_split"] = split
+    if cpu:
+        reps, t0 = 0, time.perf_counter()
         while True:
             for m in ep.micro_batches:
                 oracle.ep_share_forward(m.x_f32, m.eid, ep.W13_f32, ep.W2_f32)
             reps += 1
-            if _t.perf_counter() - t0 >= args.cpu_seconds:
+            if time.perf_counter() - t0 >= args.cpu_seconds:
                 break
-        el = _t.perf_counter() - t0
-        cpu = {"value": round(rows * reps / el, 1), "unit": "rows/s", "cores": len(os.sched_getaffinity(0)),
-               "kind": "oracle", "sample": f"both micro-batches, {reps} repetitions, {el:.1f} s"}
+        el = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(rows * reps / el, 1), "unit": "rows/s", "cores": _blas_threads(),
+                               "kind": "oracle", "sample": f"both micro-batches, {reps} repetitions, {el:.1f} s"}
+    return out, ep
+
+
+def _bench_ep_share(args):
+    """The EP share as its own bench line (rows/s of the two-stream schedule),
+    with the CU-masked split sweep."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    core, ep = _ep_share_core(args, torch, dev, cu_split=True, cpu=not args.no_cpu_baseline)
+    t_d = core["overlap"]["T_D_two_streams_ms"]
     out = {
         "metric": "EP-share two-micro-batch expert layer rows/s (permute + SwiGLU grouped GEMM + unpermute)",
-        "value": round(rows / (t_d * 1e-3), 1),
+        "value": core["rows/s_two_streams"],
         "unit": "rows/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "settle_ms": args.settle_ms,
-        "ms_per_step": round(t_d, 5),
+        "ms_per_step": t_d,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (Dirichlet(0.5) expert shares, 8 source ranks, N(0,1) rows, N(0,0.02) weights)",
-        "config": {"workload": "ep_share_bf16", "rows_per_micro_batch": ep.R, "micro_batches": 2,
-                   "E_local": ep.E_local, "H": ep.H, "I": ep.I,
-                   "counts": [m.counts.tolist() for m in ep.micro_batches]},
-        "overlap": {"T_A_gemm_ms": round(t_a, 4), "T_B_permute_unpermute_ms": round(t_b, 4),
-                    "T_C_serial_ms": round(t_c, 4), "T_D_two_streams_ms": round(t_d, 4),
-                    "hidden_fraction": round(1 - (t_d - t_a) / t_b, 4), "speedup_serial_over_overlap": round(t_c / t_d, 4),
-                    "gemm_TFLOP/s_alone": round(flops / (t_a * 1e-3) / 1e12, 1),
-                    "gemm_TFLOP/s_in_overlap": round(flops / (t_d * 1e-3) / 1e12, 1),
-                    "cu_split": split},
-        "fused_schedule": {"T_F_ms": round(t_f, 4), "rows/s": round(rows / (t_f * 1e-3), 1),
-                           "speedup_over_two_streams": round(t_d / t_f, 4),
-                           "what": "metadata-only permute, GEMM1 reading rows through perm, GEMM2 storing rows at "
-                                   "their arrival positions (unit weights); one stream"},
-        "cpu_baseline": cpu,
+        "config": dict(workload="ep_share_bf16", **core["config"],
+                       counts=[m.counts.tolist() for m in ep.micro_batches]),
+        "overlap": core["overlap"],
+        "fused_schedule": dict(core["fused_schedule"], **{"rows/s": core["rows/s_fused"]}),
+        "roofline": core["roofline"],
+        "cpu_baseline": core.get("cpu_baseline"),
         "device": torch.cuda.get_device_name(dev),
     }
     print(json.dumps(out), flush=True)
@@ -789,27 +953,58 @@ def _blas_threads():
         return len(os.sched_getaffinity(0))
 
 
-def _cpu_baseline(w, min_seconds):
-    """The fp64 oracle (as it stands) on the host: full-layer forwards until min_seconds pass."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def _cpu_baseline(w, min_seconds, one_core_seconds=5.0, one_core_tokens=256):
+    """The fp64 oracle (as it stands) on the host: full-layer forwards until
+    min_seconds pass, with the BLAS threads it uses; then a one-thread run on the
+    first `one_core_tokens` tokens. Also the oracle's rate in GFLOP/s (the
+    grouped GEMM's 6*K*H*I and the router's 2*H*E per token)."""
     import oracle
 
     threads = _blas_threads()
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.forward(w.x_f32, w.W_gate_f32, w.W13_f32, w.W2_f32, w.K, w.renorm, bias=w.bias)
-        reps += 1
-        if time.perf_counter() - t0 >= min_seconds:
-            break
-    el = time.perf_counter() - t0
-    return {
-        "value": round(w.n * reps / el, 1),
+    flop_per_token = 6.0 * w.K * w.H * w.I + 2.0 * w.H * w.E
+
+    def run(x, secs):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.forward(x, w.W_gate_f32, w.W13_f32, w.W2_f32, w.K, w.renorm, bias=w.bias)
+            reps += 1
+            if time.perf_counter() - t0 >= secs:
+                return reps, time.perf_counter() - t0
+
+    reps, el = run(w.x_f32, min_seconds)
+    tps = w.n * reps / el
+    out = {
+        "value": round(tps, 1),
         "unit": "tokens/s",
         "cores": int(threads),
         "kind": "oracle",
         "sample": f"the full {w.n}-token layer forward (fp64 numpy, OpenBLAS), {reps} repetitions, {el:.1f} s",
-        "cpu": platform.processor() or platform.machine(),
+        "GFLOP/s": round(tps * flop_per_token / 1e9, 2),
+        "cpu": _cpu_model(),
+        "visible_cores": len(os.sched_getaffinity(0)),
     }
+    try:
+        from threadpoolctl import threadpool_limits
+
+        m = min(one_core_tokens, w.n)
+        with threadpool_limits(limits=1):
+            r1, e1 = run(w.x_f32[:m], one_core_seconds)
+        t1 = m * r1 / e1
+        out["one_core"] = {"value": round(t1, 1), "unit": "tokens/s", "GFLOP/s": round(t1 * flop_per_token / 1e9, 2),
+                           "sample": f"first {m} tokens, 1 BLAS thread, {r1} repetitions, {e1:.1f} s"}
+    except Exception as e:  # noqa: BLE001
+        out["one_core"] = {"error": str(e)}
+    return out
 
 
 if __name__ == "__main__":

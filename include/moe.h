@@ -91,6 +91,12 @@ const char* moe_status_string(moe_status s);
 /* Library version as major*10000 + minor*100 + patch. */
 int moe_version(void);
 
+/* Properties of the current HIP device that the roofline figures are derived
+ * from: compute units, peak shader clock (kHz), peak memory clock (kHz) and
+ * memory bus width (bits), from hipDeviceGetAttribute. Any pointer may be
+ * NULL. Returns MOE_EHIP when a query fails. */
+moe_status moe_device_info(int* compute_units, int* sclk_khz, int* mem_clk_khz, int* mem_bus_bits);
+
 /* ---------------------------------------------------------------------------
  * moe_route — router GEMM, softmax and top-K (Algorithm 2 steps 1-3; the
  * OlmoeTopKRouter source of the same section: F.linear, softmax, topk, and

@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     MOE_BF16,
     MOE_F32,
     MoEError,
+    device_info,
     load_library,
     moe_backward,
     moe_backward_workspace_size,

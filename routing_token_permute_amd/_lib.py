@@ -31,6 +31,7 @@ _SZ = ctypes.c_size_t
 SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [_I]),
     "moe_version": (_I, []),
+    "moe_device_info": (_I, [_VP, _VP, _VP, _VP]),
     "moe_route": (_I, [_VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP]),
     "moe_permute_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_permute": (_I, [_VP, _VP, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
@@ -114,6 +115,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
 
 def status_string(code: int) -> str:
     return load_library().moe_status_string(code).decode()
+
+
+def device_info() -> dict:
+    """Compute units, peak shader clock and memory clock/bus of the current device."""
+    lib = load_library()
+    vals = [ctypes.c_int(0) for _ in range(4)]
+    _check(lib.moe_device_info(*[ctypes.byref(v) for v in vals]), "moe_device_info")
+    return dict(compute_units=vals[0].value, sclk_khz=vals[1].value, mem_clk_khz=vals[2].value,
+                mem_bus_bits=vals[3].value)
 
 
 def _check(code: int, what: str):

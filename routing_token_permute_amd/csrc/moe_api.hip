@@ -274,6 +274,21 @@ const char* moe_status_string(moe_status s) {
 
 int moe_version(void) { return 100; }
 
+moe_status moe_device_info(int* compute_units, int* sclk_khz, int* mem_clk_khz, int* mem_bus_bits) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_EHIP;
+  const struct {
+    int* out;
+    hipDeviceAttribute_t attr;
+  } q[] = {{compute_units, hipDeviceAttributeMultiprocessorCount},
+           {sclk_khz, hipDeviceAttributeClockRate},
+           {mem_clk_khz, hipDeviceAttributeMemoryClockRate},
+           {mem_bus_bits, hipDeviceAttributeMemoryBusWidth}};
+  for (const auto& e : q)
+    if (e.out != nullptr && hipDeviceGetAttribute(e.out, e.attr, dev) != hipSuccess) return MOE_EHIP;
+  return MOE_OK;
+}
+
 moe_status moe_route(const void* x, const void* W_gate, const float* bias, int n, int H, int E, int K, int renorm,
                      moe_dtype dt, float* logits, int32_t* topk_ids, float* topk_w, hipStream_t stream) {
   if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
