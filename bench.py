@@ -841,6 +841,7 @@ def _bench_fp8(args):
     ms = _time_region(step, args.steps, torch)
     wall = time.perf_counter() - t0
     spread = _pcts(_time_each(step, max(args.steps, 10), torch))
+    _warm(step_bf16, args.warmup, torch, args.settle_ms)
     ms_bf16 = _time_region(step_bf16, args.steps, torch)
     logits, ids, wts = moe.moe_route(x, Wg, None, K, w.renorm)
     meta = moe.moe_permute(ids, None, E)

@@ -163,7 +163,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
 #pragma unroll
     for (int j = 0; j < REG; ++j) {
       const int r = (int)(wave_u * REG + j);
-      dma16(src[j] + (r < A_REG ? ka : kb), base + j * 1024);
+      // Decode-sized tiles read each weight tile once: stream it (nt).
+      if (BM < 256 && r >= A_REG)
+        dma16_stream(src[j] + kb, base + j * 1024);
+      else
+        dma16(src[j] + (r < A_REG ? ka : kb), base + j * 1024);
     }
   };
   auto issue_first = [&]() {
