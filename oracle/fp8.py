@@ -24,6 +24,23 @@ Readings (also listed with the design notes):
     fp32 division), ties to the code with an even mantissa, magnitudes beyond
     448 saturated to 448 (they can only arise from the rounding of w / s).
   * Dequantized weight: decode(code) * s, exact in fp64.
+
+FP8 activations (the dispatch payload of §8.4: "FP8 data + per-token scale",
+with the receive buffer consumed by the FP8 GEMM directly) and the token-group
+padding of "0. goin" §2.1 (the quantized dispatcher pads each expert's group
+of rows to a multiple of 16 for FP8 so that a quantized grouped GEMM sees
+aligned groups). Readings:
+  * Scale of token row i: s_i = amax_h |x[i, h]| / 448 in fp32, 1 for an
+    all-zero row; codes as for the weights (nearest E4M3 of fp32 x / s_i).
+    Each token is quantized once; its K copies in the receive buffer share
+    the codes and the scale.
+  * Receive buffer: expert-major rows in Algorithm 2's I_e order (ascending
+    flat pair index), expert e's group starting at the padded offset
+    P[e] = sum_{e' < e} 16 * ceil(n_e' / 16); the padding rows hold code 0
+    and scale 0 (they contribute nothing and their outputs are never read).
+  * The layer on FP8 activations: routing on the original activations (the
+    router is not part of the dispatch payload), experts on the dequantized
+    rows decode(code) * s_i and the dequantized FP8 weights.
 """
 
 from __future__ import annotations
@@ -111,3 +128,70 @@ def forward_fp8(x, W_gate, W13_codes, s13, W2_codes, s2, K: int, renorm: bool, b
     W13 = dequantize_columns(W13_codes, s13)
     W2 = dequantize_columns(W2_codes, s2)
     return moe_oracle.forward(x, W_gate, W13, W2, K, renorm, bias=bias, **kw)
+
+
+TOKEN_GROUP = 16  # rows per padded expert group for FP8 ("0. goin" §2.1)
+
+
+def quantize_rows(X) -> tuple:
+    """Per-token FP8 of the rows of X (n, H): (codes (n, H) uint8, scales (n,) float32)."""
+    X32 = np.asarray(X, dtype=np.float32)
+    amax = np.max(np.abs(X32), axis=1) if X32.shape[1] else np.zeros(X32.shape[0], np.float32)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    q = (X32 / scale[:, None]).astype(np.float32)  # one rounded fp32 division per element
+    return e4m3_encode(q), scale
+
+
+def dequantize_rows(codes, scale) -> np.ndarray:
+    """X'[i, h] = decode(codes[i, h]) * scale[i] in fp64."""
+    return e4m3_decode(codes) * np.asarray(scale, dtype=np.float64)[:, None]
+
+
+def padded_offsets(counts, group: int = TOKEN_GROUP) -> np.ndarray:
+    """Start of each expert's padded group: P[0] = 0, P[e+1] = P[e] + group * ceil(n_e / group)."""
+    c = np.asarray(counts, dtype=np.int64)
+    out = np.zeros(c.size + 1, dtype=np.int64)
+    out[1:] = np.cumsum((c + group - 1) // group * group)
+    return out
+
+
+def dispatch_fp8(x, e_top, E: int, group: int = TOKEN_GROUP) -> dict:
+    """The FP8 receive buffer of one GPU's experts.
+
+    Returns dict(codes (R_pad, H) uint8, scales (R_pad,) float32, offsets (E+1)
+    padded group starts, perm (R_pad,) flat pair index i*K + k of each row or -1
+    for padding, inv (nK,) padded row of each pair, counts (E,)), where R_pad =
+    offsets[E].
+    """
+    e_top = np.asarray(e_top)
+    n, K = e_top.shape
+    codes_tok, s_tok = quantize_rows(x)
+    counts = moe_oracle.expert_counts(e_top, E)
+    offs = moe_oracle.offsets_from_counts(counts)
+    perm, _ = moe_oracle.permutation(e_top, E)
+    P = padded_offsets(counts, group)
+    R = int(P[-1])
+    H = np.asarray(x).shape[1]
+    codes = np.zeros((R, H), dtype=np.uint8)
+    scales = np.zeros(R, dtype=np.float32)
+    perm_p = np.full(R, -1, dtype=np.int64)
+    inv_p = np.zeros(n * K, dtype=np.int64)
+    for e in range(E):
+        seg = perm[offs[e] : offs[e + 1]]  # I_e in ascending flat order
+        rows = P[e] + np.arange(seg.size)
+        codes[rows] = codes_tok[seg // K]
+        scales[rows] = s_tok[seg // K]
+        perm_p[rows] = seg
+        inv_p[seg] = rows
+    return dict(codes=codes, scales=scales, offsets=P, perm=perm_p, inv=inv_p, counts=counts)
+
+
+def forward_fp8a(x, W_gate, W13_codes, s13, W2_codes, s2, K: int, renorm: bool, bias=None, routing_logits_f32=None):
+    """Algorithm 2 with FP8 activations and FP8 weights: routed on x, the experts
+    run on the dequantized per-token FP8 rows and the dequantized weights (fp64)."""
+    if routing_logits_f32 is None:
+        routing_logits_f32 = moe_oracle.round_to_f32(moe_oracle.router_logits(x, W_gate, bias))
+    codes, scales = quantize_rows(x)
+    x_deq = dequantize_rows(codes, scales)
+    return moe_oracle.forward(x_deq, W_gate, dequantize_columns(W13_codes, s13), dequantize_columns(W2_codes, s2),
+                              K, renorm, bias=bias, routing_logits_f32=routing_logits_f32)

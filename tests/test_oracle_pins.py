@@ -764,3 +764,128 @@ def test_e4m3_encode_matches_nearest_search():
                           2.0 ** rng.uniform(-12, 9, 2000)])
     pts = np.concatenate([pts, -pts]).astype(np.float32).astype(np.float64)
     np.testing.assert_array_equal(f.e4m3_encode(pts), brute.e4m3_encode_by_search(pts))
+
+
+# ---------------------------------------------------------------------------
+# FP8 activations: per-token scales and the padded FP8 receive buffer
+# ---------------------------------------------------------------------------
+
+
+def test_quantize_rows_per_token_scale_exact_grid_and_search():
+    """Per-token FP8: a row on the scaled E4M3 grid with amax 448 * 2^j quantizes exactly (scale 2^j, codes round
+    trip); a zero row gets scale 1 and code 0; codes equal the nearest-value search of fp32 x / s; quantizing the
+    rows equals quantizing the columns of the transpose; the error stays within half a code gap at the top of the
+    range (2^-4 of the row's amax)."""
+    f = oracle.fp8
+    t = f.e4m3_decode_table()[:0x7F]
+    rng = np.random.default_rng(31)
+    exact = rng.choice(np.concatenate([t, -t]), size=(6, 40))
+    exact[:, 0] = 448.0
+    exact *= 2.0 ** np.arange(-3, 3)[:, None]
+    codes, s = f.quantize_rows(exact.astype(np.float32))
+    np.testing.assert_array_equal(s, (2.0 ** np.arange(-3, 3)).astype(np.float32))
+    np.testing.assert_array_equal(f.dequantize_rows(codes, s), exact)
+    z_codes, z_s = f.quantize_rows(np.zeros((2, 8), np.float32))
+    assert (z_codes == 0).all() and (z_s == 1.0).all()
+    X = (rng.standard_normal((30, 64)) * rng.uniform(0.01, 5, (30, 1))).astype(np.float32)
+    codes, s = f.quantize_rows(X)
+    amax = np.max(np.abs(X), axis=1)
+    assert (s == (amax / np.float32(448)).astype(np.float32)).all()
+    q = (X / s[:, None]).astype(np.float32).astype(np.float64)
+    np.testing.assert_array_equal(codes, brute.e4m3_encode_by_search(q))
+    c_cols, s_cols = f.quantize_columns(X.T[None])  # columns of X^T are the rows of X
+    np.testing.assert_array_equal(c_cols[0], codes)
+    np.testing.assert_array_equal(s_cols[0], s)
+    assert np.all(np.abs(f.dequantize_rows(codes, s) - X) <= amax[:, None] * 2.0**-4 * 1.0000001)
+
+
+def test_padded_offsets_token_groups():
+    """Groups of 16 rows: the worked case counts (3, 0, 16, 17, 1) -> starts (0, 16, 16, 32, 64, 80); every group
+    is a multiple of 16, holds its rows, and pads fewer than 16; an empty expert takes no rows."""
+    f = oracle.fp8
+    np.testing.assert_array_equal(f.padded_offsets([3, 0, 16, 17, 1]), [0, 16, 16, 32, 64, 80])
+    rng = np.random.default_rng(5)
+    c = rng.integers(0, 70, size=40)
+    c[::7] = 0
+    P = f.padded_offsets(c)
+    g = np.diff(P)
+    assert P[0] == 0 and (g % 16 == 0).all() and (g >= c).all() and (g - c < 16).all() and (g[c == 0] == 0).all()
+
+
+def test_dispatch_fp8_receive_buffer():
+    """The FP8 receive buffer: each (token, slot) pair appears once, at its expert's padded group in ascending
+    flat order (the unpadded permutation shifted by the group starts); its row holds the token's codes and
+    scale; padding rows hold code 0, scale 0 and perm -1; inv and perm are inverse on the real rows."""
+    f = oracle.fp8
+    w = make_layer(70, 32, 16, 8, 3, dtype="bf16", seed=9)
+    L = oracle.round_to_f32(oracle.router_logits(w.x_f32, w.W_gate_f32))
+    e_top, _, _ = oracle.route_from_logits(L, w.K, False)
+    d = f.dispatch_fp8(w.x_f32, e_top, w.E)
+    codes_tok, s_tok = f.quantize_rows(w.x_f32)
+    perm, _ = oracle.permutation(e_top, w.E)
+    offs = oracle.offsets_from_counts(oracle.expert_counts(e_top, w.E))
+    P = d["offsets"]
+    assert d["codes"].shape == (P[-1], w.H)
+    real = d["perm"] >= 0
+    assert real.sum() == w.n * w.K
+    for e in range(w.E):
+        seg = perm[offs[e] : offs[e + 1]]
+        np.testing.assert_array_equal(d["perm"][P[e] : P[e] + seg.size], seg)
+        assert (d["perm"][P[e] + seg.size : P[e + 1]] == -1).all()
+    np.testing.assert_array_equal(d["perm"][d["inv"]], np.arange(w.n * w.K))
+    np.testing.assert_array_equal(d["codes"][real], codes_tok[d["perm"][real] // w.K])
+    np.testing.assert_array_equal(d["scales"][real], s_tok[d["perm"][real] // w.K])
+    assert (d["codes"][~real] == 0).all() and (d["scales"][~real] == 0).all()
+
+
+def test_forward_fp8a_exact_activations_and_error():
+    """With activations already on each row's scaled FP8 grid, the FP8-activation layer equals the FP8-weight
+    layer (no activation quantization error); for random activations it stays within the quantization error."""
+    f = oracle.fp8
+    w = make_layer(24, 32, 16, 4, 2, dtype="f32", seed=12)
+    c13, s13 = f.quantize_columns(w.W13_f32)
+    c2, s2 = f.quantize_columns(w.W2_f32)
+    t = f.e4m3_decode_table()[:0x7F]
+    rng = np.random.default_rng(4)
+    xg = rng.choice(np.concatenate([t, -t]), size=(w.n, w.H))
+    xg[:, 0] = 448.0
+    xg = (xg * 2.0**-9).astype(np.float32)  # scale 2^-9 per row, exact
+    a = f.forward_fp8a(xg, w.W_gate_f32, c13, s13, c2, s2, w.K, w.renorm)
+    b = f.forward_fp8(xg, w.W_gate_f32, c13, s13, c2, s2, w.K, w.renorm)
+    np.testing.assert_allclose(a["y"], b["y"], rtol=0, atol=1e-15)
+    a = f.forward_fp8a(w.x_f32, w.W_gate_f32, c13, s13, c2, s2, w.K, w.renorm)
+    b = f.forward_fp8(w.x_f32, w.W_gate_f32, c13, s13, c2, s2, w.K, w.renorm)
+    assert (a["e_top"] == b["e_top"]).all()  # routing stays on the unquantized activations
+    rel = np.linalg.norm(a["y"] - b["y"]) / np.linalg.norm(b["y"])
+    assert 1e-4 < rel < 0.1
+
+
+def test_planted_fp8_activation_mistakes_are_caught(monkeypatch):
+    f = oracle.fp8
+    orig_q, orig_pad, orig_disp = f.quantize_rows, f.padded_offsets, f.dispatch_fp8
+
+    # 1. One scale for the whole matrix instead of one per token.
+    def quantize_global(X):
+        X32 = np.asarray(X, dtype=np.float32)
+        s = np.float32(np.max(np.abs(X32)) / np.float32(448))
+        return f.e4m3_encode((X32 / s).astype(np.float32)), np.full(X32.shape[0], s, np.float32)
+
+    monkeypatch.setattr(f, "quantize_rows", quantize_global)
+    assert not _pins_pass(test_quantize_rows_per_token_scale_exact_grid_and_search)
+    monkeypatch.undo()
+
+    # 2. Groups padded to 8 rows.
+    monkeypatch.setattr(f, "padded_offsets", lambda c, group=8: orig_pad(c, 8))
+    assert not _pins_pass(test_padded_offsets_token_groups)
+    monkeypatch.undo()
+
+    # 3. Padding rows given scale 1.
+    def dispatch_pad_scale_one(x, e_top, E, group=16):
+        d = orig_disp(x, e_top, E, group)
+        d["scales"] = np.where(d["perm"] < 0, np.float32(1), d["scales"]).astype(np.float32)
+        return d
+
+    monkeypatch.setattr(f, "dispatch_fp8", dispatch_pad_scale_one)
+    assert not _pins_pass(test_dispatch_fp8_receive_buffer)
+    monkeypatch.undo()
+    assert f.quantize_rows is orig_q
