@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 METRIC = "MoE layer fwd tokens/s + grouped-GEMM TFLOP/s (% bf16 peak), OLMoE n=4096"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
 
 
 def _parse():
@@ -41,7 +42,7 @@ def _parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="olmoe_bf16",
                    choices=["olmoe_bf16", "olmoe_skewed_bf16", "decode_bf16", "ep_share_bf16", "olmoe_train_bf16",
-                            "decode_fp8", "olmoe_fp8"])
+                            "decode_fp8", "olmoe_fp8", "decode_fp8a", "olmoe_fp8a"])
     p.add_argument("--stage-reps", type=int, default=20)
     p.add_argument("--settle-ms", type=float, default=300.0,
                    help="after the warmup steps, keep running untimed steps until this much wall time has passed "
@@ -459,7 +460,7 @@ def main():
     if args.workload == "olmoe_train_bf16":
         _bench_train(args)
         return
-    if args.workload in ("decode_fp8", "olmoe_fp8"):
+    if args.workload in ("decode_fp8", "olmoe_fp8", "decode_fp8a", "olmoe_fp8a"):
         _bench_fp8(args)
         return
     dev = torch.device("cuda:0")
@@ -810,14 +811,17 @@ def _bench_fp8(args):
     """The layer with FP8 E4M3 expert weights (per-column fp32 scales, quantized
     on the device before timing) on the decode (n=32) or OLMoE (n=4096) batch:
     tokens/s, the FP8 GEMMs' bandwidth against their weight bytes, and the bf16
-    layer on the same inputs for comparison."""
+    layer on the same inputs for comparison. The *_fp8a workloads also carry the
+    activations as per-token FP8 (moe_forward_fp8a: padded FP8 receive buffer,
+    FP8 x FP8 GEMM1)."""
     import torch
 
     import routing_token_permute_amd as moe
     from workloads import make_config
 
     dev = torch.device("cuda:0")
-    base = "decode_bf16" if args.workload == "decode_fp8" else "olmoe_bf16"
+    base = "decode_bf16" if args.workload.startswith("decode") else "olmoe_bf16"
+    act8 = args.workload.endswith("fp8a")
     w = make_config(base)
     n, H, I, E, K = w.n, w.H, w.I, w.E, w.K  # noqa: E741
 
@@ -830,8 +834,13 @@ def _bench_fp8(args):
     y = torch.empty((n, H), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(moe.moe_forward_workspace_size(n, H, I, E, K, torch.bfloat16), dtype=torch.uint8, device=dev)
 
+    ws8 = torch.empty(moe.moe_forward_fp8a_workspace_size(n, H, I, E, K), dtype=torch.uint8, device=dev)
+
     def step():
-        moe.moe_forward_fp8(x, Wg, q13, s13, q2, s2, K, w.renorm, y=y, ws=ws)
+        if act8:
+            moe.moe_forward_fp8a(x, Wg, q13, s13, q2, s2, K, w.renorm, y=y, ws=ws8)
+        else:
+            moe.moe_forward_fp8(x, Wg, q13, s13, q2, s2, K, w.renorm, y=y, ws=ws)
 
     def step_bf16():
         moe.moe_forward(x, Wg, W13, W2, K, w.renorm, y=y, ws=ws)
@@ -856,26 +865,45 @@ def _bench_fp8(args):
         "gemm2_fp8": _time_region_graph(lambda: moe.moe_expert_w2_fp8(h, meta["offsets"], q2, s2, Y_perm=Yp), R, torch),
     }
     nk = n * K
+    if act8:  # the FP8 dispatch and the FP8 x FP8 GEMM1 on the padded receive buffer
+        codes_tok, s_tok = moe.moe_quantize_rows_fp8(x)
+        d8 = moe.moe_dispatch_fp8(meta, codes_tok, s_tok, K)
+        h8 = moe.moe_expert_w13_swiglu_fp8a(d8["x_q"], d8["x_scale"], d8["offsets_padded"], q13, s13)
+        torch.cuda.synchronize()
+        rpad = int(d8["offsets_padded"][-1].item())
+        st["quantize_rows_fp8"] = _time_region_graph(lambda: moe.moe_quantize_rows_fp8(x, codes=codes_tok, scales=s_tok),
+                                                     R, torch)
+        st["dispatch_fp8"] = _time_region_graph(lambda: moe.moe_dispatch_fp8(meta, codes_tok, s_tok, K, out=d8), R, torch)
+        st["gemm1_swiglu_fp8a"] = _time_region_graph(
+            lambda: moe.moe_expert_w13_swiglu_fp8a(d8["x_q"], d8["x_scale"], d8["offsets_padded"], q13, s13, h=h8),
+            R, torch)
     bytes_ = {  # algorithmic: activations once, FP8 codes and scales of the hit experts once, outputs once
         "gemm1_swiglu_fp8": nk * H * 2 + hit * (2 * I * H + 2 * I * 4) + nk * I * 2 + nk * 4,
         "gemm2_fp8": nk * I * 2 + hit * (H * I + H * 4) + nk * H * 2,
     }
     flops = {"gemm1_swiglu_fp8": 2.0 * nk * H * 2 * I, "gemm2_fp8": 2.0 * nk * I * H}
+    if act8:
+        bytes_["quantize_rows_fp8"] = n * H * 2 + n * H + n * 4
+        bytes_["dispatch_fp8"] = nk * H + rpad * H + rpad * 8 + nk * 4
+        bytes_["gemm1_swiglu_fp8a"] = rpad * (H + 4) + hit * (2 * I * H + 2 * I * 4) + rpad * I * 2
+        flops["gemm1_swiglu_fp8a"] = 2.0 * nk * H * 2 * I
     stages = {}
     for k, v in st.items():
         gbs = bytes_[k] / (v * 1e-3) / 1e9
-        stages[k] = {"ms": round(v, 5), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBPS, 4),
-                     "TFLOP/s": round(flops[k] / (v * 1e-3) / 1e12, 1)}
-    dom = "gemm1_swiglu_fp8"
-    if args.workload == "decode_fp8":
-        roof = {"kernel": "gemm_w8_kernel<GATED=true, GATHER=true> (GEMM1 + SwiGLU, FP8 weights)", "bound": "hbm",
-                "achieved": stages[dom]["GB/s"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+        stages[k] = {"ms": round(v, 5), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBPS, 4)}
+        if k in flops:
+            stages[k]["TFLOP/s"] = round(flops[k] / (v * 1e-3) / 1e12, 1)
+    dom = "gemm1_swiglu_fp8a" if act8 else "gemm1_swiglu_fp8"
+    kname = ("gemm_f8f8_kernel (GEMM1 + SwiGLU, FP8 activations x FP8 weights, FP8 MFMA 32x32x64)" if act8 else
+             "gemm_w8_kernel<GATED=true, GATHER=true> (GEMM1 + SwiGLU, FP8 weights)")
+    if base == "decode_bf16":
+        roof = {"kernel": kname, "bound": "hbm", "achieved": stages[dom]["GB/s"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": stages[dom]["frac_hbm"], "traffic": None}
     else:
         tf = stages[dom]["TFLOP/s"]
-        roof = {"kernel": "gemm_w8_kernel<GATED=true, GATHER=true> (GEMM1 + SwiGLU, FP8 weights)", "bound": "mfma",
-                "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                "traffic": None}
+        peak = PEAK_FP8_TFLOPS if act8 else PEAK_BF16_TFLOPS  # FP8 x FP8 products run on the FP8 MFMA
+        roof = {"kernel": kname, "bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
+                "frac": round(tf / peak, 4), "traffic": None}
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -894,7 +922,8 @@ def _bench_fp8(args):
                "sample": f"fp64 layer on the dequantized FP8 weights, first {m} tokens, {reps} repetitions, {el:.1f} s "
                          f"(weight quantization not timed)"}
     out = {
-        "metric": f"MoE layer fwd tokens/s with FP8 E4M3 expert weights, {base.split('_')[0]} n={n}",
+        "metric": (f"MoE layer fwd tokens/s with FP8 E4M3 expert weights"
+                   f"{' and per-token FP8 activations' if act8 else ''}, {base.split('_')[0]} n={n}"),
         "value": round(n / (ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -908,7 +937,7 @@ def _bench_fp8(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 activations, fp8 e4m3 weights",
+        "dtype": "fp8 e4m3 activations (per-token scales) and weights" if act8 else "bf16 activations, fp8 e4m3 weights",
         "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights quantized per output column; OLMoE layer shapes)",
         "config": {"workload": args.workload, "n": n, "H": H, "I": I, "E": E, "K": K, "renorm": bool(w.renorm)},
         "stages": stages,

@@ -522,6 +522,64 @@ moe_status moe_forward_fp8(const void* x, const void* W_gate, const float* bias,
                            int renorm, moe_dtype dt, void* y, float* logits_out, int32_t* topk_ids_out,
                            float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * FP8 activations. "大模型系统中的通算融合" §8.4 lists MoE dispatch with FP8
+ * data and a per-token scale, the receive buffer feeding the FP8 GEMM directly;
+ * "0. goin" §2.1 pads each expert's group of rows to a multiple of 16 for FP8.
+ *
+ * moe_quantize_rows_fp8 — per-token FP8: scales[i] = max_h |x[i,h]| / 448 in
+ * fp32 (1 for a zero row), codes[i,h] = the nearest OCP E4M3 code of the fp32
+ * quotient x[i,h] / scales[i] (ties to even, saturating at 448).
+ *   x (n, H) dtype; codes (n, H) uint8 out; scales (n) fp32 out; H a multiple
+ *   of 8.
+ *
+ * moe_fp8_padded_rows — rows of the padded receive buffer for n tokens, top-K:
+ * n*K + 15 * min(E, n*K) (each expert that receives rows pads fewer than 16).
+ *
+ * moe_dispatch_fp8 — the padded FP8 receive buffer from moe_permute's counts,
+ * offsets and perm (ep = 1) and the per-token codes/scales: expert e's rows,
+ * in moe_permute's order, start at offsets_padded[e] = sum over e' < e of
+ * 16 * ceil(counts[e'] / 16); a token's K copies share its codes and scale;
+ * padding rows hold code 0, scale 0 and perm_padded -1. Rows past
+ * offsets_padded[E] are not written.
+ *   counts (E), offsets (E+1), perm (n*K) int32 from moe_permute;
+ *   codes_tok (n, H) uint8 and s_tok (n) fp32 from moe_quantize_rows_fp8;
+ *   offsets_padded (E+1) int32 out; x_q (rows, H) uint8 out and x_scale (rows)
+ *   fp32 out with rows = moe_fp8_padded_rows(n, E, K); perm_padded (rows)
+ *   int32 out: the flat pair index i*K+k of each row or -1; inv_padded (n*K)
+ *   int32 out: the buffer row of each pair. H a multiple of 16.
+ *
+ * moe_expert_w13_swiglu_fp8a — Algorithm 2 step 8 on the receive buffer:
+ * h[r] = SiLU(g) * u with [g | u] = (x_scale[r] * decode(x_q[r])) .
+ * (s13 * decode(W13q)) over expert e's columns, on the gfx950 FP8 MFMA with
+ * fp32 accumulation; h (rows_max, I) bf16 out (padding rows give 0; rows past
+ * offsets_padded[E] are not written). W13q (E, 2I, H) and s13 (E, 2I) as from
+ * moe_quantize_fp8 on W13; rows_max = moe_fp8_padded_rows(n, E, K) (an upper
+ * bound; the tile map comes from offsets_padded). H a multiple of 128.
+ *
+ * moe_forward_fp8a — the layer with FP8 activations and FP8 weights: moe_route
+ * on x (bf16), the moe_permute metadata, moe_quantize_rows_fp8,
+ * moe_dispatch_fp8, moe_expert_w13_swiglu_fp8a, moe_expert_w2_fp8 (bf16 h,
+ * FP8 W2) over the padded rows, and moe_unpermute_combine through inv_padded.
+ * Arguments as moe_forward_fp8 (dt must be MOE_BF16, H a multiple of 128);
+ * ws of at least moe_forward_fp8a_workspace_size(n, H, I, E, K) bytes.
+ * ------------------------------------------------------------------------- */
+moe_status moe_quantize_rows_fp8(const void* x, int n, int H, moe_dtype dt, uint8_t* codes, float* scales,
+                                 hipStream_t stream);
+size_t moe_fp8_padded_rows(int n, int E, int K);
+moe_status moe_dispatch_fp8(const int32_t* counts, const int32_t* offsets, const int32_t* perm, int n, int E, int K,
+                            const uint8_t* codes_tok, const float* s_tok, int H, int32_t* offsets_padded,
+                            uint8_t* x_q, float* x_scale, int32_t* perm_padded, int32_t* inv_padded,
+                            hipStream_t stream);
+moe_status moe_expert_w13_swiglu_fp8a(const uint8_t* x_q, const float* x_scale, const int32_t* offsets_padded,
+                                      int rows_max, const uint8_t* W13q, const float* s13, int E, int H, int I,
+                                      void* h, hipStream_t stream);
+size_t moe_forward_fp8a_workspace_size(int n, int H, int I, int E, int K);
+moe_status moe_forward_fp8a(const void* x, const void* W_gate, const float* bias, const uint8_t* W13q,
+                            const float* s13, const uint8_t* W2q, const float* s2, int n, int H, int I, int E, int K,
+                            int renorm, moe_dtype dt, void* y, float* logits_out, int32_t* topk_ids_out,
+                            float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

@@ -79,6 +79,15 @@ SIGNATURES = {
         _I,
         [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     ),
+    "moe_quantize_rows_fp8": (_I, [_VP, _I, _I, _I, _VP, _VP, _VP]),
+    "moe_fp8_padded_rows": (_SZ, [_I, _I, _I]),
+    "moe_dispatch_fp8": (_I, [_VP, _VP, _VP, _I, _I, _I, _VP, _VP, _I, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "moe_expert_w13_swiglu_fp8a": (_I, [_VP, _VP, _VP, _I, _VP, _VP, _I, _I, _I, _VP, _VP]),
+    "moe_forward_fp8a_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
+    "moe_forward_fp8a": (
+        _I,
+        [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    ),
     "moe_backward_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "moe_backward": (
         _I,
@@ -841,3 +850,110 @@ def moe_forward_fp8(x, W_gate, W13q, s13, W2q, s2, K: int, renorm: bool, bias=No
     )
     _check(code, "moe_forward_fp8")
     return (y, *extra) if routing_out else y
+
+
+# ---------------------------------------------------------------------------
+# FP8 activations
+# ---------------------------------------------------------------------------
+
+
+@_on_stream
+def moe_quantize_rows_fp8(x, codes=None, scales=None, stream=None):
+    """Per-token FP8 E4M3 codes (n, H) uint8 and fp32 scales (n,) of x (n, H)."""
+    lib = load_library()
+    n, H = x.shape
+    dev = x.device
+    _need(x, "x", (n, H))
+    codes = _empty((n, H), torch.uint8, dev) if codes is None else codes
+    scales = _empty((n,), torch.float32, dev) if scales is None else scales
+    _need(codes, "codes", (n, H), torch.uint8, dev)
+    _need(scales, "scales", (n,), torch.float32, dev)
+    _check(lib.moe_quantize_rows_fp8(_ptr(x), n, H, _dt(x), _ptr(codes), _ptr(scales), _stream(dev, stream)),
+           "moe_quantize_rows_fp8")
+    return codes, scales
+
+
+def moe_fp8_padded_rows(n: int, E: int, K: int) -> int:
+    return int(load_library().moe_fp8_padded_rows(n, E, K))
+
+
+@_on_stream
+def moe_dispatch_fp8(meta, codes_tok, s_tok, K: int, out=None, stream=None):
+    """The padded FP8 receive buffer from moe_permute's metadata (`meta`: counts, offsets, perm) and the
+    per-token codes/scales. Returns dict(offsets_padded, x_q, x_scale, perm_padded, inv_padded)."""
+    lib = load_library()
+    n, H = codes_tok.shape
+    E = meta["counts"].shape[0]
+    dev = codes_tok.device
+    R = moe_fp8_padded_rows(n, E, K)
+    _need(codes_tok, "codes_tok", (n, H), torch.uint8, dev)
+    _need(s_tok, "s_tok", (n,), torch.float32, dev)
+    for k, shp in (("counts", (E,)), ("offsets", (E + 1,)), ("perm", (n * K,))):
+        _need(meta[k], k, shp, torch.int32, dev)
+    shapes = dict(offsets_padded=((E + 1,), torch.int32), x_q=((R, H), torch.uint8), x_scale=((R,), torch.float32),
+                  perm_padded=((R,), torch.int32), inv_padded=((n * K,), torch.int32))
+    out = dict(out or {})
+    for k, (shp, dt) in shapes.items():
+        out.setdefault(k, _empty(shp, dt, dev))
+        _need(out[k], k, shp, dt, dev)
+    _check(lib.moe_dispatch_fp8(_ptr(meta["counts"]), _ptr(meta["offsets"]), _ptr(meta["perm"]), n, E, K,
+                                _ptr(codes_tok), _ptr(s_tok), H, *[_ptr(out[k]) for k in shapes],
+                                _stream(dev, stream)), "moe_dispatch_fp8")
+    return out
+
+
+@_on_stream
+def moe_expert_w13_swiglu_fp8a(x_q, x_scale, offsets_padded, W13q, s13, h=None, stream=None):
+    """GEMM1 + SwiGLU on the FP8 receive buffer with FP8 W13 codes; h (rows, I) bf16."""
+    lib = load_library()
+    R, H = x_q.shape
+    E, N, _ = W13q.shape
+    I = N // 2  # noqa: E741
+    dev = x_q.device
+    _need(x_q, "x_q", (R, H), torch.uint8, dev)
+    _need(x_scale, "x_scale", (R,), torch.float32, dev)
+    _need(offsets_padded, "offsets_padded", (E + 1,), torch.int32, dev)
+    _need(W13q, "W13q", (E, N, H), torch.uint8, dev)
+    _need(s13, "s13", (E, N), torch.float32, dev)
+    h = _empty((R, I), torch.bfloat16, dev) if h is None else h
+    _need(h, "h", (R, I), torch.bfloat16, dev)
+    _check(lib.moe_expert_w13_swiglu_fp8a(_ptr(x_q), _ptr(x_scale), _ptr(offsets_padded), R, _ptr(W13q), _ptr(s13),
+                                          E, H, I, _ptr(h), _stream(dev, stream)), "moe_expert_w13_swiglu_fp8a")
+    return h
+
+
+def moe_forward_fp8a_workspace_size(n, H, I, E, K) -> int:  # noqa: E741
+    return int(load_library().moe_forward_fp8a_workspace_size(n, H, I, E, K))
+
+
+@_on_stream
+def moe_forward_fp8a(x, W_gate, W13q, s13, W2q, s2, K: int, renorm: bool, bias=None, y=None, ws=None,
+                     routing_out=False, stream=None):
+    """The layer with FP8 activations and FP8 weights. Returns y, or (y, logits, topk_ids, topk_w, counts)."""
+    lib = load_library()
+    n, H = x.shape
+    E = W_gate.shape[1]
+    I = W13q.shape[1] // 2  # noqa: E741
+    dev = x.device
+    _need(x, "x", (n, H), torch.bfloat16)
+    _need(W_gate, "W_gate", (H, E), torch.bfloat16, dev)
+    _need(W13q, "W13q", (E, 2 * I, H), torch.uint8, dev)
+    _need(s13, "s13", (E, 2 * I), torch.float32, dev)
+    _need(W2q, "W2q", (E, H, I), torch.uint8, dev)
+    _need(s2, "s2", (E, H), torch.float32, dev)
+    if bias is not None:
+        _need(bias, "bias", (E,), torch.float32, dev)
+    y = _empty((n, H), torch.bfloat16, dev) if y is None else y
+    _need(y, "y", (n, H), torch.bfloat16, dev)
+    ws = _workspace(lib.moe_forward_fp8a_workspace_size(n, H, I, E, K), dev, ws)
+    extra = [None] * 4
+    if routing_out:
+        extra = [_empty((n, E), torch.float32, dev), _empty((n, K), torch.int32, dev),
+                 _empty((n, K), torch.float32, dev), _empty((E,), torch.int32, dev)]
+    code = lib.moe_forward_fp8a(
+        _ptr(x), _ptr(W_gate), _ptr(bias), _ptr(W13q), _ptr(s13), _ptr(W2q), _ptr(s2), n, H, I, E, K,
+        int(bool(renorm)), MOE_BF16, _ptr(y), *[_ptr(t) for t in extra], _ptr(ws), ws.numel(), _stream(dev, stream),
+    )
+    _check(code, "moe_forward_fp8a")
+    return (y, *extra) if routing_out else y
+

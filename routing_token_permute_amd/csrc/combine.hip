@@ -22,10 +22,10 @@ constexpr int kBatch = 8;
 template <bool BF16, bool ADD = false>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y, const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w, int n, int row_vecs, int K,
-                                                      void* __restrict__ y, const float* __restrict__ add) {
+                                                      void* __restrict__ y, const float* __restrict__ add,
+                                                      int total) {
   constexpr int EPV = BF16 ? 8 : 4;  // elements per 16-byte vector
   const int i = blockIdx.x;
-  const int total = n * K;
   const u32x4_t* Yv = (const u32x4_t*)Y;
   for (int c = threadIdx.x; c < row_vecs; c += 256) {
     float acc[EPV];
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y
       for (int j = 0; j < kBatch; ++j) {
         const int k = k0 + j;
         const int r = (k < K) ? inv[(size_t)i * K + k] : -1;
-        ok[j] = (unsigned)r < (unsigned)total;  // rows out of range add nothing
+        ok[j] = (unsigned)r < (unsigned)total;  // rows outside Y (total rows) add nothing
         wk[j] = ok[j] ? ((w != nullptr) ? w[(size_t)i * K + k] : 1.f) : 0.f;
         v[j] = ok[j] ? Yv[(size_t)r * row_vecs + c] : u32x4_t{0u, 0u, 0u, 0u};
       }
@@ -137,14 +137,19 @@ hipError_t launch_sum_slots(const void* Y_tok, int n, int H, int K, moe_dtype dt
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const void* Y_perm, const int32_t* inv, const float* topk_w, int n, int H, int K,
-                          moe_dtype dt, void* y, hipStream_t s) {
+hipError_t launch_combine_rows(const void* Y_perm, int y_rows, const int32_t* inv, const float* topk_w, int n, int H,
+                               int K, moe_dtype dt, void* y, hipStream_t s) {
   if (n == 0) return hipSuccess;
   if (dt == MOE_BF16)
-    combine_kernel<true><<<n, 256, 0, s>>>(Y_perm, inv, topk_w, n, H / 8, K, y, nullptr);
+    combine_kernel<true><<<n, 256, 0, s>>>(Y_perm, inv, topk_w, n, H / 8, K, y, nullptr, y_rows);
   else
-    combine_kernel<false><<<n, 256, 0, s>>>(Y_perm, inv, topk_w, n, H / 4, K, y, nullptr);
+    combine_kernel<false><<<n, 256, 0, s>>>(Y_perm, inv, topk_w, n, H / 4, K, y, nullptr, y_rows);
   return hipGetLastError();
+}
+
+hipError_t launch_combine(const void* Y_perm, const int32_t* inv, const float* topk_w, int n, int H, int K,
+                          moe_dtype dt, void* y, hipStream_t s) {
+  return launch_combine_rows(Y_perm, n * K, inv, topk_w, n, H, K, dt, y, s);
 }
 
 hipError_t launch_dispatch_backward(const void* dX_perm, const int32_t* inv, const float* add, int n, int H, int K,
@@ -153,9 +158,9 @@ hipError_t launch_dispatch_backward(const void* dX_perm, const int32_t* inv, con
   // Unit weights: each token sums the gradients of its K rows (slot order).
   if (add == nullptr) return launch_combine(dX_perm, inv, nullptr, n, H, K, dt, dx, s);
   if (dt == MOE_BF16)
-    combine_kernel<true, true><<<n, 256, 0, s>>>(dX_perm, inv, nullptr, n, H / 8, K, dx, add);
+    combine_kernel<true, true><<<n, 256, 0, s>>>(dX_perm, inv, nullptr, n, H / 8, K, dx, add, n * K);
   else
-    combine_kernel<false, true><<<n, 256, 0, s>>>(dX_perm, inv, nullptr, n, H / 4, K, dx, add);
+    combine_kernel<false, true><<<n, 256, 0, s>>>(dX_perm, inv, nullptr, n, H / 4, K, dx, add, n * K);
   return hipGetLastError();
 }
 

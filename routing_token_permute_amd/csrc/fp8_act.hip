@@ -1,0 +1,426 @@
+// FP8 activations: the per-token FP8 dispatch payload and the FP8 x FP8 first
+// expert GEMM that consumes it.
+//
+// "大模型系统中的通算融合" §8.4 lists MoE dispatch with FP8 data and a
+// per-token (or per-block) scale, and asks that the receive buffer feed the
+// FP8 GEMM directly rather than being widened back to bf16 first; "0. goin"
+// §2.1 notes that the quantized token dispatcher pads each expert's group of
+// rows to a multiple of 16 (FP8) so that the quantized grouped GEMM sees
+// aligned groups. Here, on one GPU:
+//
+//   * quantize_rows_kernel: one fp32 scale per token row, s = amax / 448 (1
+//     for a zero row), and the nearest E4M3 code of each fp32 quotient x / s.
+//   * dispatch_fp8_kernel: the receive buffer, expert-major in Algorithm 2's
+//     I_e order (the order moe_permute produced), each expert's group starting
+//     at a multiple of 16 rows; a token's K copies share its codes and scale;
+//     padding rows hold code 0 and scale 0.
+//   * gemm_f8f8_kernel (GEMM1 + SwiGLU of Algorithm 2 step 8 in §1.2 of
+//     "MoE 分布式推理基础（基于 vLLM）"): FP8 activation rows times FP8 weight
+//     columns (moe_quantize_fp8's column-major codes), both K-contiguous, on
+//     the gfx950 FP8 MFMA 32x32x64 with fp32 accumulation; the row and column
+//     scales multiply the accumulators in the epilogue before SiLU * up.
+#include <algorithm>
+
+#include "gemm_tiles.hpp"
+
+namespace moe {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Per-token quantization: one wave per row, 8 elements per lane per step.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const void* __restrict__ x, int n, int H,
+                                                            uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n) return;
+  auto load8 = [&](int h0, float* v) {
+    if constexpr (BF16) {
+      const u32x4_t u = *(const u32x4_t*)((const uint16_t*)x + (size_t)row * H + h0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] = __uint_as_float(u[q] << 16);
+        v[2 * q + 1] = __uint_as_float(u[q] & 0xFFFF0000u);
+      }
+    } else {
+      const f32x4_t a = *(const f32x4_t*)((const float*)x + (size_t)row * H + h0);
+      const f32x4_t b = *(const f32x4_t*)((const float*)x + (size_t)row * H + h0 + 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[q] = a[q];
+        v[4 + q] = b[q];
+      }
+    }
+  };
+  float m = 0.f;
+  for (int h0 = lane * 8; h0 < H; h0 += 512) {
+    float v[8];
+    load8(h0, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  const float s = m > 0.f ? m / 448.f : 1.f;
+  if (lane == 0) scales[row] = s;
+  for (int h0 = lane * 8; h0 < H; h0 += 512) {
+    float v[8];
+    load8(h0, v);
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j >> 2] |= e4m3_nearest(v[j] / s) << (8 * (j & 3));
+    *(u32x2_t*)(codes + (size_t)row * H + h0) = u32x2_t{w[0], w[1]};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The padded FP8 receive buffer. Every block rebuilds the padded group starts
+// P[e] from the counts in LDS; one wave then fills one buffer row.
+// ---------------------------------------------------------------------------
+constexpr int kTokenGroup = 16;
+
+__global__ __launch_bounds__(256) void dispatch_fp8_kernel(const int32_t* __restrict__ counts,
+                                                           const int32_t* __restrict__ offsets,
+                                                           const int32_t* __restrict__ perm, int E, int K, int nk,
+                                                           int rows_max, const uint8_t* __restrict__ codes_tok,
+                                                           const float* __restrict__ s_tok, int H,
+                                                           int32_t* __restrict__ offsets_padded,
+                                                           uint8_t* __restrict__ x_q, float* __restrict__ x_scale,
+                                                           int32_t* __restrict__ perm_padded,
+                                                           int32_t* __restrict__ inv_padded) {
+  __shared__ int P[kMaxExperts + 1];
+  __shared__ int cnt[kMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (wave == 0) {
+    int carry = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      const int e = e0 + lane;
+      const int c = e < E ? max(0, counts[e]) : 0;
+      const int g = (c + kTokenGroup - 1) / kTokenGroup * kTokenGroup;
+      int incl = g;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      if (e < E) {
+        P[e] = carry + incl - g;
+        cnt[e] = c;
+      }
+      carry += __shfl(incl, 63);
+    }
+    if (lane == 0) P[E] = carry;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int e = tid; e <= E; e += 256) offsets_padded[e] = P[e];
+  const int q = blockIdx.x * 4 + wave;  // buffer row
+  if (q >= rows_max || q >= P[E]) return;
+  // Expert of row q: the last e with P[e] <= q (groups are non-empty only for hit experts).
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (P[mid] <= q)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  const int e = lo, j = q - P[e];
+  uint8_t* dst = x_q + (size_t)q * H;
+  if (j < cnt[e]) {
+    const int f = perm[offsets[e] + j];
+    const bool ok = (unsigned)f < (unsigned)nk;
+    const int tok = ok ? f / K : 0;
+    const uint8_t* src = codes_tok + (size_t)tok * H;
+    for (int h0 = lane * 16; h0 < H; h0 += 1024) *(u32x4_t*)(dst + h0) = *(const u32x4_t*)(src + h0);
+    if (lane == 0) {
+      x_scale[q] = ok ? s_tok[tok] : 0.f;
+      perm_padded[q] = ok ? f : -1;
+      if (ok) inv_padded[f] = q;
+    }
+  } else {
+    for (int h0 = lane * 16; h0 < H; h0 += 1024) *(u32x4_t*)(dst + h0) = u32x4_t{0u, 0u, 0u, 0u};
+    if (lane == 0) {
+      x_scale[q] = 0.f;
+      perm_padded[q] = -1;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// GEMM1 + SwiGLU with FP8 activations and FP8 weights.
+// ---------------------------------------------------------------------------
+// Stages advance K by 128 codes: BM activation rows and 256 weight columns
+// (128 gate columns then the matching 128 up columns) of 128 bytes each.
+// Chunk c (16 bytes) of a row r sits at slot c ^ ((r / 2) % 8): the 16 lanes of
+// one quarter of a wave-wide ds_read_b128 (16 rows at one chunk) then hit 16
+// distinct groups of four banks.
+constexpr int kF8BK = 128;
+constexpr int kF8Row = kF8BK;  // bytes per staged row (A and B alike)
+constexpr int kF8MaxStages = 3;
+
+template <int BM>
+struct F8Cfg {
+  static constexpr int A_BYTES = BM * kF8Row;
+  static constexpr int B_BYTES = BN * kF8Row;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int FIT = (160 * 1024) / STAGE;
+  static constexpr int NSTAGE = FIT > kF8MaxStages ? kF8MaxStages : FIT;
+  static constexpr int LDS_BYTES = NSTAGE * STAGE;
+  static constexpr int REGIONS = STAGE / 1024;
+  static constexpr int A_REG = A_BYTES / 1024;
+};
+
+__device__ __forceinline__ int f8_swz(int row) { return (row >> 1) & 7; }
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// WM x WN waves split the BM x 256 tile; each wave owns (BM / WM) rows and
+// (256 / WN) staged columns, half gate and half the matching up columns, as
+// 32 x 32 MFMA tiles.
+template <int BM, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
+    const uint8_t* __restrict__ Aq, const float* __restrict__ a_scale, const int32_t* __restrict__ offsets, int E,
+    int rows, int Kdim, const uint8_t* __restrict__ Bq, long long b_stride, const float* __restrict__ b_scale,
+    int N, int I, uint16_t* __restrict__ C, int NB, int n_slots) {
+  using Cfg = F8Cfg<BM>;
+  constexpr int STAGE = Cfg::STAGE, NSTAGE = Cfg::NSTAGE, A_BYTES = Cfg::A_BYTES, A_REG = Cfg::A_REG;
+  constexpr int NW = WM * WN;
+  constexpr int MT = BM / WM / 32;        // 32-row MFMA tiles per wave
+  constexpr int NTH = BN / WN / 32 / 2;   // 32-column gate tiles per wave (as many up tiles)
+  constexpr int REG = Cfg::REGIONS / NW;  // 1 KB DMA regions per wave per stage
+  static_assert(MT >= 1 && NTH >= 1 && REG * NW == Cfg::REGIONS, "tile split");
+  static_assert(NSTAGE >= 2 && (NSTAGE - 2) * REG <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) char smem_raw[Cfg::LDS_BYTES];
+  lds_char_t* smem = (lds_char_t*)smem_raw;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int nk = Kdim / kF8BK;
+
+  int slot_id = blockIdx.x;
+  auto next_tile = [&]() {
+    Tile t{0, 0, 0, 0, false};
+    while (slot_id < n_slots && !t.valid) {
+      t = find_tile<BM>(offsets, E, rows, NB, xcd_remap(slot_id, n_slots));
+      slot_id += gridDim.x;
+    }
+    return t;
+  };
+
+  // DMA: region r of a stage holds 8 rows of 128 bytes; the first A_REG
+  // regions hold A, the rest B. Lane L writes row L / 8, slot L % 8, and so
+  // fetches chunk (L % 8) ^ swz(row) of that row.
+  const uint8_t* src[REG];
+  auto set_sources = [&](const Tile& t) {
+    const int mrows = t.r1 - t.r0;
+#pragma unroll
+    for (int j = 0; j < REG; ++j) {
+      const int r = wave * REG + j;
+      const int rr = (r < A_REG ? r : r - A_REG) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ f8_swz(rr);
+      if (r < A_REG) {
+        const int arow = t.r0 + min(rr, mrows - 1);
+        src[j] = Aq + (size_t)arow * Kdim + c * 16;
+      } else {
+        int gc = t.nb * (BN / 2) + (rr & (BN / 2 - 1));
+        if (gc >= I) gc = 0;
+        const int code_row = rr < BN / 2 ? gc : I + gc;
+        src[j] = Bq + (size_t)t.e * b_stride + (size_t)code_row * Kdim + c * 16;
+      }
+    }
+  };
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  auto issue = [&](int kt, int stage) {
+    const uint32_t base = lds0 + stage * STAGE + (uint32_t)wave * REG * 1024;
+#pragma unroll
+    for (int j = 0; j < REG; ++j) dma16(src[j] + (size_t)kt * kF8BK, base + j * 1024);
+  };
+  auto issue_first = [&]() {
+#pragma unroll
+    for (int p = 0; p < NSTAGE - 1; ++p)
+      if (p < nk) issue(p, p);
+  };
+  auto wait_dma = [&](int stages) {
+    if (stages >= 2)
+      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(2 * REG) : "memory");
+    else if (stages == 1)
+      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(REG) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+  };
+
+  // Operands of k-substep ks (64 codes): lane l of a 32 x 32 tile reads row
+  // (l % 32), chunks 4 ks + 2 (l / 32) and the next. A and B use the same
+  // k arrangement, which is all the product needs.
+  const int a_row0 = wm * (BM / WM);
+  auto rd32 = [&](const lds_char_t* base, int row, int ks) {
+    const int c0 = 4 * ks + 2 * hi;
+    const int sw = f8_swz(row);
+    const u32x4_t lo = lds_read_b128(base + row * kF8Row + ((c0 ^ sw) << 4));
+    const u32x4_t up = lds_read_b128(base + row * kF8Row + (((c0 + 1) ^ sw) << 4));
+    return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
+  };
+  f32x16_t acc[MT][2 * NTH];
+  int vm = 0;  // 32-row MFMA tiles of this wave that hold a valid row
+  auto kstep = [&](int stage) {
+    const lds_char_t* As = smem + stage * STAGE;
+    const lds_char_t* Bs = As + A_BYTES;
+#pragma unroll 1
+    for (int ks = 0; ks < 2; ++ks) {
+      i32x8_t b[2 * NTH];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int nt = 0; nt < NTH; ++nt)
+          b[h * NTH + nt] = rd32(Bs, h * (BN / 2) + wn * (BN / 2 / WN) + nt * 32 + l32, ks);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (mt >= vm) continue;
+        const i32x8_t a = rd32(As, a_row0 + mt * 32 + l32, ks);
+#pragma unroll
+        for (int q = 0; q < 2 * NTH; ++q)
+          acc[mt][q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[q], a, acc[mt][q], 0, 0, 0, 127, 0, 127);
+      }
+    }
+  };
+
+  // Epilogue: weights first, so lane l of tile (mt, q) holds output row
+  // mt*32 + (l % 32) at the staged columns 8 (r / 4) + 4 (l / 32) + (r % 4),
+  // r = 0..15: four runs of four consecutive columns. Lanes l and l ^ 32
+  // swap runs so that each writes 8 consecutive bf16 values (16 bytes).
+  auto store_tile = [&](const Tile& t) {
+    const int mrows = t.r1 - t.r0;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int row = a_row0 + mt * 32 + l32;
+      const bool row_ok = mt < vm && row < mrows;
+      const float sa = row_ok ? a_scale[t.r0 + row] : 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NTH; ++nt) {
+        const int gcol0 = t.nb * (BN / 2) + wn * (BN / 2 / WN) + nt * 32;  // first h column of the tile
+        uint32_t pk[8];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float hv[2];
+#pragma unroll
+          for (int d = 0; d < 2; ++d) {
+            const int col = gcol0 + 8 * ((r + d) / 4) + 4 * hi + ((r + d) % 4);
+            const int cc = col < I ? col : 0;
+            const float sg = b_scale[(size_t)t.e * N + cc], su = b_scale[(size_t)t.e * N + I + cc];
+            hv[d] = swiglu_f32(acc[mt][nt][r + d] * sa * sg, acc[mt][NTH + nt][r + d] * sa * su);
+          }
+          pk[r / 2] = (uint32_t)f32_to_bf16(hv[0]) | ((uint32_t)f32_to_bf16(hv[1]) << 16);
+        }
+        // Runs q = 0..3 are pk[2q], pk[2q+1] (columns 8q + 4 hi .. +3). Of the
+        // runs 2p and 2p+1, lane half 0 keeps run 2p and receives the
+        // partner's run 2p (columns +4); lane half 1 keeps run 2p+1 and
+        // receives the partner's run 2p+1 (its first four columns).
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const uint32_t k0 = hi ? pk[4 * p + 2] : pk[4 * p], k1 = hi ? pk[4 * p + 3] : pk[4 * p + 1];
+          const uint32_t s0 = hi ? pk[4 * p] : pk[4 * p + 2], s1 = hi ? pk[4 * p + 1] : pk[4 * p + 3];
+          const uint32_t g0 = (uint32_t)__shfl_xor((int)s0, 32);
+          const uint32_t g1 = (uint32_t)__shfl_xor((int)s1, 32);
+          const int col = gcol0 + 16 * p + 8 * hi;
+          if (row_ok && col < I) {
+            const u32x4_t v = hi ? u32x4_t{g0, g1, k0, k1} : u32x4_t{k0, k1, g0, g1};
+            *(u32x4_t*)(C + (size_t)(t.r0 + row) * I + col) = v;
+          }
+        }
+      }
+    }
+  };
+
+  Tile t = next_tile();
+  if (!t.valid) return;
+  set_sources(t);
+  issue_first();
+  for (;;) {
+    const int mrows = __builtin_amdgcn_readfirstlane(t.r1 - t.r0);
+    vm = min(MT, max(0, (mrows - a_row0 + 31) / 32));
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int q = 0; q < 2 * NTH; ++q)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mt][q][r] = 0.f;
+    int slot = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_dma(min(NSTAGE - 2, nk - 1 - kt));
+      __syncthreads();
+      if (kt + NSTAGE - 1 < nk) issue(kt + NSTAGE - 1, slot == 0 ? NSTAGE - 1 : slot - 1);
+      if (vm > 0) kstep(slot);
+      slot = (slot == NSTAGE - 1) ? 0 : slot + 1;
+    }
+    __syncthreads();
+    const Tile nt_ = next_tile();
+    if (nt_.valid) {
+      set_sources(nt_);
+      issue_first();
+    }
+    store_tile(t);
+    if (!nt_.valid) break;
+    t = nt_;
+  }
+}
+
+constexpr int kF8BM = 256, kF8WM = 4, kF8WN = 4;
+constexpr int kF8SmallBM = 32, kF8SmallWM = 1, kF8SmallWN = 4;
+constexpr int kF8SmallRowsPerExpert = 64;
+
+template <int BM, int WM, int WN>
+void launch_f8f8_cfg(const uint8_t* Aq, const float* a_scale, const int32_t* offsets, int E, int rows, int H,
+                     const uint8_t* W13q, const float* s13, int I, void* h, hipStream_t s) {
+  const int NB = ceil_div(I, BN / 2);
+  const int n_slots = max_row_tiles(rows, E, BM) * NB;
+  const int grid = std::min(n_slots, stream_cu_count(s));
+  gemm_f8f8_kernel<BM, WM, WN><<<grid, 64 * WM * WN, 0, s>>>(Aq, a_scale, offsets, E, rows, H, W13q,
+                                                             (long long)2 * I * H, s13, 2 * I, I, (uint16_t*)h, NB,
+                                                             n_slots);
+}
+
+}  // namespace
+
+size_t fp8_padded_rows(int n, int E, int K) {
+  const long long nk = (long long)n * K;
+  return (size_t)(nk + (long long)std::min<long long>(E, nk) * (kTokenGroup - 1));
+}
+
+hipError_t launch_quantize_rows_fp8(const void* x, int n, int H, moe_dtype dt, uint8_t* codes, float* scales,
+                                    hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (dt == MOE_BF16)
+    quantize_rows_kernel<true><<<ceil_div(n, 4), 256, 0, s>>>(x, n, H, codes, scales);
+  else
+    quantize_rows_kernel<false><<<ceil_div(n, 4), 256, 0, s>>>(x, n, H, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_fp8(const int32_t* counts, const int32_t* offsets, const int32_t* perm, int n, int E,
+                               int K, const uint8_t* codes_tok, const float* s_tok, int H, int32_t* offsets_padded,
+                               uint8_t* x_q, float* x_scale, int32_t* perm_padded, int32_t* inv_padded,
+                               hipStream_t s) {
+  const int rows_max = (int)fp8_padded_rows(n, E, K);
+  const int blocks = std::max(1, ceil_div(rows_max, 4));
+  dispatch_fp8_kernel<<<blocks, 256, 0, s>>>(counts, offsets, perm, E, K, n * K, rows_max, codes_tok, s_tok, H,
+                                             offsets_padded, x_q, x_scale, perm_padded, inv_padded);
+  return hipGetLastError();
+}
+
+hipError_t launch_w13_swiglu_fp8a(const uint8_t* x_q, const float* x_scale, const int32_t* offsets_padded,
+                                  int rows_max, const uint8_t* W13q, const float* s13, int E, int H, int I, void* h,
+                                  hipStream_t s) {
+  if (rows_max == 0) return hipSuccess;
+  if ((long long)rows_max <= (long long)kF8SmallRowsPerExpert * E)
+    launch_f8f8_cfg<kF8SmallBM, kF8SmallWM, kF8SmallWN>(x_q, x_scale, offsets_padded, E, rows_max, H, W13q, s13, I,
+                                                         h, s);
+  else
+    launch_f8f8_cfg<kF8BM, kF8WM, kF8WN>(x_q, x_scale, offsets_padded, E, rows_max, H, W13q, s13, I, h, s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -333,29 +333,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_w8_kernel(
   }
 }
 
-// Nearest E4M3 code of x (ties to the even mantissa, magnitudes saturated at
-// 448; NaN is not expected), from the format: 1 sign, 4 exponent bits (bias
-// 7), 3 mantissa bits, subnormals m * 2^-9, largest finite 1.75 * 2^8.
-__device__ __forceinline__ uint32_t e4m3_nearest(float x) {
-  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  const float a = fminf(fabsf(x), 448.f);
-  uint32_t code;
-  if (a < 0.015625f) {  // below 2^-6: steps of 2^-9 (m = 8 is the smallest normal, code 8)
-    code = (uint32_t)rintf(a * 512.f);
-  } else {
-    const uint32_t b = __float_as_uint(a);
-    int ex = (int)(b >> 23) - 127 + 7;                             // biased E4M3 exponent, 1..15
-    const float f = __uint_as_float((b & 0x007FFFFFu) | 0x3F800000u);  // 1.m in [1, 2)
-    int m = (int)rintf((f - 1.f) * 8.f);                           // exact scaling, then RNE
-    if (m == 8) {
-      m = 0;
-      ++ex;
-    }
-    code = ((uint32_t)ex << 3) | (uint32_t)m;
-  }
-  return code == 0 ? 0u : (sign | code);
-}
-
 // One workgroup per (64 columns, expert): column amax over K, the scale, then
 // the codes, written column-major through an LDS transpose of 64 x 64 blocks.
 template <bool BF16>

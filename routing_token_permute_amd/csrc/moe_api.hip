@@ -81,6 +81,45 @@ ForwardLayout forward_layout(int n, int H, int I, int E, int K, moe_dtype dt) {
   return L;
 }
 
+// moe_forward_fp8a workspace, in order: routing, unpadded dispatch metadata,
+// the per-token FP8 rows, the padded FP8 receive buffer and its metadata, h
+// and Y_perm over the padded rows.
+struct Fp8aLayout {
+  size_t logits, ids, w, counts, offsets, offsets_p, splits, perm, inv, pscratch, codes_tok, s_tok, x_q, x_scale,
+      perm_p, inv_p, h, Y_perm, total;
+};
+
+Fp8aLayout fp8a_layout(int n, int H, int I, int E, int K) {
+  Fp8aLayout L{};
+  const size_t nk = (size_t)n * K, R = fp8_padded_rows(n, E, K);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes > 0 ? bytes : 1);
+    return at;
+  };
+  L.logits = take((size_t)n * E * 4);
+  L.ids = take(nk * 4);
+  L.w = take(nk * 4);
+  L.counts = take((size_t)E * 4);
+  L.offsets = take((size_t)(E + 1) * 4);
+  L.offsets_p = take((size_t)(E + 1) * 4);
+  L.splits = take(4);
+  L.perm = take(nk * 4);
+  L.inv = take(nk * 4);
+  L.pscratch = take(permute_ws(n, E, K));
+  L.codes_tok = take((size_t)n * H);
+  L.s_tok = take((size_t)n * 4);
+  L.x_q = take(R * H);
+  L.x_scale = take(R * 4);
+  L.perm_p = take(R * 4);
+  L.inv_p = take(nk * 4);
+  L.h = take(R * I * 2);
+  L.Y_perm = take(R * H * 2);
+  L.total = o;
+  return L;
+}
+
 // moe_forward_train workspace: what the forward uses but does not save.
 struct TrainLayout {
   size_t counts, splits, pscratch, total;
@@ -741,6 +780,111 @@ moe_status moe_forward_fp8(const void* x, const void* W_gate, const float* bias,
   e = launch_w2_fp8(base + L.h, offsets, n * K, W2q, s2, E, H, I, base + L.Y_perm, stream);
   if (e != hipSuccess) return MOE_EHIP;
   return from_hip(launch_combine(base + L.Y_perm, inv, w, n, H, K, dt, y, stream));
+}
+
+
+// ---------------------------------------------------------------------------
+// FP8 activations: per-token FP8 dispatch into a padded receive buffer and
+// the FP8 x FP8 first expert GEMM
+// ---------------------------------------------------------------------------
+
+size_t moe_fp8_padded_rows(int n, int E, int K) {
+  if (n < 0 || E < 1 || K < 1) return 0;
+  return fp8_padded_rows(n, E, K);
+}
+
+moe_status moe_quantize_rows_fp8(const void* x, int n, int H, moe_dtype dt, uint8_t* codes, float* scales,
+                                 hipStream_t stream) {
+  if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
+  if (n < 0 || !hidden_ok(H, dt) || H % 8 != 0) return MOE_EINVAL;  // eight elements per lane step
+  if (n == 0) return MOE_OK;
+  if (x == nullptr || codes == nullptr || scales == nullptr) return MOE_EINVAL;
+  if (!vec_ok({x, codes}) || !word_ok({scales})) return MOE_EINVAL;
+  return from_hip(launch_quantize_rows_fp8(x, n, H, dt, codes, scales, stream));
+}
+
+moe_status moe_dispatch_fp8(const int32_t* counts, const int32_t* offsets, const int32_t* perm, int n, int E, int K,
+                            const uint8_t* codes_tok, const float* s_tok, int H, int32_t* offsets_padded,
+                            uint8_t* x_q, float* x_scale, int32_t* perm_padded, int32_t* inv_padded,
+                            hipStream_t stream) {
+  if (n < 0 || !experts_ok(E, K) || H <= 0 || H > kMaxHidden || H % 16 != 0) return MOE_EINVAL;
+  if ((long long)n * K > INT32_MAX / 2) return MOE_EINVAL;
+  if (counts == nullptr || offsets == nullptr || offsets_padded == nullptr) return MOE_EINVAL;
+  if (n > 0 && (perm == nullptr || codes_tok == nullptr || s_tok == nullptr || x_q == nullptr ||
+                x_scale == nullptr || perm_padded == nullptr || inv_padded == nullptr))
+    return MOE_EINVAL;
+  if (!vec_ok({codes_tok, x_q}) || !word_ok({counts, offsets, perm, s_tok, offsets_padded, x_scale, perm_padded,
+                                             inv_padded}))
+    return MOE_EINVAL;
+  return from_hip(launch_dispatch_fp8(counts, offsets, perm, n, E, K, codes_tok, s_tok, H, offsets_padded, x_q,
+                                      x_scale, perm_padded, inv_padded, stream));
+}
+
+moe_status moe_expert_w13_swiglu_fp8a(const uint8_t* x_q, const float* x_scale, const int32_t* offsets_padded,
+                                      int rows_max, const uint8_t* W13q, const float* s13, int E, int H, int I,
+                                      void* h, hipStream_t stream) {
+  if (rows_max < 0 || E < 1 || E > kMaxExperts || !hidden_ok(H, MOE_BF16) || H % 128 != 0 ||
+      !hidden_ok(I, MOE_BF16))
+    return MOE_EINVAL;
+  if (rows_max == 0) return MOE_OK;
+  if (x_q == nullptr || x_scale == nullptr || offsets_padded == nullptr || W13q == nullptr || s13 == nullptr ||
+      h == nullptr)
+    return MOE_EINVAL;
+  if (!vec_ok({x_q, W13q, s13, h}) || !word_ok({x_scale, offsets_padded})) return MOE_EINVAL;
+  return from_hip(launch_w13_swiglu_fp8a(x_q, x_scale, offsets_padded, rows_max, W13q, s13, E, H, I, h, stream));
+}
+
+size_t moe_forward_fp8a_workspace_size(int n, int H, int I, int E, int K) {
+  if (n < 0 || H < 1 || I < 1 || E < 1 || K < 1) return 0;
+  return fp8a_layout(n, H, I, E, K).total;
+}
+
+moe_status moe_forward_fp8a(const void* x, const void* W_gate, const float* bias, const uint8_t* W13q,
+                            const float* s13, const uint8_t* W2q, const float* s2, int n, int H, int I, int E, int K,
+                            int renorm, moe_dtype dt, void* y, float* logits_out, int32_t* topk_ids_out,
+                            float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
+  if (dt != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (n < 0 || !experts_ok(E, K) || !hidden_ok(H, dt) || H % 128 != 0 || !hidden_ok(I, dt)) return MOE_EINVAL;
+  if ((long long)n * K > INT32_MAX / 2) return MOE_EINVAL;
+  if (n > 0 && (x == nullptr || W_gate == nullptr || W13q == nullptr || s13 == nullptr || W2q == nullptr ||
+                s2 == nullptr || y == nullptr))
+    return MOE_EINVAL;
+  if (!vec_ok({x, W_gate, W13q, s13, W2q, s2, y, ws}) ||
+      !word_ok({bias, logits_out, topk_ids_out, topk_w_out, counts_out}))
+    return MOE_EINVAL;
+  if (n == 0)
+    return counts_out ? from_hip(launch_fill_zero(counts_out, (size_t)E * 4, stream)) : MOE_OK;
+  const Fp8aLayout L = fp8a_layout(n, H, I, E, K);
+  if (ws == nullptr || ws_bytes < L.total) return MOE_EWORKSPACE;
+  char* base = (char*)ws;
+  float* logits = logits_out ? logits_out : (float*)(base + L.logits);
+  int32_t* ids = topk_ids_out ? topk_ids_out : (int32_t*)(base + L.ids);
+  float* w = topk_w_out ? topk_w_out : (float*)(base + L.w);
+  int32_t* counts = counts_out ? counts_out : (int32_t*)(base + L.counts);
+  int32_t* offsets = (int32_t*)(base + L.offsets);
+  int32_t* offsets_p = (int32_t*)(base + L.offsets_p);
+  int32_t* perm = (int32_t*)(base + L.perm);
+  int32_t* inv = (int32_t*)(base + L.inv);
+  uint8_t* codes_tok = (uint8_t*)(base + L.codes_tok);
+  float* s_tok = (float*)(base + L.s_tok);
+  uint8_t* x_q = (uint8_t*)(base + L.x_q);
+  float* x_scale = (float*)(base + L.x_scale);
+  int32_t* perm_p = (int32_t*)(base + L.perm_p);
+  int32_t* inv_p = (int32_t*)(base + L.inv_p);
+  const int R = (int)fp8_padded_rows(n, E, K);
+  hipError_t e = launch_route(x, W_gate, bias, n, H, E, K, renorm, dt, logits, ids, w, stream);
+  if (e == hipSuccess)
+    e = launch_permute(ids, nullptr, n, H, E, K, 1, dt, counts, offsets, (int32_t*)(base + L.splits), perm, inv,
+                       nullptr, (int32_t*)(base + L.pscratch), stream);
+  if (e == hipSuccess) e = launch_quantize_rows_fp8(x, n, H, dt, codes_tok, s_tok, stream);
+  if (e == hipSuccess)
+    e = launch_dispatch_fp8(counts, offsets, perm, n, E, K, codes_tok, s_tok, H, offsets_p, x_q, x_scale, perm_p,
+                            inv_p, stream);
+  if (e == hipSuccess) e = launch_w13_swiglu_fp8a(x_q, x_scale, offsets_p, R, W13q, s13, E, H, I, base + L.h, stream);
+  if (e == hipSuccess) e = launch_w2_fp8(base + L.h, offsets_p, R, W2q, s2, E, H, I, base + L.Y_perm, stream);
+  if (e == hipSuccess) e = launch_combine_rows(base + L.Y_perm, R, inv_p, w, n, H, K, dt, y, stream);
+  return from_hip(e);
 }
 
 }  // extern "C"

@@ -69,6 +69,9 @@ hipError_t launch_w2_scatter(const void* h, const int32_t* offsets, int rows, co
 hipError_t launch_sum_slots(const void* Y_tok, int n, int H, int K, moe_dtype dt, void* y, hipStream_t s);
 hipError_t launch_combine(const void* Y_perm, const int32_t* inv, const float* topk_w, int n, int H, int K,
                           moe_dtype dt, void* y, hipStream_t s);
+// The same over a Y of y_rows rows (a padded buffer): inv entries in [0, y_rows) are gathered.
+hipError_t launch_combine_rows(const void* Y_perm, int y_rows, const int32_t* inv, const float* topk_w, int n, int H,
+                               int K, moe_dtype dt, void* y, hipStream_t s);
 
 // ---- backward ----
 
@@ -133,6 +136,24 @@ hipError_t launch_w13_swiglu_gather_fp8(const void* x, const int32_t* perm, int 
 hipError_t launch_w2_fp8(const void* h, const int32_t* offsets, int rows, const uint8_t* W2q, const float* s2, int E,
                          int H, int I, void* Y_perm, hipStream_t s);
 
+// ---- FP8 activations ----
+
+// Rows of the padded FP8 receive buffer for n tokens, top-K: n*K plus at most
+// 15 padding rows per expert that received rows.
+size_t fp8_padded_rows(int n, int E, int K);
+// codes (n, H) = nearest E4M3 codes of x / scales, scales (n) = row amax / 448 (1 for a zero row).
+hipError_t launch_quantize_rows_fp8(const void* x, int n, int H, moe_dtype dt, uint8_t* codes, float* scales,
+                                    hipStream_t s);
+// The padded receive buffer from moe_permute's counts, offsets and perm and the per-token codes/scales.
+hipError_t launch_dispatch_fp8(const int32_t* counts, const int32_t* offsets, const int32_t* perm, int n, int E,
+                               int K, const uint8_t* codes_tok, const float* s_tok, int H, int32_t* offsets_padded,
+                               uint8_t* x_q, float* x_scale, int32_t* perm_padded, int32_t* inv_padded,
+                               hipStream_t s);
+// GEMM1 + SwiGLU with FP8 activation rows (padded groups) and FP8 W13 codes (E, 2I, H).
+hipError_t launch_w13_swiglu_fp8a(const uint8_t* x_q, const float* x_scale, const int32_t* offsets_padded,
+                                  int rows_max, const uint8_t* W13q, const float* s13, int E, int H, int I, void* h,
+                                  hipStream_t s);
+
 }  // namespace moe
 
 // ---- device helpers ----
@@ -171,6 +192,29 @@ __device__ __forceinline__ float swiglu_f32(float g, float u) {
 // per lane); lane c of the group receives column c of those 4 rows.
 __device__ __forceinline__ bf16x4_t lds_read_tr16(const lds_char_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)p);
+}
+
+// Nearest E4M3 code of x (ties to the even mantissa, magnitudes saturated at
+// 448; NaN is not expected), from the format: 1 sign, 4 exponent bits (bias
+// 7), 3 mantissa bits, subnormals m * 2^-9, largest finite 1.75 * 2^8.
+__device__ __forceinline__ uint32_t e4m3_nearest(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fminf(fabsf(x), 448.f);
+  uint32_t code;
+  if (a < 0.015625f) {  // below 2^-6: steps of 2^-9 (m = 8 is the smallest normal, code 8)
+    code = (uint32_t)rintf(a * 512.f);
+  } else {
+    const uint32_t b = __float_as_uint(a);
+    int ex = (int)(b >> 23) - 127 + 7;                             // biased E4M3 exponent, 1..15
+    const float f = __uint_as_float((b & 0x007FFFFFu) | 0x3F800000u);  // 1.m in [1, 2)
+    int m = (int)rintf((f - 1.f) * 8.f);                           // exact scaling, then RNE
+    if (m == 8) {
+      m = 0;
+      ++ex;
+    }
+    code = ((uint32_t)ex << 3) | (uint32_t)m;
+  }
+  return code == 0 ? 0u : (sign | code);
 }
 
 __device__ __forceinline__ u32x4_t lds_read_b128(const lds_char_t* p) {
