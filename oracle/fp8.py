@@ -25,9 +25,9 @@ Readings (also listed with the design notes):
     448 saturated to 448 (they can only arise from the rounding of w / s).
   * Dequantized weight: decode(code) * s, exact in fp64.
 
-FP8 activations (the dispatch payload of §8.4: "FP8 data + per-token scale",
-with the receive buffer consumed by the FP8 GEMM directly) and the token-group
-padding of "0. goin" §2.1 (the quantized dispatcher pads each expert's group
+FP8 activations (the dispatch payload of §8.4: FP8 values that travel with a
+scale per token, in a receive buffer that the FP8 GEMM reads as it is) and the
+token-group padding of "0. goin" §2.1 (the quantized dispatcher pads each expert's group
 of rows to a multiple of 16 for FP8 so that a quantized grouped GEMM sees
 aligned groups). Readings:
   * Scale of token row i: s_i = amax_h |x[i, h]| / 448 in fp32, 1 for an

@@ -151,28 +151,30 @@ __global__ __launch_bounds__(256) void dispatch_fp8_kernel(const int32_t* __rest
 // ---------------------------------------------------------------------------
 // GEMM1 + SwiGLU with FP8 activations and FP8 weights.
 // ---------------------------------------------------------------------------
-// Stages advance K by 128 codes: BM activation rows and 256 weight columns
-// (128 gate columns then the matching 128 up columns) of 128 bytes each.
-// Chunk c (16 bytes) of a row r sits at slot c ^ ((r / 2) % 8): the 16 lanes of
-// one quarter of a wave-wide ds_read_b128 (16 rows at one chunk) then hit 16
-// distinct groups of four banks.
-constexpr int kF8BK = 128;
-constexpr int kF8Row = kF8BK;  // bytes per staged row (A and B alike)
-constexpr int kF8MaxStages = 3;
-
-template <int BM>
+// Stages advance K by BK codes (64 or 128): BM activation rows and 256
+// weight columns (128 gate columns then the matching 128 up columns) of BK
+// bytes each. Chunk c (16 bytes) of a row r sits at slot c ^ ((r / 2) % (BK /
+// 16)): the 16 lanes of one quarter of a wave-wide ds_read_b128 (16 rows at
+// one chunk) then run at the full LDS rate (for 64-byte rows this is the
+// bf16 tiles' A layout, measured conflict-free).
+template <int BM, int BK, int CAP>
 struct F8Cfg {
-  static constexpr int A_BYTES = BM * kF8Row;
-  static constexpr int B_BYTES = BN * kF8Row;
+  static_assert(BK == 64 || BK == 128, "k-step");
+  static constexpr int ROW = BK;               // bytes per staged row (A and B alike)
+  static constexpr int CPR = BK / 16;          // 16-byte chunks per row
+  static constexpr int ROWS_PER_REGION = 1024 / ROW;
+  static constexpr int A_BYTES = BM * ROW;
+  static constexpr int B_BYTES = BN * ROW;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int FIT = (160 * 1024) / STAGE;
-  static constexpr int NSTAGE = FIT > kF8MaxStages ? kF8MaxStages : FIT;
+  static constexpr int NSTAGE = FIT > CAP ? CAP : FIT;
   static constexpr int LDS_BYTES = NSTAGE * STAGE;
   static constexpr int REGIONS = STAGE / 1024;
   static constexpr int A_REG = A_BYTES / 1024;
 };
 
-__device__ __forceinline__ int f8_swz(int row) { return (row >> 1) & 7; }
+template <int BK>
+__device__ __forceinline__ int f8_swz(int row) { return (row >> 1) & (BK / 16 - 1); }
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -180,26 +182,27 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // WM x WN waves split the BM x 256 tile; each wave owns (BM / WM) rows and
 // (256 / WN) staged columns, half gate and half the matching up columns, as
 // 32 x 32 MFMA tiles.
-template <int BM, int WM, int WN>
+template <int BM, int BK, int CAP, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
     const uint8_t* __restrict__ Aq, const float* __restrict__ a_scale, const int32_t* __restrict__ offsets, int E,
     int rows, int Kdim, const uint8_t* __restrict__ Bq, long long b_stride, const float* __restrict__ b_scale,
     int N, int I, uint16_t* __restrict__ C, int NB, int n_slots) {
-  using Cfg = F8Cfg<BM>;
+  using Cfg = F8Cfg<BM, BK, CAP>;
   constexpr int STAGE = Cfg::STAGE, NSTAGE = Cfg::NSTAGE, A_BYTES = Cfg::A_BYTES, A_REG = Cfg::A_REG;
+  constexpr int ROW = Cfg::ROW, CPR = Cfg::CPR, RPR = Cfg::ROWS_PER_REGION;
   constexpr int NW = WM * WN;
   constexpr int MT = BM / WM / 32;        // 32-row MFMA tiles per wave
   constexpr int NTH = BN / WN / 32 / 2;   // 32-column gate tiles per wave (as many up tiles)
   constexpr int REG = Cfg::REGIONS / NW;  // 1 KB DMA regions per wave per stage
   static_assert(MT >= 1 && NTH >= 1 && REG * NW == Cfg::REGIONS, "tile split");
-  static_assert(NSTAGE >= 2 && (NSTAGE - 2) * REG <= 63, "vmcnt range");
+  static_assert(NSTAGE >= 2 && NSTAGE - 2 <= 2 && 2 * REG <= 63, "vmcnt range (wait_dma covers two later stages)");
   __shared__ __attribute__((aligned(16))) char smem_raw[Cfg::LDS_BYTES];
   lds_char_t* smem = (lds_char_t*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int nk = Kdim / kF8BK;
+  const int nk = Kdim / BK;
 
   int slot_id = blockIdx.x;
   auto next_tile = [&]() {
@@ -211,17 +214,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
     return t;
   };
 
-  // DMA: region r of a stage holds 8 rows of 128 bytes; the first A_REG
-  // regions hold A, the rest B. Lane L writes row L / 8, slot L % 8, and so
-  // fetches chunk (L % 8) ^ swz(row) of that row.
+  // DMA: region r of a stage holds RPR rows of BK bytes; the first A_REG
+  // regions hold A, the rest B. Lane L writes row L / CPR, slot L % CPR, and
+  // so fetches chunk (L % CPR) ^ swz(row) of that row.
   const uint8_t* src[REG];
   auto set_sources = [&](const Tile& t) {
     const int mrows = t.r1 - t.r0;
 #pragma unroll
     for (int j = 0; j < REG; ++j) {
       const int r = wave * REG + j;
-      const int rr = (r < A_REG ? r : r - A_REG) * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ f8_swz(rr);
+      const int rr = (r < A_REG ? r : r - A_REG) * RPR + lane / CPR;
+      const int c = (lane % CPR) ^ f8_swz<BK>(rr);
       if (r < A_REG) {
         const int arow = t.r0 + min(rr, mrows - 1);
         src[j] = Aq + (size_t)arow * Kdim + c * 16;
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
   auto issue = [&](int kt, int stage) {
     const uint32_t base = lds0 + stage * STAGE + (uint32_t)wave * REG * 1024;
 #pragma unroll
-    for (int j = 0; j < REG; ++j) dma16(src[j] + (size_t)kt * kF8BK, base + j * 1024);
+    for (int j = 0; j < REG; ++j) dma16(src[j] + (size_t)kt * BK, base + j * 1024);
   };
   auto issue_first = [&]() {
 #pragma unroll
@@ -259,9 +262,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
   const int a_row0 = wm * (BM / WM);
   auto rd32 = [&](const lds_char_t* base, int row, int ks) {
     const int c0 = 4 * ks + 2 * hi;
-    const int sw = f8_swz(row);
-    const u32x4_t lo = lds_read_b128(base + row * kF8Row + ((c0 ^ sw) << 4));
-    const u32x4_t up = lds_read_b128(base + row * kF8Row + (((c0 + 1) ^ sw) << 4));
+    const int sw = f8_swz<BK>(row);
+    const u32x4_t lo = lds_read_b128(base + row * ROW + ((c0 ^ sw) << 4));
+    const u32x4_t up = lds_read_b128(base + row * ROW + (((c0 + 1) ^ sw) << 4));
     return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
   };
   f32x16_t acc[MT][2 * NTH];
@@ -270,7 +273,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
     const lds_char_t* As = smem + stage * STAGE;
     const lds_char_t* Bs = As + A_BYTES;
 #pragma unroll 1
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < BK / 64; ++ks) {
       i32x8_t b[2 * NTH];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -290,10 +293,32 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
 
   // Epilogue: weights first, so lane l of tile (mt, q) holds output row
   // mt*32 + (l % 32) at the staged columns 8 (r / 4) + 4 (l / 32) + (r % 4),
-  // r = 0..15: four runs of four consecutive columns. Lanes l and l ^ 32
-  // swap runs so that each writes 8 consecutive bf16 values (16 bytes).
+  // r = 0..15: four runs of four consecutive columns. The column scales are
+  // folded into the accumulators first, one run at a time (every row tile of
+  // the wave shares them), so that few values are live at once; then the
+  // row scale and SwiGLU. Lanes l and l ^ 32 swap runs so that each writes 8
+  // consecutive bf16 values (16 bytes).
   auto store_tile = [&](const Tile& t) {
     const int mrows = t.r1 - t.r0;
+    const float* sc = b_scale + (size_t)t.e * N;
+#pragma unroll
+    for (int nt = 0; nt < NTH; ++nt) {
+      const int gcol0 = t.nb * (BN / 2) + wn * (BN / 2 / WN) + nt * 32;  // first h column of the tile
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = gcol0 + 8 * q + 4 * hi + j;
+          const int cc = col < I ? col : 0;
+          const float sg = sc[cc], su = sc[I + cc];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            acc[mt][nt][4 * q + j] *= sg;
+            acc[mt][NTH + nt][4 * q + j] *= su;
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int row = a_row0 + mt * 32 + l32;
@@ -305,15 +330,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
         uint32_t pk[8];
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          float hv[2];
-#pragma unroll
-          for (int d = 0; d < 2; ++d) {
-            const int col = gcol0 + 8 * ((r + d) / 4) + 4 * hi + ((r + d) % 4);
-            const int cc = col < I ? col : 0;
-            const float sg = b_scale[(size_t)t.e * N + cc], su = b_scale[(size_t)t.e * N + I + cc];
-            hv[d] = swiglu_f32(acc[mt][nt][r + d] * sa * sg, acc[mt][NTH + nt][r + d] * sa * su);
-          }
-          pk[r / 2] = (uint32_t)f32_to_bf16(hv[0]) | ((uint32_t)f32_to_bf16(hv[1]) << 16);
+          const float h0 = swiglu_f32(acc[mt][nt][r] * sa, acc[mt][NTH + nt][r] * sa);
+          const float h1 = swiglu_f32(acc[mt][nt][r + 1] * sa, acc[mt][NTH + nt][r + 1] * sa);
+          pk[r / 2] = (uint32_t)f32_to_bf16(h0) | ((uint32_t)f32_to_bf16(h1) << 16);
         }
         // Runs q = 0..3 are pk[2q], pk[2q+1] (columns 8q + 4 hi .. +3). Of the
         // runs 2p and 2p+1, lane half 0 keeps run 2p and receives the
@@ -368,17 +387,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
   }
 }
 
-constexpr int kF8BM = 256, kF8WM = 4, kF8WN = 4;
-constexpr int kF8SmallBM = 32, kF8SmallWM = 1, kF8SmallWN = 4;
+// Large batches: 256-row tiles, 16 waves, 64-code stages on a 4-deep ring
+// (32 KB each). Decode-like batches: 32-row tiles, 4 waves, 128-code stages on
+// a 3-deep ring (36 KB each), which keeps more weight bytes in flight.
+constexpr int kF8BM = 256, kF8BK = 64, kF8Cap = 4, kF8WM = 4, kF8WN = 4;
+constexpr int kF8SmallBM = 32, kF8SmallBK = 128, kF8SmallCap = 3, kF8SmallWM = 1, kF8SmallWN = 4;
 constexpr int kF8SmallRowsPerExpert = 64;
 
-template <int BM, int WM, int WN>
+template <int BM, int BK, int CAP, int WM, int WN>
 void launch_f8f8_cfg(const uint8_t* Aq, const float* a_scale, const int32_t* offsets, int E, int rows, int H,
                      const uint8_t* W13q, const float* s13, int I, void* h, hipStream_t s) {
   const int NB = ceil_div(I, BN / 2);
   const int n_slots = max_row_tiles(rows, E, BM) * NB;
   const int grid = std::min(n_slots, stream_cu_count(s));
-  gemm_f8f8_kernel<BM, WM, WN><<<grid, 64 * WM * WN, 0, s>>>(Aq, a_scale, offsets, E, rows, H, W13q,
+  gemm_f8f8_kernel<BM, BK, CAP, WM, WN><<<grid, 64 * WM * WN, 0, s>>>(Aq, a_scale, offsets, E, rows, H, W13q,
                                                              (long long)2 * I * H, s13, 2 * I, I, (uint16_t*)h, NB,
                                                              n_slots);
 }
@@ -416,10 +438,10 @@ hipError_t launch_w13_swiglu_fp8a(const uint8_t* x_q, const float* x_scale, cons
                                   hipStream_t s) {
   if (rows_max == 0) return hipSuccess;
   if ((long long)rows_max <= (long long)kF8SmallRowsPerExpert * E)
-    launch_f8f8_cfg<kF8SmallBM, kF8SmallWM, kF8SmallWN>(x_q, x_scale, offsets_padded, E, rows_max, H, W13q, s13, I,
+    launch_f8f8_cfg<kF8SmallBM, kF8SmallBK, kF8SmallCap, kF8SmallWM, kF8SmallWN>(x_q, x_scale, offsets_padded, E, rows_max, H, W13q, s13, I,
                                                          h, s);
   else
-    launch_f8f8_cfg<kF8BM, kF8WM, kF8WN>(x_q, x_scale, offsets_padded, E, rows_max, H, W13q, s13, I, h, s);
+    launch_f8f8_cfg<kF8BM, kF8BK, kF8Cap, kF8WM, kF8WN>(x_q, x_scale, offsets_padded, E, rows_max, H, W13q, s13, I, h, s);
   return hipGetLastError();
 }
 
