@@ -374,6 +374,8 @@ def _layer_bench(w, args, torch, moe, dev, detail):
            "grouped_gemm": {"TFLOP/s": round(gg, 1), "frac_bf16_peak": round(gg / PEAK_BF16_TFLOPS, 4),
                             "GFLOP": round((flops1 + flops2) / 1e9, 1)},
            "stages": stages, "expert_load": _expert_load(counts), "roofline": roof}
+    if w.dtype == "bf16" and nk > 64 * E:
+        out["persistent_experiment"] = _persistent_bench(w, args, torch, moe, dev, (x, Wg, W13, W2, bias), ms)
     if not detail:
         return out
     # The alternative second half (routing weights and un-permutation in GEMM2's
@@ -413,6 +415,30 @@ def _layer_bench(w, args, torch, moe, dev, detail):
     stages["row_gather_standalone"] = {"ms": round(gather_ms, 5),
                                        "GB/s": round((n * H * esz + nk * H * esz) / (gather_ms * 1e-3) / 1e9, 1)}
     return out
+
+
+def _persistent_bench(w, args, torch, moe, dev, tensors, forward_ms):
+    """moe_forward_persistent (GEMM1 + SwiGLU and GEMM2 in one persistent kernel with per-XCD task
+    queues, a warm-up of L1 row tiles and an optional ring pool for h) timed like moe_forward, for two
+    schedules: a deep warm-up without a ring, and a ring of 16 row-tile slots per queue."""
+    x, Wg, W13, W2, bias = tensors
+    y = torch.empty((w.n, w.H), dtype=x.dtype, device=dev)
+    res = {"forward_ms": round(forward_ms, 5)}
+    for warm, pool in ((16, 0), (8, 16)):
+        nbytes = moe.moe_forward_persistent_workspace_size(w.n, w.H, w.I, w.E, w.K, pool)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+        def step():
+            moe.moe_forward_persistent(x, Wg, W13, W2, w.K, w.renorm, bias=bias, warmup_row_tiles=warm,
+                                       pool_row_tiles=pool, y=y, ws=ws)
+
+        _warm(step, args.warmup, torch, args.settle_ms)
+        pm = _time_region(step, args.steps, torch)
+        flag = int(ws[nbytes - 4:].view(torch.int32).item())
+        key = f"warm{warm}_pool{pool}"
+        res[key] = {"ms": round(pm, 5), "speedup_over_forward": round(forward_ms / pm, 3), "flag": flag,
+                    "h_bytes": (w.n * w.K * w.I * 2) if pool == 0 else 8 * pool * 256 * w.I * 2}
+    return res
 
 
 def _peaks(moe):
@@ -513,6 +539,7 @@ def main():
         "roofline": roof,
         "expert_load": head["expert_load"],
         "wall_s_timed_region": head["wall_s_timed_region"],
+        "persistent_experiment": head.get("persistent_experiment"),
         "configs": configs,
         "peaks": _peaks(moe),
         "cpu_baseline": cpu,

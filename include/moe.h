@@ -287,6 +287,34 @@ moe_status moe_forward_noalloc(const void* x, const void* W_gate, const float* b
                                float* logits_out, int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out,
                                hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * moe_forward_persistent — moe_forward with GEMM1 + SwiGLU and GEMM2 in ONE
+ * persistent kernel, scheduled as "大模型系统中的通算融合" §4.4 describes
+ * DeepGEMM's Mega MoE scheduler (restated for one GPU): L1 tiles (GEMM1 +
+ * SwiGLU) and L2 tiles (GEMM2) of each row tile are handed out from one task
+ * queue per XCD, the L1 tiles of `warmup_row_tiles` row tiles first, then
+ * alternating L1 tiles of later row tiles with L2 tiles of earlier ones; an
+ * L2 tile starts once every L1 tile of its rows has published h (per-row-
+ * tile counters with agent-scope release/acquire); h lives in a ring pool of
+ * `pool_row_tiles` row-tile slots per queue (0: one buffer for all rows).
+ * Outputs are bitwise equal to moe_forward's. bf16 only (MOE_EUNSUPPORTED
+ * otherwise); warmup_row_tiles >= 1, and pool_row_tiles either 0 or larger
+ * than warmup_row_tiles (MOE_EINVAL otherwise), so that every wait targets
+ * a task handed out earlier and the schedule cannot deadlock. Each wait is
+ * bounded nonetheless: if one runs out (a scheduling fault, never expected)
+ * the kernel finishes with wrong outputs and sets the workspace's last int32
+ * to nonzero instead of hanging.
+ *
+ *   arguments as moe_forward; ws at least
+ *   moe_forward_persistent_workspace_size(n, H, I, E, K, pool_row_tiles)
+ *   bytes (the last 4 bytes are the flag word above).
+ * ------------------------------------------------------------------------- */
+size_t moe_forward_persistent_workspace_size(int n, int H, int I, int E, int K, int pool_row_tiles);
+moe_status moe_forward_persistent(const void* x, const void* W_gate, const float* bias, const void* W13,
+                                  const void* W2, int n, int H, int I, int E, int K, int renorm, moe_dtype dt,
+                                  int warmup_row_tiles, int pool_row_tiles, void* y, float* logits_out,
+                                  int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, void* ws,
+                                  size_t ws_bytes, hipStream_t stream);
 
 /* ===========================================================================
  * Backward (training) pass of the same layer.

@@ -46,6 +46,11 @@ SIGNATURES = {
     "moe_forward_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "moe_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "moe_forward_noalloc_max_bytes": (_SZ, []),
+    "moe_forward_persistent_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "moe_forward_persistent": (
+        _I,
+        [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    ),
     "moe_forward_noalloc": (
         _I,
         [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP],
@@ -455,6 +460,43 @@ def moe_forward(x, W_gate, W13, W2, K: int, renorm: bool, bias=None, y=None, ws=
         _ptr(y), *[_ptr(t) for t in extra], _ptr(ws), ws.numel(), _stream(dev, stream),
     )
     _check(code, "moe_forward")
+    return (y, *extra) if routing_out else y
+
+
+def moe_forward_persistent_workspace_size(n, H, I, E, K, pool_row_tiles=0) -> int:  # noqa: E741
+    return int(load_library().moe_forward_persistent_workspace_size(n, H, I, E, K, pool_row_tiles))
+
+
+@_on_stream
+def moe_forward_persistent(x, W_gate, W13, W2, K: int, renorm: bool, bias=None, warmup_row_tiles=16,
+                           pool_row_tiles=0, y=None, ws=None, routing_out=False, stream=None):
+    """moe_forward with GEMM1 + SwiGLU and GEMM2 in one persistent kernel (bf16). Returns y, or
+    (y, logits, topk_ids, topk_w, counts) with routing_out. The workspace's last int32 is the
+    scheduler's flag word (nonzero if a bounded wait ran out)."""
+    lib = load_library()
+    n, H = x.shape
+    E = W_gate.shape[1]
+    I = W13.shape[2] // 2  # noqa: E741
+    dev = x.device
+    _need(x, "x", (n, H), torch.bfloat16)
+    _need(W_gate, "W_gate", (H, E), torch.bfloat16, dev)
+    _need(W13, "W13", (E, H, 2 * I), torch.bfloat16, dev)
+    _need(W2, "W2", (E, I, H), torch.bfloat16, dev)
+    if bias is not None:
+        _need(bias, "bias", (E,), torch.float32, dev)
+    y = _empty((n, H), torch.bfloat16, dev) if y is None else y
+    _need(y, "y", (n, H), torch.bfloat16, dev)
+    ws = _workspace(lib.moe_forward_persistent_workspace_size(n, H, I, E, K, pool_row_tiles), dev, ws)
+    extra = [None] * 4
+    if routing_out:
+        extra = [_empty((n, E), torch.float32, dev), _empty((n, K), torch.int32, dev),
+                 _empty((n, K), torch.float32, dev), _empty((E,), torch.int32, dev)]
+    code = lib.moe_forward_persistent(
+        _ptr(x), _ptr(W_gate), _ptr(bias), _ptr(W13), _ptr(W2), n, H, I, E, K, int(bool(renorm)), MOE_BF16,
+        int(warmup_row_tiles), int(pool_row_tiles), _ptr(y), *[_ptr(t) for t in extra], _ptr(ws), ws.numel(),
+        _stream(dev, stream),
+    )
+    _check(code, "moe_forward_persistent")
     return (y, *extra) if routing_out else y
 
 

@@ -246,6 +246,37 @@ moe_status forward_enqueue(const void* x, const void* W_gate, const float* bias,
   return from_hip(launch_combine(base + L.Y_perm, inv, w, n, H, K, dt, y, stream));
 }
 
+// moe_forward_persistent workspace: routing and metadata as in
+// forward_layout, h (ring pool or all rows), Y_perm, and the scheduler's
+// counters last, so that its flag word is the workspace's last int32.
+struct PersistentLayout {
+  size_t logits, ids, w, counts, offsets, splits, perm, inv, pscratch, h, Y_perm, counters, total;
+};
+PersistentLayout persistent_layout(int n, int H, int I, int E, int K, int pool) {
+  PersistentLayout L{};
+  const size_t nk = (size_t)n * K;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes > 0 ? bytes : 1);
+    return at;
+  };
+  L.logits = take((size_t)n * E * 4);
+  L.ids = take(nk * 4);
+  L.w = take(nk * 4);
+  L.counts = take((size_t)E * 4);
+  L.offsets = take((size_t)(E + 1) * 4);
+  L.splits = take(4);
+  L.perm = take(nk * 4);
+  L.inv = take(nk * 4);
+  L.pscratch = take(permute_ws(n, E, K));
+  L.h = take(fused_ffn_h_bytes((int)nk, E, I, pool));
+  L.Y_perm = take(nk * H * 2);
+  L.counters = o;
+  L.total = o + fused_ffn_counter_bytes((int)nk, E);
+  return L;
+}
+
 // Scratch of moe_forward_noalloc: the workspace of moe_forward, in a static
 // device array that every device the library runs on holds from the first
 // call to the end of the process. Every call on a device shares it (calls
@@ -462,6 +493,48 @@ moe_status moe_forward(const void* x, const void* W_gate, const float* bias, con
   if (ws == nullptr || ws_bytes < forward_layout(n, H, I, E, K, dt).total) return MOE_EWORKSPACE;
   return forward_enqueue(x, W_gate, bias, W13, W2, n, H, I, E, K, renorm, dt, y, logits_out, topk_ids_out,
                          topk_w_out, counts_out, (char*)ws, stream);
+}
+
+size_t moe_forward_persistent_workspace_size(int n, int H, int I, int E, int K, int pool_row_tiles) {
+  if (n < 0 || H < 1 || I < 1 || E < 1 || K < 1 || pool_row_tiles < 0) return 0;
+  if ((long long)n * K > INT32_MAX) return 0;
+  return persistent_layout(n, H, I, E, K, pool_row_tiles).total;
+}
+
+moe_status moe_forward_persistent(const void* x, const void* W_gate, const float* bias, const void* W13,
+                                  const void* W2, int n, int H, int I, int E, int K, int renorm, moe_dtype dt,
+                                  int warmup_row_tiles, int pool_row_tiles, void* y, float* logits_out,
+                                  int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  const moe_status st = check_forward(x, W_gate, bias, W13, W2, n, H, I, E, K, dt, y, logits_out, topk_ids_out,
+                                      topk_w_out, counts_out);
+  if (st != MOE_OK) return st;
+  if (dt != MOE_BF16) return MOE_EUNSUPPORTED;
+  // The ring must hold the warm-up row tiles and one more, so that an L1 tile
+  // only ever waits for L2 tiles taken before it.
+  if (warmup_row_tiles < 1 || pool_row_tiles < 0 || (pool_row_tiles > 0 && pool_row_tiles <= warmup_row_tiles))
+    return MOE_EINVAL;
+  if (!vec_ok({ws})) return MOE_EINVAL;
+  if (n == 0) return counts_out ? from_hip(launch_fill_zero(counts_out, (size_t)E * 4, stream)) : MOE_OK;
+  const PersistentLayout L = persistent_layout(n, H, I, E, K, pool_row_tiles);
+  if (ws == nullptr || ws_bytes < L.total) return MOE_EWORKSPACE;
+  char* base = (char*)ws;
+  float* logits = logits_out ? logits_out : (float*)(base + L.logits);
+  int32_t* ids = topk_ids_out ? topk_ids_out : (int32_t*)(base + L.ids);
+  float* w = topk_w_out ? topk_w_out : (float*)(base + L.w);
+  int32_t* counts = counts_out ? counts_out : (int32_t*)(base + L.counts);
+  int32_t* offsets = (int32_t*)(base + L.offsets);
+  int32_t* perm = (int32_t*)(base + L.perm);
+  int32_t* inv = (int32_t*)(base + L.inv);
+  hipError_t e = launch_route(x, W_gate, bias, n, H, E, K, renorm, dt, logits, ids, w, stream);
+  if (e == hipSuccess)
+    e = launch_permute(ids, nullptr, n, H, E, K, 1, dt, counts, offsets, (int32_t*)(base + L.splits), perm, inv,
+                       nullptr, (int32_t*)(base + L.pscratch), stream);
+  if (e == hipSuccess)
+    e = launch_fused_ffn(x, perm, n, K, offsets, W13, W2, E, H, I, warmup_row_tiles, pool_row_tiles, base + L.h,
+                         base + L.Y_perm, (int*)(base + L.counters), stream);
+  if (e == hipSuccess) e = launch_combine(base + L.Y_perm, inv, w, n, H, K, dt, y, stream);
+  return from_hip(e);
 }
 
 size_t moe_forward_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }

@@ -73,6 +73,18 @@ hipError_t launch_combine(const void* Y_perm, const int32_t* inv, const float* t
 hipError_t launch_combine_rows(const void* Y_perm, int y_rows, const int32_t* inv, const float* topk_w, int n, int H,
                                int K, moe_dtype dt, void* y, hipStream_t s);
 
+// Persistent single-kernel GEMM1 + SwiGLU + GEMM2 (bf16): route and permute
+// metadata as for launch_w13_swiglu_gather, h in `hbuf` (a ring of `pool`
+// row-tile slots per XCD queue, or all rows when pool is 0), Y_perm expert-
+// major. `counters`: fused_ffn_counter_bytes(n*K, E) bytes, zeroed by the
+// launcher; its last int32 becomes nonzero if a bounded wait ran out.
+int fused_ffn_max_row_tiles(int rows, int E);
+size_t fused_ffn_counter_bytes(int rows, int E);
+size_t fused_ffn_h_bytes(int rows, int E, int I, int pool);
+hipError_t launch_fused_ffn(const void* x, const int32_t* perm, int n, int K, const int32_t* offsets, const void* W13,
+                            const void* W2, int E, int H, int I, int warm, int pool, void* hbuf, void* Y_perm,
+                            int* counters, hipStream_t s);
+
 // ---- backward ----
 
 // GEMM1 that also writes the pre-activations [gate | up] (rows, 2I) for the backward.

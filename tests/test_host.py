@@ -271,3 +271,28 @@ def test_zero_tokens_needs_no_workspace(lib):
     assert lib.moe_forward(None, None, None, None, None, 0, 64, 64, 8, 2, 0, 1, None, None, None, None, None,
                            None, 0, None) == 0
     assert lib.moe_workspace_size(16, 64, 64, 8, 2, 1) == lib.moe_forward_workspace_size(16, 64, 64, 8, 2, 1)
+
+
+def test_persistent_forward_rejects_bad_arguments(lib):
+    """moe_forward_persistent: bf16 only, a warm-up of at least one row tile, a ring either off (0) or
+    larger than the warm-up, and a workspace of the stated size, all checked before any launch."""
+    s = None
+    ws = lib.moe_forward_persistent_workspace_size(16, 64, 64, 8, 2, 0)
+    assert ws > 0
+    # a ring pool bounds h: at the OLMoE shape 8 queues x 8 slots x 256 rows x I is below n*K rows x I
+    assert (lib.moe_forward_persistent_workspace_size(4096, 2048, 1024, 64, 8, 8)
+            < lib.moe_forward_persistent_workspace_size(4096, 2048, 1024, 64, 8, 0))
+    assert lib.moe_forward_persistent_workspace_size(16, 64, 64, 8, 2, -1) == 0
+    args = [P, P, None, P, P, 16, 64, 64, 8, 2, 0, 1, 4, 0, P, None, None, None, None, P, ws, s]
+    bad = list(args)
+    bad[11] = 0  # fp32
+    assert lib.moe_forward_persistent(*bad) == EUNSUP
+    bad = list(args)
+    bad[12] = 0  # no warm-up
+    assert lib.moe_forward_persistent(*bad) == EINVAL
+    bad = list(args)
+    bad[13] = 4  # ring not larger than the warm-up
+    assert lib.moe_forward_persistent(*bad) == EINVAL
+    bad = list(args)
+    bad[20] = ws - 1
+    assert lib.moe_forward_persistent(*bad) == EWS
