@@ -147,6 +147,11 @@ def dequantize_rows(codes, scale) -> np.ndarray:
     return e4m3_decode(codes) * np.asarray(scale, dtype=np.float64)[:, None]
 
 
+def fp8_round_rows(X) -> np.ndarray:
+    """X as per-row FP8 holds it: dequantize_rows(quantize_rows(X)), fp64."""
+    return dequantize_rows(*quantize_rows(X))
+
+
 def padded_offsets(counts, group: int = TOKEN_GROUP) -> np.ndarray:
     """Start of each expert's padded group: P[0] = 0, P[e+1] = P[e] + group * ceil(n_e / group)."""
     c = np.asarray(counts, dtype=np.int64)
@@ -186,12 +191,35 @@ def dispatch_fp8(x, e_top, E: int, group: int = TOKEN_GROUP) -> dict:
     return dict(codes=codes, scales=scales, offsets=P, perm=perm_p, inv=inv_p, counts=counts)
 
 
-def forward_fp8a(x, W_gate, W13_codes, s13, W2_codes, s2, K: int, renorm: bool, bias=None, routing_logits_f32=None):
+def forward_fp8a(x, W_gate, W13_codes, s13, W2_codes, s2, K: int, renorm: bool, bias=None, routing_logits_f32=None,
+                 fp8_h: bool = True):
     """Algorithm 2 with FP8 activations and FP8 weights: routed on x, the experts
-    run on the dequantized per-token FP8 rows and the dequantized weights (fp64)."""
+    run on the dequantized per-token FP8 rows and the dequantized weights (fp64).
+    With fp8_h (the layer's form), each expert's intermediate rows
+    h = SiLU(gate) * up are quantized the same way before the down projection
+    ([Fusion] §8.4 lists FP8 activations among its low-precision forms): one
+    fp32 scale per row of h and the nearest E4M3 code of h rounded to fp32."""
     if routing_logits_f32 is None:
         routing_logits_f32 = moe_oracle.round_to_f32(moe_oracle.router_logits(x, W_gate, bias))
     codes, scales = quantize_rows(x)
     x_deq = dequantize_rows(codes, scales)
-    return moe_oracle.forward(x_deq, W_gate, dequantize_columns(W13_codes, s13), dequantize_columns(W2_codes, s2),
-                              K, renorm, bias=bias, routing_logits_f32=routing_logits_f32)
+    W13 = dequantize_columns(W13_codes, s13)
+    W2 = dequantize_columns(W2_codes, s2)
+    out = moe_oracle.forward(x_deq, W_gate, W13, W2, K, renorm, bias=bias, routing_logits_f32=routing_logits_f32)
+    if not fp8_h:
+        return out
+    # Steps 8-11 again with h quantized per row between the two products.
+    n, H = x_deq.shape
+    E = W13.shape[0]
+    perm, offsets, w_top = out["perm"], out["offsets"], out["w_top"]
+    y = np.zeros((n, H), dtype=np.float64)
+    for e in range(E):
+        seg = perm[offsets[e] : offsets[e + 1]]
+        if seg.size == 0:
+            continue
+        tok, slot = seg // K, seg % K
+        h = moe_oracle.expert_gate_up(x_deq[tok], W13[e])
+        Y_e = fp8_round_rows(h) @ W2[e]
+        np.add.at(y, tok, Y_e * w_top[tok, slot][:, None])
+    out["y"] = y
+    return out

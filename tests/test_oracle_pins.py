@@ -850,14 +850,50 @@ def test_forward_fp8a_exact_activations_and_error():
     xg = rng.choice(np.concatenate([t, -t]), size=(w.n, w.H))
     xg[:, 0] = 448.0
     xg = (xg * 2.0**-9).astype(np.float32)  # scale 2^-9 per row, exact
-    a = f.forward_fp8a(xg, w.W_gate_f32, c13, s13, c2, s2, w.K, w.renorm)
+    a = f.forward_fp8a(xg, w.W_gate_f32, c13, s13, c2, s2, w.K, w.renorm, fp8_h=False)
     b = f.forward_fp8(xg, w.W_gate_f32, c13, s13, c2, s2, w.K, w.renorm)
     np.testing.assert_allclose(a["y"], b["y"], rtol=0, atol=1e-15)
-    a = f.forward_fp8a(w.x_f32, w.W_gate_f32, c13, s13, c2, s2, w.K, w.renorm)
+    a = f.forward_fp8a(w.x_f32, w.W_gate_f32, c13, s13, c2, s2, w.K, w.renorm, fp8_h=False)
     b = f.forward_fp8(w.x_f32, w.W_gate_f32, c13, s13, c2, s2, w.K, w.renorm)
     assert (a["e_top"] == b["e_top"]).all()  # routing stays on the unquantized activations
     rel = np.linalg.norm(a["y"] - b["y"]) / np.linalg.norm(b["y"])
     assert 1e-4 < rel < 0.1
+
+
+def _fp8_h_identity_layer(n=40, I=48, seed=31):
+    """E = K = 1 with renormalisation (y = Y exactly) and W2 = (448 * 2^-10) * identity (I = H), whose column
+    codes are exactly 448 with scale 2^-10, so y = 0.4375 * (h as the layer quantizes it), exactly in fp64."""
+    f = oracle.fp8
+    rng = np.random.default_rng(seed)
+    H = I
+    x = rng.standard_normal((n, H)).astype(np.float32)
+    W_gate = rng.standard_normal((H, 1)).astype(np.float32)
+    W13 = (0.2 * rng.standard_normal((1, H, 2 * I))).astype(np.float32)
+    W2 = (np.eye(I, dtype=np.float32) * np.float32(448 * 2.0**-10))[None]
+    c13, s13 = f.quantize_columns(W13)
+    c2, s2 = f.quantize_columns(W2)
+    assert (s2 == np.float32(2.0**-10)).all() and (f.dequantize_columns(c2, s2) == W2).all()
+    q = f.forward_fp8a(x, W_gate, c13, s13, c2, s2, 1, True)["y"] / 0.4375
+    h = f.forward_fp8a(x, W_gate, c13, s13, c2, s2, 1, True, fp8_h=False)["y"] / 0.4375
+    return q, h
+
+
+def test_fp8a_intermediate_rows_on_their_scaled_grid():
+    """The FP8 h of the layer: every row of the quantized h lies on the E4M3 grid scaled by its own row's
+    amax / 448 (the largest element maps to 448), and each element is the nearest grid value of h (within
+    half a gap: 2^-4 of its magnitude for normal values, 2^-10 of the row scale below 2^-6)."""
+    q, h = _fp8_h_identity_layer()
+    grid = oracle.fp8.e4m3_decode_table()[:0x7F]
+    grid = np.concatenate([grid, -grid])
+    for i in range(q.shape[0]):
+        amax = np.max(np.abs(q[i]))
+        assert amax > 0
+        s = amax / 448.0
+        v = q[i] / s
+        assert np.isin(v, grid).all(), f"row {i} is not on its own scaled E4M3 grid"
+        tol = np.maximum(2.0**-4 * np.abs(h[i]), 2.0**-10 * s) * (1 + 1e-6)
+        assert (np.abs(q[i] - h[i]) <= tol).all()
+    assert np.abs(q - h).max() > 0  # the quantization happened
 
 
 def test_planted_fp8_activation_mistakes_are_caught(monkeypatch):
@@ -872,6 +908,19 @@ def test_planted_fp8_activation_mistakes_are_caught(monkeypatch):
 
     monkeypatch.setattr(f, "quantize_rows", quantize_global)
     assert not _pins_pass(test_quantize_rows_per_token_scale_exact_grid_and_search)
+    monkeypatch.undo()
+
+    # 1b. h quantized with one scale per column instead of one per row, and h not quantized at all.
+    def round_cols(X):
+        X32 = np.asarray(X, dtype=np.float32)
+        s = np.max(np.abs(X32), axis=0) / np.float32(448)
+        s = np.where(s > 0, s, np.float32(1)).astype(np.float32)
+        return f.e4m3_decode(f.e4m3_encode((X32 / s[None, :]).astype(np.float32))) * s[None, :].astype(np.float64)
+
+    monkeypatch.setattr(f, "fp8_round_rows", round_cols)
+    assert not _pins_pass(test_fp8a_intermediate_rows_on_their_scaled_grid)
+    monkeypatch.setattr(f, "fp8_round_rows", lambda X: np.asarray(X, dtype=np.float64))
+    assert not _pins_pass(test_fp8a_intermediate_rows_on_their_scaled_grid)
     monkeypatch.undo()
 
     # 2. Groups padded to 8 rows.
