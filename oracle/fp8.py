@@ -147,6 +147,15 @@ def dequantize_rows(codes, scale) -> np.ndarray:
     return e4m3_decode(codes) * np.asarray(scale, dtype=np.float64)[:, None]
 
 
+def round_to_bf16(a) -> np.ndarray:
+    """Nearest bf16 value (8 significant bits, fp32's exponent range), ties to
+    the even significand, as fp64: frexp gives a in [0.5, 1) * 2^e, the
+    significand is rounded to 2^-8 steps half-to-even, and scaled back."""
+    a = np.asarray(a, dtype=np.float64)
+    m, e = np.frexp(a)
+    return np.ldexp(np.round(m * 256.0) / 256.0, e)
+
+
 def fp8_round_rows(X) -> np.ndarray:
     """X as per-row FP8 holds it: dequantize_rows(quantize_rows(X)), fp64."""
     return dequantize_rows(*quantize_rows(X))
@@ -197,8 +206,10 @@ def forward_fp8a(x, W_gate, W13_codes, s13, W2_codes, s2, K: int, renorm: bool, 
     run on the dequantized per-token FP8 rows and the dequantized weights (fp64).
     With fp8_h (the layer's form), each expert's intermediate rows
     h = SiLU(gate) * up are quantized the same way before the down projection
-    ([Fusion] §8.4 lists FP8 activations among its low-precision forms): one
-    fp32 scale per row of h and the nearest E4M3 code of h rounded to fp32."""
+    ([Fusion] §8.4 lists FP8 activations among its low-precision forms): h is
+    rounded to bf16 as the bf16 layer stores it between the two products, then
+    one fp32 scale per row and the nearest E4M3 code, decided in fp32 like the
+    token rows' codes."""
     if routing_logits_f32 is None:
         routing_logits_f32 = moe_oracle.round_to_f32(moe_oracle.router_logits(x, W_gate, bias))
     codes, scales = quantize_rows(x)
@@ -219,7 +230,7 @@ def forward_fp8a(x, W_gate, W13_codes, s13, W2_codes, s2, K: int, renorm: bool, 
             continue
         tok, slot = seg // K, seg % K
         h = moe_oracle.expert_gate_up(x_deq[tok], W13[e])
-        Y_e = fp8_round_rows(h) @ W2[e]
+        Y_e = fp8_round_rows(round_to_bf16(h)) @ W2[e]
         np.add.at(y, tok, Y_e * w_top[tok, slot][:, None])
     out["y"] = y
     return out

@@ -891,9 +891,27 @@ def test_fp8a_intermediate_rows_on_their_scaled_grid():
         s = amax / 448.0
         v = q[i] / s
         assert np.isin(v, grid).all(), f"row {i} is not on its own scaled E4M3 grid"
-        tol = np.maximum(2.0**-4 * np.abs(h[i]), 2.0**-10 * s) * (1 + 1e-6)
+        # half an E4M3 gap of the bf16 value, plus the bf16 rounding itself (2^-9 relative)
+        tol = (np.maximum(2.0**-4 * np.abs(h[i]) * (1 + 2.0**-8), 2.0**-10 * s) + 2.0**-9 * np.abs(h[i])) * (1 + 1e-9)
         assert (np.abs(q[i] - h[i]) <= tol).all()
     assert np.abs(q - h).max() > 0  # the quantization happened
+
+
+def test_round_to_bf16_matches_the_format():
+    """round_to_bf16: representable values unchanged, midpoints to the even significand, and equal to torch's
+    fp32 -> bfloat16 conversion (round to nearest even) on random fp32 values of every magnitude."""
+    import torch
+
+    f = oracle.fp8
+    for v in [1.0, -2.5, 0.0, 3.0 * 2.0**-20, 65280.0]:
+        assert f.round_to_bf16(v) == v
+    assert f.round_to_bf16(1.0 + 2.0**-8) == 1.0  # halfway between 1 and 1 + 2^-7: even
+    assert f.round_to_bf16(1.0 + 3 * 2.0**-8) == 1.0 + 2.0**-6
+    assert f.round_to_bf16(1.0 + 2.0**-8 + 2.0**-30) == 1.0 + 2.0**-7
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(20000) * np.exp(rng.uniform(-30, 30, 20000))).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert (f.round_to_bf16(x) == ref).all()
 
 
 def test_planted_fp8_activation_mistakes_are_caught(monkeypatch):
