@@ -904,6 +904,12 @@ def _bench_fp8(args):
         st["gemm1_swiglu_fp8a"] = _time_region_graph(
             lambda: moe.moe_expert_w13_swiglu_fp8a(d8["x_q"], d8["x_scale"], d8["offsets_padded"], q13, s13, h=h8),
             R, torch)
+        hq, hs = moe.moe_quantize_rows_fp8(h8)
+        Y8 = moe.moe_expert_w2_fp8a(hq, hs, d8["offsets_padded"], q2, s2)
+        torch.cuda.synchronize()
+        st["quantize_h_fp8"] = _time_region_graph(lambda: moe.moe_quantize_rows_fp8(h8, codes=hq, scales=hs), R, torch)
+        st["gemm2_fp8a"] = _time_region_graph(
+            lambda: moe.moe_expert_w2_fp8a(hq, hs, d8["offsets_padded"], q2, s2, Y_perm=Y8), R, torch)
     bytes_ = {  # algorithmic: activations once, FP8 codes and scales of the hit experts once, outputs once
         "gemm1_swiglu_fp8": nk * H * 2 + hit * (2 * I * H + 2 * I * 4) + nk * I * 2 + nk * 4,
         "gemm2_fp8": nk * I * 2 + hit * (H * I + H * 4) + nk * H * 2,
@@ -914,6 +920,10 @@ def _bench_fp8(args):
         bytes_["dispatch_fp8"] = nk * H + rpad * H + rpad * 8 + nk * 4
         bytes_["gemm1_swiglu_fp8a"] = rpad * (H + 4) + hit * (2 * I * H + 2 * I * 4) + rpad * I * 2
         flops["gemm1_swiglu_fp8a"] = 2.0 * nk * H * 2 * I
+        rmax = h8.shape[0]
+        bytes_["quantize_h_fp8"] = rmax * I * 2 + rmax * I + rmax * 4
+        bytes_["gemm2_fp8a"] = rpad * (I + 4) + hit * (H * I + H * 4) + rpad * H * 2
+        flops["gemm2_fp8a"] = 2.0 * nk * I * H
     stages = {}
     for k, v in st.items():
         gbs = bytes_[k] / (v * 1e-3) / 1e9

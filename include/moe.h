@@ -585,12 +585,22 @@ moe_status moe_forward_fp8(const void* x, const void* W_gate, const float* bias,
  * moe_quantize_fp8 on W13; rows_max = moe_fp8_padded_rows(n, E, K) (an upper
  * bound; the tile map comes from offsets_padded). H a multiple of 128.
  *
+ * moe_expert_w2_fp8a — GEMM2 with FP8 activations: Y_perm row r (bf16) =
+ * (h_scale[r] * decode(h_q[r])) . (s2 * decode(W2q)) over the expert of row r
+ * (offsets_padded), on the FP8 MFMA with fp32 accumulation. h_q (rows_max, I)
+ * uint8 and h_scale (rows_max) fp32 are h quantized per row as
+ * moe_quantize_rows_fp8 does it ("大模型系统中的通算融合" §8.4 lists FP8
+ * activations among the low-precision forms); W2q (E, H, I) and s2 (E, H) as
+ * from moe_quantize_fp8 on W2; Y_perm (rows_max, H) bf16 out (rows past
+ * offsets_padded[E] not written). I a multiple of 128.
+ *
  * moe_forward_fp8a — the layer with FP8 activations and FP8 weights: moe_route
  * on x (bf16), the moe_permute metadata, moe_quantize_rows_fp8,
- * moe_dispatch_fp8, moe_expert_w13_swiglu_fp8a, moe_expert_w2_fp8 (bf16 h,
- * FP8 W2) over the padded rows, and moe_unpermute_combine through inv_padded.
- * Arguments as moe_forward_fp8 (dt must be MOE_BF16, H a multiple of 128);
- * ws of at least moe_forward_fp8a_workspace_size(n, H, I, E, K) bytes.
+ * moe_dispatch_fp8, moe_expert_w13_swiglu_fp8a, moe_quantize_rows_fp8 on h,
+ * moe_expert_w2_fp8a over the padded rows, and moe_unpermute_combine through
+ * inv_padded. Arguments as moe_forward_fp8 (dt must be MOE_BF16, H and I
+ * multiples of 128); ws of at least moe_forward_fp8a_workspace_size(n, H, I,
+ * E, K) bytes.
  * ------------------------------------------------------------------------- */
 moe_status moe_quantize_rows_fp8(const void* x, int n, int H, moe_dtype dt, uint8_t* codes, float* scales,
                                  hipStream_t stream);
@@ -602,6 +612,9 @@ moe_status moe_dispatch_fp8(const int32_t* counts, const int32_t* offsets, const
 moe_status moe_expert_w13_swiglu_fp8a(const uint8_t* x_q, const float* x_scale, const int32_t* offsets_padded,
                                       int rows_max, const uint8_t* W13q, const float* s13, int E, int H, int I,
                                       void* h, hipStream_t stream);
+moe_status moe_expert_w2_fp8a(const uint8_t* h_q, const float* h_scale, const int32_t* offsets_padded, int rows_max,
+                              const uint8_t* W2q, const float* s2, int E, int H, int I, void* Y_perm,
+                              hipStream_t stream);
 size_t moe_forward_fp8a_workspace_size(int n, int H, int I, int E, int K);
 moe_status moe_forward_fp8a(const void* x, const void* W_gate, const float* bias, const uint8_t* W13q,
                             const float* s13, const uint8_t* W2q, const float* s2, int n, int H, int I, int E, int K,

@@ -88,6 +88,7 @@ SIGNATURES = {
     "moe_fp8_padded_rows": (_SZ, [_I, _I, _I]),
     "moe_dispatch_fp8": (_I, [_VP, _VP, _VP, _I, _I, _I, _VP, _VP, _I, _VP, _VP, _VP, _VP, _VP, _VP]),
     "moe_expert_w13_swiglu_fp8a": (_I, [_VP, _VP, _VP, _I, _VP, _VP, _I, _I, _I, _VP, _VP]),
+    "moe_expert_w2_fp8a": (_I, [_VP, _VP, _VP, _I, _VP, _VP, _I, _I, _I, _VP, _VP]),
     "moe_forward_fp8a_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
     "moe_forward_fp8a": (
         _I,
@@ -962,6 +963,25 @@ def moe_expert_w13_swiglu_fp8a(x_q, x_scale, offsets_padded, W13q, s13, h=None, 
     _check(lib.moe_expert_w13_swiglu_fp8a(_ptr(x_q), _ptr(x_scale), _ptr(offsets_padded), R, _ptr(W13q), _ptr(s13),
                                           E, H, I, _ptr(h), _stream(dev, stream)), "moe_expert_w13_swiglu_fp8a")
     return h
+
+
+@_on_stream
+def moe_expert_w2_fp8a(h_q, h_scale, offsets_padded, W2q, s2, Y_perm=None, stream=None):
+    """GEMM2 with FP8 activations over the padded receive buffer: Y_perm (rows_max, H) bf16 from h quantized
+    per row (h_q (rows_max, I) uint8, h_scale (rows_max,) fp32) and the FP8 W2 codes/scales."""
+    lib = load_library()
+    R, I = h_q.shape  # noqa: E741
+    E, H = s2.shape
+    dev = h_q.device
+    _need(h_q, "h_q", (R, I), torch.uint8)
+    _need(h_scale, "h_scale", (R,), torch.float32, dev)
+    _need(offsets_padded, "offsets_padded", (E + 1,), torch.int32, dev)
+    _need(W2q, "W2q", (E, H, I), torch.uint8, dev)
+    Y_perm = _empty((R, H), torch.bfloat16, dev) if Y_perm is None else Y_perm
+    _need(Y_perm, "Y_perm", (R, H), torch.bfloat16, dev)
+    _check(lib.moe_expert_w2_fp8a(_ptr(h_q), _ptr(h_scale), _ptr(offsets_padded), R, _ptr(W2q), _ptr(s2), E, H, I,
+                                  _ptr(Y_perm), _stream(dev, stream)), "moe_expert_w2_fp8a")
+    return Y_perm
 
 
 def moe_forward_fp8a_workspace_size(n, H, I, E, K) -> int:  # noqa: E741

@@ -27,9 +27,12 @@ namespace moe {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Per-token quantization: one wave per row, 8 elements per lane per step.
+// Per-token quantization: one wave per row, 8 elements per lane per chunk.
 // ---------------------------------------------------------------------------
-template <bool BF16>
+// CH > 0: rows of at most 512 * CH elements, whose chunks each lane keeps in
+// registers between the amax and the codes (one read of the row); CH = 0:
+// any width, the row read twice.
+template <bool BF16, int CH>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* __restrict__ x, int n, int H,
                                                             uint8_t* __restrict__ codes, float* __restrict__ scales) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -53,24 +56,50 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* __restri
       }
     }
   };
+  auto store8 = [&](int h0, const float* v, float s) {
+    float q[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = v[j] / s;  // one correctly rounded fp32 division each
+    *(u32x2_t*)(codes + (size_t)row * H + h0) =
+        u32x2_t{e4m3_pack4(q[0], q[1], q[2], q[3]), e4m3_pack4(q[4], q[5], q[6], q[7])};
+  };
   float m = 0.f;
-  for (int h0 = lane * 8; h0 < H; h0 += 512) {
-    float v[8];
-    load8(h0, v);
+  if constexpr (CH > 0) {
+    float v[CH][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
-  }
+    for (int c = 0; c < CH; ++c) {
+      const int h0 = lane * 8 + c * 512;
+      if (h0 < H) {
+        load8(h0, v[c]);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  const float s = m > 0.f ? m / 448.f : 1.f;
-  if (lane == 0) scales[row] = s;
-  for (int h0 = lane * 8; h0 < H; h0 += 512) {
-    float v[8];
-    load8(h0, v);
-    uint32_t w[2] = {0u, 0u};
+        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[c][j]));
+      }
+    }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) w[j >> 2] |= e4m3_nearest(v[j] / s) << (8 * (j & 3));
-    *(u32x2_t*)(codes + (size_t)row * H + h0) = u32x2_t{w[0], w[1]};
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    const float s = m > 0.f ? m / 448.f : 1.f;
+    if (lane == 0) scales[row] = s;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int h0 = lane * 8 + c * 512;
+      if (h0 < H) store8(h0, v[c], s);
+    }
+  } else {
+    for (int h0 = lane * 8; h0 < H; h0 += 512) {
+      float v[8];
+      load8(h0, v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    const float s = m > 0.f ? m / 448.f : 1.f;
+    if (lane == 0) scales[row] = s;
+    for (int h0 = lane * 8; h0 < H; h0 += 512) {
+      float v[8];
+      load8(h0, v);
+      store8(h0, v, s);
+    }
   }
 }
 
@@ -182,7 +211,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // WM x WN waves split the BM x 256 tile; each wave owns (BM / WM) rows and
 // (256 / WN) staged columns, half gate and half the matching up columns, as
 // 32 x 32 MFMA tiles.
-template <int BM, int BK, int CAP, int WM, int WN>
+template <bool GATED, int BM, int BK, int CAP, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
     const uint8_t* __restrict__ Aq, const float* __restrict__ a_scale, const int32_t* __restrict__ offsets, int E,
     int rows, int Kdim, const uint8_t* __restrict__ Bq, long long b_stride, const float* __restrict__ b_scale,
@@ -192,7 +221,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
   constexpr int ROW = Cfg::ROW, CPR = Cfg::CPR, RPR = Cfg::ROWS_PER_REGION;
   constexpr int NW = WM * WN;
   constexpr int MT = BM / WM / 32;        // 32-row MFMA tiles per wave
-  constexpr int NTH = BN / WN / 32 / 2;   // 32-column gate tiles per wave (as many up tiles)
+  constexpr int NQ = BN / WN / 32;         // 32-column MFMA tiles per wave
+  constexpr int NTH = NQ / 2;              // GEMM1: as many gate tiles as up tiles
   constexpr int REG = Cfg::REGIONS / NW;  // 1 KB DMA regions per wave per stage
   static_assert(MT >= 1 && NTH >= 1 && REG * NW == Cfg::REGIONS, "tile split");
   static_assert(NSTAGE >= 2 && NSTAGE - 2 <= 2 && 2 * REG <= 63, "vmcnt range (wait_dma covers two later stages)");
@@ -229,9 +259,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
         const int arow = t.r0 + min(rr, mrows - 1);
         src[j] = Aq + (size_t)arow * Kdim + c * 16;
       } else {
-        int gc = t.nb * (BN / 2) + (rr & (BN / 2 - 1));
-        if (gc >= I) gc = 0;
-        const int code_row = rr < BN / 2 ? gc : I + gc;
+        int code_row;
+        if constexpr (GATED) {  // 128 gate columns, then the matching 128 up columns
+          int gc = t.nb * (BN / 2) + (rr & (BN / 2 - 1));
+          if (gc >= I) gc = 0;
+          code_row = rr < BN / 2 ? gc : I + gc;
+        } else {
+          code_row = t.nb * BN + rr;
+          if (code_row >= N) code_row = 0;
+        }
         src[j] = Bq + (size_t)t.e * b_stride + (size_t)code_row * Kdim + c * 16;
       }
     }
@@ -267,25 +303,30 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
     const u32x4_t up = lds_read_b128(base + row * ROW + (((c0 + 1) ^ sw) << 4));
     return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
   };
-  f32x16_t acc[MT][2 * NTH];
+  f32x16_t acc[MT][NQ];
+  // Staged B row of column tile q's lane: GEMM1 pairs gate tile q < NTH with
+  // up tile q + NTH; GEMM2 takes the wave's NQ tiles in order.
+  auto b_row = [&](int q) {
+    if constexpr (GATED)
+      return (q / NTH) * (BN / 2) + wn * (BN / 2 / WN) + (q % NTH) * 32 + l32;
+    else
+      return wn * (BN / WN) + q * 32 + l32;
+  };
   int vm = 0;  // 32-row MFMA tiles of this wave that hold a valid row
   auto kstep = [&](int stage) {
     const lds_char_t* As = smem + stage * STAGE;
     const lds_char_t* Bs = As + A_BYTES;
 #pragma unroll 1
     for (int ks = 0; ks < BK / 64; ++ks) {
-      i32x8_t b[2 * NTH];
+      i32x8_t b[NQ];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int nt = 0; nt < NTH; ++nt)
-          b[h * NTH + nt] = rd32(Bs, h * (BN / 2) + wn * (BN / 2 / WN) + nt * 32 + l32, ks);
+      for (int q = 0; q < NQ; ++q) b[q] = rd32(Bs, b_row(q), ks);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if (mt >= vm) continue;
         const i32x8_t a = rd32(As, a_row0 + mt * 32 + l32, ks);
 #pragma unroll
-        for (int q = 0; q < 2 * NTH; ++q)
+        for (int q = 0; q < NQ; ++q)
           acc[mt][q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[q], a, acc[mt][q], 0, 0, 0, 127, 0, 127);
       }
     }
@@ -294,28 +335,37 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
   // Epilogue: weights first, so lane l of tile (mt, q) holds output row
   // mt*32 + (l % 32) at the staged columns 8 (r / 4) + 4 (l / 32) + (r % 4),
   // r = 0..15: four runs of four consecutive columns. The column scales are
-  // folded into the accumulators first, one run at a time (every row tile of
-  // the wave shares them), so that few values are live at once; then the
-  // row scale and SwiGLU. Lanes l and l ^ 32 swap runs so that each writes 8
-  // consecutive bf16 values (16 bytes).
+  // folded into the accumulators first, one column at a time (every row tile
+  // of the wave shares them), so that few values are live at once; then the
+  // row scale (and for GEMM1 SwiGLU). Lanes l and l ^ 32 swap runs so that
+  // each writes 8 consecutive bf16 values (16 bytes). Output columns: GEMM1
+  // I (h), GEMM2 N; row stride alike.
+  constexpr int kOutTiles = GATED ? NTH : NQ;
+  const int ncols = GATED ? I : N;
+  auto out_col0 = [&](const Tile& t, int q) {
+    return GATED ? t.nb * (BN / 2) + wn * (BN / 2 / WN) + q * 32 : t.nb * BN + wn * (BN / WN) + q * 32;
+  };
   auto store_tile = [&](const Tile& t) {
     const int mrows = t.r1 - t.r0;
     const float* sc = b_scale + (size_t)t.e * N;
 #pragma unroll
-    for (int nt = 0; nt < NTH; ++nt) {
-      const int gcol0 = t.nb * (BN / 2) + wn * (BN / 2 / WN) + nt * 32;  // first h column of the tile
+    for (int q = 0; q < kOutTiles; ++q) {
+      const int gcol0 = out_col0(t, q);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = gcol0 + 8 * q + 4 * hi + j;
-          const int cc = col < I ? col : 0;
+      for (int r = 0; r < 16; ++r) {
+        const int col = gcol0 + 8 * (r / 4) + 4 * hi + (r % 4);
+        const int cc = col < ncols ? col : 0;
+        if constexpr (GATED) {
           const float sg = sc[cc], su = sc[I + cc];
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
-            acc[mt][nt][4 * q + j] *= sg;
-            acc[mt][NTH + nt][4 * q + j] *= su;
+            acc[mt][q][r] *= sg;
+            acc[mt][NTH + q][r] *= su;
           }
+        } else {
+          const float sn = sc[cc];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt][q][r] *= sn;
         }
       }
     }
@@ -325,14 +375,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
       const bool row_ok = mt < vm && row < mrows;
       const float sa = row_ok ? a_scale[t.r0 + row] : 0.f;
 #pragma unroll
-      for (int nt = 0; nt < NTH; ++nt) {
-        const int gcol0 = t.nb * (BN / 2) + wn * (BN / 2 / WN) + nt * 32;  // first h column of the tile
+      for (int q = 0; q < kOutTiles; ++q) {
+        const int gcol0 = out_col0(t, q);
         uint32_t pk[8];
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const float h0 = swiglu_f32(acc[mt][nt][r] * sa, acc[mt][NTH + nt][r] * sa);
-          const float h1 = swiglu_f32(acc[mt][nt][r + 1] * sa, acc[mt][NTH + nt][r + 1] * sa);
-          pk[r / 2] = (uint32_t)f32_to_bf16(h0) | ((uint32_t)f32_to_bf16(h1) << 16);
+          float v0, v1;
+          if constexpr (GATED) {
+            v0 = swiglu_f32(acc[mt][q][r] * sa, acc[mt][NTH + q][r] * sa);
+            v1 = swiglu_f32(acc[mt][q][r + 1] * sa, acc[mt][NTH + q][r + 1] * sa);
+          } else {
+            v0 = acc[mt][q][r] * sa;
+            v1 = acc[mt][q][r + 1] * sa;
+          }
+          pk[r / 2] = (uint32_t)f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16);
         }
         // Runs q = 0..3 are pk[2q], pk[2q+1] (columns 8q + 4 hi .. +3). Of the
         // runs 2p and 2p+1, lane half 0 keeps run 2p and receives the
@@ -345,9 +401,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
           const uint32_t g0 = (uint32_t)__shfl_xor((int)s0, 32);
           const uint32_t g1 = (uint32_t)__shfl_xor((int)s1, 32);
           const int col = gcol0 + 16 * p + 8 * hi;
-          if (row_ok && col < I) {
+          if (row_ok && col < ncols) {
             const u32x4_t v = hi ? u32x4_t{g0, g1, k0, k1} : u32x4_t{k0, k1, g0, g1};
-            *(u32x4_t*)(C + (size_t)(t.r0 + row) * I + col) = v;
+            *(u32x4_t*)(C + (size_t)(t.r0 + row) * ncols + col) = v;
           }
         }
       }
@@ -364,7 +420,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int q = 0; q < 2 * NTH; ++q)
+      for (int q = 0; q < NQ; ++q)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mt][q][r] = 0.f;
     int slot = 0;
@@ -394,15 +450,29 @@ constexpr int kF8BM = 256, kF8BK = 64, kF8Cap = 4, kF8WM = 4, kF8WN = 4;
 constexpr int kF8SmallBM = 32, kF8SmallBK = 128, kF8SmallCap = 3, kF8SmallWM = 1, kF8SmallWN = 4;
 constexpr int kF8SmallRowsPerExpert = 64;
 
-template <int BM, int BK, int CAP, int WM, int WN>
-void launch_f8f8_cfg(const uint8_t* Aq, const float* a_scale, const int32_t* offsets, int E, int rows, int H,
-                     const uint8_t* W13q, const float* s13, int I, void* h, hipStream_t s) {
-  const int NB = ceil_div(I, BN / 2);
+// C (rows, ncols) bf16 = (A codes x A row scales) . (B codes x B column
+// scales)^T over each expert's rows: GEMM1 (GATED: B = W13 codes (E, 2I, H),
+// h = SwiGLU of the paired columns, ncols = I) or GEMM2 (B = W2 codes
+// (E, H, I), ncols = H).
+template <bool GATED, int BM, int BK, int CAP, int WM, int WN>
+void launch_f8f8_cfg(const uint8_t* Aq, const float* a_scale, const int32_t* offsets, int E, int rows, int Kdim,
+                     const uint8_t* Bq, const float* b_scale, int N, int I, void* C, hipStream_t s) {
+  const int NB = GATED ? ceil_div(I, BN / 2) : ceil_div(N, BN);
   const int n_slots = max_row_tiles(rows, E, BM) * NB;
   const int grid = std::min(n_slots, stream_cu_count(s));
-  gemm_f8f8_kernel<BM, BK, CAP, WM, WN><<<grid, 64 * WM * WN, 0, s>>>(Aq, a_scale, offsets, E, rows, H, W13q,
-                                                             (long long)2 * I * H, s13, 2 * I, I, (uint16_t*)h, NB,
-                                                             n_slots);
+  gemm_f8f8_kernel<GATED, BM, BK, CAP, WM, WN><<<grid, 64 * WM * WN, 0, s>>>(
+      Aq, a_scale, offsets, E, rows, Kdim, Bq, (long long)N * Kdim, b_scale, N, I, (uint16_t*)C, NB, n_slots);
+}
+
+template <bool GATED>
+void launch_f8f8(const uint8_t* Aq, const float* a_scale, const int32_t* offsets, int E, int rows, int Kdim,
+                 const uint8_t* Bq, const float* b_scale, int N, int I, void* C, hipStream_t s) {
+  if ((long long)rows <= (long long)kF8SmallRowsPerExpert * E)
+    launch_f8f8_cfg<GATED, kF8SmallBM, kF8SmallBK, kF8SmallCap, kF8SmallWM, kF8SmallWN>(Aq, a_scale, offsets, E, rows,
+                                                                                       Kdim, Bq, b_scale, N, I, C, s);
+  else
+    launch_f8f8_cfg<GATED, kF8BM, kF8BK, kF8Cap, kF8WM, kF8WN>(Aq, a_scale, offsets, E, rows, Kdim, Bq, b_scale, N, I,
+                                                             C, s);
 }
 
 }  // namespace
@@ -415,10 +485,18 @@ size_t fp8_padded_rows(int n, int E, int K) {
 hipError_t launch_quantize_rows_fp8(const void* x, int n, int H, moe_dtype dt, uint8_t* codes, float* scales,
                                     hipStream_t s) {
   if (n == 0) return hipSuccess;
-  if (dt == MOE_BF16)
-    quantize_rows_kernel<true><<<ceil_div(n, 4), 256, 0, s>>>(x, n, H, codes, scales);
-  else
-    quantize_rows_kernel<false><<<ceil_div(n, 4), 256, 0, s>>>(x, n, H, codes, scales);
+  const int g = ceil_div(n, 4);
+  if (dt == MOE_BF16) {
+    if (H <= 2048)
+      quantize_rows_kernel<true, 4><<<g, 256, 0, s>>>(x, n, H, codes, scales);
+    else
+      quantize_rows_kernel<true, 0><<<g, 256, 0, s>>>(x, n, H, codes, scales);
+  } else {
+    if (H <= 2048)
+      quantize_rows_kernel<false, 4><<<g, 256, 0, s>>>(x, n, H, codes, scales);
+    else
+      quantize_rows_kernel<false, 0><<<g, 256, 0, s>>>(x, n, H, codes, scales);
+  }
   return hipGetLastError();
 }
 
@@ -437,11 +515,14 @@ hipError_t launch_w13_swiglu_fp8a(const uint8_t* x_q, const float* x_scale, cons
                                   int rows_max, const uint8_t* W13q, const float* s13, int E, int H, int I, void* h,
                                   hipStream_t s) {
   if (rows_max == 0) return hipSuccess;
-  if ((long long)rows_max <= (long long)kF8SmallRowsPerExpert * E)
-    launch_f8f8_cfg<kF8SmallBM, kF8SmallBK, kF8SmallCap, kF8SmallWM, kF8SmallWN>(x_q, x_scale, offsets_padded, E, rows_max, H, W13q, s13, I,
-                                                         h, s);
-  else
-    launch_f8f8_cfg<kF8BM, kF8BK, kF8Cap, kF8WM, kF8WN>(x_q, x_scale, offsets_padded, E, rows_max, H, W13q, s13, I, h, s);
+  launch_f8f8<true>(x_q, x_scale, offsets_padded, E, rows_max, H, W13q, s13, 2 * I, I, h, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_w2_fp8a(const uint8_t* h_q, const float* h_scale, const int32_t* offsets_padded, int rows_max,
+                          const uint8_t* W2q, const float* s2, int E, int H, int I, void* Y_perm, hipStream_t s) {
+  if (rows_max == 0) return hipSuccess;
+  launch_f8f8<false>(h_q, h_scale, offsets_padded, E, rows_max, I, W2q, s2, H, I, Y_perm, s);
   return hipGetLastError();
 }
 

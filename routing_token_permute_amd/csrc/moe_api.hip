@@ -86,7 +86,7 @@ ForwardLayout forward_layout(int n, int H, int I, int E, int K, moe_dtype dt) {
 // and Y_perm over the padded rows.
 struct Fp8aLayout {
   size_t logits, ids, w, counts, offsets, offsets_p, splits, perm, inv, pscratch, codes_tok, s_tok, x_q, x_scale,
-      perm_p, inv_p, h, Y_perm, total;
+      perm_p, inv_p, h, h_q, h_scale, Y_perm, total;
 };
 
 Fp8aLayout fp8a_layout(int n, int H, int I, int E, int K) {
@@ -115,6 +115,8 @@ Fp8aLayout fp8a_layout(int n, int H, int I, int E, int K) {
   L.perm_p = take(R * 4);
   L.inv_p = take(nk * 4);
   L.h = take(R * I * 2);
+  L.h_q = take(R * I);
+  L.h_scale = take(R * 4);
   L.Y_perm = take(R * H * 2);
   L.total = o;
   return L;
@@ -907,6 +909,20 @@ moe_status moe_expert_w13_swiglu_fp8a(const uint8_t* x_q, const float* x_scale, 
   return from_hip(launch_w13_swiglu_fp8a(x_q, x_scale, offsets_padded, rows_max, W13q, s13, E, H, I, h, stream));
 }
 
+moe_status moe_expert_w2_fp8a(const uint8_t* h_q, const float* h_scale, const int32_t* offsets_padded, int rows_max,
+                              const uint8_t* W2q, const float* s2, int E, int H, int I, void* Y_perm,
+                              hipStream_t stream) {
+  if (rows_max < 0 || E < 1 || E > kMaxExperts || !hidden_ok(H, MOE_BF16) || !hidden_ok(I, MOE_BF16) ||
+      I % 128 != 0)
+    return MOE_EINVAL;
+  if (rows_max == 0) return MOE_OK;
+  if (h_q == nullptr || h_scale == nullptr || offsets_padded == nullptr || W2q == nullptr || s2 == nullptr ||
+      Y_perm == nullptr)
+    return MOE_EINVAL;
+  if (!vec_ok({h_q, W2q, s2, Y_perm}) || !word_ok({h_scale, offsets_padded})) return MOE_EINVAL;
+  return from_hip(launch_w2_fp8a(h_q, h_scale, offsets_padded, rows_max, W2q, s2, E, H, I, Y_perm, stream));
+}
+
 size_t moe_forward_fp8a_workspace_size(int n, int H, int I, int E, int K) {
   if (n < 0 || H < 1 || I < 1 || E < 1 || K < 1) return 0;
   return fp8a_layout(n, H, I, E, K).total;
@@ -918,7 +934,8 @@ moe_status moe_forward_fp8a(const void* x, const void* W_gate, const float* bias
                             float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
   if (dt != MOE_BF16) return MOE_EUNSUPPORTED;
-  if (n < 0 || !experts_ok(E, K) || !hidden_ok(H, dt) || H % 128 != 0 || !hidden_ok(I, dt)) return MOE_EINVAL;
+  if (n < 0 || !experts_ok(E, K) || !hidden_ok(H, dt) || H % 128 != 0 || !hidden_ok(I, dt) || I % 128 != 0)
+    return MOE_EINVAL;
   if ((long long)n * K > INT32_MAX / 2) return MOE_EINVAL;
   if (n > 0 && (x == nullptr || W_gate == nullptr || W13q == nullptr || s13 == nullptr || W2q == nullptr ||
                 s2 == nullptr || y == nullptr))
@@ -955,7 +972,13 @@ moe_status moe_forward_fp8a(const void* x, const void* W_gate, const float* bias
     e = launch_dispatch_fp8(counts, offsets, perm, n, E, K, codes_tok, s_tok, H, offsets_p, x_q, x_scale, perm_p,
                             inv_p, stream);
   if (e == hipSuccess) e = launch_w13_swiglu_fp8a(x_q, x_scale, offsets_p, R, W13q, s13, E, H, I, base + L.h, stream);
-  if (e == hipSuccess) e = launch_w2_fp8(base + L.h, offsets_p, R, W2q, s2, E, H, I, base + L.Y_perm, stream);
+  // h per row in FP8 (rows past the last group are quantized too and never read), then GEMM2 on the FP8 MFMA.
+  if (e == hipSuccess)
+    e = launch_quantize_rows_fp8(base + L.h, R, I, MOE_BF16, (uint8_t*)(base + L.h_q), (float*)(base + L.h_scale),
+                                 stream);
+  if (e == hipSuccess)
+    e = launch_w2_fp8a((uint8_t*)(base + L.h_q), (float*)(base + L.h_scale), offsets_p, R, W2q, s2, E, H, I,
+                       base + L.Y_perm, stream);
   if (e == hipSuccess) e = launch_combine_rows(base + L.Y_perm, R, inv_p, w, n, H, K, dt, y, stream);
   return from_hip(e);
 }

@@ -165,6 +165,10 @@ hipError_t launch_dispatch_fp8(const int32_t* counts, const int32_t* offsets, co
 hipError_t launch_w13_swiglu_fp8a(const uint8_t* x_q, const float* x_scale, const int32_t* offsets_padded,
                                   int rows_max, const uint8_t* W13q, const float* s13, int E, int H, int I, void* h,
                                   hipStream_t s);
+// GEMM2 with FP8 activations: Y_perm (rows_max, H) bf16 = (h codes x per-row
+// scales) . (W2 codes x column scales) over the padded receive buffer's rows.
+hipError_t launch_w2_fp8a(const uint8_t* h_q, const float* h_scale, const int32_t* offsets_padded, int rows_max,
+                          const uint8_t* W2q, const float* s2, int E, int H, int I, void* Y_perm, hipStream_t s);
 
 }  // namespace moe
 
@@ -227,6 +231,20 @@ __device__ __forceinline__ uint32_t e4m3_nearest(float x) {
     code = ((uint32_t)ex << 3) | (uint32_t)m;
   }
   return code == 0 ? 0u : (sign | code);
+}
+
+// Four nearest E4M3 codes packed little-endian, by the gfx950 conversion
+// (v_cvt_pk_fp8_f32: OCP E4M3, round to nearest even, subnormals kept), with a
+// negative zero mapped to code 0 as e4m3_nearest does. For |v| < 464, where
+// nearest-with-saturation and the plain nearest value agree (the callers'
+// quotients x / s are at most 448 (1 + 2^-23)).
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  const uint32_t w = (uint32_t)r;
+  // bit 7 of each byte: set where the byte's magnitude is nonzero
+  const uint32_t nz = ((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) & 0x80808080u;
+  return w & (0x7F7F7F7Fu | nz);
 }
 
 __device__ __forceinline__ u32x4_t lds_read_b128(const lds_char_t* p) {

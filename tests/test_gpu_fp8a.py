@@ -32,7 +32,8 @@ def dev():
     return require_gpu()
 
 
-@pytest.mark.parametrize("n,H,dtype", [(7, 128, "bf16"), (300, 2048, "bf16"), (33, 192, "f32"), (4096, 2048, "bf16")])
+@pytest.mark.parametrize("n,H,dtype", [(7, 128, "bf16"), (300, 2048, "bf16"), (33, 192, "f32"), (4096, 2048, "bf16"),
+                                     (9, 4096, "bf16"), (5, 2184, "f32"), (40, 1024, "bf16")])
 def test_quantize_rows_fp8_bit_exact(dev, n, H, dtype):
     rng = np.random.default_rng(n + H)
     if dtype == "bf16":
@@ -52,6 +53,34 @@ def test_quantize_rows_fp8_bit_exact(dev, n, H, dtype):
     assert (scales.cpu().numpy().view(np.uint32) == s_ref.view(np.uint32)).all(), "scales differ"
     bad = int((codes.cpu().numpy() != c_ref).sum())
     assert bad == 0, f"{bad} codes differ"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quantize_rows_fp8_ties_subnormals_and_signed_zero(dev, dtype):
+    """Rows whose amax is 448 (scale exactly 1) holding every midpoint between consecutive E4M3 values, normal
+    and subnormal, both signs, and tiny values that round to zero from either side: the codes must be the
+    oracle's bit for bit (ties to the even mantissa, no negative-zero code)."""
+    t = of8.e4m3_decode_table()[:0x7F]
+    mids = (t[:-1] + t[1:]) / 2
+    vals = np.concatenate([[448.0], mids, -mids, t, -t[1:], [2.0**-11, -2.0**-11, -2.0**-12, 0.0, -0.0]])
+    H = 512
+    row = np.zeros(H)
+    row[:vals.size] = vals
+    x = np.stack([row, np.roll(row, 7), -row]).astype(np.float32)
+    if dtype == "bf16":
+        bits = x.view(np.uint32)
+        assert ((bits & 0xFFFF) == 0).all()  # every value is exact in bf16
+        xd = torch.from_numpy((bits >> 16).astype(np.uint16).view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        xd = torch.from_numpy(x).to(dev)
+    codes, scales = moe.moe_quantize_rows_fp8(xd)
+    torch.cuda.synchronize()
+    c_ref, s_ref = of8.quantize_rows(x)
+    assert (scales.cpu().numpy() == 1.0).all() and (s_ref == 1.0).all()
+    got = codes.cpu().numpy()
+    bad = np.argwhere(got != c_ref)
+    assert bad.size == 0, f"{len(bad)} codes differ, e.g. value {x[tuple(bad[0])]}: {got[tuple(bad[0])]:#x} vs " \
+                          f"{c_ref[tuple(bad[0])]:#x}"
 
 
 def _route_and_dispatch(dev, w, t):
@@ -129,13 +158,54 @@ def test_w13_swiglu_fp8a(dev, n, H, I, E, K):  # noqa: E741
     assert_close(got[real], ref[real], "bf16", f"fp8a gate_up n={n} E={E}", intermediate=True)
 
 
+@pytest.mark.parametrize("R_real,E,H,I,skew", [(700, 8, 256, 128, False), (200, 16, 384, 256, True),
+                                                (32768, 64, 2048, 1024, False), (248, 62, 2048, 1024, False)])
+def test_w2_fp8a(dev, R_real, E, H, I, skew):  # noqa: E741
+    """GEMM2 on FP8 activations alone: seeded h rows quantized per row by the oracle, in a receive buffer
+    padded to 16-row groups (padding rows code 0, scale 0), against the oracle's dequantized product."""
+    rng = np.random.default_rng(R_real + E)
+    p = rng.dirichlet(np.full(E, 0.3 if skew else 5.0))
+    counts = rng.multinomial(R_real, p)
+    P = of8.padded_offsets(counts)
+    R = int(P[-1])
+    h = (rng.standard_normal((R, I)) * rng.uniform(0.1, 4.0, (R, 1))).astype(np.float32)
+    codes, scales = of8.quantize_rows(h)
+    real = np.zeros(R, bool)
+    for e in range(E):
+        real[P[e]:P[e] + counts[e]] = True
+    codes[~real] = 0
+    scales[~real] = 0
+    W2 = (rng.standard_normal((E, I, H)) * 0.02).astype(np.float32)
+    c2, r2 = of8.quantize_columns(W2)
+    Y = moe.moe_expert_w2_fp8a(torch.from_numpy(codes).to(dev), torch.from_numpy(scales).to(dev),
+                               torch.from_numpy(P.astype(np.int32)).to(dev), torch.from_numpy(c2).to(dev),
+                               torch.from_numpy(r2).to(dev))
+    torch.cuda.synchronize()
+    ref = om.grouped_down(of8.dequantize_rows(codes, scales), P, of8.dequantize_columns(c2, r2))
+    got = to_f64(Y[:R])
+    assert (got[~real] == 0).all(), "padding rows must be zero"
+    assert_close(got[real], ref[real], "bf16", f"fp8a down R={R} E={E} H={H} I={I}", intermediate=True)
+
+
 @pytest.mark.parametrize("name", ["decode_bf16", "olmoe_bf16", "olmoe_skewed_bf16", "small"])
 def test_forward_fp8a_configs(dev, name):
+    """The layer against the oracle, every row. Two integer decisions are compared given identical
+    floating-point inputs, as the routing is: the ids from the device's fp32 logits (held to the fp64 router
+    product), and the FP8 codes of h from the device's bf16 h (held to the oracle's fp64 h under the
+    intermediate bounds): an h element within a bf16 ulp of an E4M3 midpoint may round either way, and a
+    flipped code moves y by up to 2^-3 of that element's share. The rest of the layer is then held to the
+    bf16 bounds: y against the oracle's product of those codes and the oracle's combine."""
     w = make_config(name) if name != "small" else make_layer(200, 256, 128, 16, 4, dtype="bf16", renorm=True, seed=8)
     t = layer_tensors(w, dev)
     (q13, s13, q2, s2), (c13, r13, c2, r2) = _fp8_weights(w, t)
     y, logits, ids, wts, counts = moe.moe_forward_fp8a(t["x"], t["W_gate"], q13, s13, q2, s2, w.K, w.renorm,
                                                        bias=t["bias"], routing_out=True)
+    # The same kernels stage by stage, for the device's h and its codes.
+    meta = moe.moe_permute(ids, None, w.E)
+    codes_tok, s_tok = moe.moe_quantize_rows_fp8(t["x"])
+    d8 = moe.moe_dispatch_fp8(meta, codes_tok, s_tok, w.K)
+    h = moe.moe_expert_w13_swiglu_fp8a(d8["x_q"], d8["x_scale"], d8["offsets_padded"], q13, s13)
+    hq, hs = moe.moe_quantize_rows_fp8(h)
     torch.cuda.synchronize()
     ref_logits = oracle.router_logits(w.x_f32, w.W_gate_f32, w.bias)
     L = logits.cpu().numpy()
@@ -146,8 +216,23 @@ def test_forward_fp8a_configs(dev, name):
                            routing_logits_f32=L)
     assert (ids.cpu().numpy() == ref["e_top"]).all()
     assert (counts.cpu().numpy() == ref["counts"]).all()
-    assert_close(to_f64(y), ref["y"], "bf16", f"forward fp8a {name}")
-    # FP8 activations move the output by about their quantization error, not more.
+    rd = of8.dispatch_fp8(w.x_f32, ids.cpu().numpy(), w.E)
+    P = rd["offsets"]
+    R = int(P[-1])
+    real = rd["perm"] >= 0
+    h_ref = om.grouped_gate_up(of8.dequantize_rows(rd["codes"], rd["scales"]), P, of8.dequantize_columns(c13, r13))
+    h_dev = h[:R].float().cpu().numpy()
+    assert_close(h_dev[real].astype(np.float64), h_ref[real], "bf16", f"fp8a layer h {name}", intermediate=True)
+    hc_ref, hs_ref = of8.quantize_rows(h_dev)
+    assert (hs[:R].cpu().numpy().view(np.uint32) == hs_ref.view(np.uint32)).all(), "h scales differ"
+    assert int((hq[:R].cpu().numpy() != hc_ref).sum()) == 0, "h codes differ"
+    Y_ref = om.grouped_down(of8.dequantize_rows(hc_ref, hs_ref), P, of8.dequantize_columns(c2, r2))
+    y_ref = om.combine_slot_order(Y_ref, rd["inv"], ref["w_top"], w.n, w.K)
+    assert_close(to_f64(y), y_ref, "bf16", f"forward fp8a {name}")
+    # Against the oracle's own layer (its h rounded from fp64): only the code flips of near-midpoint elements
+    # separate the two, and FP8 activations move the output by about their quantization error, not more.
+    rel = np.linalg.norm(to_f64(y) - ref["y"]) / np.linalg.norm(ref["y"])
+    assert rel < 1e-2
     wq = of8.forward_fp8(w.x_f32, w.W_gate_f32, c13, r13, c2, r2, w.K, w.renorm, bias=w.bias, routing_logits_f32=L)
     rel = np.linalg.norm(ref["y"] - wq["y"]) / np.linalg.norm(wq["y"])
     print(f"[forward fp8a {name}] FP8 vs bf16 activations: rel_frob={rel:.3e}", flush=True)
