@@ -487,7 +487,7 @@ def main():
         _bench_train(args)
         return
     if args.workload in ("decode_fp8", "olmoe_fp8", "decode_fp8a", "olmoe_fp8a"):
-        _bench_fp8(args)
+        print(json.dumps(_bench_fp8(args)), flush=True)
         return
     dev = torch.device("cuda:0")
     w = make_config(args.workload)
@@ -512,6 +512,11 @@ def main():
                                       "frac_hbm_over_forward": round(wbytes / (r["ms"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
             configs[name] = r
         configs["ep_share_bf16"] = _ep_share_core(args, torch, dev, cu_split=False, cpu=False)[0]
+        # The FP8 layers ([Fusion] §8.4): FP8 activations with per-row scales and FP8 weights, on the FP8 MFMA.
+        for name in ("olmoe_fp8a", "decode_fp8a"):
+            r = _bench_fp8(args, workload=name, cpu_leg=False)
+            configs[name] = {k: r[k] for k in ("ms_per_step", "value", "unit", "step_spread", "ms_per_step_bf16_weights",
+                                               "speedup_over_bf16_weights", "dtype", "stages", "roofline")}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -834,7 +839,7 @@ def _bench_train(args):
     print(json.dumps(out), flush=True)
 
 
-def _bench_fp8(args):
+def _bench_fp8(args, workload=None, cpu_leg=True):
     """The layer with FP8 E4M3 expert weights (per-column fp32 scales, quantized
     on the device before timing) on the decode (n=32) or OLMoE (n=4096) batch:
     tokens/s, the FP8 GEMMs' bandwidth against their weight bytes, and the bf16
@@ -847,8 +852,9 @@ def _bench_fp8(args):
     from workloads import make_config
 
     dev = torch.device("cuda:0")
-    base = "decode_bf16" if args.workload.startswith("decode") else "olmoe_bf16"
-    act8 = args.workload.endswith("fp8a")
+    wl = workload or args.workload
+    base = "decode_bf16" if wl.startswith("decode") else "olmoe_bf16"
+    act8 = wl.endswith("fp8a")
     w = make_config(base)
     n, H, I, E, K = w.n, w.H, w.I, w.E, w.K  # noqa: E741
 
@@ -942,7 +948,7 @@ def _bench_fp8(args):
         roof = {"kernel": kname, "bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
                 "frac": round(tf / peak, 4), "traffic": None}
     cpu = None
-    if not args.no_cpu_baseline:
+    if cpu_leg and not args.no_cpu_baseline:
         import oracle
 
         c13, r13 = oracle.fp8.quantize_columns(w.W13_f32)
@@ -976,7 +982,7 @@ def _bench_fp8(args):
         "vs_baseline": None,
         "dtype": "fp8 e4m3 activations (per-token scales) and weights" if act8 else "bf16 activations, fp8 e4m3 weights",
         "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights quantized per output column; OLMoE layer shapes)",
-        "config": {"workload": args.workload, "n": n, "H": H, "I": I, "E": E, "K": K, "renorm": bool(w.renorm)},
+        "config": {"workload": wl, "n": n, "H": H, "I": I, "E": E, "K": K, "renorm": bool(w.renorm)},
         "stages": stages,
         "roofline": roof,
         "experts_hit": hit,
@@ -984,7 +990,7 @@ def _bench_fp8(args):
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(dev),
     }
-    print(json.dumps(out), flush=True)
+    return out
 
 
 def _cpu_baseline_train(w, dy_seed, min_seconds, sample_tokens=512):
