@@ -54,6 +54,8 @@ def _parse():
                    help="olmoe_bf16: leave out the other configurations (tiny, skewed, decode, EP share)")
     p.add_argument("--profile-forward", type=int, default=0, metavar="N",
                    help="only run N moe_forward calls of the workload (for rocprofv3 counter passes)")
+    p.add_argument("--profile-layer", choices=["bf16", "fp8a", "persistent"], default="bf16",
+                   help="with --profile-forward: moe_forward (bf16), moe_forward_fp8a or moe_forward_persistent")
     p.add_argument("--summarize-counters", nargs="+", metavar="DIR",
                    help="turn rocprofv3 --pmc csv directories into the per-kernel counter summary printed on stdout")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle wall time for the CPU baseline")
@@ -97,6 +99,15 @@ def _kernel_label(name):
         args = name.split("gemm_bf16_kernel<", 1)[1].split(">", 1)[0].split(",")
         gated, bm = args[0].strip() == "true", args[3].strip()
         return ("gemm1_swiglu" if gated else "gemm2") + f"_bm{bm}"
+    if "gemm_f8f8_kernel<" in name:
+        args = name.split("gemm_f8f8_kernel<", 1)[1].split(">", 1)[0].split(",")
+        gated, bm = args[0].strip() == "true", args[1].strip()
+        return ("gemm1_swiglu_f8f8" if gated else "gemm2_f8f8") + f"_bm{bm}"
+    for k, lab in (("quantize_rows_kernel", "quantize_rows_fp8"), ("dispatch_fp8_kernel", "dispatch_fp8"),
+                   ("quantize_fp8_kernel", "quantize_weights_fp8"), ("fused_ffn_kernel", "fused_ffn"),
+                   ("fill_zero_kernel", "fill_zero")):
+        if k in name:
+            return lab
     if "FillFunctor" in name:
         return "fill_1GiB"
     if "copy" in name.lower() or "elementwise" in name.lower():
@@ -153,6 +164,8 @@ def _summarize_counters(dirs):
                     k[key] = round(m[c] / (cus * cyc), 4)
         if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in m:
             k["mfma_bf16_TFLOP/s"] = round(m["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / dur / 1e12, 1)
+        if "SQ_INSTS_VALU_MFMA_MOPS_F8" in m:
+            k["mfma_f8_TFLOP/s"] = round(m["SQ_INSTS_VALU_MFMA_MOPS_F8"] * 512 / dur / 1e12, 1)
         if "SQ_WAIT_ANY" in m and m.get("SQ_WAVE_CYCLES"):
             k["wave_wait_share"] = round(m["SQ_WAIT_ANY"] / m["SQ_WAVE_CYCLES"], 4)
         if "SQ_LDS_BANK_CONFLICT" in m:
@@ -500,16 +513,18 @@ def main():
     configs = {}
     if args.workload == "olmoe_bf16" and not args.headline_only:
         for name in ("tiny_f32", "olmoe_skewed_bf16", "decode_bf16"):
-            r = _layer_bench(make_config(name), args, torch, moe, dev, detail=False)
+            wc = make_config(name)
+            r = _layer_bench(wc, args, torch, moe, dev, detail=False)
             if name == "tiny_f32":  # parity configuration: launch-bound, no roofline
                 r = {k: r[k] for k in ("ms", "tokens/s", "step_spread", "expert_load")}
                 r["note"] = "parity configuration (n=64, H=128): launch-bound, time reported, no roofline"
             if name == "decode_bf16":
-                wc = make_config(name)
                 hit = r["expert_load"]["experts_hit"]
                 wbytes = hit * 3 * wc.H * wc.I * 2  # W13 (H x 2I) and W2 (I x H) of the hit experts
                 r["weight_stream"] = {"bytes": wbytes, "GB/s_over_forward": round(wbytes / (r["ms"] * 1e-3) / 1e9, 1),
                                       "frac_hbm_over_forward": round(wbytes / (r["ms"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+            if not args.no_cpu_baseline:  # a short oracle sample of the same configuration, all threads and one
+                r["cpu_baseline"] = _cpu_baseline(wc, min_seconds=2.0, one_core_seconds=2.0)
             configs[name] = r
         configs["ep_share_bf16"] = _ep_share_core(args, torch, dev, cu_split=False, cpu=False)[0]
         # The FP8 layers ([Fusion] §8.4): FP8 activations with per-row scales and FP8 weights, on the FP8 MFMA.
@@ -562,10 +577,19 @@ def _profile_forward(args, torch, moe):
     w = make_config(args.workload)
     x, Wg, W13, W2 = (_to_dev_bits(w, k, dev, torch) for k in ("x", "W_gate", "W13", "W2"))
     bias = None if w.bias is None else torch.from_numpy(w.bias).to(dev)
+    if args.profile_layer == "fp8a":  # FP8 activations and weights (the weights quantized once, first)
+        q13, s13 = moe.moe_quantize_fp8(W13)
+        q2, s2 = moe.moe_quantize_fp8(W2)
+        step = lambda: moe.moe_forward_fp8a(x, Wg, q13, s13, q2, s2, w.K, w.renorm, bias=bias)  # noqa: E731
+    elif args.profile_layer == "persistent":
+        step = lambda: moe.moe_forward_persistent(x, Wg, W13, W2, w.K, w.renorm, bias=bias)  # noqa: E731
+    else:
+        step = lambda: moe.moe_forward(x, Wg, W13, W2, w.K, w.renorm, bias=bias)  # noqa: E731
     for _ in range(args.profile_forward):
-        moe.moe_forward(x, Wg, W13, W2, w.K, w.renorm, bias=bias)
+        step()
     torch.cuda.synchronize()
-    print(json.dumps({"profiled": args.workload, "forwards": args.profile_forward}), flush=True)
+    print(json.dumps({"profiled": args.workload, "layer": args.profile_layer, "forwards": args.profile_forward}),
+          flush=True)
 
 
 def _ep_share_core(args, torch, dev, cu_split=True, cpu=True):
