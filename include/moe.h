@@ -297,8 +297,8 @@ moe_status moe_forward_noalloc(const void* x, const void* W_gate, const float* b
  * L2 tile starts once every L1 tile of its rows has published h (per-row-
  * tile counters with agent-scope release/acquire); h lives in a ring pool of
  * `pool_row_tiles` row-tile slots per queue (0: one buffer for all rows).
- * Outputs are bitwise equal to moe_forward's. bf16 only (MOE_EUNSUPPORTED
- * otherwise); warmup_row_tiles >= 1, and pool_row_tiles either 0 or larger
+ * Outputs are bitwise equal to moe_forward's. bf16 only, and at most 2^24
+ * tasks per queue (MOE_EUNSUPPORTED otherwise); warmup_row_tiles >= 1, and pool_row_tiles either 0 or larger
  * than warmup_row_tiles (MOE_EINVAL otherwise), so that every wait targets
  * a task handed out earlier and the schedule cannot deadlock. Each wait is
  * bounded nonetheless: if one runs out (a scheduling fault, never expected)

@@ -518,6 +518,10 @@ moe_status moe_forward_persistent(const void* x, const void* W_gate, const float
     return MOE_EINVAL;
   if (!vec_ok({ws})) return MOE_EINVAL;
   if (n == 0) return counts_out ? from_hip(launch_fill_zero(counts_out, (size_t)E * 4, stream)) : MOE_OK;
+  // A ticket packs its queue into the top byte: at most 2^24 tasks per queue.
+  const long long tasks_per_queue =
+      ((long long)fused_ffn_max_row_tiles(n * K, E) / 8 + 1) * (ceil_div(I, 128) + ceil_div(H, 256));
+  if (tasks_per_queue >= (1LL << 24)) return MOE_EUNSUPPORTED;
   const PersistentLayout L = persistent_layout(n, H, I, E, K, pool_row_tiles);
   if (ws == nullptr || ws_bytes < L.total) return MOE_EWORKSPACE;
   char* base = (char*)ws;
