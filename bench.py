@@ -922,24 +922,25 @@ def _bench_fp8(args, workload=None, cpu_leg=True):
         "gemm2_fp8": _time_region_graph(lambda: moe.moe_expert_w2_fp8(h, meta["offsets"], q2, s2, Y_perm=Yp), R, torch),
     }
     nk = n * K
-    if act8:  # the FP8 dispatch and the FP8 x FP8 GEMM1 on the padded receive buffer
+    if act8:  # the stages moe_forward_fp8a runs: FP8 rows read in place, FP8 x FP8 GEMMs, h quantized per row
         codes_tok, s_tok = moe.moe_quantize_rows_fp8(x)
+        h8 = moe.moe_expert_w13_swiglu_gather_fp8a(codes_tok, s_tok, meta["perm"], K, meta["offsets"], q13, s13)
+        hq, hs = moe.moe_quantize_rows_fp8(h8)
+        Y8 = moe.moe_expert_w2_fp8a(hq, hs, meta["offsets"], q2, s2)
         d8 = moe.moe_dispatch_fp8(meta, codes_tok, s_tok, K)
-        h8 = moe.moe_expert_w13_swiglu_fp8a(d8["x_q"], d8["x_scale"], d8["offsets_padded"], q13, s13)
         torch.cuda.synchronize()
         rpad = int(d8["offsets_padded"][-1].item())
         st["quantize_rows_fp8"] = _time_region_graph(lambda: moe.moe_quantize_rows_fp8(x, codes=codes_tok, scales=s_tok),
                                                      R, torch)
-        st["dispatch_fp8"] = _time_region_graph(lambda: moe.moe_dispatch_fp8(meta, codes_tok, s_tok, K, out=d8), R, torch)
         st["gemm1_swiglu_fp8a"] = _time_region_graph(
-            lambda: moe.moe_expert_w13_swiglu_fp8a(d8["x_q"], d8["x_scale"], d8["offsets_padded"], q13, s13, h=h8),
-            R, torch)
-        hq, hs = moe.moe_quantize_rows_fp8(h8)
-        Y8 = moe.moe_expert_w2_fp8a(hq, hs, d8["offsets_padded"], q2, s2)
-        torch.cuda.synchronize()
+            lambda: moe.moe_expert_w13_swiglu_gather_fp8a(codes_tok, s_tok, meta["perm"], K, meta["offsets"], q13, s13,
+                                                          h=h8), R, torch)
         st["quantize_h_fp8"] = _time_region_graph(lambda: moe.moe_quantize_rows_fp8(h8, codes=hq, scales=hs), R, torch)
         st["gemm2_fp8a"] = _time_region_graph(
-            lambda: moe.moe_expert_w2_fp8a(hq, hs, d8["offsets_padded"], q2, s2, Y_perm=Y8), R, torch)
+            lambda: moe.moe_expert_w2_fp8a(hq, hs, meta["offsets"], q2, s2, Y_perm=Y8), R, torch)
+        # The padded receive buffer an expert-parallel exchange would deliver (not on the one-GPU layer's path).
+        st["alt_dispatch_fp8"] = _time_region_graph(lambda: moe.moe_dispatch_fp8(meta, codes_tok, s_tok, K, out=d8),
+                                                    R, torch)
     bytes_ = {  # algorithmic: activations once, FP8 codes and scales of the hit experts once, outputs once
         "gemm1_swiglu_fp8": nk * H * 2 + hit * (2 * I * H + 2 * I * 4) + nk * I * 2 + nk * 4,
         "gemm2_fp8": nk * I * 2 + hit * (H * I + H * 4) + nk * H * 2,
@@ -947,12 +948,11 @@ def _bench_fp8(args, workload=None, cpu_leg=True):
     flops = {"gemm1_swiglu_fp8": 2.0 * nk * H * 2 * I, "gemm2_fp8": 2.0 * nk * I * H}
     if act8:
         bytes_["quantize_rows_fp8"] = n * H * 2 + n * H + n * 4
-        bytes_["dispatch_fp8"] = nk * H + rpad * H + rpad * 8 + nk * 4
-        bytes_["gemm1_swiglu_fp8a"] = rpad * (H + 4) + hit * (2 * I * H + 2 * I * 4) + rpad * I * 2
+        bytes_["alt_dispatch_fp8"] = nk * H + rpad * H + rpad * 8 + nk * 4
+        bytes_["gemm1_swiglu_fp8a"] = n * (H + 4) + nk * 4 + hit * (2 * I * H + 2 * I * 4) + nk * I * 2
         flops["gemm1_swiglu_fp8a"] = 2.0 * nk * H * 2 * I
-        rmax = h8.shape[0]
-        bytes_["quantize_h_fp8"] = rmax * I * 2 + rmax * I + rmax * 4
-        bytes_["gemm2_fp8a"] = rpad * (I + 4) + hit * (H * I + H * 4) + rpad * H * 2
+        bytes_["quantize_h_fp8"] = nk * I * 2 + nk * I + nk * 4
+        bytes_["gemm2_fp8a"] = nk * (I + 4) + hit * (H * I + H * 4) + nk * H * 2
         flops["gemm2_fp8a"] = 2.0 * nk * I * H
     stages = {}
     for k, v in st.items():
@@ -961,7 +961,8 @@ def _bench_fp8(args, workload=None, cpu_leg=True):
         if k in flops:
             stages[k]["TFLOP/s"] = round(flops[k] / (v * 1e-3) / 1e12, 1)
     dom = "gemm1_swiglu_fp8a" if act8 else "gemm1_swiglu_fp8"
-    kname = ("gemm_f8f8_kernel (GEMM1 + SwiGLU, FP8 activations x FP8 weights, FP8 MFMA 32x32x64)" if act8 else
+    kname = ("gemm_f8f8_kernel<GATED, GATHER> (GEMM1 + SwiGLU, FP8 token rows read through perm x FP8 weights, "
+             "FP8 MFMA 32x32x64)" if act8 else
              "gemm_w8_kernel<GATED=true, GATHER=true> (GEMM1 + SwiGLU, FP8 weights)")
     if base == "decode_bf16":
         roof = {"kernel": kname, "bound": "hbm", "achieved": stages[dom]["GB/s"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",

@@ -594,13 +594,22 @@ moe_status moe_forward_fp8(const void* x, const void* W_gate, const float* bias,
  * from moe_quantize_fp8 on W2; Y_perm (rows_max, H) bf16 out (rows past
  * offsets_padded[E] not written). I a multiple of 128.
  *
+ * moe_expert_w13_swiglu_gather_fp8a — moe_expert_w13_swiglu_fp8a with the
+ * activations read in place instead of from a receive buffer: row r of the
+ * expert-major order (offsets, unpadded) is token perm[r] / K of codes_tok
+ * (n, H) uint8 with scale s_tok[perm[r] / K] (moe_quantize_rows_fp8 of x);
+ * perm as from moe_permute; h (n*K, I) bf16 out. H a multiple of 128.
+ *
  * moe_forward_fp8a — the layer with FP8 activations and FP8 weights: moe_route
- * on x (bf16), the moe_permute metadata, moe_quantize_rows_fp8,
- * moe_dispatch_fp8, moe_expert_w13_swiglu_fp8a, moe_quantize_rows_fp8 on h,
- * moe_expert_w2_fp8a over the padded rows, and moe_unpermute_combine through
- * inv_padded. Arguments as moe_forward_fp8 (dt must be MOE_BF16, H and I
- * multiples of 128); ws of at least moe_forward_fp8a_workspace_size(n, H, I,
- * E, K) bytes.
+ * on x (bf16), the moe_permute metadata, moe_quantize_rows_fp8 of x,
+ * moe_expert_w13_swiglu_gather_fp8a, moe_quantize_rows_fp8 of h,
+ * moe_expert_w2_fp8a and moe_unpermute_combine. On one GPU the per-token FP8
+ * rows are read in place through perm, as moe_forward reads x; the padded
+ * receive buffer of moe_dispatch_fp8 is the form an expert-parallel exchange
+ * delivers, which moe_expert_w13_swiglu_fp8a and moe_expert_w2_fp8a take as
+ * well. Arguments as moe_forward_fp8 (dt must be MOE_BF16, H and I multiples
+ * of 128); ws of at least moe_forward_fp8a_workspace_size(n, H, I, E, K)
+ * bytes.
  * ------------------------------------------------------------------------- */
 moe_status moe_quantize_rows_fp8(const void* x, int n, int H, moe_dtype dt, uint8_t* codes, float* scales,
                                  hipStream_t stream);
@@ -612,6 +621,9 @@ moe_status moe_dispatch_fp8(const int32_t* counts, const int32_t* offsets, const
 moe_status moe_expert_w13_swiglu_fp8a(const uint8_t* x_q, const float* x_scale, const int32_t* offsets_padded,
                                       int rows_max, const uint8_t* W13q, const float* s13, int E, int H, int I,
                                       void* h, hipStream_t stream);
+moe_status moe_expert_w13_swiglu_gather_fp8a(const uint8_t* codes_tok, const float* s_tok, const int32_t* perm,
+                                             int n, int K, const int32_t* offsets, const uint8_t* W13q,
+                                             const float* s13, int E, int H, int I, void* h, hipStream_t stream);
 moe_status moe_expert_w2_fp8a(const uint8_t* h_q, const float* h_scale, const int32_t* offsets_padded, int rows_max,
                               const uint8_t* W2q, const float* s2, int E, int H, int I, void* Y_perm,
                               hipStream_t stream);

@@ -89,6 +89,7 @@ SIGNATURES = {
     "moe_dispatch_fp8": (_I, [_VP, _VP, _VP, _I, _I, _I, _VP, _VP, _I, _VP, _VP, _VP, _VP, _VP, _VP]),
     "moe_expert_w13_swiglu_fp8a": (_I, [_VP, _VP, _VP, _I, _VP, _VP, _I, _I, _I, _VP, _VP]),
     "moe_expert_w2_fp8a": (_I, [_VP, _VP, _VP, _I, _VP, _VP, _I, _I, _I, _VP, _VP]),
+    "moe_expert_w13_swiglu_gather_fp8a": (_I, [_VP, _VP, _VP, _I, _I, _VP, _VP, _VP, _I, _I, _I, _VP, _VP]),
     "moe_forward_fp8a_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
     "moe_forward_fp8a": (
         _I,
@@ -962,6 +963,28 @@ def moe_expert_w13_swiglu_fp8a(x_q, x_scale, offsets_padded, W13q, s13, h=None, 
     _need(h, "h", (R, I), torch.bfloat16, dev)
     _check(lib.moe_expert_w13_swiglu_fp8a(_ptr(x_q), _ptr(x_scale), _ptr(offsets_padded), R, _ptr(W13q), _ptr(s13),
                                           E, H, I, _ptr(h), _stream(dev, stream)), "moe_expert_w13_swiglu_fp8a")
+    return h
+
+
+@_on_stream
+def moe_expert_w13_swiglu_gather_fp8a(codes_tok, s_tok, perm, K: int, offsets, W13q, s13, h=None, stream=None):
+    """GEMM1 + SwiGLU on FP8 activations read in place: row r of the expert-major order is token perm[r] // K
+    of the per-token codes (n, H) and scales (n,). Returns h (n*K, I) bf16."""
+    lib = load_library()
+    n, H = codes_tok.shape
+    E, twoI = s13.shape
+    I = twoI // 2  # noqa: E741
+    dev = codes_tok.device
+    _need(codes_tok, "codes_tok", (n, H), torch.uint8)
+    _need(s_tok, "s_tok", (n,), torch.float32, dev)
+    _need(perm, "perm", (n * K,), torch.int32, dev)
+    _need(offsets, "offsets", (E + 1,), torch.int32, dev)
+    _need(W13q, "W13q", (E, 2 * I, H), torch.uint8, dev)
+    h = _empty((n * K, I), torch.bfloat16, dev) if h is None else h
+    _need(h, "h", (n * K, I), torch.bfloat16, dev)
+    _check(lib.moe_expert_w13_swiglu_gather_fp8a(_ptr(codes_tok), _ptr(s_tok), _ptr(perm), n, K, _ptr(offsets),
+                                                 _ptr(W13q), _ptr(s13), E, H, I, _ptr(h), _stream(dev, stream)),
+           "moe_expert_w13_swiglu_gather_fp8a")
     return h
 
 

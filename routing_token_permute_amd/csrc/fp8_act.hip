@@ -211,11 +211,16 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // WM x WN waves split the BM x 256 tile; each wave owns (BM / WM) rows and
 // (256 / WN) staged columns, half gate and half the matching up columns, as
 // 32 x 32 MFMA tiles.
-template <bool GATED, int BM, int BK, int CAP, int WM, int WN>
+// GATHER (GEMM1 only): A row r is the token row perm[r] / topk of Aq (n_a
+// token rows) and its scale a_scale[perm[r] / topk]: the per-token FP8 rows
+// are read in place, with no dispatched copy.
+template <bool GATED, bool GATHER, int BM, int BK, int CAP, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
-    const uint8_t* __restrict__ Aq, const float* __restrict__ a_scale, const int32_t* __restrict__ offsets, int E,
-    int rows, int Kdim, const uint8_t* __restrict__ Bq, long long b_stride, const float* __restrict__ b_scale,
-    int N, int I, uint16_t* __restrict__ C, int NB, int n_slots) {
+    const uint8_t* __restrict__ Aq, const float* __restrict__ a_scale, const int32_t* __restrict__ perm, int topk,
+    int n_a, const int32_t* __restrict__ offsets, int E, int rows, int Kdim, const uint8_t* __restrict__ Bq,
+    long long b_stride, const float* __restrict__ b_scale, int N, int I, uint16_t* __restrict__ C, int NB,
+    int n_slots) {
+  static_assert(!GATHER || GATED, "the row gather belongs to GEMM1");
   using Cfg = F8Cfg<BM, BK, CAP>;
   constexpr int STAGE = Cfg::STAGE, NSTAGE = Cfg::NSTAGE, A_BYTES = Cfg::A_BYTES, A_REG = Cfg::A_REG;
   constexpr int ROW = Cfg::ROW, CPR = Cfg::CPR, RPR = Cfg::ROWS_PER_REGION;
@@ -256,7 +261,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
       const int rr = (r < A_REG ? r : r - A_REG) * RPR + lane / CPR;
       const int c = (lane % CPR) ^ f8_swz<BK>(rr);
       if (r < A_REG) {
-        const int arow = t.r0 + min(rr, mrows - 1);
+        int arow = t.r0 + min(rr, mrows - 1);
+        if constexpr (GATHER) {
+          const int f = perm[arow];
+          arow = ((unsigned)f < (unsigned)(n_a * topk)) ? f / topk : 0;
+        }
         src[j] = Aq + (size_t)arow * Kdim + c * 16;
       } else {
         int code_row;
@@ -373,7 +382,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
     for (int mt = 0; mt < MT; ++mt) {
       const int row = a_row0 + mt * 32 + l32;
       const bool row_ok = mt < vm && row < mrows;
-      const float sa = row_ok ? a_scale[t.r0 + row] : 0.f;
+      float sa = 0.f;
+      if (row_ok) {
+        if constexpr (GATHER) {
+          const int f = perm[t.r0 + row];
+          sa = ((unsigned)f < (unsigned)(n_a * topk)) ? a_scale[f / topk] : 0.f;
+        } else {
+          sa = a_scale[t.r0 + row];
+        }
+      }
 #pragma unroll
       for (int q = 0; q < kOutTiles; ++q) {
         const int gcol0 = out_col0(t, q);
@@ -454,25 +471,28 @@ constexpr int kF8SmallRowsPerExpert = 64;
 // scales)^T over each expert's rows: GEMM1 (GATED: B = W13 codes (E, 2I, H),
 // h = SwiGLU of the paired columns, ncols = I) or GEMM2 (B = W2 codes
 // (E, H, I), ncols = H).
-template <bool GATED, int BM, int BK, int CAP, int WM, int WN>
-void launch_f8f8_cfg(const uint8_t* Aq, const float* a_scale, const int32_t* offsets, int E, int rows, int Kdim,
-                     const uint8_t* Bq, const float* b_scale, int N, int I, void* C, hipStream_t s) {
+template <bool GATED, bool GATHER, int BM, int BK, int CAP, int WM, int WN>
+void launch_f8f8_cfg(const uint8_t* Aq, const float* a_scale, const int32_t* perm, int topk, int n_a,
+                     const int32_t* offsets, int E, int rows, int Kdim, const uint8_t* Bq, const float* b_scale, int N,
+                     int I, void* C, hipStream_t s) {
   const int NB = GATED ? ceil_div(I, BN / 2) : ceil_div(N, BN);
   const int n_slots = max_row_tiles(rows, E, BM) * NB;
   const int grid = std::min(n_slots, stream_cu_count(s));
-  gemm_f8f8_kernel<GATED, BM, BK, CAP, WM, WN><<<grid, 64 * WM * WN, 0, s>>>(
-      Aq, a_scale, offsets, E, rows, Kdim, Bq, (long long)N * Kdim, b_scale, N, I, (uint16_t*)C, NB, n_slots);
+  gemm_f8f8_kernel<GATED, GATHER, BM, BK, CAP, WM, WN><<<grid, 64 * WM * WN, 0, s>>>(
+      Aq, a_scale, perm, topk, n_a, offsets, E, rows, Kdim, Bq, (long long)N * Kdim, b_scale, N, I, (uint16_t*)C, NB,
+      n_slots);
 }
 
-template <bool GATED>
+template <bool GATED, bool GATHER = false>
 void launch_f8f8(const uint8_t* Aq, const float* a_scale, const int32_t* offsets, int E, int rows, int Kdim,
-                 const uint8_t* Bq, const float* b_scale, int N, int I, void* C, hipStream_t s) {
+                 const uint8_t* Bq, const float* b_scale, int N, int I, void* C, hipStream_t s,
+                 const int32_t* perm = nullptr, int topk = 1, int n_a = 0) {
   if ((long long)rows <= (long long)kF8SmallRowsPerExpert * E)
-    launch_f8f8_cfg<GATED, kF8SmallBM, kF8SmallBK, kF8SmallCap, kF8SmallWM, kF8SmallWN>(Aq, a_scale, offsets, E, rows,
-                                                                                       Kdim, Bq, b_scale, N, I, C, s);
+    launch_f8f8_cfg<GATED, GATHER, kF8SmallBM, kF8SmallBK, kF8SmallCap, kF8SmallWM, kF8SmallWN>(
+        Aq, a_scale, perm, topk, n_a, offsets, E, rows, Kdim, Bq, b_scale, N, I, C, s);
   else
-    launch_f8f8_cfg<GATED, kF8BM, kF8BK, kF8Cap, kF8WM, kF8WN>(Aq, a_scale, offsets, E, rows, Kdim, Bq, b_scale, N, I,
-                                                             C, s);
+    launch_f8f8_cfg<GATED, GATHER, kF8BM, kF8BK, kF8Cap, kF8WM, kF8WN>(Aq, a_scale, perm, topk, n_a, offsets, E, rows,
+                                                                     Kdim, Bq, b_scale, N, I, C, s);
 }
 
 }  // namespace
@@ -516,6 +536,15 @@ hipError_t launch_w13_swiglu_fp8a(const uint8_t* x_q, const float* x_scale, cons
                                   hipStream_t s) {
   if (rows_max == 0) return hipSuccess;
   launch_f8f8<true>(x_q, x_scale, offsets_padded, E, rows_max, H, W13q, s13, 2 * I, I, h, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_w13_swiglu_gather_fp8a(const uint8_t* codes_tok, const float* s_tok, const int32_t* perm, int n,
+                                         int K, const int32_t* offsets, const uint8_t* W13q, const float* s13, int E,
+                                         int H, int I, void* h, hipStream_t s) {
+  const int rows = n * K;
+  if (rows == 0) return hipSuccess;
+  launch_f8f8<true, true>(codes_tok, s_tok, offsets, E, rows, H, W13q, s13, 2 * I, I, h, s, perm, K, n);
   return hipGetLastError();
 }
 

@@ -81,17 +81,15 @@ ForwardLayout forward_layout(int n, int H, int I, int E, int K, moe_dtype dt) {
   return L;
 }
 
-// moe_forward_fp8a workspace, in order: routing, unpadded dispatch metadata,
-// the per-token FP8 rows, the padded FP8 receive buffer and its metadata, h
-// and Y_perm over the padded rows.
+// moe_forward_fp8a workspace, in order: routing, dispatch metadata, the
+// per-token FP8 rows, h and its per-row FP8 form, and Y_perm (nK rows each).
 struct Fp8aLayout {
-  size_t logits, ids, w, counts, offsets, offsets_p, splits, perm, inv, pscratch, codes_tok, s_tok, x_q, x_scale,
-      perm_p, inv_p, h, h_q, h_scale, Y_perm, total;
+  size_t logits, ids, w, counts, offsets, splits, perm, inv, pscratch, codes_tok, s_tok, h, h_q, h_scale, Y_perm,
+      total;
 };
-
 Fp8aLayout fp8a_layout(int n, int H, int I, int E, int K) {
   Fp8aLayout L{};
-  const size_t nk = (size_t)n * K, R = fp8_padded_rows(n, E, K);
+  const size_t nk = (size_t)n * K;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -103,21 +101,16 @@ Fp8aLayout fp8a_layout(int n, int H, int I, int E, int K) {
   L.w = take(nk * 4);
   L.counts = take((size_t)E * 4);
   L.offsets = take((size_t)(E + 1) * 4);
-  L.offsets_p = take((size_t)(E + 1) * 4);
   L.splits = take(4);
   L.perm = take(nk * 4);
   L.inv = take(nk * 4);
   L.pscratch = take(permute_ws(n, E, K));
   L.codes_tok = take((size_t)n * H);
   L.s_tok = take((size_t)n * 4);
-  L.x_q = take(R * H);
-  L.x_scale = take(R * 4);
-  L.perm_p = take(R * 4);
-  L.inv_p = take(nk * 4);
-  L.h = take(R * I * 2);
-  L.h_q = take(R * I);
-  L.h_scale = take(R * 4);
-  L.Y_perm = take(R * H * 2);
+  L.h = take(nk * I * 2);
+  L.h_q = take(nk * I);
+  L.h_scale = take(nk * 4);
+  L.Y_perm = take(nk * H * 2);
   L.total = o;
   return L;
 }
@@ -913,6 +906,21 @@ moe_status moe_expert_w13_swiglu_fp8a(const uint8_t* x_q, const float* x_scale, 
   return from_hip(launch_w13_swiglu_fp8a(x_q, x_scale, offsets_padded, rows_max, W13q, s13, E, H, I, h, stream));
 }
 
+moe_status moe_expert_w13_swiglu_gather_fp8a(const uint8_t* codes_tok, const float* s_tok, const int32_t* perm,
+                                             int n, int K, const int32_t* offsets, const uint8_t* W13q,
+                                             const float* s13, int E, int H, int I, void* h, hipStream_t stream) {
+  if (n < 0 || !experts_ok(E, K) || !hidden_ok(H, MOE_BF16) || H % 128 != 0 || !hidden_ok(I, MOE_BF16))
+    return MOE_EINVAL;
+  if ((long long)n * K > INT32_MAX) return MOE_EINVAL;
+  if (n == 0) return MOE_OK;
+  if (codes_tok == nullptr || s_tok == nullptr || perm == nullptr || offsets == nullptr || W13q == nullptr ||
+      s13 == nullptr || h == nullptr)
+    return MOE_EINVAL;
+  if (!vec_ok({codes_tok, W13q, s13, h}) || !word_ok({s_tok, perm, offsets})) return MOE_EINVAL;
+  return from_hip(
+      launch_w13_swiglu_gather_fp8a(codes_tok, s_tok, perm, n, K, offsets, W13q, s13, E, H, I, h, stream));
+}
+
 moe_status moe_expert_w2_fp8a(const uint8_t* h_q, const float* h_scale, const int32_t* offsets_padded, int rows_max,
                               const uint8_t* W2q, const float* s2, int E, int H, int I, void* Y_perm,
                               hipStream_t stream) {
@@ -957,33 +965,29 @@ moe_status moe_forward_fp8a(const void* x, const void* W_gate, const float* bias
   float* w = topk_w_out ? topk_w_out : (float*)(base + L.w);
   int32_t* counts = counts_out ? counts_out : (int32_t*)(base + L.counts);
   int32_t* offsets = (int32_t*)(base + L.offsets);
-  int32_t* offsets_p = (int32_t*)(base + L.offsets_p);
   int32_t* perm = (int32_t*)(base + L.perm);
   int32_t* inv = (int32_t*)(base + L.inv);
   uint8_t* codes_tok = (uint8_t*)(base + L.codes_tok);
   float* s_tok = (float*)(base + L.s_tok);
-  uint8_t* x_q = (uint8_t*)(base + L.x_q);
-  float* x_scale = (float*)(base + L.x_scale);
-  int32_t* perm_p = (int32_t*)(base + L.perm_p);
-  int32_t* inv_p = (int32_t*)(base + L.inv_p);
-  const int R = (int)fp8_padded_rows(n, E, K);
+  const int nk = n * K;
+  // On one GPU the per-token FP8 rows are read in place through perm (as the
+  // bf16 layer reads x): the padded receive buffer of moe_dispatch_fp8 is what
+  // an expert-parallel exchange would deliver, and not needed here.
   hipError_t e = launch_route(x, W_gate, bias, n, H, E, K, renorm, dt, logits, ids, w, stream);
   if (e == hipSuccess)
     e = launch_permute(ids, nullptr, n, H, E, K, 1, dt, counts, offsets, (int32_t*)(base + L.splits), perm, inv,
                        nullptr, (int32_t*)(base + L.pscratch), stream);
   if (e == hipSuccess) e = launch_quantize_rows_fp8(x, n, H, dt, codes_tok, s_tok, stream);
   if (e == hipSuccess)
-    e = launch_dispatch_fp8(counts, offsets, perm, n, E, K, codes_tok, s_tok, H, offsets_p, x_q, x_scale, perm_p,
-                            inv_p, stream);
-  if (e == hipSuccess) e = launch_w13_swiglu_fp8a(x_q, x_scale, offsets_p, R, W13q, s13, E, H, I, base + L.h, stream);
-  // h per row in FP8 (rows past the last group are quantized too and never read), then GEMM2 on the FP8 MFMA.
+    e = launch_w13_swiglu_gather_fp8a(codes_tok, s_tok, perm, n, K, offsets, W13q, s13, E, H, I, base + L.h, stream);
+  // h per row in FP8, then GEMM2 on the FP8 MFMA.
   if (e == hipSuccess)
-    e = launch_quantize_rows_fp8(base + L.h, R, I, MOE_BF16, (uint8_t*)(base + L.h_q), (float*)(base + L.h_scale),
+    e = launch_quantize_rows_fp8(base + L.h, nk, I, MOE_BF16, (uint8_t*)(base + L.h_q), (float*)(base + L.h_scale),
                                  stream);
   if (e == hipSuccess)
-    e = launch_w2_fp8a((uint8_t*)(base + L.h_q), (float*)(base + L.h_scale), offsets_p, R, W2q, s2, E, H, I,
+    e = launch_w2_fp8a((uint8_t*)(base + L.h_q), (float*)(base + L.h_scale), offsets, nk, W2q, s2, E, H, I,
                        base + L.Y_perm, stream);
-  if (e == hipSuccess) e = launch_combine_rows(base + L.Y_perm, R, inv_p, w, n, H, K, dt, y, stream);
+  if (e == hipSuccess) e = launch_combine(base + L.Y_perm, inv, w, n, H, K, dt, y, stream);
   return from_hip(e);
 }
 

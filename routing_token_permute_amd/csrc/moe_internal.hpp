@@ -165,6 +165,12 @@ hipError_t launch_dispatch_fp8(const int32_t* counts, const int32_t* offsets, co
 hipError_t launch_w13_swiglu_fp8a(const uint8_t* x_q, const float* x_scale, const int32_t* offsets_padded,
                                   int rows_max, const uint8_t* W13q, const float* s13, int E, int H, int I, void* h,
                                   hipStream_t s);
+// GEMM1 + SwiGLU with FP8 activations read in place: row r of the expert-major
+// order is token perm[r] / K of the per-token codes (n, H) and scales (n);
+// h (n*K, I) bf16 over the unpadded offsets.
+hipError_t launch_w13_swiglu_gather_fp8a(const uint8_t* codes_tok, const float* s_tok, const int32_t* perm, int n,
+                                         int K, const int32_t* offsets, const uint8_t* W13q, const float* s13, int E,
+                                         int H, int I, void* h, hipStream_t s);
 // GEMM2 with FP8 activations: Y_perm (rows_max, H) bf16 = (h codes x per-row
 // scales) . (W2 codes x column scales) over the padded receive buffer's rows.
 hipError_t launch_w2_fp8a(const uint8_t* h_q, const float* h_scale, const int32_t* offsets_padded, int rows_max,

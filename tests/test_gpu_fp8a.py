@@ -156,6 +156,13 @@ def test_w13_swiglu_fp8a(dev, n, H, I, E, K):  # noqa: E741
     real = rd["perm"] >= 0
     assert (got[~real] == 0).all(), "padding rows must be zero"
     assert_close(got[real], ref[real], "bf16", f"fp8a gate_up n={n} E={E}", intermediate=True)
+    # The in-place form (token rows read through perm, unpadded rows) computes every output the same way.
+    codes_tok, s_tok = moe.moe_quantize_rows_fp8(t["x"])
+    hg = moe.moe_expert_w13_swiglu_gather_fp8a(codes_tok, s_tok, meta["perm"], K, meta["offsets"], q13, s13)
+    torch.cuda.synchronize()
+    offs = meta["offsets"].cpu().numpy()
+    rows_p = np.concatenate([np.arange(P[e], P[e] + offs[e + 1] - offs[e]) for e in range(E)]).astype(np.int64)
+    assert torch.equal(hg.view(torch.int16).cpu(), h.view(torch.int16).cpu()[rows_p]), "gather form differs"
 
 
 @pytest.mark.parametrize("R_real,E,H,I,skew", [(700, 8, 256, 128, False), (200, 16, 384, 256, True),
@@ -203,8 +210,7 @@ def test_forward_fp8a_configs(dev, name):
     # The same kernels stage by stage, for the device's h and its codes.
     meta = moe.moe_permute(ids, None, w.E)
     codes_tok, s_tok = moe.moe_quantize_rows_fp8(t["x"])
-    d8 = moe.moe_dispatch_fp8(meta, codes_tok, s_tok, w.K)
-    h = moe.moe_expert_w13_swiglu_fp8a(d8["x_q"], d8["x_scale"], d8["offsets_padded"], q13, s13)
+    h = moe.moe_expert_w13_swiglu_gather_fp8a(codes_tok, s_tok, meta["perm"], w.K, meta["offsets"], q13, s13)
     hq, hs = moe.moe_quantize_rows_fp8(h)
     torch.cuda.synchronize()
     ref_logits = oracle.router_logits(w.x_f32, w.W_gate_f32, w.bias)
@@ -216,18 +222,16 @@ def test_forward_fp8a_configs(dev, name):
                            routing_logits_f32=L)
     assert (ids.cpu().numpy() == ref["e_top"]).all()
     assert (counts.cpu().numpy() == ref["counts"]).all()
-    rd = of8.dispatch_fp8(w.x_f32, ids.cpu().numpy(), w.E)
-    P = rd["offsets"]
-    R = int(P[-1])
-    real = rd["perm"] >= 0
-    h_ref = om.grouped_gate_up(of8.dequantize_rows(rd["codes"], rd["scales"]), P, of8.dequantize_columns(c13, r13))
-    h_dev = h[:R].float().cpu().numpy()
-    assert_close(h_dev[real].astype(np.float64), h_ref[real], "bf16", f"fp8a layer h {name}", intermediate=True)
+    offsets, perm, inv = ref["offsets"], ref["perm"], ref["inv"]
+    ct, st = of8.quantize_rows(w.x_f32)
+    h_ref = om.grouped_gate_up(of8.dequantize_rows(ct, st)[perm // w.K], offsets, of8.dequantize_columns(c13, r13))
+    h_dev = h.float().cpu().numpy()
+    assert_close(h_dev.astype(np.float64), h_ref, "bf16", f"fp8a layer h {name}", intermediate=True)
     hc_ref, hs_ref = of8.quantize_rows(h_dev)
-    assert (hs[:R].cpu().numpy().view(np.uint32) == hs_ref.view(np.uint32)).all(), "h scales differ"
-    assert int((hq[:R].cpu().numpy() != hc_ref).sum()) == 0, "h codes differ"
-    Y_ref = om.grouped_down(of8.dequantize_rows(hc_ref, hs_ref), P, of8.dequantize_columns(c2, r2))
-    y_ref = om.combine_slot_order(Y_ref, rd["inv"], ref["w_top"], w.n, w.K)
+    assert (hs.cpu().numpy().view(np.uint32) == hs_ref.view(np.uint32)).all(), "h scales differ"
+    assert int((hq.cpu().numpy() != hc_ref).sum()) == 0, "h codes differ"
+    Y_ref = om.grouped_down(of8.dequantize_rows(hc_ref, hs_ref), offsets, of8.dequantize_columns(c2, r2))
+    y_ref = om.combine_slot_order(Y_ref, inv, ref["w_top"], w.n, w.K)
     assert_close(to_f64(y), y_ref, "bf16", f"forward fp8a {name}")
     # Against the oracle's own layer (its h rounded from fp64): only the code flips of near-midpoint elements
     # separate the two, and FP8 activations move the output by about their quantization error, not more.
