@@ -101,8 +101,8 @@ def _kernel_label(name):
         return ("gemm1_swiglu" if gated else "gemm2") + f"_bm{bm}"
     if "gemm_f8f8_kernel<" in name:
         args = name.split("gemm_f8f8_kernel<", 1)[1].split(">", 1)[0].split(",")
-        gated, bm = args[0].strip() == "true", args[1].strip()
-        return ("gemm1_swiglu_f8f8" if gated else "gemm2_f8f8") + f"_bm{bm}"
+        gated, gather, bm = args[0].strip() == "true", args[1].strip() == "true", args[2].strip()
+        return ("gemm1_swiglu_f8f8" if gated else "gemm2_f8f8") + ("_gather" if gather else "") + f"_bm{bm}"
     for k, lab in (("quantize_rows_kernel", "quantize_rows_fp8"), ("dispatch_fp8_kernel", "dispatch_fp8"),
                    ("quantize_fp8_kernel", "quantize_weights_fp8"), ("fused_ffn_kernel", "fused_ffn"),
                    ("fill_zero_kernel", "fill_zero")):
