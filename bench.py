@@ -98,7 +98,8 @@ def _kernel_label(name):
     if "gemm_bf16_kernel<" in name:
         args = name.split("gemm_bf16_kernel<", 1)[1].split(">", 1)[0].split(",")
         gated, bm = args[0].strip() == "true", args[3].strip()
-        return ("gemm1_swiglu" if gated else "gemm2") + f"_bm{bm}"
+        ids = len(args) > 8 and args[8].strip() == "true"
+        return ("gemm1_swiglu" if gated else "gemm2") + ("_from_ids" if ids else "") + f"_bm{bm}"
     if "gemm_f8f8_kernel<" in name:
         args = name.split("gemm_f8f8_kernel<", 1)[1].split(">", 1)[0].split(",")
         gated, gather, bm = args[0].strip() == "true", args[1].strip() == "true", args[2].strip()
@@ -339,6 +340,12 @@ def _layer_bench(w, args, torch, moe, dev, detail):
     yc = moe.moe_unpermute_combine(Yp, meta["inv"], wts, n, K)
     torch.cuda.synchronize()
     counts = meta["counts"].cpu().numpy()
+    # Decode-sized bf16 batches: moe_forward runs GEMM1 straight from the ids (the GEMM places the pairs
+    # itself and writes the metadata) in place of moe_permute + the gathered GEMM1.
+    try:
+        h_ids, meta_ids = moe.moe_expert_w13_swiglu_from_ids(x, ids, W13)
+    except moe.MoEError:
+        h_ids = meta_ids = None
     R = args.stage_reps
     st = {
         "route": _time_region_graph(lambda: moe.moe_route(x, Wg, bias, K, w.renorm, logits=logits, topk_ids=ids, topk_w=wts), R, torch),
@@ -347,6 +354,9 @@ def _layer_bench(w, args, torch, moe, dev, detail):
         "gemm2": _time_region_graph(lambda: moe.moe_expert_w2(h, meta["offsets"], W2, Y_perm=Yp), R, torch),
         "combine": _time_region_graph(lambda: moe.moe_unpermute_combine(Yp, meta["inv"], wts, n, K, y=yc), R, torch),
     }
+    if meta_ids is not None:
+        st["gemm1_swiglu_from_ids"] = _time_region_graph(
+            lambda: moe.moe_expert_w13_swiglu_from_ids(x, ids, W13, h=h_ids, out=meta_ids), R, torch)
     nk = n * K
     hit = int((counts > 0).sum())
     flops1 = 2.0 * nk * H * 2 * I
@@ -359,26 +369,31 @@ def _layer_bench(w, args, torch, moe, dev, detail):
         "gemm1_swiglu": nk * H * esz + hit * H * 2 * I * esz + nk * I * esz + nk * 4,
         "gemm2": nk * I * esz + hit * I * H * esz + nk * H * esz,
         "combine": nk * H * esz + nk * 8 + n * H * esz,
+        # ids read once, rows gathered once, weights of the hit experts once, h and the metadata written once
+        "gemm1_swiglu_from_ids": nk * 4 + nk * H * esz + hit * H * 2 * I * esz + nk * I * esz + nk * 8 + (2 * E + 2) * 4,
     }
+    g1 = "gemm1_swiglu_from_ids" if meta_ids is not None else "gemm1_swiglu"
     stages = {}
     for k, v in st.items():
         s_ = {"ms": round(v, 5), "GB/s": round(bytes_[k] / (v * 1e-3) / 1e9, 1)}
         s_["frac_hbm"] = round(s_["GB/s"] / PEAK_HBM_GBPS, 4)
-        if k == "gemm1_swiglu":
+        if k in ("gemm1_swiglu", "gemm1_swiglu_from_ids"):
             s_["TFLOP/s"] = round(flops1 / (v * 1e-3) / 1e12, 1)
         if k == "gemm2":
             s_["TFLOP/s"] = round(flops2 / (v * 1e-3) / 1e12, 1)
         stages[k] = s_
-    gg_ms = st["gemm1_swiglu"] + st["gemm2"]
+    gg_ms = st[g1] + st["gemm2"]
     gg = (flops1 + flops2) / (gg_ms * 1e-3) / 1e12
-    g1_kernel = "gemm_bf16_kernel<GATED=true, GATHER=true> (GEMM1 with fused row gather + SwiGLU epilogue)"
+    g1_kernel = ("gemm_bf16_kernel<GATED=true, GATHER=true, IDS=true> (decode GEMM1 that places the routing ids "
+                 "itself, with fused row gather + SwiGLU epilogue)" if meta_ids is not None else
+                 "gemm_bf16_kernel<GATED=true, GATHER=true> (GEMM1 with fused row gather + SwiGLU epilogue)")
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
-    if flops1 / bytes_["gemm1_swiglu"] >= ridge:
-        a = stages["gemm1_swiglu"]["TFLOP/s"]
+    if flops1 / bytes_[g1] >= ridge:
+        a = stages[g1]["TFLOP/s"]
         roof = {"kernel": g1_kernel, "bound": "mfma", "achieved": a, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(a / PEAK_BF16_TFLOPS, 4)}
     else:
-        a = stages["gemm1_swiglu"]["GB/s"]
+        a = stages[g1]["GB/s"]
         roof = {"kernel": g1_kernel, "bound": "hbm", "achieved": a, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(a / PEAK_HBM_GBPS, 4)}
     roof["traffic"] = None
@@ -386,6 +401,8 @@ def _layer_bench(w, args, torch, moe, dev, detail):
            "wall_s_timed_region": round(wall, 3),
            "grouped_gemm": {"TFLOP/s": round(gg, 1), "frac_bf16_peak": round(gg / PEAK_BF16_TFLOPS, 4),
                             "GFLOP": round((flops1 + flops2) / 1e9, 1)},
+           "forward_stages": (["route", "gemm1_swiglu_from_ids", "gemm2", "combine"] if meta_ids is not None else
+                              ["route", "permute", "gemm1_swiglu", "gemm2", "combine"]),
            "stages": stages, "expert_load": _expert_load(counts), "roofline": roof}
     if w.dtype == "bf16" and nk > 64 * E:
         out["persistent_experiment"] = _persistent_bench(w, args, torch, moe, dev, (x, Wg, W13, W2, bias), ms)

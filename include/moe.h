@@ -195,6 +195,27 @@ moe_status moe_expert_w13_swiglu_gather(const void* x, const int32_t* perm, int 
 moe_status moe_expert_w2(const void* h, const int32_t* offsets, int rows, const void* W2, int E, int H, int I,
                          moe_dtype dt, void* Y_perm, hipStream_t stream);
 
+/* moe_expert_w13_swiglu_from_ids — Algorithm 2 steps 5-8 in one launch for a
+ * decode-sized batch: moe_permute's metadata (no x_perm) and
+ * moe_expert_w13_swiglu_gather's h, computed straight from the routing ids.
+ * Every workgroup places the pairs itself in on-chip memory; one of them also
+ * writes counts, offsets, splits, perm and inv, with the values (and the
+ * meaning) moe_permute gives them, for the kernels that follow. h is bit for
+ * bit what moe_permute + moe_expert_w13_swiglu_gather give.
+ *   x (n, H) bf16; topk_ids (n, K) int32 with K distinct experts per token in
+ *   [0, E) (as moe_route writes them); W13 (E, H, 2I) bf16; ep as moe_permute;
+ *   h (n*K, I) bf16 out; counts (E), offsets (E+1), splits (ep), perm (n*K),
+ *   inv (n*K) int32 out.
+ * Shapes it serves: dt = MOE_BF16, n <= 32, n*K <= 1024, E <= 256; others
+ * return MOE_EUNSUPPORTED (use moe_permute and moe_expert_w13_swiglu_gather).
+ * An id outside [0, E) is neither counted nor placed; ids repeated within a
+ * token give unspecified h rows (still in bounds). n == 0 writes zero counts,
+ * offsets and splits. */
+moe_status moe_expert_w13_swiglu_from_ids(const void* x, const int32_t* topk_ids, int n, int K, const void* W13,
+                                          int E, int H, int I, int ep, moe_dtype dt, void* h, int32_t* counts,
+                                          int32_t* offsets, int32_t* splits, int32_t* perm, int32_t* inv,
+                                          hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * moe_expert_w2_scatter — Algorithm 2 steps 9-11 with the weight and the
  * un-permutation in GEMM2's epilogue: the second MoE layer of "大模型系统中的

@@ -39,6 +39,8 @@ SIGNATURES = {
     "moe_grouped_swiglu": (_I, [_VP, _VP, _I, _VP, _VP, _I, _I, _I, _I, _VP, _VP, _SZ, _VP]),
     "moe_expert_w13_swiglu": (_I, [_VP, _VP, _I, _VP, _I, _I, _I, _I, _VP, _VP]),
     "moe_expert_w13_swiglu_gather": (_I, [_VP, _VP, _I, _I, _VP, _VP, _I, _I, _I, _I, _VP, _VP]),
+    "moe_expert_w13_swiglu_from_ids": (_I, [_VP, _VP, _I, _I, _VP, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP,
+                                            _VP]),
     "moe_expert_w2": (_I, [_VP, _VP, _I, _VP, _I, _I, _I, _I, _VP, _VP]),
     "moe_expert_w2_scatter": (_I, [_VP, _VP, _I, _VP, _VP, _VP, _I, _I, _I, _I, _VP, _VP]),
     "moe_sum_slots": (_I, [_VP, _I, _I, _I, _I, _VP, _VP]),
@@ -352,6 +354,34 @@ def moe_expert_w13_swiglu_gather(x, perm, K, offsets, W13, h=None, stream=None):
     )
     _check(code, "moe_expert_w13_swiglu_gather")
     return h
+
+
+@_on_stream
+def moe_expert_w13_swiglu_from_ids(x, topk_ids, W13, ep: int = 1, h=None, out=None, stream=None):
+    """Decode-sized GEMM1 straight from the routing ids: h (n*K, I) and the metadata dict of
+    moe_permute (counts, offsets, splits, perm, inv) from one launch. Returns (h, meta)."""
+    lib = load_library()
+    n, H = x.shape
+    K = topk_ids.shape[1]
+    E, _, I2 = W13.shape
+    I = I2 // 2  # noqa: E741
+    dev = x.device
+    _need(x, "x", (n, H))
+    _need(topk_ids, "topk_ids", (n, K), torch.int32, dev)
+    _need(W13, "W13", (E, H, 2 * I), x.dtype, dev)
+    h = _empty((n * K, I), x.dtype, dev) if h is None else h
+    _need(h, "h", (n * K, I), x.dtype, dev)
+    out = dict(out or {})
+    for name, shape in (("counts", (E,)), ("offsets", (E + 1,)), ("splits", (ep,)), ("perm", (n * K,)),
+                        ("inv", (n * K,))):
+        out.setdefault(name, _empty(shape, torch.int32, dev))
+        _need(out[name], name, shape, torch.int32, dev)
+    code = lib.moe_expert_w13_swiglu_from_ids(
+        _ptr(x), _ptr(topk_ids), n, K, _ptr(W13), E, H, I, ep, _dt(x), _ptr(h), _ptr(out["counts"]),
+        _ptr(out["offsets"]), _ptr(out["splits"]), _ptr(out["perm"]), _ptr(out["inv"]), _stream(dev, stream),
+    )
+    _check(code, "moe_expert_w13_swiglu_from_ids")
+    return h, out
 
 
 @_on_stream

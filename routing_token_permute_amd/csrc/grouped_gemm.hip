@@ -38,6 +38,7 @@
 #include <algorithm>
 
 #include "gemm_tiles.hpp"
+#include "place_pairs.hpp"
 
 namespace moe {
 namespace {
@@ -49,6 +50,21 @@ namespace {
 constexpr int kBM = 256, kBK = 32, kGemmWM = 4, kGemmWN = 4;
 constexpr int kSmallBM = 32, kSmallBK = 64, kSmallWM = 1, kSmallWN = 4;
 constexpr int kSmallRowsPerExpert = 64;  // rows / E at or below this: small tiles
+// GEMM1 from the routing ids (IDS): at most this many (token, slot) pairs.
+constexpr int kIdsMaxPairs = 1024;
+
+// IDS: the routing ids the GEMM places itself, and where workgroup 0 writes
+// the dispatch metadata (counts, offsets, splits, perm, inv) for the kernels
+// that follow.
+struct IdsMeta {
+  const int32_t* ids;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* splits;
+  int32_t* perm;
+  int32_t* inv;
+  int ep, id_bits;
+};
 
 // GATED (GEMM1): the 256 staged columns are 128 gate columns followed by the
 // matching 128 up columns; the tile writes 128 columns of h. Otherwise
@@ -63,7 +79,16 @@ constexpr int kSmallRowsPerExpert = 64;  // rows / E at or below this: small til
 // routing weight and the un-permutation are fused into the epilogue.
 // SAVE (GEMM1 only): the pre-activations [gate | up] are also written, rounded
 // to bf16, to gu_out (row stride 2 * up_col), for the backward pass.
-template <bool GATED, bool GATHER, bool SCATTER, int BM, int BK, int WM, int WN, bool SAVE = false>
+// IDS (gathered GEMM1 with one row tile per expert, i.e. no expert has more
+// than BM rows): there is no perm or offsets yet. Every workgroup stages the
+// n_a * topk routing ids in LDS and places them itself (place_pairs, the same
+// stable placement moe_permute makes), then reads its tiles' rows and
+// gathered token indices from LDS; slot t is expert t / NB, column block
+// t % NB, and the slots of experts without rows are skipped. Workgroup 0 also
+// writes the metadata to memory for the kernels that follow, so no separate
+// permute launch runs before this GEMM.
+template <bool GATED, bool GATHER, bool SCATTER, int BM, int BK, int WM, int WN, bool SAVE = false,
+          bool IDS = false>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                                     const int32_t* __restrict__ perm, int topk,
                                                                     int n_a, const float* __restrict__ wrow,
@@ -72,7 +97,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
                                                                     const uint16_t* __restrict__ B, int ldb,
                                                                     long long b_expert_stride, int Nout, int up_col,
                                                                     uint16_t* __restrict__ C, int ldc, int NB,
-                                                                    int n_slots, uint16_t* __restrict__ gu_out) {
+                                                                    int n_slots, uint16_t* __restrict__ gu_out,
+                                                                    IdsMeta im) {
   // The 256-row tiles run on a 3-stage ring: measured a little faster than
   // four or five stages for both GEMMs, whose deeper copy lead buys nothing.
   using Cfg = TileCfg<BM, BK, (BM == 256) ? 3 : kMaxStages>;
@@ -87,6 +113,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
   static_assert(NT % (GATED ? 4 : 2) == 0 && MT >= 1 && REG * NW == Cfg::REGIONS, "tile split");
   static_assert(!(SCATTER && (GATED || GATHER)), "the weighted scatter is a GEMM2 epilogue");
   static_assert(!SAVE || GATED, "the pre-activations belong to GEMM1");
+  static_assert(!IDS || (GATED && GATHER && !SAVE && BM < 256), "placement from ids: gathered decode GEMM1");
   // Epilogue stores per wave and tile when they go out as buffer stores
   // (every wave issues all of them; lanes without a valid output carry an
   // out-of-range offset, which the hardware drops), so that the waits of the
@@ -104,6 +131,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
   const int g = lane >> 4, li = lane & 15, rr = li >> 2, cc = li & 3;
   const int nk = Kdim / BK;
 
+  // IDS: the placement of the pairs, in LDS (one-element arrays otherwise).
+  __shared__ int ids_l[IDS ? kIdsMaxPairs : 1];
+  __shared__ int perm_l[IDS ? kIdsMaxPairs : 1];
+  __shared__ int cnt_l[IDS ? NW : 1][IDS ? kMaxExperts : 1];
+  __shared__ int offs_l[IDS ? kMaxExperts + 1 : 1];
   // Tile slots: this workgroup takes slots blockIdx.x, blockIdx.x + gridDim.x,
   // ... of the n_slots the worst split of the rows can need; a slot past the
   // real tile count comes back invalid.
@@ -111,7 +143,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
   auto next_tile = [&]() {
     Tile t{0, 0, 0, 0, false};
     while (slot_id < n_slots && !t.valid) {
-      t = find_tile<BM>(offsets, E, rows, NB, xcd_remap(slot_id, n_slots));
+      if constexpr (IDS) {
+        const int tt = xcd_remap(slot_id, n_slots);
+        const int e = tt / NB;
+        const int r0 = offs_l[e], r1 = offs_l[e + 1];
+        t = Tile{e, r0, r1, tt - e * NB, r1 > r0};
+      } else {
+        t = find_tile<BM>(offsets, E, rows, NB, xcd_remap(slot_id, n_slots));
+      }
       slot_id += gridDim.x;
     }
     return t;
@@ -136,7 +175,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
         const int c = (lane % CPR) ^ a_swz<BK>(row);
         int arow = t.r0 + min(row, mrows - 1);
         if constexpr (GATHER) {
-          const int f = perm[arow];
+          const int f = IDS ? perm_l[arow] : perm[arow];
           arow = ((unsigned)f < (unsigned)(n_a * topk)) ? f / topk : 0;
         }
         src[j] = A + (size_t)arow * Kdim + c * 8;
@@ -474,6 +513,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
   // tile, the first NSTAGE-1 k-steps of the next one are put in flight (the
   // barrier after the main loop frees the whole ring), so the DMA of the
   // next tile and the stores of this one overlap.
+  if constexpr (IDS) {
+    const int total = n_a * topk;  // <= kIdsMaxPairs (checked by the launcher)
+    for (int f = tid; f < total; f += 64 * NW) ids_l[f] = im.ids[f];
+    place_pairs<NW>(ids_l, total, E, im.ep, im.id_bits, cnt_l, offs_l, perm_l,
+                    PlaceOut{blockIdx.x == 0, im.counts, im.offsets, im.splits, im.perm, im.inv});
+    __syncthreads();
+  }
   Tile t = next_tile();
   if (!t.valid) return;
   set_sources(t);
@@ -566,7 +612,7 @@ void launch_cfg(const void* a, const int32_t* perm, int topk, int n_a, const flo
   const int grid = std::min(n_slots, stream_cu_count(s));
   gemm_bf16_kernel<GATED, GATHER, SCATTER, BM, BK, WM, WN, SAVE><<<grid, 64 * WM * WN, 0, s>>>(
       (const uint16_t*)a, perm, topk, n_a, wrow, offsets, E, rows, Kdim, (const uint16_t*)B, ldb, bstride, Nout,
-      up_col, (uint16_t*)C, ldc, NB, n_slots, (uint16_t*)gu_out);
+      up_col, (uint16_t*)C, ldc, NB, n_slots, (uint16_t*)gu_out, IdsMeta{});
 }
 
 template <bool GATED, bool GATHER, bool SCATTER = false, bool SAVE = false>
@@ -614,6 +660,28 @@ hipError_t launch_w13_swiglu_gather_train(const void* x, const int32_t* perm, in
                                           const void* W13, int E, int H, int I, moe_dtype dt, void* h, void* gate_up,
                                           hipStream_t s) {
   return w13_impl<true, true>(x, perm, K, n, offsets, n * K, W13, E, H, I, dt, h, s, gate_up);
+}
+
+bool w13_from_ids_ok(int n, int K, int E, moe_dtype dt) {
+  return dt == MOE_BF16 && n > 0 && n <= kSmallBM && (long long)n * K <= kIdsMaxPairs && E <= kMaxExperts &&
+         (long long)n * K <= (long long)kSmallRowsPerExpert * E;
+}
+
+hipError_t launch_w13_swiglu_from_ids(const void* x, const int32_t* ids, int n, int K, const void* W13, int E,
+                                      int H, int I, int ep, void* h, int32_t* counts, int32_t* offsets,
+                                      int32_t* splits, int32_t* perm, int32_t* inv, hipStream_t s) {
+  if (!w13_from_ids_ok(n, K, E, MOE_BF16) || ep <= 0 || E % ep != 0) return hipErrorInvalidValue;
+  int id_bits = 0;
+  while ((1 << id_bits) < E) ++id_bits;
+  const int NB = ceil_div(I, BN / 2);
+  const int n_slots = E * NB;
+  const int grid = std::min(n_slots, stream_cu_count(s));
+  gemm_bf16_kernel<true, true, false, kSmallBM, kSmallBK, kSmallWM, kSmallWN, false, true>
+      <<<grid, 64 * kSmallWM * kSmallWN, 0, s>>>((const uint16_t*)x, nullptr, K, n, nullptr, nullptr, E, n * K, H,
+                                                 (const uint16_t*)W13, 2 * I, (long long)H * 2 * I, I, I,
+                                                 (uint16_t*)h, I, NB, n_slots, nullptr,
+                                                 IdsMeta{ids, counts, offsets, splits, perm, inv, ep, id_bits});
+  return hipGetLastError();
 }
 
 hipError_t launch_w2(const void* h, const int32_t* offsets, int rows, const void* W2, int E, int H, int I,

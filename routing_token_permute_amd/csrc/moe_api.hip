@@ -227,11 +227,18 @@ moe_status forward_enqueue(const void* x, const void* W_gate, const float* bias,
 
   hipError_t e = launch_route(x, W_gate, bias, n, H, E, K, renorm, dt, logits, ids, w, stream);
   if (e != hipSuccess) return MOE_EHIP;
-  // Metadata only: GEMM1 gathers the token rows itself through perm.
-  e = launch_permute(ids, nullptr, n, H, E, K, 1, dt, counts, offsets, splits, perm, inv, nullptr,
-                     (int32_t*)(base + L.pscratch), stream);
-  if (e != hipSuccess) return MOE_EHIP;
-  e = launch_w13_swiglu_gather(x, perm, n, K, offsets, W13, E, H, I, dt, base + L.h, stream);
+  if (w13_from_ids_ok(n, K, E, dt)) {
+    // Decode-sized batch: GEMM1 places the pairs itself and writes the
+    // metadata for GEMM2 and the combine (one launch fewer).
+    e = launch_w13_swiglu_from_ids(x, ids, n, K, W13, E, H, I, 1, base + L.h, counts, offsets, splits, perm, inv,
+                                   stream);
+  } else {
+    // Metadata only: GEMM1 gathers the token rows itself through perm.
+    e = launch_permute(ids, nullptr, n, H, E, K, 1, dt, counts, offsets, splits, perm, inv, nullptr,
+                       (int32_t*)(base + L.pscratch), stream);
+    if (e != hipSuccess) return MOE_EHIP;
+    e = launch_w13_swiglu_gather(x, perm, n, K, offsets, W13, E, H, I, dt, base + L.h, stream);
+  }
   if (e != hipSuccess) return MOE_EHIP;
   // Expert-major GEMM2, then the gathered weighted combine: measured a little
   // faster here than moe_expert_w2_scatter + moe_sum_slots, whose scattered
@@ -427,6 +434,27 @@ moe_status moe_expert_w13_swiglu_gather(const void* x, const int32_t* perm, int 
   const moe_status st = check_expert_gemm(x, offsets, n * K, W13, E, H, I, dt, h);
   if (st != MOE_OK) return st;
   return from_hip(launch_w13_swiglu_gather(x, perm, n, K, offsets, W13, E, H, I, dt, h, stream));
+}
+
+moe_status moe_expert_w13_swiglu_from_ids(const void* x, const int32_t* topk_ids, int n, int K, const void* W13,
+                                          int E, int H, int I, int ep, moe_dtype dt, void* h, int32_t* counts,
+                                          int32_t* offsets, int32_t* splits, int32_t* perm, int32_t* inv,
+                                          hipStream_t stream) {
+  if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
+  if (n < 0 || !experts_ok(E, K) || ep < 1 || E % ep != 0 || !hidden_ok(H, dt) || !hidden_ok(I, dt))
+    return MOE_EINVAL;
+  if ((long long)n * K > INT32_MAX) return MOE_EINVAL;
+  if (counts == nullptr || offsets == nullptr || splits == nullptr) return MOE_EINVAL;
+  if (!word_ok({topk_ids, counts, offsets, splits, perm, inv})) return MOE_EINVAL;
+  if (n == 0)
+    return from_hip(launch_permute(nullptr, nullptr, 0, H, E, K, ep, dt, counts, offsets, splits, nullptr, nullptr,
+                                   nullptr, nullptr, stream));
+  if (!w13_from_ids_ok(n, K, E, dt)) return MOE_EUNSUPPORTED;
+  if (x == nullptr || topk_ids == nullptr || W13 == nullptr || h == nullptr || perm == nullptr || inv == nullptr)
+    return MOE_EINVAL;
+  if (!vec_ok({x, W13, h})) return MOE_EINVAL;
+  return from_hip(launch_w13_swiglu_from_ids(x, topk_ids, n, K, W13, E, H, I, ep, h, counts, offsets, splits, perm,
+                                             inv, stream));
 }
 
 moe_status moe_expert_w2(const void* h, const int32_t* offsets, int rows, const void* W2, int E, int H, int I,

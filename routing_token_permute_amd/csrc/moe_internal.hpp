@@ -85,6 +85,15 @@ hipError_t launch_fused_ffn(const void* x, const int32_t* perm, int n, int K, co
                             const void* W2, int E, int H, int I, int warm, int pool, void* hbuf, void* Y_perm,
                             int* counters, hipStream_t s);
 
+// Decode-sized GEMM1 (bf16, n <= 32 tokens, n * K <= 1024 pairs, E <= 256):
+// the GEMM places the routing ids itself (the placement moe_permute makes) and
+// also writes counts, offsets, splits, perm and inv, so no permute launch
+// precedes it. w13_from_ids_ok says whether a shape qualifies.
+bool w13_from_ids_ok(int n, int K, int E, moe_dtype dt);
+hipError_t launch_w13_swiglu_from_ids(const void* x, const int32_t* ids, int n, int K, const void* W13, int E,
+                                      int H, int I, int ep, void* h, int32_t* counts, int32_t* offsets,
+                                      int32_t* splits, int32_t* perm, int32_t* inv, hipStream_t s);
+
 // ---- backward ----
 
 // GEMM1 that also writes the pre-activations [gate | up] (rows, 2I) for the backward.

@@ -23,7 +23,7 @@
 //              pairs keep ascending flat order inside every expert segment.
 // When x is given, a row gather follows: one wave per destination row copies
 // 16-byte vectors.
-#include "moe_internal.hpp"
+#include "place_pairs.hpp"
 
 namespace moe {
 namespace {
@@ -54,18 +54,6 @@ __global__ __launch_bounds__(kPermThreads) void permute_count_kernel(const int32
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kPermThreads) block_counts[(size_t)blockIdx.x * E + e] = hist[e];
-}
-
-// Lanes of this wave whose expert id equals this lane's (ballots over the id
-// bits); `valid` lanes only match valid lanes.
-__device__ __forceinline__ uint64_t same_expert_lanes(int e, bool valid, int id_bits) {
-  uint64_t same = __ballot(valid);
-  for (int b = 0; b < id_bits; ++b) {
-    const bool bit = (e >> b) & 1;
-    const uint64_t m = __ballot(bit);
-    same &= bit ? m : ~m;
-  }
-  return same;
 }
 
 __device__ __forceinline__ void wave_sync_lds() {
@@ -219,16 +207,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_place_kernel(const int32
   }
 }
 
-// Up to kSingleMaxPairs pairs: one workgroup of 16 waves does everything with
-// the ids staged in LDS (one round trip to memory). Wave w owns pairs
-// [w * chunk, (w + 1) * chunk) in 64-pair steps. Pass 1 counts them per
-// (wave, expert) with LDS atomic adds by the first lane of each group of
-// same-expert lanes; the per-expert totals, the exclusive offsets and the
-// per-wave starting rows follow; pass 2 repeats the walk, the group leader
-// reserving its group's rows with an atomic add that returns the old count,
-// and every lane placing its pair at leader's old count + its rank among the
-// lower lanes of its group. Each wave's adds to one counter run in program
-// order, so pairs keep ascending flat order inside every expert segment.
+// Up to kSingleMaxPairs pairs: one workgroup of 16 waves stages the ids in
+// LDS (one round trip to memory) and places them (place_pairs).
 constexpr int kSingleWaves = 16;
 // Up to here one workgroup beats the count + place launches (4 steps per
 // wave; at 32768 pairs the walks take about 37 us against 14 us for them).
@@ -244,9 +224,7 @@ __global__ __launch_bounds__(64 * kSingleWaves) void permute_single_kernel(const
   __shared__ __attribute__((aligned(16))) int sid[kSingleMaxPairs];
   __shared__ int cnt[kSingleWaves][kMaxExperts];
   __shared__ int offs[kMaxExperts + 1];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  for (int i = tid; i < kSingleWaves * kMaxExperts; i += 64 * kSingleWaves) (&cnt[0][0])[i] = 0;
+  const int tid = threadIdx.x;
   // Stage the ids: 16-byte pieces where the source is aligned, the rest one by one.
   const int vec = ((uintptr_t)ids % 16 == 0) ? total / 4 : 0;
   {
@@ -264,86 +242,8 @@ __global__ __launch_bounds__(64 * kSingleWaves) void permute_single_kernel(const
     }
     for (int f = 4 * vec + tid; f < total; f += 64 * kSingleWaves) sid[f] = ids[f];
   }
-  __syncthreads();
-  const int chunk = ((total + kSingleWaves * 64 - 1) / (kSingleWaves * 64)) * 64;
-  const int f0 = wave * chunk, f1 = min(total, f0 + chunk);
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  // Pass 1: counts per (wave, expert).
-#pragma unroll 4
-  for (int base = f0; base < f1; base += 64) {
-    const int f = base + lane;
-    const int e = (f < f1) ? sid[f] : -1;
-    const bool valid = (unsigned)e < (unsigned)E;
-    const uint64_t same = same_expert_lanes(e, valid, id_bits);
-    if (valid && (same & below) == 0) atomicAdd(&cnt[wave][e], (int)__popcll(same));
-  }
-  __syncthreads();
-  // Totals, exclusive offsets (wave 0: 4 consecutive experts per lane, then a
-  // shuffle scan), and each wave's first row per expert.
-  if (wave == 0) {
-    int t4[4], run = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane * 4 + j;
-      int tt = 0;
-      if (e < E)
-        for (int w = 0; w < kSingleWaves; ++w) tt += cnt[w][e];
-      t4[j] = tt;
-      run += tt;
-    }
-    int incl = run;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(incl, off);
-      if (lane >= off) incl += o;
-    }
-    int ex = incl - run;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane * 4 + j;
-      if (e < E) {
-        offs[e] = ex;
-        counts[e] = t4[j];
-        offsets[e] = ex;
-      }
-      ex += t4[j];
-    }
-    if (lane == 63) {
-      offs[E] = incl;
-      offsets[E] = incl;
-    }
-  }
-  __syncthreads();
-  if (tid < ep) {
-    const int El = E / ep;
-    splits[tid] = offs[(tid + 1) * El] - offs[tid * El];
-  }
-  if (tid < E) {
-    int run = offs[tid];
-    for (int w = 0; w < kSingleWaves; ++w) {
-      const int c = cnt[w][tid];
-      cnt[w][tid] = run;
-      run += c;
-    }
-  }
-  __syncthreads();
-  // Pass 2: stable placement.
-#pragma unroll 4
-  for (int base = f0; base < f1; base += 64) {
-    const int f = base + lane;
-    const int e = (f < f1) ? sid[f] : -1;
-    const bool valid = (unsigned)e < (unsigned)E;
-    const uint64_t same = same_expert_lanes(e, valid, id_bits);
-    const int rank = __popcll(same & below);
-    int old = 0;
-    if (valid && rank == 0) old = atomicAdd(&cnt[wave][e], (int)__popcll(same));
-    const int leader = valid ? (__ffsll((long long)same) - 1) : lane;
-    const int pos = __shfl(old, leader) + rank;
-    if (valid) {
-      perm[pos] = f;
-      inv[f] = pos;
-    }
-  }
+  place_pairs<kSingleWaves>(sid, total, E, ep, id_bits, cnt, offs, nullptr,
+                            PlaceOut{true, counts, offsets, splits, perm, inv});
 }
 
 // No pairs: counts, offsets and splits are all zero.

@@ -296,3 +296,22 @@ def test_persistent_forward_rejects_bad_arguments(lib):
     bad = list(args)
     bad[20] = ws - 1
     assert lib.moe_forward_persistent(*bad) == EWS
+
+
+def test_w13_from_ids_rejects_unserved_shapes(lib):
+    """moe_expert_w13_swiglu_from_ids serves bf16 decode batches only (n <= 32, n*K <= 1024, E <= 256);
+    every other shape, dtype or argument error is refused before any launch."""
+    s = None
+    # x, ids, n, K, W13, E, H, I, ep, dt, h, counts, offsets, splits, perm, inv, stream
+    args = [P, P, 32, 8, P, 64, 128, 128, 1, 1, P, P, P, P, P, P, s]
+    for i, v, code in ((9, 0, EUNSUP),      # fp32
+                       (2, 33, EUNSUP),     # more tokens than one row tile holds
+                       (3, 33, EUNSUP),     # 32 x 33 pairs > 1024
+                       (8, 3, EINVAL),      # ep does not divide E
+                       (6, 100, EINVAL),    # H not a multiple of the tile width
+                       (2, -1, EINVAL),
+                       (10, None, EINVAL),  # no h
+                       (14, None, EINVAL)):  # no perm
+        bad = list(args)
+        bad[i] = v
+        assert lib.moe_expert_w13_swiglu_from_ids(*bad) == code, (i, v)
