@@ -225,6 +225,46 @@ def _warm(fn, n, torch, settle_ms):
         torch.cuda.synchronize()
 
 
+class _TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence: recording it writes a
+    timestamp without the system-scope cache write-back and invalidation a default event performs, which
+    would otherwise slow the kernels that follow it. The HIP runtime is the one the library runs on
+    (its symbols resolved through the library's handle)."""
+
+    _DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+
+        self._lib = _moe_lib()
+        self._ct = ctypes
+        h = ctypes.c_void_p()
+        if self._lib.hipEventCreateWithFlags(ctypes.byref(h), ctypes.c_uint(self._DISABLE_SYSTEM_FENCE)) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        self.handle = h.value
+
+    def elapsed_ms(self, end):
+        ct = self._ct
+        if self._lib.hipEventSynchronize(ct.c_void_p(end.handle)) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        ms = ct.c_float()
+        if self._lib.hipEventElapsedTime(ct.byref(ms), ct.c_void_p(self.handle), ct.c_void_p(end.handle)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        try:
+            self._lib.hipEventDestroy(self._ct.c_void_p(self.handle))
+        except Exception:  # noqa: BLE001 - interpreter shutdown
+            pass
+
+
+def _moe_lib():
+    import routing_token_permute_amd as moe
+
+    return moe.load_library()
+
+
 def _time_region(fn, reps, torch):
     """Average ms per call of fn() over `reps` calls, HIP events on the current stream."""
     start = torch.cuda.Event(enable_timing=True)
@@ -328,10 +368,21 @@ def _layer_bench(w, args, torch, moe, dev, detail):
     def step():
         moe.moe_forward(x, Wg, W13, W2, K, w.renorm, bias=bias, y=y, ws=ws)
 
+    # The timed steps record a pair of HIP events around the layer's GEMM1 launch (moe_forward_timed, on
+    # the stream the layer runs on), which gives the dominant kernel's duration inside the timed region.
+    # The events skip the system-scope fence on record, so they cost the steps no cache write-back.
+    g1_ev = [(_TimingEvent(), _TimingEvent()) for _ in range(args.steps)]
+    g1_iter = iter(g1_ev)
+
+    def step_timed():
+        a_, b_ = next(g1_iter)
+        moe.moe_forward_timed(x, Wg, W13, W2, K, w.renorm, a_.handle, b_.handle, bias=bias, y=y, ws=ws)
+
     _warm(step, args.warmup, torch, args.settle_ms)
     t0 = time.perf_counter()
-    ms = _time_region(step, args.steps, torch)
+    ms = _time_region(step_timed, args.steps, torch)
     wall = time.perf_counter() - t0
+    g1_live_ms = sum(a_.elapsed_ms(b_) for a_, b_ in g1_ev) / len(g1_ev)
     spread = _pcts(_time_each(step, max(args.steps, 10), torch))
     logits, ids, wts = moe.moe_route(x, Wg, bias, K, w.renorm)
     meta = moe.moe_permute(ids, None, E)
@@ -389,14 +440,18 @@ def _layer_bench(w, args, torch, moe, dev, detail):
                  "gemm_bf16_kernel<GATED=true, GATHER=true> (GEMM1 with fused row gather + SwiGLU epilogue)")
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
     if flops1 / bytes_[g1] >= ridge:
-        a = stages[g1]["TFLOP/s"]
+        a = round(flops1 / (g1_live_ms * 1e-3) / 1e12, 1)
         roof = {"kernel": g1_kernel, "bound": "mfma", "achieved": a, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(a / PEAK_BF16_TFLOPS, 4)}
     else:
-        a = stages[g1]["GB/s"]
+        a = round(bytes_[g1] / (g1_live_ms * 1e-3) / 1e9, 1)
         roof = {"kernel": g1_kernel, "bound": "hbm", "achieved": a, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(a / PEAK_HBM_GBPS, 4)}
     roof["traffic"] = None
+    roof["kernel_ms"] = round(g1_live_ms, 5)
+    roof["timing"] = ("mean of HIP events recorded right before and after the GEMM1 launch inside each timed "
+                      "moe_forward call (moe_forward_timed), on the layer's stream")
+    roof["kernel_ms_alone"] = round(st[g1], 5)  # the same launch replayed alone from a HIP graph
     out = {"ms": round(ms, 5), "tokens/s": round(n / (ms * 1e-3), 1), "step_spread": spread,
            "wall_s_timed_region": round(wall, 3),
            "grouped_gemm": {"TFLOP/s": round(gg, 1), "frac_bf16_peak": round(gg / PEAK_BF16_TFLOPS, 4),
@@ -885,8 +940,8 @@ def _bench_fp8(args, workload=None, cpu_leg=True):
     on the device before timing) on the decode (n=32) or OLMoE (n=4096) batch:
     tokens/s, the FP8 GEMMs' bandwidth against their weight bytes, and the bf16
     layer on the same inputs for comparison. The *_fp8a workloads also carry the
-    activations as per-token FP8 (moe_forward_fp8a: padded FP8 receive buffer,
-    FP8 x FP8 GEMM1)."""
+    activations as per-token FP8 (moe_forward_fp8a: FP8 x FP8 GEMMs, the token
+    rows read in place; the padded receive buffer timed beside it)."""
     import torch
 
     import routing_token_permute_amd as moe
@@ -958,6 +1013,15 @@ def _bench_fp8(args, workload=None, cpu_leg=True):
         # The padded receive buffer an expert-parallel exchange would deliver (not on the one-GPU layer's path).
         st["alt_dispatch_fp8"] = _time_region_graph(lambda: moe.moe_dispatch_fp8(meta, codes_tok, s_tok, K, out=d8),
                                                     R, torch)
+        # Decode-sized batches: the layer runs GEMM1 straight from the ids (no permute launch).
+        try:
+            h8i, meta8i = moe.moe_expert_w13_swiglu_from_ids_fp8a(codes_tok, s_tok, ids, q13, s13)
+        except moe.MoEError:
+            meta8i = None
+        if meta8i is not None:
+            st["gemm1_swiglu_fp8a_from_ids"] = _time_region_graph(
+                lambda: moe.moe_expert_w13_swiglu_from_ids_fp8a(codes_tok, s_tok, ids, q13, s13, h=h8i, out=meta8i),
+                R, torch)
     bytes_ = {  # algorithmic: activations once, FP8 codes and scales of the hit experts once, outputs once
         "gemm1_swiglu_fp8": nk * H * 2 + hit * (2 * I * H + 2 * I * 4) + nk * I * 2 + nk * 4,
         "gemm2_fp8": nk * I * 2 + hit * (H * I + H * 4) + nk * H * 2,
@@ -971,6 +1035,8 @@ def _bench_fp8(args, workload=None, cpu_leg=True):
         bytes_["quantize_h_fp8"] = nk * I * 2 + nk * I + nk * 4
         bytes_["gemm2_fp8a"] = nk * (I + 4) + hit * (H * I + H * 4) + nk * H * 2
         flops["gemm2_fp8a"] = 2.0 * nk * I * H
+        bytes_["gemm1_swiglu_fp8a_from_ids"] = bytes_["gemm1_swiglu_fp8a"] + nk * 8 + (2 * E + 2) * 4
+        flops["gemm1_swiglu_fp8a_from_ids"] = flops["gemm1_swiglu_fp8a"]
     stages = {}
     for k, v in st.items():
         gbs = bytes_[k] / (v * 1e-3) / 1e9
@@ -981,6 +1047,10 @@ def _bench_fp8(args, workload=None, cpu_leg=True):
     kname = ("gemm_f8f8_kernel<GATED, GATHER> (GEMM1 + SwiGLU, FP8 token rows read through perm x FP8 weights, "
              "FP8 MFMA 32x32x64)" if act8 else
              "gemm_w8_kernel<GATED=true, GATHER=true> (GEMM1 + SwiGLU, FP8 weights)")
+    if "gemm1_swiglu_fp8a_from_ids" in st:
+        dom = "gemm1_swiglu_fp8a_from_ids"
+        kname = ("gemm_f8f8_kernel<GATED, GATHER, IDS> (decode GEMM1 + SwiGLU that places the routing ids itself, "
+                 "FP8 token rows x FP8 weights, FP8 MFMA 32x32x64)")
     if base == "decode_bf16":
         roof = {"kernel": kname, "bound": "hbm", "achieved": stages[dom]["GB/s"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": stages[dom]["frac_hbm"], "traffic": None}

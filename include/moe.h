@@ -269,7 +269,9 @@ moe_status moe_unpermute_combine(const void* Y_perm, const int32_t* inv, const f
  * moe_forward — the whole layer, Algorithm 2: moe_route, the metadata part
  * of moe_permute (ep=1), moe_expert_w13_swiglu_gather, moe_expert_w2 and
  * moe_unpermute_combine enqueued back to back on one stream, with no host
- * synchronisation.
+ * synchronisation. For shapes moe_expert_w13_swiglu_from_ids serves (bf16,
+ * n <= 32) that call replaces the permute and the gathered GEMM1 (same
+ * results, one launch fewer).
  *
  *   y            (n, H) dtype out.
  *   logits_out   (n, E) fp32 out, or NULL.
@@ -287,6 +289,18 @@ moe_status moe_forward(const void* x, const void* W_gate, const float* bias, con
                        int n, int H, int I, int E, int K, int renorm, moe_dtype dt, void* y, float* logits_out,
                        int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
                        hipStream_t stream);
+
+/* moe_forward_timed — moe_forward that also records two caller-created HIP
+ * events on `stream`, right before and right after the layer's GEMM1 launch
+ * (the gathered GEMM1 + SwiGLU, or at n <= 32 the GEMM1 from the ids), so
+ * that a caller can time the layer's dominant kernel inside the layer call.
+ * Either event may be NULL (then it is not recorded); with both NULL this is
+ * moe_forward. The events stay the caller's. With n == 0 nothing is recorded. */
+moe_status moe_forward_timed(const void* x, const void* W_gate, const float* bias, const void* W13, const void* W2,
+                             int n, int H, int I, int E, int K, int renorm, moe_dtype dt, void* y,
+                             float* logits_out, int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out,
+                             void* ws, size_t ws_bytes, hipEvent_t gemm1_begin, hipEvent_t gemm1_end,
+                             hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * moe_forward_noalloc — moe_forward for callers that cannot allocate device
@@ -621,9 +635,18 @@ moe_status moe_forward_fp8(const void* x, const void* W_gate, const float* bias,
  * (n, H) uint8 with scale s_tok[perm[r] / K] (moe_quantize_rows_fp8 of x);
  * perm as from moe_permute; h (n*K, I) bf16 out. H a multiple of 128.
  *
+ * moe_expert_w13_swiglu_from_ids_fp8a — moe_expert_w13_swiglu_gather_fp8a for
+ * a decode-sized batch straight from the routing ids, as
+ * moe_expert_w13_swiglu_from_ids does it for bf16: the GEMM places the pairs
+ * itself and also writes counts, offsets, splits, perm and inv (moe_permute's
+ * values). topk_ids (n, K) int32 with K distinct experts per token; ep as
+ * moe_permute. Shapes it serves: n <= 32, n*K <= 1024, E <= 256, else
+ * MOE_EUNSUPPORTED; n == 0 writes zero counts, offsets and splits.
+ *
  * moe_forward_fp8a — the layer with FP8 activations and FP8 weights: moe_route
  * on x (bf16), the moe_permute metadata, moe_quantize_rows_fp8 of x,
- * moe_expert_w13_swiglu_gather_fp8a, moe_quantize_rows_fp8 of h,
+ * moe_expert_w13_swiglu_gather_fp8a (at n <= 32:
+ * moe_expert_w13_swiglu_from_ids_fp8a in place of both), moe_quantize_rows_fp8 of h,
  * moe_expert_w2_fp8a and moe_unpermute_combine. On one GPU the per-token FP8
  * rows are read in place through perm, as moe_forward reads x; the padded
  * receive buffer of moe_dispatch_fp8 is the form an expert-parallel exchange
@@ -645,6 +668,11 @@ moe_status moe_expert_w13_swiglu_fp8a(const uint8_t* x_q, const float* x_scale, 
 moe_status moe_expert_w13_swiglu_gather_fp8a(const uint8_t* codes_tok, const float* s_tok, const int32_t* perm,
                                              int n, int K, const int32_t* offsets, const uint8_t* W13q,
                                              const float* s13, int E, int H, int I, void* h, hipStream_t stream);
+moe_status moe_expert_w13_swiglu_from_ids_fp8a(const uint8_t* codes_tok, const float* s_tok,
+                                               const int32_t* topk_ids, int n, int K, const uint8_t* W13q,
+                                               const float* s13, int E, int H, int I, int ep, void* h,
+                                               int32_t* counts, int32_t* offsets, int32_t* splits, int32_t* perm,
+                                               int32_t* inv, hipStream_t stream);
 moe_status moe_expert_w2_fp8a(const uint8_t* h_q, const float* h_scale, const int32_t* offsets_padded, int rows_max,
                               const uint8_t* W2q, const float* s2, int E, int H, int I, void* Y_perm,
                               hipStream_t stream);

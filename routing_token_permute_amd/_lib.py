@@ -39,6 +39,8 @@ SIGNATURES = {
     "moe_grouped_swiglu": (_I, [_VP, _VP, _I, _VP, _VP, _I, _I, _I, _I, _VP, _VP, _SZ, _VP]),
     "moe_expert_w13_swiglu": (_I, [_VP, _VP, _I, _VP, _I, _I, _I, _I, _VP, _VP]),
     "moe_expert_w13_swiglu_gather": (_I, [_VP, _VP, _I, _I, _VP, _VP, _I, _I, _I, _I, _VP, _VP]),
+    "moe_expert_w13_swiglu_from_ids_fp8a": (_I, [_VP, _VP, _VP, _I, _I, _VP, _VP, _I, _I, _I, _I, _VP, _VP, _VP, _VP,
+                                                 _VP, _VP, _VP]),
     "moe_expert_w13_swiglu_from_ids": (_I, [_VP, _VP, _I, _I, _VP, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP,
                                             _VP]),
     "moe_expert_w2": (_I, [_VP, _VP, _I, _VP, _I, _I, _I, _I, _VP, _VP]),
@@ -60,6 +62,10 @@ SIGNATURES = {
     "moe_forward": (
         _I,
         [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+    ),
+    "moe_forward_timed": (
+        _I,
+        [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP, _VP],
     ),
     "moe_expert_w13_swiglu_gather_train": (_I, [_VP, _VP, _I, _I, _VP, _VP, _I, _I, _I, _I, _VP, _VP, _VP]),
     "moe_forward_train_workspace_size": (_SZ, [_I, _I, _I]),
@@ -493,6 +499,41 @@ def moe_forward(x, W_gate, W13, W2, K: int, renorm: bool, bias=None, y=None, ws=
     )
     _check(code, "moe_forward")
     return (y, *extra) if routing_out else y
+
+
+@_on_stream
+def moe_forward_timed(x, W_gate, W13, W2, K: int, renorm: bool, gemm1_begin, gemm1_end, bias=None, y=None, ws=None,
+                      stream=None):
+    """moe_forward that records two timing events on the stream right before and after the layer's GEMM1
+    launch. Each event is a torch.cuda.Event (enable_timing=True, recorded once before so that it exists),
+    a raw hipEvent_t handle (int), or None. Returns y."""
+    lib = load_library()
+    n, H = x.shape
+    E = W_gate.shape[1]
+    I = W13.shape[2] // 2  # noqa: E741
+    dev = x.device
+    _need(x, "x", (n, H))
+    _need(W_gate, "W_gate", (H, E), x.dtype, dev)
+    _need(W13, "W13", (E, H, 2 * I), x.dtype, dev)
+    _need(W2, "W2", (E, I, H), x.dtype, dev)
+    if bias is not None:
+        _need(bias, "bias", (E,), torch.float32, dev)
+    y = _empty((n, H), x.dtype, dev) if y is None else y
+    _need(y, "y", (n, H), x.dtype, dev)
+    dt = _dt(x)
+    ws = _workspace(lib.moe_forward_workspace_size(n, H, I, E, K, dt), dev, ws)
+    handles = []
+    for ev in (gemm1_begin, gemm1_end):
+        h = ev if (ev is None or isinstance(ev, int)) else ev.cuda_event
+        if ev is not None and not h:
+            raise MoEError("record the event once before passing it (torch creates it on first record)")
+        handles.append(h)
+    code = lib.moe_forward_timed(
+        _ptr(x), _ptr(W_gate), _ptr(bias), _ptr(W13), _ptr(W2), n, H, I, E, K, int(bool(renorm)), dt,
+        _ptr(y), None, None, None, None, _ptr(ws), ws.numel(), handles[0], handles[1], _stream(dev, stream),
+    )
+    _check(code, "moe_forward_timed")
+    return y
 
 
 def moe_forward_persistent_workspace_size(n, H, I, E, K, pool_row_tiles=0) -> int:  # noqa: E741
@@ -1016,6 +1057,38 @@ def moe_expert_w13_swiglu_gather_fp8a(codes_tok, s_tok, perm, K: int, offsets, W
                                                  _ptr(W13q), _ptr(s13), E, H, I, _ptr(h), _stream(dev, stream)),
            "moe_expert_w13_swiglu_gather_fp8a")
     return h
+
+
+@_on_stream
+def moe_expert_w13_swiglu_from_ids_fp8a(codes_tok, s_tok, topk_ids, W13q, s13, ep: int = 1, h=None, out=None,
+                                        stream=None):
+    """The FP8 x FP8 GEMM1 of a decode-sized batch straight from the routing ids: h (n*K, I) bf16 and the
+    moe_permute metadata dict (counts, offsets, splits, perm, inv) from one launch. Returns (h, meta)."""
+    lib = load_library()
+    n, H = codes_tok.shape
+    K = topk_ids.shape[1]
+    E, I2, _ = W13q.shape
+    I = I2 // 2  # noqa: E741
+    dev = codes_tok.device
+    _need(codes_tok, "codes_tok", (n, H), torch.uint8)
+    _need(s_tok, "s_tok", (n,), torch.float32, dev)
+    _need(topk_ids, "topk_ids", (n, K), torch.int32, dev)
+    _need(W13q, "W13q", (E, 2 * I, H), torch.uint8, dev)
+    _need(s13, "s13", (E, 2 * I), torch.float32, dev)
+    h = _empty((n * K, I), torch.bfloat16, dev) if h is None else h
+    _need(h, "h", (n * K, I), torch.bfloat16, dev)
+    out = dict(out or {})
+    for name, shape in (("counts", (E,)), ("offsets", (E + 1,)), ("splits", (ep,)), ("perm", (n * K,)),
+                        ("inv", (n * K,))):
+        out.setdefault(name, _empty(shape, torch.int32, dev))
+        _need(out[name], name, shape, torch.int32, dev)
+    code = lib.moe_expert_w13_swiglu_from_ids_fp8a(
+        _ptr(codes_tok), _ptr(s_tok), _ptr(topk_ids), n, K, _ptr(W13q), _ptr(s13), E, H, I, ep, _ptr(h),
+        _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["splits"]), _ptr(out["perm"]), _ptr(out["inv"]),
+        _stream(dev, stream),
+    )
+    _check(code, "moe_expert_w13_swiglu_from_ids_fp8a")
+    return h, out
 
 
 @_on_stream

@@ -22,6 +22,7 @@
 #include <algorithm>
 
 #include "gemm_tiles.hpp"
+#include "place_pairs.hpp"
 
 namespace moe {
 namespace {
@@ -214,13 +215,18 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // GATHER (GEMM1 only): A row r is the token row perm[r] / topk of Aq (n_a
 // token rows) and its scale a_scale[perm[r] / topk]: the per-token FP8 rows
 // are read in place, with no dispatched copy.
-template <bool GATED, bool GATHER, int BM, int BK, int CAP, int WM, int WN>
+// IDS (gathered GEMM1 on decode-sized batches, one row tile per expert): no
+// perm or offsets yet; every workgroup places the n_a * topk routing ids
+// itself in LDS (place_pairs), slot t is expert t / NB and column block
+// t % NB, and workgroup 0 writes the metadata for the kernels that follow.
+template <bool GATED, bool GATHER, int BM, int BK, int CAP, int WM, int WN, bool IDS = false>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
     const uint8_t* __restrict__ Aq, const float* __restrict__ a_scale, const int32_t* __restrict__ perm, int topk,
     int n_a, const int32_t* __restrict__ offsets, int E, int rows, int Kdim, const uint8_t* __restrict__ Bq,
     long long b_stride, const float* __restrict__ b_scale, int N, int I, uint16_t* __restrict__ C, int NB,
-    int n_slots) {
+    int n_slots, IdsMeta im) {
   static_assert(!GATHER || GATED, "the row gather belongs to GEMM1");
+  static_assert(!IDS || (GATHER && BM < 256), "placement from ids: gathered decode GEMM1");
   using Cfg = F8Cfg<BM, BK, CAP>;
   constexpr int STAGE = Cfg::STAGE, NSTAGE = Cfg::NSTAGE, A_BYTES = Cfg::A_BYTES, A_REG = Cfg::A_REG;
   constexpr int ROW = Cfg::ROW, CPR = Cfg::CPR, RPR = Cfg::ROWS_PER_REGION;
@@ -239,11 +245,32 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
   const int l32 = lane & 31, hi = lane >> 5;
   const int nk = Kdim / BK;
 
+  // IDS: the placement of the pairs, in LDS (one-element arrays otherwise).
+  __shared__ int ids_l[IDS ? kIdsMaxPairs : 1];
+  __shared__ int perm_l[IDS ? kIdsMaxPairs : 1];
+  __shared__ int cnt_l[IDS ? NW : 1][IDS ? kMaxExperts : 1];
+  __shared__ int offs_l[IDS ? kMaxExperts + 1 : 1];
+  if constexpr (IDS) {
+    const int total = n_a * topk;  // <= kIdsMaxPairs (checked by the launcher)
+    for (int f = tid; f < total; f += 64 * NW) ids_l[f] = im.ids[f];
+    place_pairs<NW>(ids_l, total, E, im.ep, im.id_bits, cnt_l, offs_l, perm_l,
+                    PlaceOut{blockIdx.x == 0, im.counts, im.offsets, im.splits, im.perm, im.inv});
+    __syncthreads();
+  }
+  auto pair_at = [&](int r) { return IDS ? perm_l[r] : perm[r]; };
+
   int slot_id = blockIdx.x;
   auto next_tile = [&]() {
     Tile t{0, 0, 0, 0, false};
     while (slot_id < n_slots && !t.valid) {
-      t = find_tile<BM>(offsets, E, rows, NB, xcd_remap(slot_id, n_slots));
+      if constexpr (IDS) {
+        const int tt = xcd_remap(slot_id, n_slots);
+        const int e = tt / NB;
+        const int r0 = offs_l[e], r1 = offs_l[e + 1];
+        t = Tile{e, r0, r1, tt - e * NB, r1 > r0};
+      } else {
+        t = find_tile<BM>(offsets, E, rows, NB, xcd_remap(slot_id, n_slots));
+      }
       slot_id += gridDim.x;
     }
     return t;
@@ -263,7 +290,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
       if (r < A_REG) {
         int arow = t.r0 + min(rr, mrows - 1);
         if constexpr (GATHER) {
-          const int f = perm[arow];
+          const int f = pair_at(arow);
           arow = ((unsigned)f < (unsigned)(n_a * topk)) ? f / topk : 0;
         }
         src[j] = Aq + (size_t)arow * Kdim + c * 16;
@@ -385,7 +412,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
       float sa = 0.f;
       if (row_ok) {
         if constexpr (GATHER) {
-          const int f = perm[t.r0 + row];
+          const int f = pair_at(t.r0 + row);
           sa = ((unsigned)f < (unsigned)(n_a * topk)) ? a_scale[f / topk] : 0.f;
         } else {
           sa = a_scale[t.r0 + row];
@@ -480,7 +507,7 @@ void launch_f8f8_cfg(const uint8_t* Aq, const float* a_scale, const int32_t* per
   const int grid = std::min(n_slots, stream_cu_count(s));
   gemm_f8f8_kernel<GATED, GATHER, BM, BK, CAP, WM, WN><<<grid, 64 * WM * WN, 0, s>>>(
       Aq, a_scale, perm, topk, n_a, offsets, E, rows, Kdim, Bq, (long long)N * Kdim, b_scale, N, I, (uint16_t*)C, NB,
-      n_slots);
+      n_slots, IdsMeta{});
 }
 
 template <bool GATED, bool GATHER = false>
@@ -545,6 +572,28 @@ hipError_t launch_w13_swiglu_gather_fp8a(const uint8_t* codes_tok, const float* 
   const int rows = n * K;
   if (rows == 0) return hipSuccess;
   launch_f8f8<true, true>(codes_tok, s_tok, offsets, E, rows, H, W13q, s13, 2 * I, I, h, s, perm, K, n);
+  return hipGetLastError();
+}
+
+bool w13_from_ids_fp8a_ok(int n, int K, int E) {
+  return n > 0 && n <= kF8SmallBM && (long long)n * K <= kIdsMaxPairs && E <= kMaxExperts &&
+         (long long)n * K <= (long long)kF8SmallRowsPerExpert * E;
+}
+
+hipError_t launch_w13_swiglu_from_ids_fp8a(const uint8_t* codes_tok, const float* s_tok, const int32_t* ids, int n,
+                                           int K, const uint8_t* W13q, const float* s13, int E, int H, int I, int ep,
+                                           void* h, int32_t* counts, int32_t* offsets, int32_t* splits,
+                                           int32_t* perm, int32_t* inv, hipStream_t s) {
+  if (!w13_from_ids_fp8a_ok(n, K, E) || ep <= 0 || E % ep != 0) return hipErrorInvalidValue;
+  int id_bits = 0;
+  while ((1 << id_bits) < E) ++id_bits;
+  const int NB = ceil_div(I, BN / 2);
+  const int n_slots = E * NB;
+  const int grid = std::min(n_slots, stream_cu_count(s));
+  gemm_f8f8_kernel<true, true, kF8SmallBM, kF8SmallBK, kF8SmallCap, kF8SmallWM, kF8SmallWN, true>
+      <<<grid, 64 * kF8SmallWM * kF8SmallWN, 0, s>>>(codes_tok, s_tok, nullptr, K, n, nullptr, E, n * K, H, W13q,
+                                                      (long long)2 * I * H, s13, 2 * I, I, (uint16_t*)h, NB, n_slots,
+                                                      IdsMeta{ids, counts, offsets, splits, perm, inv, ep, id_bits});
   return hipGetLastError();
 }
 

@@ -50,21 +50,6 @@ namespace {
 constexpr int kBM = 256, kBK = 32, kGemmWM = 4, kGemmWN = 4;
 constexpr int kSmallBM = 32, kSmallBK = 64, kSmallWM = 1, kSmallWN = 4;
 constexpr int kSmallRowsPerExpert = 64;  // rows / E at or below this: small tiles
-// GEMM1 from the routing ids (IDS): at most this many (token, slot) pairs.
-constexpr int kIdsMaxPairs = 1024;
-
-// IDS: the routing ids the GEMM places itself, and where workgroup 0 writes
-// the dispatch metadata (counts, offsets, splits, perm, inv) for the kernels
-// that follow.
-struct IdsMeta {
-  const int32_t* ids;
-  int32_t* counts;
-  int32_t* offsets;
-  int32_t* splits;
-  int32_t* perm;
-  int32_t* inv;
-  int ep, id_bits;
-};
 
 // GATED (GEMM1): the 256 staged columns are 128 gate columns followed by the
 // matching 128 up columns; the tile writes 128 columns of h. Otherwise

@@ -211,10 +211,11 @@ moe_status check_forward(const void* x, const void* W_gate, const float* bias, c
 
 // The layer's launches over a workspace laid out by forward_layout at `base`
 // (n > 0, arguments checked).
+// g1_begin / g1_end: optional events recorded right before and after GEMM1.
 moe_status forward_enqueue(const void* x, const void* W_gate, const float* bias, const void* W13, const void* W2,
                            int n, int H, int I, int E, int K, int renorm, moe_dtype dt, void* y, float* logits_out,
                            int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, char* base,
-                           hipStream_t stream) {
+                           hipStream_t stream, hipEvent_t g1_begin = nullptr, hipEvent_t g1_end = nullptr) {
   const ForwardLayout L = forward_layout(n, H, I, E, K, dt);
   float* logits = logits_out ? logits_out : (float*)(base + L.logits);
   int32_t* ids = topk_ids_out ? topk_ids_out : (int32_t*)(base + L.ids);
@@ -230,6 +231,7 @@ moe_status forward_enqueue(const void* x, const void* W_gate, const float* bias,
   if (w13_from_ids_ok(n, K, E, dt)) {
     // Decode-sized batch: GEMM1 places the pairs itself and writes the
     // metadata for GEMM2 and the combine (one launch fewer).
+    if (g1_begin != nullptr && hipEventRecord(g1_begin, stream) != hipSuccess) return MOE_EHIP;
     e = launch_w13_swiglu_from_ids(x, ids, n, K, W13, E, H, I, 1, base + L.h, counts, offsets, splits, perm, inv,
                                    stream);
   } else {
@@ -237,9 +239,11 @@ moe_status forward_enqueue(const void* x, const void* W_gate, const float* bias,
     e = launch_permute(ids, nullptr, n, H, E, K, 1, dt, counts, offsets, splits, perm, inv, nullptr,
                        (int32_t*)(base + L.pscratch), stream);
     if (e != hipSuccess) return MOE_EHIP;
+    if (g1_begin != nullptr && hipEventRecord(g1_begin, stream) != hipSuccess) return MOE_EHIP;
     e = launch_w13_swiglu_gather(x, perm, n, K, offsets, W13, E, H, I, dt, base + L.h, stream);
   }
   if (e != hipSuccess) return MOE_EHIP;
+  if (g1_end != nullptr && hipEventRecord(g1_end, stream) != hipSuccess) return MOE_EHIP;
   // Expert-major GEMM2, then the gathered weighted combine: measured a little
   // faster here than moe_expert_w2_scatter + moe_sum_slots, whose scattered
   // row stores cost GEMM2 more than the contiguous sum saves.
@@ -503,10 +507,11 @@ size_t moe_workspace_size(int n, int H, int I, int E, int K, moe_dtype dt) {
   return moe_forward_workspace_size(n, H, I, E, K, dt);
 }
 
-moe_status moe_forward(const void* x, const void* W_gate, const float* bias, const void* W13, const void* W2, int n,
-                       int H, int I, int E, int K, int renorm, moe_dtype dt, void* y, float* logits_out,
-                       int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
-                       hipStream_t stream) {
+moe_status moe_forward_timed(const void* x, const void* W_gate, const float* bias, const void* W13, const void* W2,
+                             int n, int H, int I, int E, int K, int renorm, moe_dtype dt, void* y,
+                             float* logits_out, int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out,
+                             void* ws, size_t ws_bytes, hipEvent_t gemm1_begin, hipEvent_t gemm1_end,
+                             hipStream_t stream) {
   const moe_status st = check_forward(x, W_gate, bias, W13, W2, n, H, I, E, K, dt, y, logits_out, topk_ids_out,
                                       topk_w_out, counts_out);
   if (st != MOE_OK) return st;
@@ -515,7 +520,15 @@ moe_status moe_forward(const void* x, const void* W_gate, const float* bias, con
     return counts_out ? from_hip(launch_fill_zero(counts_out, (size_t)E * 4, stream)) : MOE_OK;
   if (ws == nullptr || ws_bytes < forward_layout(n, H, I, E, K, dt).total) return MOE_EWORKSPACE;
   return forward_enqueue(x, W_gate, bias, W13, W2, n, H, I, E, K, renorm, dt, y, logits_out, topk_ids_out,
-                         topk_w_out, counts_out, (char*)ws, stream);
+                         topk_w_out, counts_out, (char*)ws, stream, gemm1_begin, gemm1_end);
+}
+
+moe_status moe_forward(const void* x, const void* W_gate, const float* bias, const void* W13, const void* W2, int n,
+                       int H, int I, int E, int K, int renorm, moe_dtype dt, void* y, float* logits_out,
+                       int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  return moe_forward_timed(x, W_gate, bias, W13, W2, n, H, I, E, K, renorm, dt, y, logits_out, topk_ids_out,
+                           topk_w_out, counts_out, ws, ws_bytes, nullptr, nullptr, stream);
 }
 
 size_t moe_forward_persistent_workspace_size(int n, int H, int I, int E, int K, int pool_row_tiles) {
@@ -949,6 +962,29 @@ moe_status moe_expert_w13_swiglu_gather_fp8a(const uint8_t* codes_tok, const flo
       launch_w13_swiglu_gather_fp8a(codes_tok, s_tok, perm, n, K, offsets, W13q, s13, E, H, I, h, stream));
 }
 
+moe_status moe_expert_w13_swiglu_from_ids_fp8a(const uint8_t* codes_tok, const float* s_tok,
+                                               const int32_t* topk_ids, int n, int K, const uint8_t* W13q,
+                                               const float* s13, int E, int H, int I, int ep, void* h,
+                                               int32_t* counts, int32_t* offsets, int32_t* splits, int32_t* perm,
+                                               int32_t* inv, hipStream_t stream) {
+  if (n < 0 || !experts_ok(E, K) || ep < 1 || E % ep != 0 || !hidden_ok(H, MOE_BF16) || H % 128 != 0 ||
+      !hidden_ok(I, MOE_BF16) || I % 128 != 0)
+    return MOE_EINVAL;
+  if ((long long)n * K > INT32_MAX) return MOE_EINVAL;
+  if (counts == nullptr || offsets == nullptr || splits == nullptr) return MOE_EINVAL;
+  if (!word_ok({topk_ids, counts, offsets, splits, perm, inv, s_tok})) return MOE_EINVAL;
+  if (n == 0)
+    return from_hip(launch_permute(nullptr, nullptr, 0, H, E, K, ep, MOE_BF16, counts, offsets, splits, nullptr,
+                                   nullptr, nullptr, nullptr, stream));
+  if (!w13_from_ids_fp8a_ok(n, K, E)) return MOE_EUNSUPPORTED;
+  if (codes_tok == nullptr || s_tok == nullptr || topk_ids == nullptr || W13q == nullptr || s13 == nullptr ||
+      h == nullptr || perm == nullptr || inv == nullptr)
+    return MOE_EINVAL;
+  if (!vec_ok({codes_tok, W13q, s13, h})) return MOE_EINVAL;
+  return from_hip(launch_w13_swiglu_from_ids_fp8a(codes_tok, s_tok, topk_ids, n, K, W13q, s13, E, H, I, ep, h,
+                                                  counts, offsets, splits, perm, inv, stream));
+}
+
 moe_status moe_expert_w2_fp8a(const uint8_t* h_q, const float* h_scale, const int32_t* offsets_padded, int rows_max,
                               const uint8_t* W2q, const float* s2, int E, int H, int I, void* Y_perm,
                               hipStream_t stream) {
@@ -1002,12 +1038,22 @@ moe_status moe_forward_fp8a(const void* x, const void* W_gate, const float* bias
   // bf16 layer reads x): the padded receive buffer of moe_dispatch_fp8 is what
   // an expert-parallel exchange would deliver, and not needed here.
   hipError_t e = launch_route(x, W_gate, bias, n, H, E, K, renorm, dt, logits, ids, w, stream);
-  if (e == hipSuccess)
-    e = launch_permute(ids, nullptr, n, H, E, K, 1, dt, counts, offsets, (int32_t*)(base + L.splits), perm, inv,
-                       nullptr, (int32_t*)(base + L.pscratch), stream);
-  if (e == hipSuccess) e = launch_quantize_rows_fp8(x, n, H, dt, codes_tok, s_tok, stream);
-  if (e == hipSuccess)
-    e = launch_w13_swiglu_gather_fp8a(codes_tok, s_tok, perm, n, K, offsets, W13q, s13, E, H, I, base + L.h, stream);
+  if (w13_from_ids_fp8a_ok(n, K, E)) {
+    // Decode-sized batch: GEMM1 places the pairs itself and writes the
+    // metadata for GEMM2 and the combine (no permute launch).
+    if (e == hipSuccess) e = launch_quantize_rows_fp8(x, n, H, dt, codes_tok, s_tok, stream);
+    if (e == hipSuccess)
+      e = launch_w13_swiglu_from_ids_fp8a(codes_tok, s_tok, ids, n, K, W13q, s13, E, H, I, 1, base + L.h, counts,
+                                          offsets, (int32_t*)(base + L.splits), perm, inv, stream);
+  } else {
+    if (e == hipSuccess)
+      e = launch_permute(ids, nullptr, n, H, E, K, 1, dt, counts, offsets, (int32_t*)(base + L.splits), perm, inv,
+                         nullptr, (int32_t*)(base + L.pscratch), stream);
+    if (e == hipSuccess) e = launch_quantize_rows_fp8(x, n, H, dt, codes_tok, s_tok, stream);
+    if (e == hipSuccess)
+      e = launch_w13_swiglu_gather_fp8a(codes_tok, s_tok, perm, n, K, offsets, W13q, s13, E, H, I, base + L.h,
+                                        stream);
+  }
   // h per row in FP8, then GEMM2 on the FP8 MFMA.
   if (e == hipSuccess)
     e = launch_quantize_rows_fp8(base + L.h, nk, I, MOE_BF16, (uint8_t*)(base + L.h_q), (float*)(base + L.h_scale),

@@ -180,6 +180,15 @@ hipError_t launch_w13_swiglu_fp8a(const uint8_t* x_q, const float* x_scale, cons
 hipError_t launch_w13_swiglu_gather_fp8a(const uint8_t* codes_tok, const float* s_tok, const int32_t* perm, int n,
                                          int K, const int32_t* offsets, const uint8_t* W13q, const float* s13, int E,
                                          int H, int I, void* h, hipStream_t s);
+// The same from the routing ids on decode-sized batches (n <= 32, n * K <=
+// 1024, E <= 256): the GEMM places the pairs itself and writes counts,
+// offsets, splits, perm and inv. w13_from_ids_fp8a_ok says whether it serves
+// a shape.
+bool w13_from_ids_fp8a_ok(int n, int K, int E);
+hipError_t launch_w13_swiglu_from_ids_fp8a(const uint8_t* codes_tok, const float* s_tok, const int32_t* ids, int n,
+                                           int K, const uint8_t* W13q, const float* s13, int E, int H, int I, int ep,
+                                           void* h, int32_t* counts, int32_t* offsets, int32_t* splits,
+                                           int32_t* perm, int32_t* inv, hipStream_t s);
 // GEMM2 with FP8 activations: Y_perm (rows_max, H) bf16 = (h codes x per-row
 // scales) . (W2 codes x column scales) over the padded receive buffer's rows.
 hipError_t launch_w2_fp8a(const uint8_t* h_q, const float* h_scale, const int32_t* offsets_padded, int rows_max,

@@ -48,6 +48,22 @@ struct PlaceOut {
   int32_t* inv;      // (total)
 };
 
+// A GEMM that places the routing ids itself (decode-sized batches): at most
+// this many (token, slot) pairs, staged in LDS.
+constexpr int kIdsMaxPairs = 1024;
+
+// Such a GEMM's ids, and where its workgroup 0 writes the dispatch metadata
+// (counts, offsets, splits, perm, inv) for the kernels that follow.
+struct IdsMeta {
+  const int32_t* ids;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* splits;
+  int32_t* perm;
+  int32_t* inv;
+  int ep, id_bits;
+};
+
 // NW waves of the calling workgroup run this together; every thread of the
 // workgroup must call it (it contains barriers). sid: the `total` ids in LDS.
 // cnt: an LDS array of NW x kMaxExperts counters. offs: an LDS array of

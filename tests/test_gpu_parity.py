@@ -445,6 +445,30 @@ def test_forward_large_batch_sampled(dev):
     assert_close(to_f64(y)[sample], ref["y"], "bf16", f"{what}, 512 sampled tokens")
 
 
+@pytest.mark.parametrize("name", ["decode_bf16", "olmoe_bf16"])
+def test_forward_timed_matches_forward_and_brackets_gemm1(dev, name):
+    """moe_forward_timed gives moe_forward's bits; its two events bracket GEMM1 inside the call (a positive
+    span shorter than the whole call); an event torch has not created yet is refused."""
+    w = make_config(name)
+    t = layer_tensors(w, dev)
+    y = moe.moe_forward(t["x"], t["W_gate"], t["W13"], t["W2"], w.K, w.renorm, bias=t["bias"])
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record()
+    g1.record()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    y2 = moe.moe_forward_timed(t["x"], t["W_gate"], t["W13"], t["W2"], w.K, w.renorm, g0, g1, bias=t["bias"])
+    end.record()
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    span, whole = g0.elapsed_time(g1), start.elapsed_time(end)
+    print(f"[{name}] GEMM1 {span * 1e3:.1f} us of {whole * 1e3:.1f} us", flush=True)
+    assert 0 < span < whole
+    with pytest.raises(moe.MoEError):
+        moe.moe_forward_timed(t["x"], t["W_gate"], t["W13"], t["W2"], w.K, w.renorm,
+                              torch.cuda.Event(enable_timing=True), None, bias=t["bias"])
+
+
 def test_forward_side_stream_internal_workspace(dev):
     """moe_forward on a side stream with the binding allocating the workspace and outputs: those blocks
     belong to the side stream, so work on the main stream that allocates and overwrites memory right

@@ -315,3 +315,16 @@ def test_w13_from_ids_rejects_unserved_shapes(lib):
         bad = list(args)
         bad[i] = v
         assert lib.moe_expert_w13_swiglu_from_ids(*bad) == code, (i, v)
+
+
+def test_w13_from_ids_fp8a_rejects_unserved_shapes(lib):
+    """The FP8 form serves the same decode shapes (n <= 32, n*K <= 1024, E <= 256, H and I multiples of
+    128) and refuses the rest before any launch."""
+    s = None
+    # codes, s_tok, ids, n, K, W13q, s13, E, H, I, ep, h, counts, offsets, splits, perm, inv, stream
+    args = [P, P, P, 32, 8, P, P, 64, 128, 128, 1, P, P, P, P, P, P, s]
+    for i, v, code in ((3, 33, EUNSUP), (4, 33, EUNSUP), (8, 192, EINVAL), (9, 64, EINVAL), (10, 3, EINVAL),
+                       (11, None, EINVAL), (16, None, EINVAL)):
+        bad = list(args)
+        bad[i] = v
+        assert lib.moe_expert_w13_swiglu_from_ids_fp8a(*bad) == code, (i, v)
