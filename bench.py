@@ -103,7 +103,9 @@ def _kernel_label(name):
     if "gemm_f8f8_kernel<" in name:
         args = name.split("gemm_f8f8_kernel<", 1)[1].split(">", 1)[0].split(",")
         gated, gather, bm = args[0].strip() == "true", args[1].strip() == "true", args[2].strip()
-        return ("gemm1_swiglu_f8f8" if gated else "gemm2_f8f8") + ("_gather" if gather else "") + f"_bm{bm}"
+        ids = len(args) > 7 and args[7].strip() == "true"
+        return (("gemm1_swiglu_f8f8" if gated else "gemm2_f8f8") + ("_from_ids" if ids else "_gather" if gather else "")
+                + f"_bm{bm}")
     for k, lab in (("quantize_rows_kernel", "quantize_rows_fp8"), ("dispatch_fp8_kernel", "dispatch_fp8"),
                    ("quantize_fp8_kernel", "quantize_weights_fp8"), ("fused_ffn_kernel", "fused_ffn"),
                    ("fill_zero_kernel", "fill_zero")):
