@@ -75,6 +75,9 @@ CASES = [
     (31, 128, 128, 128, 33, 1, "routed"),  # 1023 pairs
     (32, 128, 128, 64, 1, 1, "routed"),
     (24, 128, 128, 64, 8, 1, "invalid"),
+    (5, 128, 128, 1, 1, 1, "routed"),  # one expert: every pair in one tile
+    (7, 64, 64, 2, 2, 2, "routed"),  # every token picks both experts; a single 64-deep k-step
+    (32, 128, 192, 4, 4, 1, "routed"),  # K = E: all 32 tokens in every expert; a masked column tail
 ]
 
 
@@ -157,6 +160,8 @@ FP8_CASES = [
     (32, 2048, 1024, 64, 8, 1, "routed"),  # the OLMoE decode batch
     (32, 128, 128, 256, 32, 8, "routed"),  # 1024 pairs over 256 experts
     (24, 128, 128, 64, 8, 1, "invalid"),
+    (5, 128, 128, 1, 1, 1, "routed"),
+    (32, 128, 256, 4, 4, 2, "routed"),  # K = E: all 32 tokens in every expert
 ]
 
 
