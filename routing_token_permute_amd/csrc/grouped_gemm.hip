@@ -23,6 +23,9 @@
 //     transpose read (ds_read_b64_tr_b16); A rows are K-contiguous and read
 //     with ds_read_b128. Both LDS layouts are XOR-swizzled so those reads run
 //     without bank conflicts.
+//   * Decode-sized batches (n <= 32 tokens) can skip the permute launch:
+//     GEMM1 then places the routing ids itself in LDS (IDS below), each
+//     expert being one row tile.
 //   * GEMM1 tiles pair 128 gate columns j with the 128 up columns I + j, so a
 //     lane holds gate and up of the same output in registers and the SwiGLU
 //     epilogue (fp32, then bf16 round-to-nearest-even) needs no extra pass.
@@ -494,10 +497,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
       store_tile_plain(t);
   };
 
-  // Persistent loop over this workgroup's tiles. Before the epilogue of a
-  // tile, the first NSTAGE-1 k-steps of the next one are put in flight (the
-  // barrier after the main loop frees the whole ring), so the DMA of the
-  // next tile and the stores of this one overlap.
+  // IDS: stage the ids and place the pairs (every workgroup; workgroup 0 also
+  // writes the metadata) before the first tile is looked up.
   if constexpr (IDS) {
     const int total = n_a * topk;  // <= kIdsMaxPairs (checked by the launcher)
     for (int f = tid; f < total; f += 64 * NW) ids_l[f] = im.ids[f];
@@ -505,6 +506,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
                     PlaceOut{blockIdx.x == 0, im.counts, im.offsets, im.splits, im.perm, im.inv});
     __syncthreads();
   }
+  // Persistent loop over this workgroup's tiles. Before the epilogue of a
+  // tile, the first NSTAGE-1 k-steps of the next one are put in flight (the
+  // barrier after the main loop frees the whole ring), so the DMA of the
+  // next tile and the stores of this one overlap.
   Tile t = next_tile();
   if (!t.valid) return;
   set_sources(t);
