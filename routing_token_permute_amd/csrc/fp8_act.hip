@@ -18,7 +18,10 @@
 //     "MoE 分布式推理基础（基于 vLLM）"): FP8 activation rows times FP8 weight
 //     columns (moe_quantize_fp8's column-major codes), both K-contiguous, on
 //     the gfx950 FP8 MFMA 32x32x64 with fp32 accumulation; the row and column
-//     scales multiply the accumulators in the epilogue before SiLU * up.
+//     scales multiply the accumulators in the epilogue before SiLU * up. On one
+//     GPU the layer reads each pair's token row in place through perm (GATHER)
+//     instead of from the receive buffer, and at n <= 32 places the routing
+//     ids itself (IDS); the same kernel without SwiGLU is GEMM2 on FP8 h.
 #include <algorithm>
 
 #include "gemm_tiles.hpp"
