@@ -1015,6 +1015,14 @@ def _bench_fp8(args, workload=None, cpu_leg=True):
         "gemm2_fp8": _time_region_graph(lambda: moe.moe_expert_w2_fp8(h, meta["offsets"], q2, s2, Y_perm=Yp), R, torch),
     }
     nk = n * K
+    if not act8:  # decode-sized batches: the layer runs the FP8-weight GEMM1 straight from the ids
+        try:
+            h8w, meta8w = moe.moe_expert_w13_swiglu_from_ids_fp8(x, ids, q13, s13)
+        except moe.MoEError:
+            meta8w = None
+        if meta8w is not None:
+            st["gemm1_swiglu_fp8_from_ids"] = _time_region_graph(
+                lambda: moe.moe_expert_w13_swiglu_from_ids_fp8(x, ids, q13, s13, h=h8w, out=meta8w), R, torch)
     if act8:  # the stages moe_forward_fp8a runs: FP8 rows read in place, FP8 x FP8 GEMMs, h quantized per row
         codes_tok, s_tok = moe.moe_quantize_rows_fp8(x)
         h8 = moe.moe_expert_w13_swiglu_gather_fp8a(codes_tok, s_tok, meta["perm"], K, meta["offsets"], q13, s13)
@@ -1048,6 +1056,8 @@ def _bench_fp8(args, workload=None, cpu_leg=True):
         "gemm2_fp8": nk * I * 2 + hit * (H * I + H * 4) + nk * H * 2,
     }
     flops = {"gemm1_swiglu_fp8": 2.0 * nk * H * 2 * I, "gemm2_fp8": 2.0 * nk * I * H}
+    bytes_["gemm1_swiglu_fp8_from_ids"] = bytes_["gemm1_swiglu_fp8"] + nk * 8 + (2 * E + 2) * 4
+    flops["gemm1_swiglu_fp8_from_ids"] = flops["gemm1_swiglu_fp8"]
     if act8:
         bytes_["quantize_rows_fp8"] = n * H * 2 + n * H + n * 4
         bytes_["alt_dispatch_fp8"] = nk * H + rpad * H + rpad * 8 + nk * 4
@@ -1068,6 +1078,10 @@ def _bench_fp8(args, workload=None, cpu_leg=True):
     kname = ("gemm_f8f8_kernel<GATED, GATHER> (GEMM1 + SwiGLU, FP8 token rows read through perm x FP8 weights, "
              "FP8 MFMA 32x32x64)" if act8 else
              "gemm_w8_kernel<GATED=true, GATHER=true> (GEMM1 + SwiGLU, FP8 weights)")
+    if "gemm1_swiglu_fp8_from_ids" in st:
+        dom = "gemm1_swiglu_fp8_from_ids"
+        kname = ("gemm_w8_kernel<GATED, GATHER, IDS> (decode GEMM1 + SwiGLU that places the routing ids itself, "
+                 "FP8 weights)")
     if "gemm1_swiglu_fp8a_from_ids" in st:
         dom = "gemm1_swiglu_fp8a_from_ids"
         kname = ("gemm_f8f8_kernel<GATED, GATHER, IDS> (decode GEMM1 + SwiGLU that places the routing ids itself, "

@@ -567,6 +567,19 @@ moe_status moe_expert_w13_swiglu_gather_fp8(const void* x, const int32_t* perm, 
                                             const uint8_t* W13q, const float* s13, int E, int H, int I, moe_dtype dt,
                                             void* h, hipStream_t stream);
 
+/* moe_expert_w13_swiglu_from_ids_fp8 — moe_expert_w13_swiglu_gather_fp8 for a
+ * decode-sized batch straight from the routing ids, as
+ * moe_expert_w13_swiglu_from_ids does it for bf16 weights: the GEMM places the
+ * pairs itself and also writes counts, offsets, splits, perm and inv
+ * (moe_permute's values). x (n, H) bf16; topk_ids (n, K) int32 with K distinct
+ * experts per token; ep as moe_permute. Shapes it serves: n <= 32,
+ * n*K <= 1024, E <= 256, else MOE_EUNSUPPORTED; n == 0 writes zero counts,
+ * offsets and splits. */
+moe_status moe_expert_w13_swiglu_from_ids_fp8(const void* x, const int32_t* topk_ids, int n, int K,
+                                              const uint8_t* W13q, const float* s13, int E, int H, int I, int ep,
+                                              void* h, int32_t* counts, int32_t* offsets, int32_t* splits,
+                                              int32_t* perm, int32_t* inv, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * moe_expert_w2_fp8 — moe_expert_w2 with FP8 W2: Y_perm[p] = h[p] · W2'[e],
  * W2'[e][k, n] = decode(W2q[e, n, k]) * s2[e, n].
@@ -577,7 +590,8 @@ moe_status moe_expert_w2_fp8(const void* h, const int32_t* offsets, int rows, co
 
 /* ---------------------------------------------------------------------------
  * moe_forward_fp8 — moe_forward with FP8 expert weights (route, permute
- * metadata, FP8 GEMM1 with the gather fused, FP8 GEMM2, combine). Workspace:
+ * metadata, FP8 GEMM1 with the gather fused, FP8 GEMM2, combine; at n <= 32
+ * moe_expert_w13_swiglu_from_ids_fp8 in place of the first two). Workspace:
  * moe_forward_workspace_size(n, H, I, E, K, MOE_BF16) bytes.
  * ------------------------------------------------------------------------- */
 moe_status moe_forward_fp8(const void* x, const void* W_gate, const float* bias, const uint8_t* W13q,

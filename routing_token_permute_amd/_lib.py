@@ -41,6 +41,8 @@ SIGNATURES = {
     "moe_expert_w13_swiglu_gather": (_I, [_VP, _VP, _I, _I, _VP, _VP, _I, _I, _I, _I, _VP, _VP]),
     "moe_expert_w13_swiglu_from_ids_fp8a": (_I, [_VP, _VP, _VP, _I, _I, _VP, _VP, _I, _I, _I, _I, _VP, _VP, _VP, _VP,
                                                  _VP, _VP, _VP]),
+    "moe_expert_w13_swiglu_from_ids_fp8": (_I, [_VP, _VP, _I, _I, _VP, _VP, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP,
+                                                _VP, _VP]),
     "moe_expert_w13_swiglu_from_ids": (_I, [_VP, _VP, _I, _I, _VP, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP,
                                             _VP]),
     "moe_expert_w2": (_I, [_VP, _VP, _I, _VP, _I, _I, _I, _I, _VP, _VP]),
@@ -1057,6 +1059,35 @@ def moe_expert_w13_swiglu_gather_fp8a(codes_tok, s_tok, perm, K: int, offsets, W
                                                  _ptr(W13q), _ptr(s13), E, H, I, _ptr(h), _stream(dev, stream)),
            "moe_expert_w13_swiglu_gather_fp8a")
     return h
+
+
+@_on_stream
+def moe_expert_w13_swiglu_from_ids_fp8(x, topk_ids, W13q, s13, ep: int = 1, h=None, out=None, stream=None):
+    """GEMM1 with FP8 weights on a decode-sized batch straight from the routing ids: h (n*K, I) bf16 and the
+    moe_permute metadata dict (counts, offsets, splits, perm, inv) from one launch. Returns (h, meta)."""
+    lib = load_library()
+    n, H = x.shape
+    K = topk_ids.shape[1]
+    E, I2, _ = W13q.shape
+    I = I2 // 2  # noqa: E741
+    dev = x.device
+    _need(x, "x", (n, H), torch.bfloat16)
+    _need(topk_ids, "topk_ids", (n, K), torch.int32, dev)
+    _need(W13q, "W13q", (E, 2 * I, H), torch.uint8, dev)
+    _need(s13, "s13", (E, 2 * I), torch.float32, dev)
+    h = _empty((n * K, I), torch.bfloat16, dev) if h is None else h
+    _need(h, "h", (n * K, I), torch.bfloat16, dev)
+    out = dict(out or {})
+    for name, shape in (("counts", (E,)), ("offsets", (E + 1,)), ("splits", (ep,)), ("perm", (n * K,)),
+                        ("inv", (n * K,))):
+        out.setdefault(name, _empty(shape, torch.int32, dev))
+        _need(out[name], name, shape, torch.int32, dev)
+    code = lib.moe_expert_w13_swiglu_from_ids_fp8(
+        _ptr(x), _ptr(topk_ids), n, K, _ptr(W13q), _ptr(s13), E, H, I, ep, _ptr(h), _ptr(out["counts"]),
+        _ptr(out["offsets"]), _ptr(out["splits"]), _ptr(out["perm"]), _ptr(out["inv"]), _stream(dev, stream),
+    )
+    _check(code, "moe_expert_w13_swiglu_from_ids_fp8")
+    return h, out
 
 
 @_on_stream

@@ -28,6 +28,7 @@
 #include <algorithm>
 
 #include "gemm_tiles.hpp"
+#include "place_pairs.hpp"
 
 namespace moe {
 namespace {
@@ -77,14 +78,19 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(u32x2_t w) {
 // (2I, H) code matrix, rows 128..255 the matching up columns I + nb*128 + r;
 // the tile writes 128 columns of h. Otherwise (GEMM2) 256 columns of Y.
 // GATHER: A row r is token row perm[r] / topk of x.
+// IDS (gathered GEMM1 on decode-sized batches, one row tile per expert): no
+// perm or offsets yet; every workgroup places the n_a * topk routing ids
+// itself in LDS (place_pairs), slot t is expert t / NB and column block
+// t % NB, and workgroup 0 writes the metadata for the kernels that follow.
 // Bq: codes of expert e at Bq + e * b_stride, N rows of Kdim bytes.
 // scale: fp32 column scales of expert e at scale + e * N (N = 2I or H).
-template <bool GATED, bool GATHER, int BM, int WM, int WN>
+template <bool GATED, bool GATHER, int BM, int WM, int WN, bool IDS = false>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_w8_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ perm, int topk, int n_a,
     const int32_t* __restrict__ offsets, int E, int rows, int Kdim, const uint8_t* __restrict__ Bq,
     long long b_stride, const float* __restrict__ scale, int N, int Nout, int up_col, uint16_t* __restrict__ C,
-    int ldc, int NB, int n_slots) {
+    int ldc, int NB, int n_slots, IdsMeta im) {
+  static_assert(!IDS || (GATED && GATHER && BM < 256), "placement from ids: gathered decode GEMM1");
   using Cfg = W8Cfg<BM>;
   constexpr int A_BYTES = Cfg::A_BYTES, STAGE = Cfg::STAGE, NSTAGE = Cfg::NSTAGE;
   constexpr int NW = WM * WN;
@@ -103,11 +109,31 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_w8_kernel(
   const int g = lane >> 4, li = lane & 15;
   const int nk = Kdim / kW8BK;
 
+  // IDS: the placement of the pairs, in LDS (one-element arrays otherwise).
+  __shared__ int ids_l[IDS ? kIdsMaxPairs : 1];
+  __shared__ int perm_l[IDS ? kIdsMaxPairs : 1];
+  __shared__ int cnt_l[IDS ? NW : 1][IDS ? kMaxExperts : 1];
+  __shared__ int offs_l[IDS ? kMaxExperts + 1 : 1];
+  if constexpr (IDS) {
+    const int total = n_a * topk;  // <= kIdsMaxPairs (checked by the launcher)
+    for (int f = tid; f < total; f += 64 * NW) ids_l[f] = im.ids[f];
+    place_pairs<NW>(ids_l, total, E, im.ep, im.id_bits, cnt_l, offs_l, perm_l,
+                    PlaceOut{blockIdx.x == 0, im.counts, im.offsets, im.splits, im.perm, im.inv});
+    __syncthreads();
+  }
+
   int slot_id = blockIdx.x;
   auto next_tile = [&]() {
     Tile t{0, 0, 0, 0, false};
     while (slot_id < n_slots && !t.valid) {
-      t = find_tile<BM>(offsets, E, rows, NB, xcd_remap(slot_id, n_slots));
+      if constexpr (IDS) {
+        const int tt = xcd_remap(slot_id, n_slots);
+        const int e = tt / NB;
+        const int r0 = offs_l[e], r1 = offs_l[e + 1];
+        t = Tile{e, r0, r1, tt - e * NB, r1 > r0};
+      } else {
+        t = find_tile<BM>(offsets, E, rows, NB, xcd_remap(slot_id, n_slots));
+      }
       slot_id += gridDim.x;
     }
     return t;
@@ -141,7 +167,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_w8_kernel(
         const int c = (lane % 8) ^ w8_a_swz(row);
         int arow = t.r0 + min(row, mrows - 1);
         if constexpr (GATHER) {
-          const int f = perm[arow];
+          const int f = IDS ? perm_l[arow] : perm[arow];
           arow = ((unsigned)f < (unsigned)(n_a * topk)) ? f / topk : 0;
         }
         src[j] = (const char*)(A + (size_t)arow * Kdim) + c * 16;
@@ -388,7 +414,7 @@ void launch_w8_cfg(const void* a, const int32_t* perm, int topk, int n_a, const 
   const int grid = std::min(n_slots, stream_cu_count(s));
   gemm_w8_kernel<GATED, GATHER, BM, WM, WN><<<grid, 64 * WM * WN, 0, s>>>(
       (const uint16_t*)a, perm, topk, n_a, offsets, E, rows, Kdim, (const uint8_t*)Bq, bstride, scale, N, Nout,
-      up_col, (uint16_t*)C, ldc, NB, n_slots);
+      up_col, (uint16_t*)C, ldc, NB, n_slots, IdsMeta{});
 }
 
 template <bool GATED, bool GATHER>
@@ -423,6 +449,27 @@ hipError_t launch_w13_swiglu_gather_fp8(const void* x, const int32_t* perm, int 
   if (rows == 0) return hipSuccess;
   launch_w8<true, true>(x, perm, K, n, offsets, E, rows, H, W13q, (long long)2 * I * H, s13, 2 * I, I, I, h, I,
                         ceil_div(I, BN / 2), s);
+  return hipGetLastError();
+}
+
+bool w13_from_ids_fp8_ok(int n, int K, int E) {
+  return n > 0 && n <= kW8SmallBM && (long long)n * K <= kIdsMaxPairs && E <= kMaxExperts &&
+         (long long)n * K <= (long long)kW8SmallRowsPerExpert * E;
+}
+
+hipError_t launch_w13_swiglu_from_ids_fp8(const void* x, const int32_t* ids, int n, int K, const uint8_t* W13q,
+                                          const float* s13, int E, int H, int I, int ep, void* h, int32_t* counts,
+                                          int32_t* offsets, int32_t* splits, int32_t* perm, int32_t* inv,
+                                          hipStream_t s) {
+  if (!w13_from_ids_fp8_ok(n, K, E) || ep <= 0 || E % ep != 0) return hipErrorInvalidValue;
+  int id_bits = 0;
+  while ((1 << id_bits) < E) ++id_bits;
+  const int NB = ceil_div(I, BN / 2);
+  const int n_slots = E * NB;
+  const int grid = std::min(n_slots, stream_cu_count(s));
+  gemm_w8_kernel<true, true, kW8SmallBM, kW8SmallWM, kW8SmallWN, true><<<grid, 64 * kW8SmallWM * kW8SmallWN, 0, s>>>(
+      (const uint16_t*)x, nullptr, K, n, nullptr, E, n * K, H, W13q, (long long)2 * I * H, s13, 2 * I, I, I,
+      (uint16_t*)h, I, NB, n_slots, IdsMeta{ids, counts, offsets, splits, perm, inv, ep, id_bits});
   return hipGetLastError();
 }
 

@@ -850,6 +850,27 @@ moe_status moe_expert_w13_swiglu_gather_fp8(const void* x, const int32_t* perm, 
   return from_hip(launch_w13_swiglu_gather_fp8(x, perm, n, K, offsets, W13q, s13, E, H, I, h, stream));
 }
 
+moe_status moe_expert_w13_swiglu_from_ids_fp8(const void* x, const int32_t* topk_ids, int n, int K,
+                                              const uint8_t* W13q, const float* s13, int E, int H, int I, int ep,
+                                              void* h, int32_t* counts, int32_t* offsets, int32_t* splits,
+                                              int32_t* perm, int32_t* inv, hipStream_t stream) {
+  if (n < 0 || !experts_ok(E, K) || ep < 1 || E % ep != 0 || !hidden_ok(H, MOE_BF16) || !hidden_ok(I, MOE_BF16))
+    return MOE_EINVAL;
+  if ((long long)n * K > INT32_MAX) return MOE_EINVAL;
+  if (counts == nullptr || offsets == nullptr || splits == nullptr) return MOE_EINVAL;
+  if (!word_ok({topk_ids, counts, offsets, splits, perm, inv})) return MOE_EINVAL;
+  if (n == 0)
+    return from_hip(launch_permute(nullptr, nullptr, 0, H, E, K, ep, MOE_BF16, counts, offsets, splits, nullptr,
+                                   nullptr, nullptr, nullptr, stream));
+  if (!w13_from_ids_fp8_ok(n, K, E)) return MOE_EUNSUPPORTED;
+  if (x == nullptr || topk_ids == nullptr || W13q == nullptr || s13 == nullptr || h == nullptr || perm == nullptr ||
+      inv == nullptr)
+    return MOE_EINVAL;
+  if (!vec_ok({x, W13q, s13, h})) return MOE_EINVAL;
+  return from_hip(launch_w13_swiglu_from_ids_fp8(x, topk_ids, n, K, W13q, s13, E, H, I, ep, h, counts, offsets,
+                                                 splits, perm, inv, stream));
+}
+
 moe_status moe_expert_w2_fp8(const void* h, const int32_t* offsets, int rows, const uint8_t* W2q, const float* s2,
                              int E, int H, int I, moe_dtype dt, void* Y_perm, hipStream_t stream) {
   const moe_status st = check_fp8_gemm(h, offsets, rows, W2q, s2, E, H, I, dt, Y_perm);
@@ -885,10 +906,17 @@ moe_status moe_forward_fp8(const void* x, const void* W_gate, const float* bias,
   int32_t* inv = (int32_t*)(base + L.inv);
   hipError_t e = launch_route(x, W_gate, bias, n, H, E, K, renorm, dt, logits, ids, w, stream);
   if (e != hipSuccess) return MOE_EHIP;
-  e = launch_permute(ids, nullptr, n, H, E, K, 1, dt, counts, offsets, (int32_t*)(base + L.splits), perm, inv,
-                     nullptr, (int32_t*)(base + L.pscratch), stream);
-  if (e != hipSuccess) return MOE_EHIP;
-  e = launch_w13_swiglu_gather_fp8(x, perm, n, K, offsets, W13q, s13, E, H, I, base + L.h, stream);
+  if (w13_from_ids_fp8_ok(n, K, E)) {
+    // Decode-sized batch: GEMM1 places the pairs itself and writes the
+    // metadata for GEMM2 and the combine (no permute launch).
+    e = launch_w13_swiglu_from_ids_fp8(x, ids, n, K, W13q, s13, E, H, I, 1, base + L.h, counts, offsets,
+                                       (int32_t*)(base + L.splits), perm, inv, stream);
+  } else {
+    e = launch_permute(ids, nullptr, n, H, E, K, 1, dt, counts, offsets, (int32_t*)(base + L.splits), perm, inv,
+                       nullptr, (int32_t*)(base + L.pscratch), stream);
+    if (e != hipSuccess) return MOE_EHIP;
+    e = launch_w13_swiglu_gather_fp8(x, perm, n, K, offsets, W13q, s13, E, H, I, base + L.h, stream);
+  }
   if (e != hipSuccess) return MOE_EHIP;
   e = launch_w2_fp8(base + L.h, offsets, n * K, W2q, s2, E, H, I, base + L.Y_perm, stream);
   if (e != hipSuccess) return MOE_EHIP;

@@ -153,6 +153,14 @@ hipError_t launch_quantize_fp8(const void* W, int E, int Kd, int N, moe_dtype dt
 hipError_t launch_w13_swiglu_gather_fp8(const void* x, const int32_t* perm, int n, int K, const int32_t* offsets,
                                         const uint8_t* W13q, const float* s13, int E, int H, int I, void* h,
                                         hipStream_t s);
+// The same from the routing ids on decode-sized batches (n <= 32, n * K <=
+// 1024, E <= 256): the GEMM places the pairs itself and writes counts,
+// offsets, splits, perm and inv.
+bool w13_from_ids_fp8_ok(int n, int K, int E);
+hipError_t launch_w13_swiglu_from_ids_fp8(const void* x, const int32_t* ids, int n, int K, const uint8_t* W13q,
+                                          const float* s13, int E, int H, int I, int ep, void* h, int32_t* counts,
+                                          int32_t* offsets, int32_t* splits, int32_t* perm, int32_t* inv,
+                                          hipStream_t s);
 // GEMM2 with W2 codes (E, H, I) and scales (E, H).
 hipError_t launch_w2_fp8(const void* h, const int32_t* offsets, int rows, const uint8_t* W2q, const float* s2, int E,
                          int H, int I, void* Y_perm, hipStream_t s);

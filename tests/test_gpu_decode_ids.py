@@ -223,3 +223,67 @@ def test_forward_fp8a_decode_matches_staged_calls(dev, n, H, I, E, K, renorm):  
     torch.cuda.synchronize()
     assert torch.equal(ids, ids2) and torch.equal(counts, meta["counts"])
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), f"{what}: y differs from the staged calls"
+
+
+W8_CASES = [
+    # n, H, I, E, K, ep, kind
+    (3, 128, 128, 8, 2, 1, "routed"),
+    (32, 2048, 1024, 64, 8, 1, "routed"),  # the OLMoE decode batch
+    (32, 128, 128, 256, 32, 4, "routed"),  # 1024 pairs over 256 experts
+    (24, 128, 192, 64, 8, 1, "invalid"),  # a masked column tail
+]
+
+
+@pytest.mark.parametrize("n,H,I,E,K,ep,kind", W8_CASES)
+def test_w13_from_ids_fp8_weights(dev, n, H, I, E, K, ep, kind):  # noqa: E741
+    """GEMM1 with FP8 weights from the ids: metadata bit-exact against the oracle's placement, h bit for bit
+    the gathered FP8-weight GEMM1's on that placement, and within the bf16 bounds of the oracle's product
+    with the dequantized weight columns."""
+    from oracle import fp8 as of8
+
+    what = f"w13_from_ids_fp8 n={n} E={E} K={K} ep={ep} {kind}"
+    print(f"[{what}]", flush=True)
+    e_top = _ids(n, E, K, kind, seed=n * 139 + E)
+    ref = _placement(e_top, E, ep)
+    w = make_layer(n, H, I, E, K, seed=n + 5 * H + E)
+    t = layer_tensors(w, dev)
+    q13, s13 = moe.moe_quantize_fp8(t["W13"])
+    ids_d = torch.from_numpy(e_top.astype(np.int32)).to(dev)
+    h, meta = moe.moe_expert_w13_swiglu_from_ids_fp8(t["x"], ids_d, q13, s13, ep)
+    torch.cuda.synchronize()
+    rows = int(ref["offsets"][-1])
+    for k in ("counts", "offsets", "splits"):
+        assert (meta[k].cpu().numpy() == ref[k]).all(), f"{what}: {k} differ"
+    assert (meta["perm"].cpu().numpy()[:rows] == ref["perm"][:rows]).all(), f"{what}: perm differs"
+    assert (meta["inv"].cpu().numpy()[ref["valid"]] == ref["inv"][ref["valid"]]).all(), f"{what}: inv differs"
+    perm_full = np.zeros(n * K, dtype=np.int32)
+    perm_full[:rows] = ref["perm"][:rows]
+    h2 = moe.moe_expert_w13_swiglu_gather_fp8(t["x"], torch.from_numpy(perm_full).to(dev), K,
+                                             torch.from_numpy(ref["offsets"].astype(np.int32)).to(dev), q13, s13)
+    torch.cuda.synchronize()
+    assert torch.equal(h[:rows].view(torch.int16), h2[:rows].view(torch.int16)), f"{what}: h differs"
+    c13, r13 = of8.quantize_columns(w.W13_f32)
+    ref_h = om.grouped_gate_up(w.x_f32[ref["perm"][:rows] // K], ref["offsets"], of8.dequantize_columns(c13, r13))
+    assert_close(to_f64(h[:rows]), ref_h, "bf16", what, intermediate=True)
+
+
+@pytest.mark.parametrize("n,H,I,E,K,renorm", [(9, 256, 128, 16, 4, True), (32, 2048, 1024, 64, 8, False)])
+def test_forward_fp8_decode_matches_staged_calls(dev, n, H, I, E, K, renorm):  # noqa: E741
+    """moe_forward_fp8 at n <= 32 (the FP8-weight GEMM1 places the ids itself) gives the bits of the staged
+    calls: route, permute, gathered FP8-weight GEMM1, FP8-weight GEMM2, combine."""
+    what = f"forward fp8 from ids n={n} E={E} K={K}"
+    print(f"[{what}]", flush=True)
+    w = make_layer(n, H, I, E, K, dtype="bf16", renorm=renorm, seed=n * 13 + E)
+    t = layer_tensors(w, dev)
+    q13, s13 = moe.moe_quantize_fp8(t["W13"])
+    q2, s2 = moe.moe_quantize_fp8(t["W2"])
+    y, logits, ids, wts, counts = moe.moe_forward_fp8(t["x"], t["W_gate"], q13, s13, q2, s2, K, renorm,
+                                                      routing_out=True)
+    _, ids2, wts2 = moe.moe_route(t["x"], t["W_gate"], None, K, renorm)
+    meta = moe.moe_permute(ids2, None, E)
+    h = moe.moe_expert_w13_swiglu_gather_fp8(t["x"], meta["perm"], K, meta["offsets"], q13, s13)
+    Y = moe.moe_expert_w2_fp8(h, meta["offsets"], q2, s2)
+    y2 = moe.moe_unpermute_combine(Y, meta["inv"], wts2, n, K)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(counts, meta["counts"])
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), f"{what}: y differs from the staged calls"

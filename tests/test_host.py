@@ -328,3 +328,15 @@ def test_w13_from_ids_fp8a_rejects_unserved_shapes(lib):
         bad = list(args)
         bad[i] = v
         assert lib.moe_expert_w13_swiglu_from_ids_fp8a(*bad) == code, (i, v)
+
+
+def test_w13_from_ids_fp8_weights_rejects_unserved_shapes(lib):
+    """The FP8-weight form serves the same decode shapes and refuses the rest before any launch."""
+    s = None
+    # x, ids, n, K, W13q, s13, E, H, I, ep, h, counts, offsets, splits, perm, inv, stream
+    args = [P, P, 32, 8, P, P, 64, 128, 128, 1, P, P, P, P, P, P, s]
+    for i, v, code in ((2, 33, EUNSUP), (3, 33, EUNSUP), (7, 100, EINVAL), (9, 3, EINVAL), (10, None, EINVAL),
+                       (15, None, EINVAL)):
+        bad = list(args)
+        bad[i] = v
+        assert lib.moe_expert_w13_swiglu_from_ids_fp8(*bad) == code, (i, v)
