@@ -490,10 +490,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
   }
 }
 
-// Large batches: 256-row tiles, 16 waves, 64-code stages on a 4-deep ring
-// (32 KB each). Decode-like batches: 32-row tiles, 4 waves, 128-code stages on
-// a 3-deep ring (36 KB each), which keeps more weight bytes in flight.
-constexpr int kF8BM = 256, kF8BK = 64, kF8Cap = 4, kF8WM = 4, kF8WN = 4;
+// Large batches: 256-row tiles, 16 waves, 128-code stages on a 2-deep ring
+// (64 KB each; half the barriers per FLOP of 64-code stages on a 4-deep ring,
+// measured 3-4% faster for both GEMMs). Decode-like batches: 32-row tiles, 4
+// waves, 128-code stages on a 3-deep ring (36 KB each), which keeps more
+// weight bytes in flight.
+constexpr int kF8BM = 256, kF8BK = 128, kF8Cap = 2, kF8WM = 4, kF8WN = 4;
 constexpr int kF8SmallBM = 32, kF8SmallBK = 128, kF8SmallCap = 3, kF8SmallWM = 1, kF8SmallWN = 4;
 constexpr int kF8SmallRowsPerExpert = 64;
 
