@@ -14,7 +14,8 @@
 //     wave-wide prefix sum of the per-expert tile counts), so no host
 //     synchronisation is needed.
 //   * Both operands go straight from HBM into a ring of LDS stages with
-//     global_load_lds_dwordx4 (32-deep k-steps, three stages of 32 KB),
+//     global_load_lds_dwordx4 (GEMM1: 64-deep k-steps, two stages of 64 KB;
+//     GEMM2: 32-deep k-steps, three stages of 32 KB),
 //     each lane fetching the chunk that lands where the swizzled layout
 //     wants it. GEMM1 reads its A rows x[perm[r] / K] in that same copy, so
 //     no permuted copy of the tokens is made.
@@ -50,7 +51,10 @@ namespace {
 // large experts use 256-row tiles with 16 waves; when experts average few
 // rows (decode-like batches) 32-row tiles with a 4-stage ring keep the
 // weight stream deep instead.
-constexpr int kBM = 256, kBK = 32, kGemmWM = 4, kGemmWN = 4;
+// GEMM1 stages 64-deep k-steps on a 2-deep ring (half the barriers per FLOP;
+// measured 2-4% faster), GEMM2 32-deep ones on a 3-deep ring (1-2% faster
+// than 64-deep for its 32 k-steps per tile).
+constexpr int kBM = 256, kBK = 32, kBK1 = 64, kGemmWM = 4, kGemmWN = 4;
 constexpr int kSmallBM = 32, kSmallBK = 64, kSmallWM = 1, kSmallWN = 4;
 constexpr int kSmallRowsPerExpert = 64;  // rows / E at or below this: small tiles
 
@@ -87,8 +91,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
                                                                     uint16_t* __restrict__ C, int ldc, int NB,
                                                                     int n_slots, uint16_t* __restrict__ gu_out,
                                                                     IdsMeta im) {
-  // The 256-row tiles run on a 3-stage ring: measured a little faster than
-  // four or five stages for both GEMMs, whose deeper copy lead buys nothing.
+  // The 256-row tiles run on at most three stages (three of 32 KB for GEMM2;
+  // GEMM1's 64 KB stages fit two): measured a little faster than four or five
+  // stages, whose deeper copy lead buys nothing.
   using Cfg = TileCfg<BM, BK, (BM == 256) ? 3 : kMaxStages>;
   constexpr int A_BYTES = Cfg::A_BYTES, STAGE = Cfg::STAGE, NSTAGE = Cfg::NSTAGE, A_ROW = Cfg::A_ROW;
   constexpr int KS = BK / 32;              // 32-deep MFMA steps per stage
@@ -230,38 +235,36 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
   // MFMAs over them. `full` is a constant at each call site: the branch-free
   // form serves waves whose row slab is full, the guarded one the partly
   // filled slab of a short tile.
-  using AOps = bf16x8_t[KS][MT];
-  using BOps = bf16x8_t[KS][NT];
-  auto load_ops = [&](int stage, bool full, AOps& a, BOps& b) {
+  // Operands of one 32-deep MFMA step ks of a stage are read just before its
+  // MFMAs, so a 64-deep stage holds no more operand registers than a 32-deep
+  // one.
+  using AOps = bf16x8_t[MT];
+  using BOps = bf16x8_t[NT];
+  auto load_ops = [&](int stage, int ks, bool full, AOps& a, BOps& b) {
     const lds_char_t* As = smem + stage * STAGE;
     const lds_char_t* Bs = As + A_BYTES;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const lds_char_t* p = Bs + b_col[nt] + ks * 32 * B_ROW;
-        const bf16x4_t lo = lds_read_tr16(p);
-        const bf16x4_t hi = lds_read_tr16(p + 4 * B_ROW);
-        b[ks][nt] = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        if (full || mt < vm)
-          a[ks][mt] = __builtin_bit_cast(bf16x8_t, lds_read_b128(As + a_lane + mt * 16 * A_ROW + (ks ? a_c1 : a_c0)));
+    for (int nt = 0; nt < NT; ++nt) {
+      const lds_char_t* p = Bs + b_col[nt] + ks * 32 * B_ROW;
+      const bf16x4_t lo = lds_read_tr16(p);
+      const bf16x4_t hi = lds_read_tr16(p + 4 * B_ROW);
+      b[nt] = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      if (full || mt < vm)
+        a[mt] = __builtin_bit_cast(bf16x8_t, lds_read_b128(As + a_lane + mt * 16 * A_ROW + (ks ? a_c1 : a_c0)));
   };
   // The B operand goes first, so each accumulator tile is the transposed
   // product (see the epilogue).
   auto mma = [&](bool full, const AOps& a, const BOps& b) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int mt = 0; mt < MT; ++mt)
+      if (full || mt < vm) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        if (full || mt < vm) {
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[ks][nt], a[ks][mt], acc[mt][nt], 0, 0, 0);
-        }
+        for (int nt = 0; nt < NT; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[nt], a[mt], acc[mt][nt], 0, 0, 0);
+      }
   };
   // Waits until at most `stages` of this wave's later DMA stages are still
   // in flight (every stage is DMA_PER_STAGE loads per lane). Stores still in
@@ -310,10 +313,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
       __syncthreads();
       if (kt + NSTAGE - 1 < nk) issue(kt + NSTAGE - 1, slot == 0 ? NSTAGE - 1 : slot - 1);
       if (full || vm > 0) {
-        AOps a;
-        BOps b;
-        load_ops(slot, full, a, b);
-        mma(full, a, b);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          AOps a;
+          BOps b;
+          load_ops(slot, ks, full, a, b);
+          mma(full, a, b);
+        }
       }
       slot = (slot == NSTAGE - 1) ? 0 : slot + 1;
     }
@@ -613,7 +619,7 @@ void launch_bf16(const void* a, const int32_t* perm, int topk, int n_a, const in
     launch_cfg<GATED, GATHER, SCATTER, kSmallBM, kSmallBK, kSmallWM, kSmallWN, SAVE>(
         a, perm, topk, n_a, wrow, offsets, E, rows, Kdim, B, ldb, bstride, Nout, up_col, C, ldc, NB, gu_out, s);
   else
-    launch_cfg<GATED, GATHER, SCATTER, kBM, kBK, kGemmWM, kGemmWN, SAVE>(
+    launch_cfg<GATED, GATHER, SCATTER, kBM, GATED ? kBK1 : kBK, kGemmWM, kGemmWN, SAVE>(
         a, perm, topk, n_a, wrow, offsets, E, rows, Kdim, B, ldb, bstride, Nout, up_col, C, ldc, NB, gu_out, s);
 }
 
