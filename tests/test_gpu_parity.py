@@ -211,6 +211,7 @@ GROUPED_CASES = [
     (130, 5, 64, 64, "f32", "edge"),
     (300, 8, 128, 64, "f32", "random"),
     (76800, 256, 128, 64, "bf16", "random"),  # E at its maximum, 2 row tiles per expert: >1 tile per workgroup
+    (700, 4, 64, 128, "bf16", "random"),  # 256-row tiles with a single 64-deep k-step in GEMM1
 ]
 
 
