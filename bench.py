@@ -656,7 +656,7 @@ def main():
         "configs": configs,
         "peaks": _peaks(moe),
         "cpu_baseline": cpu,
-        "device": torch.cuda.get_device_name(dev),
+        "device": _device_name(torch, dev),
     }
     print(json.dumps(out), flush=True)
 
@@ -820,7 +820,7 @@ def _bench_ep_share(args):
         "fused_schedule": dict(core["fused_schedule"], **{"rows/s": core["rows/s_fused"]}),
         "roofline": core["roofline"],
         "cpu_baseline": core.get("cpu_baseline"),
-        "device": torch.cuda.get_device_name(dev),
+        "device": _device_name(torch, dev),
     }
     print(json.dumps(out), flush=True)
 
@@ -951,7 +951,7 @@ def _bench_train(args):
         "experts_hit": hit,
         "wall_s_timed_region": round(wall, 3),
         "cpu_baseline": cpu,
-        "device": torch.cuda.get_device_name(dev),
+        "device": _device_name(torch, dev),
     }
     print(json.dumps(out), flush=True)
 
@@ -1135,7 +1135,7 @@ def _bench_fp8(args, workload=None, cpu_leg=True):
         "experts_hit": hit,
         "wall_s_timed_region": round(wall, 3),
         "cpu_baseline": cpu,
-        "device": torch.cuda.get_device_name(dev),
+        "device": _device_name(torch, dev),
     }
     return out
 
@@ -1171,6 +1171,14 @@ def _blas_threads():
         return int(max([d.get("num_threads", 1) for d in threadpool_info()] or [1]))
     except Exception:  # noqa: BLE001
         return len(os.sched_getaffinity(0))
+
+
+def _device_name(torch, dev):
+    """The device's name with its architecture (hosts without the marketing
+    name table report a generic or empty name)."""
+    name = torch.cuda.get_device_name(dev) or ""
+    arch = getattr(torch.cuda.get_device_properties(dev), "gcnArchName", "") or ""
+    return f"{name} ({arch})" if name and arch else (name or arch)
 
 
 def _cpu_model():

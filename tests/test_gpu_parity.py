@@ -415,6 +415,15 @@ def test_forward_small_shapes(dev, n, H, I, E, K, dtype, renorm):  # noqa: E741
     _forward_parity(dev, w, f"forward n={n} E={E} K={K}")
 
 
+@pytest.mark.parametrize("n,H,I,E,K", [(256, 7168, 2048, 8, 2), (100, 4096, 1536, 16, 4)])
+def test_forward_wide_layer(dev, n, H, I, E, K):  # noqa: E741
+    """A wide layer (up to H = 7168, I = 2048): GEMM1 runs 112 k-steps of 64 and 16 column blocks, GEMM2 28
+    column blocks, the router 112 slices of W_gate; every row against the oracle. Weights ~ N(0, 0.01^2), so
+    that y stays about as large as at the OLMoE shape and the absolute bound keeps its meaning there."""
+    w = make_layer(n, H, I, E, K, seed=H + I, w_std=0.01)
+    _forward_parity(dev, w, f"wide layer H={H} I={I}")
+
+
 def test_forward_large_batch_sampled(dev):
     """The OLMoE layer on 16384 tokens (131072 expert rows, about 20 GEMM tiles per CU): every token's
     routing and dispatch is checked bit-exact (the oracle routes from the device's fp32 logits, which are
