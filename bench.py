@@ -572,7 +572,7 @@ def main():
         return
     if args.gpus != 1:
         print(
-            f"bench.py measures one GPU only: the layer runs on a single MI355X and this build has no "
+            f"bench.py measures one GPU only: the layer runs on a single MI355X and the library has no "
             f"multi-GPU path (asked for --gpus {args.gpus}).",
             file=sys.stderr,
         )
