@@ -54,8 +54,9 @@ def _parse():
                    help="olmoe_bf16: leave out the other configurations (tiny, skewed, decode, EP share)")
     p.add_argument("--profile-forward", type=int, default=0, metavar="N",
                    help="only run N moe_forward calls of the workload (for rocprofv3 counter passes)")
-    p.add_argument("--profile-layer", choices=["bf16", "fp8a", "persistent"], default="bf16",
-                   help="with --profile-forward: moe_forward (bf16), moe_forward_fp8a or moe_forward_persistent")
+    p.add_argument("--profile-layer", choices=["packed", "bf16", "fp8a", "persistent"], default="packed",
+                   help="with --profile-forward: moe_forward_packed (bf16, the weights packed once first), "
+                        "moe_forward (bf16), moe_forward_fp8a or moe_forward_persistent")
     p.add_argument("--summarize-counters", nargs="+", metavar="DIR",
                    help="turn rocprofv3 --pmc csv directories into the per-kernel counter summary printed on stdout")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle wall time for the CPU baseline")
@@ -99,7 +100,9 @@ def _kernel_label(name):
         args = name.split("gemm_bf16_kernel<", 1)[1].split(">", 1)[0].split(",")
         gated, bm = args[0].strip() == "true", args[3].strip()
         ids = len(args) > 8 and args[8].strip() == "true"
-        return ("gemm1_swiglu" if gated else "gemm2") + ("_from_ids" if ids else "") + f"_bm{bm}"
+        packed = len(args) > 9 and args[9].strip() == "true"
+        return (("gemm1_swiglu" if gated else "gemm2") + ("_from_ids" if ids else "") + f"_bm{bm}"
+                + ("_packed" if packed else ""))
     if "gemm_f8f8_kernel<" in name:
         args = name.split("gemm_f8f8_kernel<", 1)[1].split(">", 1)[0].split(",")
         gated, gather, bm = args[0].strip() == "true", args[1].strip() == "true", args[2].strip()
@@ -199,7 +202,7 @@ def _traffic_bytes():
         return None
     if d.get("source_sha256_16") != _source_hash():
         return None
-    return d.get("kernels", {}).get("gemm1_swiglu_bm256", {}).get("hbm_bytes")
+    return d.get("kernels", {}).get("gemm1_swiglu_bm256_packed", {}).get("hbm_bytes")
 
 
 def _copy_calibration():
@@ -380,30 +383,57 @@ def _layer_bench(w, args, torch, moe, dev, detail):
     y = torch.empty((n, H), dtype=tdt, device=dev)
     ws = torch.empty(moe.moe_forward_workspace_size(n, H, I, E, K, tdt), dtype=torch.uint8, device=dev)
 
-    def step():
+    # bf16 layers run over weights packed once into the GEMMs' tile order (moe_pack_w13 / moe_pack_w2,
+    # before any timing: the weights are static); the plain-layout moe_forward is timed beside it.
+    packed = w.dtype == "bf16"
+    if packed:
+        W13p, W2p = moe.moe_pack_w13(W13), moe.moe_pack_w2(W2)
+
+    def step_plain():
         moe.moe_forward(x, Wg, W13, W2, K, w.renorm, bias=bias, y=y, ws=ws)
 
-    # The timed steps record a pair of HIP events around the layer's GEMM1 launch (moe_forward_timed, on
-    # the stream the layer runs on), which gives the dominant kernel's duration inside the timed region.
+    def step():
+        if packed:
+            moe.moe_forward_packed(x, Wg, W13p, W2p, K, w.renorm, bias=bias, y=y, ws=ws)
+        else:
+            step_plain()
+
+    # The timed steps record a pair of HIP events around the layer's GEMM1 launch (moe_forward_packed's or
+    # moe_forward_timed's event arguments, on the stream the layer runs on), which gives the dominant
+    # kernel's duration inside the timed region.
     # The events skip the system-scope fence on record, so they cost the steps no cache write-back.
+    n_warm_ev = 4  # event pairs recorded before the timed region, so that no first record falls inside it
     try:
-        g1_ev = [(_TimingEvent(), _TimingEvent()) for _ in range(args.steps)]
+        g1_ev = [(_TimingEvent(), _TimingEvent()) for _ in range(args.steps + n_warm_ev)]
         fence_free = True
     except RuntimeError:  # the runtime refused the flag: torch's default timing events instead
-        g1_ev = [(_TorchTimingEvent(torch), _TorchTimingEvent(torch)) for _ in range(args.steps)]
+        g1_ev = [(_TorchTimingEvent(torch), _TorchTimingEvent(torch)) for _ in range(args.steps + n_warm_ev)]
         fence_free = False
     g1_iter = iter(g1_ev)
 
     def step_timed():
         a_, b_ = next(g1_iter)
-        moe.moe_forward_timed(x, Wg, W13, W2, K, w.renorm, a_.handle, b_.handle, bias=bias, y=y, ws=ws)
+        if packed:
+            moe.moe_forward_packed(x, Wg, W13p, W2p, K, w.renorm, bias=bias, y=y, ws=ws, gemm1_begin=a_.handle,
+                                   gemm1_end=b_.handle)
+        else:
+            moe.moe_forward_timed(x, Wg, W13, W2, K, w.renorm, a_.handle, b_.handle, bias=bias, y=y, ws=ws)
 
+    # The timed call path itself first, events included (its first call in a process can stall the host for
+    # tens of milliseconds), then the warm-up and clock-settle phase right before the timed region.
+    for _ in range(n_warm_ev):
+        step_timed()
+    g1_ev = g1_ev[n_warm_ev:]
     _warm(step, args.warmup, torch, args.settle_ms)
     t0 = time.perf_counter()
     ms = _time_region(step_timed, args.steps, torch)
     wall = time.perf_counter() - t0
     g1_live_ms = sum(a_.elapsed_ms(b_) for a_, b_ in g1_ev) / len(g1_ev)
     spread = _pcts(_time_each(step, max(args.steps, 10), torch))
+    ms_plain = None
+    if packed:
+        _warm(step_plain, args.warmup, torch, 0)
+        ms_plain = _time_region(step_plain, args.steps, torch)
     logits, ids, wts = moe.moe_route(x, Wg, bias, K, w.renorm)
     meta = moe.moe_permute(ids, None, E)
     h = moe.moe_expert_w13_swiglu_gather(x, meta["perm"], K, meta["offsets"], W13)
@@ -411,23 +441,35 @@ def _layer_bench(w, args, torch, moe, dev, detail):
     yc = moe.moe_unpermute_combine(Yp, meta["inv"], wts, n, K)
     torch.cuda.synchronize()
     counts = meta["counts"].cpu().numpy()
-    # Decode-sized bf16 batches: moe_forward runs GEMM1 straight from the ids (the GEMM places the pairs
+    # Decode-sized bf16 batches: the layer runs GEMM1 straight from the ids (the GEMM places the pairs
     # itself and writes the metadata) in place of moe_permute + the gathered GEMM1.
     try:
         h_ids, meta_ids = moe.moe_expert_w13_swiglu_from_ids(x, ids, W13)
     except moe.MoEError:
         h_ids = meta_ids = None
     R = args.stage_reps
+    if packed:  # the GEMM stages the timed layer runs: over the packed weights
+        g1_call = lambda: moe.moe_expert_w13_swiglu_gather_packed(x, meta["perm"], K, meta["offsets"], W13p, I, h=h)  # noqa: E731
+        g2_call = lambda: moe.moe_expert_w2_packed(h, meta["offsets"], W2p, H, Y_perm=Yp)  # noqa: E731
+        ids_call = lambda: moe.moe_expert_w13_swiglu_from_ids_packed(x, ids, W13p, I, h=h_ids, out=meta_ids)  # noqa: E731
+    else:
+        g1_call = lambda: moe.moe_expert_w13_swiglu_gather(x, meta["perm"], K, meta["offsets"], W13, h=h)  # noqa: E731
+        g2_call = lambda: moe.moe_expert_w2(h, meta["offsets"], W2, Y_perm=Yp)  # noqa: E731
+        ids_call = lambda: moe.moe_expert_w13_swiglu_from_ids(x, ids, W13, h=h_ids, out=meta_ids)  # noqa: E731
     st = {
         "route": _time_region_graph(lambda: moe.moe_route(x, Wg, bias, K, w.renorm, logits=logits, topk_ids=ids, topk_w=wts), R, torch),
         "permute": _time_region_graph(lambda: moe.moe_permute(ids, None, E, out=meta), R, torch),
-        "gemm1_swiglu": _time_region_graph(lambda: moe.moe_expert_w13_swiglu_gather(x, meta["perm"], K, meta["offsets"], W13, h=h), R, torch),
-        "gemm2": _time_region_graph(lambda: moe.moe_expert_w2(h, meta["offsets"], W2, Y_perm=Yp), R, torch),
+        "gemm1_swiglu": _time_region_graph(g1_call, R, torch),
+        "gemm2": _time_region_graph(g2_call, R, torch),
         "combine": _time_region_graph(lambda: moe.moe_unpermute_combine(Yp, meta["inv"], wts, n, K, y=yc), R, torch),
     }
     if meta_ids is not None:
-        st["gemm1_swiglu_from_ids"] = _time_region_graph(
-            lambda: moe.moe_expert_w13_swiglu_from_ids(x, ids, W13, h=h_ids, out=meta_ids), R, torch)
+        st["gemm1_swiglu_from_ids"] = _time_region_graph(ids_call, R, torch)
+    if packed and detail:  # the same GEMMs over the plain weight layout
+        st["alt_gemm1_swiglu_plain_weights"] = _time_region_graph(
+            lambda: moe.moe_expert_w13_swiglu_gather(x, meta["perm"], K, meta["offsets"], W13, h=h), R, torch)
+        st["alt_gemm2_plain_weights"] = _time_region_graph(
+            lambda: moe.moe_expert_w2(h, meta["offsets"], W2, Y_perm=Yp), R, torch)
     nk = n * K
     hit = int((counts > 0).sum())
     flops1 = 2.0 * nk * H * 2 * I
@@ -443,21 +485,26 @@ def _layer_bench(w, args, torch, moe, dev, detail):
         # ids read once, rows gathered once, weights of the hit experts once, h and the metadata written once
         "gemm1_swiglu_from_ids": nk * 4 + nk * H * esz + hit * H * 2 * I * esz + nk * I * esz + nk * 8 + (2 * E + 2) * 4,
     }
+    bytes_["alt_gemm1_swiglu_plain_weights"] = bytes_["gemm1_swiglu"]
+    bytes_["alt_gemm2_plain_weights"] = bytes_["gemm2"]
     g1 = "gemm1_swiglu_from_ids" if meta_ids is not None else "gemm1_swiglu"
     stages = {}
     for k, v in st.items():
         s_ = {"ms": round(v, 5), "GB/s": round(bytes_[k] / (v * 1e-3) / 1e9, 1)}
         s_["frac_hbm"] = round(s_["GB/s"] / PEAK_HBM_GBPS, 4)
-        if k in ("gemm1_swiglu", "gemm1_swiglu_from_ids"):
+        if k in ("gemm1_swiglu", "gemm1_swiglu_from_ids", "alt_gemm1_swiglu_plain_weights"):
             s_["TFLOP/s"] = round(flops1 / (v * 1e-3) / 1e12, 1)
-        if k == "gemm2":
+        if k in ("gemm2", "alt_gemm2_plain_weights"):
             s_["TFLOP/s"] = round(flops2 / (v * 1e-3) / 1e12, 1)
         stages[k] = s_
     gg_ms = st[g1] + st["gemm2"]
     gg = (flops1 + flops2) / (gg_ms * 1e-3) / 1e12
-    g1_kernel = ("gemm_bf16_kernel<GATED=true, GATHER=true, IDS=true> (decode GEMM1 that places the routing ids "
-                 "itself, with fused row gather + SwiGLU epilogue)" if meta_ids is not None else
-                 "gemm_bf16_kernel<GATED=true, GATHER=true> (GEMM1 with fused row gather + SwiGLU epilogue)")
+    over = ", over the packed weights" if packed else ""
+    g1_kernel = (f"gemm_bf16_kernel<GATED=true, GATHER=true, IDS=true{', BPK=true' if packed else ''}> (decode GEMM1 "
+                 f"that places the routing ids itself, with fused row gather + SwiGLU epilogue{over})"
+                 if meta_ids is not None else
+                 f"gemm_bf16_kernel<GATED=true, GATHER=true{', BPK=true' if packed else ''}> (GEMM1 with fused row "
+                 f"gather + SwiGLU epilogue{over})")
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
     if flops1 / bytes_[g1] >= ridge:
         a = round(flops1 / (g1_live_ms * 1e-3) / 1e12, 1)
@@ -470,18 +517,23 @@ def _layer_bench(w, args, torch, moe, dev, detail):
     roof["traffic"] = None
     roof["kernel_ms"] = round(g1_live_ms, 5)
     roof["timing"] = ("mean of HIP events recorded right before and after the GEMM1 launch inside each timed "
-                      "moe_forward call (moe_forward_timed), on the layer's stream"
+                      + ("moe_forward_packed call" if packed else "moe_forward call (moe_forward_timed)")
+                      + ", on the layer's stream"
                       + ("" if fence_free else "; default events (the fence-free flag was refused)"))
     roof["kernel_ms_alone"] = round(st[g1], 5)  # the same launch replayed alone from a HIP graph
     out = {"ms": round(ms, 5), "tokens/s": round(n / (ms * 1e-3), 1), "step_spread": spread,
            "wall_s_timed_region": round(wall, 3),
+           "weights": ("packed once into the GEMMs' tile order before timing (moe_pack_w13 / moe_pack_w2); "
+                       "the layer is moe_forward_packed" if packed else "plain layout; the layer is moe_forward"),
+           "ms_plain_weights": None if ms_plain is None else round(ms_plain, 5),
            "grouped_gemm": {"TFLOP/s": round(gg, 1), "frac_bf16_peak": round(gg / PEAK_BF16_TFLOPS, 4),
                             "GFLOP": round((flops1 + flops2) / 1e9, 1)},
            "forward_stages": (["route", "gemm1_swiglu_from_ids", "gemm2", "combine"] if meta_ids is not None else
                               ["route", "permute", "gemm1_swiglu", "gemm2", "combine"]),
            "stages": stages, "expert_load": _expert_load(counts), "roofline": roof}
     if w.dtype == "bf16" and nk > 64 * E:
-        out["persistent_experiment"] = _persistent_bench(w, args, torch, moe, dev, (x, Wg, W13, W2, bias), ms)
+        out["persistent_experiment"] = _persistent_bench(w, args, torch, moe, dev, (x, Wg, W13, W2, bias), ms,
+                                                         ms_plain)
     if not detail:
         return out
     # The alternative second half (routing weights and un-permutation in GEMM2's
@@ -523,13 +575,16 @@ def _layer_bench(w, args, torch, moe, dev, detail):
     return out
 
 
-def _persistent_bench(w, args, torch, moe, dev, tensors, forward_ms):
+def _persistent_bench(w, args, torch, moe, dev, tensors, forward_ms, plain_ms=None):
     """moe_forward_persistent (GEMM1 + SwiGLU and GEMM2 in one persistent kernel with per-XCD task
-    queues, a warm-up of L1 row tiles and an optional ring pool for h) timed like moe_forward, for two
-    schedules: a deep warm-up without a ring, and a ring of 16 row-tile slots per queue."""
+    queues, a warm-up of L1 row tiles and an optional ring pool for h; plain weight layout) timed like
+    the layer, for two schedules: a deep warm-up without a ring, and a ring of 16 row-tile slots per
+    queue. Compared with the timed layer and with moe_forward on the same plain weights."""
     x, Wg, W13, W2, bias = tensors
     y = torch.empty((w.n, w.H), dtype=x.dtype, device=dev)
     res = {"forward_ms": round(forward_ms, 5)}
+    if plain_ms is not None:
+        res["forward_plain_weights_ms"] = round(plain_ms, 5)
     for warm, pool in ((16, 0), (8, 16)):
         nbytes = moe.moe_forward_persistent_workspace_size(w.n, w.H, w.I, w.E, w.K, pool)
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -544,6 +599,8 @@ def _persistent_bench(w, args, torch, moe, dev, tensors, forward_ms):
         key = f"warm{warm}_pool{pool}"
         res[key] = {"ms": round(pm, 5), "speedup_over_forward": round(forward_ms / pm, 3), "flag": flag,
                     "h_bytes": (w.n * w.K * w.I * 2) if pool == 0 else 8 * pool * 256 * w.I * 2}
+        if plain_ms is not None:
+            res[key]["speedup_over_plain_forward"] = round(plain_ms / pm, 3)
     return res
 
 
@@ -647,6 +704,8 @@ def main():
         "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights, OLMoE layer shapes; no checkpoint)",
         "config": {"workload": args.workload, "n": w.n, "H": w.H, "I": w.I, "E": w.E, "K": w.K,
                    "renorm": bool(w.renorm), "skewed_bias": w.bias is not None},
+        "weights": head["weights"],
+        "ms_per_step_plain_weights": head["ms_plain_weights"],
         "grouped_gemm": head["grouped_gemm"],
         "stages": head["stages"],
         "roofline": roof,
@@ -676,6 +735,9 @@ def _profile_forward(args, torch, moe):
         step = lambda: moe.moe_forward_fp8a(x, Wg, q13, s13, q2, s2, w.K, w.renorm, bias=bias)  # noqa: E731
     elif args.profile_layer == "persistent":
         step = lambda: moe.moe_forward_persistent(x, Wg, W13, W2, w.K, w.renorm, bias=bias)  # noqa: E731
+    elif args.profile_layer == "packed":
+        W13p, W2p = moe.moe_pack_w13(W13), moe.moe_pack_w2(W2)
+        step = lambda: moe.moe_forward_packed(x, Wg, W13p, W2p, w.K, w.renorm, bias=bias)  # noqa: E731
     else:
         step = lambda: moe.moe_forward(x, Wg, W13, W2, w.K, w.renorm, bias=bias)  # noqa: E731
     for _ in range(args.profile_forward):
@@ -992,8 +1054,10 @@ def _bench_fp8(args, workload=None, cpu_leg=True):
         else:
             moe.moe_forward_fp8(x, Wg, q13, s13, q2, s2, K, w.renorm, y=y, ws=ws)
 
-    def step_bf16():
-        moe.moe_forward(x, Wg, W13, W2, K, w.renorm, y=y, ws=ws)
+    W13p, W2p = moe.moe_pack_w13(W13), moe.moe_pack_w2(W2)
+
+    def step_bf16():  # the bf16 layer as the headline runs it (packed weights)
+        moe.moe_forward_packed(x, Wg, W13p, W2p, K, w.renorm, y=y, ws=ws)
 
     _warm(step, args.warmup, torch, args.settle_ms)
     t0 = time.perf_counter()

@@ -303,6 +303,63 @@ moe_status moe_forward_timed(const void* x, const void* W_gate, const float* bia
                              hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Packed expert weights. "大模型系统中的通算融合" §4.4 describes a fused MoE
+ * kernel that takes its weights converted once, ahead of time, into the
+ * kernel's own layout, and §8.5 counts such pre-converted weights among the
+ * ways to keep layout copies off the critical path. moe_pack_w13 and
+ * moe_pack_w2 make that conversion for the bf16 GEMMs here: for each expert
+ * and each 32 rows of K, one 16 KB unit per 256-column output block (the
+ * blocks' units side by side), each column's 32 values contiguous and
+ * swizzled as the GEMM's on-chip tiles want them, so that a GEMM stage copies
+ * whole contiguous units and reads its weight operands like its token
+ * operands. Unit u of block nb of expert e starts at element
+ * ((e * K/32 + u) * NB + nb) * 8192; within a unit, column c's 16-byte chunk q
+ * (its k-values 8q .. 8q+7) sits at element c * 32 + 8 * (q ^ ((c / 2) % 4)).
+ * GEMM1's blocks hold 128 gate columns followed by the matching 128 up
+ * columns. Columns past the matrix (I or H
+ * not a multiple of 128 / 256) are stored as zeros. The values are the
+ * weights' own: moe_forward_packed gives bit for bit what moe_forward gives.
+ *
+ *   moe_packed_w13_bytes / moe_packed_w2_bytes: bytes of the packed form
+ *     (E * ceil(I/128) * 256 * H * 2, E * ceil(H/256) * 256 * I * 2); 0 for
+ *     shapes outside the bf16 GEMMs' range (1 <= E <= 256, H and I positive
+ *     multiples of 64).
+ *   moe_pack_w13: W13 (E, H, 2I) bf16 -> W13p; moe_pack_w2: W2 (E, I, H) bf16
+ *     -> W2p. Both buffers device memory, 16-byte aligned, the caller's; W13p /
+ *     W2p must hold the bytes above and must not overlap the input. One
+ *     launch, stream-ordered. MOE_EINVAL for a bad shape or pointer.
+ * ------------------------------------------------------------------------- */
+size_t moe_packed_w13_bytes(int E, int H, int I);
+size_t moe_packed_w2_bytes(int E, int H, int I);
+moe_status moe_pack_w13(const void* W13, int E, int H, int I, void* W13p, hipStream_t stream);
+moe_status moe_pack_w2(const void* W2, int E, int H, int I, void* W2p, hipStream_t stream);
+
+/* The layer's GEMMs over packed weights, staged as their plain-layout
+ * counterparts (bf16 only; every other argument, the validation and the
+ * results, bit for bit, as moe_expert_w13_swiglu_gather,
+ * moe_expert_w13_swiglu_from_ids and moe_expert_w2 with dt = MOE_BF16). */
+moe_status moe_expert_w13_swiglu_gather_packed(const void* x, const int32_t* perm, int n, int K,
+                                               const int32_t* offsets, const void* W13p, int E, int H, int I,
+                                               void* h, hipStream_t stream);
+moe_status moe_expert_w13_swiglu_from_ids_packed(const void* x, const int32_t* topk_ids, int n, int K,
+                                                 const void* W13p, int E, int H, int I, int ep, void* h,
+                                                 int32_t* counts, int32_t* offsets, int32_t* splits, int32_t* perm,
+                                                 int32_t* inv, hipStream_t stream);
+moe_status moe_expert_w2_packed(const void* h, const int32_t* offsets, int rows, const void* W2p, int E, int H,
+                                int I, void* Y_perm, hipStream_t stream);
+
+/* moe_forward_packed — moe_forward (bf16 only) over packed weights: W13p and
+ * W2p as moe_pack_w13 / moe_pack_w2 write them; every other argument, the
+ * workspace size (moe_forward_workspace_size with MOE_BF16) and the results
+ * as moe_forward's, bit for bit. gemm1_begin / gemm1_end: optional events,
+ * as in moe_forward_timed. */
+moe_status moe_forward_packed(const void* x, const void* W_gate, const float* bias, const void* W13p,
+                              const void* W2p, int n, int H, int I, int E, int K, int renorm, void* y,
+                              float* logits_out, int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out,
+                              void* ws, size_t ws_bytes, hipEvent_t gemm1_begin, hipEvent_t gemm1_end,
+                              hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * moe_forward_noalloc — moe_forward for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc): the same arguments without the workspace, the same

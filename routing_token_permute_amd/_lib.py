@@ -69,6 +69,18 @@ SIGNATURES = {
         _I,
         [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP, _VP],
     ),
+    "moe_expert_w13_swiglu_gather_packed": (_I, [_VP, _VP, _I, _I, _VP, _VP, _I, _I, _I, _VP, _VP]),
+    "moe_expert_w13_swiglu_from_ids_packed": (
+        _I, [_VP, _VP, _I, _I, _VP, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "moe_expert_w2_packed": (_I, [_VP, _VP, _I, _VP, _I, _I, _I, _VP, _VP]),
+    "moe_packed_w13_bytes": (_SZ, [_I, _I, _I]),
+    "moe_packed_w2_bytes": (_SZ, [_I, _I, _I]),
+    "moe_pack_w13": (_I, [_VP, _I, _I, _I, _VP, _VP]),
+    "moe_pack_w2": (_I, [_VP, _I, _I, _I, _VP, _VP]),
+    "moe_forward_packed": (
+        _I,
+        [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP, _VP],
+    ),
     "moe_expert_w13_swiglu_gather_train": (_I, [_VP, _VP, _I, _I, _VP, _VP, _I, _I, _I, _I, _VP, _VP, _VP]),
     "moe_forward_train_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_forward_train": (
@@ -536,6 +548,154 @@ def moe_forward_timed(x, W_gate, W13, W2, K: int, renorm: bool, gemm1_begin, gem
     )
     _check(code, "moe_forward_timed")
     return y
+
+
+def _event_handles(events):
+    handles = []
+    for ev in events:
+        h = ev if (ev is None or isinstance(ev, int)) else ev.cuda_event
+        if ev is not None and not h:
+            raise MoEError("record the event once before passing it (torch creates it on first record)")
+        handles.append(h)
+    return handles
+
+
+@_on_stream
+def moe_pack_w13(W13, stream=None):
+    """W13 (E, H, 2I) bf16 in the GEMMs' packed form: a bf16 tensor of shape
+    (E, H/32, ceil(I/128), 256, 32) (expert, 32-deep unit, column block, column, k
+    as stored: the 16-byte k-chunks of column c sit at slot chunk ^ ((c/2) % 4))."""
+    lib = load_library()
+    E, H, I2 = W13.shape
+    I = I2 // 2  # noqa: E741
+    _need(W13, "W13", (E, H, 2 * I), torch.bfloat16)
+    out = _empty((E, H // 32, -(-I // 128), 256, 32), torch.bfloat16, W13.device)
+    if out.numel() * 2 != lib.moe_packed_w13_bytes(E, H, I):
+        raise MoEError("moe_pack_w13: unsupported shape")
+    _check(lib.moe_pack_w13(_ptr(W13), E, H, I, _ptr(out), _stream(W13.device, stream)), "moe_pack_w13")
+    return out
+
+
+@_on_stream
+def moe_pack_w2(W2, stream=None):
+    """W2 (E, I, H) bf16 in the packed form: (E, I/32, ceil(H/256), 256, 32)."""
+    lib = load_library()
+    E, I, H = W2.shape  # noqa: E741
+    _need(W2, "W2", (E, I, H), torch.bfloat16)
+    out = _empty((E, I // 32, -(-H // 256), 256, 32), torch.bfloat16, W2.device)
+    if out.numel() * 2 != lib.moe_packed_w2_bytes(E, H, I):
+        raise MoEError("moe_pack_w2: unsupported shape")
+    _check(lib.moe_pack_w2(_ptr(W2), E, H, I, _ptr(out), _stream(W2.device, stream)), "moe_pack_w2")
+    return out
+
+
+def _packed_dims(W13p=None, W2p=None):
+    """(E, H or I from the unit count, blocks) of a packed weight tensor."""
+    t = W13p if W13p is not None else W2p
+    if t.dim() != 5 or tuple(t.shape[3:]) != (256, 32) or t.dtype != torch.bfloat16:
+        raise MoEError(f"packed weights must be bf16 of shape (E, K/32, blocks, 256, 32), got {tuple(t.shape)}")
+    return t.shape[0], t.shape[1] * 32, t.shape[2]
+
+
+@_on_stream
+def moe_expert_w13_swiglu_gather_packed(x, perm, K, offsets, W13p, I, h=None, stream=None):  # noqa: E741
+    """moe_expert_w13_swiglu_gather over W13 packed by moe_pack_w13 (bf16); I is the layer's
+    intermediate size (the packed blocks round it up to 128)."""
+    lib = load_library()
+    n, H = x.shape
+    E, Hp, NB = _packed_dims(W13p=W13p)
+    dev = x.device
+    if Hp != H or NB != -(-I // 128):
+        raise MoEError("W13p does not match x and I")
+    _need(x, "x", (n, H), torch.bfloat16)
+    _need(perm, "perm", (n * K,), torch.int32, dev)
+    _need(offsets, "offsets", (E + 1,), torch.int32, dev)
+    h = _empty((n * K, I), torch.bfloat16, dev) if h is None else h
+    _need(h, "h", (n * K, I), torch.bfloat16, dev)
+    code = lib.moe_expert_w13_swiglu_gather_packed(_ptr(x), _ptr(perm), n, K, _ptr(offsets), _ptr(W13p), E, H, I,
+                                                   _ptr(h), _stream(dev, stream))
+    _check(code, "moe_expert_w13_swiglu_gather_packed")
+    return h
+
+
+@_on_stream
+def moe_expert_w13_swiglu_from_ids_packed(x, topk_ids, W13p, I, ep: int = 1, h=None, out=None,  # noqa: E741
+                                          stream=None):
+    """moe_expert_w13_swiglu_from_ids over W13 packed by moe_pack_w13 (bf16). Returns (h, meta)."""
+    lib = load_library()
+    n, H = x.shape
+    K = topk_ids.shape[1]
+    E, Hp, NB = _packed_dims(W13p=W13p)
+    dev = x.device
+    if Hp != H or NB != -(-I // 128):
+        raise MoEError("W13p does not match x and I")
+    _need(x, "x", (n, H), torch.bfloat16)
+    _need(topk_ids, "topk_ids", (n, K), torch.int32, dev)
+    h = _empty((n * K, I), torch.bfloat16, dev) if h is None else h
+    _need(h, "h", (n * K, I), torch.bfloat16, dev)
+    out = dict(out or {})
+    for name, shape in (("counts", (E,)), ("offsets", (E + 1,)), ("splits", (ep,)), ("perm", (n * K,)),
+                        ("inv", (n * K,))):
+        out.setdefault(name, _empty(shape, torch.int32, dev))
+        _need(out[name], name, shape, torch.int32, dev)
+    code = lib.moe_expert_w13_swiglu_from_ids_packed(
+        _ptr(x), _ptr(topk_ids), n, K, _ptr(W13p), E, H, I, ep, _ptr(h), _ptr(out["counts"]), _ptr(out["offsets"]),
+        _ptr(out["splits"]), _ptr(out["perm"]), _ptr(out["inv"]), _stream(dev, stream),
+    )
+    _check(code, "moe_expert_w13_swiglu_from_ids_packed")
+    return h, out
+
+
+@_on_stream
+def moe_expert_w2_packed(h, offsets, W2p, H, Y_perm=None, stream=None):
+    """moe_expert_w2 over W2 packed by moe_pack_w2 (bf16); H is the layer's hidden size."""
+    lib = load_library()
+    rows, I = h.shape  # noqa: E741
+    E, Ip, NB = _packed_dims(W2p=W2p)
+    dev = h.device
+    if Ip != I or NB != -(-H // 256):
+        raise MoEError("W2p does not match h and H")
+    _need(h, "h", (rows, I), torch.bfloat16)
+    _need(offsets, "offsets", (E + 1,), torch.int32, dev)
+    Y_perm = _empty((rows, H), torch.bfloat16, dev) if Y_perm is None else Y_perm
+    _need(Y_perm, "Y_perm", (rows, H), torch.bfloat16, dev)
+    code = lib.moe_expert_w2_packed(_ptr(h), _ptr(offsets), rows, _ptr(W2p), E, H, I, _ptr(Y_perm),
+                                    _stream(dev, stream))
+    _check(code, "moe_expert_w2_packed")
+    return Y_perm
+
+
+@_on_stream
+def moe_forward_packed(x, W_gate, W13p, W2p, K: int, renorm: bool, bias=None, y=None, ws=None, routing_out=False,
+                       gemm1_begin=None, gemm1_end=None, stream=None):
+    """moe_forward (bf16) over weights packed by moe_pack_w13 / moe_pack_w2; the same results bit for
+    bit. Returns y, or (y, logits, topk_ids, topk_w, counts) with routing_out. gemm1_begin / gemm1_end:
+    optional timing events around GEMM1, as in moe_forward_timed."""
+    lib = load_library()
+    n, H = x.shape
+    E = W_gate.shape[1]
+    I = W2p.shape[1] * 32  # noqa: E741
+    dev = x.device
+    _need(x, "x", (n, H), torch.bfloat16)
+    _need(W_gate, "W_gate", (H, E), torch.bfloat16, dev)
+    _need(W13p, "W13p", (E, H // 32, -(-I // 128), 256, 32), torch.bfloat16, dev)
+    _need(W2p, "W2p", (E, I // 32, -(-H // 256), 256, 32), torch.bfloat16, dev)
+    if bias is not None:
+        _need(bias, "bias", (E,), torch.float32, dev)
+    y = _empty((n, H), torch.bfloat16, dev) if y is None else y
+    _need(y, "y", (n, H), torch.bfloat16, dev)
+    ws = _workspace(lib.moe_forward_workspace_size(n, H, I, E, K, MOE_BF16), dev, ws)
+    extra = [None] * 4
+    if routing_out:
+        extra = [_empty((n, E), torch.float32, dev), _empty((n, K), torch.int32, dev),
+                 _empty((n, K), torch.float32, dev), _empty((E,), torch.int32, dev)]
+    handles = _event_handles((gemm1_begin, gemm1_end))
+    code = lib.moe_forward_packed(
+        _ptr(x), _ptr(W_gate), _ptr(bias), _ptr(W13p), _ptr(W2p), n, H, I, E, K, int(bool(renorm)), _ptr(y),
+        *[_ptr(t) for t in extra], _ptr(ws), ws.numel(), handles[0], handles[1], _stream(dev, stream),
+    )
+    _check(code, "moe_forward_packed")
+    return (y, *extra) if routing_out else y
 
 
 def moe_forward_persistent_workspace_size(n, H, I, E, K, pool_row_tiles=0) -> int:  # noqa: E741

@@ -16,6 +16,20 @@ static_assert(BN == 256, "LDS layouts below assume 256-column stages");
 
 constexpr int kMaxStages = 5;
 
+// Packed weights (moe_pack_w13 / moe_pack_w2): the K rows of each expert in
+// units of 32 per 256-column output block. A unit is 256 columns x 32 k
+// (16 KB), each column's 32 k-values contiguous (64 bytes, four 16-byte
+// chunks), chunk q of column c at slot q ^ ((c / 2) % 4): the layout of the
+// A tiles of a 32-deep stage, so that a stage's B part is a copy of whole
+// units and B operands are read with ds_read_b128. Unit u of block nb of
+// expert e starts at element ((e * (Kdim / 32) + u) * NB + nb) * kPackUnit:
+// the NB blocks' units of one k-range sit side by side, so the tiles of one
+// expert that run at the same time read neighbouring units (one block's units
+// laid end to end put those streams exactly 1 MB apart at the OLMoE shape,
+// and GEMM1 ran 11% slower).
+constexpr int kPackUnit = 256 * 32;           // bf16 elements per unit
+constexpr int kPackUnitBytes = kPackUnit * 2;  // 16 KB
+
 // Stage geometry for a BM-row tile advancing BK (32 or 64) along K: A is
 // BM x BK, B is BK x 256. As many stages as fit in 160 KB of LDS, at most
 // CAP (all but one stay in flight while one is multiplied).

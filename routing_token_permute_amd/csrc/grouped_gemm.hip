@@ -80,7 +80,7 @@ constexpr int kSmallRowsPerExpert = 64;  // rows / E at or below this: small til
 // writes the metadata to memory for the kernels that follow, so no separate
 // permute launch runs before this GEMM.
 template <bool GATED, bool GATHER, bool SCATTER, int BM, int BK, int WM, int WN, bool SAVE = false,
-          bool IDS = false>
+          bool IDS = false, bool BPK = false>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                                     const int32_t* __restrict__ perm, int topk,
                                                                     int n_a, const float* __restrict__ wrow,
@@ -172,6 +172,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
           arow = ((unsigned)f < (unsigned)(n_a * topk)) ? f / topk : 0;
         }
         src[j] = A + (size_t)arow * Kdim + c * 8;
+      } else if constexpr (BPK) {
+        // Packed weights: the stage's B part is a straight copy of its BK / 32
+        // units of column block t.nb, 16 regions of 1 KB each (ldb = NB * 256,
+        // so that the k-step advance kt * BK * ldb is BK / 32 unit rows).
+        const int rb = r - A_REG;
+        src[j] = B + ((size_t)t.e * (Kdim / 32) * NB + t.nb + (size_t)(rb >> 4) * NB) * kPackUnit +
+                 (rb & 15) * 512 + lane * 8;
       } else {
         const int k = 2 * (r - A_REG) + (lane >> 5);
         const int c = (lane & 31) ^ b_swz(k);
@@ -225,7 +232,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
       col0 = (nt < NT / 2) ? (wn * (BN / 2 / WN) + nt * 16) : (BN / 2 + wn * (BN / 2 / WN) + (nt - NT / 2) * 16);
     else
       col0 = wn * (BN / WN) + nt * 16;
-    b_col[nt] = b_lane + (((col0 >> 3) ^ bsw) << 4);
+    if constexpr (BPK)  // column col0 + li of the unit, k-chunk g (the A operand's form)
+      b_col[nt] = (col0 + li) * 64 + ((g ^ ((li >> 1) & 3)) << 4);
+    else
+      b_col[nt] = b_lane + (((col0 >> 3) ^ bsw) << 4);
   }
 
   f32x4_t acc[MT][NT];
@@ -245,10 +255,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16
     const lds_char_t* Bs = As + A_BYTES;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const lds_char_t* p = Bs + b_col[nt] + ks * 32 * B_ROW;
-      const bf16x4_t lo = lds_read_tr16(p);
-      const bf16x4_t hi = lds_read_tr16(p + 4 * B_ROW);
-      b[nt] = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      if constexpr (BPK) {
+        b[nt] = __builtin_bit_cast(bf16x8_t, lds_read_b128(Bs + ks * kPackUnitBytes + b_col[nt]));
+      } else {
+        const lds_char_t* p = Bs + b_col[nt] + ks * 32 * B_ROW;
+        const bf16x4_t lo = lds_read_tr16(p);
+        const bf16x4_t hi = lds_read_tr16(p + 4 * B_ROW);
+        b[nt] = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -600,35 +614,41 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 
 namespace {
 
-template <bool GATED, bool GATHER, bool SCATTER, int BM, int BK, int WM, int WN, bool SAVE>
+template <bool GATED, bool GATHER, bool SCATTER, int BM, int BK, int WM, int WN, bool SAVE, bool BPK>
 void launch_cfg(const void* a, const int32_t* perm, int topk, int n_a, const float* wrow, const int32_t* offsets,
                 int E, int rows, int Kdim, const void* B, int ldb, long long bstride, int Nout, int up_col, void* C,
                 int ldc, int NB, void* gu_out, hipStream_t s) {
   const int n_slots = max_row_tiles(rows, E, BM) * NB;
   const int grid = std::min(n_slots, stream_cu_count(s));
-  gemm_bf16_kernel<GATED, GATHER, SCATTER, BM, BK, WM, WN, SAVE><<<grid, 64 * WM * WN, 0, s>>>(
+  gemm_bf16_kernel<GATED, GATHER, SCATTER, BM, BK, WM, WN, SAVE, false, BPK><<<grid, 64 * WM * WN, 0, s>>>(
       (const uint16_t*)a, perm, topk, n_a, wrow, offsets, E, rows, Kdim, (const uint16_t*)B, ldb, bstride, Nout,
       up_col, (uint16_t*)C, ldc, NB, n_slots, (uint16_t*)gu_out, IdsMeta{});
 }
 
-template <bool GATED, bool GATHER, bool SCATTER = false, bool SAVE = false>
+// BPK: B is in the packed form (ldb = 256, bstride unused).
+template <bool GATED, bool GATHER, bool SCATTER = false, bool SAVE = false, bool BPK = false>
 void launch_bf16(const void* a, const int32_t* perm, int topk, int n_a, const int32_t* offsets, int E, int rows,
                  int Kdim, const void* B, int ldb, long long bstride, int Nout, int up_col, void* C, int ldc, int NB,
                  hipStream_t s, const float* wrow = nullptr, void* gu_out = nullptr) {
   if ((long long)rows <= (long long)kSmallRowsPerExpert * E)
-    launch_cfg<GATED, GATHER, SCATTER, kSmallBM, kSmallBK, kSmallWM, kSmallWN, SAVE>(
+    launch_cfg<GATED, GATHER, SCATTER, kSmallBM, kSmallBK, kSmallWM, kSmallWN, SAVE, BPK>(
         a, perm, topk, n_a, wrow, offsets, E, rows, Kdim, B, ldb, bstride, Nout, up_col, C, ldc, NB, gu_out, s);
   else
-    launch_cfg<GATED, GATHER, SCATTER, kBM, GATED ? kBK1 : kBK, kGemmWM, kGemmWN, SAVE>(
+    launch_cfg<GATED, GATHER, SCATTER, kBM, GATED ? kBK1 : kBK, kGemmWM, kGemmWN, SAVE, BPK>(
         a, perm, topk, n_a, wrow, offsets, E, rows, Kdim, B, ldb, bstride, Nout, up_col, C, ldc, NB, gu_out, s);
 }
 
 template <bool GATHER, bool SAVE = false>
 hipError_t w13_impl(const void* a, const int32_t* perm, int topk, int n_a, const int32_t* offsets, int rows,
                     const void* W13, int E, int H, int I, moe_dtype dt, void* h, hipStream_t s,
-                    void* gu_out = nullptr) {
+                    void* gu_out = nullptr, bool packed = false) {
   if (rows == 0) return hipSuccess;
-  if (dt == MOE_BF16) {
+  if (packed && dt != MOE_BF16) return hipErrorInvalidValue;
+  if (packed) {
+    const int NB = ceil_div(I, BN / 2);
+    launch_bf16<true, GATHER, false, SAVE, true>(a, perm, topk, n_a, offsets, E, rows, H, W13, NB * 256, 0, I, I, h,
+                                                 I, NB, s, nullptr, gu_out);
+  } else if (dt == MOE_BF16) {
     launch_bf16<true, GATHER, false, SAVE>(a, perm, topk, n_a, offsets, E, rows, H, W13, 2 * I,
                                            (long long)H * 2 * I, I, I, h, I, ceil_div(I, BN / 2), s, nullptr,
                                            gu_out);
@@ -648,8 +668,9 @@ hipError_t launch_w13_swiglu(const void* x_perm, const int32_t* offsets, int row
 }
 
 hipError_t launch_w13_swiglu_gather(const void* x, const int32_t* perm, int n, int K, const int32_t* offsets,
-                                    const void* W13, int E, int H, int I, moe_dtype dt, void* h, hipStream_t s) {
-  return w13_impl<true>(x, perm, K, n, offsets, n * K, W13, E, H, I, dt, h, s);
+                                    const void* W13, int E, int H, int I, moe_dtype dt, void* h, hipStream_t s,
+                                    bool packed) {
+  return w13_impl<true>(x, perm, K, n, offsets, n * K, W13, E, H, I, dt, h, s, nullptr, packed);
 }
 
 hipError_t launch_w13_swiglu_gather_train(const void* x, const int32_t* perm, int n, int K, const int32_t* offsets,
@@ -665,25 +686,36 @@ bool w13_from_ids_ok(int n, int K, int E, moe_dtype dt) {
 
 hipError_t launch_w13_swiglu_from_ids(const void* x, const int32_t* ids, int n, int K, const void* W13, int E,
                                       int H, int I, int ep, void* h, int32_t* counts, int32_t* offsets,
-                                      int32_t* splits, int32_t* perm, int32_t* inv, hipStream_t s) {
+                                      int32_t* splits, int32_t* perm, int32_t* inv, hipStream_t s, bool packed) {
   if (!w13_from_ids_ok(n, K, E, MOE_BF16) || ep <= 0 || E % ep != 0) return hipErrorInvalidValue;
   int id_bits = 0;
   while ((1 << id_bits) < E) ++id_bits;
   const int NB = ceil_div(I, BN / 2);
   const int n_slots = E * NB;
   const int grid = std::min(n_slots, stream_cu_count(s));
-  gemm_bf16_kernel<true, true, false, kSmallBM, kSmallBK, kSmallWM, kSmallWN, false, true>
-      <<<grid, 64 * kSmallWM * kSmallWN, 0, s>>>((const uint16_t*)x, nullptr, K, n, nullptr, nullptr, E, n * K, H,
-                                                 (const uint16_t*)W13, 2 * I, (long long)H * 2 * I, I, I,
-                                                 (uint16_t*)h, I, NB, n_slots, nullptr,
-                                                 IdsMeta{ids, counts, offsets, splits, perm, inv, ep, id_bits});
+  const IdsMeta im{ids, counts, offsets, splits, perm, inv, ep, id_bits};
+  if (packed)
+    gemm_bf16_kernel<true, true, false, kSmallBM, kSmallBK, kSmallWM, kSmallWN, false, true, true>
+        <<<grid, 64 * kSmallWM * kSmallWN, 0, s>>>((const uint16_t*)x, nullptr, K, n, nullptr, nullptr, E, n * K, H,
+                                                   (const uint16_t*)W13, NB * 256, 0, I, I, (uint16_t*)h, I, NB,
+                                                   n_slots, nullptr, im);
+  else
+    gemm_bf16_kernel<true, true, false, kSmallBM, kSmallBK, kSmallWM, kSmallWN, false, true>
+        <<<grid, 64 * kSmallWM * kSmallWN, 0, s>>>((const uint16_t*)x, nullptr, K, n, nullptr, nullptr, E, n * K, H,
+                                                   (const uint16_t*)W13, 2 * I, (long long)H * 2 * I, I, I,
+                                                   (uint16_t*)h, I, NB, n_slots, nullptr, im);
   return hipGetLastError();
 }
 
 hipError_t launch_w2(const void* h, const int32_t* offsets, int rows, const void* W2, int E, int H, int I,
-                     moe_dtype dt, void* Y_perm, hipStream_t s) {
+                     moe_dtype dt, void* Y_perm, hipStream_t s, bool packed) {
   if (rows == 0) return hipSuccess;
-  if (dt == MOE_BF16) {
+  if (packed && dt != MOE_BF16) return hipErrorInvalidValue;
+  if (packed) {
+    const int NB = ceil_div(H, BN);
+    launch_bf16<false, false, false, false, true>(h, nullptr, 1, rows, offsets, E, rows, I, W2, NB * 256, 0, H, 0,
+                                                  Y_perm, H, NB, s);
+  } else if (dt == MOE_BF16) {
     launch_bf16<false, false>(h, nullptr, 1, rows, offsets, E, rows, I, W2, H, (long long)I * H, H, 0, Y_perm, H,
                               ceil_div(H, BN), s);
   } else {
@@ -708,6 +740,58 @@ hipError_t launch_w2_scatter(const void* h, const int32_t* offsets, int rows, co
                                                            I, (const float*)W2, H, (long long)I * H, H, 0,
                                                            (float*)Y_tok, H, nullptr);
   }
+  return hipGetLastError();
+}
+
+namespace {
+
+// One workgroup per 32-deep unit (expert e, unit u, column block nb); thread c
+// writes column c of the block: its 32 k-values as four 16-byte chunks at
+// their swizzled slots. Gated (half = I > 0): columns 0-127 are the gate
+// columns nb * 128 + c, 128-255 the matching up columns I + nb * 128 + c - 128;
+// otherwise column nb * 256 + c. Columns past the matrix are zero.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __restrict__ W, int Kdim, int Ncols,
+                                                           int NB, int half, uint16_t* __restrict__ out) {
+  const int units = Kdim / 32;
+  const int nb = blockIdx.x % NB;
+  const int eu = blockIdx.x / NB;  // e * units + u
+  const int u = eu % units, e = eu / units;
+  const int c = threadIdx.x;
+  int col;
+  bool ok;
+  if (half > 0) {
+    const int j = nb * 128 + (c & 127);
+    ok = j < half;
+    col = (c < 128) ? j : half + j;
+  } else {
+    col = nb * 256 + c;
+    ok = col < Ncols;
+  }
+  const uint16_t* src = W + (size_t)e * Kdim * Ncols + (size_t)u * 32 * Ncols + (ok ? col : 0);
+  uint16_t* dst = out + (size_t)blockIdx.x * kPackUnit + c * 32;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = ok ? src[(size_t)(8 * q + 2 * i) * Ncols] : 0u;
+      const uint32_t hi = ok ? src[(size_t)(8 * q + 2 * i + 1) * Ncols] : 0u;
+      w[i] = lo | (hi << 16);
+    }
+    *(u32x4_t*)(dst + ((q ^ ((c >> 1) & 3)) << 3)) = u32x4_t{w[0], w[1], w[2], w[3]};
+  }
+}
+
+}  // namespace
+
+size_t packed_weight_bytes(int E, int Kdim, int NB) { return (size_t)E * NB * (Kdim / 32) * kPackUnitBytes; }
+
+hipError_t launch_pack_weights(const void* W, int E, int Kdim, int Ncols, int half, int NB, void* out,
+                               hipStream_t s) {
+  if (E <= 0 || Kdim % 32 != 0 || Kdim <= 0 || NB <= 0) return hipErrorInvalidValue;
+  const long long blocks = (long long)E * NB * (Kdim / 32);
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  pack_weights_kernel<<<(int)blocks, 256, 0, s>>>((const uint16_t*)W, Kdim, Ncols, NB, half, (uint16_t*)out);
   return hipGetLastError();
 }
 

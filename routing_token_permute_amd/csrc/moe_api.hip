@@ -215,7 +215,8 @@ moe_status check_forward(const void* x, const void* W_gate, const float* bias, c
 moe_status forward_enqueue(const void* x, const void* W_gate, const float* bias, const void* W13, const void* W2,
                            int n, int H, int I, int E, int K, int renorm, moe_dtype dt, void* y, float* logits_out,
                            int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, char* base,
-                           hipStream_t stream, hipEvent_t g1_begin = nullptr, hipEvent_t g1_end = nullptr) {
+                           hipStream_t stream, hipEvent_t g1_begin = nullptr, hipEvent_t g1_end = nullptr,
+                           bool packed = false) {
   const ForwardLayout L = forward_layout(n, H, I, E, K, dt);
   float* logits = logits_out ? logits_out : (float*)(base + L.logits);
   int32_t* ids = topk_ids_out ? topk_ids_out : (int32_t*)(base + L.ids);
@@ -233,21 +234,21 @@ moe_status forward_enqueue(const void* x, const void* W_gate, const float* bias,
     // metadata for GEMM2 and the combine (one launch fewer).
     if (g1_begin != nullptr && hipEventRecord(g1_begin, stream) != hipSuccess) return MOE_EHIP;
     e = launch_w13_swiglu_from_ids(x, ids, n, K, W13, E, H, I, 1, base + L.h, counts, offsets, splits, perm, inv,
-                                   stream);
+                                   stream, packed);
   } else {
     // Metadata only: GEMM1 gathers the token rows itself through perm.
     e = launch_permute(ids, nullptr, n, H, E, K, 1, dt, counts, offsets, splits, perm, inv, nullptr,
                        (int32_t*)(base + L.pscratch), stream);
     if (e != hipSuccess) return MOE_EHIP;
     if (g1_begin != nullptr && hipEventRecord(g1_begin, stream) != hipSuccess) return MOE_EHIP;
-    e = launch_w13_swiglu_gather(x, perm, n, K, offsets, W13, E, H, I, dt, base + L.h, stream);
+    e = launch_w13_swiglu_gather(x, perm, n, K, offsets, W13, E, H, I, dt, base + L.h, stream, packed);
   }
   if (e != hipSuccess) return MOE_EHIP;
   if (g1_end != nullptr && hipEventRecord(g1_end, stream) != hipSuccess) return MOE_EHIP;
   // Expert-major GEMM2, then the gathered weighted combine: measured a little
   // faster here than moe_expert_w2_scatter + moe_sum_slots, whose scattered
   // row stores cost GEMM2 more than the contiguous sum saves.
-  e = launch_w2(base + L.h, offsets, n * K, W2, E, H, I, dt, base + L.Y_perm, stream);
+  e = launch_w2(base + L.h, offsets, n * K, W2, E, H, I, dt, base + L.Y_perm, stream, packed);
   if (e != hipSuccess) return MOE_EHIP;
   return from_hip(launch_combine(base + L.Y_perm, inv, w, n, H, K, dt, y, stream));
 }
@@ -430,20 +431,20 @@ moe_status moe_expert_w13_swiglu(const void* x_perm, const int32_t* offsets, int
   return from_hip(launch_w13_swiglu(x_perm, offsets, rows, W13, E, H, I, dt, h, stream));
 }
 
-moe_status moe_expert_w13_swiglu_gather(const void* x, const int32_t* perm, int n, int K, const int32_t* offsets,
-                                        const void* W13, int E, int H, int I, moe_dtype dt, void* h,
-                                        hipStream_t stream) {
+namespace {
+moe_status w13_gather_call(const void* x, const int32_t* perm, int n, int K, const int32_t* offsets,
+                           const void* W13, int E, int H, int I, moe_dtype dt, void* h, hipStream_t stream,
+                           bool packed) {
   if (n < 0 || K < 1 || K > kMaxTopK || (long long)n * K > INT32_MAX) return MOE_EINVAL;
   if ((n > 0 && perm == nullptr) || !word_ok({perm})) return MOE_EINVAL;
   const moe_status st = check_expert_gemm(x, offsets, n * K, W13, E, H, I, dt, h);
   if (st != MOE_OK) return st;
-  return from_hip(launch_w13_swiglu_gather(x, perm, n, K, offsets, W13, E, H, I, dt, h, stream));
+  return from_hip(launch_w13_swiglu_gather(x, perm, n, K, offsets, W13, E, H, I, dt, h, stream, packed));
 }
 
-moe_status moe_expert_w13_swiglu_from_ids(const void* x, const int32_t* topk_ids, int n, int K, const void* W13,
-                                          int E, int H, int I, int ep, moe_dtype dt, void* h, int32_t* counts,
-                                          int32_t* offsets, int32_t* splits, int32_t* perm, int32_t* inv,
-                                          hipStream_t stream) {
+moe_status w13_from_ids_call(const void* x, const int32_t* topk_ids, int n, int K, const void* W13, int E, int H,
+                             int I, int ep, moe_dtype dt, void* h, int32_t* counts, int32_t* offsets,
+                             int32_t* splits, int32_t* perm, int32_t* inv, hipStream_t stream, bool packed) {
   if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
   if (n < 0 || !experts_ok(E, K) || ep < 1 || E % ep != 0 || !hidden_ok(H, dt) || !hidden_ok(I, dt))
     return MOE_EINVAL;
@@ -458,7 +459,36 @@ moe_status moe_expert_w13_swiglu_from_ids(const void* x, const int32_t* topk_ids
     return MOE_EINVAL;
   if (!vec_ok({x, W13, h})) return MOE_EINVAL;
   return from_hip(launch_w13_swiglu_from_ids(x, topk_ids, n, K, W13, E, H, I, ep, h, counts, offsets, splits, perm,
-                                             inv, stream));
+                                             inv, stream, packed));
+}
+}  // namespace
+
+moe_status moe_expert_w13_swiglu_gather(const void* x, const int32_t* perm, int n, int K, const int32_t* offsets,
+                                        const void* W13, int E, int H, int I, moe_dtype dt, void* h,
+                                        hipStream_t stream) {
+  return w13_gather_call(x, perm, n, K, offsets, W13, E, H, I, dt, h, stream, false);
+}
+
+moe_status moe_expert_w13_swiglu_gather_packed(const void* x, const int32_t* perm, int n, int K,
+                                               const int32_t* offsets, const void* W13p, int E, int H, int I,
+                                               void* h, hipStream_t stream) {
+  return w13_gather_call(x, perm, n, K, offsets, W13p, E, H, I, MOE_BF16, h, stream, true);
+}
+
+moe_status moe_expert_w13_swiglu_from_ids(const void* x, const int32_t* topk_ids, int n, int K, const void* W13,
+                                          int E, int H, int I, int ep, moe_dtype dt, void* h, int32_t* counts,
+                                          int32_t* offsets, int32_t* splits, int32_t* perm, int32_t* inv,
+                                          hipStream_t stream) {
+  return w13_from_ids_call(x, topk_ids, n, K, W13, E, H, I, ep, dt, h, counts, offsets, splits, perm, inv, stream,
+                           false);
+}
+
+moe_status moe_expert_w13_swiglu_from_ids_packed(const void* x, const int32_t* topk_ids, int n, int K,
+                                                 const void* W13p, int E, int H, int I, int ep, void* h,
+                                                 int32_t* counts, int32_t* offsets, int32_t* splits, int32_t* perm,
+                                                 int32_t* inv, hipStream_t stream) {
+  return w13_from_ids_call(x, topk_ids, n, K, W13p, E, H, I, ep, MOE_BF16, h, counts, offsets, splits, perm, inv,
+                           stream, true);
 }
 
 moe_status moe_expert_w2(const void* h, const int32_t* offsets, int rows, const void* W2, int E, int H, int I,
@@ -466,6 +496,13 @@ moe_status moe_expert_w2(const void* h, const int32_t* offsets, int rows, const 
   const moe_status st = check_expert_gemm(h, offsets, rows, W2, E, H, I, dt, Y_perm);
   if (st != MOE_OK) return st;
   return from_hip(launch_w2(h, offsets, rows, W2, E, H, I, dt, Y_perm, stream));
+}
+
+moe_status moe_expert_w2_packed(const void* h, const int32_t* offsets, int rows, const void* W2p, int E, int H,
+                                int I, void* Y_perm, hipStream_t stream) {
+  const moe_status st = check_expert_gemm(h, offsets, rows, W2p, E, H, I, MOE_BF16, Y_perm);
+  if (st != MOE_OK) return st;
+  return from_hip(launch_w2(h, offsets, rows, W2p, E, H, I, MOE_BF16, Y_perm, stream, true));
 }
 
 moe_status moe_expert_w2_scatter(const void* h, const int32_t* offsets, int rows, const int32_t* perm,
@@ -521,6 +558,44 @@ moe_status moe_forward_timed(const void* x, const void* W_gate, const float* bia
   if (ws == nullptr || ws_bytes < forward_layout(n, H, I, E, K, dt).total) return MOE_EWORKSPACE;
   return forward_enqueue(x, W_gate, bias, W13, W2, n, H, I, E, K, renorm, dt, y, logits_out, topk_ids_out,
                          topk_w_out, counts_out, (char*)ws, stream, gemm1_begin, gemm1_end);
+}
+
+size_t moe_packed_w13_bytes(int E, int H, int I) {
+  if (E < 1 || E > kMaxExperts || !hidden_ok(H, MOE_BF16) || !hidden_ok(I, MOE_BF16)) return 0;
+  return packed_weight_bytes(E, H, ceil_div(I, 128));
+}
+
+size_t moe_packed_w2_bytes(int E, int H, int I) {
+  if (E < 1 || E > kMaxExperts || !hidden_ok(H, MOE_BF16) || !hidden_ok(I, MOE_BF16)) return 0;
+  return packed_weight_bytes(E, I, ceil_div(H, 256));
+}
+
+moe_status moe_pack_w13(const void* W13, int E, int H, int I, void* W13p, hipStream_t stream) {
+  if (E < 1 || E > kMaxExperts || !hidden_ok(H, MOE_BF16) || !hidden_ok(I, MOE_BF16)) return MOE_EINVAL;
+  if (W13 == nullptr || W13p == nullptr || !vec_ok({W13, W13p})) return MOE_EINVAL;
+  return from_hip(launch_pack_weights(W13, E, H, 2 * I, I, ceil_div(I, 128), W13p, stream));
+}
+
+moe_status moe_pack_w2(const void* W2, int E, int H, int I, void* W2p, hipStream_t stream) {
+  if (E < 1 || E > kMaxExperts || !hidden_ok(H, MOE_BF16) || !hidden_ok(I, MOE_BF16)) return MOE_EINVAL;
+  if (W2 == nullptr || W2p == nullptr || !vec_ok({W2, W2p})) return MOE_EINVAL;
+  return from_hip(launch_pack_weights(W2, E, I, H, 0, ceil_div(H, 256), W2p, stream));
+}
+
+moe_status moe_forward_packed(const void* x, const void* W_gate, const float* bias, const void* W13p,
+                              const void* W2p, int n, int H, int I, int E, int K, int renorm, void* y,
+                              float* logits_out, int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out,
+                              void* ws, size_t ws_bytes, hipEvent_t gemm1_begin, hipEvent_t gemm1_end,
+                              hipStream_t stream) {
+  const moe_status st = check_forward(x, W_gate, bias, W13p, W2p, n, H, I, E, K, MOE_BF16, y, logits_out,
+                                      topk_ids_out, topk_w_out, counts_out);
+  if (st != MOE_OK) return st;
+  if (!vec_ok({ws})) return MOE_EINVAL;
+  if (n == 0)  // no tokens: nothing to compute; the optional counts are all zero
+    return counts_out ? from_hip(launch_fill_zero(counts_out, (size_t)E * 4, stream)) : MOE_OK;
+  if (ws == nullptr || ws_bytes < forward_layout(n, H, I, E, K, MOE_BF16).total) return MOE_EWORKSPACE;
+  return forward_enqueue(x, W_gate, bias, W13p, W2p, n, H, I, E, K, renorm, MOE_BF16, y, logits_out, topk_ids_out,
+                         topk_w_out, counts_out, (char*)ws, stream, gemm1_begin, gemm1_end, true);
 }
 
 moe_status moe_forward(const void* x, const void* W_gate, const float* bias, const void* W13, const void* W2, int n,

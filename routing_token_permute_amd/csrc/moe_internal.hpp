@@ -55,10 +55,23 @@ hipError_t launch_grouped_swiglu(const void* x_perm, const int32_t* offsets, int
 hipError_t launch_w13_swiglu(const void* x_perm, const int32_t* offsets, int rows, const void* W13, int E, int H,
                              int I, moe_dtype dt, void* h, hipStream_t s);
 // GEMM1 reading token rows x[perm[r] / K] directly (no permuted copy of x).
+// packed: the weights are in the packed form of launch_pack_weights (bf16).
 hipError_t launch_w13_swiglu_gather(const void* x, const int32_t* perm, int n, int K, const int32_t* offsets,
-                                    const void* W13, int E, int H, int I, moe_dtype dt, void* h, hipStream_t s);
+                                    const void* W13, int E, int H, int I, moe_dtype dt, void* h, hipStream_t s,
+                                    bool packed = false);
 hipError_t launch_w2(const void* h, const int32_t* offsets, int rows, const void* W2, int E, int H, int I,
-                     moe_dtype dt, void* Y_perm, hipStream_t s);
+                     moe_dtype dt, void* Y_perm, hipStream_t s, bool packed = false);
+
+// bf16 weights of E experts, each Kdim x Ncols row-major, rewritten in the
+// GEMMs' tile order: per expert, per 32 K rows, one 16 KB unit for each of the
+// NB 256-column output blocks (the layout is described where the GEMM tiles
+// are defined). half > 0: W13 with gate columns [0, half) and up columns
+// [half, 2 * half), block nb holding gate columns nb * 128 + [0, 128) and the
+// matching up columns; half == 0: W2, block nb holding columns nb * 256 +
+// [0, 256). Columns past the matrix are zero. Kdim % 32 == 0.
+size_t packed_weight_bytes(int E, int Kdim, int NB);
+hipError_t launch_pack_weights(const void* W, int E, int Kdim, int Ncols, int half, int NB, void* out,
+                               hipStream_t s);
 
 // GEMM2 with the routing weight and the un-permutation in its epilogue:
 // Y_tok[perm[p]] = topk_w[perm[p]] * (h[p] . W2[e(p)]), rows in flat pair order.
@@ -92,7 +105,8 @@ hipError_t launch_fused_ffn(const void* x, const int32_t* perm, int n, int K, co
 bool w13_from_ids_ok(int n, int K, int E, moe_dtype dt);
 hipError_t launch_w13_swiglu_from_ids(const void* x, const int32_t* ids, int n, int K, const void* W13, int E,
                                       int H, int I, int ep, void* h, int32_t* counts, int32_t* offsets,
-                                      int32_t* splits, int32_t* perm, int32_t* inv, hipStream_t s);
+                                      int32_t* splits, int32_t* perm, int32_t* inv, hipStream_t s,
+                                      bool packed = false);
 
 // ---- backward ----
 

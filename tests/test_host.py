@@ -340,3 +340,38 @@ def test_w13_from_ids_fp8_weights_rejects_unserved_shapes(lib):
         bad = list(args)
         bad[i] = v
         assert lib.moe_expert_w13_swiglu_from_ids_fp8(*bad) == code, (i, v)
+
+
+def test_packed_weights_reject_bad_arguments(lib):
+    """Packed sizes follow the documented layout and are 0 outside the bf16 GEMMs' range; the pack calls and
+    moe_forward_packed refuse bad shapes, null and misaligned pointers, and a short workspace, before any
+    HIP call."""
+    s = None
+    assert lib.moe_packed_w13_bytes(64, 2048, 1024) == 64 * 8 * 256 * 2048 * 2
+    assert lib.moe_packed_w2_bytes(64, 2048, 1024) == 64 * 8 * 256 * 1024 * 2
+    assert lib.moe_packed_w13_bytes(3, 128, 192) == 3 * 2 * 256 * 128 * 2  # I = 192: two 128-column blocks
+    assert lib.moe_packed_w2_bytes(3, 320, 64) == 3 * 2 * 256 * 64 * 2  # H = 320: two 256-column blocks
+    for E, H, I in ((0, 64, 64), (257, 64, 64), (8, 96, 64), (8, 64, 32), (8, 0, 64)):
+        assert lib.moe_packed_w13_bytes(E, H, I) == 0 and lib.moe_packed_w2_bytes(E, H, I) == 0
+        assert lib.moe_pack_w13(P, E, H, I, P, s) == EINVAL
+        assert lib.moe_pack_w2(P, E, H, I, P, s) == EINVAL
+    assert lib.moe_pack_w13(None, 8, 64, 64, P, s) == EINVAL
+    assert lib.moe_pack_w2(P, 8, 64, 64, None, s) == EINVAL
+    M8 = ctypes.c_void_p(0x10008)  # 8-byte aligned only
+    assert lib.moe_pack_w13(M8, 8, 64, 64, P, s) == EINVAL
+    assert lib.moe_pack_w2(P, 8, 64, 64, M8, s) == EINVAL
+    ws = lib.moe_forward_workspace_size(16, 64, 64, 8, 2, 1)
+    args = [P, P, None, P, P, 16, 64, 64, 8, 2, 0, P, None, None, None, None, P, ws, None, None, s]
+    bad = list(args)
+    bad[17] = ws - 1
+    assert lib.moe_forward_packed(*bad) == EWS
+    for i in (0, 1, 3, 4, 11):  # x, W_gate, W13p, W2p, y
+        bad = list(args)
+        bad[i] = None
+        assert lib.moe_forward_packed(*bad) == EINVAL
+    bad = list(args)
+    bad[3] = M8
+    assert lib.moe_forward_packed(*bad) == EINVAL
+    bad = list(args)
+    bad[9] = 9  # K > E
+    assert lib.moe_forward_packed(*bad) == EINVAL
