@@ -79,6 +79,11 @@ constexpr int kSmallRowsPerExpert = 64;  // rows / E at or below this: small til
 // t % NB, and the slots of experts without rows are skipped. Workgroup 0 also
 // writes the metadata to memory for the kernels that follow, so no separate
 // permute launch runs before this GEMM.
+// BPK: B is the packed form of the weights (per expert and 32 K rows, one
+// 16 KB unit per 256-column block, each column's 32 values contiguous with the
+// A tiles' swizzle; ldb = NB * 256). A stage's B part is then a copy of whole
+// units, and B operands are read with ds_read_b128 like A operands; the
+// arithmetic, and so every output bit, is that of the plain layout.
 template <bool GATED, bool GATHER, bool SCATTER, int BM, int BK, int WM, int WN, bool SAVE = false,
           bool IDS = false, bool BPK = false>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
@@ -625,7 +630,7 @@ void launch_cfg(const void* a, const int32_t* perm, int topk, int n_a, const flo
       up_col, (uint16_t*)C, ldc, NB, n_slots, (uint16_t*)gu_out, IdsMeta{});
 }
 
-// BPK: B is in the packed form (ldb = 256, bstride unused).
+// BPK: B is in the packed form (ldb = NB * 256, bstride unused).
 template <bool GATED, bool GATHER, bool SCATTER = false, bool SAVE = false, bool BPK = false>
 void launch_bf16(const void* a, const int32_t* perm, int topk, int n_a, const int32_t* offsets, int E, int rows,
                  int Kdim, const void* B, int ldb, long long bstride, int Nout, int up_col, void* C, int ldc, int NB,
