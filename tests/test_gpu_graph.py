@@ -36,6 +36,31 @@ def _replays(graph, outs, expected, eager_work):
             assert torch.equal(_bits(o), _bits(expected[name])), f"replay {r}: {name} differs from the eager call"
 
 
+@pytest.mark.parametrize("name", ["decode_bf16", "olmoe_bf16"])
+def test_packed_forward_graph_replays_match_eager(dev, name):
+    """moe_forward_packed (GEMM1 from the ids at decode, the gathered GEMM1 at the OLMoE shape) in a graph."""
+    w = make_config(name)
+    t = layer_tensors(w, dev)
+    W13p, W2p = moe.moe_pack_w13(t["W13"]), moe.moe_pack_w2(t["W2"])
+    y_eager = moe.moe_forward_packed(t["x"], t["W_gate"], W13p, W2p, w.K, w.renorm)
+    ws = torch.empty(moe.moe_forward_workspace_size(w.n, w.H, w.I, w.E, w.K, t["x"].dtype), dtype=torch.uint8,
+                     device=dev)
+    y = torch.empty_like(y_eager)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream(dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(s):
+        moe.moe_forward_packed(t["x"], t["W_gate"], W13p, W2p, w.K, w.renorm, y=y, ws=ws)  # warm-up on s
+    torch.cuda.current_stream(dev).wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        moe.moe_forward_packed(t["x"], t["W_gate"], W13p, W2p, w.K, w.renorm, y=y, ws=ws)
+    junk = torch.empty_like(y_eager)
+    _replays(g, {"y": y}, {"y": y_eager},
+             lambda: moe.moe_forward_packed(t["x"], t["W_gate"], W13p, W2p, w.K, w.renorm, y=junk))
+
+
 @pytest.mark.parametrize("name", ["decode_bf16", "tiny_f32"])
 def test_forward_graph_replays_match_eager(dev, name):
     w = make_config(name)
