@@ -69,6 +69,13 @@ ROUTE_CASES = [
     (33, 68, 5, 3, "f32", False, None),
     (65536, 256, 64, 8, "bf16", False, None),  # 4096 workgroups
     (20000, 512, 128, 8, "bf16", True, None),  # 128 experts: 8 expert tiles, 4 waves over H
+    # at most 256 tokens and E = 8 * 2^k: one workgroup per token
+    (32, 2048, 64, 8, "bf16", False, None),    # the decode batch
+    (17, 64, 8, 2, "bf16", True, None),        # E = 8: 256 rows per step, more than H
+    (200, 192, 32, 4, "bf16", False, None),
+    (256, 512, 128, 4, "bf16", True, "zipf"),  # -inf experts
+    (100, 128, 256, 64, "bf16", False, None),
+    (257, 256, 64, 8, "bf16", False, None),    # one token more: the batched router
 ]
 
 
