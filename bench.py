@@ -88,7 +88,7 @@ def _source_hash():
 
 
 def _kernel_label(name):
-    if "route_bf16_kernel" in name or "route_f32_kernel" in name:
+    if "route_bf16_kernel" in name or "route_f32_kernel" in name or "route_bf16_rows_kernel" in name:
         return "route"
     for k in ("permute_single_kernel", "permute_count_kernel", "permute_place_kernel", "gather_rows_kernel",
               "sum_slots_kernel"):
@@ -111,7 +111,7 @@ def _kernel_label(name):
                 + f"_bm{bm}")
     for k, lab in (("quantize_rows_kernel", "quantize_rows_fp8"), ("dispatch_fp8_kernel", "dispatch_fp8"),
                    ("quantize_fp8_kernel", "quantize_weights_fp8"), ("fused_ffn_kernel", "fused_ffn"),
-                   ("fill_zero_kernel", "fill_zero")):
+                   ("fill_zero_kernel", "fill_zero"), ("pack_weights_kernel", "pack_weights")):
         if k in name:
             return lab
     if "FillFunctor" in name:
