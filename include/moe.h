@@ -116,8 +116,10 @@ moe_status moe_device_info(int* compute_units, int* sclk_khz, int* mem_clk_khz, 
  *           the fp32 logits (-0.0 counts as +0.0).
  *   topk_w  (n, K) fp32 out: softmax probability of each selected expert
  *           (max-subtracted, fp32), renormalised if asked.
- * The router product accumulates in fp32 (bf16: MFMA). NaN logits are not
- * supported (the selection is then unspecified, still in bounds).
+ * The router product accumulates in fp32 (bf16: MFMA; for at most 256 tokens
+ * and E a power of two times 8, one workgroup per token with fp32 FMA, the
+ * partial sums added in a fixed order). NaN logits are not supported (the
+ * selection is then unspecified, still in bounds).
  * ------------------------------------------------------------------------- */
 moe_status moe_route(const void* x, const void* W_gate, const float* bias, int n, int H, int E, int K,
                      int renorm, moe_dtype dt, float* logits, int32_t* topk_ids, float* topk_w,
