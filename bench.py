@@ -533,7 +533,7 @@ def _layer_bench(w, args, torch, moe, dev, detail):
            "stages": stages, "expert_load": _expert_load(counts), "roofline": roof}
     if w.dtype == "bf16" and nk > 64 * E:
         out["persistent_experiment"] = _persistent_bench(w, args, torch, moe, dev, (x, Wg, W13, W2, bias), ms,
-                                                         ms_plain)
+                                                         ms_plain, (W13p, W2p) if packed else None)
     if not detail:
         return out
     # The alternative second half (routing weights and un-permutation in GEMM2's
@@ -575,14 +575,15 @@ def _layer_bench(w, args, torch, moe, dev, detail):
     return out
 
 
-def _persistent_bench(w, args, torch, moe, dev, tensors, forward_ms, plain_ms=None):
-    """moe_forward_persistent (GEMM1 + SwiGLU and GEMM2 in one persistent kernel with per-XCD task
-    queues, a warm-up of L1 row tiles and an optional ring pool for h; plain weight layout) timed like
-    the layer, for two schedules: a deep warm-up without a ring, and a ring of 16 row-tile slots per
-    queue. Compared with the timed layer and with moe_forward on the same plain weights."""
+def _persistent_bench(w, args, torch, moe, dev, tensors, forward_ms, plain_ms=None, packed=None):
+    """The persistent single kernel (GEMM1 + SwiGLU and GEMM2 with per-XCD task queues, a warm-up of L1
+    row tiles and an optional ring pool for h) timed like the layer, for two schedules: a deep warm-up
+    without a ring, and a ring of 16 row-tile slots per queue; over the packed weights when given
+    (moe_forward_persistent_packed), else the plain ones. Compared with the timed layer and with
+    moe_forward on the plain weights."""
     x, Wg, W13, W2, bias = tensors
     y = torch.empty((w.n, w.H), dtype=x.dtype, device=dev)
-    res = {"forward_ms": round(forward_ms, 5)}
+    res = {"forward_ms": round(forward_ms, 5), "weights": "packed" if packed is not None else "plain"}
     if plain_ms is not None:
         res["forward_plain_weights_ms"] = round(plain_ms, 5)
     for warm, pool in ((16, 0), (8, 16)):
@@ -590,8 +591,12 @@ def _persistent_bench(w, args, torch, moe, dev, tensors, forward_ms, plain_ms=No
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
 
         def step():
-            moe.moe_forward_persistent(x, Wg, W13, W2, w.K, w.renorm, bias=bias, warmup_row_tiles=warm,
-                                       pool_row_tiles=pool, y=y, ws=ws)
+            if packed is not None:
+                moe.moe_forward_persistent_packed(x, Wg, packed[0], packed[1], w.K, w.renorm, bias=bias,
+                                                  warmup_row_tiles=warm, pool_row_tiles=pool, y=y, ws=ws)
+            else:
+                moe.moe_forward_persistent(x, Wg, W13, W2, w.K, w.renorm, bias=bias, warmup_row_tiles=warm,
+                                           pool_row_tiles=pool, y=y, ws=ws)
 
         _warm(step, args.warmup, torch, args.settle_ms)
         pm = _time_region(step, args.steps, torch)

@@ -410,6 +410,15 @@ moe_status moe_forward_persistent(const void* x, const void* W_gate, const float
                                   int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, void* ws,
                                   size_t ws_bytes, hipStream_t stream);
 
+/* moe_forward_persistent_packed — moe_forward_persistent over weights packed
+ * by moe_pack_w13 / moe_pack_w2 (bf16); the same workspace, schedule
+ * arguments and results, bit for bit (and bit for bit moe_forward_packed's). */
+moe_status moe_forward_persistent_packed(const void* x, const void* W_gate, const float* bias, const void* W13p,
+                                         const void* W2p, int n, int H, int I, int E, int K, int renorm,
+                                         int warmup_row_tiles, int pool_row_tiles, void* y, float* logits_out,
+                                         int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, void* ws,
+                                         size_t ws_bytes, hipStream_t stream);
+
 /* ===========================================================================
  * Backward (training) pass of the same layer.
  *

@@ -73,6 +73,8 @@ SIGNATURES = {
     "moe_expert_w13_swiglu_from_ids_packed": (
         _I, [_VP, _VP, _I, _I, _VP, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "moe_expert_w2_packed": (_I, [_VP, _VP, _I, _VP, _I, _I, _I, _VP, _VP]),
+    "moe_forward_persistent_packed": (
+        _I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "moe_packed_w13_bytes": (_SZ, [_I, _I, _I]),
     "moe_packed_w2_bytes": (_SZ, [_I, _I, _I]),
     "moe_pack_w13": (_I, [_VP, _I, _I, _I, _VP, _VP]),
@@ -732,6 +734,38 @@ def moe_forward_persistent(x, W_gate, W13, W2, K: int, renorm: bool, bias=None, 
         _stream(dev, stream),
     )
     _check(code, "moe_forward_persistent")
+    return (y, *extra) if routing_out else y
+
+
+@_on_stream
+def moe_forward_persistent_packed(x, W_gate, W13p, W2p, K: int, renorm: bool, bias=None, warmup_row_tiles=16,
+                                  pool_row_tiles=0, y=None, ws=None, routing_out=False, stream=None):
+    """moe_forward_persistent over weights packed by moe_pack_w13 / moe_pack_w2 (bf16); the same results
+    bit for bit. Returns y, or (y, logits, topk_ids, topk_w, counts) with routing_out."""
+    lib = load_library()
+    n, H = x.shape
+    E = W_gate.shape[1]
+    I = W2p.shape[1] * 32  # noqa: E741
+    dev = x.device
+    _need(x, "x", (n, H), torch.bfloat16)
+    _need(W_gate, "W_gate", (H, E), torch.bfloat16, dev)
+    _need(W13p, "W13p", (E, H // 32, -(-I // 128), 256, 32), torch.bfloat16, dev)
+    _need(W2p, "W2p", (E, I // 32, -(-H // 256), 256, 32), torch.bfloat16, dev)
+    if bias is not None:
+        _need(bias, "bias", (E,), torch.float32, dev)
+    y = _empty((n, H), torch.bfloat16, dev) if y is None else y
+    _need(y, "y", (n, H), torch.bfloat16, dev)
+    ws = _workspace(lib.moe_forward_persistent_workspace_size(n, H, I, E, K, pool_row_tiles), dev, ws)
+    extra = [None] * 4
+    if routing_out:
+        extra = [_empty((n, E), torch.float32, dev), _empty((n, K), torch.int32, dev),
+                 _empty((n, K), torch.float32, dev), _empty((E,), torch.int32, dev)]
+    code = lib.moe_forward_persistent_packed(
+        _ptr(x), _ptr(W_gate), _ptr(bias), _ptr(W13p), _ptr(W2p), n, H, I, E, K, int(bool(renorm)),
+        int(warmup_row_tiles), int(pool_row_tiles), _ptr(y), *[_ptr(t) for t in extra], _ptr(ws), ws.numel(),
+        _stream(dev, stream),
+    )
+    _check(code, "moe_forward_persistent_packed")
     return (y, *extra) if routing_out else y
 
 

@@ -132,6 +132,10 @@ __device__ bool wait_at_least(int* c, int target) {
   return false;
 }
 
+// BPK: W13 and W2 in the packed form (per expert and 32 K rows, one 16 KB unit
+// per 256-column block; see the grouped GEMM): a stage's B part is one unit,
+// read with ds_read_b128; the arithmetic and its order are unchanged.
+template <bool BPK>
 __global__ __launch_bounds__(64 * kFWM * kFWN, 1) void fused_ffn_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ perm, int topk, int n_a,
     const int32_t* __restrict__ offsets, int E, int rows, const uint16_t* __restrict__ W13,
@@ -194,7 +198,8 @@ __global__ __launch_bounds__(64 * kFWM * kFWN, 1) void fused_ffn_kernel(
   auto set_sources = [&](const FTask& t, const Tile& tt) {
     const int mrows = tt.r1 - tt.r0;
     const bool l1 = t.kind == 1;
-    ldb = l1 ? 2 * I : H;
+    const int nbl = l1 ? (I + BN / 2 - 1) / (BN / 2) : (H + BN - 1) / BN;  // column blocks of the task's weights
+    ldb = BPK ? nbl * 256 : (l1 ? 2 * I : H);
     nk = (l1 ? H : I) / BK;
     const uint16_t* hb = l1 ? nullptr : h_rows(t, tt);
 #pragma unroll
@@ -212,6 +217,11 @@ __global__ __launch_bounds__(64 * kFWM * kFWN, 1) void fused_ffn_kernel(
         } else {
           src[j] = hb + (size_t)lr * I + c * 8;
         }
+      } else if constexpr (BPK) {  // one 16 KB unit: a straight copy
+        const int rb = r - A_REG;
+        const uint16_t* wb = l1 ? W13 + (size_t)tt.e * (H / 32) * nbl * kPackUnit
+                                : W2 + (size_t)tt.e * (I / 32) * nbl * kPackUnit;
+        src[j] = wb + (size_t)t.nb * kPackUnit + rb * 512 + lane * 8;
       } else {
         const int k = 2 * (r - A_REG) + (lane >> 5);
         const int c = (lane & 31) ^ b_swz(k);
@@ -256,7 +266,7 @@ __global__ __launch_bounds__(64 * kFWM * kFWN, 1) void fused_ffn_kernel(
       const int col0 = gated ? ((nt < NT / 2) ? (wn * (BN / 2 / WN) + nt * 16)
                                               : (BN / 2 + wn * (BN / 2 / WN) + (nt - NT / 2) * 16))
                              : wn * (BN / WN) + nt * 16;
-      b_col[nt] = b_lane + (((col0 >> 3) ^ bsw) << 4);
+      b_col[nt] = BPK ? (col0 + li) * 64 + ((g ^ ((li >> 1) & 3)) << 4) : b_lane + (((col0 >> 3) ^ bsw) << 4);
     }
   };
 
@@ -271,10 +281,14 @@ __global__ __launch_bounds__(64 * kFWM * kFWN, 1) void fused_ffn_kernel(
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const lds_char_t* p = Bs + b_col[nt] + ks * 32 * B_ROW;
-        const bf16x4_t lo = lds_read_tr16(p);
-        const bf16x4_t hi = lds_read_tr16(p + 4 * B_ROW);
-        b[ks][nt] = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if constexpr (BPK) {
+          b[ks][nt] = __builtin_bit_cast(bf16x8_t, lds_read_b128(Bs + ks * kPackUnitBytes + b_col[nt]));
+        } else {
+          const lds_char_t* p = Bs + b_col[nt] + ks * 32 * B_ROW;
+          const bf16x4_t lo = lds_read_tr16(p);
+          const bf16x4_t hi = lds_read_tr16(p + 4 * B_ROW);
+          b[ks][nt] = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -511,7 +525,7 @@ size_t fused_ffn_h_bytes(int rows, int E, int I, int pool) {
 
 hipError_t launch_fused_ffn(const void* x, const int32_t* perm, int n, int K, const int32_t* offsets, const void* W13,
                             const void* W2, int E, int H, int I, int warm, int pool, void* hbuf, void* Y_perm,
-                            int* counters, hipStream_t s) {
+                            int* counters, hipStream_t s, bool packed) {
   const int rows = n * K;
   if (rows == 0) return hipSuccess;
   const int Mmax = fused_ffn_max_row_tiles(rows, E);
@@ -519,9 +533,10 @@ hipError_t launch_fused_ffn(const void* x, const int32_t* perm, int n, int K, co
   if (e != hipSuccess) return e;
   const long long tasks = (long long)Mmax * (ceil_div(I, BN / 2) + ceil_div(H, BN));
   const int grid = (int)std::min<long long>(tasks, stream_cu_count(s));
-  fused_ffn_kernel<<<grid, 64 * kFWM * kFWN, 0, s>>>((const uint16_t*)x, perm, K, n, offsets, E, rows,
-                                                     (const uint16_t*)W13, (const uint16_t*)W2, H, I,
-                                                     (uint16_t*)hbuf, pool, (uint16_t*)Y_perm, counters, Mmax, warm);
+  auto kern = packed ? fused_ffn_kernel<true> : fused_ffn_kernel<false>;
+  kern<<<grid, 64 * kFWM * kFWN, 0, s>>>((const uint16_t*)x, perm, K, n, offsets, E, rows, (const uint16_t*)W13,
+                                         (const uint16_t*)W2, H, I, (uint16_t*)hbuf, pool, (uint16_t*)Y_perm,
+                                         counters, Mmax, warm);
   return hipGetLastError();
 }
 

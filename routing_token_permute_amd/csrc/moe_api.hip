@@ -612,11 +612,11 @@ size_t moe_forward_persistent_workspace_size(int n, int H, int I, int E, int K, 
   return persistent_layout(n, H, I, E, K, pool_row_tiles).total;
 }
 
-moe_status moe_forward_persistent(const void* x, const void* W_gate, const float* bias, const void* W13,
-                                  const void* W2, int n, int H, int I, int E, int K, int renorm, moe_dtype dt,
-                                  int warmup_row_tiles, int pool_row_tiles, void* y, float* logits_out,
-                                  int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, void* ws,
-                                  size_t ws_bytes, hipStream_t stream) {
+namespace {
+moe_status persistent_call(const void* x, const void* W_gate, const float* bias, const void* W13, const void* W2,
+                           int n, int H, int I, int E, int K, int renorm, moe_dtype dt, int warmup_row_tiles,
+                           int pool_row_tiles, void* y, float* logits_out, int32_t* topk_ids_out, float* topk_w_out,
+                           int32_t* counts_out, void* ws, size_t ws_bytes, hipStream_t stream, bool packed) {
   const moe_status st = check_forward(x, W_gate, bias, W13, W2, n, H, I, E, K, dt, y, logits_out, topk_ids_out,
                                       topk_w_out, counts_out);
   if (st != MOE_OK) return st;
@@ -647,9 +647,29 @@ moe_status moe_forward_persistent(const void* x, const void* W_gate, const float
                        nullptr, (int32_t*)(base + L.pscratch), stream);
   if (e == hipSuccess)
     e = launch_fused_ffn(x, perm, n, K, offsets, W13, W2, E, H, I, warmup_row_tiles, pool_row_tiles, base + L.h,
-                         base + L.Y_perm, (int*)(base + L.counters), stream);
+                         base + L.Y_perm, (int*)(base + L.counters), stream, packed);
   if (e == hipSuccess) e = launch_combine(base + L.Y_perm, inv, w, n, H, K, dt, y, stream);
   return from_hip(e);
+}
+}  // namespace
+
+moe_status moe_forward_persistent(const void* x, const void* W_gate, const float* bias, const void* W13,
+                                  const void* W2, int n, int H, int I, int E, int K, int renorm, moe_dtype dt,
+                                  int warmup_row_tiles, int pool_row_tiles, void* y, float* logits_out,
+                                  int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  return persistent_call(x, W_gate, bias, W13, W2, n, H, I, E, K, renorm, dt, warmup_row_tiles, pool_row_tiles, y,
+                         logits_out, topk_ids_out, topk_w_out, counts_out, ws, ws_bytes, stream, false);
+}
+
+moe_status moe_forward_persistent_packed(const void* x, const void* W_gate, const float* bias, const void* W13p,
+                                         const void* W2p, int n, int H, int I, int E, int K, int renorm,
+                                         int warmup_row_tiles, int pool_row_tiles, void* y, float* logits_out,
+                                         int32_t* topk_ids_out, float* topk_w_out, int32_t* counts_out, void* ws,
+                                         size_t ws_bytes, hipStream_t stream) {
+  return persistent_call(x, W_gate, bias, W13p, W2p, n, H, I, E, K, renorm, MOE_BF16, warmup_row_tiles,
+                         pool_row_tiles, y, logits_out, topk_ids_out, topk_w_out, counts_out, ws, ws_bytes, stream,
+                         true);
 }
 
 size_t moe_forward_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }

@@ -96,7 +96,8 @@ size_t fused_ffn_counter_bytes(int rows, int E);
 size_t fused_ffn_h_bytes(int rows, int E, int I, int pool);
 hipError_t launch_fused_ffn(const void* x, const int32_t* perm, int n, int K, const int32_t* offsets, const void* W13,
                             const void* W2, int E, int H, int I, int warm, int pool, void* hbuf, void* Y_perm,
-                            int* counters, hipStream_t s);
+                            int* counters, hipStream_t s,
+                            bool packed = false);
 
 // Decode-sized GEMM1 (bf16, n <= 32 tokens, n * K <= 1024 pairs, E <= 256):
 // the GEMM places the routing ids itself (the placement moe_permute makes) and

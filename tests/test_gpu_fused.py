@@ -59,6 +59,27 @@ def test_persistent_matches_forward_bitwise(dev, name, warm, pool):
     print(f"[persistent {name} warm={warm} pool={pool}] bitwise equal to moe_forward", flush=True)
 
 
+@pytest.mark.parametrize("name,warm,pool", [("olmoe_bf16", 4, 0), ("olmoe_skewed_bf16", 4, 8), ("ragged", 3, 4),
+                                            ("decode_bf16", 4, 5)])
+def test_persistent_packed_matches_forward_bitwise(dev, name, warm, pool):
+    """The persistent kernel over packed weights: bit for bit moe_forward (and so moe_forward_packed)."""
+    w = _layer(name)
+    t = layer_tensors(w, dev)
+    ref = moe.moe_forward(t["x"], t["W_gate"], t["W13"], t["W2"], w.K, w.renorm, bias=t["bias"], routing_out=True)
+    W13p, W2p = moe.moe_pack_w13(t["W13"]), moe.moe_pack_w2(t["W2"])
+    lib = moe.load_library()
+    nbytes = lib.moe_forward_persistent_workspace_size(w.n, w.H, w.I, w.E, w.K, pool)
+    ws = torch.full((nbytes,), 0x5A, dtype=torch.uint8, device=dev)
+    got = moe.moe_forward_persistent_packed(t["x"], t["W_gate"], W13p, W2p, w.K, w.renorm, bias=t["bias"],
+                                            warmup_row_tiles=warm, pool_row_tiles=pool, ws=ws, routing_out=True)
+    torch.cuda.synchronize()
+    assert int(ws[nbytes - 4:].view(torch.int32).item()) == 0, "a bounded wait of the persistent scheduler ran out"
+    for what, a, b in zip(("y", "logits", "topk_ids", "topk_w", "counts"), ref, got):
+        a = a.view(torch.int16) if a.dtype == torch.bfloat16 else a
+        b = b.view(torch.int16) if b.dtype == torch.bfloat16 else b
+        assert torch.equal(a, b), f"{name} warm={warm} pool={pool}: {what} differs from moe_forward"
+
+
 def test_persistent_against_oracle(dev):
     w = make_layer(600, 256, 128, 8, 2, dtype="bf16", seed=23)
     t = layer_tensors(w, dev)
