@@ -296,6 +296,13 @@ def test_persistent_forward_rejects_bad_arguments(lib):
     bad = list(args)
     bad[20] = ws - 1
     assert lib.moe_forward_persistent(*bad) == EWS
+    # the packed form: the same checks (no dtype argument: bf16)
+    pargs = [P, P, None, P, P, 16, 64, 64, 8, 2, 0, 4, 0, P, None, None, None, None, P, ws, s]
+    for i, v, code in ((11, 0, EINVAL), (12, 4, EINVAL), (19, ws - 1, EWS), (3, None, EINVAL),
+                       (4, ctypes.c_void_p(0x10008), EINVAL)):
+        bad = list(pargs)
+        bad[i] = v
+        assert lib.moe_forward_persistent_packed(*bad) == code, i
 
 
 def test_w13_from_ids_rejects_unserved_shapes(lib):
