@@ -349,6 +349,10 @@ moe_status moe_expert_w13_swiglu_from_ids_packed(const void* x, const int32_t* t
                                                  int32_t* inv, hipStream_t stream);
 moe_status moe_expert_w2_packed(const void* h, const int32_t* offsets, int rows, const void* W2p, int E, int H,
                                 int I, void* Y_perm, hipStream_t stream);
+/* moe_expert_w2_scatter over packed W2 (bf16; as moe_expert_w2_scatter otherwise, bit for bit). */
+moe_status moe_expert_w2_scatter_packed(const void* h, const int32_t* offsets, int rows, const int32_t* perm,
+                                        const float* topk_w, const void* W2p, int E, int H, int I, void* Y_tok,
+                                        hipStream_t stream);
 
 /* moe_forward_packed — moe_forward (bf16 only) over packed weights: W13p and
  * W2p as moe_pack_w13 / moe_pack_w2 write them; every other argument, the

@@ -73,6 +73,7 @@ SIGNATURES = {
     "moe_expert_w13_swiglu_from_ids_packed": (
         _I, [_VP, _VP, _I, _I, _VP, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "moe_expert_w2_packed": (_I, [_VP, _VP, _I, _VP, _I, _I, _I, _VP, _VP]),
+    "moe_expert_w2_scatter_packed": (_I, [_VP, _VP, _I, _VP, _VP, _VP, _I, _I, _I, _VP, _VP]),
     "moe_forward_persistent_packed": (
         _I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "moe_packed_w13_bytes": (_SZ, [_I, _I, _I]),
@@ -665,6 +666,28 @@ def moe_expert_w2_packed(h, offsets, W2p, H, Y_perm=None, stream=None):
                                     _stream(dev, stream))
     _check(code, "moe_expert_w2_packed")
     return Y_perm
+
+
+@_on_stream
+def moe_expert_w2_scatter_packed(h, offsets, perm, topk_w, W2p, H, Y_tok=None, stream=None):
+    """moe_expert_w2_scatter over W2 packed by moe_pack_w2 (bf16); H is the layer's hidden size."""
+    lib = load_library()
+    rows, I = h.shape  # noqa: E741
+    E, Ip, NB = _packed_dims(W2p=W2p)
+    dev = h.device
+    if Ip != I or NB != -(-H // 256):
+        raise MoEError("W2p does not match h and H")
+    _need(h, "h", (rows, I), torch.bfloat16)
+    _need(offsets, "offsets", (E + 1,), torch.int32, dev)
+    _need(perm, "perm", (rows,), torch.int32, dev)
+    if topk_w.numel() != rows or topk_w.dtype != torch.float32 or not topk_w.is_contiguous() or topk_w.device != dev:
+        raise MoEError(f"topk_w: expected {rows} contiguous fp32 values on {dev}")
+    Y_tok = _empty((rows, H), torch.bfloat16, dev) if Y_tok is None else Y_tok
+    _need(Y_tok, "Y_tok", (rows, H), torch.bfloat16, dev)
+    code = lib.moe_expert_w2_scatter_packed(_ptr(h), _ptr(offsets), rows, _ptr(perm), _ptr(topk_w), _ptr(W2p), E, H,
+                                            I, _ptr(Y_tok), _stream(dev, stream))
+    _check(code, "moe_expert_w2_scatter_packed")
+    return Y_tok
 
 
 @_on_stream

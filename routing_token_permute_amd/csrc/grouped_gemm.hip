@@ -734,9 +734,14 @@ hipError_t launch_w2(const void* h, const int32_t* offsets, int rows, const void
 
 hipError_t launch_w2_scatter(const void* h, const int32_t* offsets, int rows, const int32_t* perm,
                              const float* topk_w, const void* W2, int E, int H, int I, moe_dtype dt, void* Y_tok,
-                             hipStream_t s) {
+                             hipStream_t s, bool packed) {
   if (rows == 0) return hipSuccess;
-  if (dt == MOE_BF16) {
+  if (packed && dt != MOE_BF16) return hipErrorInvalidValue;
+  if (packed) {
+    const int NB = ceil_div(H, BN);
+    launch_bf16<false, false, true, false, true>(h, perm, 1, rows, offsets, E, rows, I, W2, NB * 256, 0, H, 0, Y_tok,
+                                                 H, NB, s, topk_w);
+  } else if (dt == MOE_BF16) {
     launch_bf16<false, false, true>(h, perm, 1, rows, offsets, E, rows, I, W2, H, (long long)I * H, H, 0, Y_tok, H,
                                     ceil_div(H, BN), s, topk_w);
   } else {

@@ -515,6 +515,16 @@ moe_status moe_expert_w2_scatter(const void* h, const int32_t* offsets, int rows
   return from_hip(launch_w2_scatter(h, offsets, rows, perm, topk_w, W2, E, H, I, dt, Y_tok, stream));
 }
 
+moe_status moe_expert_w2_scatter_packed(const void* h, const int32_t* offsets, int rows, const int32_t* perm,
+                                        const float* topk_w, const void* W2p, int E, int H, int I, void* Y_tok,
+                                        hipStream_t stream) {
+  const moe_status st = check_expert_gemm(h, offsets, rows, W2p, E, H, I, MOE_BF16, Y_tok);
+  if (st != MOE_OK) return st;
+  if (rows > 0 && (perm == nullptr || topk_w == nullptr)) return MOE_EINVAL;
+  if (!word_ok({perm, topk_w})) return MOE_EINVAL;
+  return from_hip(launch_w2_scatter(h, offsets, rows, perm, topk_w, W2p, E, H, I, MOE_BF16, Y_tok, stream, true));
+}
+
 moe_status moe_sum_slots(const void* Y_tok, int n, int H, int K, moe_dtype dt, void* y, hipStream_t stream) {
   if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
   if (n < 0 || K < 1 || K > kMaxTopK || !hidden_ok(H, dt)) return MOE_EINVAL;

@@ -77,7 +77,8 @@ hipError_t launch_pack_weights(const void* W, int E, int Kdim, int Ncols, int ha
 // Y_tok[perm[p]] = topk_w[perm[p]] * (h[p] . W2[e(p)]), rows in flat pair order.
 hipError_t launch_w2_scatter(const void* h, const int32_t* offsets, int rows, const int32_t* perm,
                              const float* topk_w, const void* W2, int E, int H, int I, moe_dtype dt, void* Y_tok,
-                             hipStream_t s);
+                             hipStream_t s,
+                             bool packed = false);
 // y[i] = sum_k Y_tok[i*K + k] in slot order (fp32 accumulation).
 hipError_t launch_sum_slots(const void* Y_tok, int n, int H, int K, moe_dtype dt, void* y, hipStream_t s);
 hipError_t launch_combine(const void* Y_perm, const int32_t* inv, const float* topk_w, int n, int H, int K,

@@ -96,20 +96,27 @@ def permute_meta(mb: MicroBatch, E_local: int, stream) -> None:
     _lib.moe_permute(mb.eid, None, E_local, out=meta, ws=mb.ws_perm, stream=stream)
 
 
-def experts_fused(mb: MicroBatch, W13: torch.Tensor, W2: torch.Tensor, stream) -> None:
+def experts_fused(mb: MicroBatch, W13: torch.Tensor, W2: torch.Tensor, stream, packed=None) -> None:
     """GEMM1 + SwiGLU reading the received rows through perm, then GEMM2 storing
-    each row at its arrival position."""
+    each row at its arrival position. `packed`: (W13p, W2p) as moe_pack_w13 /
+    moe_pack_w2 write them, used in place of W13 and W2 (the same results)."""
     perm, offsets = mb.meta["perm"], mb.meta["offsets"]
+    if packed is not None:
+        I = mb.h.shape[1]  # noqa: E741
+        _lib.moe_expert_w13_swiglu_gather_packed(mb.x, perm, 1, offsets, packed[0], I, h=mb.h, stream=stream)
+        _lib.moe_expert_w2_scatter_packed(mb.h, offsets, perm, mb.ones, packed[1], mb.x.shape[1], Y_tok=mb.out_fused,
+                                          stream=stream)
+        return
     _lib.moe_expert_w13_swiglu_gather(mb.x, perm, 1, offsets, W13, h=mb.h, stream=stream)
     _lib.moe_expert_w2_scatter(mb.h, offsets, perm, mb.ones, W2, Y_tok=mb.out_fused, stream=stream)
 
 
-def run_fused(a: MicroBatch, b: MicroBatch, W13, W2, E_local: int, stream) -> None:
+def run_fused(a: MicroBatch, b: MicroBatch, W13, W2, E_local: int, stream, packed=None) -> None:
     """Both micro-batches on one stream with the permute and unpermute folded
-    into the GEMMs; outputs in out_fused."""
+    into the GEMMs; outputs in out_fused. `packed`: optional (W13p, W2p)."""
     for mb in (a, b):
         permute_meta(mb, E_local, stream)
-        experts_fused(mb, W13, W2, stream)
+        experts_fused(mb, W13, W2, stream, packed)
 
 
 def run_serial(a: MicroBatch, b: MicroBatch, W13, W2, E_local: int, stream) -> None:

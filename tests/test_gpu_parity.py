@@ -575,7 +575,8 @@ def test_ep_share_two_streams_match_serial(dev):
 
 def test_ep_share_fused_matches_serial(dev):
     """The fused schedule (metadata-only permute, gather-fused GEMM1, GEMM2 storing rows at their arrival
-    positions with unit weights) gives bitwise the serial schedule's outputs, twice in a row."""
+    positions with unit weights) gives bitwise the serial schedule's outputs, twice in a row, on the plain and
+    on the packed weights."""
     from routing_token_permute_amd import ep_share as eps
 
     ep = make_config("ep_share_bf16")
@@ -586,10 +587,11 @@ def test_ep_share_fused_matches_serial(dev):
            for m in ep.micro_batches]
     s0 = torch.cuda.current_stream(dev)
     eps.run_serial(mbs[0], mbs[1], t13, t2, ep.E_local, s0)
-    for _ in range(2):
+    packed = (moe.moe_pack_w13(t13), moe.moe_pack_w2(t2))
+    for pk in (None, packed, None, packed):  # plain and packed weights, each twice
         for mb in mbs:
             mb.out_fused.zero_()
-        eps.run_fused(mbs[0], mbs[1], t13, t2, ep.E_local, s0)
+        eps.run_fused(mbs[0], mbs[1], t13, t2, ep.E_local, s0, packed=pk)
         torch.cuda.synchronize()
         for mb in mbs:
             assert torch.equal(mb.out.view(torch.int16), mb.out_fused.view(torch.int16))
