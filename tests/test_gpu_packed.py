@@ -113,6 +113,7 @@ def test_forward_packed_matches_forward(dev, name):
     (700, 320, 128, 16, 4, False),  # H = 320: five 64-deep GEMM1 k-steps, GEMM2's second block ragged
     (1, 64, 64, 8, 2, False),
     (2000, 64, 64, 64, 8, True),    # 32-row and 256-row tiles side by side
+    (256, 7168, 2048, 8, 2, False),  # wide: 224 K-units per expert for GEMM1, 28 column blocks for GEMM2
 ])
 def test_forward_packed_ragged_shapes(dev, n, H, I, E, K, skewed):  # noqa: E741
     w = make_layer(n, H, I, E, K, seed=n + H + I + E, bias=zipf_bias(E) if skewed else None)
