@@ -54,9 +54,11 @@ def _parse():
                    help="olmoe_bf16: leave out the other configurations (tiny, skewed, decode, EP share)")
     p.add_argument("--profile-forward", type=int, default=0, metavar="N",
                    help="only run N moe_forward calls of the workload (for rocprofv3 counter passes)")
-    p.add_argument("--profile-layer", choices=["packed", "bf16", "fp8a", "persistent"], default="packed",
+    p.add_argument("--profile-layer", choices=["packed", "bf16", "fp8a", "persistent", "persistent_packed"],
+                   default="packed",
                    help="with --profile-forward: moe_forward_packed (bf16, the weights packed once first), "
-                        "moe_forward (bf16), moe_forward_fp8a or moe_forward_persistent")
+                        "moe_forward (bf16), moe_forward_fp8a, moe_forward_persistent or "
+                        "moe_forward_persistent_packed")
     p.add_argument("--summarize-counters", nargs="+", metavar="DIR",
                    help="turn rocprofv3 --pmc csv directories into the per-kernel counter summary printed on stdout")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle wall time for the CPU baseline")
@@ -740,6 +742,9 @@ def _profile_forward(args, torch, moe):
         step = lambda: moe.moe_forward_fp8a(x, Wg, q13, s13, q2, s2, w.K, w.renorm, bias=bias)  # noqa: E731
     elif args.profile_layer == "persistent":
         step = lambda: moe.moe_forward_persistent(x, Wg, W13, W2, w.K, w.renorm, bias=bias)  # noqa: E731
+    elif args.profile_layer == "persistent_packed":
+        W13p, W2p = moe.moe_pack_w13(W13), moe.moe_pack_w2(W2)
+        step = lambda: moe.moe_forward_persistent_packed(x, Wg, W13p, W2p, w.K, w.renorm, bias=bias)  # noqa: E731
     elif args.profile_layer == "packed":
         W13p, W2p = moe.moe_pack_w13(W13), moe.moe_pack_w2(W2)
         step = lambda: moe.moe_forward_packed(x, Wg, W13p, W2p, w.K, w.renorm, bias=bias)  # noqa: E731
