@@ -768,56 +768,6 @@ moe_status moe_forward_fp8a(const void* x, const void* W_gate, const float* bias
                             int renorm, moe_dtype dt, void* y, float* logits_out, int32_t* topk_ids_out,
                             float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* ---------------------------------------------------------------------------
- * Packed FP8 weight codes: the conversion "大模型系统中的通算融合" §4.4 and
- * §8.5 describe (weights rearranged once, ahead of time, into the fused
- * kernel's layout), for the FP8 x FP8 GEMMs above. For each expert and each
- * 128 K codes, one 32 KB unit per 256-column output block (the blocks' units
- * side by side): unit u of block nb of expert e starts at byte
- * ((e * K/128 + u) * NB + nb) * 32768, and within it column c's 16-byte chunk
- * q (its codes 16q .. 16q+15) sits at byte c * 128 + 16 * (q ^ ((c / 2) % 8)).
- * GEMM1's blocks hold 128 gate columns followed by the matching 128 up
- * columns (NB = ceil(I / 128)); GEMM2's 256 output columns (NB =
- * ceil(H / 256)). Columns past the matrix are stored as code 0. The scales
- * (s13, s2) stay as moe_quantize_fp8 writes them.
- *
- *   moe_packed_fp8_w13_bytes / moe_packed_fp8_w2_bytes: bytes of the packed
- *     form (E * ceil(I/128) * 256 * H, E * ceil(H/256) * 256 * I); 0 outside
- *     the FP8 GEMMs' range (1 <= E <= 256, H and I positive multiples of 64,
- *     the packed K dimension a multiple of 128: H for W13, I for W2).
- *   moe_pack_fp8_w13: W13q (E, 2I, H) uint8 -> W13qp; moe_pack_fp8_w2: W2q
- *     (E, H, I) uint8 -> W2qp (both codes as moe_quantize_fp8 writes them).
- *     Device memory, 16-byte aligned, the caller's; the output must hold the
- *     bytes above and must not overlap the input. One launch, stream-ordered.
- *     MOE_EINVAL for a bad shape or pointer.
- *
- * moe_expert_w13_swiglu_gather_fp8a_packed, moe_expert_w13_swiglu_from_ids_fp8a_packed,
- * moe_expert_w2_fp8a_packed and moe_forward_fp8a_packed take the packed codes
- * in place of W13q / W2q; every other argument, the validation, the workspace
- * and the results are those of the unpacked entry, bit for bit.
- * ------------------------------------------------------------------------- */
-size_t moe_packed_fp8_w13_bytes(int E, int H, int I);
-size_t moe_packed_fp8_w2_bytes(int E, int H, int I);
-moe_status moe_pack_fp8_w13(const uint8_t* W13q, int E, int H, int I, uint8_t* W13qp, hipStream_t stream);
-moe_status moe_pack_fp8_w2(const uint8_t* W2q, int E, int H, int I, uint8_t* W2qp, hipStream_t stream);
-moe_status moe_expert_w13_swiglu_gather_fp8a_packed(const uint8_t* codes_tok, const float* s_tok,
-                                                    const int32_t* perm, int n, int K, const int32_t* offsets,
-                                                    const uint8_t* W13qp, const float* s13, int E, int H, int I,
-                                                    void* h, hipStream_t stream);
-moe_status moe_expert_w13_swiglu_from_ids_fp8a_packed(const uint8_t* codes_tok, const float* s_tok,
-                                                      const int32_t* topk_ids, int n, int K, const uint8_t* W13qp,
-                                                      const float* s13, int E, int H, int I, int ep, void* h,
-                                                      int32_t* counts, int32_t* offsets, int32_t* splits,
-                                                      int32_t* perm, int32_t* inv, hipStream_t stream);
-moe_status moe_expert_w2_fp8a_packed(const uint8_t* h_q, const float* h_scale, const int32_t* offsets_padded,
-                                     int rows_max, const uint8_t* W2qp, const float* s2, int E, int H, int I,
-                                     void* Y_perm, hipStream_t stream);
-moe_status moe_forward_fp8a_packed(const void* x, const void* W_gate, const float* bias, const uint8_t* W13qp,
-                                   const float* s13, const uint8_t* W2qp, const float* s2, int n, int H, int I, int E,
-                                   int K, int renorm, moe_dtype dt, void* y, float* logits_out, int32_t* topk_ids_out,
-                                   float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
-                                   hipStream_t stream);
-
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

@@ -120,18 +120,6 @@ SIGNATURES = {
         _I,
         [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
     ),
-    "moe_forward_fp8a_packed": (
-        _I,
-        [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
-    ),
-    "moe_packed_fp8_w13_bytes": (_SZ, [_I, _I, _I]),
-    "moe_packed_fp8_w2_bytes": (_SZ, [_I, _I, _I]),
-    "moe_pack_fp8_w13": (_I, [_VP, _I, _I, _I, _VP, _VP]),
-    "moe_pack_fp8_w2": (_I, [_VP, _I, _I, _I, _VP, _VP]),
-    "moe_expert_w2_fp8a_packed": (_I, [_VP, _VP, _VP, _I, _VP, _VP, _I, _I, _I, _VP, _VP]),
-    "moe_expert_w13_swiglu_gather_fp8a_packed": (_I, [_VP, _VP, _VP, _I, _I, _VP, _VP, _VP, _I, _I, _I, _VP, _VP]),
-    "moe_expert_w13_swiglu_from_ids_fp8a_packed": (_I, [_VP, _VP, _VP, _I, _I, _VP, _VP, _I, _I, _I, _I, _VP, _VP,
-                                                        _VP, _VP, _VP, _VP, _VP]),
     "moe_backward_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "moe_backward": (
         _I,
@@ -1268,50 +1256,8 @@ def moe_expert_w13_swiglu_fp8a(x_q, x_scale, offsets_padded, W13q, s13, h=None, 
     return h
 
 
-def _need_fp8_codes(Wq, name, E, N, Kdim, half, packed, dev):
-    """Plain FP8 codes (E, N, Kdim), or their packed form (E, Kdim/128, blocks, 256, 128) uint8."""
-    if not packed:
-        _need(Wq, name, (E, N, Kdim), torch.uint8, dev)
-        return
-    NB = -(-half // 128) if half else -(-N // 256)
-    _need(Wq, name, (E, Kdim // 128, NB, 256, 128), torch.uint8, dev)
-    if Kdim % 128:
-        raise MoEError(f"{name}: packed codes need K a multiple of 128, got {Kdim}")
-
-
-def _pack_fp8(Wq, E, Kdim, N, half, fn, what, stream):
-    lib = load_library()
-    NB = -(-half // 128) if half else -(-N // 256)
-    out = _empty((E, Kdim // 128, NB, 256, 128), torch.uint8, Wq.device)
-    H, I = (Kdim, half) if half else (N, Kdim)  # noqa: E741
-    nbytes = (lib.moe_packed_fp8_w13_bytes if half else lib.moe_packed_fp8_w2_bytes)(E, H, I)
-    if nbytes == 0 or out.numel() != nbytes:
-        raise MoEError(f"{what}: unsupported shape")
-    _check(fn(_ptr(Wq), E, H, I, _ptr(out), _stream(Wq.device, stream)), what)
-    return out
-
-
 @_on_stream
-def moe_pack_fp8_w13(W13q, stream=None):
-    """FP8 W13 codes (E, 2I, H) uint8 (moe_quantize_fp8 of W13) in the FP8 GEMMs' packed form: (E, H/128,
-    ceil(I/128), 256, 128) uint8 (expert, 128-deep unit, column block, column, code as stored: the 16-byte
-    chunks of column c sit at slot chunk ^ ((c/2) % 8)). The scales are used as they are."""
-    E, I2, H = W13q.shape
-    _need(W13q, "W13q", (E, I2, H), torch.uint8)
-    return _pack_fp8(W13q, E, H, I2, I2 // 2, load_library().moe_pack_fp8_w13, "moe_pack_fp8_w13", stream)
-
-
-@_on_stream
-def moe_pack_fp8_w2(W2q, stream=None):
-    """FP8 W2 codes (E, H, I) uint8 in the packed form: (E, I/128, ceil(H/256), 256, 128) uint8."""
-    E, H, I = W2q.shape  # noqa: E741
-    _need(W2q, "W2q", (E, H, I), torch.uint8)
-    return _pack_fp8(W2q, E, I, H, 0, load_library().moe_pack_fp8_w2, "moe_pack_fp8_w2", stream)
-
-
-@_on_stream
-def moe_expert_w13_swiglu_gather_fp8a(codes_tok, s_tok, perm, K: int, offsets, W13q, s13, h=None, stream=None,
-                                      _packed=False):
+def moe_expert_w13_swiglu_gather_fp8a(codes_tok, s_tok, perm, K: int, offsets, W13q, s13, h=None, stream=None):
     """GEMM1 + SwiGLU on FP8 activations read in place: row r of the expert-major order is token perm[r] // K
     of the per-token codes (n, H) and scales (n,). Returns h (n*K, I) bf16."""
     lib = load_library()
@@ -1323,20 +1269,13 @@ def moe_expert_w13_swiglu_gather_fp8a(codes_tok, s_tok, perm, K: int, offsets, W
     _need(s_tok, "s_tok", (n,), torch.float32, dev)
     _need(perm, "perm", (n * K,), torch.int32, dev)
     _need(offsets, "offsets", (E + 1,), torch.int32, dev)
-    _need_fp8_codes(W13q, "W13q", E, 2 * I, H, I, _packed, dev)
+    _need(W13q, "W13q", (E, 2 * I, H), torch.uint8, dev)
     h = _empty((n * K, I), torch.bfloat16, dev) if h is None else h
     _need(h, "h", (n * K, I), torch.bfloat16, dev)
-    name = "moe_expert_w13_swiglu_gather_fp8a" + ("_packed" if _packed else "")
-    _check(getattr(lib, name)(_ptr(codes_tok), _ptr(s_tok), _ptr(perm), n, K, _ptr(offsets), _ptr(W13q), _ptr(s13),
-                              E, H, I, _ptr(h), _stream(dev, stream)), name)
+    _check(lib.moe_expert_w13_swiglu_gather_fp8a(_ptr(codes_tok), _ptr(s_tok), _ptr(perm), n, K, _ptr(offsets),
+                                                 _ptr(W13q), _ptr(s13), E, H, I, _ptr(h), _stream(dev, stream)),
+           "moe_expert_w13_swiglu_gather_fp8a")
     return h
-
-
-def moe_expert_w13_swiglu_gather_fp8a_packed(codes_tok, s_tok, perm, K: int, offsets, W13qp, s13, h=None,
-                                             stream=None):
-    """moe_expert_w13_swiglu_gather_fp8a over codes packed by moe_pack_fp8_w13 (the same h bit for bit)."""
-    return moe_expert_w13_swiglu_gather_fp8a(codes_tok, s_tok, perm, K, offsets, W13qp, s13, h=h, stream=stream,
-                                             _packed=True)
 
 
 @_on_stream
@@ -1370,19 +1309,19 @@ def moe_expert_w13_swiglu_from_ids_fp8(x, topk_ids, W13q, s13, ep: int = 1, h=No
 
 @_on_stream
 def moe_expert_w13_swiglu_from_ids_fp8a(codes_tok, s_tok, topk_ids, W13q, s13, ep: int = 1, h=None, out=None,
-                                        stream=None, _packed=False):
+                                        stream=None):
     """The FP8 x FP8 GEMM1 of a decode-sized batch straight from the routing ids: h (n*K, I) bf16 and the
     moe_permute metadata dict (counts, offsets, splits, perm, inv) from one launch. Returns (h, meta)."""
     lib = load_library()
     n, H = codes_tok.shape
     K = topk_ids.shape[1]
-    E, I2 = s13.shape
+    E, I2, _ = W13q.shape
     I = I2 // 2  # noqa: E741
     dev = codes_tok.device
     _need(codes_tok, "codes_tok", (n, H), torch.uint8)
     _need(s_tok, "s_tok", (n,), torch.float32, dev)
     _need(topk_ids, "topk_ids", (n, K), torch.int32, dev)
-    _need_fp8_codes(W13q, "W13q", E, 2 * I, H, I, _packed, dev)
+    _need(W13q, "W13q", (E, 2 * I, H), torch.uint8, dev)
     _need(s13, "s13", (E, 2 * I), torch.float32, dev)
     h = _empty((n * K, I), torch.bfloat16, dev) if h is None else h
     _need(h, "h", (n * K, I), torch.bfloat16, dev)
@@ -1391,25 +1330,17 @@ def moe_expert_w13_swiglu_from_ids_fp8a(codes_tok, s_tok, topk_ids, W13q, s13, e
                         ("inv", (n * K,))):
         out.setdefault(name, _empty(shape, torch.int32, dev))
         _need(out[name], name, shape, torch.int32, dev)
-    name = "moe_expert_w13_swiglu_from_ids_fp8a" + ("_packed" if _packed else "")
-    code = getattr(lib, name)(
+    code = lib.moe_expert_w13_swiglu_from_ids_fp8a(
         _ptr(codes_tok), _ptr(s_tok), _ptr(topk_ids), n, K, _ptr(W13q), _ptr(s13), E, H, I, ep, _ptr(h),
         _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["splits"]), _ptr(out["perm"]), _ptr(out["inv"]),
         _stream(dev, stream),
     )
-    _check(code, name)
+    _check(code, "moe_expert_w13_swiglu_from_ids_fp8a")
     return h, out
 
 
-def moe_expert_w13_swiglu_from_ids_fp8a_packed(codes_tok, s_tok, topk_ids, W13qp, s13, ep: int = 1, h=None,
-                                               out=None, stream=None):
-    """moe_expert_w13_swiglu_from_ids_fp8a over codes packed by moe_pack_fp8_w13 (the same results bit for bit)."""
-    return moe_expert_w13_swiglu_from_ids_fp8a(codes_tok, s_tok, topk_ids, W13qp, s13, ep=ep, h=h, out=out,
-                                               stream=stream, _packed=True)
-
-
 @_on_stream
-def moe_expert_w2_fp8a(h_q, h_scale, offsets_padded, W2q, s2, Y_perm=None, stream=None, _packed=False):
+def moe_expert_w2_fp8a(h_q, h_scale, offsets_padded, W2q, s2, Y_perm=None, stream=None):
     """GEMM2 with FP8 activations over the padded receive buffer: Y_perm (rows_max, H) bf16 from h quantized
     per row (h_q (rows_max, I) uint8, h_scale (rows_max,) fp32) and the FP8 W2 codes/scales."""
     lib = load_library()
@@ -1419,18 +1350,12 @@ def moe_expert_w2_fp8a(h_q, h_scale, offsets_padded, W2q, s2, Y_perm=None, strea
     _need(h_q, "h_q", (R, I), torch.uint8)
     _need(h_scale, "h_scale", (R,), torch.float32, dev)
     _need(offsets_padded, "offsets_padded", (E + 1,), torch.int32, dev)
-    _need_fp8_codes(W2q, "W2q", E, H, I, 0, _packed, dev)
+    _need(W2q, "W2q", (E, H, I), torch.uint8, dev)
     Y_perm = _empty((R, H), torch.bfloat16, dev) if Y_perm is None else Y_perm
     _need(Y_perm, "Y_perm", (R, H), torch.bfloat16, dev)
-    name = "moe_expert_w2_fp8a" + ("_packed" if _packed else "")
-    _check(getattr(lib, name)(_ptr(h_q), _ptr(h_scale), _ptr(offsets_padded), R, _ptr(W2q), _ptr(s2), E, H, I,
-                              _ptr(Y_perm), _stream(dev, stream)), name)
+    _check(lib.moe_expert_w2_fp8a(_ptr(h_q), _ptr(h_scale), _ptr(offsets_padded), R, _ptr(W2q), _ptr(s2), E, H, I,
+                                  _ptr(Y_perm), _stream(dev, stream)), "moe_expert_w2_fp8a")
     return Y_perm
-
-
-def moe_expert_w2_fp8a_packed(h_q, h_scale, offsets_padded, W2qp, s2, Y_perm=None, stream=None):
-    """moe_expert_w2_fp8a over codes packed by moe_pack_fp8_w2 (the same Y_perm bit for bit)."""
-    return moe_expert_w2_fp8a(h_q, h_scale, offsets_padded, W2qp, s2, Y_perm=Y_perm, stream=stream, _packed=True)
 
 
 def moe_forward_fp8a_workspace_size(n, H, I, E, K) -> int:  # noqa: E741
@@ -1439,18 +1364,18 @@ def moe_forward_fp8a_workspace_size(n, H, I, E, K) -> int:  # noqa: E741
 
 @_on_stream
 def moe_forward_fp8a(x, W_gate, W13q, s13, W2q, s2, K: int, renorm: bool, bias=None, y=None, ws=None,
-                     routing_out=False, stream=None, _packed=False):
+                     routing_out=False, stream=None):
     """The layer with FP8 activations and FP8 weights. Returns y, or (y, logits, topk_ids, topk_w, counts)."""
     lib = load_library()
     n, H = x.shape
     E = W_gate.shape[1]
-    I = s13.shape[1] // 2  # noqa: E741
+    I = W13q.shape[1] // 2  # noqa: E741
     dev = x.device
     _need(x, "x", (n, H), torch.bfloat16)
     _need(W_gate, "W_gate", (H, E), torch.bfloat16, dev)
-    _need_fp8_codes(W13q, "W13q", E, 2 * I, H, I, _packed, dev)
+    _need(W13q, "W13q", (E, 2 * I, H), torch.uint8, dev)
     _need(s13, "s13", (E, 2 * I), torch.float32, dev)
-    _need_fp8_codes(W2q, "W2q", E, H, I, 0, _packed, dev)
+    _need(W2q, "W2q", (E, H, I), torch.uint8, dev)
     _need(s2, "s2", (E, H), torch.float32, dev)
     if bias is not None:
         _need(bias, "bias", (E,), torch.float32, dev)
@@ -1461,19 +1386,10 @@ def moe_forward_fp8a(x, W_gate, W13q, s13, W2q, s2, K: int, renorm: bool, bias=N
     if routing_out:
         extra = [_empty((n, E), torch.float32, dev), _empty((n, K), torch.int32, dev),
                  _empty((n, K), torch.float32, dev), _empty((E,), torch.int32, dev)]
-    name = "moe_forward_fp8a" + ("_packed" if _packed else "")
-    code = getattr(lib, name)(
+    code = lib.moe_forward_fp8a(
         _ptr(x), _ptr(W_gate), _ptr(bias), _ptr(W13q), _ptr(s13), _ptr(W2q), _ptr(s2), n, H, I, E, K,
         int(bool(renorm)), MOE_BF16, _ptr(y), *[_ptr(t) for t in extra], _ptr(ws), ws.numel(), _stream(dev, stream),
     )
-    _check(code, name)
+    _check(code, "moe_forward_fp8a")
     return (y, *extra) if routing_out else y
-
-
-def moe_forward_fp8a_packed(x, W_gate, W13qp, s13, W2qp, s2, K: int, renorm: bool, bias=None, y=None, ws=None,
-                            routing_out=False, stream=None):
-    """moe_forward_fp8a over codes packed by moe_pack_fp8_w13 / moe_pack_fp8_w2 (the same results bit for
-    bit)."""
-    return moe_forward_fp8a(x, W_gate, W13qp, s13, W2qp, s2, K, renorm, bias=bias, y=y, ws=ws,
-                            routing_out=routing_out, stream=stream, _packed=True)
 

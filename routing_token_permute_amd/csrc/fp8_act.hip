@@ -222,10 +222,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // perm or offsets yet; every workgroup places the n_a * topk routing ids
 // itself in LDS (place_pairs), slot t is expert t / NB and column block
 // t % NB, and workgroup 0 writes the metadata for the kernels that follow.
-// BPK: the weight codes are in the packed form of launch_pack_fp8 (per expert
-// and 128 K codes, one 32 KB unit per 256-column block, laid out as a stage's
-// B part): each stage's B part is a copy of one contiguous unit.
-template <bool GATED, bool GATHER, int BM, int BK, int CAP, int WM, int WN, bool IDS = false, bool BPK = false>
+template <bool GATED, bool GATHER, int BM, int BK, int CAP, int WM, int WN, bool IDS = false>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
     const uint8_t* __restrict__ Aq, const float* __restrict__ a_scale, const int32_t* __restrict__ perm, int topk,
     int n_a, const int32_t* __restrict__ offsets, int E, int rows, int Kdim, const uint8_t* __restrict__ Bq,
@@ -235,7 +232,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
   static_assert(!IDS || (GATHER && BM < 256), "placement from ids: gathered decode GEMM1");
   using Cfg = F8Cfg<BM, BK, CAP>;
   constexpr int STAGE = Cfg::STAGE, NSTAGE = Cfg::NSTAGE, A_BYTES = Cfg::A_BYTES, A_REG = Cfg::A_REG;
-  constexpr int B_UNIT = Cfg::B_BYTES;  // bytes of one packed unit (BPK)
   constexpr int ROW = Cfg::ROW, CPR = Cfg::CPR, RPR = Cfg::ROWS_PER_REGION;
   constexpr int NW = WM * WN;
   constexpr int MT = BM / WM / 32;        // 32-row MFMA tiles per wave
@@ -301,8 +297,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
           arow = ((unsigned)f < (unsigned)(n_a * topk)) ? f / topk : 0;
         }
         src[j] = Aq + (size_t)arow * Kdim + c * 16;
-      } else if constexpr (BPK) {  // the unit of (expert, k-range 0, block t.nb), region r - A_REG
-        src[j] = Bq + ((size_t)t.e * nk * NB + t.nb) * (size_t)B_UNIT + (r - A_REG) * 1024 + lane * 16;
       } else {
         int code_row;
         if constexpr (GATED) {  // 128 gate columns, then the matching 128 up columns
@@ -321,11 +315,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_f8f8_kernel(
   auto issue = [&](int kt, int stage) {
     const uint32_t base = lds0 + stage * STAGE + (uint32_t)wave * REG * 1024;
 #pragma unroll
-    for (int j = 0; j < REG; ++j) {
-      // Packed codes: the next k-range's unit of the same block is NB units on.
-      const bool packed_b = BPK && wave * REG + j >= A_REG;
-      dma16(src[j] + (size_t)kt * (packed_b ? (size_t)NB * B_UNIT : (size_t)BK), base + j * 1024);
-    }
+    for (int j = 0; j < REG; ++j) dma16(src[j] + (size_t)kt * BK, base + j * 1024);
   };
   auto issue_first = [&]() {
 #pragma unroll
@@ -513,64 +503,28 @@ constexpr int kF8SmallRowsPerExpert = 64;
 // scales)^T over each expert's rows: GEMM1 (GATED: B = W13 codes (E, 2I, H),
 // h = SwiGLU of the paired columns, ncols = I) or GEMM2 (B = W2 codes
 // (E, H, I), ncols = H).
-template <bool GATED, bool GATHER, int BM, int BK, int CAP, int WM, int WN, bool BPK>
+template <bool GATED, bool GATHER, int BM, int BK, int CAP, int WM, int WN>
 void launch_f8f8_cfg(const uint8_t* Aq, const float* a_scale, const int32_t* perm, int topk, int n_a,
                      const int32_t* offsets, int E, int rows, int Kdim, const uint8_t* Bq, const float* b_scale, int N,
                      int I, void* C, hipStream_t s) {
   const int NB = GATED ? ceil_div(I, BN / 2) : ceil_div(N, BN);
   const int n_slots = max_row_tiles(rows, E, BM) * NB;
   const int grid = std::min(n_slots, stream_cu_count(s));
-  gemm_f8f8_kernel<GATED, GATHER, BM, BK, CAP, WM, WN, false, BPK><<<grid, 64 * WM * WN, 0, s>>>(
+  gemm_f8f8_kernel<GATED, GATHER, BM, BK, CAP, WM, WN><<<grid, 64 * WM * WN, 0, s>>>(
       Aq, a_scale, perm, topk, n_a, offsets, E, rows, Kdim, Bq, (long long)N * Kdim, b_scale, N, I, (uint16_t*)C, NB,
       n_slots, IdsMeta{});
 }
 
-// BPK: Bq in the packed form of launch_pack_fp8.
-template <bool GATED, bool GATHER = false, bool BPK = false>
+template <bool GATED, bool GATHER = false>
 void launch_f8f8(const uint8_t* Aq, const float* a_scale, const int32_t* offsets, int E, int rows, int Kdim,
                  const uint8_t* Bq, const float* b_scale, int N, int I, void* C, hipStream_t s,
                  const int32_t* perm = nullptr, int topk = 1, int n_a = 0) {
   if ((long long)rows <= (long long)kF8SmallRowsPerExpert * E)
-    launch_f8f8_cfg<GATED, GATHER, kF8SmallBM, kF8SmallBK, kF8SmallCap, kF8SmallWM, kF8SmallWN, BPK>(
+    launch_f8f8_cfg<GATED, GATHER, kF8SmallBM, kF8SmallBK, kF8SmallCap, kF8SmallWM, kF8SmallWN>(
         Aq, a_scale, perm, topk, n_a, offsets, E, rows, Kdim, Bq, b_scale, N, I, C, s);
   else
-    launch_f8f8_cfg<GATED, GATHER, kF8BM, kF8BK, kF8Cap, kF8WM, kF8WN, BPK>(Aq, a_scale, perm, topk, n_a, offsets, E,
-                                                                          rows, Kdim, Bq, b_scale, N, I, C, s);
-}
-
-// One workgroup per packed unit (expert e, 128-code k-range u, column block
-// nb): 256 code rows x 128 codes, row r's 16-byte chunk q at byte r * 128 +
-// 16 * (q ^ ((r / 2) % 8)) (a stage's B layout). Gated (half = I > 0): rows
-// 0-127 are the gate columns nb * 128 + r, 128-255 the matching up columns
-// I + nb * 128 + r - 128; otherwise column nb * 256 + r. Rows past the matrix
-// are zero. codes: (E, Ncols, Kdim), each column's Kdim codes contiguous.
-constexpr int kF8Unit = BN * kF8BK;  // bytes per packed unit (32 KB)
-__global__ __launch_bounds__(256) void pack_fp8_kernel(const uint8_t* __restrict__ codes, int Kdim, int Ncols,
-                                                       int NB, int half, uint8_t* __restrict__ out) {
-  const int units = Kdim / kF8BK;
-  const int nb = blockIdx.x % NB;
-  const int eu = blockIdx.x / NB;
-  const int u = eu % units, e = eu / units;
-  uint8_t* dst = out + (size_t)blockIdx.x * kF8Unit;
-#pragma unroll
-  for (int i = 0; i < kF8Unit / 16 / 256; ++i) {
-    const int p = threadIdx.x + 256 * i;  // 16-byte piece of the unit
-    const int r = p >> 3, slot = p & 7;
-    const int q = slot ^ ((r >> 1) & 7);
-    int col;
-    bool ok;
-    if (half > 0) {
-      const int j = nb * 128 + (r & 127);
-      ok = j < half;
-      col = (r < 128) ? j : half + j;
-    } else {
-      col = nb * 256 + r;
-      ok = col < Ncols;
-    }
-    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-    if (ok) v = *(const u32x4_t*)(codes + ((size_t)e * Ncols + col) * Kdim + (size_t)u * kF8BK + q * 16);
-    *(u32x4_t*)(dst + p * 16) = v;
-  }
+    launch_f8f8_cfg<GATED, GATHER, kF8BM, kF8BK, kF8Cap, kF8WM, kF8WN>(Aq, a_scale, perm, topk, n_a, offsets, E, rows,
+                                                                     Kdim, Bq, b_scale, N, I, C, s);
 }
 
 }  // namespace
@@ -619,13 +573,10 @@ hipError_t launch_w13_swiglu_fp8a(const uint8_t* x_q, const float* x_scale, cons
 
 hipError_t launch_w13_swiglu_gather_fp8a(const uint8_t* codes_tok, const float* s_tok, const int32_t* perm, int n,
                                          int K, const int32_t* offsets, const uint8_t* W13q, const float* s13, int E,
-                                         int H, int I, void* h, hipStream_t s, bool packed) {
+                                         int H, int I, void* h, hipStream_t s) {
   const int rows = n * K;
   if (rows == 0) return hipSuccess;
-  if (packed)
-    launch_f8f8<true, true, true>(codes_tok, s_tok, offsets, E, rows, H, W13q, s13, 2 * I, I, h, s, perm, K, n);
-  else
-    launch_f8f8<true, true>(codes_tok, s_tok, offsets, E, rows, H, W13q, s13, 2 * I, I, h, s, perm, K, n);
+  launch_f8f8<true, true>(codes_tok, s_tok, offsets, E, rows, H, W13q, s13, 2 * I, I, h, s, perm, K, n);
   return hipGetLastError();
 }
 
@@ -637,45 +588,24 @@ bool w13_from_ids_fp8a_ok(int n, int K, int E) {
 hipError_t launch_w13_swiglu_from_ids_fp8a(const uint8_t* codes_tok, const float* s_tok, const int32_t* ids, int n,
                                            int K, const uint8_t* W13q, const float* s13, int E, int H, int I, int ep,
                                            void* h, int32_t* counts, int32_t* offsets, int32_t* splits,
-                                           int32_t* perm, int32_t* inv, hipStream_t s, bool packed) {
+                                           int32_t* perm, int32_t* inv, hipStream_t s) {
   if (!w13_from_ids_fp8a_ok(n, K, E) || ep <= 0 || E % ep != 0) return hipErrorInvalidValue;
   int id_bits = 0;
   while ((1 << id_bits) < E) ++id_bits;
   const int NB = ceil_div(I, BN / 2);
   const int n_slots = E * NB;
   const int grid = std::min(n_slots, stream_cu_count(s));
-  const IdsMeta im{ids, counts, offsets, splits, perm, inv, ep, id_bits};
-  if (packed)
-    gemm_f8f8_kernel<true, true, kF8SmallBM, kF8SmallBK, kF8SmallCap, kF8SmallWM, kF8SmallWN, true, true>
-        <<<grid, 64 * kF8SmallWM * kF8SmallWN, 0, s>>>(codes_tok, s_tok, nullptr, K, n, nullptr, E, n * K, H, W13q,
-                                                        0, s13, 2 * I, I, (uint16_t*)h, NB, n_slots, im);
-  else
-    gemm_f8f8_kernel<true, true, kF8SmallBM, kF8SmallBK, kF8SmallCap, kF8SmallWM, kF8SmallWN, true>
-        <<<grid, 64 * kF8SmallWM * kF8SmallWN, 0, s>>>(codes_tok, s_tok, nullptr, K, n, nullptr, E, n * K, H, W13q,
-                                                        (long long)2 * I * H, s13, 2 * I, I, (uint16_t*)h, NB,
-                                                        n_slots, im);
+  gemm_f8f8_kernel<true, true, kF8SmallBM, kF8SmallBK, kF8SmallCap, kF8SmallWM, kF8SmallWN, true>
+      <<<grid, 64 * kF8SmallWM * kF8SmallWN, 0, s>>>(codes_tok, s_tok, nullptr, K, n, nullptr, E, n * K, H, W13q,
+                                                      (long long)2 * I * H, s13, 2 * I, I, (uint16_t*)h, NB, n_slots,
+                                                      IdsMeta{ids, counts, offsets, splits, perm, inv, ep, id_bits});
   return hipGetLastError();
 }
 
 hipError_t launch_w2_fp8a(const uint8_t* h_q, const float* h_scale, const int32_t* offsets_padded, int rows_max,
-                          const uint8_t* W2q, const float* s2, int E, int H, int I, void* Y_perm, hipStream_t s,
-                          bool packed) {
+                          const uint8_t* W2q, const float* s2, int E, int H, int I, void* Y_perm, hipStream_t s) {
   if (rows_max == 0) return hipSuccess;
-  if (packed)
-    launch_f8f8<false, false, true>(h_q, h_scale, offsets_padded, E, rows_max, I, W2q, s2, H, I, Y_perm, s);
-  else
-    launch_f8f8<false>(h_q, h_scale, offsets_padded, E, rows_max, I, W2q, s2, H, I, Y_perm, s);
-  return hipGetLastError();
-}
-
-size_t packed_fp8_bytes(int E, int Kdim, int NB) { return (size_t)E * NB * (Kdim / kF8BK) * kF8Unit; }
-
-hipError_t launch_pack_fp8(const uint8_t* codes, int E, int Kdim, int Ncols, int half, int NB, uint8_t* out,
-                           hipStream_t s) {
-  if (E <= 0 || Kdim <= 0 || Kdim % kF8BK != 0 || NB <= 0) return hipErrorInvalidValue;
-  const long long blocks = (long long)E * NB * (Kdim / kF8BK);
-  if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  pack_fp8_kernel<<<(int)blocks, 256, 0, s>>>(codes, Kdim, Ncols, NB, half, out);
+  launch_f8f8<false>(h_q, h_scale, offsets_padded, E, rows_max, I, W2q, s2, H, I, Y_perm, s);
   return hipGetLastError();
 }
 

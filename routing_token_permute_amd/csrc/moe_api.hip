@@ -1080,13 +1080,9 @@ moe_status moe_expert_w13_swiglu_fp8a(const uint8_t* x_q, const float* x_scale, 
   return from_hip(launch_w13_swiglu_fp8a(x_q, x_scale, offsets_padded, rows_max, W13q, s13, E, H, I, h, stream));
 }
 
-}  // extern "C"
-
-namespace {
-
-moe_status w13_gather_fp8a_call(const uint8_t* codes_tok, const float* s_tok, const int32_t* perm, int n, int K,
-                                const int32_t* offsets, const uint8_t* W13q, const float* s13, int E, int H, int I,
-                                void* h, hipStream_t stream, bool packed) {
+moe_status moe_expert_w13_swiglu_gather_fp8a(const uint8_t* codes_tok, const float* s_tok, const int32_t* perm,
+                                             int n, int K, const int32_t* offsets, const uint8_t* W13q,
+                                             const float* s13, int E, int H, int I, void* h, hipStream_t stream) {
   if (n < 0 || !experts_ok(E, K) || !hidden_ok(H, MOE_BF16) || H % 128 != 0 || !hidden_ok(I, MOE_BF16))
     return MOE_EINVAL;
   if ((long long)n * K > INT32_MAX) return MOE_EINVAL;
@@ -1096,13 +1092,14 @@ moe_status w13_gather_fp8a_call(const uint8_t* codes_tok, const float* s_tok, co
     return MOE_EINVAL;
   if (!vec_ok({codes_tok, W13q, s13, h}) || !word_ok({s_tok, perm, offsets})) return MOE_EINVAL;
   return from_hip(
-      launch_w13_swiglu_gather_fp8a(codes_tok, s_tok, perm, n, K, offsets, W13q, s13, E, H, I, h, stream, packed));
+      launch_w13_swiglu_gather_fp8a(codes_tok, s_tok, perm, n, K, offsets, W13q, s13, E, H, I, h, stream));
 }
 
-moe_status w13_from_ids_fp8a_call(const uint8_t* codes_tok, const float* s_tok, const int32_t* topk_ids, int n,
-                                  int K, const uint8_t* W13q, const float* s13, int E, int H, int I, int ep, void* h,
-                                  int32_t* counts, int32_t* offsets, int32_t* splits, int32_t* perm, int32_t* inv,
-                                  hipStream_t stream, bool packed) {
+moe_status moe_expert_w13_swiglu_from_ids_fp8a(const uint8_t* codes_tok, const float* s_tok,
+                                               const int32_t* topk_ids, int n, int K, const uint8_t* W13q,
+                                               const float* s13, int E, int H, int I, int ep, void* h,
+                                               int32_t* counts, int32_t* offsets, int32_t* splits, int32_t* perm,
+                                               int32_t* inv, hipStream_t stream) {
   if (n < 0 || !experts_ok(E, K) || ep < 1 || E % ep != 0 || !hidden_ok(H, MOE_BF16) || H % 128 != 0 ||
       !hidden_ok(I, MOE_BF16) || I % 128 != 0)
     return MOE_EINVAL;
@@ -1118,12 +1115,12 @@ moe_status w13_from_ids_fp8a_call(const uint8_t* codes_tok, const float* s_tok, 
     return MOE_EINVAL;
   if (!vec_ok({codes_tok, W13q, s13, h})) return MOE_EINVAL;
   return from_hip(launch_w13_swiglu_from_ids_fp8a(codes_tok, s_tok, topk_ids, n, K, W13q, s13, E, H, I, ep, h,
-                                                  counts, offsets, splits, perm, inv, stream, packed));
+                                                  counts, offsets, splits, perm, inv, stream));
 }
 
-moe_status w2_fp8a_call(const uint8_t* h_q, const float* h_scale, const int32_t* offsets_padded, int rows_max,
-                        const uint8_t* W2q, const float* s2, int E, int H, int I, void* Y_perm, hipStream_t stream,
-                        bool packed) {
+moe_status moe_expert_w2_fp8a(const uint8_t* h_q, const float* h_scale, const int32_t* offsets_padded, int rows_max,
+                              const uint8_t* W2q, const float* s2, int E, int H, int I, void* Y_perm,
+                              hipStream_t stream) {
   if (rows_max < 0 || E < 1 || E > kMaxExperts || !hidden_ok(H, MOE_BF16) || !hidden_ok(I, MOE_BF16) ||
       I % 128 != 0)
     return MOE_EINVAL;
@@ -1132,15 +1129,18 @@ moe_status w2_fp8a_call(const uint8_t* h_q, const float* h_scale, const int32_t*
       Y_perm == nullptr)
     return MOE_EINVAL;
   if (!vec_ok({h_q, W2q, s2, Y_perm}) || !word_ok({h_scale, offsets_padded})) return MOE_EINVAL;
-  return from_hip(
-      launch_w2_fp8a(h_q, h_scale, offsets_padded, rows_max, W2q, s2, E, H, I, Y_perm, stream, packed));
+  return from_hip(launch_w2_fp8a(h_q, h_scale, offsets_padded, rows_max, W2q, s2, E, H, I, Y_perm, stream));
 }
 
-moe_status forward_fp8a_call(const void* x, const void* W_gate, const float* bias, const uint8_t* W13q,
-                             const float* s13, const uint8_t* W2q, const float* s2, int n, int H, int I, int E, int K,
-                             int renorm, moe_dtype dt, void* y, float* logits_out, int32_t* topk_ids_out,
-                             float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes, hipStream_t stream,
-                             bool packed) {
+size_t moe_forward_fp8a_workspace_size(int n, int H, int I, int E, int K) {
+  if (n < 0 || H < 1 || I < 1 || E < 1 || K < 1) return 0;
+  return fp8a_layout(n, H, I, E, K).total;
+}
+
+moe_status moe_forward_fp8a(const void* x, const void* W_gate, const float* bias, const uint8_t* W13q,
+                            const float* s13, const uint8_t* W2q, const float* s2, int n, int H, int I, int E, int K,
+                            int renorm, moe_dtype dt, void* y, float* logits_out, int32_t* topk_ids_out,
+                            float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!dtype_ok(dt)) return MOE_EUNSUPPORTED;
   if (dt != MOE_BF16) return MOE_EUNSUPPORTED;
   if (n < 0 || !experts_ok(E, K) || !hidden_ok(H, dt) || H % 128 != 0 || !hidden_ok(I, dt) || I % 128 != 0)
@@ -1177,7 +1177,7 @@ moe_status forward_fp8a_call(const void* x, const void* W_gate, const float* bia
     if (e == hipSuccess) e = launch_quantize_rows_fp8(x, n, H, dt, codes_tok, s_tok, stream);
     if (e == hipSuccess)
       e = launch_w13_swiglu_from_ids_fp8a(codes_tok, s_tok, ids, n, K, W13q, s13, E, H, I, 1, base + L.h, counts,
-                                          offsets, (int32_t*)(base + L.splits), perm, inv, stream, packed);
+                                          offsets, (int32_t*)(base + L.splits), perm, inv, stream);
   } else {
     if (e == hipSuccess)
       e = launch_permute(ids, nullptr, n, H, E, K, 1, dt, counts, offsets, (int32_t*)(base + L.splits), perm, inv,
@@ -1185,7 +1185,7 @@ moe_status forward_fp8a_call(const void* x, const void* W_gate, const float* bia
     if (e == hipSuccess) e = launch_quantize_rows_fp8(x, n, H, dt, codes_tok, s_tok, stream);
     if (e == hipSuccess)
       e = launch_w13_swiglu_gather_fp8a(codes_tok, s_tok, perm, n, K, offsets, W13q, s13, E, H, I, base + L.h,
-                                        stream, packed);
+                                        stream);
   }
   // h per row in FP8, then GEMM2 on the FP8 MFMA.
   if (e == hipSuccess)
@@ -1193,102 +1193,9 @@ moe_status forward_fp8a_call(const void* x, const void* W_gate, const float* bia
                                  stream);
   if (e == hipSuccess)
     e = launch_w2_fp8a((uint8_t*)(base + L.h_q), (float*)(base + L.h_scale), offsets, nk, W2q, s2, E, H, I,
-                       base + L.Y_perm, stream, packed);
+                       base + L.Y_perm, stream);
   if (e == hipSuccess) e = launch_combine(base + L.Y_perm, inv, w, n, H, K, dt, y, stream);
   return from_hip(e);
-}
-
-}  // namespace
-
-extern "C" {
-
-moe_status moe_expert_w13_swiglu_gather_fp8a(const uint8_t* codes_tok, const float* s_tok, const int32_t* perm,
-                                             int n, int K, const int32_t* offsets, const uint8_t* W13q,
-                                             const float* s13, int E, int H, int I, void* h, hipStream_t stream) {
-  return w13_gather_fp8a_call(codes_tok, s_tok, perm, n, K, offsets, W13q, s13, E, H, I, h, stream, false);
-}
-
-moe_status moe_expert_w13_swiglu_gather_fp8a_packed(const uint8_t* codes_tok, const float* s_tok,
-                                                    const int32_t* perm, int n, int K, const int32_t* offsets,
-                                                    const uint8_t* W13qp, const float* s13, int E, int H, int I,
-                                                    void* h, hipStream_t stream) {
-  return w13_gather_fp8a_call(codes_tok, s_tok, perm, n, K, offsets, W13qp, s13, E, H, I, h, stream, true);
-}
-
-moe_status moe_expert_w13_swiglu_from_ids_fp8a(const uint8_t* codes_tok, const float* s_tok,
-                                               const int32_t* topk_ids, int n, int K, const uint8_t* W13q,
-                                               const float* s13, int E, int H, int I, int ep, void* h,
-                                               int32_t* counts, int32_t* offsets, int32_t* splits, int32_t* perm,
-                                               int32_t* inv, hipStream_t stream) {
-  return w13_from_ids_fp8a_call(codes_tok, s_tok, topk_ids, n, K, W13q, s13, E, H, I, ep, h, counts, offsets, splits,
-                                perm, inv, stream, false);
-}
-
-moe_status moe_expert_w13_swiglu_from_ids_fp8a_packed(const uint8_t* codes_tok, const float* s_tok,
-                                                      const int32_t* topk_ids, int n, int K, const uint8_t* W13qp,
-                                                      const float* s13, int E, int H, int I, int ep, void* h,
-                                                      int32_t* counts, int32_t* offsets, int32_t* splits,
-                                                      int32_t* perm, int32_t* inv, hipStream_t stream) {
-  return w13_from_ids_fp8a_call(codes_tok, s_tok, topk_ids, n, K, W13qp, s13, E, H, I, ep, h, counts, offsets,
-                                splits, perm, inv, stream, true);
-}
-
-moe_status moe_expert_w2_fp8a(const uint8_t* h_q, const float* h_scale, const int32_t* offsets_padded, int rows_max,
-                              const uint8_t* W2q, const float* s2, int E, int H, int I, void* Y_perm,
-                              hipStream_t stream) {
-  return w2_fp8a_call(h_q, h_scale, offsets_padded, rows_max, W2q, s2, E, H, I, Y_perm, stream, false);
-}
-
-moe_status moe_expert_w2_fp8a_packed(const uint8_t* h_q, const float* h_scale, const int32_t* offsets_padded,
-                                     int rows_max, const uint8_t* W2qp, const float* s2, int E, int H, int I,
-                                     void* Y_perm, hipStream_t stream) {
-  return w2_fp8a_call(h_q, h_scale, offsets_padded, rows_max, W2qp, s2, E, H, I, Y_perm, stream, true);
-}
-
-size_t moe_forward_fp8a_workspace_size(int n, int H, int I, int E, int K) {
-  if (n < 0 || H < 1 || I < 1 || E < 1 || K < 1) return 0;
-  return fp8a_layout(n, H, I, E, K).total;
-}
-
-moe_status moe_forward_fp8a(const void* x, const void* W_gate, const float* bias, const uint8_t* W13q,
-                            const float* s13, const uint8_t* W2q, const float* s2, int n, int H, int I, int E, int K,
-                            int renorm, moe_dtype dt, void* y, float* logits_out, int32_t* topk_ids_out,
-                            float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  return forward_fp8a_call(x, W_gate, bias, W13q, s13, W2q, s2, n, H, I, E, K, renorm, dt, y, logits_out,
-                           topk_ids_out, topk_w_out, counts_out, ws, ws_bytes, stream, false);
-}
-
-moe_status moe_forward_fp8a_packed(const void* x, const void* W_gate, const float* bias, const uint8_t* W13qp,
-                                   const float* s13, const uint8_t* W2qp, const float* s2, int n, int H, int I, int E,
-                                   int K, int renorm, moe_dtype dt, void* y, float* logits_out, int32_t* topk_ids_out,
-                                   float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
-                                   hipStream_t stream) {
-  return forward_fp8a_call(x, W_gate, bias, W13qp, s13, W2qp, s2, n, H, I, E, K, renorm, dt, y, logits_out,
-                           topk_ids_out, topk_w_out, counts_out, ws, ws_bytes, stream, true);
-}
-
-size_t moe_packed_fp8_w13_bytes(int E, int H, int I) {
-  if (E < 1 || E > kMaxExperts || !hidden_ok(H, MOE_BF16) || H % 128 != 0 || !hidden_ok(I, MOE_BF16)) return 0;
-  return packed_fp8_bytes(E, H, ceil_div(I, 128));
-}
-
-size_t moe_packed_fp8_w2_bytes(int E, int H, int I) {
-  if (E < 1 || E > kMaxExperts || !hidden_ok(H, MOE_BF16) || !hidden_ok(I, MOE_BF16) || I % 128 != 0) return 0;
-  return packed_fp8_bytes(E, I, ceil_div(H, 256));
-}
-
-moe_status moe_pack_fp8_w13(const uint8_t* W13q, int E, int H, int I, uint8_t* W13qp, hipStream_t stream) {
-  if (E < 1 || E > kMaxExperts || !hidden_ok(H, MOE_BF16) || H % 128 != 0 || !hidden_ok(I, MOE_BF16))
-    return MOE_EINVAL;
-  if (W13q == nullptr || W13qp == nullptr || !vec_ok({W13q, W13qp})) return MOE_EINVAL;
-  return from_hip(launch_pack_fp8(W13q, E, H, 2 * I, I, ceil_div(I, 128), W13qp, stream));
-}
-
-moe_status moe_pack_fp8_w2(const uint8_t* W2q, int E, int H, int I, uint8_t* W2qp, hipStream_t stream) {
-  if (E < 1 || E > kMaxExperts || !hidden_ok(H, MOE_BF16) || !hidden_ok(I, MOE_BF16) || I % 128 != 0)
-    return MOE_EINVAL;
-  if (W2q == nullptr || W2qp == nullptr || !vec_ok({W2q, W2qp})) return MOE_EINVAL;
-  return from_hip(launch_pack_fp8(W2q, E, I, H, 0, ceil_div(H, 256), W2qp, stream));
 }
 
 }  // extern "C"

@@ -203,7 +203,7 @@ hipError_t launch_w13_swiglu_fp8a(const uint8_t* x_q, const float* x_scale, cons
 // h (n*K, I) bf16 over the unpadded offsets.
 hipError_t launch_w13_swiglu_gather_fp8a(const uint8_t* codes_tok, const float* s_tok, const int32_t* perm, int n,
                                          int K, const int32_t* offsets, const uint8_t* W13q, const float* s13, int E,
-                                         int H, int I, void* h, hipStream_t s, bool packed = false);
+                                         int H, int I, void* h, hipStream_t s);
 // The same from the routing ids on decode-sized batches (n <= 32, n * K <=
 // 1024, E <= 256): the GEMM places the pairs itself and writes counts,
 // offsets, splits, perm and inv. w13_from_ids_fp8a_ok says whether it serves
@@ -212,19 +212,11 @@ bool w13_from_ids_fp8a_ok(int n, int K, int E);
 hipError_t launch_w13_swiglu_from_ids_fp8a(const uint8_t* codes_tok, const float* s_tok, const int32_t* ids, int n,
                                            int K, const uint8_t* W13q, const float* s13, int E, int H, int I, int ep,
                                            void* h, int32_t* counts, int32_t* offsets, int32_t* splits,
-                                           int32_t* perm, int32_t* inv, hipStream_t s, bool packed = false);
+                                           int32_t* perm, int32_t* inv, hipStream_t s);
 // GEMM2 with FP8 activations: Y_perm (rows_max, H) bf16 = (h codes x per-row
 // scales) . (W2 codes x column scales) over the padded receive buffer's rows.
 hipError_t launch_w2_fp8a(const uint8_t* h_q, const float* h_scale, const int32_t* offsets_padded, int rows_max,
-                          const uint8_t* W2q, const float* s2, int E, int H, int I, void* Y_perm, hipStream_t s,
-                          bool packed = false);
-// packed (the three FP8 x FP8 launchers above): the weight codes in the form
-// launch_pack_fp8 writes. The pack: codes (E, Ncols, Kdim) with Kdim % 128
-// == 0 into E * (Kdim / 128) * NB units of 32 KB; half = I for W13 (NB =
-// ceil(I / 128)), 0 for W2 (NB = ceil(Ncols / 256)).
-size_t packed_fp8_bytes(int E, int Kdim, int NB);
-hipError_t launch_pack_fp8(const uint8_t* codes, int E, int Kdim, int Ncols, int half, int NB, uint8_t* out,
-                           hipStream_t s);
+                          const uint8_t* W2q, const float* s2, int E, int H, int I, void* Y_perm, hipStream_t s);
 
 }  // namespace moe
 

@@ -173,105 +173,3 @@ def test_from_ids_packed_matches_plain(dev, n, E, K):
     assert _same(h, hp)
     for k in ("counts", "offsets", "splits", "perm", "inv"):
         assert torch.equal(meta[k], metap[k]), k
-
-
-# ---- packed FP8 codes (moe_pack_fp8_w13 / moe_pack_fp8_w2) ----
-
-def _pack_fp8_reference(Wq, half):
-    """The packed FP8 layout, written out: Wq (E, N, Kdim) uint8 codes, each column's Kdim codes contiguous;
-    per expert and 128 codes of K, one unit of 256 columns x 128 codes per output block, column c's 16-byte
-    chunks at slot chunk ^ ((c / 2) % 8)."""
-    E, N, Kdim = Wq.shape
-    cols = _block_columns(N, half)
-    NB = cols.shape[0]
-    out = np.zeros((E, Kdim // 128, NB, 256, 128), dtype=np.uint8)
-    chunks = Wq.reshape(E, N, Kdim // 128, 8, 16)  # (e, column, unit, chunk q, byte)
-    for nb in range(NB):
-        for c in range(256):
-            col = cols[nb, c]
-            if col < 0:
-                continue
-            for q in range(8):
-                slot = q ^ ((c >> 1) & 7)
-                out[:, :, nb, c, 16 * slot:16 * slot + 16] = chunks[:, col, :, q, :]
-    return out
-
-
-@pytest.mark.parametrize("E,H,I", [(3, 128, 192), (2, 384, 128), (4, 256, 64), (8, 2048, 1024)])
-def test_pack_fp8_layout(dev, E, H, I):  # noqa: E741
-    """Any byte values land at the documented places, bit for bit (I = 192: a half-empty GEMM1 block; H = 384:
-    a half-empty GEMM2 block; I = 64 for W13 only, since W2's K dimension I must be a multiple of 128)."""
-    rng = np.random.default_rng(E * 7 + H + I)
-    w13 = rng.integers(0, 256, size=(E, 2 * I, H), dtype=np.uint8)
-    got13 = moe.moe_pack_fp8_w13(torch.from_numpy(w13).to(dev)).cpu().numpy()
-    assert (got13 == _pack_fp8_reference(w13, I)).all()
-    if I % 128 == 0:
-        w2 = rng.integers(0, 256, size=(E, H, I), dtype=np.uint8)
-        got2 = moe.moe_pack_fp8_w2(torch.from_numpy(w2).to(dev)).cpu().numpy()
-        assert (got2 == _pack_fp8_reference(w2, 0)).all()
-
-
-def _fp8a_both(dev, w):
-    t = layer_tensors(w, dev)
-    q13, s13 = moe.moe_quantize_fp8(t["W13"])
-    q2, s2 = moe.moe_quantize_fp8(t["W2"])
-    p13, p2 = moe.moe_pack_fp8_w13(q13), moe.moe_pack_fp8_w2(q2)
-    plain = moe.moe_forward_fp8a(t["x"], t["W_gate"], q13, s13, q2, s2, w.K, w.renorm, bias=t["bias"],
-                                 routing_out=True)
-    packed = moe.moe_forward_fp8a_packed(t["x"], t["W_gate"], p13, s13, p2, s2, w.K, w.renorm, bias=t["bias"],
-                                         routing_out=True)
-    torch.cuda.synchronize()
-    return plain, packed
-
-
-@pytest.mark.parametrize("name", ["olmoe_bf16", "olmoe_skewed_bf16", "decode_bf16"])
-def test_forward_fp8a_packed_matches_fp8a(dev, name):
-    """The FP8 layer over packed codes against the same layer over the plain codes (itself held to the
-    oracle elsewhere): 256-row tiles, the skewed load, and the decode GEMM1 from the ids; every output bit
-    for bit."""
-    plain, packed = _fp8a_both(dev, make_config(name))
-    for what, a, b in zip(("y", "logits", "topk_ids", "topk_w", "counts"), plain, packed):
-        assert _same(a, b), f"{name}: {what} differ"
-
-
-@pytest.mark.parametrize("n,H,I,E,K,skewed", [
-    (300, 128, 256, 8, 2, False),
-    (45, 384, 128, 32, 4, True),     # H = 384: GEMM2's second column block half empty
-    (700, 256, 384, 16, 4, False),   # I = 384: three GEMM1 blocks, three 128-deep GEMM2 units
-    (1, 128, 128, 8, 2, False),
-    (2000, 128, 128, 64, 8, True),   # 32-row and 256-row tiles side by side
-    (256, 7168, 2048, 8, 2, False),  # wide: 56 K-units per expert for GEMM1, 28 column blocks for GEMM2
-])
-def test_forward_fp8a_packed_ragged_shapes(dev, n, H, I, E, K, skewed):  # noqa: E741
-    w = make_layer(n, H, I, E, K, seed=n + H + I + E + 1, bias=zipf_bias(E) if skewed else None)
-    plain, packed = _fp8a_both(dev, w)
-    for what, a, b in zip(("y", "logits", "topk_ids", "topk_w", "counts"), plain, packed):
-        assert _same(a, b), f"n={n} H={H} I={I} E={E} K={K}: {what} differ"
-
-
-@pytest.mark.parametrize("n,H,I,E,K", [(4096, 2048, 1024, 64, 8), (300, 384, 128, 8, 2), (32, 256, 384, 16, 4)])
-def test_staged_fp8a_packed_gemms_match_plain(dev, n, H, I, E, K):  # noqa: E741
-    """The three FP8 x FP8 GEMM calls over packed codes give the plain calls' outputs bit for bit: the
-    gathered GEMM1, the decode GEMM1 from the ids (with its metadata) and GEMM2."""
-    w = make_layer(n, H, I, E, K, seed=5 * n + E)
-    t = layer_tensors(w, dev)
-    q13, s13 = moe.moe_quantize_fp8(t["W13"])
-    q2, s2 = moe.moe_quantize_fp8(t["W2"])
-    p13, p2 = moe.moe_pack_fp8_w13(q13), moe.moe_pack_fp8_w2(q2)
-    _, ids, _ = moe.moe_route(t["x"], t["W_gate"], None, K, False)
-    meta = moe.moe_permute(ids, None, E)
-    codes_tok, s_tok = moe.moe_quantize_rows_fp8(t["x"])
-    h = moe.moe_expert_w13_swiglu_gather_fp8a(codes_tok, s_tok, meta["perm"], K, meta["offsets"], q13, s13)
-    hp = moe.moe_expert_w13_swiglu_gather_fp8a_packed(codes_tok, s_tok, meta["perm"], K, meta["offsets"], p13, s13)
-    hq, hs = moe.moe_quantize_rows_fp8(h)
-    Y = moe.moe_expert_w2_fp8a(hq, hs, meta["offsets"], q2, s2)
-    Yp = moe.moe_expert_w2_fp8a_packed(hq, hs, meta["offsets"], p2, s2)
-    torch.cuda.synchronize()
-    assert _same(h, hp) and _same(Y, Yp)
-    if n <= 32:
-        hi, mi = moe.moe_expert_w13_swiglu_from_ids_fp8a(codes_tok, s_tok, ids, q13, s13)
-        hip, mip = moe.moe_expert_w13_swiglu_from_ids_fp8a_packed(codes_tok, s_tok, ids, p13, s13)
-        torch.cuda.synchronize()
-        assert _same(hi, hip)
-        for k in ("counts", "offsets", "splits", "perm", "inv"):
-            assert torch.equal(mi[k], mip[k]), k

@@ -382,51 +382,3 @@ def test_packed_weights_reject_bad_arguments(lib):
     bad = list(args)
     bad[9] = 9  # K > E
     assert lib.moe_forward_packed(*bad) == EINVAL
-
-
-def test_packed_fp8_codes_reject_bad_arguments(lib):
-    """Packed FP8 sizes follow the documented layout (one byte per code, 128-deep units) and are 0 where the
-    packed K dimension is not a multiple of 128; the pack calls and the packed FP8 entries refuse bad shapes
-    and pointers before any HIP call, as the unpacked ones do."""
-    s = None
-    assert lib.moe_packed_fp8_w13_bytes(64, 2048, 1024) == 64 * 8 * 256 * 2048
-    assert lib.moe_packed_fp8_w2_bytes(64, 2048, 1024) == 64 * 8 * 256 * 1024
-    assert lib.moe_packed_fp8_w13_bytes(3, 128, 192) == 3 * 2 * 256 * 128  # I = 192: two 128-column blocks
-    assert lib.moe_packed_fp8_w2_bytes(3, 320, 128) == 3 * 2 * 256 * 128  # H = 320: two 256-column blocks
-    assert lib.moe_packed_fp8_w13_bytes(8, 192, 128) == 0  # H not a multiple of 128
-    assert lib.moe_packed_fp8_w2_bytes(8, 128, 192) == 0  # I not a multiple of 128
-    for E, H, I in ((0, 128, 128), (257, 128, 128), (8, 64, 128), (8, 0, 128)):
-        assert lib.moe_packed_fp8_w13_bytes(E, H, I) == 0
-        assert lib.moe_pack_fp8_w13(P, E, H, I, P, s) == EINVAL
-    for E, H, I in ((0, 128, 128), (8, 128, 64), (8, 96, 128)):
-        assert lib.moe_packed_fp8_w2_bytes(E, H, I) == 0
-        assert lib.moe_pack_fp8_w2(P, E, H, I, P, s) == EINVAL
-    M8 = ctypes.c_void_p(0x10008)  # 8-byte aligned only
-    assert lib.moe_pack_fp8_w13(None, 8, 128, 128, P, s) == EINVAL
-    assert lib.moe_pack_fp8_w2(P, 8, 128, 128, M8, s) == EINVAL
-    ws = lib.moe_forward_fp8a_workspace_size(16, 128, 128, 8, 2)
-    # x, W_gate, bias, W13qp, s13, W2qp, s2, n, H, I, E, K, renorm, dt, y, logits, ids, w, counts, ws, ws_bytes, s
-    args = [P, P, None, P, P, P, P, 16, 128, 128, 8, 2, 0, 1, P, None, None, None, None, P, ws, s]  # dt 1: bf16
-    for i, v, code in ((20, ws - 1, EWS), (3, None, EINVAL), (5, M8, EINVAL), (8, 192, EINVAL), (9, 192, EINVAL),
-                       (11, 9, EINVAL)):
-        bad = list(args)
-        bad[i] = v
-        assert lib.moe_forward_fp8a_packed(*bad) == code, (i, v)
-    # codes_tok, s_tok, ids, n, K, W13qp, s13, E, H, I, ep, h, counts, offsets, splits, perm, inv, stream
-    args = [P, P, P, 32, 8, P, P, 64, 128, 128, 1, P, P, P, P, P, P, s]
-    for i, v, code in ((3, 33, EUNSUP), (8, 192, EINVAL), (9, 192, EINVAL), (10, 3, EINVAL), (11, None, EINVAL)):
-        bad = list(args)
-        bad[i] = v
-        assert lib.moe_expert_w13_swiglu_from_ids_fp8a_packed(*bad) == code, (i, v)
-    # h_q, h_scale, offsets_padded, rows_max, W2qp, s2, E, H, I, Y_perm, stream
-    args = [P, P, P, 64, P, P, 8, 128, 128, P, s]
-    for i, v in ((4, None), (8, 192), (9, M8)):
-        bad = list(args)
-        bad[i] = v
-        assert lib.moe_expert_w2_fp8a_packed(*bad) == EINVAL, (i, v)
-    # codes_tok, s_tok, perm, n, K, offsets, W13qp, s13, E, H, I, h, stream
-    args = [P, P, P, 16, 2, P, P, P, 8, 128, 128, P, s]
-    for i, v in ((6, None), (9, 192), (11, M8)):
-        bad = list(args)
-        bad[i] = v
-        assert lib.moe_expert_w13_swiglu_gather_fp8a_packed(*bad) == EINVAL, (i, v)
