@@ -194,7 +194,7 @@ def test_w2_fp8a(dev, R_real, E, H, I, skew):  # noqa: E741
     assert_close(got[real], ref[real], "bf16", f"fp8a down R={R} E={E} H={H} I={I}", intermediate=True)
 
 
-@pytest.mark.parametrize("name", ["decode_bf16", "olmoe_bf16", "olmoe_skewed_bf16", "small"])
+@pytest.mark.parametrize("name", ["decode_bf16", "olmoe_bf16", "olmoe_skewed_bf16", "small", "wide"])
 def test_forward_fp8a_configs(dev, name):
     """The layer against the oracle, every row. Two integer decisions are compared given identical
     floating-point inputs, as the routing is: the ids from the device's fp32 logits (held to the fp64 router
@@ -202,7 +202,12 @@ def test_forward_fp8a_configs(dev, name):
     intermediate bounds): an h element within a bf16 ulp of an E4M3 midpoint may round either way, and a
     flipped code moves y by up to 2^-3 of that element's share. The rest of the layer is then held to the
     bf16 bounds: y against the oracle's product of those codes and the oracle's combine."""
-    w = make_config(name) if name != "small" else make_layer(200, 256, 128, 16, 4, dtype="bf16", renorm=True, seed=8)
+    if name == "small":
+        w = make_layer(200, 256, 128, 16, 4, dtype="bf16", renorm=True, seed=8)
+    elif name == "wide":  # H = 7168, I = 2048: GEMM1 56 k-steps of 128 codes and 16 column blocks, GEMM2 28 blocks
+        w = make_layer(256, 7168, 2048, 8, 2, dtype="bf16", seed=71, w_std=0.01)
+    else:
+        w = make_config(name)
     t = layer_tensors(w, dev)
     (q13, s13, q2, s2), (c13, r13, c2, r2) = _fp8_weights(w, t)
     y, logits, ids, wts, counts = moe.moe_forward_fp8a(t["x"], t["W_gate"], q13, s13, q2, s2, w.K, w.renorm,
