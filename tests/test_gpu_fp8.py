@@ -153,6 +153,15 @@ def test_forward_fp8_small_shapes(dev, n, H, I, E, K, renorm):  # noqa: E741
     _forward_fp8_parity(dev, w, f"forward fp8 n={n} E={E} K={K}")
 
 
+@pytest.mark.parametrize("n", [256, 16])
+def test_forward_fp8_wide_layer(dev, n):
+    """FP8 weights on a wide layer (H = 7168, I = 2048): the gathered GEMM1 (n = 256) and the decode GEMM1
+    from the ids (n = 16) over 7168-deep columns, GEMM2 over 28 column blocks; every row against the oracle.
+    Weights ~ N(0, 0.01^2), as in the bf16 wide-layer test."""
+    w = make_layer(n, 7168, 2048, 8, 2, seed=7 + n, w_std=0.01)
+    _forward_fp8_parity(dev, w, f"forward fp8 wide n={n}")
+
+
 def test_fp8_rejects_fp32_activations(dev):
     w = make_layer(8, 64, 64, 4, 2, dtype="f32", seed=1)
     t = layer_tensors(w, dev)
