@@ -340,6 +340,14 @@ def test_backward_small_shapes(dev, n, H, I, E, K, dtype, renorm):  # noqa: E741
     _backward_parity(dev, w, f"backward n={n} H={H} I={I} E={E} K={K} {dtype}")
 
 
+def test_backward_wide_layer(dev):
+    """The backward on a wide layer (H = 7168, I = 2048): the data gradients reduce over 2048- and 7168-wide
+    rows, dW13 and dW2 are 7168 x 4096 and 2048 x 7168 per expert; every gradient against the oracle.
+    Weights ~ N(0, 0.01^2), as in the forward's wide-layer test."""
+    w = make_layer(128, 7168, 2048, 8, 2, seed=29, w_std=0.01)
+    _backward_parity(dev, w, "backward wide H=7168 I=2048")
+
+
 @pytest.mark.parametrize("name", ["tiny_f32", "decode_bf16", "olmoe_bf16", "olmoe_skewed_bf16"])
 def test_backward_configs(dev, name):
     w = make_config(name)
